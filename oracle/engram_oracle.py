@@ -1,0 +1,315 @@
+"""Plain CPU oracle for the Engram conditional-memory forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+calls it and shares no code with it; the two meet only through the seeded
+inputs in `hashed_gram_embedding_amd.inputs`, which hold none of the method.
+
+What is computed, in the order and notation of "DeepSeek Engram series guide"
+(foosynaptic deepseek-tech-notes, section "Engram working principle"):
+
+  Step 1  x'_t = P(x_t)                         vocabulary projection
+  Step 2  g_{t,n} = (x'_{t-n+1}, ..., x'_t)     suffix n-grams, n = 2..N
+  Step 3  z_{t,n,k} = phi_{n,k}(g_{t,n}),  e_{t,n,k} = E_{n,k}[z_{t,n,k}]
+          phi is a multiplicative-XOR hash into a prime-sized table.  The page
+          does not give phi; it is fixed here as
+              z = (XOR_i  x'_{t-i} * m_{n,k,i}  mod 2^64)  mod p_{n,k}
+          with i = 0 the current token and ids before the sequence start
+          taken as 0 (or from the decode history).
+  Step 4  e_t = concat over n = 2..N (outer), k = 1..K (inner) of e_{t,n,k}
+  Step 5  k_t = W_K e_t,  v_t = W_V e_t
+  Step 6  alpha_t = sigmoid( RMSNorm(h_t) . RMSNorm(k_t) / sqrt(d) ),
+          v~_t = alpha_t v_t
+  Step 7  Y = SiLU( Conv1D( RMSNorm(V~) ) ) + V~, depthwise causal conv with
+          kernel w = 4 and dilation N
+  Step 8  H <- H + Y
+  Multi-branch variant (same page, "variant on a multi-branch backbone"):
+          per-branch gate alpha^(m) from h^(m) and W_K^(m) e_t, shared W_V,
+          u^(m) = alpha^(m) W_V e_t; each branch has its own conv and residual.
+
+Readings where the pages are silent (all listed in the design notes):
+  * RMSNorm(x) = x / sqrt(mean(x^2) + eps), over the d channels of one token
+    and one branch, with no learned gain.
+  * Conv taps follow the cross-correlation convention: weight [.., w-1]
+    multiplies the current position, weight [.., j] the position
+    (w-1-j)*dilation steps back; positions before the start read 0 (or the
+    decode state); there is no bias.
+  * int8 rows (lower-precision storage, "Engram module" article section 8,
+    and the single select-and-dequantise kernel of the DRAM/SSD offload
+    study) dequantise as float32(q) * float32(scale), rounded to bfloat16
+    (nearest-even) when the gathered rows are bfloat16.
+  * Decode state: the last N-1 compressed ids, and the last (w-1)*N conv
+    inputs u = RMSNorm(v~), oldest first.
+
+All floating-point arithmetic is float64 on values upcast exactly from their
+storage type; hashing is uint64 with wraparound.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MASK64 = (1 << 64) - 1
+
+
+# --------------------------------------------------------------------------
+# storage-format conversions (exact upcasts, one rounding helper)
+# --------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """uint16 bfloat16 bit patterns -> float64 (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16, nearest-even; returned as float64.
+
+    A bfloat16 keeps the top 16 bits of a float32.  Rounding to nearest-even
+    adds half of the dropped range (0x8000), minus one unless the kept part is
+    odd, then truncates.  Finite inputs only.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    keep_odd = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + keep_odd) >> np.uint64(16)) << np.uint64(16)
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def storage_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_to_f64(a)
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Step 1: vocabulary projection
+# --------------------------------------------------------------------------
+
+def compress(tokens: np.ndarray, proj: np.ndarray) -> np.ndarray:
+    """x'_t = P(x_t) for every token (Step 1)."""
+    return np.asarray(proj, dtype=np.int64)[np.asarray(tokens, dtype=np.int64)]
+
+
+# --------------------------------------------------------------------------
+# Step 2: suffix n-grams
+# --------------------------------------------------------------------------
+
+def history_id(xc: np.ndarray, b: int, pos: int, hist) -> int:
+    """Compressed id at position `pos` of sequence b; pos < 0 reads the decode
+    history (oldest first, last entry is position -1) or the pad id 0."""
+    if pos >= 0:
+        return int(xc[b, pos])
+    if hist is None:
+        return 0
+    h = np.asarray(hist)
+    j = h.shape[1] + pos
+    return int(h[b, j]) if j >= 0 else 0
+
+
+def suffix_ngram(xc: np.ndarray, b: int, t: int, n: int, hist=None) -> tuple:
+    """g_{t,n} = (x'_{t-n+1}, ..., x'_t) (Step 2), oldest first."""
+    return tuple(history_id(xc, b, t - n + 1 + i, hist) for i in range(n))
+
+
+def shifted_ids(xc: np.ndarray, i: int, hist) -> np.ndarray:
+    """Array of x'_{t-i} over all (b, t), with history / pad for t-i < 0."""
+    B, T = xc.shape
+    out = np.zeros((B, T), dtype=np.int64)
+    if i < T:
+        out[:, i:] = xc[:, : T - i]
+    for t in range(min(i, T)):
+        for b in range(B):
+            out[b, t] = history_id(xc, b, t - i, hist)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Step 3: multiplicative-XOR hash into prime-sized tables
+# --------------------------------------------------------------------------
+
+def hash_gram(gram_newest_first, mult_nk: np.ndarray, prime: int) -> int:
+    """phi_{n,k}: XOR over i of (id_i * m_{n,k,i}) mod 2^64, then mod p.
+    gram_newest_first[0] is x'_t, [1] is x'_{t-1}, ..."""
+    acc = np.zeros(1, dtype=np.uint64)
+    for i, x in enumerate(gram_newest_first):
+        acc ^= np.array([x], dtype=np.uint64) * np.asarray(mult_nk, dtype=np.uint64)[i]
+    return int(acc[0] % np.uint64(prime))
+
+
+def hash_grams(grams_newest_first: np.ndarray, mult_nk: np.ndarray, prime: int) -> np.ndarray:
+    """Vectorised phi_{n,k} over an array of n-grams [G, n] (newest first)."""
+    g = np.asarray(grams_newest_first, dtype=np.uint64)
+    acc = np.zeros(g.shape[0], dtype=np.uint64)
+    for i in range(g.shape[1]):
+        acc ^= g[:, i] * np.uint64(int(mult_nk[i]))
+    return (acc % np.uint64(int(prime))).astype(np.int64)
+
+
+def hash_indices(tokens: np.ndarray, proj: np.ndarray, mult: np.ndarray, prime: np.ndarray,
+                 max_n: int, heads: int, hist=None) -> np.ndarray:
+    """z[b, t, j] for table j = (n-2)*K + k (Steps 1-3).
+
+    tokens [B, T] raw ids; hist [B, N-1] compressed ids before t = 0 (oldest
+    first) or None for pad 0.  Returns int64 [B, T, (N-1)*K]."""
+    xc = compress(tokens, proj)
+    B, T = xc.shape
+    z = np.zeros((B, T, (max_n - 1) * heads), dtype=np.int64)
+    back = [shifted_ids(xc, i, hist).astype(np.uint64) for i in range(max_n)]
+    for n in range(2, max_n + 1):
+        for k in range(heads):
+            acc = np.zeros((B, T), dtype=np.uint64)
+            for i in range(n):
+                acc ^= back[i] * np.uint64(int(mult[n - 2, k, i]))
+            j = (n - 2) * heads + k
+            z[:, :, j] = (acc % np.uint64(int(prime[j]))).astype(np.int64)
+    return z
+
+
+# --------------------------------------------------------------------------
+# Steps 3-4: table lookup and concatenation
+# --------------------------------------------------------------------------
+
+def table_rows_f64(rows: np.ndarray, dtype: str, global_rows: np.ndarray,
+                   scale=None, out_dtype: str = "bf16") -> np.ndarray:
+    """Values of the requested rows as the gathered output type holds them.
+
+    f32 / bf16 rows are exact copies (an f32 row gathered into a bf16 output
+    is rounded to nearest-even); int8 rows are float32(q) * float32(scale),
+    rounded to bf16 for a bf16 output."""
+    r = np.asarray(rows)[global_rows]
+    if dtype == "i8":
+        s = np.asarray(scale, dtype=np.float32)[global_rows]
+        prod = r.astype(np.float32) * s[..., None]         # one IEEE float32 multiply
+        return round_f32_to_bf16(prod) if out_dtype == "bf16" else prod.astype(np.float64)
+    if dtype == "bf16":
+        return bf16_to_f64(r)
+    if out_dtype == "bf16":
+        return round_f32_to_bf16(r)
+    return r.astype(np.float64)
+
+
+def gather(z: np.ndarray, rows: np.ndarray, dtype: str, row_offset: np.ndarray, dim: int,
+           scale=None, out_dtype: str = "bf16") -> np.ndarray:
+    """e_t = concat_j E_j[z_{t,j}] (Steps 3-4).  z [..., n_tables] local rows;
+    returns float64 [..., n_tables * dim]."""
+    z = np.asarray(z, dtype=np.int64)
+    g = z + np.asarray(row_offset, dtype=np.int64)
+    vals = table_rows_f64(rows, dtype, g, scale, out_dtype)   # [..., n_tables, dim]
+    return vals.reshape(*z.shape[:-1], z.shape[-1] * dim)
+
+
+# --------------------------------------------------------------------------
+# Step 5: key / value projections
+# --------------------------------------------------------------------------
+
+def project_kv(e: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """[v | k^(0) | ... | k^(M-1)] = e W^T with W stacked [W_V; W_K^(0..M-1)],
+    each block [d, d_mem] (Step 5 and the fused-projection remark of the
+    multi-branch variant)."""
+    return np.asarray(e, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+
+
+# --------------------------------------------------------------------------
+# Step 6: context-aware gate
+# --------------------------------------------------------------------------
+
+def rmsnorm(x: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-np.asarray(x, dtype=np.float64)))
+
+
+def gate(h: np.ndarray, k: np.ndarray, eps: float) -> np.ndarray:
+    """alpha = sigmoid(RMSNorm(h) . RMSNorm(k) / sqrt(d)) over the last axis (Step 6)."""
+    d = h.shape[-1]
+    return sigmoid(np.sum(rmsnorm(h, eps) * rmsnorm(k, eps), axis=-1) / np.sqrt(d))
+
+
+# --------------------------------------------------------------------------
+# Step 7: short causal depthwise convolution
+# --------------------------------------------------------------------------
+
+def short_conv(u: np.ndarray, conv_w: np.ndarray, dilation: int, prev=None) -> np.ndarray:
+    """c_t[ch] = sum_j conv_w[ch, j] * u_{t-(w-1-j)*dilation}[ch] (Step 7).
+
+    u [T, d] for one sequence and branch; conv_w [d, w]; prev [(w-1)*dilation, d]
+    holds u at positions -(w-1)*dilation .. -1 (oldest first) or None for 0."""
+    T, d = u.shape
+    w = conv_w.shape[1]
+    span = (w - 1) * dilation
+    full = np.zeros((span + T, d), dtype=np.float64)
+    if prev is not None:
+        full[:span] = prev
+    full[span:] = u
+    c = np.zeros((T, d), dtype=np.float64)
+    for j in range(w):
+        back = (w - 1 - j) * dilation
+        c += conv_w[None, :, j] * full[span - back: span - back + T]
+    return c
+
+
+def silu(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x * sigmoid(x)
+
+
+# --------------------------------------------------------------------------
+# Steps 1-8: one Engram layer
+# --------------------------------------------------------------------------
+
+def new_state(B: int, max_n: int, branches: int, span: int, d: int) -> dict:
+    return {"ids": np.zeros((B, max_n - 1), dtype=np.int64),
+            "u": np.zeros((B, branches, span, d), dtype=np.float64),
+            "pos": np.zeros(B, dtype=np.int64)}
+
+
+def forward(tokens: np.ndarray, H: np.ndarray, layer, h_dtype: str, state=None,
+            e_dtype=None) -> dict:
+    """One Engram layer over tokens [B, T] and hidden states H [B, T, M, d].
+
+    `layer` is a `LayerInputs`-like object (hash, tables, w, conv_w, eps,
+    kernel_w, dilation, d, branches).  h_dtype is the storage type of H, W and
+    the gathered rows ("f32" or "bf16").  With `state` (see new_state) the
+    chunk continues earlier tokens and a new state is returned.
+    Returns float64 arrays: z, e, kv, alpha [B,T,M], vt, u, c, Y [B,T,M,d],
+    H_out, and `state`.
+    """
+    hp, tab = layer.hash, layer.tables
+    B, T = tokens.shape
+    M, d, eps = layer.branches, layer.d, layer.eps
+    span = (layer.kernel_w - 1) * layer.dilation
+    hist = None if state is None else state["ids"]
+    e_dtype = e_dtype or h_dtype
+
+    z = hash_indices(tokens, hp.proj, hp.mult, hp.prime, hp.max_n, hp.heads, hist)   # Steps 1-3
+    e = gather(z, tab.rows, tab.dtype, tab.row_offset, tab.dim, tab.scale, e_dtype)  # Steps 3-4
+    W = storage_to_f64(layer.w, h_dtype)
+    kv = project_kv(e, W)                                                            # Step 5
+    v = kv[..., :d]
+    h = storage_to_f64(H, h_dtype)
+
+    alpha = np.zeros((B, T, M))
+    vt = np.zeros((B, T, M, d))
+    u = np.zeros((B, T, M, d))
+    c = np.zeros((B, T, M, d))
+    for m in range(M):
+        k_m = kv[..., (1 + m) * d:(2 + m) * d]
+        alpha[:, :, m] = gate(h[:, :, m, :], k_m, eps)                               # Step 6
+        vt[:, :, m, :] = alpha[:, :, m, None] * v
+        u[:, :, m, :] = rmsnorm(vt[:, :, m, :], eps)                                 # Step 7
+        for b in range(B):
+            prev = None if state is None else state["u"][b, m]
+            c[b, :, m, :] = short_conv(u[b, :, m, :], layer.conv_w[m], layer.dilation, prev)
+    Y = silu(c) + vt
+    H_out = h + Y                                                                    # Step 8
+
+    out = {"z": z, "e": e, "kv": kv, "alpha": alpha, "vt": vt, "u": u, "c": c, "Y": Y, "H_out": H_out}
+    if state is not None:
+        xc = compress(tokens, hp.proj)
+        ids = np.concatenate([state["ids"], xc], axis=1)[:, -(hp.max_n - 1):]
+        uu = np.concatenate([state["u"], np.transpose(u, (0, 2, 1, 3))], axis=2)[:, :, -span:]
+        out["state"] = {"ids": ids, "u": uu, "pos": state["pos"] + T}
+    return out
