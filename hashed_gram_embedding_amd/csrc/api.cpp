@@ -1,0 +1,385 @@
+// C ABI of libengram.so (declared in include/engram.h): argument checks on
+// host-visible values, workspace carving and kernel launch order.  Nothing
+// here touches device data or synchronises, except engram_host_alloc/free.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "engram.h"
+#include "engram_internal.h"
+
+#define ENGRAM_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+engram_status fail(engram_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+engram_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ENGRAM_OK;
+  return fail(ENGRAM_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t dtype_size(int dt) {
+  switch (dt) {
+    case ENGRAM_F32: return 4;
+    case ENGRAM_BF16: return 2;
+    case ENGRAM_I8: return 1;
+    default: return 0;
+  }
+}
+
+engram_status check_hash(const engram_hash_params* hp, engram::HashArgs* out) {
+  if (hp == nullptr) return fail(ENGRAM_EINVAL, "hash params are NULL");
+  if (hp->proj == nullptr || hp->mult == nullptr || hp->prime == nullptr)
+    return fail(ENGRAM_EINVAL, "hash params: proj, mult and prime must be non-NULL");
+  if (hp->vocab <= 0) return fail(ENGRAM_EINVAL, "hash params: vocab must be positive");
+  if (hp->max_n < 2 || hp->max_n > ENGRAM_MAX_ORDER)
+    return fail(ENGRAM_EUNSUPPORTED, "hash params: max_n=%d outside [2, %d]", hp->max_n, ENGRAM_MAX_ORDER);
+  const int nt = (hp->max_n - 1) * hp->heads;
+  if (hp->heads < 1 || nt > ENGRAM_MAX_TABLES)
+    return fail(ENGRAM_EUNSUPPORTED, "hash params: (max_n-1)*heads=%d outside [1, %d]", nt, ENGRAM_MAX_TABLES);
+  if (out != nullptr) *out = engram::HashArgs{};
+  for (int n = 2; n <= hp->max_n; ++n) {
+    for (int k = 0; k < hp->heads; ++k) {
+      const int j = (n - 2) * hp->heads + k;
+      const uint32_t p = hp->prime[j];
+      if (p < 2 || p > 0x7fffffffu)
+        return fail(ENGRAM_EINVAL, "hash params: prime[%d]=%u outside [2, 2^31)", j, p);
+      if (out != nullptr) {
+        out->prime[j] = p;
+        out->order[j] = n;
+        for (int i = 0; i < n; ++i)
+          out->mult[j][i] = hp->mult[(static_cast<int64_t>(n - 2) * hp->heads + k) * hp->max_n + i];
+      }
+    }
+  }
+  if (out != nullptr) {
+    out->n_tables = nt;
+    out->max_n = hp->max_n;
+  }
+  return ENGRAM_OK;
+}
+
+engram_status check_tables(const engram_tables* tab, engram::TableArgs* out) {
+  if (tab == nullptr) return fail(ENGRAM_EINVAL, "tables are NULL");
+  if (tab->n_tables < 1 || tab->n_tables > ENGRAM_MAX_TABLES)
+    return fail(ENGRAM_EUNSUPPORTED, "tables: n_tables=%d outside [1, %d]", tab->n_tables, ENGRAM_MAX_TABLES);
+  if (tab->dim < 8 || tab->dim % 8 != 0)
+    return fail(ENGRAM_EUNSUPPORTED, "tables: dim=%d must be a positive multiple of 8", tab->dim);
+  if (tab->dtype != ENGRAM_F32 && tab->dtype != ENGRAM_BF16 && tab->dtype != ENGRAM_I8)
+    return fail(ENGRAM_EUNSUPPORTED, "tables: unknown dtype %d", static_cast<int>(tab->dtype));
+  if (tab->rows == nullptr || tab->row_offset == nullptr || tab->n_rows == nullptr)
+    return fail(ENGRAM_EINVAL, "tables: rows, row_offset and n_rows must be non-NULL");
+  const size_t row_align = tab->dtype == ENGRAM_I8 ? 8 : 16;
+  if (!aligned(tab->rows, row_align))
+    return fail(ENGRAM_EINVAL, "tables: rows must be %zu-byte aligned", row_align);
+  if (tab->total_rows <= 0) return fail(ENGRAM_EINVAL, "tables: total_rows must be positive");
+  for (int j = 0; j < tab->n_tables; ++j) {
+    const int64_t off = tab->row_offset[j], n = tab->n_rows[j];
+    if (off < 0 || n < 1 || n > 0x7fffffffLL || off + n > tab->total_rows)
+      return fail(ENGRAM_EINVAL, "tables: table %d (offset %lld, rows %lld) outside [0, total_rows=%lld)",
+                  j, static_cast<long long>(off), static_cast<long long>(n),
+                  static_cast<long long>(tab->total_rows));
+  }
+  if (tab->dtype == ENGRAM_I8 && tab->row_scale == nullptr)
+    return fail(ENGRAM_EINVAL, "tables: int8 rows need row_scale");
+  if (tab->cache_slot != nullptr) {
+    if (tab->cache_rows == nullptr || tab->cache_n < 0)
+      return fail(ENGRAM_EINVAL, "tables: a cache needs cache_rows and cache_n >= 0");
+    if (!aligned(tab->cache_rows, row_align))
+      return fail(ENGRAM_EINVAL, "tables: cache_rows must be %zu-byte aligned", row_align);
+    if (tab->dtype == ENGRAM_I8 && tab->cache_scale == nullptr)
+      return fail(ENGRAM_EINVAL, "tables: an int8 cache needs cache_scale");
+  }
+  if (out != nullptr) {
+    *out = engram::TableArgs{};
+    for (int j = 0; j < tab->n_tables; ++j) out->row_offset[j] = tab->row_offset[j];
+    out->rows = tab->rows;
+    out->scale = tab->row_scale;
+    out->cache_slot = tab->cache_slot;
+    out->cache_rows = tab->cache_rows;
+    out->cache_scale = tab->cache_scale;
+    out->n_tables = tab->n_tables;
+    out->dim = tab->dim;
+    out->dtype = tab->dtype;
+  }
+  return ENGRAM_OK;
+}
+
+engram_status check_gc(const engram_gate_conv_params* p, engram::GateConvArgs* out) {
+  if (p == nullptr) return fail(ENGRAM_EINVAL, "gate/conv params are NULL");
+  if (p->d < 64 || p->d % 64 != 0)
+    return fail(ENGRAM_EUNSUPPORTED, "gate/conv: d=%d must be a positive multiple of 64", p->d);
+  if (p->branches < 1) return fail(ENGRAM_EINVAL, "gate/conv: branches must be >= 1");
+  if (p->kernel_w < 2 || p->kernel_w > ENGRAM_MAX_KERNEL_W)
+    return fail(ENGRAM_EUNSUPPORTED, "gate/conv: kernel_w=%d outside [2, %d]", p->kernel_w, ENGRAM_MAX_KERNEL_W);
+  if (p->dilation < 1 || (p->kernel_w - 1) * p->dilation > ENGRAM_MAX_CONV_SPAN)
+    return fail(ENGRAM_EUNSUPPORTED, "gate/conv: (kernel_w-1)*dilation must lie in [1, %d]", ENGRAM_MAX_CONV_SPAN);
+  if (!(p->eps >= 0.0f)) return fail(ENGRAM_EINVAL, "gate/conv: eps must be >= 0");
+  if (p->hdtype != ENGRAM_F32 && p->hdtype != ENGRAM_BF16)
+    return fail(ENGRAM_EUNSUPPORTED, "gate/conv: hdtype must be F32 or BF16");
+  if (p->conv_w == nullptr) return fail(ENGRAM_EINVAL, "gate/conv: conv_w is NULL");
+  if (out != nullptr) {
+    out->d = p->d;
+    out->branches = p->branches;
+    out->kernel_w = p->kernel_w;
+    out->dilation = p->dilation;
+    out->eps = p->eps;
+    out->hdtype = p->hdtype;
+    out->conv_w = p->conv_w;
+  }
+  return ENGRAM_OK;
+}
+
+engram_status check_state(const engram_decode_state* st, bool need_ids) {
+  if (st == nullptr) return ENGRAM_OK;
+  if (st->conv == nullptr || st->pos == nullptr || (need_ids && st->ids == nullptr))
+    return fail(ENGRAM_EINVAL, "decode state: ids, conv and pos must be non-NULL");
+  if (!aligned(st->conv, 16)) return fail(ENGRAM_EINVAL, "decode state: conv must be 16-byte aligned");
+  return ENGRAM_OK;
+}
+
+struct GcWorkspace {
+  float* alpha;
+  float* gamma;
+};
+
+size_t gc_ws_bytes(int64_t n_tok, int M) { return 2 * align_up(static_cast<size_t>(n_tok) * M * sizeof(float)); }
+
+GcWorkspace carve_gc(char* ws, int64_t n_tok, int M) {
+  const size_t a = align_up(static_cast<size_t>(n_tok) * M * sizeof(float));
+  return GcWorkspace{reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + a)};
+}
+
+// Steps 6-8 after the projections are in kv.
+engram_status run_gate_conv(void* H, const void* kv, int64_t B, int64_t T, const engram::GateConvArgs& g,
+                            engram_decode_state* st, const int32_t* tokens, const int32_t* proj,
+                            int32_t max_n, float* alpha_out, float* y_out, char* ws, hipStream_t s) {
+  const int64_t n_tok = B * T;
+  GcWorkspace w = carve_gc(ws, n_tok, g.branches);
+  float* alpha = alpha_out != nullptr ? alpha_out : w.alpha;
+  engram_status r = hip_status(engram::launch_gate(H, kv, n_tok, g, alpha, w.gamma, s), "gate launch");
+  if (r != ENGRAM_OK) return r;
+  engram::StateArgs sa{};
+  if (st != nullptr) sa = engram::StateArgs{st->ids, st->conv, st->pos};
+  r = hip_status(engram::launch_conv(H, kv, B, T, g, alpha, w.gamma, st != nullptr ? &sa : nullptr, y_out, s),
+                 "conv launch");
+  if (r != ENGRAM_OK) return r;
+  if (st != nullptr) {
+    if (tokens == nullptr) sa.ids = nullptr;
+    r = hip_status(engram::launch_state_commit(kv, B, T, g, w.gamma, sa, tokens, proj, max_n, s),
+                   "state commit launch");
+  }
+  return r;
+}
+
+struct ForwardWorkspace {
+  int32_t* z;
+  void* e;
+  void* kv;
+  char* gc;
+};
+
+size_t forward_ws_bytes(int64_t n_tok, const engram_layer* L) {
+  const int nt = L->tables.n_tables;
+  const int64_t d_mem = static_cast<int64_t>(nt) * L->tables.dim;
+  const size_t es = dtype_size(L->gc.hdtype);
+  const int64_t n_out = static_cast<int64_t>(1 + L->gc.branches) * L->gc.d;
+  return align_up(static_cast<size_t>(n_tok) * nt * sizeof(int32_t)) +
+         align_up(static_cast<size_t>(n_tok) * d_mem * es) +
+         align_up(static_cast<size_t>(n_tok) * n_out * es) + gc_ws_bytes(n_tok, L->gc.branches);
+}
+
+ForwardWorkspace carve_forward(char* ws, int64_t n_tok, const engram_layer* L) {
+  const int nt = L->tables.n_tables;
+  const int64_t d_mem = static_cast<int64_t>(nt) * L->tables.dim;
+  const size_t es = dtype_size(L->gc.hdtype);
+  ForwardWorkspace f;
+  f.z = reinterpret_cast<int32_t*>(ws);
+  ws += align_up(static_cast<size_t>(n_tok) * nt * sizeof(int32_t));
+  f.e = ws;
+  ws += align_up(static_cast<size_t>(n_tok) * d_mem * es);
+  f.kv = ws;
+  ws += align_up(static_cast<size_t>(n_tok) * (1 + L->gc.branches) * L->gc.d * es);
+  f.gc = ws;
+  return f;
+}
+
+engram_status check_layer(const engram_layer* L, engram::HashArgs* ha, engram::TableArgs* ta,
+                          engram::GateConvArgs* ga) {
+  if (L == nullptr) return fail(ENGRAM_EINVAL, "layer is NULL");
+  engram_status r = check_hash(&L->hash, ha);
+  if (r != ENGRAM_OK) return r;
+  r = check_tables(&L->tables, ta);
+  if (r != ENGRAM_OK) return r;
+  r = check_gc(&L->gc, ga);
+  if (r != ENGRAM_OK) return r;
+  const int nt = (L->hash.max_n - 1) * L->hash.heads;
+  if (L->tables.n_tables != nt)
+    return fail(ENGRAM_EINVAL, "layer: tables.n_tables=%d but the hash has (N-1)*K=%d tables",
+                L->tables.n_tables, nt);
+  for (int j = 0; j < nt; ++j)
+    if (L->tables.n_rows[j] != static_cast<int64_t>(L->hash.prime[j]))
+      return fail(ENGRAM_EINVAL, "layer: table %d has %lld rows but prime %u", j,
+                  static_cast<long long>(L->tables.n_rows[j]), L->hash.prime[j]);
+  if (L->w == nullptr) return fail(ENGRAM_EINVAL, "layer: w is NULL");
+  const int64_t d_mem = static_cast<int64_t>(nt) * L->tables.dim;
+  if (L->gc.hdtype == ENGRAM_BF16 && d_mem % 64 != 0)
+    return fail(ENGRAM_EUNSUPPORTED, "layer: bf16 projections need n_tables*dim (%lld) to be a multiple of 64",
+                static_cast<long long>(d_mem));
+  if (!aligned(L->w, 16)) return fail(ENGRAM_EINVAL, "layer: w must be 16-byte aligned");
+  return ENGRAM_OK;
+}
+
+}  // namespace
+
+ENGRAM_API int32_t engram_abi_version(void) { return ENGRAM_ABI_VERSION; }
+
+ENGRAM_API const char* engram_last_error(void) { return g_last_error.c_str(); }
+
+ENGRAM_API engram_status engram_hash_indices(const int32_t* tokens, int64_t B, int64_t T,
+                                             const int32_t* hist, const engram_hash_params* hp,
+                                             int32_t* z, hipStream_t stream) {
+  engram::HashArgs ha;
+  engram_status r = check_hash(hp, &ha);
+  if (r != ENGRAM_OK) return r;
+  if (B < 0 || T < 0) return fail(ENGRAM_EINVAL, "hash: B and T must be >= 0");
+  if (B * T == 0) return ENGRAM_OK;
+  if (tokens == nullptr || z == nullptr) return fail(ENGRAM_EINVAL, "hash: tokens and z must be non-NULL");
+  return hip_status(engram::launch_hash(tokens, B, T, hist, hp->proj, ha, z, stream), "hash launch");
+}
+
+ENGRAM_API engram_status engram_gather(const int32_t* z, int64_t n_tok, const engram_tables* tab,
+                                       engram_dtype out_dtype, void* e, hipStream_t stream) {
+  engram::TableArgs ta;
+  engram_status r = check_tables(tab, &ta);
+  if (r != ENGRAM_OK) return r;
+  if (out_dtype != ENGRAM_F32 && out_dtype != ENGRAM_BF16)
+    return fail(ENGRAM_EUNSUPPORTED, "gather: out_dtype must be F32 or BF16");
+  if (n_tok < 0) return fail(ENGRAM_EINVAL, "gather: n_tok must be >= 0");
+  if (n_tok == 0) return ENGRAM_OK;
+  if (z == nullptr || e == nullptr) return fail(ENGRAM_EINVAL, "gather: z and e must be non-NULL");
+  if (!aligned(e, 16)) return fail(ENGRAM_EINVAL, "gather: e must be 16-byte aligned");
+  return hip_status(engram::launch_gather(z, n_tok, ta, out_dtype, e, stream), "gather launch");
+}
+
+ENGRAM_API engram_status engram_project_kv(const void* e, const void* w, int64_t n_tok, int64_t d_mem,
+                                           int64_t n_out, engram_dtype dtype, void* kv,
+                                           hipStream_t stream) {
+  if (dtype != ENGRAM_F32 && dtype != ENGRAM_BF16)
+    return fail(ENGRAM_EUNSUPPORTED, "project_kv: dtype must be F32 or BF16");
+  if (n_tok < 0 || d_mem < 1 || n_out < 1)
+    return fail(ENGRAM_EINVAL, "project_kv: need n_tok >= 0, d_mem >= 1, n_out >= 1");
+  if (d_mem > 0x7fffffff || n_out > 0x7fffffff) return fail(ENGRAM_EUNSUPPORTED, "project_kv: dims too large");
+  if (dtype == ENGRAM_BF16 && (d_mem % 64 != 0 || n_out % 64 != 0))
+    return fail(ENGRAM_EUNSUPPORTED, "project_kv: bf16 needs d_mem and n_out to be multiples of 64");
+  if (n_tok == 0) return ENGRAM_OK;
+  if (e == nullptr || w == nullptr || kv == nullptr)
+    return fail(ENGRAM_EINVAL, "project_kv: e, w and kv must be non-NULL");
+  if (!aligned(e, 16) || !aligned(w, 16)) return fail(ENGRAM_EINVAL, "project_kv: e and w must be 16-byte aligned");
+  return hip_status(engram::launch_project_kv(e, w, n_tok, d_mem, n_out, dtype, kv, stream), "project_kv launch");
+}
+
+ENGRAM_API size_t engram_gate_conv_workspace(int64_t B, int64_t T, const engram_gate_conv_params* p) {
+  if (p == nullptr || B < 0 || T < 0 || p->branches < 1) return 0;
+  return gc_ws_bytes(B * T, p->branches);
+}
+
+ENGRAM_API engram_status engram_gate_conv_forward(void* H, const void* kv, int64_t B, int64_t T,
+                                                  const engram_gate_conv_params* p,
+                                                  engram_decode_state* st, float* alpha_out,
+                                                  float* y_out, void* ws, size_t ws_bytes,
+                                                  hipStream_t stream) {
+  engram::GateConvArgs g;
+  engram_status r = check_gc(p, &g);
+  if (r != ENGRAM_OK) return r;
+  if ((r = check_state(st, false)) != ENGRAM_OK) return r;
+  if (B < 0 || T < 0) return fail(ENGRAM_EINVAL, "gate_conv: B and T must be >= 0");
+  if (B * T == 0) return ENGRAM_OK;
+  if (H == nullptr || kv == nullptr) return fail(ENGRAM_EINVAL, "gate_conv: H and kv must be non-NULL");
+  if (!aligned(H, 16) || !aligned(kv, 16)) return fail(ENGRAM_EINVAL, "gate_conv: H and kv must be 16-byte aligned");
+  if (y_out != nullptr && !aligned(y_out, 16)) return fail(ENGRAM_EINVAL, "gate_conv: y_out must be 16-byte aligned");
+  const size_t need = gc_ws_bytes(B * T, p->branches);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(ENGRAM_EINVAL, "gate_conv: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  return run_gate_conv(H, kv, B, T, g, st, nullptr, nullptr, 0, alpha_out, y_out, static_cast<char*>(ws), stream);
+}
+
+ENGRAM_API size_t engram_forward_workspace(int64_t B, int64_t T, const engram_layer* L) {
+  if (L == nullptr || B < 0 || T < 0 || L->gc.branches < 1 || L->tables.n_tables < 1) return 0;
+  return forward_ws_bytes(B * T, L);
+}
+
+ENGRAM_API engram_status engram_forward(const int32_t* tokens, void* H, int64_t B, int64_t T,
+                                        const engram_layer* L, engram_decode_state* st,
+                                        float* alpha_out, float* y_out, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  engram::HashArgs ha;
+  engram::TableArgs ta;
+  engram::GateConvArgs g;
+  engram_status r = check_layer(L, &ha, &ta, &g);
+  if (r != ENGRAM_OK) return r;
+  if ((r = check_state(st, true)) != ENGRAM_OK) return r;
+  if (B < 0 || T < 0) return fail(ENGRAM_EINVAL, "forward: B and T must be >= 0");
+  const int64_t n_tok = B * T;
+  if (n_tok == 0) return ENGRAM_OK;
+  if (tokens == nullptr || H == nullptr) return fail(ENGRAM_EINVAL, "forward: tokens and H must be non-NULL");
+  if (!aligned(H, 16)) return fail(ENGRAM_EINVAL, "forward: H must be 16-byte aligned");
+  if (y_out != nullptr && !aligned(y_out, 16)) return fail(ENGRAM_EINVAL, "forward: y_out must be 16-byte aligned");
+  const size_t need = forward_ws_bytes(n_tok, L);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(ENGRAM_EINVAL, "forward: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+
+  ForwardWorkspace f = carve_forward(static_cast<char*>(ws), n_tok, L);
+  const int64_t d_mem = static_cast<int64_t>(L->tables.n_tables) * L->tables.dim;
+  const int64_t n_out = static_cast<int64_t>(1 + g.branches) * g.d;
+  r = hip_status(engram::launch_hash(tokens, B, T, st != nullptr ? st->ids : nullptr, L->hash.proj, ha, f.z, stream),
+                 "hash launch");
+  if (r != ENGRAM_OK) return r;
+  r = hip_status(engram::launch_gather(f.z, n_tok, ta, g.hdtype, f.e, stream), "gather launch");
+  if (r != ENGRAM_OK) return r;
+  r = hip_status(engram::launch_project_kv(f.e, L->w, n_tok, d_mem, n_out, g.hdtype, f.kv, stream),
+                 "project_kv launch");
+  if (r != ENGRAM_OK) return r;
+  return run_gate_conv(H, f.kv, B, T, g, st, tokens, L->hash.proj, L->hash.max_n, alpha_out, y_out, f.gc, stream);
+}
+
+ENGRAM_API engram_status engram_host_alloc(size_t bytes, void** host_ptr, void** device_alias) {
+  if (host_ptr == nullptr || device_alias == nullptr || bytes == 0)
+    return fail(ENGRAM_EINVAL, "host_alloc: need bytes > 0 and non-NULL out pointers");
+  *host_ptr = nullptr;
+  *device_alias = nullptr;
+  void* h = nullptr;
+  hipError_t e = hipHostMalloc(&h, bytes, hipHostMallocMapped | hipHostMallocPortable);
+  if (e != hipSuccess) return hip_status(e, "hipHostMalloc");
+  void* dptr = nullptr;
+  e = hipHostGetDevicePointer(&dptr, h, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(h);
+    return hip_status(e, "hipHostGetDevicePointer");
+  }
+  *host_ptr = h;
+  *device_alias = dptr;
+  return ENGRAM_OK;
+}
+
+ENGRAM_API engram_status engram_host_free(void* host_ptr) {
+  if (host_ptr == nullptr) return ENGRAM_OK;
+  return hip_status(hipHostFree(host_ptr), "hipHostFree");
+}

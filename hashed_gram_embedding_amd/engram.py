@@ -1,0 +1,308 @@
+"""ctypes binding of libengram.so (C ABI in include/engram.h).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the layer runs in the library's kernels.
+There is no fallback: if the library is missing or a call fails, an error is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libengram.so")
+
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
+F32, BF16, I8 = 0, 1, 2
+MAX_TABLES, MAX_ORDER = 32, 4
+
+_DT = {"f32": F32, "bf16": BF16, "i8": I8}
+_TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
+
+c_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class HashParams(ctypes.Structure):
+    _fields_ = [("proj", ctypes.c_void_p), ("vocab", ctypes.c_int64), ("max_n", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("mult", ctypes.c_void_p), ("prime", ctypes.c_void_p)]
+
+
+class Tables(ctypes.Structure):
+    _fields_ = [("n_tables", ctypes.c_int32), ("dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("rows", ctypes.c_void_p), ("row_offset", ctypes.c_void_p), ("n_rows", ctypes.c_void_p),
+                ("total_rows", ctypes.c_int64), ("row_scale", ctypes.c_void_p),
+                ("cache_slot", ctypes.c_void_p), ("cache_rows", ctypes.c_void_p),
+                ("cache_scale", ctypes.c_void_p), ("cache_n", ctypes.c_int64)]
+
+
+class GateConvParams(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("branches", ctypes.c_int32), ("kernel_w", ctypes.c_int32),
+                ("dilation", ctypes.c_int32), ("eps", ctypes.c_float), ("hdtype", ctypes.c_int32),
+                ("conv_w", ctypes.c_void_p)]
+
+
+class LayerStruct(ctypes.Structure):
+    _fields_ = [("hash", HashParams), ("tables", Tables), ("w", ctypes.c_void_p), ("gc", GateConvParams)]
+
+
+class DecodeStateStruct(ctypes.Structure):
+    _fields_ = [("ids", ctypes.c_void_p), ("conv", ctypes.c_void_p), ("pos", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+class EngramError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"engram status {status}: {msg}")
+        self.status = status
+
+
+def lib():
+    """Load libengram.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m hashed_gram_embedding_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "engram_abi_version": (i32, []),
+        "engram_last_error": (ctypes.c_char_p, []),
+        "engram_hash_indices": (i32, [vp, i64, i64, vp, ctypes.POINTER(HashParams), vp, vp]),
+        "engram_gather": (i32, [vp, i64, ctypes.POINTER(Tables), i32, vp, vp]),
+        "engram_project_kv": (i32, [vp, vp, i64, i64, i64, i32, vp, vp]),
+        "engram_gate_conv_workspace": (sz, [i64, i64, ctypes.POINTER(GateConvParams)]),
+        "engram_gate_conv_forward": (i32, [vp, vp, i64, i64, ctypes.POINTER(GateConvParams),
+                                           ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
+        "engram_forward_workspace": (sz, [i64, i64, ctypes.POINTER(LayerStruct)]),
+        "engram_forward": (i32, [vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
+                                 ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
+        "engram_host_alloc": (i32, [sz, ctypes.POINTER(vp), ctypes.POINTER(vp)]),
+        "engram_host_free": (i32, [vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def exported_names():
+    return ["engram_abi_version", "engram_last_error", "engram_hash_indices", "engram_gather",
+            "engram_project_kv", "engram_gate_conv_workspace", "engram_gate_conv_forward",
+            "engram_forward_workspace", "engram_forward", "engram_host_alloc", "engram_host_free"]
+
+
+def last_error() -> str:
+    return lib().engram_last_error().decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise EngramError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def to_device(a: np.ndarray, kind: str, device) -> torch.Tensor:
+    """numpy array -> device tensor; kind "bf16" reinterprets uint16 bits."""
+    if kind == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """bfloat16 device tensor -> numpy uint16 bit patterns."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# device-side layer description
+# --------------------------------------------------------------------------
+
+class HashSpec:
+    """Device copy of P plus the host arrays of the hash parameters."""
+
+    def __init__(self, hp, device="cuda"):
+        self.hp = hp
+        self.proj = to_device(np.asarray(hp.proj, dtype=np.int32), "i32", device)
+        self.mult = np.ascontiguousarray(hp.mult, dtype=np.uint64)
+        self.prime = np.ascontiguousarray(hp.prime, dtype=np.uint32)
+        self.n_tables = (hp.max_n - 1) * hp.heads
+        self.s = HashParams(self.proj.data_ptr(), hp.vocab, hp.max_n, hp.heads,
+                            self.mult.ctypes.data, self.prime.ctypes.data)
+
+
+class Layer:
+    """Device copies of one layer's parameters plus the ctypes descriptor.
+
+    Tables live in HBM unless `host_rows` is given: then `rows` must already
+    be the device alias of pinned host memory from HostBuffer."""
+
+    def __init__(self, li, hdtype: str, device="cuda", rows_device: Optional[torch.Tensor] = None,
+                 rows_ptr: Optional[int] = None, scale_ptr: Optional[int] = None):
+        hp, tab = li.hash, li.tables
+        self.li = li
+        self.hdtype = _DT[hdtype]
+        self.hs = HashSpec(hp, device)
+        self.row_offset = np.ascontiguousarray(tab.row_offset, dtype=np.int64)
+        self.n_rows = np.ascontiguousarray(tab.n_rows, dtype=np.int64)
+        self.table_dtype = _DT[tab.dtype]
+        if rows_ptr is None:
+            self.rows = rows_device if rows_device is not None else to_device(tab.rows, tab.dtype, device)
+            rows_ptr = self.rows.data_ptr()
+            self.scale = None
+            if tab.dtype == "i8":
+                self.scale = to_device(tab.scale.astype(np.float32), "f32", device)
+                scale_ptr = self.scale.data_ptr()
+        self.w = to_device(li.w, "bf16" if hdtype == "bf16" else "f32", device)
+        self.conv_w = to_device(li.conv_w.astype(np.float32), "f32", device)
+        self.cache_slot = self.cache_rows = self.cache_scale = None
+        self.cache_n = 0
+        self.s = LayerStruct()
+        self.s.hash = self.hs.s
+        self.s.tables = Tables(tab.n_rows.shape[0], tab.dim, self.table_dtype, rows_ptr,
+                               self.row_offset.ctypes.data, self.n_rows.ctypes.data, tab.total_rows,
+                               scale_ptr, None, None, None, 0)
+        self.s.w = self.w.data_ptr()
+        self.s.gc = GateConvParams(li.d, li.branches, li.kernel_w, li.dilation, li.eps, self.hdtype,
+                                   self.conv_w.data_ptr())
+
+    def set_cache(self, slot: Optional[torch.Tensor], rows: Optional[torch.Tensor],
+                  scale: Optional[torch.Tensor] = None):
+        self.cache_slot, self.cache_rows, self.cache_scale = slot, rows, scale
+        t = self.s.tables
+        t.cache_slot = None if slot is None else slot.data_ptr()
+        t.cache_rows = None if rows is None else rows.data_ptr()
+        t.cache_scale = None if scale is None else scale.data_ptr()
+        self.cache_n = 0 if rows is None else rows.shape[0]
+        t.cache_n = self.cache_n
+
+    @property
+    def M(self):
+        return self.li.branches
+
+    @property
+    def d(self):
+        return self.li.d
+
+
+class DecodeState:
+    """Zero-initialised decode state for S sequences (see engram_decode_state)."""
+
+    def __init__(self, S: int, max_n: int, branches: int, span: int, d: int, device="cuda"):
+        self.ids = torch.zeros((S, max_n - 1), dtype=torch.int32, device=device)
+        self.conv = torch.zeros((S, branches, span, d), dtype=torch.float32, device=device)
+        self.pos = torch.zeros(S, dtype=torch.int32, device=device)
+        self.s = DecodeStateStruct(self.ids.data_ptr(), self.conv.data_ptr(), self.pos.data_ptr())
+
+
+class HostBuffer:
+    """Pinned, mapped host memory readable by kernels (engram_host_alloc)."""
+
+    def __init__(self, nbytes: int):
+        h, d = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(lib().engram_host_alloc(nbytes, ctypes.byref(h), ctypes.byref(d)))
+        self.host, self.dev, self.nbytes = h.value, d.value, nbytes
+
+    def numpy(self, dtype, shape):
+        buf = (ctypes.c_char * self.nbytes).from_address(self.host)
+        return np.frombuffer(buf, dtype=dtype, count=int(np.prod(shape))).reshape(shape)
+
+    def free(self):
+        if self.host:
+            _check(lib().engram_host_free(ctypes.c_void_p(self.host)))
+            self.host = self.dev = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+# --------------------------------------------------------------------------
+# entry points (same names as the C ABI, minus the prefix)
+# --------------------------------------------------------------------------
+
+def hash_indices(tokens: torch.Tensor, spec, hist: Optional[torch.Tensor] = None,
+                 z: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """spec: a HashSpec or a Layer."""
+    hs = spec.hs if isinstance(spec, Layer) else spec
+    B, T = tokens.shape
+    if z is None:
+        z = torch.empty((B, T, hs.n_tables), dtype=torch.int32, device=tokens.device)
+    _check(lib().engram_hash_indices(_ptr(tokens), B, T, _ptr(hist), ctypes.byref(hs.s),
+                                     _ptr(z), _stream(stream)))
+    return z
+
+
+def gather(z: torch.Tensor, layer: Layer, out_dtype: str = "bf16", e: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    nt, dim = layer.s.tables.n_tables, layer.s.tables.dim
+    n_tok = z.numel() // nt
+    if e is None:
+        e = torch.empty((*z.shape[:-1], nt * dim), dtype=_TORCH_DT[_DT[out_dtype]], device=z.device)
+    _check(lib().engram_gather(_ptr(z), n_tok, ctypes.byref(layer.s.tables), _DT[out_dtype], _ptr(e),
+                               _stream(stream)))
+    return e
+
+
+def project_kv(e: torch.Tensor, w: torch.Tensor, kv: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    d_mem = e.shape[-1]
+    n_tok = e.numel() // d_mem
+    n_out = w.shape[0]
+    dt = BF16 if e.dtype == torch.bfloat16 else F32
+    if kv is None:
+        kv = torch.empty((*e.shape[:-1], n_out), dtype=e.dtype, device=e.device)
+    _check(lib().engram_project_kv(_ptr(e), _ptr(w), n_tok, d_mem, n_out, dt, _ptr(kv), _stream(stream)))
+    return kv
+
+
+def gate_conv_forward(H: torch.Tensor, kv: torch.Tensor, layer: Layer, state: Optional[DecodeState] = None,
+                      want_alpha: bool = False, want_y: bool = False, stream=None):
+    B, T = H.shape[0], H.shape[1]
+    M, d = layer.M, layer.d
+    alpha = torch.empty((B, T, M), dtype=torch.float32, device=H.device) if want_alpha else None
+    y = torch.empty((B, T, M, d), dtype=torch.float32, device=H.device) if want_y else None
+    nbytes = lib().engram_gate_conv_workspace(B, T, ctypes.byref(layer.s.gc))
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=H.device)
+    st = ctypes.byref(state.s) if state is not None else None
+    _check(lib().engram_gate_conv_forward(_ptr(H), _ptr(kv), B, T, ctypes.byref(layer.s.gc), st,
+                                          _ptr(alpha), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    return alpha, y
+
+
+def forward_workspace(B: int, T: int, layer: Layer) -> int:
+    return int(lib().engram_forward_workspace(B, T, ctypes.byref(layer.s)))
+
+
+def forward(tokens: torch.Tensor, H: torch.Tensor, layer: Layer, state: Optional[DecodeState] = None,
+            want_alpha: bool = False, want_y: bool = False, ws: Optional[torch.Tensor] = None, stream=None):
+    """One Engram layer; H is updated in place.  Returns (alpha, y) when asked."""
+    B, T = tokens.shape
+    M, d = layer.M, layer.d
+    alpha = torch.empty((B, T, M), dtype=torch.float32, device=H.device) if want_alpha else None
+    y = torch.empty((B, T, M, d), dtype=torch.float32, device=H.device) if want_y else None
+    if ws is None:
+        ws = torch.empty(max(forward_workspace(B, T, layer), 256), dtype=torch.uint8, device=H.device)
+    st = ctypes.byref(state.s) if state is not None else None
+    _check(lib().engram_forward(_ptr(tokens), _ptr(H), B, T, ctypes.byref(layer.s), st, _ptr(alpha), _ptr(y),
+                                _ptr(ws), ws.numel(), _stream(stream)))
+    return alpha, y

@@ -1,0 +1,213 @@
+/*
+ * engram.h -- C ABI of libengram.so: the Engram conditional-memory layer
+ * (hashed n-gram embeddings) on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "DeepSeek Engram series guide" (foosynaptic
+ * deepseek-tech-notes), section "Engram working principle", Steps 1-8, and
+ * its multi-branch variant.  Per token position t:
+ *   x'_t = P(x_t)                                     (Step 1)
+ *   g_{t,n} = (x'_{t-n+1}, ..., x'_t), n = 2..N       (Step 2)
+ *   z_{t,n,k} = (XOR_i x'_{t-i} m_{n,k,i} mod 2^64) mod p_{n,k}   (Step 3)
+ *   e_t = concat_{n outer, k inner} E_{n,k}[z_{t,n,k}]            (Step 4)
+ *   v_t = W_V e_t, k_t^(m) = W_K^(m) e_t              (Step 5, variant)
+ *   alpha_t^(m) = sigmoid(RMSNorm(h_t^(m)) . RMSNorm(k_t^(m)) / sqrt(d))  (Step 6)
+ *   Y^(m) = SiLU(Conv1D(RMSNorm(alpha^(m) V))) + alpha^(m) V   (Step 7)
+ *   H^(m) <- H^(m) + Y^(m)                            (Step 8)
+ * The pages leave the hash function open; this library fixes the
+ * multiplicative-XOR form above, with ids before the sequence start read as
+ * 0 (or from the decode history).
+ *
+ * Conventions shared by every call:
+ *  - "device" pointers are HIP device memory (or, where stated, the device
+ *    alias of mapped pinned host memory); "host" pointers are read on the
+ *    host during the call only.  The caller owns every buffer; the library
+ *    keeps no pointer after a call returns and allocates no device memory
+ *    (scratch comes in through `ws`).
+ *  - Every compute call is asynchronous on `stream` (0 = the null stream)
+ *    and never synchronises.  Calls are reentrant; calls that write the same
+ *    buffers must be ordered by the caller.
+ *  - All argument checks that need only host-visible values run before any
+ *    launch; on failure nothing is launched and a message is kept for
+ *    engram_last_error() (per calling thread).  Device-resident values are
+ *    the caller's contract: 0 <= token < vocab, 0 <= z < n_rows[j],
+ *    cache slots < cache_n.
+ *  - Status codes: ENGRAM_OK, ENGRAM_EINVAL (null or misaligned pointer, bad
+ *    size, inconsistent descriptors, workspace too small),
+ *    ENGRAM_EUNSUPPORTED (dtype combination or shape outside the supported
+ *    set), ENGRAM_EHIP (a HIP runtime or launch error; its text is in
+ *    engram_last_error()).
+ *  - bf16 is IEEE bfloat16; every rounding to it is to nearest, ties to even.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ENGRAM_ABI_VERSION 1
+#define ENGRAM_MAX_TABLES 32 /* (N-1)*K */
+#define ENGRAM_MAX_ORDER 4   /* N */
+#define ENGRAM_MAX_KERNEL_W 8
+#define ENGRAM_MAX_CONV_SPAN 32 /* (kernel_w - 1) * dilation */
+
+typedef enum engram_status {
+  ENGRAM_OK = 0,
+  ENGRAM_EINVAL = -1,
+  ENGRAM_EUNSUPPORTED = -2,
+  ENGRAM_EHIP = -3
+} engram_status;
+
+typedef enum engram_dtype {
+  ENGRAM_F32 = 0,
+  ENGRAM_BF16 = 1,
+  ENGRAM_I8 = 2 /* table rows only: int8 with one float32 scale per row */
+} engram_dtype;
+
+/* Steps 1-3: vocabulary projection and the multi-head hash. */
+typedef struct engram_hash_params {
+  const int32_t* proj;    /* device [vocab]: P, raw id -> compressed id        */
+  int64_t vocab;          /* raw vocabulary size                               */
+  int32_t max_n;          /* N: n-gram orders 2..N, 2 <= N <= ENGRAM_MAX_ORDER */
+  int32_t heads;          /* K heads per order, (N-1)*K <= ENGRAM_MAX_TABLES   */
+  const uint64_t* mult;   /* host [N-1][K][N]: m_{n,k,i} at [n-2][k][i]; i = 0
+                             multiplies the current token; entries i >= n are
+                             unused                                            */
+  const uint32_t* prime;  /* host [(N-1)*K]: table size p_{n,k} of table
+                             j = (n-2)*K + k, 2 <= p < 2^31                     */
+} engram_hash_params;
+
+/* Steps 3-4: the prime-sized tables E_j, j = (n-2)*K + k, stored back to back
+ * in one row array.  Low-precision storage with dequantisation inside the
+ * gather follows the mixed-precision direction of "Engram module: ..."
+ * (section 8) and the single select-and-dequantise kernel that reads either
+ * HBM or pinned host memory ("Engram embedding expansion: co-design for
+ * DRAM/SSD offload", section on DRAM offload). */
+typedef struct engram_tables {
+  int32_t n_tables;          /* = (N-1)*K                                        */
+  int32_t dim;               /* columns per row (d_head), a multiple of 8        */
+  engram_dtype dtype;        /* ENGRAM_F32, ENGRAM_BF16 or ENGRAM_I8             */
+  const void* rows;          /* [total_rows][dim], 16-byte aligned: device memory
+                                or the device alias of mapped pinned host memory
+                                (engram_host_alloc)                              */
+  const int64_t* row_offset; /* host [n_tables]: first row of table j in `rows`  */
+  const int64_t* n_rows;     /* host [n_tables]: rows of table j; must equal p_j */
+  int64_t total_rows;        /* rows in `rows`; every table must fit inside      */
+  const float* row_scale;    /* [total_rows], same memory kind as rows; I8 only  */
+  /* optional hot cache in HBM, checked first (NULL cache_slot = none): */
+  const int32_t* cache_slot; /* device [total_rows]: cache slot of a row, or -1  */
+  const void* cache_rows;    /* device [cache_n][dim], same dtype as rows        */
+  const float* cache_scale;  /* device [cache_n]; I8 only                        */
+  int64_t cache_n;           /* slots in the cache                               */
+} engram_tables;
+
+/* Steps 6-8: gate, short conv and residual. */
+typedef struct engram_gate_conv_params {
+  int32_t d;              /* hidden width per branch, a multiple of 64             */
+  int32_t branches;       /* M >= 1 residual branches                              */
+  int32_t kernel_w;       /* conv taps w, 1..ENGRAM_MAX_KERNEL_W (pages: 4)         */
+  int32_t dilation;       /* conv dilation (pages: N); (w-1)*dilation <= 32         */
+  float eps;              /* RMSNorm epsilon                                       */
+  engram_dtype hdtype;    /* ENGRAM_F32 or ENGRAM_BF16: storage type of H, kv, the
+                             projection weights and the gathered rows              */
+  const float* conv_w;    /* device [M][d][kernel_w]; tap kernel_w-1 multiplies the
+                             current position, tap j the position
+                             (kernel_w-1-j)*dilation steps back                     */
+} engram_gate_conv_params;
+
+/* One Engram layer. */
+typedef struct engram_layer {
+  engram_hash_params hash;
+  engram_tables tables;
+  const void* w;          /* device [(1+M)*d][n_tables*dim], hdtype, row-major:
+                             rows 0..d-1 are W_V, rows (1+m)*d .. (2+m)*d-1 are
+                             W_K^(m) (Step 5; the multi-branch variant fuses the
+                             shared W_V with the M keys into one product)          */
+  engram_gate_conv_params gc;
+} engram_layer;
+
+/* Decode / chunked-prefill state of S sequences (not on the pages; it is
+ * what the causal n-gram window and conv need to continue a sequence). */
+typedef struct engram_decode_state {
+  int32_t* ids;   /* device [S][N-1]: compressed ids of the last N-1 tokens,
+                     oldest first (0 = pad before the start)                   */
+  float* conv;    /* device [S][M][span][d], span = (kernel_w-1)*dilation: the
+                     conv inputs u = RMSNorm(alpha v) of the last span
+                     positions; absolute position p lives in slot p % span;
+                     zero-initialised for a new sequence                       */
+  int32_t* pos;   /* device [S]: tokens consumed so far                        */
+} engram_decode_state;
+
+/* Library identity and per-thread error text. */
+int32_t engram_abi_version(void);
+const char* engram_last_error(void);
+
+/* Steps 1-3.  tokens: device int32 [B][T] raw ids.  hist: device int32
+ * [B][N-1] compressed ids preceding t = 0 (oldest first) or NULL for pad 0.
+ * z: device int32 [B][T][(N-1)*K], z[b][t][j] = local row in table j.
+ * B*T = 0 is a no-op. */
+engram_status engram_hash_indices(const int32_t* tokens, int64_t B, int64_t T,
+                                  const int32_t* hist, const engram_hash_params* hp,
+                                  int32_t* z, hipStream_t stream);
+
+/* Steps 3-4.  z: device int32 [n_tok][n_tables].  e: device
+ * [n_tok][n_tables*dim] of out_dtype (F32 or BF16).  Rows are copied exactly
+ * (f32 -> bf16 rounds to nearest even); I8 rows become
+ * float32(q) * float32(scale), then rounded when out_dtype is BF16.  With a
+ * cache, a row whose cache_slot is >= 0 is read from cache_rows, otherwise
+ * from rows; the result is identical either way. */
+engram_status engram_gather(const int32_t* z, int64_t n_tok, const engram_tables* tab,
+                            engram_dtype out_dtype, void* e, hipStream_t stream);
+
+/* Step 5.  kv[t][o] = sum_c e[t][c] * w[o][c] with float32 accumulation.
+ * e: device [n_tok][d_mem], w: device [n_out][d_mem], kv: device
+ * [n_tok][n_out], all of `dtype` (F32, or BF16 with d_mem and n_out
+ * multiples of 64). */
+engram_status engram_project_kv(const void* e, const void* w, int64_t n_tok, int64_t d_mem,
+                                int64_t n_out, engram_dtype dtype, void* kv,
+                                hipStream_t stream);
+
+/* Steps 6-8 on precomputed projections.  H: device [B][T][M][d] (hdtype),
+ * read as h and overwritten with h + Y.  kv: device [B][T][(1+M)*d]
+ * (hdtype): v, then k^(0..M-1).  st: NULL for independent sequences starting
+ * at t = 0; otherwise B = S sequences continuing from st, which is advanced
+ * by T tokens (its ids are left for engram_forward to update: here no tokens
+ * are seen, so st->ids and st->pos are read-only).  alpha_out: device float
+ * [B][T][M] or NULL.  y_out: device float [B][T][M][d] or NULL.  ws: device
+ * scratch of at least engram_gate_conv_workspace() bytes, 256-byte aligned. */
+size_t engram_gate_conv_workspace(int64_t B, int64_t T, const engram_gate_conv_params* p);
+engram_status engram_gate_conv_forward(void* H, const void* kv, int64_t B, int64_t T,
+                                       const engram_gate_conv_params* p,
+                                       engram_decode_state* st, float* alpha_out,
+                                       float* y_out, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/* Steps 1-8 for one layer.  tokens: device int32 [B][T]; H: device
+ * [B][T][M][d] updated in place.  st: as for engram_gate_conv_forward; when
+ * given, the hash reads st->ids as the history and the state (ids, conv,
+ * pos) is advanced by T tokens.  alpha_out / y_out as above.  ws: device
+ * scratch of at least engram_forward_workspace() bytes, 256-byte aligned. */
+size_t engram_forward_workspace(int64_t B, int64_t T, const engram_layer* L);
+engram_status engram_forward(const int32_t* tokens, void* H, int64_t B, int64_t T,
+                             const engram_layer* L, engram_decode_state* st,
+                             float* alpha_out, float* y_out, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* Pinned host memory that kernels read directly over PCIe (tables kept in
+ * host DRAM; the DRAM-offload study reads them through unified addressing).
+ * engram_host_alloc returns the host pointer and its device alias; the
+ * memory must stay allocated until every stream that reads it has drained.
+ * engram_host_free releases memory from engram_host_alloc (synchronous). */
+engram_status engram_host_alloc(size_t bytes, void** host_ptr, void** device_alias);
+engram_status engram_host_free(void* host_ptr);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

@@ -266,6 +266,31 @@ def new_state(B: int, max_n: int, branches: int, span: int, d: int) -> dict:
             "pos": np.zeros(B, dtype=np.int64)}
 
 
+def gate_conv(H: np.ndarray, kv: np.ndarray, conv_w: np.ndarray, dilation: int, eps: float,
+              state_u=None) -> dict:
+    """Steps 6-8 from given projections, for every branch.
+
+    H [B, T, M, d] and kv [B, T, (1+M)*d] (v, then k^(0..M-1)) as float64;
+    conv_w [M, d, w]; state_u [B, M, (w-1)*dilation, d] conv inputs before
+    t = 0 (oldest first) or None.  Returns alpha, vt, u, c, Y and H_out."""
+    B, T, M, d = H.shape
+    v = kv[..., :d]
+    alpha = np.zeros((B, T, M))
+    vt = np.zeros((B, T, M, d))
+    u = np.zeros((B, T, M, d))
+    c = np.zeros((B, T, M, d))
+    for m in range(M):
+        k_m = kv[..., (1 + m) * d:(2 + m) * d]
+        alpha[:, :, m] = gate(H[:, :, m, :], k_m, eps)                               # Step 6
+        vt[:, :, m, :] = alpha[:, :, m, None] * v
+        u[:, :, m, :] = rmsnorm(vt[:, :, m, :], eps)                                 # Step 7
+        for b in range(B):
+            prev = None if state_u is None else state_u[b, m]
+            c[b, :, m, :] = short_conv(u[b, :, m, :], conv_w[m], dilation, prev)
+    Y = silu(c) + vt
+    return {"alpha": alpha, "vt": vt, "u": u, "c": c, "Y": Y, "H_out": H + Y}       # Step 8
+
+
 def forward(tokens: np.ndarray, H: np.ndarray, layer, h_dtype: str, state=None,
             e_dtype=None) -> dict:
     """One Engram layer over tokens [B, T] and hidden states H [B, T, M, d].
@@ -279,37 +304,19 @@ def forward(tokens: np.ndarray, H: np.ndarray, layer, h_dtype: str, state=None,
     """
     hp, tab = layer.hash, layer.tables
     B, T = tokens.shape
-    M, d, eps = layer.branches, layer.d, layer.eps
     span = (layer.kernel_w - 1) * layer.dilation
     hist = None if state is None else state["ids"]
     e_dtype = e_dtype or h_dtype
 
     z = hash_indices(tokens, hp.proj, hp.mult, hp.prime, hp.max_n, hp.heads, hist)   # Steps 1-3
     e = gather(z, tab.rows, tab.dtype, tab.row_offset, tab.dim, tab.scale, e_dtype)  # Steps 3-4
-    W = storage_to_f64(layer.w, h_dtype)
-    kv = project_kv(e, W)                                                            # Step 5
-    v = kv[..., :d]
-    h = storage_to_f64(H, h_dtype)
-
-    alpha = np.zeros((B, T, M))
-    vt = np.zeros((B, T, M, d))
-    u = np.zeros((B, T, M, d))
-    c = np.zeros((B, T, M, d))
-    for m in range(M):
-        k_m = kv[..., (1 + m) * d:(2 + m) * d]
-        alpha[:, :, m] = gate(h[:, :, m, :], k_m, eps)                               # Step 6
-        vt[:, :, m, :] = alpha[:, :, m, None] * v
-        u[:, :, m, :] = rmsnorm(vt[:, :, m, :], eps)                                 # Step 7
-        for b in range(B):
-            prev = None if state is None else state["u"][b, m]
-            c[b, :, m, :] = short_conv(u[b, :, m, :], layer.conv_w[m], layer.dilation, prev)
-    Y = silu(c) + vt
-    H_out = h + Y                                                                    # Step 8
-
-    out = {"z": z, "e": e, "kv": kv, "alpha": alpha, "vt": vt, "u": u, "c": c, "Y": Y, "H_out": H_out}
+    kv = project_kv(e, storage_to_f64(layer.w, h_dtype))                             # Step 5
+    out = gate_conv(storage_to_f64(H, h_dtype), kv, layer.conv_w, layer.dilation, layer.eps,
+                    None if state is None else state["u"])                           # Steps 6-8
+    out.update({"z": z, "e": e, "kv": kv})
     if state is not None:
         xc = compress(tokens, hp.proj)
         ids = np.concatenate([state["ids"], xc], axis=1)[:, -(hp.max_n - 1):]
-        uu = np.concatenate([state["u"], np.transpose(u, (0, 2, 1, 3))], axis=2)[:, :, -span:]
+        uu = np.concatenate([state["u"], np.transpose(out["u"], (0, 2, 1, 3))], axis=2)[:, :, -span:]
         out["state"] = {"ids": ids, "u": uu, "pos": state["pos"] + T}
     return out

@@ -1,0 +1,173 @@
+"""The C-ABI library: it loads, exports every function include/engram.h
+declares, and rejects bad host-visible arguments with the documented status
+before launching anything (these calls never reach the GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from hashed_gram_embedding_amd import engram as eg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "engram.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(eg.LIB_PATH), reason="libengram.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(engram_[a-z_]+)\s*\(", text)))
+
+
+def exported_functions():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", eg.LIB_PATH], capture_output=True, text=True).stdout
+    return sorted(set(m for m in re.findall(r" T (engram_\w+)", out)))
+
+
+def test_exports_match_header():
+    decl = declared_functions()
+    assert len(decl) >= 11
+    assert decl == exported_functions()
+    assert sorted(eg.exported_names()) == decl
+    L = eg.lib()
+    for name in decl:
+        assert hasattr(L, name)
+
+
+def test_abi_version():
+    assert eg.lib().engram_abi_version() == 1
+
+
+def _hash_params(**over):
+    proj = ctypes.c_void_p(0x1000)
+    mult = np.ones((2, 2, 3), dtype=np.uint64)
+    prime = np.array([1009, 1013, 1019, 1021], dtype=np.uint32)
+    hp = eg.HashParams(proj, 1000, 3, 2, mult.ctypes.data, prime.ctypes.data)
+    for k, v in over.items():
+        setattr(hp, k, v)
+    return hp, (mult, prime)
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    return st, eg.last_error()
+
+
+def test_hash_rejects_bad_arguments():
+    L = eg.lib()
+    tok = ctypes.c_void_p(0x2000)
+    z = ctypes.c_void_p(0x3000)
+    hp, keep = _hash_params()
+    assert L.engram_hash_indices(tok, 0, 5, None, ctypes.byref(hp), z, None) == eg.OK   # empty: no-op
+    st, msg = _status(L.engram_hash_indices, None, 1, 5, None, ctypes.byref(hp), z, None)
+    assert st == eg.EINVAL and "tokens" in msg
+    st, _ = _status(L.engram_hash_indices, tok, -1, 5, None, ctypes.byref(hp), z, None)
+    assert st == eg.EINVAL
+    bad, keep2 = _hash_params(max_n=5)
+    st, msg = _status(L.engram_hash_indices, tok, 1, 5, None, ctypes.byref(bad), z, None)
+    assert st == eg.EUNSUPPORTED and "max_n" in msg
+    bad, keep3 = _hash_params(heads=17)
+    assert L.engram_hash_indices(tok, 1, 5, None, ctypes.byref(bad), z, None) == eg.EUNSUPPORTED
+    prime0 = np.array([1, 1013, 1019, 1021], dtype=np.uint32)
+    bad, keep4 = _hash_params(prime=prime0.ctypes.data)
+    st, msg = _status(L.engram_hash_indices, tok, 1, 5, None, ctypes.byref(bad), z, None)
+    assert st == eg.EINVAL and "prime" in msg
+    assert L.engram_hash_indices(tok, 1, 5, None, None, z, None) == eg.EINVAL
+
+
+def _tables(**over):
+    off = np.array([0, 1009, 2022, 3041], dtype=np.int64)
+    n = np.array([1009, 1013, 1019, 1021], dtype=np.int64)
+    t = eg.Tables(4, 16, eg.F32, 0x10000, off.ctypes.data, n.ctypes.data, 4062, None, None, None, None, 0)
+    for k, v in over.items():
+        setattr(t, k, v)
+    return t, (off, n)
+
+
+def test_gather_rejects_bad_arguments():
+    L = eg.lib()
+    z, e = ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    t, keep = _tables()
+    assert L.engram_gather(z, 0, ctypes.byref(t), eg.F32, e, None) == eg.OK
+    assert L.engram_gather(z, 4, ctypes.byref(t), eg.I8, e, None) == eg.EUNSUPPORTED   # out dtype
+    t2, k2 = _tables(dim=12)
+    assert L.engram_gather(z, 4, ctypes.byref(t2), eg.F32, e, None) == eg.EUNSUPPORTED
+    t3, k3 = _tables(total_rows=4000)
+    st, msg = _status(L.engram_gather, z, 4, ctypes.byref(t3), eg.F32, e, None)
+    assert st == eg.EINVAL and "table 3" in msg
+    t4, k4 = _tables(dtype=eg.I8)
+    st, msg = _status(L.engram_gather, z, 4, ctypes.byref(t4), eg.BF16, e, None)
+    assert st == eg.EINVAL and "row_scale" in msg
+    t5, k5 = _tables(rows=0x10008)
+    assert L.engram_gather(z, 4, ctypes.byref(t5), eg.F32, e, None) == eg.EINVAL      # misaligned
+    t6, k6 = _tables(cache_slot=0x5000)
+    st, msg = _status(L.engram_gather, z, 4, ctypes.byref(t6), eg.F32, e, None)
+    assert st == eg.EINVAL and "cache" in msg
+    assert L.engram_gather(None, 4, ctypes.byref(t), eg.F32, e, None) == eg.EINVAL
+
+
+def test_project_rejects_bad_arguments():
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    assert L.engram_project_kv(p, p, 8, 96, 128, eg.BF16, p, None) == eg.EUNSUPPORTED
+    assert L.engram_project_kv(p, p, 8, 128, 100, eg.BF16, p, None) == eg.EUNSUPPORTED
+    assert L.engram_project_kv(p, p, 8, 128, 128, eg.I8, p, None) == eg.EUNSUPPORTED
+    assert L.engram_project_kv(p, p, 0, 128, 128, eg.BF16, p, None) == eg.OK
+    assert L.engram_project_kv(None, p, 8, 128, 128, eg.BF16, p, None) == eg.EINVAL
+
+
+def _gc(**over):
+    g = eg.GateConvParams(1024, 1, 4, 3, 1e-6, eg.BF16, 0x10000)
+    for k, v in over.items():
+        setattr(g, k, v)
+    return g
+
+
+def test_gate_conv_rejects_bad_arguments_and_small_workspace():
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    g = _gc()
+    need = L.engram_gate_conv_workspace(2, 10, ctypes.byref(g))
+    assert need >= 2 * 2 * 10 * 4
+    st, msg = _status(L.engram_gate_conv_forward, p, p, 2, 10, ctypes.byref(g), None, None, None, p, need - 1, None)
+    assert st == eg.EINVAL and "workspace" in msg
+    for bad in (_gc(d=1000), _gc(kernel_w=1), _gc(kernel_w=9), _gc(dilation=11), _gc(hdtype=eg.I8)):
+        assert L.engram_gate_conv_forward(p, p, 2, 10, ctypes.byref(bad), None, None, None, p, need, None) \
+            == eg.EUNSUPPORTED
+    assert L.engram_gate_conv_forward(p, p, 2, 10, ctypes.byref(_gc(conv_w=None)), None, None, None, p, need,
+                                      None) == eg.EINVAL
+    st_bad = eg.DecodeStateStruct(0x10000, None, 0x20000)
+    assert L.engram_gate_conv_forward(p, p, 2, 10, ctypes.byref(g), ctypes.byref(st_bad), None, None, p, need,
+                                      None) == eg.EINVAL
+
+
+def test_forward_checks_layer_consistency():
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    hp, keep_h = _hash_params()
+    t, keep_t = _tables()
+    lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=64, hdtype=eg.F32))
+    need = L.engram_forward_workspace(1, 64, ctypes.byref(lay))
+    assert need > 0
+    st, msg = _status(L.engram_forward, p, p, 1, 64, ctypes.byref(lay), None, None, None, p, need - 256, None)
+    assert st == eg.EINVAL and "workspace" in msg
+    n_bad = np.array([1009, 1013, 1019, 1000], dtype=np.int64)
+    t_bad, _ = _tables(n_rows=n_bad.ctypes.data)
+    lay2 = eg.LayerStruct(hp, t_bad, 0x10000, _gc(d=64, hdtype=eg.F32))
+    st, msg = _status(L.engram_forward, p, p, 1, 64, ctypes.byref(lay2), None, None, None, p, need, None)
+    assert st == eg.EINVAL and "prime" in msg
+    t3, _k = _tables(n_tables=3)
+    lay3 = eg.LayerStruct(hp, t3, 0x10000, _gc(d=64, hdtype=eg.F32))
+    assert L.engram_forward(p, p, 1, 64, ctypes.byref(lay3), None, None, None, p, need, None) == eg.EINVAL
+    assert L.engram_forward(p, p, 0, 64, ctypes.byref(lay), None, None, None, None, 0, None) == eg.OK
+
+
+def test_host_alloc_rejects_zero_bytes():
+    L = eg.lib()
+    h, d = ctypes.c_void_p(), ctypes.c_void_p()
+    assert L.engram_host_alloc(0, ctypes.byref(h), ctypes.byref(d)) == eg.EINVAL
+    assert L.engram_host_free(None) == eg.OK
