@@ -36,25 +36,28 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, choices=[1, 2])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     return ap.parse_args()
 
 
 def stage_units(w, lay):
-    """Algorithmic bytes / flops per launch of each kernel of the layer."""
+    """Algorithmic bytes (HBM-bound kernels) or flops (matrix-core kernel)
+    per launch of each kernel of the layer forward."""
     n_tok = w.B * w.T
     nt = lay.hash.n_tables
     dim = lay.tables.dim
     d, M = lay.d, lay.branches
     es = 2 if w.dtype == "bf16" else 4
-    row_bytes = dim * es
+    row_bytes = dim * (1 if lay.tables.dtype == "i8" else es) + (4 if lay.tables.dtype == "i8" else 0)
     d_mem = nt * dim
+    kv_row = (1 + M) * d * 4                                   # float32 projections
     return {
-        "hash": ("hbm", n_tok * (4 + 4 * nt)),                       # token ids in, z out
-        "gather": ("hbm", n_tok * nt * row_bytes * 2),              # rows in, e out
-        "project_kv": ("mfma", 2.0 * n_tok * (1 + M) * d * d_mem),  # flops
-        "gate": ("hbm", n_tok * M * (3 * d * es + 8)),              # h, k, v in; alpha, gamma out
-        "conv": ("hbm", n_tok * M * (d * es * 3 + 8)),              # v in, H in/out, alpha/gamma
+        "hash_kernel": ("hbm", n_tok * (4 + 4 * nt)),                      # token ids in, z out
+        "gather_kernel": ("hbm", n_tok * nt * (4 + row_bytes + dim * es)),  # z, rows in; e out
+        "gemm_bf16_kernel": ("mfma", 2.0 * n_tok * (1 + M) * d * d_mem),   # flops
+        "gate_kernel": ("hbm", n_tok * (M * (d * es + d * 4 + 8) + d * 4)),  # h, k^(m), v in; alpha, gamma out
+        "conv_kernel": ("hbm", n_tok * (d * 4 + M * (2 * d * es + 8))),    # v in, H in/out, alpha, gamma
     }
 
 
@@ -80,54 +83,64 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        eg.forward(tok, H, L, ws=ws, stream=stream)
+        eg.forward(tok, H, L, ws=ws)            # on the current stream
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    # the step is captured once into a HIP graph and replayed, so that host
+    # launch overhead does not pace a step of a few tens of microseconds
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):           # captures on a side stream
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+    else:
+        run = step
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(args.steps):
-        step()
+        run()
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
 
-    # per-kernel durations: the same kernels launched stage by stage through
-    # the per-step entry points, bracketed by HIP events on the same stream
-    z = torch.empty((w.B, w.T, lay.hash.n_tables), dtype=torch.int32, device=dev)
-    e = torch.empty((w.B, w.T, lay.d_mem), dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32, device=dev)
-    kv = torch.empty((w.B, w.T, (1 + lay.branches) * lay.d), dtype=e.dtype, device=dev)
-    names = ["hash", "gather", "project_kv", "gate_conv"]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    acc = np.zeros(len(names))
+    # per-kernel durations: HIP events that the library records on the launch
+    # stream around each kernel of the same forward (eager launches)
+    eg.profile_enable(True)
+    acc = {}
     for it in range(args.warmup + args.steps):
-        ev[0].record(stream)
-        eg.hash_indices(tok, L, z=z, stream=stream)
-        ev[1].record(stream)
-        eg.gather(z, L, w.dtype, e=e, stream=stream)
-        ev[2].record(stream)
-        eg.project_kv(e, L.w, kv=kv, stream=stream)
-        ev[3].record(stream)
-        eg.gate_conv_forward(H, kv, L, stream=stream)
-        ev[4].record(stream)
-        torch.cuda.synchronize()
-        if it >= args.warmup:
-            acc += [ev[i].elapsed_time(ev[i + 1]) for i in range(len(names))]
-    stage_ms = dict(zip(names, (acc / args.steps).tolist()))
+        step()
+        for name, t in eg.profile_read():
+            if it >= args.warmup:
+                acc[name] = acc.get(name, 0.0) + t
+    eg.profile_enable(False)
+    stage_ms = {k: v / args.steps for k, v in acc.items()}
 
     units = stage_units(w, lay)
-    gather_gbps = units["gather"][1] / (stage_ms["gather"] * 1e-3) / 1e9
-    gemm_tflops = units["project_kv"][1] / (stage_ms["project_kv"] * 1e-3) / 1e12
-    dominant = max(("gather", "project_kv"), key=lambda k: stage_ms[k])
-    if dominant == "project_kv":
-        roof = {"bound": "mfma", "kernel": "gemm_bf16_kernel", "achieved": round(gemm_tflops, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": None}
+    rates = {}
+    for k, t in stage_ms.items():
+        if k in units:
+            kind, amount = units[k]
+            rates[k] = amount / (t * 1e-3) / (1e9 if kind == "hbm" else 1e12)
+    dominant = max((k for k in stage_ms if k in units), key=lambda k: stage_ms[k])
+    kind, amount = units[dominant]
+    if kind == "mfma":
+        roof = {"bound": "mfma", "kernel": dominant, "achieved": round(rates[dominant], 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(rates[dominant] / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "units_per_launch": amount}
     else:
-        roof = {"bound": "hbm", "kernel": "gather_kernel", "achieved": round(gather_gbps, 1),
-                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gather_gbps / PEAK_HBM_GBPS, 4),
-                "traffic": None}
+        roof = {"bound": "hbm", "kernel": dominant, "achieved": round(rates[dominant], 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(rates[dominant] / PEAK_HBM_GBPS, 4),
+                "traffic": None, "units_per_launch": amount}
+    gather_gbps = rates.get("gather_kernel")
+    gemm_tflops = rates.get("gemm_bf16_kernel")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -149,9 +162,11 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "branches": lay.branches, "d": lay.d,
                    "d_mem": lay.d_mem, "tables": lay.hash.n_tables, "table_rows": lay.tables.total_rows,
                    "table_dtype": lay.tables.dtype},
-        "gather_GBps": round(gather_gbps, 1),
-        "gemm_TFLOPs": round(gemm_tflops, 2),
-        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "timing": "HIP graph replay" if graph is not None else "eager launches",
+        "gather_GBps": None if gather_gbps is None else round(gather_gbps, 1),
+        "gemm_TFLOPs": None if gemm_tflops is None else round(gemm_tflops, 2),
+        "kernel_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "kernel_rate": {k: round(v, 2) for k, v in rates.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -142,6 +142,7 @@ engram_status check_gc(const engram_gate_conv_params* p, engram::GateConvArgs* o
     out->dilation = p->dilation;
     out->eps = p->eps;
     out->hdtype = p->hdtype;
+    out->kvdtype = p->hdtype;
     out->conv_w = p->conv_w;
   }
   return ENGRAM_OK;
@@ -153,6 +154,33 @@ engram_status check_state(const engram_decode_state* st, bool need_ids) {
     return fail(ENGRAM_EINVAL, "decode state: ids, conv and pos must be non-NULL");
   if (!aligned(st->conv, 16)) return fail(ENGRAM_EINVAL, "decode state: conv must be 16-byte aligned");
   return ENGRAM_OK;
+}
+
+// ---- stage timing (per calling thread) ----
+constexpr int kMaxStages = 12;
+
+struct Profiler {
+  bool on = false;
+  bool created = false;
+  int n = 0;                        // events recorded by the last profiled call
+  hipEvent_t ev[kMaxStages + 1];
+  const char* names[kMaxStages];
+};
+
+thread_local Profiler g_prof;
+
+// Records the start of a stage (or, with name == nullptr, the end of the last one).
+void prof_mark(hipStream_t s, const char* name) {
+  Profiler& p = g_prof;
+  if (!p.on || p.n > kMaxStages) return;
+  if (name != nullptr && p.n == kMaxStages) return;
+  (void)hipEventRecord(p.ev[p.n], s);
+  if (name != nullptr) p.names[p.n] = name;
+  ++p.n;
+}
+
+void prof_begin() {
+  if (g_prof.on) g_prof.n = 0;
 }
 
 struct GcWorkspace {
@@ -174,18 +202,22 @@ engram_status run_gate_conv(void* H, const void* kv, int64_t B, int64_t T, const
   const int64_t n_tok = B * T;
   GcWorkspace w = carve_gc(ws, n_tok, g.branches);
   float* alpha = alpha_out != nullptr ? alpha_out : w.alpha;
+  prof_mark(s, "gate_kernel");
   engram_status r = hip_status(engram::launch_gate(H, kv, n_tok, g, alpha, w.gamma, s), "gate launch");
   if (r != ENGRAM_OK) return r;
   engram::StateArgs sa{};
   if (st != nullptr) sa = engram::StateArgs{st->ids, st->conv, st->pos};
+  prof_mark(s, "conv_kernel");
   r = hip_status(engram::launch_conv(H, kv, B, T, g, alpha, w.gamma, st != nullptr ? &sa : nullptr, y_out, s),
                  "conv launch");
   if (r != ENGRAM_OK) return r;
   if (st != nullptr) {
     if (tokens == nullptr) sa.ids = nullptr;
+    prof_mark(s, "state_commit_kernel");
     r = hip_status(engram::launch_state_commit(kv, B, T, g, w.gamma, sa, tokens, proj, max_n, s),
                    "state commit launch");
   }
+  prof_mark(s, nullptr);
   return r;
 }
 
@@ -203,7 +235,7 @@ size_t forward_ws_bytes(int64_t n_tok, const engram_layer* L) {
   const int64_t n_out = static_cast<int64_t>(1 + L->gc.branches) * L->gc.d;
   return align_up(static_cast<size_t>(n_tok) * nt * sizeof(int32_t)) +
          align_up(static_cast<size_t>(n_tok) * d_mem * es) +
-         align_up(static_cast<size_t>(n_tok) * n_out * es) + gc_ws_bytes(n_tok, L->gc.branches);
+         align_up(static_cast<size_t>(n_tok) * n_out * sizeof(float)) + gc_ws_bytes(n_tok, L->gc.branches);
 }
 
 ForwardWorkspace carve_forward(char* ws, int64_t n_tok, const engram_layer* L) {
@@ -216,7 +248,7 @@ ForwardWorkspace carve_forward(char* ws, int64_t n_tok, const engram_layer* L) {
   f.e = ws;
   ws += align_up(static_cast<size_t>(n_tok) * d_mem * es);
   f.kv = ws;
-  ws += align_up(static_cast<size_t>(n_tok) * (1 + L->gc.branches) * L->gc.d * es);
+  ws += align_up(static_cast<size_t>(n_tok) * (1 + L->gc.branches) * L->gc.d * sizeof(float));
   f.gc = ws;
   return f;
 }
@@ -293,7 +325,8 @@ ENGRAM_API engram_status engram_project_kv(const void* e, const void* w, int64_t
   if (e == nullptr || w == nullptr || kv == nullptr)
     return fail(ENGRAM_EINVAL, "project_kv: e, w and kv must be non-NULL");
   if (!aligned(e, 16) || !aligned(w, 16)) return fail(ENGRAM_EINVAL, "project_kv: e and w must be 16-byte aligned");
-  return hip_status(engram::launch_project_kv(e, w, n_tok, d_mem, n_out, dtype, kv, stream), "project_kv launch");
+  return hip_status(engram::launch_project_kv(e, w, n_tok, d_mem, n_out, dtype, dtype, kv, stream),
+                    "project_kv launch");
 }
 
 ENGRAM_API size_t engram_gate_conv_workspace(int64_t B, int64_t T, const engram_gate_conv_params* p) {
@@ -349,15 +382,55 @@ ENGRAM_API engram_status engram_forward(const int32_t* tokens, void* H, int64_t 
   ForwardWorkspace f = carve_forward(static_cast<char*>(ws), n_tok, L);
   const int64_t d_mem = static_cast<int64_t>(L->tables.n_tables) * L->tables.dim;
   const int64_t n_out = static_cast<int64_t>(1 + g.branches) * g.d;
+  prof_begin();
+  prof_mark(stream, "hash_kernel");
   r = hip_status(engram::launch_hash(tokens, B, T, st != nullptr ? st->ids : nullptr, L->hash.proj, ha, f.z, stream),
                  "hash launch");
   if (r != ENGRAM_OK) return r;
+  prof_mark(stream, "gather_kernel");
   r = hip_status(engram::launch_gather(f.z, n_tok, ta, g.hdtype, f.e, stream), "gather launch");
   if (r != ENGRAM_OK) return r;
-  r = hip_status(engram::launch_project_kv(f.e, L->w, n_tok, d_mem, n_out, g.hdtype, f.kv, stream),
+  // the projections stay in float32: v is normalised and convolved next
+  prof_mark(stream, "gemm_bf16_kernel");
+  r = hip_status(engram::launch_project_kv(f.e, L->w, n_tok, d_mem, n_out, g.hdtype, ENGRAM_F32, f.kv, stream),
                  "project_kv launch");
   if (r != ENGRAM_OK) return r;
+  g.kvdtype = ENGRAM_F32;
   return run_gate_conv(H, f.kv, B, T, g, st, tokens, L->hash.proj, L->hash.max_n, alpha_out, y_out, f.gc, stream);
+}
+
+ENGRAM_API engram_status engram_profile_enable(int32_t on) {
+  Profiler& p = g_prof;
+  if (on && !p.created) {
+    for (int i = 0; i <= kMaxStages; ++i) {
+      hipError_t e = hipEventCreate(&p.ev[i]);
+      if (e != hipSuccess) return hip_status(e, "hipEventCreate");
+    }
+    p.created = true;
+  }
+  p.on = on != 0;
+  p.n = 0;
+  return ENGRAM_OK;
+}
+
+ENGRAM_API engram_status engram_profile_read(float* ms, const char** names, int32_t cap, int32_t* n_stages) {
+  Profiler& p = g_prof;
+  if (n_stages == nullptr || (cap > 0 && ms == nullptr))
+    return fail(ENGRAM_EINVAL, "profile_read: n_stages and ms must be non-NULL");
+  *n_stages = 0;
+  if (!p.created || p.n < 2) return fail(ENGRAM_EINVAL, "profile_read: no profiled call recorded");
+  hipError_t e = hipEventSynchronize(p.ev[p.n - 1]);
+  if (e != hipSuccess) return hip_status(e, "hipEventSynchronize");
+  const int stages = p.n - 1;
+  for (int i = 0; i < stages && i < cap; ++i) {
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, p.ev[i], p.ev[i + 1]);
+    if (e != hipSuccess) return hip_status(e, "hipEventElapsedTime");
+    ms[i] = t;
+    if (names != nullptr) names[i] = p.names[i];
+  }
+  *n_stages = stages;
+  return ENGRAM_OK;
 }
 
 ENGRAM_API engram_status engram_host_alloc(size_t bytes, void** host_ptr, void** device_alias) {

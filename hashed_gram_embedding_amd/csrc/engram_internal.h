@@ -36,7 +36,8 @@ struct GateConvArgs {
   int32_t kernel_w;
   int32_t dilation;
   float eps;
-  int32_t hdtype;
+  int32_t hdtype;   // storage of H
+  int32_t kvdtype;  // storage of kv (F32 or BF16)
   const float* conv_w;
 };
 
@@ -53,7 +54,7 @@ hipError_t launch_gather(const int32_t* z, int64_t n_tok, const TableArgs& ta, i
                          void* e, hipStream_t s);
 
 hipError_t launch_project_kv(const void* e, const void* w, int64_t n_tok, int64_t d_mem,
-                             int64_t n_out, int dtype, void* kv, hipStream_t s);
+                             int64_t n_out, int in_dtype, int out_dtype, void* kv, hipStream_t s);
 
 // alpha[t][m] and gamma[t][m] = alpha / sqrt(alpha^2 mean(v^2) + eps) for every token.
 hipError_t launch_gate(const void* H, const void* kv, int64_t n_tok, const GateConvArgs& g,

@@ -57,7 +57,7 @@ __device__ __forceinline__ void load8f(const float* base, int64_t off, float* f)
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-template <int HT>
+template <int HT, int KT>
 __global__ void __launch_bounds__(256)
 gate_kernel(const void* __restrict__ H, const void* __restrict__ kv, int64_t n_tok, GateConvArgs g,
             float* __restrict__ alpha, float* __restrict__ gamma) {
@@ -75,8 +75,8 @@ gate_kernel(const void* __restrict__ H, const void* __restrict__ kv, int64_t n_t
   for (int c = lane; c < (d >> 3); c += 64) {
     float h[8], k[8], v[8];
     load8h<HT>(H, h_off + c * 8, h);
-    load8h<HT>(kv, k_off + c * 8, k);
-    load8h<HT>(kv, v_off + c * 8, v);
+    load8h<KT>(kv, k_off + c * 8, k);
+    load8h<KT>(kv, v_off + c * 8, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       shh += h[i] * h[i];
@@ -100,7 +100,7 @@ gate_kernel(const void* __restrict__ H, const void* __restrict__ kv, int64_t n_t
   }
 }
 
-template <int HT>
+template <int HT, int KT>
 __global__ void __launch_bounds__(256)
 conv_kernel(void* __restrict__ H, const void* __restrict__ kv, int64_t B, int64_t T, GateConvArgs g,
             const float* __restrict__ alpha, const float* __restrict__ gamma, StateArgs st,
@@ -134,7 +134,7 @@ conv_kernel(void* __restrict__ H, const void* __restrict__ kv, int64_t B, int64_
     float u[8];
     if (s >= 0) {
       const int64_t bs = b * T + s;
-      load8h<HT>(kv, bs * row_kv + ch0, u);
+      load8h<KT>(kv, bs * row_kv + ch0, u);
       if (back == 0) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) vt[i] = u[i];
@@ -166,7 +166,7 @@ conv_kernel(void* __restrict__ H, const void* __restrict__ kv, int64_t B, int64_
   if (y_out != nullptr) store8f(y_out, h_off, y);
 }
 
-template <int HT>
+template <int KT>
 __global__ void __launch_bounds__(256)
 state_commit_kernel(const void* __restrict__ kv, int64_t T, GateConvArgs g,
                     const float* __restrict__ gamma, StateArgs st, const int32_t* __restrict__ tokens,
@@ -189,7 +189,7 @@ state_commit_kernel(const void* __restrict__ kv, int64_t T, GateConvArgs g,
     const int slot = static_cast<int>((static_cast<int64_t>(pos0) + p) % span);
     const int64_t bs = b * T + p;
     float u[8];
-    load8h<HT>(kv, bs * row_kv + c8 * 8, u);
+    load8h<KT>(kv, bs * row_kv + c8 * 8, u);
     const float gm = gamma[bs * M + m];
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[i] *= gm;
@@ -215,10 +215,13 @@ hipError_t launch_gate(const void* H, const void* kv, int64_t n_tok, const GateC
   const int64_t pairs = n_tok * g.branches;
   if (pairs == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((pairs + 3) / 4));
-  if (g.hdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL(gate_kernel<ENGRAM_BF16>, grid, dim3(256), 0, s, H, kv, n_tok, g, alpha, gamma);
+  const dim3 block(256);
+  if (g.hdtype == ENGRAM_BF16 && g.kvdtype == ENGRAM_BF16)
+    hipLaunchKernelGGL((gate_kernel<ENGRAM_BF16, ENGRAM_BF16>), grid, block, 0, s, H, kv, n_tok, g, alpha, gamma);
+  else if (g.hdtype == ENGRAM_BF16)
+    hipLaunchKernelGGL((gate_kernel<ENGRAM_BF16, ENGRAM_F32>), grid, block, 0, s, H, kv, n_tok, g, alpha, gamma);
   else
-    hipLaunchKernelGGL(gate_kernel<ENGRAM_F32>, grid, dim3(256), 0, s, H, kv, n_tok, g, alpha, gamma);
+    hipLaunchKernelGGL((gate_kernel<ENGRAM_F32, ENGRAM_F32>), grid, block, 0, s, H, kv, n_tok, g, alpha, gamma);
   return hipGetLastError();
 }
 
@@ -228,13 +231,19 @@ hipError_t launch_conv(void* H, const void* kv, int64_t B, int64_t T, const Gate
   const int64_t total = B * T * g.branches * (g.d / 8);
   if (total == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+  const dim3 block(256);
   StateArgs sa{};
   if (st != nullptr) sa = *st;
   const int has = st != nullptr;
-  if (g.hdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL(conv_kernel<ENGRAM_BF16>, grid, dim3(256), 0, s, H, kv, B, T, g, alpha, gamma, sa, has, y_out);
+  if (g.hdtype == ENGRAM_BF16 && g.kvdtype == ENGRAM_BF16)
+    hipLaunchKernelGGL((conv_kernel<ENGRAM_BF16, ENGRAM_BF16>), grid, block, 0, s, H, kv, B, T, g, alpha, gamma, sa,
+                       has, y_out);
+  else if (g.hdtype == ENGRAM_BF16)
+    hipLaunchKernelGGL((conv_kernel<ENGRAM_BF16, ENGRAM_F32>), grid, block, 0, s, H, kv, B, T, g, alpha, gamma, sa,
+                       has, y_out);
   else
-    hipLaunchKernelGGL(conv_kernel<ENGRAM_F32>, grid, dim3(256), 0, s, H, kv, B, T, g, alpha, gamma, sa, has, y_out);
+    hipLaunchKernelGGL((conv_kernel<ENGRAM_F32, ENGRAM_F32>), grid, block, 0, s, H, kv, B, T, g, alpha, gamma, sa,
+                       has, y_out);
   return hipGetLastError();
 }
 
@@ -242,7 +251,7 @@ hipError_t launch_state_commit(const void* kv, int64_t B, int64_t T, const GateC
                                const float* gamma, const StateArgs& st, const int32_t* tokens,
                                const int32_t* proj, int32_t max_n, hipStream_t s) {
   if (B == 0 || T == 0) return hipSuccess;
-  if (g.hdtype == ENGRAM_BF16)
+  if (g.kvdtype == ENGRAM_BF16)
     hipLaunchKernelGGL(state_commit_kernel<ENGRAM_BF16>, dim3(static_cast<unsigned>(B)), dim3(256), 0, s,
                        kv, T, g, gamma, st, tokens, proj, max_n);
   else

@@ -16,6 +16,10 @@
 // numbers are remapped such that each XCD walks a contiguous range, n
 // fastest; the tiles that share an e row block then share one L2.
 //
+// The bf16 path can write kv as bf16 (the standalone projection entry point)
+// or keep the float32 accumulators (inside the layer forward, where v feeds a
+// normalisation and the conv and bf16 rounding would cost accuracy).
+//
 // f32 path: plain per-output dot products (small shapes only).
 #include "device_util.h"
 #include "engram_internal.h"
@@ -34,9 +38,10 @@ constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
+template <typename OutT>
 __global__ void __launch_bounds__(kThreads)
 gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-                 uint16_t* __restrict__ C, int64_t M, int N, int K, int tiles_m, int tiles_n) {
+                 OutT* __restrict__ C, int64_t M, int N, int K, int tiles_m, int tiles_n) {
   __shared__ uint4 As[BM * BK / 8];
   __shared__ uint4 Bs[BN * BK / 8];
 
@@ -135,7 +140,10 @@ gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int gn = n0 + wn * 64 + j * 16 + (lane & 15);
-        if (gn < N) C[gm * N + gn] = f32_to_bf16(acc[i][j][r]);
+        if (gn < N) {
+          if constexpr (sizeof(OutT) == 2) C[gm * N + gn] = f32_to_bf16(acc[i][j][r]);
+          else C[gm * N + gn] = acc[i][j][r];
+        }
       }
     }
   }
@@ -158,15 +166,22 @@ gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ W, float*
 }  // namespace
 
 hipError_t launch_project_kv(const void* e, const void* w, int64_t n_tok, int64_t d_mem,
-                             int64_t n_out, int dtype, void* kv, hipStream_t s) {
+                             int64_t n_out, int in_dtype, int out_dtype, void* kv, hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
-  if (dtype == ENGRAM_BF16) {
+  if (in_dtype == ENGRAM_BF16) {
     const int tiles_m = static_cast<int>((n_tok + BM - 1) / BM);
     const int tiles_n = static_cast<int>((n_out + BN - 1) / BN);
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), 0, s,
-                       static_cast<const uint16_t*>(e), static_cast<const uint16_t*>(w),
-                       static_cast<uint16_t*>(kv), n_tok, static_cast<int>(n_out),
-                       static_cast<int>(d_mem), tiles_m, tiles_n);
+    const dim3 grid(tiles_m * tiles_n);
+    const auto* A = static_cast<const uint16_t*>(e);
+    const auto* W = static_cast<const uint16_t*>(w);
+    if (out_dtype == ENGRAM_BF16)
+      hipLaunchKernelGGL(gemm_bf16_kernel<uint16_t>, grid, dim3(kThreads), 0, s, A, W,
+                         static_cast<uint16_t*>(kv), n_tok, static_cast<int>(n_out),
+                         static_cast<int>(d_mem), tiles_m, tiles_n);
+    else
+      hipLaunchKernelGGL(gemm_bf16_kernel<float>, grid, dim3(kThreads), 0, s, A, W,
+                         static_cast<float*>(kv), n_tok, static_cast<int>(n_out),
+                         static_cast<int>(d_mem), tiles_m, tiles_n);
   } else {
     const int64_t total = n_tok * n_out;
     hipLaunchKernelGGL(gemm_f32_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,

@@ -84,6 +84,9 @@ def lib():
         "engram_forward_workspace": (sz, [i64, i64, ctypes.POINTER(LayerStruct)]),
         "engram_forward": (i32, [vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
                                  ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
+        "engram_profile_enable": (i32, [i32]),
+        "engram_profile_read": (i32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), i32,
+                                      ctypes.POINTER(i32)]),
         "engram_host_alloc": (i32, [sz, ctypes.POINTER(vp), ctypes.POINTER(vp)]),
         "engram_host_free": (i32, [vp]),
     }
@@ -98,7 +101,8 @@ def lib():
 def exported_names():
     return ["engram_abi_version", "engram_last_error", "engram_hash_indices", "engram_gather",
             "engram_project_kv", "engram_gate_conv_workspace", "engram_gate_conv_forward",
-            "engram_forward_workspace", "engram_forward", "engram_host_alloc", "engram_host_free"]
+            "engram_forward_workspace", "engram_forward", "engram_profile_enable", "engram_profile_read",
+            "engram_host_alloc", "engram_host_free"]
 
 
 def last_error() -> str:
@@ -287,6 +291,20 @@ def gate_conv_forward(H: torch.Tensor, kv: torch.Tensor, layer: Layer, state: Op
     _check(lib().engram_gate_conv_forward(_ptr(H), _ptr(kv), B, T, ctypes.byref(layer.s.gc), st,
                                           _ptr(alpha), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
     return alpha, y
+
+
+def profile_enable(on: bool = True):
+    _check(lib().engram_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    """[(kernel name, ms)] of the stages of the last profiled forward call."""
+    cap = 16
+    ms = (ctypes.c_float * cap)()
+    names = (ctypes.c_char_p * cap)()
+    n = ctypes.c_int32()
+    _check(lib().engram_profile_read(ms, names, cap, ctypes.byref(n)))
+    return [(names[i].decode(), float(ms[i])) for i in range(n.value)]
 
 
 def forward_workspace(B: int, T: int, layer: Layer) -> int:

@@ -198,6 +198,17 @@ engram_status engram_forward(const int32_t* tokens, void* H, int64_t B, int64_t 
                              float* alpha_out, float* y_out, void* ws, size_t ws_bytes,
                              hipStream_t stream);
 
+/* Stage timing, for benchmarks.  engram_profile_enable(1) makes later
+ * engram_forward calls on the calling thread record a HIP event on their
+ * stream before each kernel launch and after the last one (events owned by
+ * the library, reused by each call).  engram_profile_read waits for the last
+ * event of the most recent profiled call, writes up to `cap` stage durations
+ * in milliseconds to ms[] and their kernel names to names[] (static strings;
+ * names may be NULL), and returns the stage count in *n_stages.
+ * engram_profile_enable(0) stops recording. */
+engram_status engram_profile_enable(int32_t on);
+engram_status engram_profile_read(float* ms, const char** names, int32_t cap, int32_t* n_stages);
+
 /* Pinned host memory that kernels read directly over PCIe (tables kept in
  * host DRAM; the DRAM-offload study reads them through unified addressing).
  * engram_host_alloc returns the host pointer and its device alias; the

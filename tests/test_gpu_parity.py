@@ -292,3 +292,32 @@ def test_forward_full_size_single_branch_sampled():
         k = s - lo
         check_bf16_layer(a_g[:, s:s + 64], ref["alpha"][:, k:], y_g[:, s:s + 64], ref["Y"][:, k:],
                          h_g[:, s:s + 64], h_in[:, s:s + 64], tag=f"window{s}")
+
+
+def test_graph_replays_match_eager():
+    """The forward captured in a HIP graph gives, on every replay, exactly the
+    eager result (the kernels are deterministic and issue no memsets)."""
+    log("graph replay vs eager")
+    w = small(1, B=2, T=150)
+    L = eg.Layer(w.layers[0], "bf16", DEV)
+    tok = dev_tokens(w)
+    H0 = dev_H(w)
+    ws = torch.empty(eg.forward_workspace(w.B, w.T, L), dtype=torch.uint8, device=DEV)
+    ref = H0.clone()
+    eg.forward(tok, ref, L, ws=ws)
+    H = H0.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        eg.forward(tok, H, L, ws=ws, stream=s)
+    for r in range(4):
+        H.copy_(H0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(H.view(torch.int16), ref.view(torch.int16)), r
+        other = H0.clone()
+        eg.forward(tok, other, L, ws=ws)          # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other.view(torch.int16), ref.view(torch.int16))
