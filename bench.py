@@ -42,22 +42,29 @@ def parse():
 
 
 def stage_units(w, lay):
-    """Algorithmic bytes (HBM-bound kernels) or flops (matrix-core kernel)
-    per launch of each kernel of the layer forward."""
+    """Algorithmic bytes (HBM-bound kernels) or flops (matrix-core kernels)
+    per launch of each kernel of the layer forward, keyed by the kernel names
+    the library reports."""
     n_tok = w.B * w.T
     nt = lay.hash.n_tables
     dim = lay.tables.dim
     d, M = lay.d, lay.branches
     es = 2 if w.dtype == "bf16" else 4
-    row_bytes = dim * (1 if lay.tables.dtype == "i8" else es) + (4 if lay.tables.dtype == "i8" else 0)
+    i8 = lay.tables.dtype == "i8"
+    row_bytes = dim * (1 if i8 else es) + (4 if i8 else 0)
     d_mem = nt * dim
-    kv_row = (1 + M) * d * 4                                   # float32 projections
+    fused = w.dtype == "bf16" and d % 128 == 0
+    n_stat = (1 + M) * d // 128 if fused else 1 + M
+    flops = 2.0 * n_tok * (1 + M) * d * d_mem
     return {
-        "hash_kernel": ("hbm", n_tok * (4 + 4 * nt)),                      # token ids in, z out
-        "gather_kernel": ("hbm", n_tok * nt * (4 + row_bytes + dim * es)),  # z, rows in; e out
-        "gemm_bf16_kernel": ("mfma", 2.0 * n_tok * (1 + M) * d * d_mem),   # flops
-        "gate_kernel": ("hbm", n_tok * (M * (d * es + d * 4 + 8) + d * 4)),  # h, k^(m), v in; alpha, gamma out
-        "conv_kernel": ("hbm", n_tok * (d * 4 + M * (2 * d * es + 8))),    # v in, H in/out, alpha, gamma
+        # token ids in; rows in; e out
+        "gather_kernel<hashed>": ("hbm", n_tok * (4 + nt * (row_bytes + dim * es))),
+        "proj_gate_kernel": ("mfma", flops),
+        "gemm_kernel": ("mfma", flops),
+        # h, k, v in; statistics out
+        "gate_stats_kernel": ("hbm", n_tok * (M * 2 * d * 4 + d * 4 + M * d * es + 16 * n_stat)),
+        # v (float32) and statistics in; H in and out; alpha, gamma out
+        "conv_kernel": ("hbm", n_tok * (d * 4 + 16 * n_stat + M * (2 * d * es + 8))),
     }
 
 
@@ -139,8 +146,8 @@ def main():
         roof = {"bound": "hbm", "kernel": dominant, "achieved": round(rates[dominant], 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(rates[dominant] / PEAK_HBM_GBPS, 4),
                 "traffic": None, "units_per_launch": amount}
-    gather_gbps = rates.get("gather_kernel")
-    gemm_tflops = rates.get("gemm_bf16_kernel")
+    gather_gbps = rates.get("gather_kernel<hashed>")
+    gemm_tflops = rates.get("proj_gate_kernel", rates.get("gemm_kernel"))
 
     cpu = None
     if not args.no_cpu_baseline:

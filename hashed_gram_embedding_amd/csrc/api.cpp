@@ -63,6 +63,7 @@ engram_status check_hash(const engram_hash_params* hp, engram::HashArgs* out) {
         return fail(ENGRAM_EINVAL, "hash params: prime[%d]=%u outside [2, 2^31)", j, p);
       if (out != nullptr) {
         out->prime[j] = p;
+        out->inv[j] = ~static_cast<uint64_t>(0) / p;
         out->order[j] = n;
         for (int i = 0; i < n; ++i)
           out->mult[j][i] = hp->mult[(static_cast<int64_t>(n - 2) * hp->heads + k) * hp->max_n + i];
@@ -183,74 +184,107 @@ void prof_begin() {
   if (g_prof.on) g_prof.n = 0;
 }
 
-struct GcWorkspace {
-  float* alpha;
-  float* gamma;
+// ---- workspace layouts ----
+// A bump allocator over the caller's workspace: every region starts on a
+// 256-byte boundary.  With base == nullptr it only measures.
+struct Carve {
+  char* base;
+  size_t used = 0;
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base == nullptr ? nullptr : reinterpret_cast<T*>(base + used);
+    used += align_up(count * sizeof(T));
+    return p;
+  }
 };
 
-size_t gc_ws_bytes(int64_t n_tok, int M) { return 2 * align_up(static_cast<size_t>(n_tok) * M * sizeof(float)); }
+struct GcWorkspace {
+  float4* stats;   // [n_tok][1+M]
+  float* gamma;    // [n_tok][M]
+};
 
-GcWorkspace carve_gc(char* ws, int64_t n_tok, int M) {
-  const size_t a = align_up(static_cast<size_t>(n_tok) * M * sizeof(float));
-  return GcWorkspace{reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + a)};
+GcWorkspace carve_gc(Carve& c, int64_t n_tok, int M) {
+  GcWorkspace w;
+  w.stats = c.take<float4>(static_cast<size_t>(n_tok) * (1 + M));
+  w.gamma = c.take<float>(static_cast<size_t>(n_tok) * M);
+  return w;
 }
 
-// Steps 6-8 after the projections are in kv.
-engram_status run_gate_conv(void* H, const void* kv, int64_t B, int64_t T, const engram::GateConvArgs& g,
-                            engram_decode_state* st, const int32_t* tokens, const int32_t* proj,
-                            int32_t max_n, float* alpha_out, float* y_out, char* ws, hipStream_t s) {
-  const int64_t n_tok = B * T;
-  GcWorkspace w = carve_gc(ws, n_tok, g.branches);
-  float* alpha = alpha_out != nullptr ? alpha_out : w.alpha;
-  prof_mark(s, "gate_kernel");
-  engram_status r = hip_status(engram::launch_gate(H, kv, n_tok, g, alpha, w.gamma, s), "gate launch");
-  if (r != ENGRAM_OK) return r;
-  engram::StateArgs sa{};
-  if (st != nullptr) sa = engram::StateArgs{st->ids, st->conv, st->pos};
+// Fused bf16 path: gathered rows, float32 v, per-tile gate statistics.
+bool use_fused(const engram_layer* L) {
+  return L->gc.hdtype == ENGRAM_BF16 && L->gc.d % engram::kProjGateTileF == 0 &&
+         (static_cast<int64_t>(L->tables.n_tables) * L->tables.dim) % 64 == 0;
+}
+
+struct ForwardWorkspace {
+  void* e;          // [n_tok][d_mem] (hdtype)
+  float* kv;        // unfused: [n_tok][(1+M)d]; fused: v only, [n_tok][d]
+  float4* stats;    // fused: [n_tok][(1+M)d/128]; unfused: [n_tok][1+M]
+  float* gamma;     // [n_tok][M]
+};
+
+ForwardWorkspace carve_forward(Carve& c, int64_t n_tok, const engram_layer* L) {
+  const int M = L->gc.branches, d = L->gc.d;
+  const int64_t d_mem = static_cast<int64_t>(L->tables.n_tables) * L->tables.dim;
+  const size_t es = dtype_size(L->gc.hdtype);
+  ForwardWorkspace f;
+  f.e = c.take<char>(static_cast<size_t>(n_tok) * d_mem * es);
+  if (use_fused(L)) {
+    f.kv = c.take<float>(static_cast<size_t>(n_tok) * d);
+    f.stats = c.take<float4>(static_cast<size_t>(n_tok) * (1 + M) * d / engram::kProjGateTileF);
+  } else {
+    f.kv = c.take<float>(static_cast<size_t>(n_tok) * (1 + M) * d);
+    f.stats = c.take<float4>(static_cast<size_t>(n_tok) * (1 + M));
+  }
+  f.gamma = c.take<float>(static_cast<size_t>(n_tok) * M);
+  return f;
+}
+
+size_t gc_ws_bytes(int64_t n_tok, int M) {
+  Carve c{nullptr};
+  carve_gc(c, n_tok, M);
+  return c.used;
+}
+
+size_t forward_ws_bytes(int64_t n_tok, const engram_layer* L) {
+  Carve c{nullptr};
+  carve_forward(c, n_tok, L);
+  return c.used;
+}
+
+// Steps 6-8 once the gate statistics are in `stats`: conv (+ residual), then
+// the decode-state commit.
+engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdtype, const float4* stats, int qv,
+                              int qk, int64_t B, int64_t T, const engram::GateConvArgs& g, engram_decode_state* st,
+                              const int32_t* tokens, const int32_t* proj, int32_t max_n, float* alpha_out,
+                              float* gamma, float* y_out, hipStream_t s) {
+  engram::ConvArgs ca{};
+  ca.H = H;
+  ca.v = v;
+  ca.v_stride = v_stride;
+  ca.stats = stats;
+  ca.qv = qv;
+  ca.qk = qk;
+  ca.nq = qv + g.branches * qk;
+  ca.B = B;
+  ca.T = T;
+  ca.g = g;
+  ca.has_state = st != nullptr;
+  if (st != nullptr) ca.st = engram::StateArgs{st->ids, st->conv, st->pos};
+  ca.alpha_out = alpha_out;
+  ca.gamma_out = gamma;
+  ca.y_out = y_out;
   prof_mark(s, "conv_kernel");
-  r = hip_status(engram::launch_conv(H, kv, B, T, g, alpha, w.gamma, st != nullptr ? &sa : nullptr, y_out, s),
-                 "conv launch");
+  engram_status r = hip_status(engram::launch_conv(ca, vdtype, s), "conv launch");
   if (r != ENGRAM_OK) return r;
   if (st != nullptr) {
-    if (tokens == nullptr) sa.ids = nullptr;
+    engram::StateArgs sa{tokens != nullptr ? st->ids : nullptr, st->conv, st->pos};
     prof_mark(s, "state_commit_kernel");
-    r = hip_status(engram::launch_state_commit(kv, B, T, g, w.gamma, sa, tokens, proj, max_n, s),
+    r = hip_status(engram::launch_state_commit(v, v_stride, vdtype, B, T, g, gamma, sa, tokens, proj, max_n, s),
                    "state commit launch");
   }
   prof_mark(s, nullptr);
   return r;
-}
-
-struct ForwardWorkspace {
-  int32_t* z;
-  void* e;
-  void* kv;
-  char* gc;
-};
-
-size_t forward_ws_bytes(int64_t n_tok, const engram_layer* L) {
-  const int nt = L->tables.n_tables;
-  const int64_t d_mem = static_cast<int64_t>(nt) * L->tables.dim;
-  const size_t es = dtype_size(L->gc.hdtype);
-  const int64_t n_out = static_cast<int64_t>(1 + L->gc.branches) * L->gc.d;
-  return align_up(static_cast<size_t>(n_tok) * nt * sizeof(int32_t)) +
-         align_up(static_cast<size_t>(n_tok) * d_mem * es) +
-         align_up(static_cast<size_t>(n_tok) * n_out * sizeof(float)) + gc_ws_bytes(n_tok, L->gc.branches);
-}
-
-ForwardWorkspace carve_forward(char* ws, int64_t n_tok, const engram_layer* L) {
-  const int nt = L->tables.n_tables;
-  const int64_t d_mem = static_cast<int64_t>(nt) * L->tables.dim;
-  const size_t es = dtype_size(L->gc.hdtype);
-  ForwardWorkspace f;
-  f.z = reinterpret_cast<int32_t*>(ws);
-  ws += align_up(static_cast<size_t>(n_tok) * nt * sizeof(int32_t));
-  f.e = ws;
-  ws += align_up(static_cast<size_t>(n_tok) * d_mem * es);
-  f.kv = ws;
-  ws += align_up(static_cast<size_t>(n_tok) * (1 + L->gc.branches) * L->gc.d * sizeof(float));
-  f.gc = ws;
-  return f;
 }
 
 engram_status check_layer(const engram_layer* L, engram::HashArgs* ha, engram::TableArgs* ta,
@@ -351,7 +385,15 @@ ENGRAM_API engram_status engram_gate_conv_forward(void* H, const void* kv, int64
   const size_t need = gc_ws_bytes(B * T, p->branches);
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
     return fail(ENGRAM_EINVAL, "gate_conv: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
-  return run_gate_conv(H, kv, B, T, g, st, nullptr, nullptr, 0, alpha_out, y_out, static_cast<char*>(ws), stream);
+  Carve c{static_cast<char*>(ws)};
+  GcWorkspace w = carve_gc(c, B * T, p->branches);
+  prof_begin();
+  prof_mark(stream, "gate_stats_kernel");
+  r = hip_status(engram::launch_gate_stats(H, kv, B * T, g, w.stats, stream), "gate statistics launch");
+  if (r != ENGRAM_OK) return r;
+  const int64_t stride = static_cast<int64_t>(1 + p->branches) * p->d;
+  return run_conv_commit(H, kv, stride, g.kvdtype, w.stats, 1, 1, B, T, g, st, nullptr, nullptr, 0, alpha_out,
+                         w.gamma, y_out, stream);
 }
 
 ENGRAM_API size_t engram_forward_workspace(int64_t B, int64_t T, const engram_layer* L) {
@@ -379,24 +421,49 @@ ENGRAM_API engram_status engram_forward(const int32_t* tokens, void* H, int64_t 
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
     return fail(ENGRAM_EINVAL, "forward: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
 
-  ForwardWorkspace f = carve_forward(static_cast<char*>(ws), n_tok, L);
+  Carve c{static_cast<char*>(ws)};
+  ForwardWorkspace f = carve_forward(c, n_tok, L);
   const int64_t d_mem = static_cast<int64_t>(L->tables.n_tables) * L->tables.dim;
-  const int64_t n_out = static_cast<int64_t>(1 + g.branches) * g.d;
+  const int M = g.branches, d = g.d;
+  const int64_t n_out = static_cast<int64_t>(1 + M) * d;
+  const int32_t* hist = st != nullptr ? st->ids : nullptr;
   prof_begin();
-  prof_mark(stream, "hash_kernel");
-  r = hip_status(engram::launch_hash(tokens, B, T, st != nullptr ? st->ids : nullptr, L->hash.proj, ha, f.z, stream),
-                 "hash launch");
+  // Steps 1-4: indices hashed inside the gather
+  prof_mark(stream, "gather_kernel<hashed>");
+  r = hip_status(engram::launch_hash_gather(tokens, B, T, hist, L->hash.proj, ha, ta, g.hdtype, f.e, stream),
+                 "hash+gather launch");
   if (r != ENGRAM_OK) return r;
-  prof_mark(stream, "gather_kernel");
-  r = hip_status(engram::launch_gather(f.z, n_tok, ta, g.hdtype, f.e, stream), "gather launch");
-  if (r != ENGRAM_OK) return r;
-  // the projections stay in float32: v is normalised and convolved next
-  prof_mark(stream, "gemm_bf16_kernel");
+  if (use_fused(L)) {
+    // Step 5 with the gate's sums folded into the product's epilogue; only v is stored
+    engram::ProjGateArgs pa{};
+    pa.e = static_cast<const uint16_t*>(f.e);
+    pa.w = static_cast<const uint16_t*>(L->w);
+    pa.H = static_cast<const uint16_t*>(H);
+    pa.v = f.kv;
+    pa.stats = f.stats;
+    pa.n_tok = n_tok;
+    pa.K = static_cast<int>(d_mem);
+    pa.N = static_cast<int>(n_out);
+    pa.d = d;
+    pa.M = M;
+    prof_mark(stream, "proj_gate_kernel");
+    r = hip_status(engram::launch_proj_gate(pa, stream), "projection launch");
+    if (r != ENGRAM_OK) return r;
+    const int q = d / engram::kProjGateTileF;
+    return run_conv_commit(H, f.kv, d, ENGRAM_F32, f.stats, q, q, B, T, g, st, tokens, L->hash.proj,
+                           L->hash.max_n, alpha_out, f.gamma, y_out, stream);
+  }
+  // Step 5 into float32 projections, then whole-row gate statistics
+  prof_mark(stream, "gemm_kernel");
   r = hip_status(engram::launch_project_kv(f.e, L->w, n_tok, d_mem, n_out, g.hdtype, ENGRAM_F32, f.kv, stream),
                  "project_kv launch");
   if (r != ENGRAM_OK) return r;
   g.kvdtype = ENGRAM_F32;
-  return run_gate_conv(H, f.kv, B, T, g, st, tokens, L->hash.proj, L->hash.max_n, alpha_out, y_out, f.gc, stream);
+  prof_mark(stream, "gate_stats_kernel");
+  r = hip_status(engram::launch_gate_stats(H, f.kv, n_tok, g, f.stats, stream), "gate statistics launch");
+  if (r != ENGRAM_OK) return r;
+  return run_conv_commit(H, f.kv, n_out, ENGRAM_F32, f.stats, 1, 1, B, T, g, st, tokens, L->hash.proj,
+                         L->hash.max_n, alpha_out, f.gamma, y_out, stream);
 }
 
 ENGRAM_API engram_status engram_profile_enable(int32_t on) {

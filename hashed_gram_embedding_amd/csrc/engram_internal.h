@@ -12,10 +12,20 @@ namespace engram {
 // Hash parameters by value: they travel in the kernel-argument segment.
 struct HashArgs {
   uint64_t mult[ENGRAM_MAX_TABLES][ENGRAM_MAX_ORDER];  // per table j: m_{n,k,i}
+  uint64_t inv[ENGRAM_MAX_TABLES];                     // floor((2^64-1) / p_j)
   uint32_t prime[ENGRAM_MAX_TABLES];
   int32_t order[ENGRAM_MAX_TABLES];                    // n of table j
   int32_t n_tables;
   int32_t max_n;
+};
+
+// Where the fused hash+gather reads its ids.
+struct HashSrc {
+  const int32_t* tokens;
+  const int32_t* proj;
+  const int32_t* hist;
+  int64_t T;
+  HashArgs a;
 };
 
 struct TableArgs {
@@ -53,22 +63,60 @@ hipError_t launch_hash(const int32_t* tokens, int64_t B, int64_t T, const int32_
 hipError_t launch_gather(const int32_t* z, int64_t n_tok, const TableArgs& ta, int out_dtype,
                          void* e, hipStream_t s);
 
+// Steps 1-4 in one kernel: rows are addressed by indices hashed in-thread.
+hipError_t launch_hash_gather(const int32_t* tokens, int64_t B, int64_t T, const int32_t* hist,
+                              const int32_t* proj, const HashArgs& a, const TableArgs& ta,
+                              int out_dtype, void* e, hipStream_t s);
+
 hipError_t launch_project_kv(const void* e, const void* w, int64_t n_tok, int64_t d_mem,
                              int64_t n_out, int in_dtype, int out_dtype, void* kv, hipStream_t s);
 
-// alpha[t][m] and gamma[t][m] = alpha / sqrt(alpha^2 mean(v^2) + eps) for every token.
-hipError_t launch_gate(const void* H, const void* kv, int64_t n_tok, const GateConvArgs& g,
-                       float* alpha, float* gamma, hipStream_t s);
+// Fused bf16 projection + gate statistics (see proj_gate.hip).
+struct ProjGateArgs {
+  const uint16_t* e;  // [n_tok][K] bf16
+  const uint16_t* w;  // [N][K] bf16, N = (1+M)*d
+  const uint16_t* H;  // [n_tok][M][d] bf16 (read only)
+  float* v;           // [n_tok][d]
+  float4* stats;      // [n_tok][N/128]
+  int64_t n_tok;
+  int K;
+  int N;
+  int d;
+  int M;
+  int tiles_f;  // set by the launcher
+  int tiles_t;  // set by the launcher
+};
+constexpr int kProjGateTileF = 128;  // feature columns per gate-statistics tile
+hipError_t launch_proj_gate(const ProjGateArgs& a, hipStream_t s);
 
-// c = conv(gamma * v), Y = SiLU(c) + alpha v, H += Y.
-hipError_t launch_conv(void* H, const void* kv, int64_t B, int64_t T, const GateConvArgs& g,
-                       const float* alpha, const float* gamma, const StateArgs* st,
-                       float* y_out, hipStream_t s);
+// Whole-row gate statistics from given projections: stats [n_tok][1+M].
+hipError_t launch_gate_stats(const void* H, const void* kv, int64_t n_tok, const GateConvArgs& g, float4* stats,
+                             hipStream_t s);
 
-// Writes the last conv inputs into the circular state, shifts ids (when
-// tokens/proj are given) and advances pos.
-hipError_t launch_state_commit(const void* kv, int64_t B, int64_t T, const GateConvArgs& g,
-                               const float* gamma, const StateArgs& st, const int32_t* tokens,
-                               const int32_t* proj, int32_t max_n, hipStream_t s);
+struct ConvArgs {
+  void* H;              // [B][T][M][d]
+  const void* v;        // v rows, row stride v_stride elements
+  int64_t v_stride;
+  const float4* stats;  // [B*T][nq]: qv v tiles, then qk tiles per branch
+  int qv;
+  int qk;
+  int nq;
+  int64_t B;
+  int64_t T;
+  GateConvArgs g;
+  StateArgs st;
+  int has_state;
+  float* alpha_out;     // [B*T][M] or null
+  float* gamma_out;     // [B*T][M] or null
+  float* y_out;         // [B][T][M][d] or null
+  int cg;               // set by the launcher
+};
+hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s);
+
+// Writes the chunk's last conv inputs into the circular state, shifts ids
+// (when tokens/proj are given) and advances pos.
+hipError_t launch_state_commit(const void* v, int64_t v_stride, int vdtype, int64_t B, int64_t T,
+                               const GateConvArgs& g, const float* gamma, const StateArgs& st,
+                               const int32_t* tokens, const int32_t* proj, int32_t max_n, hipStream_t s);
 
 }  // namespace engram

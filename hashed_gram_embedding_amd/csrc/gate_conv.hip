@@ -4,65 +4,63 @@
 //   u = RMSNorm(v~),  c_t = sum_j w[j] u_{t-(w-1-j)*dilation}   (depthwise, causal)
 //   Y = SiLU(c) + v~,  H <- H + Y
 //
-// Two kernels, because H is updated in place while the conv of token t needs
-// quantities of tokens up to (w-1)*dilation positions back:
-//  * gate_kernel reads h, k and v of every token and writes two scalars per
-//    (token, branch): alpha and gamma = alpha / sqrt(alpha^2 mean(v^2) + eps),
-//    so that u = gamma * v.  One wavefront per (token, branch); lanes
-//    accumulate sum h^2, k^2, h.k and v^2 over d and reduce by shuffles.
-//  * conv_kernel rebuilds u at the taps from gamma and v, applies the conv,
-//    SiLU and residual, and writes H.  It reads H only at the position it
-//    writes, so the in-place update cannot race with another token's gate.
-// A decode state supplies u for taps before the chunk (circular slots);
-// state_commit_kernel writes the chunk's last conv inputs back afterwards.
+// The gate needs four sums per (token, branch): h.h, k.k, h.k and v.v.  They
+// arrive as partial sums over column tiles ("gate statistics", one float4 per
+// token and tile: x = sum h^2, y = sum k^2, z = sum h.k, w = sum v^2) from the
+// fused projection kernel, or as whole-row sums from gate_stats_kernel when
+// the projections are given.  With RMSNorm(alpha v) = gamma v,
+//   gamma = alpha / sqrt(alpha^2 mean(v^2) + eps),
+// the conv input u is gamma * v.
+//
+// conv_kernel: a workgroup owns 32 tokens x 256 channels (fewer when d is not
+// a multiple of 256) of one branch of one
+// sequence.  It forms alpha and gamma for its rows and the (w-1)*dilation halo
+// rows before them, stages v of all those rows in LDS (the halo rows before a
+// continued sequence come from the decode state, already as u), then each
+// thread produces 4 channels of 8 tokens: the conv taps read LDS, SiLU and the
+// residual follow, and H is read and written only at the thread's own
+// positions.  All gate inputs were read (by the projection kernel or
+// gate_stats_kernel) before this kernel writes H, so the in-place update
+// cannot feed another token's gate.
 #include "device_util.h"
 #include "engram_internal.h"
 
 namespace engram {
 namespace {
 
-template <int HT>
-__device__ __forceinline__ void load8h(const void* base, int64_t off, float* f) {
-  if constexpr (HT == ENGRAM_BF16) {
-    unpack8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off), f);
+constexpr int TT = 32;   // output tokens per conv workgroup
+
+// Channels per conv workgroup: the largest of 256, 128, 64 that divides d.
+int conv_channels(int d) { return d % 256 == 0 ? 256 : (d % 128 == 0 ? 128 : 64); }
+
+template <int DT>
+__device__ __forceinline__ float4 load4(const void* base, int64_t off) {
+  if constexpr (DT == ENGRAM_BF16) {
+    const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off);
+    return make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xffff0000u),
+                       __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xffff0000u));
   } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-    const float4 a = p[0], b = p[1];
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
   }
 }
 
-template <int HT>
-__device__ __forceinline__ void store8h(void* base, int64_t off, const float* f) {
-  if constexpr (HT == ENGRAM_BF16) {
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) = pack8(f);
+template <int DT>
+__device__ __forceinline__ void store4(void* base, int64_t off, float4 f) {
+  if constexpr (DT == ENGRAM_BF16) {
+    const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(f.x)) | (static_cast<uint32_t>(f32_to_bf16(f.y)) << 16);
+    const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(f.z)) | (static_cast<uint32_t>(f32_to_bf16(f.w)) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + off) = make_uint2(lo, hi);
   } else {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + off);
-    p[0] = make_float4(f[0], f[1], f[2], f[3]);
-    p[1] = make_float4(f[4], f[5], f[6], f[7]);
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + off) = f;
   }
 }
 
-__device__ __forceinline__ void store8f(float* base, int64_t off, const float* f) {
-  float4* p = reinterpret_cast<float4*>(base + off);
-  p[0] = make_float4(f[0], f[1], f[2], f[3]);
-  p[1] = make_float4(f[4], f[5], f[6], f[7]);
-}
-
-__device__ __forceinline__ void load8f(const float* base, int64_t off, float* f) {
-  const float4* p = reinterpret_cast<const float4*>(base + off);
-  const float4 a = p[0], b = p[1];
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-}
-
+// Gate statistics from given projections: one wavefront per (token, branch).
+// stats[t][0].w = sum v^2 (written by the m = 0 wavefront), stats[t][1+m].xyz.
 template <int HT, int KT>
 __global__ void __launch_bounds__(256)
-gate_kernel(const void* __restrict__ H, const void* __restrict__ kv, int64_t n_tok, GateConvArgs g,
-            float* __restrict__ alpha, float* __restrict__ gamma) {
-  const int M = g.branches;
-  const int d = g.d;
+gate_stats_kernel(const void* __restrict__ H, const void* __restrict__ kv, int64_t n_tok, int M, int d,
+                  float4* __restrict__ stats) {
   const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (pair >= n_tok * M) return;
   const int lane = threadIdx.x & 63;
@@ -72,137 +70,186 @@ gate_kernel(const void* __restrict__ H, const void* __restrict__ kv, int64_t n_t
   const int64_t v_off = t * (1 + M) * d;
   const int64_t k_off = v_off + static_cast<int64_t>(1 + m) * d;
   float shh = 0.f, skk = 0.f, shk = 0.f, svv = 0.f;
-  for (int c = lane; c < (d >> 3); c += 64) {
-    float h[8], k[8], v[8];
-    load8h<HT>(H, h_off + c * 8, h);
-    load8h<KT>(kv, k_off + c * 8, k);
-    load8h<KT>(kv, v_off + c * 8, v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      shh += h[i] * h[i];
-      skk += k[i] * k[i];
-      shk += h[i] * k[i];
-      svv += v[i] * v[i];
-    }
+  for (int c = lane * 4; c < d; c += 256) {
+    const float4 h = load4<HT>(H, h_off + c);
+    const float4 k = load4<KT>(kv, k_off + c);
+    const float4 v = load4<KT>(kv, v_off + c);
+    shh += h.x * h.x + h.y * h.y + h.z * h.z + h.w * h.w;
+    skk += k.x * k.x + k.y * k.y + k.z * k.z + k.w * k.w;
+    shk += h.x * k.x + h.y * k.y + h.z * k.z + h.w * k.w;
+    svv += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
   shh = wave_sum(shh);
   skk = wave_sum(skk);
   shk = wave_sum(shk);
   svv = wave_sum(svv);
   if (lane == 0) {
-    const float inv_d = 1.0f / static_cast<float>(d);
-    const float rh = 1.0f / sqrtf(shh * inv_d + g.eps);
-    const float rk = 1.0f / sqrtf(skk * inv_d + g.eps);
-    const float logit = shk * rh * rk / sqrtf(static_cast<float>(d));
-    const float a = 1.0f / (1.0f + expf(-logit));
-    alpha[pair] = a;
-    gamma[pair] = a / sqrtf(a * a * (svv * inv_d) + g.eps);
+    stats[t * (1 + M) + 1 + m] = make_float4(shh, skk, shk, 0.f);
+    if (m == 0) stats[t * (1 + M)] = make_float4(0.f, 0.f, 0.f, svv);
   }
 }
 
-template <int HT, int KT>
+template <int HT, int VT>
 __global__ void __launch_bounds__(256)
-conv_kernel(void* __restrict__ H, const void* __restrict__ kv, int64_t B, int64_t T, GateConvArgs g,
-            const float* __restrict__ alpha, const float* __restrict__ gamma, StateArgs st,
-            int has_state, float* __restrict__ y_out) {
+conv_kernel(ConvArgs a) {
+  extern __shared__ float4 tile[];  // [rows][cg] staged v (or state u), 4 channels per float4
+  __shared__ float alpha_s[TT + ENGRAM_MAX_CONV_SPAN];
+  __shared__ float scale_s[TT + ENGRAM_MAX_CONV_SPAN];
+  const GateConvArgs& g = a.g;
   const int M = g.branches;
   const int d = g.d;
-  const int chunks = d >> 3;
-  const int64_t total = B * T * M * chunks;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= total) return;
-  const int c8 = static_cast<int>(gid % chunks);
-  const int64_t pm = gid / chunks;
-  const int m = static_cast<int>(pm % M);
-  const int64_t bt = pm / M;
-  const int64_t b = bt / T;
-  const int64_t t = bt - b * T;
-  const int span = (g.kernel_w - 1) * g.dilation;
-  const int64_t row_kv = static_cast<int64_t>(1 + M) * d;
-  const int ch0 = c8 * 8;
-  const int32_t pos0 = has_state ? st.pos[b] : 0;
+  const int kw = g.kernel_w;
+  const int span = (kw - 1) * g.dilation;
+  const int R = TT + span;
+  const int64_t T = a.T;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TT;
+  const int b = blockIdx.y / M;
+  const int m = blockIdx.y - b * M;
+  const int cg = a.cg;               // 4-channel groups per workgroup (64, 32 or 16)
+  const int c_base = blockIdx.z * cg * 4;
+  const int tid = threadIdx.x;
+  const int32_t pos0 = a.has_state ? a.st.pos[b] : 0;
 
-  float c[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = 0.f;
-  float vt[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) vt[i] = 0.f;
-  for (int j = 0; j < g.kernel_w; ++j) {
-    const int back = (g.kernel_w - 1 - j) * g.dilation;
-    const int64_t s = t - back;
-    float u[8];
-    if (s >= 0) {
-      const int64_t bs = b * T + s;
-      load8h<KT>(kv, bs * row_kv + ch0, u);
-      if (back == 0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vt[i] = u[i];
+  // phase 0: alpha and gamma of every staged row
+  if (tid < R) {
+    const int64_t t = t0 - span + tid;
+    float al = 0.f, sc = 0.f;
+    if (t >= 0 && t < T) {
+      const float4* st = a.stats + (static_cast<int64_t>(b) * T + t) * a.nq;
+      float svv = 0.f, shh = 0.f, skk = 0.f, shk = 0.f;
+      for (int q = 0; q < a.qv; ++q) svv += st[q].w;
+      const float4* sk = st + a.qv + m * a.qk;
+      for (int q = 0; q < a.qk; ++q) {
+        shh += sk[q].x;
+        skk += sk[q].y;
+        shk += sk[q].z;
       }
-      const float gm = gamma[bs * M + m];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) u[i] *= gm;
-    } else if (has_state) {
-      int slot = static_cast<int>((static_cast<int64_t>(pos0) + s) % span);
-      if (slot < 0) slot += span;
-      load8f(st.conv, ((b * M + m) * span + slot) * static_cast<int64_t>(d) + ch0, u);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) u[i] = 0.f;
+      const float inv_d = 1.0f / static_cast<float>(d);
+      const float rh = 1.0f / sqrtf(shh * inv_d + g.eps);
+      const float rk = 1.0f / sqrtf(skk * inv_d + g.eps);
+      const float logit = shk * rh * rk / sqrtf(static_cast<float>(d));
+      al = 1.0f / (1.0f + expf(-logit));
+      sc = al / sqrtf(al * al * (svv * inv_d) + g.eps);
+      if (blockIdx.z == 0 && tid >= span) {
+        const int64_t o = (static_cast<int64_t>(b) * T + t) * M + m;
+        if (a.alpha_out != nullptr) a.alpha_out[o] = al;
+        if (a.gamma_out != nullptr) a.gamma_out[o] = sc;
+      }
+    } else if (t < 0 && a.has_state) {
+      sc = 1.0f;  // the state holds u itself
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] += g.conv_w[(static_cast<int64_t>(m) * d + ch0 + i) * g.kernel_w + j] * u[i];
+    alpha_s[tid] = al;
+    scale_s[tid] = sc;
   }
-  const float a = alpha[bt * M + m];
-  float y[8], h[8];
-  const int64_t h_off = pm * d + ch0;
-  load8h<HT>(H, h_off, h);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    y[i] = c[i] / (1.0f + expf(-c[i])) + a * vt[i];
-    h[i] += y[i];
+
+  // phase 1: stage v rows (or state u rows) in LDS
+  for (int idx = tid; idx < R * cg; idx += 256) {
+    const int r = idx / cg;
+    const int q = idx - r * cg;
+    const int64_t t = t0 - span + r;
+    const int c = c_base + q * 4;
+    float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t >= 0 && t < T) {
+      val = load4<VT>(a.v, (static_cast<int64_t>(b) * T + t) * a.v_stride + c);
+    } else if (t < 0 && a.has_state) {
+      int slot = static_cast<int>((static_cast<int64_t>(pos0) + t) % span);
+      if (slot < 0) slot += span;
+      val = *reinterpret_cast<const float4*>(a.st.conv + ((static_cast<int64_t>(b) * M + m) * span + slot) * d + c);
+    }
+    tile[idx] = val;
   }
-  store8h<HT>(H, h_off, h);
-  if (y_out != nullptr) store8f(y_out, h_off, y);
+  __syncthreads();
+
+  // phase 2: conv taps, SiLU, residual for 4 channels x TT*cg/256 tokens per thread
+  const int q = tid % cg;
+  const int c = c_base + q * 4;
+  float wt[4][ENGRAM_MAX_KERNEL_W];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < ENGRAM_MAX_KERNEL_W; ++j)
+      wt[i][j] = j < kw ? g.conv_w[(static_cast<int64_t>(m) * d + c + i) * kw + j] : 0.f;
+  for (int k = tid / cg; k < TT; k += 256 / cg) {
+    const int64_t t = t0 + k;
+    if (t >= T) break;
+    const int r = span + k;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < ENGRAM_MAX_KERNEL_W; ++j) {
+      if (j < kw) {
+        const int rs = r - (kw - 1 - j) * g.dilation;
+        const float s = scale_s[rs];
+        const float4 u = tile[rs * cg + q];
+        acc.x += wt[0][j] * (s * u.x);
+        acc.y += wt[1][j] * (s * u.y);
+        acc.z += wt[2][j] * (s * u.z);
+        acc.w += wt[3][j] * (s * u.w);
+      }
+    }
+    const float al = alpha_s[r];
+    const float4 v = tile[r * cg + q];
+    float4 y;
+    y.x = acc.x / (1.0f + expf(-acc.x)) + al * v.x;
+    y.y = acc.y / (1.0f + expf(-acc.y)) + al * v.y;
+    y.z = acc.z / (1.0f + expf(-acc.z)) + al * v.z;
+    y.w = acc.w / (1.0f + expf(-acc.w)) + al * v.w;
+    const int64_t ho = ((static_cast<int64_t>(b) * T + t) * M + m) * d + c;
+    float4 h = load4<HT>(a.H, ho);
+    h.x += y.x;
+    h.y += y.y;
+    h.z += y.z;
+    h.w += y.w;
+    store4<HT>(a.H, ho, h);
+    if (a.y_out != nullptr) *reinterpret_cast<float4*>(a.y_out + ho) = y;
+  }
 }
 
-template <int KT>
+// After the conv: the chunk's last (w-1)*dilation conv inputs go to their
+// circular slots, the last N-1 compressed ids shift into the history, and pos
+// advances.  One workgroup per sequence; pos is written after the block has
+// read it everywhere.
+template <int VT>
 __global__ void __launch_bounds__(256)
-state_commit_kernel(const void* __restrict__ kv, int64_t T, GateConvArgs g,
+state_commit_kernel(const void* __restrict__ v, int64_t v_stride, int64_t T, GateConvArgs g,
                     const float* __restrict__ gamma, StateArgs st, const int32_t* __restrict__ tokens,
                     const int32_t* __restrict__ proj, int32_t max_n) {
   const int64_t b = blockIdx.x;
   const int M = g.branches;
   const int d = g.d;
-  const int chunks = d >> 3;
   const int span = (g.kernel_w - 1) * g.dilation;
   const int32_t pos0 = st.pos[b];
   const int L = static_cast<int>(T < span ? T : span);
-  const int64_t row_kv = static_cast<int64_t>(1 + M) * d;
-  const int total = M * L * chunks;
+  const int c4 = d / 4;
+  const int total = M * L * c4;
   for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int c8 = idx % chunks;
-    const int mq = idx / chunks;
+    const int cq = idx % c4;
+    const int mq = idx / c4;
     const int q = mq % L;
     const int m = mq / L;
     const int64_t p = T - L + q;
     const int slot = static_cast<int>((static_cast<int64_t>(pos0) + p) % span);
     const int64_t bs = b * T + p;
-    float u[8];
-    load8h<KT>(kv, bs * row_kv + c8 * 8, u);
+    float4 u = load4<VT>(v, bs * v_stride + cq * 4);
     const float gm = gamma[bs * M + m];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) u[i] *= gm;
-    store8f(st.conv, ((b * M + m) * span + slot) * static_cast<int64_t>(d) + c8 * 8, u);
+    u.x *= gm;
+    u.y *= gm;
+    u.z *= gm;
+    u.w *= gm;
+    *reinterpret_cast<float4*>(st.conv + ((b * M + m) * span + slot) * static_cast<int64_t>(d) + cq * 4) = u;
   }
   if (threadIdx.x == 0 && st.ids != nullptr && tokens != nullptr) {
     const int hl = max_n - 1;
-    int32_t old[ENGRAM_MAX_ORDER];
-    for (int i = 0; i < hl; ++i) old[i] = st.ids[b * hl + i];
-    for (int i = 0; i < hl; ++i) {
-      const int64_t idx = T + i;  // index in (old ids ++ chunk ids)
-      st.ids[b * hl + i] = idx < hl ? old[idx] : proj[tokens[b * T + idx - hl]];
+    int32_t next[ENGRAM_MAX_ORDER];
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDER - 1; ++i) {
+      if (i < hl) {
+        const int64_t idx = T + i;  // index in (old ids ++ chunk ids)
+        next[i] = idx < hl ? st.ids[b * hl + idx] : proj[tokens[b * T + idx - hl]];
+      }
     }
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDER - 1; ++i)
+      if (i < hl) st.ids[b * hl + i] = next[i];
   }
   __syncthreads();
   if (threadIdx.x == 0) st.pos[b] = pos0 + static_cast<int32_t>(T);
@@ -210,53 +257,51 @@ state_commit_kernel(const void* __restrict__ kv, int64_t T, GateConvArgs g,
 
 }  // namespace
 
-hipError_t launch_gate(const void* H, const void* kv, int64_t n_tok, const GateConvArgs& g,
-                       float* alpha, float* gamma, hipStream_t s) {
+hipError_t launch_gate_stats(const void* H, const void* kv, int64_t n_tok, const GateConvArgs& g, float4* stats,
+                             hipStream_t s) {
   const int64_t pairs = n_tok * g.branches;
   if (pairs == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((pairs + 3) / 4));
-  const dim3 block(256);
   if (g.hdtype == ENGRAM_BF16 && g.kvdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((gate_kernel<ENGRAM_BF16, ENGRAM_BF16>), grid, block, 0, s, H, kv, n_tok, g, alpha, gamma);
+    hipLaunchKernelGGL((gate_stats_kernel<ENGRAM_BF16, ENGRAM_BF16>), grid, dim3(256), 0, s, H, kv, n_tok,
+                       g.branches, g.d, stats);
   else if (g.hdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((gate_kernel<ENGRAM_BF16, ENGRAM_F32>), grid, block, 0, s, H, kv, n_tok, g, alpha, gamma);
+    hipLaunchKernelGGL((gate_stats_kernel<ENGRAM_BF16, ENGRAM_F32>), grid, dim3(256), 0, s, H, kv, n_tok,
+                       g.branches, g.d, stats);
   else
-    hipLaunchKernelGGL((gate_kernel<ENGRAM_F32, ENGRAM_F32>), grid, block, 0, s, H, kv, n_tok, g, alpha, gamma);
+    hipLaunchKernelGGL((gate_stats_kernel<ENGRAM_F32, ENGRAM_F32>), grid, dim3(256), 0, s, H, kv, n_tok,
+                       g.branches, g.d, stats);
   return hipGetLastError();
 }
 
-hipError_t launch_conv(void* H, const void* kv, int64_t B, int64_t T, const GateConvArgs& g,
-                       const float* alpha, const float* gamma, const StateArgs* st,
-                       float* y_out, hipStream_t s) {
-  const int64_t total = B * T * g.branches * (g.d / 8);
-  if (total == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
-  const dim3 block(256);
-  StateArgs sa{};
-  if (st != nullptr) sa = *st;
-  const int has = st != nullptr;
-  if (g.hdtype == ENGRAM_BF16 && g.kvdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((conv_kernel<ENGRAM_BF16, ENGRAM_BF16>), grid, block, 0, s, H, kv, B, T, g, alpha, gamma, sa,
-                       has, y_out);
-  else if (g.hdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((conv_kernel<ENGRAM_BF16, ENGRAM_F32>), grid, block, 0, s, H, kv, B, T, g, alpha, gamma, sa,
-                       has, y_out);
+hipError_t launch_conv(const ConvArgs& in, int vdtype, hipStream_t s) {
+  if (in.B * in.T == 0) return hipSuccess;
+  ConvArgs a = in;
+  const int ct = conv_channels(a.g.d);
+  a.cg = ct / 4;
+  const int span = (a.g.kernel_w - 1) * a.g.dilation;
+  const size_t lds = static_cast<size_t>(TT + span) * a.cg * sizeof(float4);
+  const dim3 grid(static_cast<unsigned>((a.T + TT - 1) / TT), static_cast<unsigned>(a.B * a.g.branches),
+                  static_cast<unsigned>(a.g.d / ct));
+  if (a.g.hdtype == ENGRAM_BF16 && vdtype == ENGRAM_BF16)
+    hipLaunchKernelGGL((conv_kernel<ENGRAM_BF16, ENGRAM_BF16>), grid, dim3(256), lds, s, a);
+  else if (a.g.hdtype == ENGRAM_BF16)
+    hipLaunchKernelGGL((conv_kernel<ENGRAM_BF16, ENGRAM_F32>), grid, dim3(256), lds, s, a);
   else
-    hipLaunchKernelGGL((conv_kernel<ENGRAM_F32, ENGRAM_F32>), grid, block, 0, s, H, kv, B, T, g, alpha, gamma, sa,
-                       has, y_out);
+    hipLaunchKernelGGL((conv_kernel<ENGRAM_F32, ENGRAM_F32>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_state_commit(const void* kv, int64_t B, int64_t T, const GateConvArgs& g,
-                               const float* gamma, const StateArgs& st, const int32_t* tokens,
-                               const int32_t* proj, int32_t max_n, hipStream_t s) {
+hipError_t launch_state_commit(const void* v, int64_t v_stride, int vdtype, int64_t B, int64_t T,
+                               const GateConvArgs& g, const float* gamma, const StateArgs& st,
+                               const int32_t* tokens, const int32_t* proj, int32_t max_n, hipStream_t s) {
   if (B == 0 || T == 0) return hipSuccess;
-  if (g.kvdtype == ENGRAM_BF16)
+  if (vdtype == ENGRAM_BF16)
     hipLaunchKernelGGL(state_commit_kernel<ENGRAM_BF16>, dim3(static_cast<unsigned>(B)), dim3(256), 0, s,
-                       kv, T, g, gamma, st, tokens, proj, max_n);
+                       v, v_stride, T, g, gamma, st, tokens, proj, max_n);
   else
     hipLaunchKernelGGL(state_commit_kernel<ENGRAM_F32>, dim3(static_cast<unsigned>(B)), dim3(256), 0, s,
-                       kv, T, g, gamma, st, tokens, proj, max_n);
+                       v, v_stride, T, g, gamma, st, tokens, proj, max_n);
   return hipGetLastError();
 }
 

@@ -12,8 +12,12 @@
 // bf16, 32 bytes for f32, 8 bytes for int8.  Threads are ordered (token,
 // table, chunk), so the 8 threads that cover a 128-byte bf16 row are
 // adjacent and each wavefront writes a contiguous 1 KiB span of e.
+//
+// Inside the layer forward the row index is hashed in the same thread
+// (Steps 1-3), so the indices never go through memory.
 #include "device_util.h"
 #include "engram_internal.h"
+#include "hash_device.h"
 
 namespace engram {
 namespace {
@@ -42,9 +46,10 @@ __device__ __forceinline__ void load8(const void* base, const float* scale, int6
   }
 }
 
-template <int IN, int OUT>
+template <int IN, int OUT, bool HASHED>
 __global__ void __launch_bounds__(256)
-gather_kernel(const int32_t* __restrict__ z, int64_t n_tok, TableArgs ta, void* __restrict__ e) {
+gather_kernel(const int32_t* __restrict__ z, int64_t n_tok, TableArgs ta, void* __restrict__ e,
+              HashSrc hs) {
   const int nt = ta.n_tables;
   const int chunks = ta.dim >> 3;
   const int64_t total = n_tok * nt * chunks;
@@ -53,7 +58,15 @@ gather_kernel(const int32_t* __restrict__ z, int64_t n_tok, TableArgs ta, void* 
   const int c = static_cast<int>(gid % chunks);
   const int64_t tj = gid / chunks;
   const int j = static_cast<int>(tj % nt);
-  int64_t row = ta.row_offset[j] + z[tj];
+  int32_t zj;
+  if constexpr (HASHED) {
+    const int64_t bt = tj / nt;
+    const int64_t b = bt / hs.T;
+    zj = hash_index(hs.tokens, hs.proj, hs.hist, hs.a, j, b, bt - b * hs.T, hs.T);
+  } else {
+    zj = z[tj];
+  }
+  int64_t row = ta.row_offset[j] + zj;
   const void* src = ta.rows;
   const float* scale = ta.scale;
   if (ta.cache_slot != nullptr) {
@@ -79,29 +92,42 @@ gather_kernel(const int32_t* __restrict__ z, int64_t n_tok, TableArgs ta, void* 
   }
 }
 
-template <int IN>
+template <int IN, bool HASHED>
 hipError_t launch_in(const int32_t* z, int64_t n_tok, const TableArgs& ta, int out, void* e,
-                     hipStream_t s) {
+                     const HashSrc& hs, hipStream_t s) {
   const int64_t total = n_tok * ta.n_tables * (ta.dim / 8);
   if (total == 0) return hipSuccess;
   const int threads = 256;
   const dim3 grid(static_cast<unsigned>((total + threads - 1) / threads));
   if (out == ENGRAM_BF16)
-    hipLaunchKernelGGL((gather_kernel<IN, ENGRAM_BF16>), grid, dim3(threads), 0, s, z, n_tok, ta, e);
+    hipLaunchKernelGGL((gather_kernel<IN, ENGRAM_BF16, HASHED>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
   else
-    hipLaunchKernelGGL((gather_kernel<IN, ENGRAM_F32>), grid, dim3(threads), 0, s, z, n_tok, ta, e);
+    hipLaunchKernelGGL((gather_kernel<IN, ENGRAM_F32, HASHED>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
   return hipGetLastError();
+}
+
+template <bool HASHED>
+hipError_t dispatch(const int32_t* z, int64_t n_tok, const TableArgs& ta, int out_dtype, void* e,
+                    const HashSrc& hs, hipStream_t s) {
+  switch (ta.dtype) {
+    case ENGRAM_BF16: return launch_in<ENGRAM_BF16, HASHED>(z, n_tok, ta, out_dtype, e, hs, s);
+    case ENGRAM_F32: return launch_in<ENGRAM_F32, HASHED>(z, n_tok, ta, out_dtype, e, hs, s);
+    default: return launch_in<ENGRAM_I8, HASHED>(z, n_tok, ta, out_dtype, e, hs, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gather(const int32_t* z, int64_t n_tok, const TableArgs& ta, int out_dtype,
                          void* e, hipStream_t s) {
-  switch (ta.dtype) {
-    case ENGRAM_BF16: return launch_in<ENGRAM_BF16>(z, n_tok, ta, out_dtype, e, s);
-    case ENGRAM_F32: return launch_in<ENGRAM_F32>(z, n_tok, ta, out_dtype, e, s);
-    default: return launch_in<ENGRAM_I8>(z, n_tok, ta, out_dtype, e, s);
-  }
+  return dispatch<false>(z, n_tok, ta, out_dtype, e, HashSrc{}, s);
+}
+
+hipError_t launch_hash_gather(const int32_t* tokens, int64_t B, int64_t T, const int32_t* hist,
+                              const int32_t* proj, const HashArgs& a, const TableArgs& ta,
+                              int out_dtype, void* e, hipStream_t s) {
+  HashSrc hs{tokens, proj, hist, T, a};
+  return dispatch<true>(nullptr, B * T, ta, out_dtype, e, hs, s);
 }
 
 }  // namespace engram

@@ -2,12 +2,11 @@
 // principle": vocabulary projection, suffix n-grams and the K-head
 // multiplicative-XOR hash into prime-sized tables.
 //
-// One thread per (token, table j).  The thread projects the n ids of its
-// suffix window through P (reading the decode history, or pad id 0, before
-// the sequence start), XORs the 64-bit wrapped products x' * m_{n,k,i} and
-// reduces modulo the table's prime.  The table index is the fastest-varying
-// thread coordinate, so the z stores of a wavefront are contiguous.
+// One thread per (token, table j), table index fastest so that the z stores
+// of a wavefront are contiguous.  The per-thread work (up to N id loads, N
+// 64-bit products, one Barrett reduction) is described in hash_device.h.
 #include "engram_internal.h"
+#include "hash_device.h"
 
 namespace engram {
 namespace {
@@ -24,20 +23,7 @@ hash_kernel(const int32_t* __restrict__ tokens, int64_t B, int64_t T,
   const int64_t bt = gid / nt;
   const int64_t b = bt / T;
   const int64_t t = bt - b * T;
-  const int n = a.order[j];
-  const int hist_len = a.max_n - 1;
-  uint64_t acc = 0;
-  for (int i = 0; i < n; ++i) {
-    const int64_t p = t - i;
-    uint32_t x = 0;
-    if (p >= 0) {
-      x = static_cast<uint32_t>(proj[tokens[b * T + p]]);
-    } else if (hist != nullptr) {
-      x = static_cast<uint32_t>(hist[b * hist_len + hist_len + p]);
-    }
-    acc ^= static_cast<uint64_t>(x) * a.mult[j][i];
-  }
-  z[gid] = static_cast<int32_t>(acc % static_cast<uint64_t>(a.prime[j]));
+  z[gid] = hash_index(tokens, proj, hist, a, j, b, t, T);
 }
 
 }  // namespace

@@ -1,0 +1,46 @@
+// Device-side Steps 1-3 ("DeepSeek Engram series guide", section "Engram
+// working principle"): projection, suffix n-gram and multiplicative-XOR hash
+// of one (token, table) pair, shared by the hash and the fused hash+gather
+// kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "engram_internal.h"
+
+namespace engram {
+
+// x mod p for a 64-bit x and p < 2^31, with inv = floor((2^64-1)/p):
+// q = floor(x * inv / 2^64) is floor(x/p) or one less, so r = x - q p lies in
+// [0, 2p) and one conditional subtraction finishes (Barrett reduction).
+__device__ __forceinline__ uint32_t mod_prime(uint64_t x, uint32_t p, uint64_t inv) {
+  const uint64_t q = __umul64hi(x, inv);
+  const uint64_t r = x - q * static_cast<uint64_t>(p);
+  return static_cast<uint32_t>(r >= p ? r - p : r);
+}
+
+// z of table j at position t of sequence b: XOR over i < n of
+// x'_{t-i} * m_{j,i} (wrapping in 64 bits), then mod p_j.  Positions before the
+// sequence start read the history (oldest first) or the pad id 0.
+__device__ __forceinline__ int32_t hash_index(const int32_t* __restrict__ tokens,
+                                              const int32_t* __restrict__ proj,
+                                              const int32_t* __restrict__ hist, const HashArgs& a,
+                                              int j, int64_t b, int64_t t, int64_t T) {
+  const int n = a.order[j];
+  const int hist_len = a.max_n - 1;
+  uint64_t acc = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t p = t - i;
+    uint32_t x = 0;
+    if (p >= 0) {
+      x = static_cast<uint32_t>(proj[tokens[b * T + p]]);
+    } else if (hist != nullptr) {
+      x = static_cast<uint32_t>(hist[b * hist_len + hist_len + p]);
+    }
+    acc ^= static_cast<uint64_t>(x) * a.mult[j][i];
+  }
+  return static_cast<int32_t>(mod_prime(acc, a.prime[j], a.inv[j]));
+}
+
+}  // namespace engram

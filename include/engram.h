@@ -54,7 +54,7 @@ extern "C" {
 #define ENGRAM_MAX_TABLES 32 /* (N-1)*K */
 #define ENGRAM_MAX_ORDER 4   /* N */
 #define ENGRAM_MAX_KERNEL_W 8
-#define ENGRAM_MAX_CONV_SPAN 32 /* (kernel_w - 1) * dilation */
+#define ENGRAM_MAX_CONV_SPAN 24 /* (kernel_w - 1) * dilation */
 
 typedef enum engram_status {
   ENGRAM_OK = 0,
@@ -111,7 +111,7 @@ typedef struct engram_gate_conv_params {
   int32_t d;              /* hidden width per branch, a multiple of 64             */
   int32_t branches;       /* M >= 1 residual branches                              */
   int32_t kernel_w;       /* conv taps w, 1..ENGRAM_MAX_KERNEL_W (pages: 4)         */
-  int32_t dilation;       /* conv dilation (pages: N); (w-1)*dilation <= 32         */
+  int32_t dilation;       /* conv dilation (pages: N); (w-1)*dilation <= 24         */
   float eps;              /* RMSNorm epsilon                                       */
   engram_dtype hdtype;    /* ENGRAM_F32 or ENGRAM_BF16: storage type of H, kv, the
                              projection weights and the gathered rows              */
