@@ -109,7 +109,6 @@ struct ConvArgs {
   float* alpha_out;     // [B*T][M] or null
   float* gamma_out;     // [B*T][M] or null
   float* y_out;         // [B][T][M][d] or null
-  int cg;               // set by the launcher
 };
 hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s);
 

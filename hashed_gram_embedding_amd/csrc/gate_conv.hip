@@ -89,10 +89,11 @@ gate_stats_kernel(const void* __restrict__ H, const void* __restrict__ kv, int64
   }
 }
 
-template <int HT, int VT>
+template <int HT, int VT, int CG>
 __global__ void __launch_bounds__(256)
 conv_kernel(ConvArgs a) {
-  extern __shared__ float4 tile[];  // [rows][cg] staged v (or state u), 4 channels per float4
+  constexpr int TPT = TT * CG / 256;  // output tokens per thread
+  extern __shared__ float4 lds[];     // [R][CG] staged v (or state u), then [R][qv+qk] statistics
   __shared__ float alpha_s[TT + ENGRAM_MAX_CONV_SPAN];
   __shared__ float scale_s[TT + ENGRAM_MAX_CONV_SPAN];
   const GateConvArgs& g = a.g;
@@ -105,24 +106,93 @@ conv_kernel(ConvArgs a) {
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TT;
   const int b = blockIdx.y / M;
   const int m = blockIdx.y - b * M;
-  const int cg = a.cg;               // 4-channel groups per workgroup (64, 32 or 16)
-  const int c_base = blockIdx.z * cg * 4;
+  const int c_base = blockIdx.z * CG * 4;
   const int tid = threadIdx.x;
   const int32_t pos0 = a.has_state ? a.st.pos[b] : 0;
+  float4* tile = lds;
+  float4* sstat = lds + R * CG;
+  const int nqb = a.qv + a.qk;  // statistics this branch needs per row
+
+  // phase 1: stage v rows (or state u rows) and the rows' gate statistics in
+  // LDS.  The loops have fixed trip counts (bounded by the largest halo) and
+  // are unrolled, so every load is in flight before the first one is waited on.
+  constexpr int kMaxRows = TT + ENGRAM_MAX_CONV_SPAN;
+  constexpr int kTileIters = (kMaxRows * CG + 255) / 256;
+  constexpr int kStatIters = (kMaxRows * 64 + 255) / 256;  // up to 64 statistics per row
+  const int64_t row0 = static_cast<int64_t>(b) * T;
+  {
+    // v rows of this chunk: the address is clamped into the chunk (always a
+    // valid load) and the value replaced by 0 outside it, so there is no
+    // branch around the loads
+    float4 val[kTileIters];
+#pragma unroll
+    for (int n = 0; n < kTileIters; ++n) {
+      const int idx = tid + n * 256;
+      const int r = idx / CG;
+      const int q = idx - r * CG;
+      const int64_t t = t0 - span + r;
+      const int64_t tc = t < 0 ? 0 : (t >= T ? T - 1 : t);
+      val[n] = load4<VT>(a.v, (row0 + tc) * a.v_stride + c_base + q * 4);
+    }
+#pragma unroll
+    for (int n = 0; n < kTileIters; ++n) {
+      const int idx = tid + n * 256;
+      const int r = idx / CG;
+      const int64_t t = t0 - span + r;
+      const bool inside = t >= 0 && t < T;
+      if (r < R && (inside || !(t < 0 && a.has_state)))
+        tile[idx] = inside ? val[n] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  if (a.has_state && t0 < span) {
+    // rows before the chunk start come from the decode state (already u)
+    for (int idx = tid; idx < span * CG; idx += 256) {
+      const int r = idx / CG;
+      const int q = idx - r * CG;
+      const int64_t t = t0 - span + r;
+      if (t < 0) {
+        int slot = static_cast<int>((static_cast<int64_t>(pos0) + t) % span);
+        if (slot < 0) slot += span;
+        tile[idx] = *reinterpret_cast<const float4*>(a.st.conv + ((static_cast<int64_t>(b) * M + m) * span + slot) * d +
+                                                     c_base + q * 4);
+      }
+    }
+  }
+  {
+    float4 val[kStatIters];
+#pragma unroll
+    for (int n = 0; n < kStatIters; ++n) {
+      const int idx = tid + n * 256;
+      const int r = idx / nqb;
+      const int q = idx - r * nqb;
+      const int64_t t = t0 - span + r;
+      const int64_t tc = t < 0 ? 0 : (t >= T ? T - 1 : t);
+      const int qc = q < nqb ? q : 0;
+      const int src = qc < a.qv ? qc : a.qv + m * a.qk + (qc - a.qv);
+      val[n] = a.stats[(row0 + tc) * a.nq + src];
+    }
+#pragma unroll
+    for (int n = 0; n < kStatIters; ++n) {
+      const int idx = tid + n * 256;
+      const int r = idx / nqb;
+      const int64_t t = t0 - span + r;
+      if (idx < R * nqb) sstat[idx] = (t >= 0 && t < T) ? val[n] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __syncthreads();
 
   // phase 0: alpha and gamma of every staged row
   if (tid < R) {
     const int64_t t = t0 - span + tid;
     float al = 0.f, sc = 0.f;
     if (t >= 0 && t < T) {
-      const float4* st = a.stats + (static_cast<int64_t>(b) * T + t) * a.nq;
+      const float4* st = sstat + tid * nqb;
       float svv = 0.f, shh = 0.f, skk = 0.f, shk = 0.f;
       for (int q = 0; q < a.qv; ++q) svv += st[q].w;
-      const float4* sk = st + a.qv + m * a.qk;
-      for (int q = 0; q < a.qk; ++q) {
-        shh += sk[q].x;
-        skk += sk[q].y;
-        shk += sk[q].z;
+      for (int q = a.qv; q < nqb; ++q) {
+        shh += st[q].x;
+        skk += st[q].y;
+        shk += st[q].z;
       }
       const float inv_d = 1.0f / static_cast<float>(d);
       const float rh = 1.0f / sqrtf(shh * inv_d + g.eps);
@@ -142,26 +212,10 @@ conv_kernel(ConvArgs a) {
     scale_s[tid] = sc;
   }
 
-  // phase 1: stage v rows (or state u rows) in LDS
-  for (int idx = tid; idx < R * cg; idx += 256) {
-    const int r = idx / cg;
-    const int q = idx - r * cg;
-    const int64_t t = t0 - span + r;
-    const int c = c_base + q * 4;
-    float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t >= 0 && t < T) {
-      val = load4<VT>(a.v, (static_cast<int64_t>(b) * T + t) * a.v_stride + c);
-    } else if (t < 0 && a.has_state) {
-      int slot = static_cast<int>((static_cast<int64_t>(pos0) + t) % span);
-      if (slot < 0) slot += span;
-      val = *reinterpret_cast<const float4*>(a.st.conv + ((static_cast<int64_t>(b) * M + m) * span + slot) * d + c);
-    }
-    tile[idx] = val;
-  }
-  __syncthreads();
-
-  // phase 2: conv taps, SiLU, residual for 4 channels x TT*cg/256 tokens per thread
-  const int q = tid % cg;
+  // conv weights of this thread's 4 channels, and its H values (loads issued
+  // before the barrier so that they overlap the gate arithmetic)
+  const int q = tid % CG;
+  const int k0 = tid / CG;
   const int c = c_base + q * 4;
   float wt[4][ENGRAM_MAX_KERNEL_W];
 #pragma unroll
@@ -169,7 +223,19 @@ conv_kernel(ConvArgs a) {
 #pragma unroll
     for (int j = 0; j < ENGRAM_MAX_KERNEL_W; ++j)
       wt[i][j] = j < kw ? g.conv_w[(static_cast<int64_t>(m) * d + c + i) * kw + j] : 0.f;
-  for (int k = tid / cg; k < TT; k += 256 / cg) {
+  float4 h[TPT];
+#pragma unroll
+  for (int n = 0; n < TPT; ++n) {
+    const int64_t t = t0 + k0 + n * (256 / CG);
+    h[n] = t < T ? load4<HT>(a.H, ((static_cast<int64_t>(b) * T + t) * M + m) * d + c)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+
+  // phase 2: conv taps, SiLU, residual for 4 channels x TPT tokens per thread
+#pragma unroll
+  for (int n = 0; n < TPT; ++n) {
+    const int k = k0 + n * (256 / CG);
     const int64_t t = t0 + k;
     if (t >= T) break;
     const int r = span + k;
@@ -179,7 +245,7 @@ conv_kernel(ConvArgs a) {
       if (j < kw) {
         const int rs = r - (kw - 1 - j) * g.dilation;
         const float s = scale_s[rs];
-        const float4 u = tile[rs * cg + q];
+        const float4 u = tile[rs * CG + q];
         acc.x += wt[0][j] * (s * u.x);
         acc.y += wt[1][j] * (s * u.y);
         acc.z += wt[2][j] * (s * u.z);
@@ -187,19 +253,19 @@ conv_kernel(ConvArgs a) {
       }
     }
     const float al = alpha_s[r];
-    const float4 v = tile[r * cg + q];
+    const float4 v = tile[r * CG + q];
     float4 y;
     y.x = acc.x / (1.0f + expf(-acc.x)) + al * v.x;
     y.y = acc.y / (1.0f + expf(-acc.y)) + al * v.y;
     y.z = acc.z / (1.0f + expf(-acc.z)) + al * v.z;
     y.w = acc.w / (1.0f + expf(-acc.w)) + al * v.w;
     const int64_t ho = ((static_cast<int64_t>(b) * T + t) * M + m) * d + c;
-    float4 h = load4<HT>(a.H, ho);
-    h.x += y.x;
-    h.y += y.y;
-    h.z += y.z;
-    h.w += y.w;
-    store4<HT>(a.H, ho, h);
+    float4 hn = h[n];
+    hn.x += y.x;
+    hn.y += y.y;
+    hn.z += y.z;
+    hn.w += y.w;
+    store4<HT>(a.H, ho, hn);
     if (a.y_out != nullptr) *reinterpret_cast<float4*>(a.y_out + ho) = y;
   }
 }
@@ -274,22 +340,40 @@ hipError_t launch_gate_stats(const void* H, const void* kv, int64_t n_tok, const
   return hipGetLastError();
 }
 
-hipError_t launch_conv(const ConvArgs& in, int vdtype, hipStream_t s) {
-  if (in.B * in.T == 0) return hipSuccess;
-  ConvArgs a = in;
-  const int ct = conv_channels(a.g.d);
-  a.cg = ct / 4;
+template <int CG>
+hipError_t launch_conv_cg(const ConvArgs& a, int vdtype, hipStream_t s) {
   const int span = (a.g.kernel_w - 1) * a.g.dilation;
-  const size_t lds = static_cast<size_t>(TT + span) * a.cg * sizeof(float4);
+  const size_t lds = static_cast<size_t>(TT + span) * (CG + a.qv + a.qk) * sizeof(float4);
   const dim3 grid(static_cast<unsigned>((a.T + TT - 1) / TT), static_cast<unsigned>(a.B * a.g.branches),
-                  static_cast<unsigned>(a.g.d / ct));
+                  static_cast<unsigned>(a.g.d / (CG * 4)));
+  const void* fn;
   if (a.g.hdtype == ENGRAM_BF16 && vdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((conv_kernel<ENGRAM_BF16, ENGRAM_BF16>), grid, dim3(256), lds, s, a);
+    fn = reinterpret_cast<const void*>(conv_kernel<ENGRAM_BF16, ENGRAM_BF16, CG>);
   else if (a.g.hdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((conv_kernel<ENGRAM_BF16, ENGRAM_F32>), grid, dim3(256), lds, s, a);
+    fn = reinterpret_cast<const void*>(conv_kernel<ENGRAM_BF16, ENGRAM_F32, CG>);
   else
-    hipLaunchKernelGGL((conv_kernel<ENGRAM_F32, ENGRAM_F32>), grid, dim3(256), lds, s, a);
+    fn = reinterpret_cast<const void*>(conv_kernel<ENGRAM_F32, ENGRAM_F32, CG>);
+  if (lds > 48 * 1024) {
+    // large statistics tiles (wide d) need more than the default dynamic LDS
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  if (a.g.hdtype == ENGRAM_BF16 && vdtype == ENGRAM_BF16)
+    hipLaunchKernelGGL((conv_kernel<ENGRAM_BF16, ENGRAM_BF16, CG>), grid, dim3(256), lds, s, a);
+  else if (a.g.hdtype == ENGRAM_BF16)
+    hipLaunchKernelGGL((conv_kernel<ENGRAM_BF16, ENGRAM_F32, CG>), grid, dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL((conv_kernel<ENGRAM_F32, ENGRAM_F32, CG>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s) {
+  if (a.B * a.T == 0) return hipSuccess;
+  switch (conv_channels(a.g.d)) {
+    case 256: return launch_conv_cg<64>(a, vdtype, s);
+    case 128: return launch_conv_cg<32>(a, vdtype, s);
+    default: return launch_conv_cg<16>(a, vdtype, s);
+  }
 }
 
 hipError_t launch_state_commit(const void* v, int64_t v_stride, int vdtype, int64_t B, int64_t T,

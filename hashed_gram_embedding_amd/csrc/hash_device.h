@@ -29,17 +29,25 @@ __device__ __forceinline__ int32_t hash_index(const int32_t* __restrict__ tokens
                                               int j, int64_t b, int64_t t, int64_t T) {
   const int n = a.order[j];
   const int hist_len = a.max_n - 1;
-  uint64_t acc = 0;
-  for (int i = 0; i < n; ++i) {
+  // unrolled to the largest order so that the id loads of all positions are
+  // issued before any is waited on
+  uint32_t x[ENGRAM_MAX_ORDER];
+#pragma unroll
+  for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) {
     const int64_t p = t - i;
-    uint32_t x = 0;
-    if (p >= 0) {
-      x = static_cast<uint32_t>(proj[tokens[b * T + p]]);
-    } else if (hist != nullptr) {
-      x = static_cast<uint32_t>(hist[b * hist_len + hist_len + p]);
+    x[i] = 0;
+    if (i < n) {
+      if (p >= 0) {
+        x[i] = static_cast<uint32_t>(proj[tokens[b * T + p]]);
+      } else if (hist != nullptr) {
+        x[i] = static_cast<uint32_t>(hist[b * hist_len + hist_len + p]);
+      }
     }
-    acc ^= static_cast<uint64_t>(x) * a.mult[j][i];
   }
+  uint64_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < ENGRAM_MAX_ORDER; ++i)
+    if (i < n) acc ^= static_cast<uint64_t>(x[i]) * a.mult[j][i];
   return static_cast<int32_t>(mod_prime(acc, a.prime[j], a.inv[j]));
 }
 

@@ -8,16 +8,21 @@
 // The conv kernel adds up the partials of each token (a fixed number of
 // tiles, so the result is deterministic) to form alpha and RMSNorm(alpha v).
 //
-// gfx950 bf16 matrix cores (v_mfma_f32_16x16x32_bf16), float32 accumulation.
+// gfx950 bf16 matrix cores: v_mfma_f32_32x32x16_bf16 (measured on MI355X at
+// about 1.4x the sustained rate of the 16x16x32 form), float32 accumulation.
 // The weight rows are the MFMA A operand and the token rows of e the B
-// operand: each lane then holds 4 consecutive features of one token per
-// 16x16 block, so v stores are 16-byte vectors and h loads 8-byte vectors.
-// Workgroup tile: 128 features x 256 tokens, four wavefronts of 64 x 128;
-// K advances 64 per step through double-buffered LDS (96 KiB) with the 16-byte
-// chunk c of row r stored at chunk c ^ (r & 7); the next K slice is fetched to
-// registers while the current one is multiplied.  Tiles are ordered XCD by
-// XCD (workgroup i runs on XCD i % 8) with the feature tile fastest, so the
-// workgroups that read the same e rows share an L2.
+// operand: each lane then holds four runs of 4 consecutive features of one
+// token, so v stores are 16-byte vectors and h loads 8-byte vectors.
+// Workgroup tile: 128 features x 256 tokens with eight wavefronts of 64 x 64
+// (two per SIMD, so one wavefront's matrix work overlaps another's LDS
+// traffic); K advances 64 per step through double-buffered LDS (96 KiB) with
+// the 16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 7), which puts
+// the 16 rows of a fragment read on 16 distinct 16-byte bank groups.  The
+// next K slice is fetched to registers while the current one is multiplied,
+// and the compiler's MFMA/LDS interleaving strategy 0 orders the inner loop.
+// Tiles are ordered XCD by XCD (workgroup i runs on XCD i % 8) with the
+// feature tile fastest, so the workgroups that read the same e rows share an
+// L2.
 #include <atomic>
 
 #include "device_util.h"
@@ -27,23 +32,31 @@ namespace engram {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// 16-byte staging type: a native vector (HIP's uint4 struct copies through memory)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int TF = 128;  // features per workgroup
-constexpr int TK = 256;  // tokens per workgroup
-constexpr int BK = 64;
-constexpr int kThreads = 256;
+constexpr int TF = 128;        // features per workgroup
+constexpr int TK = 256;        // tokens per workgroup
+constexpr int BK = 64;         // K slice
+constexpr int WF = 2;          // wavefronts along features
+constexpr int WT = 4;          // wavefronts along tokens
+constexpr int kThreads = 64 * WF * WT;
 constexpr int kXcds = 8;
-constexpr int kWChunks = TF * BK / 8;  // 16-byte chunks of a W slice
-constexpr int kEChunks = TK * BK / 8;  // 16-byte chunks of an e slice
+constexpr int kWChunks = TF * BK / 8;    // 16-byte chunks of a W slice
+constexpr int kEChunks = TK * BK / 8;    // 16-byte chunks of an e slice
+constexpr int NW = kWChunks / kThreads;  // W chunks staged per thread
+constexpr int NE = kEChunks / kThreads;  // e chunks staged per thread
+constexpr int I = TF / WF / 32;          // 32-row feature blocks per wavefront
+constexpr int J = TK / WT / 32;          // 32-row token blocks per wavefront
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 proj_gate_kernel(ProjGateArgs a) {
-  extern __shared__ uint4 lds[];
-  uint4* Ws = lds;                    // [2][kWChunks]
-  uint4* Es = lds + 2 * kWChunks;     // [2][kEChunks]
+  extern __shared__ u32x4_t lds[];
+  u32x4_t* Ws = lds;                  // [2][kWChunks]
+  u32x4_t* Es = lds + 2 * kWChunks;   // [2][kEChunks]
 
   const int n_tiles = a.tiles_f * a.tiles_t;
   const int L = blockIdx.x;
@@ -56,40 +69,59 @@ proj_gate_kernel(ProjGateArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wf = wave & 1;   // feature half
-  const int wt = wave >> 1;  // token half
+  const int wf = wave % WF;
+  const int wt = wave / WF;
   const int K = a.K;
 
-  f32x4_t acc[4][8];
+  f32x16_t acc[I][J];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < I; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // global -> register staging of one K slice: 4 chunks of W and 8 of e per thread
-  uint4 rw0, rw1, rw2, rw3, re[8];
+  // global -> register staging of one K slice.  Token rows past the end load
+  // the last row instead (always a valid address); their results are never
+  // stored.
+  u32x4_t rw[NW], re[NE];
   const uint16_t* wbase = a.w + static_cast<int64_t>(f0) * K;
-#define ENGRAM_LOAD_SLICE(k0)                                                                   \
-  {                                                                                             \
-    rw0 = *reinterpret_cast<const uint4*>(wbase + (tid >> 3) * K + (k0) + (tid & 7) * 8);          \
-    rw1 = *reinterpret_cast<const uint4*>(wbase + ((tid >> 3) + 32) * K + (k0) + (tid & 7) * 8);   \
-    rw2 = *reinterpret_cast<const uint4*>(wbase + ((tid >> 3) + 64) * K + (k0) + (tid & 7) * 8);   \
-    rw3 = *reinterpret_cast<const uint4*>(wbase + ((tid >> 3) + 96) * K + (k0) + (tid & 7) * 8);   \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                             \
-      const int64_t tok = t0 + (tid >> 3) + i * 32;                                             \
-      re[i] = tok < a.n_tok ? *reinterpret_cast<const uint4*>(a.e + tok * K + (k0) + (tid & 7) * 8) \
-                            : make_uint4(0, 0, 0, 0);                                           \
-    }                                                                                           \
+#define ENGRAM_LOAD_SLICE(k0)                                                                      \
+  {                                                                                                \
+    _Pragma("unroll") for (int i = 0; i < NW; ++i) {                                               \
+      const int c = tid + i * kThreads;                                                            \
+      rw[i] = *reinterpret_cast<const u32x4_t*>(wbase + (c >> 3) * K + (k0) + (c & 7) * 8);        \
+    }                                                                                              \
+    _Pragma("unroll") for (int i = 0; i < NE; ++i) {                                               \
+      const int c = tid + i * kThreads;                                                            \
+      const int64_t tok = min(t0 + (c >> 3), a.n_tok - 1);                                         \
+      re[i] = *reinterpret_cast<const u32x4_t*>(a.e + tok * K + (k0) + (c & 7) * 8);               \
+    }                                                                                              \
   }
-#define ENGRAM_STORE_SLICE(buf)                                                                 \
-  {                                                                                             \
-    uint4* ws_ = Ws + (buf) * kWChunks;                                                         \
-    uint4* es_ = Es + (buf) * kEChunks;                                                         \
-    ws_[swz((tid >> 3), tid & 7)] = rw0;                                                        \
-    ws_[swz((tid >> 3) + 32, tid & 7)] = rw1;                                                   \
-    ws_[swz((tid >> 3) + 64, tid & 7)] = rw2;                                                   \
-    ws_[swz((tid >> 3) + 96, tid & 7)] = rw3;                                                   \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) es_[swz((tid >> 3) + i * 32, tid & 7)] = re[i]; \
+#define ENGRAM_STORE_SLICE(buf)                                                                    \
+  {                                                                                                \
+    _Pragma("unroll") for (int i = 0; i < NW; ++i) {                                               \
+      const int c = tid + i * kThreads;                                                            \
+      Ws[(buf) * kWChunks + swz(c >> 3, c & 7)] = rw[i];                                           \
+    }                                                                                              \
+    _Pragma("unroll") for (int i = 0; i < NE; ++i) {                                               \
+      const int c = tid + i * kThreads;                                                            \
+      Es[(buf) * kEChunks + swz(c >> 3, c & 7)] = re[i];                                           \
+    }                                                                                              \
+  }
+#define ENGRAM_COMPUTE(buf)                                                                        \
+  {                                                                                                \
+    __builtin_amdgcn_iglp_opt(0);                                                                  \
+    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                                       \
+      const int kc = ks * 2 + (lane >> 5);                                                         \
+      bf16x8_t fa[I], fb[J];                                                                       \
+      _Pragma("unroll") for (int i = 0; i < I; ++i) fa[i] = __builtin_bit_cast(                    \
+          bf16x8_t, Ws[(buf) * kWChunks + swz(wf * (TF / WF) + i * 32 + (lane & 31), kc)]);        \
+      _Pragma("unroll") for (int j = 0; j < J; ++j) fb[j] = __builtin_bit_cast(                    \
+          bf16x8_t, Es[(buf) * kEChunks + swz(wt * (TK / WT) + j * 32 + (lane & 31), kc)]);        \
+      _Pragma("unroll") for (int i = 0; i < I; ++i) _Pragma("unroll") for (int j = 0; j < J; ++j)  \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);   \
+    }                                                                                              \
   }
 
   const int ksteps = K / BK;
@@ -99,76 +131,71 @@ proj_gate_kernel(ProjGateArgs a) {
   for (int kt = 0; kt < ksteps; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < ksteps) ENGRAM_LOAD_SLICE((kt + 1) * BK);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kc = ks * 4 + (lane >> 4);
-      bf16x8_t fa[4], fb[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = __builtin_bit_cast(bf16x8_t, Ws[cur * kWChunks + swz(wf * 64 + i * 16 + (lane & 15), kc)]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        fb[j] = __builtin_bit_cast(bf16x8_t, Es[cur * kEChunks + swz(wt * 128 + j * 16 + (lane & 15), kc)]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
+    ENGRAM_COMPUTE(cur);
     if (kt + 1 < ksteps) ENGRAM_STORE_SLICE(cur ^ 1);
     __syncthreads();
   }
 #undef ENGRAM_LOAD_SLICE
 #undef ENGRAM_STORE_SLICE
+#undef ENGRAM_COMPUTE
 
-  // ---- epilogue: lane holds features f0 + wf*64 + i*16 + (lane>>4)*4 + r of
-  // token t0 + wt*128 + j*16 + (lane & 15) ----
+  // ---- epilogue: acc[i][j][4g + r] is feature wf*64 + i*32 + g*8 + (lane>>5)*4 + r
+  // of token wt*64 + j*32 + (lane & 31) ----
   const int d = a.d;
   const bool is_v = f0 < d;
   const int m = is_v ? 0 : f0 / d - 1;
   const int c0 = is_v ? f0 : f0 - (1 + m) * d;   // column inside v or inside k^(m)
-  float4* red = reinterpret_cast<float4*>(lds);   // [TK][2] partials of the two feature halves
+  float4* red = reinterpret_cast<float4*>(lds);   // [TK][WF] partials of the feature wavefronts
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int tl = wt * 128 + j * 16 + (lane & 15);
+  for (int j = 0; j < J; ++j) {
+    const int tl = wt * (TK / WT) + j * 32 + (lane & 31);
     const int64_t tok = t0 + tl;
     const bool valid = tok < a.n_tok;
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = c0 + wf * 64 + i * 16 + (lane >> 4) * 4;
-      const f32x4_t x = acc[i][j];
-      if (is_v) {
-        if (valid) *reinterpret_cast<float4*>(a.v + tok * d + col) = make_float4(x[0], x[1], x[2], x[3]);
-        s3 += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-      } else if (valid) {
-        const uint2 hq = *reinterpret_cast<const uint2*>(a.H + (tok * a.M + m) * d + col);
-        const float h0 = __uint_as_float(hq.x << 16), h1 = __uint_as_float(hq.x & 0xffff0000u);
-        const float h2 = __uint_as_float(hq.y << 16), h3 = __uint_as_float(hq.y & 0xffff0000u);
-        s0 += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
-        s1 += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-        s2 += h0 * x[0] + h1 * x[1] + h2 * x[2] + h3 * x[3];
+    for (int i = 0; i < I; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = c0 + wf * (TF / WF) + i * 32 + g * 8 + (lane >> 5) * 4;
+        const float x0 = acc[i][j][4 * g], x1 = acc[i][j][4 * g + 1];
+        const float x2 = acc[i][j][4 * g + 2], x3 = acc[i][j][4 * g + 3];
+        if (is_v) {
+          if (valid) *reinterpret_cast<float4*>(a.v + tok * d + col) = make_float4(x0, x1, x2, x3);
+          s3 += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+        } else if (valid) {
+          const uint2 hq = *reinterpret_cast<const uint2*>(a.H + (tok * a.M + m) * d + col);
+          const float h0 = __uint_as_float(hq.x << 16), h1 = __uint_as_float(hq.x & 0xffff0000u);
+          const float h2 = __uint_as_float(hq.y << 16), h3 = __uint_as_float(hq.y & 0xffff0000u);
+          s0 += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
+          s1 += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+          s2 += h0 * x0 + h1 * x1 + h2 * x2 + h3 * x3;
+        }
       }
     }
-    s0 += __shfl_xor(s0, 16, 64); s0 += __shfl_xor(s0, 32, 64);
-    s1 += __shfl_xor(s1, 16, 64); s1 += __shfl_xor(s1, 32, 64);
-    s2 += __shfl_xor(s2, 16, 64); s2 += __shfl_xor(s2, 32, 64);
-    s3 += __shfl_xor(s3, 16, 64); s3 += __shfl_xor(s3, 32, 64);
-    if ((lane >> 4) == 0) red[tl * 2 + wf] = make_float4(s0, s1, s2, s3);
+    s0 += __shfl_xor(s0, 32, 64);
+    s1 += __shfl_xor(s1, 32, 64);
+    s2 += __shfl_xor(s2, 32, 64);
+    s3 += __shfl_xor(s3, 32, 64);
+    if ((lane >> 5) == 0) red[tl * WF + wf] = make_float4(s0, s1, s2, s3);
   }
   __syncthreads();
-  {
-    const int64_t tok = t0 + tid;
+  for (int tl = tid; tl < TK; tl += kThreads) {
+    const int64_t tok = t0 + tl;
     if (tok < a.n_tok) {
-      const float4 p = red[tid * 2], q = red[tid * 2 + 1];
-      a.stats[tok * a.tiles_f + tf] = make_float4(p.x + q.x, p.y + q.y, p.z + q.z, p.w + q.w);
+      float4 p = red[tl * WF];
+#pragma unroll
+      for (int w = 1; w < WF; ++w) {
+        const float4 q = red[tl * WF + w];
+        p = make_float4(p.x + q.x, p.y + q.y, p.z + q.z, p.w + q.w);
+      }
+      a.stats[tok * a.tiles_f + tf] = p;
     }
   }
 }
 
 }  // namespace
 
-size_t proj_gate_lds_bytes() { return static_cast<size_t>(2 * (kWChunks + kEChunks)) * sizeof(uint4); }
+size_t proj_gate_lds_bytes() { return static_cast<size_t>(2 * (kWChunks + kEChunks)) * sizeof(u32x4_t); }
 
 hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
   if (in.n_tok == 0) return hipSuccess;
