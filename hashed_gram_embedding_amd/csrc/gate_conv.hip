@@ -70,6 +70,7 @@ gate_stats_kernel(const void* __restrict__ H, const void* __restrict__ kv, int64
   const int64_t v_off = t * (1 + M) * d;
   const int64_t k_off = v_off + static_cast<int64_t>(1 + m) * d;
   float shh = 0.f, skk = 0.f, shk = 0.f, svv = 0.f;
+#pragma unroll 4
   for (int c = lane * 4; c < d; c += 256) {
     const float4 h = load4<HT>(H, h_off + c);
     const float4 k = load4<KT>(kv, k_off + c);
@@ -226,9 +227,11 @@ conv_kernel(ConvArgs a) {
   float4 h[TPT];
 #pragma unroll
   for (int n = 0; n < TPT; ++n) {
-    const int64_t t = t0 + k0 + n * (256 / CG);
-    h[n] = t < T ? load4<HT>(a.H, ((static_cast<int64_t>(b) * T + t) * M + m) * d + c)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    // clamped (always valid) address, no branch: positions past the end are
+    // loaded but never stored
+    int64_t t = t0 + k0 + n * (256 / CG);
+    t = t < T ? t : T - 1;
+    h[n] = load4<HT>(a.H, ((static_cast<int64_t>(b) * T + t) * M + m) * d + c);
   }
   __syncthreads();
 

@@ -29,19 +29,24 @@ __device__ __forceinline__ int32_t hash_index(const int32_t* __restrict__ tokens
                                               int j, int64_t b, int64_t t, int64_t T) {
   const int n = a.order[j];
   const int hist_len = a.max_n - 1;
-  // unrolled to the largest order so that the id loads of all positions are
-  // issued before any is waited on
-  uint32_t x[ENGRAM_MAX_ORDER];
+  // Unrolled to the largest order, with clamped (always valid) positions, so
+  // that the token loads of all positions and then their P lookups are each
+  // issued together; positions before the sequence start are patched from
+  // the history afterwards.
+  int32_t tok[ENGRAM_MAX_ORDER];
 #pragma unroll
   for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) {
     const int64_t p = t - i;
-    x[i] = 0;
-    if (i < n) {
-      if (p >= 0) {
-        x[i] = static_cast<uint32_t>(proj[tokens[b * T + p]]);
-      } else if (hist != nullptr) {
-        x[i] = static_cast<uint32_t>(hist[b * hist_len + hist_len + p]);
-      }
+    tok[i] = tokens[b * T + (p >= 0 ? p : 0)];
+  }
+  uint32_t x[ENGRAM_MAX_ORDER];
+#pragma unroll
+  for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) x[i] = static_cast<uint32_t>(proj[tok[i]]);
+  if (t < hist_len) {
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) {
+      const int64_t p = t - i;
+      if (p < 0) x[i] = hist != nullptr && hist_len + p >= 0 ? static_cast<uint32_t>(hist[b * hist_len + hist_len + p]) : 0u;
     }
   }
   uint64_t acc = 0;
