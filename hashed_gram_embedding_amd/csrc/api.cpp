@@ -466,6 +466,49 @@ ENGRAM_API engram_status engram_forward(const int32_t* tokens, void* H, int64_t 
                          L->hash.max_n, alpha_out, f.gamma, y_out, stream);
 }
 
+ENGRAM_API size_t engram_cache_build_workspace(int64_t total_rows) {
+  if (total_rows <= 0) return 0;
+  return engram::cache_build_workspace(total_rows);
+}
+
+ENGRAM_API engram_status engram_cache_build(const int32_t* warm_tokens, int64_t B, int64_t T,
+                                            const engram_hash_params* hp, const engram_tables* tab,
+                                            int64_t cache_n, int32_t* cache_slot, void* cache_rows,
+                                            float* cache_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  engram::HashArgs ha;
+  engram::TableArgs ta;
+  engram_status r = check_hash(hp, &ha);
+  if (r != ENGRAM_OK) return r;
+  if (tab == nullptr) return fail(ENGRAM_EINVAL, "cache_build: tables are NULL");
+  engram_tables plain = *tab;   // the cache being built is not probed
+  plain.cache_slot = nullptr;
+  if ((r = check_tables(&plain, &ta)) != ENGRAM_OK) return r;
+  if (tab->n_tables != ha.n_tables)
+    return fail(ENGRAM_EINVAL, "cache_build: tables.n_tables=%d but the hash has %d tables", tab->n_tables,
+                ha.n_tables);
+  for (int j = 0; j < ha.n_tables; ++j)
+    if (tab->n_rows[j] != static_cast<int64_t>(ha.prime[j]))
+      return fail(ENGRAM_EINVAL, "cache_build: table %d has %lld rows but prime %u", j,
+                  static_cast<long long>(tab->n_rows[j]), ha.prime[j]);
+  if (B < 0 || T < 0) return fail(ENGRAM_EINVAL, "cache_build: B and T must be >= 0");
+  if (B * T > 0 && warm_tokens == nullptr) return fail(ENGRAM_EINVAL, "cache_build: warm_tokens is NULL");
+  if (cache_n < 0 || cache_n > tab->total_rows || tab->total_rows > 0x7fffffffLL)
+    return fail(ENGRAM_EINVAL, "cache_build: need 0 <= cache_n <= total_rows < 2^31");
+  if (cache_slot == nullptr || (cache_n > 0 && cache_rows == nullptr))
+    return fail(ENGRAM_EINVAL, "cache_build: cache_slot and cache_rows must be non-NULL");
+  if (tab->dtype == ENGRAM_I8 && cache_n > 0 && cache_scale == nullptr)
+    return fail(ENGRAM_EINVAL, "cache_build: int8 tables need cache_scale");
+  if (cache_rows != nullptr && !aligned(cache_rows, 8)) return fail(ENGRAM_EINVAL, "cache_build: cache_rows must be 8-byte aligned");
+  const size_t need = engram::cache_build_workspace(tab->total_rows);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(ENGRAM_EINVAL, "cache_build: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  const int row_bytes = tab->dim * static_cast<int>(dtype_size(tab->dtype));
+  return hip_status(engram::launch_cache_build(warm_tokens, B, T, hp->proj, ha, ta, tab->total_rows, row_bytes, cache_n,
+                                               cache_slot, cache_rows, tab->dtype == ENGRAM_I8 ? cache_scale : nullptr,
+                                               ws, stream),
+                    "cache build launch");
+}
+
 ENGRAM_API engram_status engram_profile_enable(int32_t on) {
   Profiler& p = g_prof;
   if (on && !p.created) {

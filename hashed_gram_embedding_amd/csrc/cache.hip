@@ -1,0 +1,254 @@
+// Static LFU admission for the HBM hot-row cache.  The Ascend RecSDK Engram
+// article (multi-level cache) keeps the frequently accessed embedding rows in
+// fast device memory and the full table in host DRAM, choosing them by access
+// counts (LFU).  Here the counts come from a warm-up token stream hashed
+// exactly like the layer (Steps 1-3 of the Engram series guide); the cache_n
+// most frequently addressed rows are admitted (ties: lower global row first)
+// and get slots in ascending row order.
+//
+// Kernels, all on the caller's stream:
+//   count      one thread per (token, table): atomic increment of the row count
+//   histogram  counts clamped to kBins-1 into a histogram
+//   threshold  one workgroup finds the admission count c* and how many rows of
+//              count c* still fit
+//   scan x2    rank of each count-c* row among equals, then the slot of each
+//              admitted row (block scans + a scan of the block sums)
+//   copy       admitted rows (and int8 scales) into the cache
+#include "device_util.h"
+#include "engram_internal.h"
+#include "hash_device.h"
+
+namespace engram {
+namespace {
+
+constexpr int kBins = 1 << 20;           // exact while the threshold count is below kBins - 1
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 16;
+constexpr int kScanBlock = kScanThreads * kScanItems;
+
+__global__ void __launch_bounds__(256) fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void __launch_bounds__(256)
+count_kernel(const int32_t* __restrict__ tokens, int64_t B, int64_t T, const int32_t* __restrict__ proj, HashArgs a,
+             TableArgs ta, uint32_t* __restrict__ counts) {
+  const int nt = a.n_tables;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= B * T * nt) return;
+  const int j = static_cast<int>(gid % nt);
+  const int64_t bt = gid / nt;
+  const int64_t b = bt / T;
+  const int32_t z = hash_index(tokens, proj, nullptr, a, j, b, bt - b * T, T);
+  atomicAdd(counts + ta.row_offset[j] + z, 1u);
+}
+
+__global__ void __launch_bounds__(256)
+histogram_kernel(const uint32_t* __restrict__ counts, int64_t n, uint32_t* __restrict__ bins) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const uint32_t c = counts[i];
+    atomicAdd(bins + (c < kBins - 1 ? c : kBins - 1), 1u);
+  }
+}
+
+// params[0] = c*, params[1] = rows of count c* that are admitted.
+__global__ void __launch_bounds__(1024)
+threshold_kernel(const uint32_t* __restrict__ bins, int64_t cap, int64_t* __restrict__ params) {
+  constexpr int kChunk = kBins / 1024;
+  __shared__ int64_t part[1024];
+  const int tid = threadIdx.x;
+  int64_t s = 0;
+  for (int i = 0; i < kChunk; ++i) s += bins[tid * kChunk + i];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int64_t above = 0;  // rows with a count above the current chunk / bin
+    int64_t cstar = 0, need = 0;
+    bool found = false;
+    for (int ch = 1023; ch >= 0 && !found; --ch) {
+      if (above + part[ch] < cap) {
+        above += part[ch];
+        continue;
+      }
+      for (int c = (ch + 1) * kChunk - 1; c >= ch * kChunk; --c) {
+        if (above + bins[c] >= cap) {
+          cstar = c;
+          need = cap - above;
+          found = true;
+          break;
+        }
+        above += bins[c];
+      }
+    }
+    if (!found) {  // cap exceeds the row count: everything is admitted
+      cstar = 0;
+      need = cap;
+    }
+    params[0] = cstar;
+    params[1] = need;
+  }
+}
+
+// mode 0: flag = (count == c*);  mode 1: flag = admitted, using eq_rank from mode 0.
+__device__ __forceinline__ int32_t scan_flag(int mode, const uint32_t* counts, const int32_t* eq_rank,
+                                             const int64_t* params, int64_t i) {
+  const uint32_t c = counts[i];
+  const uint32_t cs = static_cast<uint32_t>(params[0]);
+  const uint32_t cc = c < kBins - 1 ? c : kBins - 1;
+  if (mode == 0) return cc == cs ? 1 : 0;
+  return (cc > cs || (cc == cs && eq_rank[i] < params[1])) ? 1 : 0;
+}
+
+// Per-block exclusive scan of the flags, block totals to sums[].
+__global__ void __launch_bounds__(kScanThreads)
+scan_local_kernel(int mode, const uint32_t* __restrict__ counts, const int32_t* __restrict__ eq_rank,
+                  const int64_t* __restrict__ params, int64_t n, int32_t* __restrict__ out, int32_t* __restrict__ sums) {
+  __shared__ int32_t warp_tot[kScanThreads / 64];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kScanBlock + threadIdx.x * kScanItems;
+  int32_t v[kScanItems];
+  int32_t run = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int64_t i = base + k;
+    v[k] = i < n ? scan_flag(mode, counts, eq_rank, params, i) : 0;
+    run += v[k];
+  }
+  // exclusive scan of the per-thread totals across the block
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t x = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) warp_tot[wave] = x;
+  __syncthreads();
+  int32_t wave_base = 0;
+  for (int w = 0; w < wave; ++w) wave_base += warp_tot[w];
+  int32_t acc = wave_base + x - run;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int64_t i = base + k;
+    if (i < n) out[i] = acc;
+    acc += v[k];
+  }
+  if (threadIdx.x == kScanThreads - 1) sums[blockIdx.x] = wave_base + x;
+}
+
+// Exclusive scan of the block totals in one workgroup (serial over chunks).
+__global__ void __launch_bounds__(1024) scan_sums_kernel(int32_t* __restrict__ sums, int64_t nb) {
+  __shared__ int64_t part[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (nb + 1023) / 1024;
+  int64_t s = 0;
+  for (int64_t i = tid * per; i < (tid + 1) * per && i < nb; ++i) s += sums[i];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int64_t acc = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int64_t t = part[i];
+      part[i] = acc;
+      acc += t;
+    }
+  }
+  __syncthreads();
+  int64_t acc = part[tid];
+  for (int64_t i = tid * per; i < (tid + 1) * per && i < nb; ++i) {
+    const int32_t t = sums[i];
+    sums[i] = static_cast<int32_t>(acc);
+    acc += t;
+  }
+}
+
+// mode 0: eq_rank[i] = global exclusive rank among equals.
+// mode 1: cache_slot[i] = slot of an admitted row, else -1.
+__global__ void __launch_bounds__(256)
+scan_finish_kernel(int mode, const uint32_t* __restrict__ counts, const int32_t* __restrict__ eq_rank,
+                   const int64_t* __restrict__ params, int64_t n, int32_t* __restrict__ out,
+                   const int32_t* __restrict__ sums) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int32_t r = out[i] + sums[i / kScanBlock];
+    if (mode == 0) {
+      out[i] = r;
+    } else {
+      out[i] = scan_flag(1, counts, eq_rank, params, i) ? r : -1;
+    }
+  }
+}
+
+// One thread per (row, 16-byte chunk) of an admitted row.
+__global__ void __launch_bounds__(256)
+copy_rows_kernel(const int32_t* __restrict__ slot, int64_t n, const uint8_t* __restrict__ rows,
+                 const float* __restrict__ scale, int row_bytes, uint8_t* __restrict__ cache,
+                 float* __restrict__ cache_scale) {
+  const int chunks = row_bytes / 8;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= n * chunks) return;
+  const int64_t r = gid / chunks;
+  const int c = static_cast<int>(gid - r * chunks);
+  const int32_t s = slot[r];
+  if (s < 0) return;
+  *reinterpret_cast<uint2*>(cache + static_cast<int64_t>(s) * row_bytes + c * 8) =
+      *reinterpret_cast<const uint2*>(rows + r * row_bytes + c * 8);
+  if (c == 0 && scale != nullptr) cache_scale[s] = scale[r];
+}
+
+unsigned grid_for(int64_t n, int threads) {
+  const int64_t b = (n + threads - 1) / threads;
+  return static_cast<unsigned>(b < 65535 * 64 ? b : 65535 * 64);
+}
+
+}  // namespace
+
+size_t cache_build_workspace(int64_t total_rows) {
+  const int64_t nb = (total_rows + kScanBlock - 1) / kScanBlock;
+  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  return al(total_rows * 4) /*counts*/ + al(kBins * 4) /*bins*/ + al(total_rows * 4) /*eq rank*/ +
+         al(nb * 4) /*block sums*/ + al(16) /*params*/;
+}
+
+hipError_t launch_cache_build(const int32_t* tokens, int64_t B, int64_t T, const int32_t* proj, const HashArgs& ha,
+                              const TableArgs& ta, int64_t total_rows, int row_bytes, int64_t cache_n,
+                              int32_t* cache_slot, void* cache_rows, float* cache_scale, void* ws, hipStream_t s) {
+  const int64_t nb = (total_rows + kScanBlock - 1) / kScanBlock;
+  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  char* p = static_cast<char*>(ws);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(p);
+  p += al(total_rows * 4);
+  uint32_t* bins = reinterpret_cast<uint32_t*>(p);
+  p += al(kBins * 4);
+  int32_t* eq_rank = reinterpret_cast<int32_t*>(p);
+  p += al(total_rows * 4);
+  int32_t* sums = reinterpret_cast<int32_t*>(p);
+  p += al(nb * 4);
+  int64_t* params = reinterpret_cast<int64_t*>(p);
+
+  hipLaunchKernelGGL(fill_u32, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, counts, total_rows, 0u);
+  hipLaunchKernelGGL(fill_u32, dim3(grid_for(kBins, 256)), dim3(256), 0, s, bins, static_cast<int64_t>(kBins), 0u);
+  const int64_t pairs = B * T * ha.n_tables;
+  if (pairs > 0)
+    hipLaunchKernelGGL(count_kernel, dim3(static_cast<unsigned>((pairs + 255) / 256)), dim3(256), 0, s, tokens, B, T,
+                       proj, ha, ta, counts);
+  hipLaunchKernelGGL(histogram_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, counts, total_rows, bins);
+  hipLaunchKernelGGL(threshold_kernel, dim3(1), dim3(1024), 0, s, bins, cache_n, params);
+  for (int mode = 0; mode < 2; ++mode) {
+    int32_t* out = mode == 0 ? eq_rank : cache_slot;
+    hipLaunchKernelGGL(scan_local_kernel, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0, s, mode, counts,
+                       eq_rank, params, total_rows, out, sums);
+    hipLaunchKernelGGL(scan_sums_kernel, dim3(1), dim3(1024), 0, s, sums, nb);
+    hipLaunchKernelGGL(scan_finish_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, mode, counts, eq_rank,
+                       params, total_rows, out, sums);
+  }
+  const int64_t work = total_rows * (row_bytes / 8);
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(static_cast<unsigned>((work + 255) / 256)), dim3(256), 0, s, cache_slot,
+                     total_rows, static_cast<const uint8_t*>(ta.rows), ta.scale, row_bytes,
+                     static_cast<uint8_t*>(cache_rows), cache_scale);
+  return hipGetLastError();
+}
+
+}  // namespace engram

@@ -118,4 +118,9 @@ hipError_t launch_state_commit(const void* v, int64_t v_stride, int vdtype, int6
                                const GateConvArgs& g, const float* gamma, const StateArgs& st,
                                const int32_t* tokens, const int32_t* proj, int32_t max_n, hipStream_t s);
 
+size_t cache_build_workspace(int64_t total_rows);
+hipError_t launch_cache_build(const int32_t* tokens, int64_t B, int64_t T, const int32_t* proj, const HashArgs& ha,
+                              const TableArgs& ta, int64_t total_rows, int row_bytes, int64_t cache_n,
+                              int32_t* cache_slot, void* cache_rows, float* cache_scale, void* ws, hipStream_t s);
+
 }  // namespace engram

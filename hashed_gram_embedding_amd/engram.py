@@ -84,6 +84,9 @@ def lib():
         "engram_forward_workspace": (sz, [i64, i64, ctypes.POINTER(LayerStruct)]),
         "engram_forward": (i32, [vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
                                  ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
+        "engram_cache_build_workspace": (sz, [i64]),
+        "engram_cache_build": (i32, [vp, i64, i64, ctypes.POINTER(HashParams), ctypes.POINTER(Tables), i64, vp, vp, vp,
+                                     vp, sz, vp]),
         "engram_profile_enable": (i32, [i32]),
         "engram_profile_read": (i32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), i32,
                                       ctypes.POINTER(i32)]),
@@ -101,7 +104,8 @@ def lib():
 def exported_names():
     return ["engram_abi_version", "engram_last_error", "engram_hash_indices", "engram_gather",
             "engram_project_kv", "engram_gate_conv_workspace", "engram_gate_conv_forward",
-            "engram_forward_workspace", "engram_forward", "engram_profile_enable", "engram_profile_read",
+            "engram_forward_workspace", "engram_forward", "engram_cache_build_workspace", "engram_cache_build",
+            "engram_profile_enable", "engram_profile_read",
             "engram_host_alloc", "engram_host_free"]
 
 
@@ -291,6 +295,25 @@ def gate_conv_forward(H: torch.Tensor, kv: torch.Tensor, layer: Layer, state: Op
     _check(lib().engram_gate_conv_forward(_ptr(H), _ptr(kv), B, T, ctypes.byref(layer.s.gc), st,
                                           _ptr(alpha), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
     return alpha, y
+
+
+def cache_build(warm_tokens: torch.Tensor, layer: Layer, cache_n: int, stream=None):
+    """Static LFU admission: returns (cache_slot [total_rows] int32, cache_rows, cache_scale or None)
+    on the device of warm_tokens; attach them with layer.set_cache(...)."""
+    dev = warm_tokens.device
+    t = layer.s.tables
+    total = t.total_rows
+    slot = torch.empty(total, dtype=torch.int32, device=dev)
+    elt = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}[t.dtype]
+    rows = torch.empty((max(cache_n, 1), t.dim), dtype=elt, device=dev)
+    scale = torch.empty(max(cache_n, 1), dtype=torch.float32, device=dev) if t.dtype == I8 else None
+    ws = torch.empty(max(lib().engram_cache_build_workspace(total), 256), dtype=torch.uint8, device=dev)
+    B, T = warm_tokens.shape
+    tab = Tables.from_buffer_copy(t)
+    tab.cache_slot = None
+    _check(lib().engram_cache_build(_ptr(warm_tokens), B, T, ctypes.byref(layer.s.hash), ctypes.byref(tab), cache_n,
+                                    _ptr(slot), _ptr(rows), _ptr(scale), _ptr(ws), ws.numel(), _stream(stream)))
+    return slot, rows, scale
 
 
 def profile_enable(on: bool = True):

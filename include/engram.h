@@ -198,6 +198,27 @@ engram_status engram_forward(const int32_t* tokens, void* H, int64_t B, int64_t 
                              float* alpha_out, float* y_out, void* ws, size_t ws_bytes,
                              hipStream_t stream);
 
+/* Static LFU admission for the HBM hot-row cache (Ascend RecSDK Engram
+ * article, multi-level cache: hot rows by access frequency in fast memory,
+ * the full table in host DRAM).  Counts how often each row of `tab` is
+ * addressed by the warm-up tokens (device int32 [B][T], hashed like the
+ * layer with pad-0 starts), admits the cache_n most frequently addressed rows
+ * (ties: lower global row first) and writes
+ *   cache_slot  device int32 [total_rows]: slot of an admitted row, else -1;
+ *               admitted rows take slots 0..cache_n-1 in ascending row order
+ *   cache_rows  device [cache_n][dim] of tab->dtype: copies of those rows
+ *   cache_scale device float [cache_n] (I8 only): their scales.
+ * tab->rows may be mapped host memory; tab's own cache fields are ignored.
+ * Asynchronous.  The ranking is exact while the admission threshold count is
+ * below 2^20 - 1 (rows counted 2^20 - 1 times or more rank as equals).
+ * ws: engram_cache_build_workspace() bytes, 256-byte aligned. */
+size_t engram_cache_build_workspace(int64_t total_rows);
+engram_status engram_cache_build(const int32_t* warm_tokens, int64_t B, int64_t T,
+                                 const engram_hash_params* hp, const engram_tables* tab,
+                                 int64_t cache_n, int32_t* cache_slot, void* cache_rows,
+                                 float* cache_scale, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
 /* Stage timing, for benchmarks.  engram_profile_enable(1) makes later
  * engram_forward calls on the calling thread record a HIP event on their
  * stream before each kernel launch and after the last one (events owned by

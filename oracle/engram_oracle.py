@@ -197,6 +197,21 @@ def gather(z: np.ndarray, rows: np.ndarray, dtype: str, row_offset: np.ndarray, 
     return vals.reshape(*z.shape[:-1], z.shape[-1] * dim)
 
 
+def lfu_admission(global_rows: np.ndarray, total_rows: int, cache_n: int) -> np.ndarray:
+    """Static LFU admission of the hot-row cache (Ascend RecSDK Engram article,
+    multi-level cache: the most frequently accessed rows live in fast memory).
+
+    Counts the accesses of each row in `global_rows`, admits the cache_n most
+    frequent rows (ties: lower row first) and numbers them 0..cache_n-1 in
+    ascending row order.  Returns the slot of every row (-1 = not cached)."""
+    counts = np.bincount(np.asarray(global_rows, dtype=np.int64).ravel(), minlength=total_rows)
+    order = np.lexsort((np.arange(total_rows), -counts))     # by count desc, then row asc
+    admitted = np.sort(order[:cache_n])
+    slot = np.full(total_rows, -1, dtype=np.int64)
+    slot[admitted] = np.arange(cache_n)
+    return slot
+
+
 # --------------------------------------------------------------------------
 # Step 5: key / value projections
 # --------------------------------------------------------------------------

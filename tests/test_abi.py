@@ -166,6 +166,27 @@ def test_forward_checks_layer_consistency():
     assert L.engram_forward(p, p, 0, 64, ctypes.byref(lay), None, None, None, None, 0, None) == eg.OK
 
 
+def test_cache_build_rejects_bad_arguments():
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    hp, keep_h = _hash_params()
+    t, keep_t = _tables()
+    need = L.engram_cache_build_workspace(4062)
+    assert need >= 2 * 4062 * 4
+    st, msg = _status(L.engram_cache_build, p, 1, 8, ctypes.byref(hp), ctypes.byref(t), 5000, p, p, None, p, need, None)
+    assert st == eg.EINVAL and "cache_n" in msg
+    st, msg = _status(L.engram_cache_build, p, 1, 8, ctypes.byref(hp), ctypes.byref(t), 10, p, p, None, p, need - 1,
+                      None)
+    assert st == eg.EINVAL and "workspace" in msg
+    assert L.engram_cache_build(p, 1, 8, ctypes.byref(hp), ctypes.byref(t), 10, None, p, None, p, need, None) \
+        == eg.EINVAL
+    t8, k8 = _tables(dtype=eg.I8, row_scale=0x20000)
+    st, msg = _status(L.engram_cache_build, p, 1, 8, ctypes.byref(hp), ctypes.byref(t8), 10, p, p, None, p, need,
+                      None)
+    assert st == eg.EINVAL and "cache_scale" in msg
+    assert L.engram_cache_build(p, 1, 8, ctypes.byref(hp), None, 10, p, p, None, p, need, None) == eg.EINVAL
+
+
 def test_host_alloc_rejects_zero_bytes():
     L = eg.lib()
     h, d = ctypes.c_void_p(), ctypes.c_void_p()

@@ -94,3 +94,16 @@ def test_int8_quantisation_input_roundtrip_bound():
     back = q.astype(np.float64) * s[:, None]
     assert np.all(np.abs(back - x) <= s[:, None] / 2 * (1 + 1e-6))
     assert np.all(np.abs(q).max(axis=1) == 127)
+
+
+def test_lfu_admission_hand_example():
+    """Counts per row [5, 3, 3, 3, 1, 0, 3]: the 4 most frequent are row 0 and
+    the three lowest rows of count 3 (1, 2, 3); row 6 (also 3) loses the tie.
+    Slots follow ascending row order."""
+    rows = [0] * 5 + [1] * 3 + [2] * 3 + [3] * 3 + [4] + [6] * 3
+    slot = orc.lfu_admission(np.array(rows), 7, 4)
+    assert list(slot) == [0, 1, 2, 3, -1, -1, -1]
+    assert list(orc.lfu_admission(np.array(rows), 7, 0)) == [-1] * 7
+    assert list(orc.lfu_admission(np.array(rows), 7, 7)) == [0, 1, 2, 3, 4, 5, 6]
+    # zero-count rows fill the cache last, lowest first
+    assert list(orc.lfu_admission(np.array([6, 6]), 7, 3)) == [0, 1, -1, -1, -1, -1, 2]
