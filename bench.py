@@ -1,15 +1,22 @@
 """Benchmark of the Engram layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--no-cpu-baseline] [--eager]
 
-One step is one full layer forward (hash, gather, projections, gate, conv and
-residual) over one batch of the workload, with every input already resident
-in HBM.  Prints one JSON line (see the design notes for the fields).
+One step is one pass of the whole layer path (hash, gather, projections,
+gate, conv and residual) over one batch, with every input already resident
+(in HBM, or in pinned host memory for the host-table configuration).  Prints
+one JSON line.
 
-The default workload is the single-branch bf16 layer: B = 1 sequence of
-T = 4096 tokens (Zipf(1.1) ids over a 128,000-id vocabulary, projected to
-98,560), 2 orders x 8 heads of 64-dim bf16 rows in 16 prime-sized tables
-(10,344,164 rows, 1.32 GB), d = d_mem = 1024.
+--config 1 (default; the metric's workload): single-branch bf16 layer, B = 1
+    sequence of T = 4096 tokens (Zipf(1.1) ids over a 128,000-id vocabulary,
+    projected to 98,560), 2 orders x 8 heads of 64-dim bf16 rows in 16
+    prime-sized tables (10,344,164 rows, 1.32 GB), d = d_mem = 1024.
+--config 2: the same tables with M = 4 branches, B = 8, T = 4096.
+--config 3: decode: 256 sequences x 1 new token through 2 layers with int8
+    rows (+ float32 row scales), after a 16-token prefill of each sequence.
+--config 4: B = 4, T = 4096 through 2 layers whose tables (33,556,876 rows,
+    4.3 GB each) live in pinned host memory, with an HBM cache of the 10 % most
+    frequent rows (static LFU admission over a 2^24-token warm-up stream).
 """
 from __future__ import annotations
 
@@ -18,8 +25,6 @@ import json
 import os
 import sys
 import time
-
-import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -34,26 +39,25 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2])
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     return ap.parse_args()
 
 
-def stage_units(w, lay):
+def kernel_units(n_tok, lay, hdtype):
     """Algorithmic bytes (HBM-bound kernels) or flops (matrix-core kernels)
-    per launch of each kernel of the layer forward, keyed by the kernel names
-    the library reports."""
-    n_tok = w.B * w.T
+    per launch of each kernel of one layer forward over n_tok tokens, keyed by
+    the kernel names the library reports."""
     nt = lay.hash.n_tables
     dim = lay.tables.dim
     d, M = lay.d, lay.branches
-    es = 2 if w.dtype == "bf16" else 4
+    es = 2 if hdtype == "bf16" else 4
     i8 = lay.tables.dtype == "i8"
     row_bytes = dim * (1 if i8 else es) + (4 if i8 else 0)
     d_mem = nt * dim
-    fused = w.dtype == "bf16" and d % 128 == 0
+    fused = hdtype == "bf16" and d % 128 == 0
     n_stat = (1 + M) * d // 128 if fused else 1 + M
     flops = 2.0 * n_tok * (1 + M) * d * d_mem
     return {
@@ -65,7 +69,59 @@ def stage_units(w, lay):
         "gate_stats_kernel": ("hbm", n_tok * (M * 2 * d * 4 + d * 4 + M * d * es + 16 * n_stat)),
         # v (float32) and statistics in; H in and out; alpha, gamma out
         "conv_kernel": ("hbm", n_tok * (d * 4 + 16 * n_stat + M * (2 * d * es + 8))),
+        # v and gamma in; conv input of the newest position out; ids, pos
+        "state_commit_kernel": ("hbm", n_tok * (d * 4 + M * (d * 4 + 4) + 16)),
     }
+
+
+def setup(args, torch, eg, inputs):
+    """Returns (layer_calls, n_tok, workload, layer_inputs, extra); layer_calls
+    holds one zero-argument callable per layer forward of a step."""
+    dev = "cuda"
+    cfg = args.config
+    if cfg in (1, 2):
+        w = inputs.make_config(cfg)
+        lay = w.layers[0]
+        L = eg.Layer(lay, w.dtype, dev)
+        tok = torch.from_numpy(w.tokens).to(dev)
+        H = eg.to_device(w.H, w.dtype, dev)
+        ws = torch.empty(eg.forward_workspace(w.B, w.T, L), dtype=torch.uint8, device=dev)
+        return [lambda: eg.forward(tok, H, L, ws=ws)], w.B * w.T, w, [lay], {}
+    if cfg == 3:
+        w = inputs.make_config(3)
+        S = w.B
+        Ls = [eg.Layer(l, "bf16", dev) for l in w.layers]
+        states = [eg.DecodeState(S, 3, 1, 9, 1024, dev) for _ in Ls]
+        ctx = torch.from_numpy(w.context).to(dev)
+        Hc = eg.to_device(w.H_context, "bf16", dev)
+        for L, st in zip(Ls, states):               # prefill the context (not timed)
+            eg.forward(ctx, Hc, L, state=st)
+        tok = torch.from_numpy(w.tokens).to(dev)
+        H = eg.to_device(w.H, "bf16", dev)
+        wss = [torch.empty(eg.forward_workspace(S, 1, L), dtype=torch.uint8, device=dev) for L in Ls]
+        calls = [(lambda L=L, st=st, ws=ws: eg.forward(tok, H, L, state=st, ws=ws))
+                 for L, st, ws in zip(Ls, states, wss)]
+        return calls, S, w, w.layers, {"decode": "256 sequences x 1 token, 2 layers, after a 16-token prefill",
+                                       "_keep": (Ls, states)}
+    # cfg == 4: host tables + HBM cache
+    w = inputs.make_config(4)
+    tok = torch.from_numpy(w.tokens).to(dev)
+    H = eg.to_device(w.H, "bf16", dev)
+    Ls, bufs, hits = [], [], []
+    for li, lay in enumerate(w.layers):
+        hb = eg.HostBuffer(lay.tables.rows.nbytes)
+        hb.numpy(lay.tables.rows.dtype, lay.tables.rows.shape)[:] = lay.tables.rows
+        bufs.append(hb)
+        L = eg.Layer(lay, "bf16", dev, rows_ptr=hb.dev)
+        warm = torch.from_numpy(inputs.lfu_warmup_tokens(4, li).reshape(16, -1)).to(dev)
+        slot, rows, _ = eg.cache_build(warm, L, lay.tables.total_rows // 10)
+        L.set_cache(slot, rows)
+        z = eg.hash_indices(tok, L).long() + torch.from_numpy(lay.tables.row_offset).to(dev)
+        hits.append(round(float((slot[z] >= 0).float().mean().item()), 4))
+        Ls.append(L)
+    ws = torch.empty(max(eg.forward_workspace(w.B, w.T, L) for L in Ls), dtype=torch.uint8, device=dev)
+    calls = [(lambda L=L: eg.forward(tok, H, L, ws=ws)) for L in Ls]
+    return calls, w.B * w.T, w, w.layers, {"cache_hit_rate": hits, "_keep": (Ls, bufs)}
 
 
 def main():
@@ -79,18 +135,12 @@ def main():
     from hashed_gram_embedding_amd import engram as eg
     from hashed_gram_embedding_amd import inputs
 
-    dev = "cuda"
-    w = inputs.make_config(args.config)
-    lay = w.layers[0]
-    L = eg.Layer(lay, w.dtype, dev)
-    tok = torch.from_numpy(w.tokens).to(dev)
-    H = eg.to_device(w.H, w.dtype, dev)
-    n_tok = w.B * w.T
-    ws = torch.empty(eg.forward_workspace(w.B, w.T, L), dtype=torch.uint8, device=dev)
+    calls, n_tok, w, lays, extra = setup(args, torch, eg, inputs)
     stream = torch.cuda.current_stream()
 
     def step():
-        eg.forward(tok, H, L, ws=ws)            # on the current stream
+        for c in calls:
+            c()                                 # on the current stream
 
     for _ in range(args.warmup):
         step()
@@ -119,24 +169,26 @@ def main():
     ms = t0.elapsed_time(t1) / args.steps
 
     # per-kernel durations: HIP events that the library records on the launch
-    # stream around each kernel of the same forward (eager launches)
+    # stream around each kernel of the same forward calls (eager launches)
     eg.profile_enable(True)
-    acc = {}
+    acc, cnt = {}, {}
     for it in range(args.warmup + args.steps):
-        step()
-        for name, t in eg.profile_read():
-            if it >= args.warmup:
-                acc[name] = acc.get(name, 0.0) + t
+        for c in calls:
+            c()
+            for name, t in eg.profile_read():
+                if it >= args.warmup:
+                    acc[name] = acc.get(name, 0.0) + t
+                    cnt[name] = cnt.get(name, 0) + 1
     eg.profile_enable(False)
-    stage_ms = {k: v / args.steps for k, v in acc.items()}
+    kernel_ms = {k: acc[k] / cnt[k] for k in acc}
 
-    units = stage_units(w, lay)
+    units = kernel_units(n_tok, lays[0], w.dtype)
     rates = {}
-    for k, t in stage_ms.items():
+    for k, t in kernel_ms.items():
         if k in units:
             kind, amount = units[k]
             rates[k] = amount / (t * 1e-3) / (1e9 if kind == "hbm" else 1e12)
-    dominant = max((k for k in stage_ms if k in units), key=lambda k: stage_ms[k])
+    dominant = max((k for k in kernel_ms if k in units), key=lambda k: kernel_ms[k])
     kind, amount = units[dominant]
     if kind == "mfma":
         roof = {"bound": "mfma", "kernel": dominant, "achieved": round(rates[dominant], 2),
@@ -147,12 +199,12 @@ def main():
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(rates[dominant] / PEAK_HBM_GBPS, 4),
                 "traffic": None, "units_per_launch": amount}
     gather_gbps = rates.get("gather_kernel<hashed>")
-    gemm_tflops = rates.get("proj_gate_kernel", rates.get("gemm_kernel"))
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.config in (1, 2):
         cpu = cpu_baseline(w, args.cpu_budget_s)
 
+    lay = lays[0]
     out = {
         "metric": METRIC,
         "value": round(n_tok / (ms * 1e-3), 1),
@@ -166,24 +218,26 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) tables, N(0,1) hidden states)",
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "branches": lay.branches, "d": lay.d,
-                   "d_mem": lay.d_mem, "tables": lay.hash.n_tables, "table_rows": lay.tables.total_rows,
-                   "table_dtype": lay.tables.dtype},
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "layers_per_step": len(calls), "branches": lay.branches,
+                   "d": lay.d, "d_mem": lay.d_mem, "tables": lay.hash.n_tables,
+                   "table_rows": int(lay.tables.n_rows.sum()), "table_dtype": lay.tables.dtype},
         "timing": "HIP graph replay" if graph is not None else "eager launches",
         "gather_GBps": None if gather_gbps is None else round(gather_gbps, 1),
-        "gemm_TFLOPs": None if gemm_tflops is None else round(gemm_tflops, 2),
-        "kernel_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
         "kernel_rate": {k: round(v, 2) for k, v in rates.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    for k, v in extra.items():
+        if not k.startswith("_"):
+            out[k] = v
     print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(w, budget_s):
     """The CPU oracle (float64, numpy) on a bounded sample of the same workload:
-    whole forward passes over the first T_s tokens, repeated until the budget is
-    used; reported as tokens/s."""
+    whole forward passes over the first 1024 tokens of sequence 0, repeated
+    until the time budget is used; reported as tokens/s."""
     from oracle import engram_oracle as orc
     try:
         from threadpoolctl import threadpool_info
@@ -200,7 +254,7 @@ def cpu_baseline(w, budget_s):
         orc.forward(tok, Hs, lay, w.dtype)
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 50:
+        if el >= budget_s:
             break
     return {"value": round(n * Ts / el, 1), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{n} forward passes of the float64 oracle over the first {Ts} tokens of sequence 0 "

@@ -1,0 +1,131 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times.  The oracle recomputes sampled windows (with the 11-position
+halo that makes a window exact), sampled decode sequences, and the exact LFU
+admission; everything else is compared element by element on those samples."""
+import numpy as np
+import pytest
+import torch
+
+from hashed_gram_embedding_amd import engram as eg
+from hashed_gram_embedding_amd import inputs
+from oracle import engram_oracle as orc
+
+from parity import check_bf16_layer, log, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+HALO = 11   # (N-1) + (w-1)*N positions of history determine a position's output
+
+
+def check_windows(w, lay, a_g, y_g, h_g, starts, rows, L=64, tag=""):
+    h_in = orc.storage_to_f64(w.H, w.dtype)
+    for b in rows:
+        for s in starts:
+            lo = max(0, s - HALO)
+            ref = orc.forward(w.tokens[b:b + 1, lo:s + L], w.H[b:b + 1, lo:s + L], lay, w.dtype)
+            k = s - lo
+            check_bf16_layer(a_g[b:b + 1, s:s + L], ref["alpha"][:, k:], y_g[b:b + 1, s:s + L], ref["Y"][:, k:],
+                             h_g[b:b + 1, s:s + L], h_in[b:b + 1, s:s + L], tag=f"{tag} b{b} s{s}")
+
+
+def test_multi_branch_full_size_sampled():
+    """B = 8, T = 4096, M = 4 branches (shared W_V, four W_K^(m), per-branch
+    gate and conv), the full 10.3M-row tables."""
+    log("multi-branch full size: inputs")
+    w = inputs.make_config(2)
+    lay = w.layers[0]
+    L = eg.Layer(lay, "bf16", DEV)
+    H = eg.to_device(w.H, "bf16", DEV)
+    log("multi-branch full size: forward")
+    alpha, y = eg.forward(torch.from_numpy(w.tokens).to(DEV), H, L, want_alpha=True, want_y=True)
+    torch.cuda.synchronize()
+    starts = [0, 777, 2048, 4096 - 64]
+    rows = [0, 3, 7]
+    # bring only the sampled windows to the host
+    a_g = np.zeros((8, 4096, 4))
+    y_g = np.zeros((8, 4096, 4, 1024))
+    h_g = np.zeros((8, 4096, 4, 1024))
+    for b in rows:
+        for s in starts:
+            a_g[b, s:s + 64] = to_f64(alpha[b, s:s + 64])
+            y_g[b, s:s + 64] = to_f64(y[b, s:s + 64])
+            h_g[b, s:s + 64] = to_f64(H[b, s:s + 64])
+    log("multi-branch full size: oracle windows")
+    check_windows(w, lay, a_g, y_g, h_g, starts, rows, tag="c2")
+
+
+def test_decode_full_size_sampled():
+    """256 sequences, int8 rows with per-row scales (703 MB per layer), each
+    of the 2 layers: a 16-token prefill with state, then 3 single-token decode
+    steps; sampled sequences match the oracle at every step and the state's
+    ids and positions match exactly."""
+    log("decode full size: inputs")
+    w = inputs.make_config(3, T=3)
+    S = w.B
+    sample = [0, 1, 100, 255]
+    for li, lay in enumerate(w.layers):
+        log(f"decode full size: layer {li}")
+        L = eg.Layer(lay, "bf16", DEV)
+        st = eg.DecodeState(S, 3, 1, 9, 1024, DEV)
+        ost = orc.new_state(len(sample), 3, 1, 9, 1024)
+        chunks = [(w.context, w.H_context)] + [(w.tokens[:, t:t + 1], w.H[:, t:t + 1]) for t in range(3)]
+        for ci, (tok, Hn) in enumerate(chunks):
+            H = eg.to_device(Hn, "bf16", DEV)
+            alpha, y = eg.forward(torch.from_numpy(np.ascontiguousarray(tok)).to(DEV), H, L, state=st,
+                                  want_alpha=True, want_y=True)
+            ref = orc.forward(tok[sample], Hn[sample], lay, "bf16", state=ost)
+            ost = ref["state"]
+            check_bf16_layer(to_f64(alpha[sample]), ref["alpha"], to_f64(y[sample]), ref["Y"], to_f64(H[sample]),
+                             orc.bf16_to_f64(Hn[sample]), tag=f"layer{li} chunk{ci}")
+        assert np.array_equal(st.ids.cpu().numpy()[sample], ost["ids"])
+        assert np.all(st.pos.cpu().numpy() == 16 + 3)
+
+
+def test_host_table_full_size_with_cache():
+    """One layer of 33,556,876 bf16 rows (4.3 GB) in pinned host memory, an
+    HBM cache of 10 % of the rows admitted from a 2^22-token warm-up (exact
+    LFU ranking checked against the oracle), and a B = 4, T = 4096 forward
+    that equals the HBM-table forward bit for bit and matches the oracle on
+    sampled windows."""
+    log("host table full size: inputs")
+    w = inputs.make_config(4, layers=1)
+    lay = w.layers[0]
+    tab = lay.tables
+    hb = eg.HostBuffer(tab.rows.nbytes)
+    try:
+        hb.numpy(tab.rows.dtype, tab.rows.shape)[:] = tab.rows
+        L = eg.Layer(lay, "bf16", DEV, rows_ptr=hb.dev)
+        warm = inputs.lfu_warmup_tokens(4, 0, n=1 << 22).reshape(16, -1)
+        n_cache = tab.total_rows // 10
+        log("host table full size: cache build")
+        slot, rows, _ = eg.cache_build(torch.from_numpy(warm).to(DEV), L, n_cache)
+        hp = lay.hash
+        z = orc.hash_indices(warm, hp.proj, hp.mult, hp.prime, 3, hp.heads)
+        ref_slot = orc.lfu_admission(z + tab.row_offset, tab.total_rows, n_cache)
+        assert np.array_equal(slot.cpu().numpy(), ref_slot)
+        L.set_cache(slot, rows)
+        tok = torch.from_numpy(w.tokens).to(DEV)
+        H0 = eg.to_device(w.H, "bf16", DEV)
+        H = H0.clone()
+        log("host table full size: forward")
+        alpha, y = eg.forward(tok, H, L, want_alpha=True, want_y=True)
+        L_dev = eg.Layer(lay, "bf16", DEV)
+        H2 = H0.clone()
+        eg.forward(tok, H2, L_dev)
+        torch.cuda.synchronize()
+        assert torch.equal(H.view(torch.int16), H2.view(torch.int16))
+        del L_dev
+        starts, rows_b = [0, 1500, 4096 - 64], [0, 3]
+        a_g = np.zeros((4, 4096, 1))
+        y_g = np.zeros((4, 4096, 1, 1024))
+        h_g = np.zeros((4, 4096, 1, 1024))
+        for b in rows_b:
+            for s in starts:
+                a_g[b, s:s + 64] = to_f64(alpha[b, s:s + 64])
+                y_g[b, s:s + 64] = to_f64(y[b, s:s + 64])
+                h_g[b, s:s + 64] = to_f64(H[b, s:s + 64])
+        check_windows(w, lay, a_g, y_g, h_g, starts, rows_b, tag="c4")
+    finally:
+        torch.cuda.synchronize()
+        hb.free()
