@@ -273,6 +273,172 @@ conv_kernel(ConvArgs a) {
   }
 }
 
+// Strip conv for a compile-time kernel width and dilation (the pages' w = 4,
+// dilation N = 3).  A workgroup owns TS consecutive tokens x up to 1024
+// channels (4 per thread) of one branch of one sequence.  Every load is issued
+// up front: the TS + (KW-1)*DIL rows of v this strip needs (halo rows before the
+// chunk come from the decode state, already as u), the thread's H values and
+// the rows' gate statistics.  The statistics are reduced by 16 lanes per row
+// into alpha and gamma in LDS (the only barrier); the dilated taps then read
+// registers whose indices are fixed at compile time.
+template <int HT, int VT, int KW, int DIL, int TS>
+__global__ void __launch_bounds__(256)
+conv_strip_kernel(ConvArgs a) {
+  constexpr int SPAN = (KW - 1) * DIL;
+  constexpr int R = TS + SPAN;                 // rows this strip reads
+  constexpr int kStatLanes = 16;               // lanes reducing one row's statistics
+  constexpr int kStatRows = 256 / kStatLanes;  // rows reduced per pass
+  __shared__ float alpha_s[R];
+  __shared__ float gamma_s[R];
+  const GateConvArgs& g = a.g;
+  const int M = g.branches;
+  const int d = g.d;
+  const int64_t T = a.T;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TS;
+  const int b = blockIdx.y / M;
+  const int m = blockIdx.y - b * M;
+  const int tid = threadIdx.x;
+  const int c = (blockIdx.z * 256 + tid) * 4;  // this thread's 4 channels
+  const bool active = c < d;
+  const int cc = active ? c : 0;               // a valid column for idle threads' loads
+  const int32_t pos0 = a.has_state ? a.st.pos[b] : 0;
+  const int64_t row0 = static_cast<int64_t>(b) * T;
+  const int nqb = a.qv + a.qk;
+
+  // ---- issue every load ----
+  float4 v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t t = t0 - SPAN + r;
+    if (t < 0 && a.has_state) {
+      // halo before the chunk: the state's circular slot of position pos0 + t
+      int slot = static_cast<int>((static_cast<int64_t>(pos0) + t) % SPAN);
+      if (slot < 0) slot += SPAN;
+      v[r] = *reinterpret_cast<const float4*>(a.st.conv + ((static_cast<int64_t>(b) * M + m) * SPAN + slot) * d + cc);
+    } else {
+      const int64_t tc = t < 0 ? 0 : (t >= T ? T - 1 : t);
+      v[r] = load4<VT>(a.v, (row0 + tc) * a.v_stride + cc);
+    }
+  }
+  float4 h[TS];
+#pragma unroll
+  for (int k = 0; k < TS; ++k) {
+    const int64_t t = t0 + k < T ? t0 + k : T - 1;
+    h[k] = load4<HT>(a.H, ((row0 + t) * M + m) * d + cc);
+  }
+  float wt[4][KW];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < KW; ++j) wt[i][j] = g.conv_w[(static_cast<int64_t>(m) * d + cc + i) * KW + j];
+
+  // ---- alpha and gamma of the R rows: 16 lanes per row, shuffle reduction.
+  // A lane loads up to kMaxQ statistics per pass (nqb <= 16 * kMaxQ = 64); all
+  // passes' loads are issued before any is used. ----
+  constexpr int kPasses = (R + kStatRows - 1) / kStatRows;
+  constexpr int kMaxQ = 4;
+  const int q0 = tid % kStatLanes;
+  float4 sp[kPasses][kMaxQ];
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int r = pass * kStatRows + tid / kStatLanes;
+    const int64_t t = t0 - SPAN + r;
+    const int64_t tc = t < 0 ? 0 : (t >= T ? T - 1 : t);
+    const float4* st = a.stats + (row0 + tc) * a.nq;
+#pragma unroll
+    for (int i = 0; i < kMaxQ; ++i) {
+      const int q = q0 + i * kStatLanes;
+      const int qc = q < nqb ? q : 0;
+      sp[pass][i] = st[qc < a.qv ? qc : a.qv + m * a.qk + (qc - a.qv)];
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int r = pass * kStatRows + tid / kStatLanes;
+    const int64_t t = t0 - SPAN + r;
+    const bool in_chunk = r < R && t >= 0 && t < T;
+    float svv = 0.f, shh = 0.f, skk = 0.f, shk = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxQ; ++i) {
+      const int q = q0 + i * kStatLanes;
+      const float4 p = sp[pass][i];
+      if (q < a.qv) {
+        svv += p.w;
+      } else if (q < nqb) {
+        shh += p.x;
+        skk += p.y;
+        shk += p.z;
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < kStatLanes; off <<= 1) {
+      svv += __shfl_xor(svv, off, 64);
+      shh += __shfl_xor(shh, off, 64);
+      skk += __shfl_xor(skk, off, 64);
+      shk += __shfl_xor(shk, off, 64);
+    }
+    if (q0 == 0 && r < R) {
+      float al = 0.f, gm = 0.f;
+      if (in_chunk) {
+        const float inv_d = 1.0f / static_cast<float>(d);
+        const float rh = 1.0f / sqrtf(shh * inv_d + g.eps);
+        const float rk = 1.0f / sqrtf(skk * inv_d + g.eps);
+        const float logit = shk * rh * rk / sqrtf(static_cast<float>(d));
+        al = 1.0f / (1.0f + expf(-logit));
+        gm = al / sqrtf(al * al * (svv * inv_d) + g.eps);
+        if (blockIdx.z == 0 && r >= SPAN) {
+          const int64_t o = (row0 + t) * M + m;
+          if (a.alpha_out != nullptr) a.alpha_out[o] = al;
+          if (a.gamma_out != nullptr) a.gamma_out[o] = gm;
+        }
+      } else if (t < 0 && a.has_state) {
+        gm = 1.0f;  // the state holds u itself
+      }
+      alpha_s[r] = al;
+      gamma_s[r] = gm;
+    }
+  }
+  __syncthreads();
+
+  // ---- u = gamma v, dilated causal taps, SiLU, residual ----
+  float4 u[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float gm = gamma_s[r];
+    u[r] = make_float4(gm * v[r].x, gm * v[r].y, gm * v[r].z, gm * v[r].w);
+  }
+#pragma unroll
+  for (int k = 0; k < TS; ++k) {
+    const int64_t t = t0 + k;
+    const int r = SPAN + k;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < KW; ++j) {
+      const float4 x = u[r - (KW - 1 - j) * DIL];
+      acc.x += wt[0][j] * x.x;
+      acc.y += wt[1][j] * x.y;
+      acc.z += wt[2][j] * x.z;
+      acc.w += wt[3][j] * x.w;
+    }
+    const float al = alpha_s[r];
+    float4 y;
+    y.x = acc.x / (1.0f + expf(-acc.x)) + al * v[r].x;
+    y.y = acc.y / (1.0f + expf(-acc.y)) + al * v[r].y;
+    y.z = acc.z / (1.0f + expf(-acc.z)) + al * v[r].z;
+    y.w = acc.w / (1.0f + expf(-acc.w)) + al * v[r].w;
+    if (active && t < T) {
+      const int64_t ho = ((row0 + t) * M + m) * d + c;
+      float4 hn = h[k];
+      hn.x += y.x;
+      hn.y += y.y;
+      hn.z += y.z;
+      hn.w += y.w;
+      store4<HT>(a.H, ho, hn);
+      if (a.y_out != nullptr) *reinterpret_cast<float4*>(a.y_out + ho) = y;
+    }
+  }
+}
+
 // After the conv: the chunk's last (w-1)*dilation conv inputs go to their
 // circular slots, the last N-1 compressed ids shift into the history, and pos
 // advances.  One workgroup per sequence; pos is written after the block has
@@ -370,8 +536,26 @@ hipError_t launch_conv_cg(const ConvArgs& a, int vdtype, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int KW, int DIL, int TS>
+hipError_t launch_conv_strip(const ConvArgs& a, int vdtype, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((a.T + TS - 1) / TS), static_cast<unsigned>(a.B * a.g.branches),
+                  static_cast<unsigned>((a.g.d + 1023) / 1024));
+  if (a.g.hdtype == ENGRAM_BF16 && vdtype == ENGRAM_BF16)
+    hipLaunchKernelGGL((conv_strip_kernel<ENGRAM_BF16, ENGRAM_BF16, KW, DIL, TS>), grid, dim3(256), 0, s, a);
+  else if (a.g.hdtype == ENGRAM_BF16)
+    hipLaunchKernelGGL((conv_strip_kernel<ENGRAM_BF16, ENGRAM_F32, KW, DIL, TS>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((conv_strip_kernel<ENGRAM_F32, ENGRAM_F32, KW, DIL, TS>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
+  // the pages' conv (w = 4, dilation 3): strip kernel; decode steps get 1-token strips
+  if (a.g.kernel_w == 4 && a.g.dilation == 3 && a.qv + a.qk <= 64) {
+    if (a.T == 1) return launch_conv_strip<4, 3, 1>(a, vdtype, s);
+    return launch_conv_strip<4, 3, 16>(a, vdtype, s);
+  }
   switch (conv_channels(a.g.d)) {
     case 256: return launch_conv_cg<64>(a, vdtype, s);
     case 128: return launch_conv_cg<32>(a, vdtype, s);
