@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <string>
 
@@ -125,9 +126,11 @@ engram_status check_tables(const engram_tables* tab, engram::TableArgs* out) {
 
 engram_status check_gc(const engram_gate_conv_params* p, engram::GateConvArgs* out) {
   if (p == nullptr) return fail(ENGRAM_EINVAL, "gate/conv params are NULL");
-  if (p->d < 64 || p->d % 64 != 0)
-    return fail(ENGRAM_EUNSUPPORTED, "gate/conv: d=%d must be a positive multiple of 64", p->d);
+  if (p->d < 64 || p->d % 64 != 0 || p->d > ENGRAM_MAX_D)
+    return fail(ENGRAM_EUNSUPPORTED, "gate/conv: d=%d must be a multiple of 64 in [64, %d]", p->d, ENGRAM_MAX_D);
   if (p->branches < 1) return fail(ENGRAM_EINVAL, "gate/conv: branches must be >= 1");
+  if (p->branches > ENGRAM_MAX_BRANCHES)
+    return fail(ENGRAM_EUNSUPPORTED, "gate/conv: branches=%d above %d", p->branches, ENGRAM_MAX_BRANCHES);
   if (p->kernel_w < 2 || p->kernel_w > ENGRAM_MAX_KERNEL_W)
     return fail(ENGRAM_EUNSUPPORTED, "gate/conv: kernel_w=%d outside [2, %d]", p->kernel_w, ENGRAM_MAX_KERNEL_W);
   if (p->dilation < 1 || (p->kernel_w - 1) * p->dilation > ENGRAM_MAX_CONV_SPAN)
@@ -378,6 +381,8 @@ ENGRAM_API engram_status engram_gate_conv_forward(void* H, const void* kv, int64
   if (r != ENGRAM_OK) return r;
   if ((r = check_state(st, false)) != ENGRAM_OK) return r;
   if (B < 0 || T < 0) return fail(ENGRAM_EINVAL, "gate_conv: B and T must be >= 0");
+  if (T > INT32_MAX) return fail(ENGRAM_EUNSUPPORTED, "gate_conv: T above 2^31-1 tokens per sequence");
+  if (B > 65535) return fail(ENGRAM_EUNSUPPORTED, "gate_conv: B above 65535 sequences per call");
   if (B * T == 0) return ENGRAM_OK;
   if (H == nullptr || kv == nullptr) return fail(ENGRAM_EINVAL, "gate_conv: H and kv must be non-NULL");
   if (!aligned(H, 16) || !aligned(kv, 16)) return fail(ENGRAM_EINVAL, "gate_conv: H and kv must be 16-byte aligned");
@@ -412,6 +417,8 @@ ENGRAM_API engram_status engram_forward(const int32_t* tokens, void* H, int64_t 
   if (r != ENGRAM_OK) return r;
   if ((r = check_state(st, true)) != ENGRAM_OK) return r;
   if (B < 0 || T < 0) return fail(ENGRAM_EINVAL, "forward: B and T must be >= 0");
+  if (T > INT32_MAX) return fail(ENGRAM_EUNSUPPORTED, "forward: T above 2^31-1 tokens per sequence");
+  if (B > 65535) return fail(ENGRAM_EUNSUPPORTED, "forward: B above 65535 sequences per call");
   const int64_t n_tok = B * T;
   if (n_tok == 0) return ENGRAM_OK;
   if (tokens == nullptr || H == nullptr) return fail(ENGRAM_EINVAL, "forward: tokens and H must be non-NULL");
@@ -449,7 +456,7 @@ ENGRAM_API engram_status engram_forward(const int32_t* tokens, void* H, int64_t 
     prof_mark(stream, "proj_gate_kernel");
     r = hip_status(engram::launch_proj_gate(pa, stream), "projection launch");
     if (r != ENGRAM_OK) return r;
-    const int q = d / engram::kProjGateTileF;
+    const int q = d / engram::proj_gate_tile_f(n_tok, static_cast<int>(n_out), d);
     return run_conv_commit(H, f.kv, d, ENGRAM_F32, f.stats, q, q, B, T, g, st, tokens, L->hash.proj,
                            L->hash.max_n, alpha_out, f.gamma, y_out, stream);
   }

@@ -11,12 +11,26 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float -> bfloat16 bits, round to nearest, ties to even (NaN stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// float -> bfloat16 bits with gfx950's conversion instruction
+// (v_cvt_pk_bf16_f32): round to nearest, ties to even; NaN stays NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two floats -> two bfloat16 in one word (lo in bits 0-15), one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// SiLU(x) = x / (1 + e^-x) from the hardware exp2 and reciprocal (about one
+// ulp each): e^-x = 2^(-x log2 e).  Large |x| saturate correctly: 2^(+big)
+// = inf gives x * 0, 2^(-big) = 0 gives x.
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * x));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -39,8 +53,7 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
   uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    w[i] = static_cast<uint32_t>(f32_to_bf16(f[2 * i])) |
-           (static_cast<uint32_t>(f32_to_bf16(f[2 * i + 1])) << 16);
+    w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 

@@ -77,7 +77,7 @@ struct ProjGateArgs {
   const uint16_t* w;  // [N][K] bf16, N = (1+M)*d
   const uint16_t* H;  // [n_tok][M][d] bf16 (read only)
   float* v;           // [n_tok][d]
-  float4* stats;      // [n_tok][N/128]
+  float4* stats;      // [n_tok][N/TF], TF = proj_gate_tile_f(n_tok, N, d)
   int64_t n_tok;
   int K;
   int N;
@@ -86,7 +86,8 @@ struct ProjGateArgs {
   int tiles_f;  // set by the launcher
   int tiles_t;  // set by the launcher
 };
-constexpr int kProjGateTileF = 128;  // feature columns per gate-statistics tile
+constexpr int kProjGateTileF = 128;  // narrowest feature tile (bounds the statistics buffer)
+int proj_gate_tile_f(int64_t n_tok, int N, int d);   // feature columns per gate-statistics tile
 hipError_t launch_proj_gate(const ProjGateArgs& a, hipStream_t s);
 
 // Whole-row gate statistics from given projections: stats [n_tok][1+M].

@@ -47,11 +47,58 @@ __device__ __forceinline__ float4 load4(const void* base, int64_t off) {
 template <int DT>
 __device__ __forceinline__ void store4(void* base, int64_t off, float4 f) {
   if constexpr (DT == ENGRAM_BF16) {
-    const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(f.x)) | (static_cast<uint32_t>(f32_to_bf16(f.y)) << 16);
-    const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(f.z)) | (static_cast<uint32_t>(f32_to_bf16(f.w)) << 16);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + off) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + off) =
+        make_uint2(pack_bf16x2(f.x, f.y), pack_bf16x2(f.z, f.w));
   } else {
     *reinterpret_cast<float4*>(static_cast<float*>(base) + off) = f;
+  }
+}
+
+// CPT (2 or 4) consecutive elements, starting at column col of a row, as
+// floats.  The row pointer is uniform across the workgroup and col is 32-bit,
+// so the access is a scalar base plus a per-lane 32-bit offset.
+template <int DT, int CPT>
+__device__ __forceinline__ void loadc(const void* row, uint32_t col, float (&f)[CPT]) {
+  static_assert(CPT == 2 || CPT == 4, "2 or 4 channels per thread");
+  if constexpr (DT == ENGRAM_BF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(row) + col;
+    if constexpr (CPT == 4) {
+      const uint2 q = *reinterpret_cast<const uint2*>(p);
+      f[0] = __uint_as_float(q.x << 16);
+      f[1] = __uint_as_float(q.x & 0xffff0000u);
+      f[2] = __uint_as_float(q.y << 16);
+      f[3] = __uint_as_float(q.y & 0xffff0000u);
+    } else {
+      const uint32_t q = *reinterpret_cast<const uint32_t*>(p);
+      f[0] = __uint_as_float(q << 16);
+      f[1] = __uint_as_float(q & 0xffff0000u);
+    }
+  } else {
+    const float* p = static_cast<const float*>(row) + col;
+    if constexpr (CPT == 4) {
+      const float4 q = *reinterpret_cast<const float4*>(p);
+      f[0] = q.x; f[1] = q.y; f[2] = q.z; f[3] = q.w;
+    } else {
+      const float2 q = *reinterpret_cast<const float2*>(p);
+      f[0] = q.x; f[1] = q.y;
+    }
+  }
+}
+
+template <int DT, int CPT>
+__device__ __forceinline__ void storec(void* row, uint32_t col, const float (&f)[CPT]) {
+  if constexpr (DT == ENGRAM_BF16) {
+    uint16_t* p = static_cast<uint16_t*>(row) + col;
+    if constexpr (CPT == 4)
+      *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+    else
+      *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(f[0], f[1]);
+  } else {
+    float* p = static_cast<float*>(row) + col;
+    if constexpr (CPT == 4)
+      *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+    else
+      *reinterpret_cast<float2*>(p) = make_float2(f[0], f[1]);
   }
 }
 
@@ -258,10 +305,10 @@ conv_kernel(ConvArgs a) {
     const float al = alpha_s[r];
     const float4 v = tile[r * CG + q];
     float4 y;
-    y.x = acc.x / (1.0f + expf(-acc.x)) + al * v.x;
-    y.y = acc.y / (1.0f + expf(-acc.y)) + al * v.y;
-    y.z = acc.z / (1.0f + expf(-acc.z)) + al * v.z;
-    y.w = acc.w / (1.0f + expf(-acc.w)) + al * v.w;
+    y.x = silu(acc.x) + al * v.x;
+    y.y = silu(acc.y) + al * v.y;
+    y.z = silu(acc.z) + al * v.z;
+    y.w = silu(acc.w) + al * v.w;
     const int64_t ho = ((static_cast<int64_t>(b) * T + t) * M + m) * d + c;
     float4 hn = h[n];
     hn.x += y.x;
@@ -274,16 +321,22 @@ conv_kernel(ConvArgs a) {
 }
 
 // Strip conv for a compile-time kernel width and dilation (the pages' w = 4,
-// dilation N = 3).  A workgroup owns TS consecutive tokens x up to 1024
-// channels (4 per thread) of one branch of one sequence.  Every load is issued
-// up front: the TS + (KW-1)*DIL rows of v this strip needs (halo rows before the
+// dilation N = 3).  A workgroup owns TS consecutive tokens x 256*CPT channels
+// (CPT per thread) of one branch of one sequence.  Every load is issued up
+// front: the TS + (KW-1)*DIL rows of v this strip needs (halo rows before the
 // chunk come from the decode state, already as u), the thread's H values and
 // the rows' gate statistics.  The statistics are reduced by 16 lanes per row
 // into alpha and gamma in LDS (the only barrier); the dilated taps then read
 // registers whose indices are fixed at compile time.
-template <int HT, int VT, int KW, int DIL, int TS>
+//
+// Workgroup order: with spx > 0, workgroup i runs on XCD i % 8 (the hardware
+// dispatches round robin) and XCD x owns strips [x*spx, (x+1)*spx), branches
+// innermost, so the halo rows shared by neighbouring strips and the v rows
+// shared by a strip's M branches are read through one L2.  spx == 0 (fewer
+// strips than XCDs) keeps the plain order.
+template <int HT, int VT, int KW, int DIL, int TS, int CPT>
 __global__ void __launch_bounds__(256)
-conv_strip_kernel(ConvArgs a) {
+conv_strip_kernel(ConvArgs a, int spx) {
   constexpr int SPAN = (KW - 1) * DIL;
   constexpr int R = TS + SPAN;                 // rows this strip reads
   constexpr int kStatLanes = 16;               // lanes reducing one row's statistics
@@ -294,43 +347,73 @@ conv_strip_kernel(ConvArgs a) {
   const int M = g.branches;
   const int d = g.d;
   const int64_t T = a.T;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TS;
-  const int b = blockIdx.y / M;
-  const int m = blockIdx.y - b * M;
+  int strip, m;
+  {
+    const int L = blockIdx.x;
+    if (spx > 0) {
+      const int k = L >> 3;
+      m = k % M;
+      strip = (L & 7) * spx + k / M;
+      if (static_cast<int64_t>(strip) * TS >= T) return;   // padding workgroup: no barrier reached yet
+    } else {
+      m = L % M;
+      strip = L / M;
+    }
+  }
+  // Sequences are shorter than 2^31 tokens and rows shorter than 2^31 bytes
+  // (checked by the host), so positions and row strides are 32-bit; each row's
+  // address is one uniform 64-bit base plus a 32 x 32-bit product.
+  constexpr int kVB = VT == ENGRAM_BF16 ? 2 : 4;
+  constexpr int kHB = HT == ENGRAM_BF16 ? 2 : 4;
+  const int Ti = static_cast<int>(T);
+  const int t0 = strip * TS;
+  const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int c = (blockIdx.z * 256 + tid) * 4;  // this thread's 4 channels
-  const bool active = c < d;
-  const int cc = active ? c : 0;               // a valid column for idle threads' loads
-  const int32_t pos0 = a.has_state ? a.st.pos[b] : 0;
+  const uint32_t c = (blockIdx.z * 256 + tid) * CPT;  // this thread's CPT channels
+  const bool active = c < static_cast<uint32_t>(d);
+  const uint32_t cc = active ? c : 0;                 // a valid column for idle threads' loads
   const int64_t row0 = static_cast<int64_t>(b) * T;
+  const char* vseq = static_cast<const char*>(a.v) + row0 * a.v_stride * kVB;
+  const int vrow = static_cast<int>(a.v_stride) * kVB;
+  char* hseq = static_cast<char*>(a.H) + (row0 * M + m) * d * kHB;
+  const int hrow = M * d * kHB;
   const int nqb = a.qv + a.qk;
 
   // ---- issue every load ----
-  float4 v[R];
+  float v[R][CPT];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t t = t0 - SPAN + r;
-    if (t < 0 && a.has_state) {
-      // halo before the chunk: the state's circular slot of position pos0 + t
-      int slot = static_cast<int>((static_cast<int64_t>(pos0) + t) % SPAN);
+    const int t = t0 - SPAN + r;
+    if (r < SPAN && t < 0 && a.has_state) {
+      // halo before the chunk: the state's circular slot of position pos + t
+      int slot = static_cast<int>((static_cast<int64_t>(a.st.pos[b]) + t) % SPAN);
       if (slot < 0) slot += SPAN;
-      v[r] = *reinterpret_cast<const float4*>(a.st.conv + ((static_cast<int64_t>(b) * M + m) * SPAN + slot) * d + cc);
+      loadc<ENGRAM_F32, CPT>(a.st.conv + ((static_cast<int64_t>(b) * M + m) * SPAN + slot) * d, cc, v[r]);
     } else {
-      const int64_t tc = t < 0 ? 0 : (t >= T ? T - 1 : t);
-      v[r] = load4<VT>(a.v, (row0 + tc) * a.v_stride + cc);
+      const int tc = t < 0 ? 0 : (t >= Ti ? Ti - 1 : t);
+      loadc<VT, CPT>(vseq + static_cast<int64_t>(tc) * vrow, cc, v[r]);
     }
   }
-  float4 h[TS];
+  float h[TS][CPT];
 #pragma unroll
   for (int k = 0; k < TS; ++k) {
-    const int64_t t = t0 + k < T ? t0 + k : T - 1;
-    h[k] = load4<HT>(a.H, ((row0 + t) * M + m) * d + cc);
+    const int t = t0 + k < Ti ? t0 + k : Ti - 1;
+    loadc<HT, CPT>(hseq + static_cast<int64_t>(t) * hrow, cc, h[k]);
   }
-  float wt[4][KW];
+  float wt[CPT][KW];
+  {
+    const float* wm = g.conv_w + static_cast<int64_t>(m) * d * KW;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < CPT; ++i) {
+      if constexpr (KW == 4) {
+        const float4 q = *reinterpret_cast<const float4*>(wm + (cc + i) * KW);
+        wt[i][0] = q.x; wt[i][1] = q.y; wt[i][2] = q.z; wt[i][3] = q.w;
+      } else {
 #pragma unroll
-    for (int j = 0; j < KW; ++j) wt[i][j] = g.conv_w[(static_cast<int64_t>(m) * d + cc + i) * KW + j];
+        for (int j = 0; j < KW; ++j) wt[i][j] = wm[(cc + i) * KW + j];
+      }
+    }
+  }
 
   // ---- alpha and gamma of the R rows: 16 lanes per row, shuffle reduction.
   // A lane loads up to kMaxQ statistics per pass (nqb <= 16 * kMaxQ = 64); all
@@ -342,8 +425,8 @@ conv_strip_kernel(ConvArgs a) {
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
     const int r = pass * kStatRows + tid / kStatLanes;
-    const int64_t t = t0 - SPAN + r;
-    const int64_t tc = t < 0 ? 0 : (t >= T ? T - 1 : t);
+    const int t = t0 - SPAN + r;
+    const int tc = t < 0 ? 0 : (t >= Ti ? Ti - 1 : t);
     const float4* st = a.stats + (row0 + tc) * a.nq;
 #pragma unroll
     for (int i = 0; i < kMaxQ; ++i) {
@@ -355,8 +438,8 @@ conv_strip_kernel(ConvArgs a) {
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
     const int r = pass * kStatRows + tid / kStatLanes;
-    const int64_t t = t0 - SPAN + r;
-    const bool in_chunk = r < R && t >= 0 && t < T;
+    const int t = t0 - SPAN + r;
+    const bool in_chunk = r < R && t >= 0 && t < Ti;
     float svv = 0.f, shh = 0.f, skk = 0.f, shk = 0.f;
 #pragma unroll
     for (int i = 0; i < kMaxQ; ++i) {
@@ -401,40 +484,30 @@ conv_strip_kernel(ConvArgs a) {
   __syncthreads();
 
   // ---- u = gamma v, dilated causal taps, SiLU, residual ----
-  float4 u[R];
+  float u[R][CPT];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float gm = gamma_s[r];
-    u[r] = make_float4(gm * v[r].x, gm * v[r].y, gm * v[r].z, gm * v[r].w);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) u[r][i] = gm * v[r][i];
   }
 #pragma unroll
   for (int k = 0; k < TS; ++k) {
-    const int64_t t = t0 + k;
+    const int t = t0 + k;
     const int r = SPAN + k;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int j = 0; j < KW; ++j) {
-      const float4 x = u[r - (KW - 1 - j) * DIL];
-      acc.x += wt[0][j] * x.x;
-      acc.y += wt[1][j] * x.y;
-      acc.z += wt[2][j] * x.z;
-      acc.w += wt[3][j] * x.w;
-    }
     const float al = alpha_s[r];
-    float4 y;
-    y.x = acc.x / (1.0f + expf(-acc.x)) + al * v[r].x;
-    y.y = acc.y / (1.0f + expf(-acc.y)) + al * v[r].y;
-    y.z = acc.z / (1.0f + expf(-acc.z)) + al * v[r].z;
-    y.w = acc.w / (1.0f + expf(-acc.w)) + al * v[r].w;
-    if (active && t < T) {
-      const int64_t ho = ((row0 + t) * M + m) * d + c;
-      float4 hn = h[k];
-      hn.x += y.x;
-      hn.y += y.y;
-      hn.z += y.z;
-      hn.w += y.w;
-      store4<HT>(a.H, ho, hn);
-      if (a.y_out != nullptr) *reinterpret_cast<float4*>(a.y_out + ho) = y;
+    float y[CPT], hn[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < KW; ++j) acc += wt[i][j] * u[r - (KW - 1 - j) * DIL][i];
+      y[i] = silu(acc) + al * v[r][i];
+      hn[i] = h[k][i] + y[i];
+    }
+    if (active && t < Ti) {
+      storec<HT, CPT>(hseq + static_cast<int64_t>(t) * hrow, c, hn);
+      if (a.y_out != nullptr) storec<ENGRAM_F32, CPT>(a.y_out + ((row0 + t) * M + m) * d, c, y);
     }
   }
 }
@@ -536,16 +609,20 @@ hipError_t launch_conv_cg(const ConvArgs& a, int vdtype, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int KW, int DIL, int TS>
+template <int KW, int DIL, int TS, int CPT>
 hipError_t launch_conv_strip(const ConvArgs& a, int vdtype, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((a.T + TS - 1) / TS), static_cast<unsigned>(a.B * a.g.branches),
-                  static_cast<unsigned>((a.g.d + 1023) / 1024));
+  const int64_t n_strips = (a.T + TS - 1) / TS;
+  const int spx = n_strips >= 8 ? static_cast<int>((n_strips + 7) / 8) : 0;
+  const int64_t gx = (spx > 0 ? 8 * static_cast<int64_t>(spx) : n_strips) * a.g.branches;
+  if (gx > 0x7fffffff || a.B > 65535) return hipErrorInvalidConfiguration;   // grid limits
+  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(a.B),
+                  static_cast<unsigned>((a.g.d + 256 * CPT - 1) / (256 * CPT)));
   if (a.g.hdtype == ENGRAM_BF16 && vdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((conv_strip_kernel<ENGRAM_BF16, ENGRAM_BF16, KW, DIL, TS>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((conv_strip_kernel<ENGRAM_BF16, ENGRAM_BF16, KW, DIL, TS, CPT>), grid, dim3(256), 0, s, a, spx);
   else if (a.g.hdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((conv_strip_kernel<ENGRAM_BF16, ENGRAM_F32, KW, DIL, TS>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((conv_strip_kernel<ENGRAM_BF16, ENGRAM_F32, KW, DIL, TS, CPT>), grid, dim3(256), 0, s, a, spx);
   else
-    hipLaunchKernelGGL((conv_strip_kernel<ENGRAM_F32, ENGRAM_F32, KW, DIL, TS>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((conv_strip_kernel<ENGRAM_F32, ENGRAM_F32, KW, DIL, TS, CPT>), grid, dim3(256), 0, s, a, spx);
   return hipGetLastError();
 }
 
@@ -553,8 +630,13 @@ hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
   // the pages' conv (w = 4, dilation 3): strip kernel; decode steps get 1-token strips
   if (a.g.kernel_w == 4 && a.g.dilation == 3 && a.qv + a.qk <= 64) {
-    if (a.T == 1) return launch_conv_strip<4, 3, 1>(a, vdtype, s);
-    return launch_conv_strip<4, 3, 16>(a, vdtype, s);
+    if (a.T == 1) return launch_conv_strip<4, 3, 1, 4>(a, vdtype, s);
+    // 16-token strips of 512 channels when that gives at least 4 workgroups
+    // per CU; otherwise 4-token strips of 1024 channels (4x the workgroups,
+    // more halo re-reads, which hit L2)
+    const int64_t wg16 = a.B * a.g.branches * ((a.T + 15) / 16) * ((a.g.d + 511) / 512);
+    if (wg16 < 1024) return launch_conv_strip<4, 3, 4, 4>(a, vdtype, s);
+    return launch_conv_strip<4, 3, 16, 2>(a, vdtype, s);
   }
   switch (conv_channels(a.g.d)) {
     case 256: return launch_conv_cg<64>(a, vdtype, s);

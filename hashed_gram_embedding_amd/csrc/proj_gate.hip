@@ -13,16 +13,18 @@
 // The weight rows are the MFMA A operand and the token rows of e the B
 // operand: each lane then holds four runs of 4 consecutive features of one
 // token, so v stores are 16-byte vectors and h loads 8-byte vectors.
-// Workgroup tile: 128 features x 256 tokens with eight wavefronts of 64 x 64
-// (two per SIMD, so one wavefront's matrix work overlaps another's LDS
-// traffic); K advances 64 per step through double-buffered LDS (96 KiB) with
-// the 16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 7), which puts
-// the 16 rows of a fragment read on 16 distinct 16-byte bank groups.  The
-// next K slice is fetched to registers while the current one is multiplied,
-// and the compiler's MFMA/LDS interleaving strategy 0 orders the inner loop.
-// Tiles are ordered XCD by XCD (workgroup i runs on XCD i % 8) with the
-// feature tile fastest, so the workgroups that read the same e rows share an
-// L2.
+// Workgroup tile: TF features x 256 tokens (TF = 128, or 256 when there are
+// enough tiles to give every CU two) with eight wavefronts (two per SIMD, so
+// one wavefront's matrix work overlaps another's LDS traffic); K advances 64
+// per step through double-buffered LDS with the 16-byte chunk c of row r
+// stored at chunk c ^ ((r >> 1) & 7).  Global loads run PD slices ahead in
+// registers.  Every load is issued unconditionally (ragged token rows and
+// slices past the end re-read a valid row or slice that is never stored), so
+// the compiler's memory-counter waits stay exact and a wait for one slice
+// never drains the loads of the next.  The epilogue issues all of a token
+// block's h loads before it uses any.  Tiles are ordered XCD by XCD
+// (workgroup i runs on XCD i % 8) with the feature tile fastest, so the
+// workgroups that read the same e rows share an L2.
 #include <atomic>
 
 #include "device_util.h"
@@ -36,24 +38,24 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // 16-byte staging type: a native vector (HIP's uint4 struct copies through memory)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int TF = 128;        // features per workgroup
 constexpr int TK = 256;        // tokens per workgroup
 constexpr int BK = 64;         // K slice
 constexpr int WF = 2;          // wavefronts along features
 constexpr int WT = 4;          // wavefronts along tokens
 constexpr int kThreads = 64 * WF * WT;
 constexpr int kXcds = 8;
-constexpr int kWChunks = TF * BK / 8;    // 16-byte chunks of a W slice
-constexpr int kEChunks = TK * BK / 8;    // 16-byte chunks of an e slice
-constexpr int NW = kWChunks / kThreads;  // W chunks staged per thread
-constexpr int NE = kEChunks / kThreads;  // e chunks staged per thread
-constexpr int I = TF / WF / 32;          // 32-row feature blocks per wavefront
-constexpr int J = TK / WT / 32;          // 32-row token blocks per wavefront
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
+template <int TF, int PD>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 proj_gate_kernel(ProjGateArgs a) {
+  constexpr int kWChunks = TF * BK / 8;    // 16-byte chunks of a W slice
+  constexpr int kEChunks = TK * BK / 8;    // 16-byte chunks of an e slice
+  constexpr int NW = kWChunks / kThreads;  // W chunks staged per thread
+  constexpr int NE = kEChunks / kThreads;  // e chunks staged per thread
+  constexpr int I = TF / WF / 32;          // 32-row feature blocks per wavefront
+  constexpr int J = TK / WT / 32;          // 32-row token blocks per wavefront
   extern __shared__ u32x4_t lds[];
   u32x4_t* Ws = lds;                  // [2][kWChunks]
   u32x4_t* Es = lds + 2 * kWChunks;   // [2][kEChunks]
@@ -72,6 +74,7 @@ proj_gate_kernel(ProjGateArgs a) {
   const int wf = wave % WF;
   const int wt = wave / WF;
   const int K = a.K;
+  const int ksteps = K / BK;   // a multiple of PD (checked by the launcher)
 
   f32x16_t acc[I][J];
 #pragma unroll
@@ -81,32 +84,31 @@ proj_gate_kernel(ProjGateArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // global -> register staging of one K slice.  Token rows past the end load
-  // the last row instead (always a valid address); their results are never
-  // stored.
-  u32x4_t rw[NW], re[NE];
+  // global -> register staging, PD slices in flight.  Token rows past the end
+  // load the last row instead; their results are never stored.
+  u32x4_t rw[PD][NW], re[PD][NE];
   const uint16_t* wbase = a.w + static_cast<int64_t>(f0) * K;
-#define ENGRAM_LOAD_SLICE(k0)                                                                      \
+#define ENGRAM_LOAD_SLICE(b, k0)                                                                   \
   {                                                                                                \
     _Pragma("unroll") for (int i = 0; i < NW; ++i) {                                               \
       const int c = tid + i * kThreads;                                                            \
-      rw[i] = *reinterpret_cast<const u32x4_t*>(wbase + (c >> 3) * K + (k0) + (c & 7) * 8);        \
+      rw[b][i] = *reinterpret_cast<const u32x4_t*>(wbase + (c >> 3) * K + (k0) + (c & 7) * 8);     \
     }                                                                                              \
     _Pragma("unroll") for (int i = 0; i < NE; ++i) {                                               \
       const int c = tid + i * kThreads;                                                            \
       const int64_t tok = min(t0 + (c >> 3), a.n_tok - 1);                                         \
-      re[i] = *reinterpret_cast<const u32x4_t*>(a.e + tok * K + (k0) + (c & 7) * 8);               \
+      re[b][i] = *reinterpret_cast<const u32x4_t*>(a.e + tok * K + (k0) + (c & 7) * 8);            \
     }                                                                                              \
   }
-#define ENGRAM_STORE_SLICE(buf)                                                                    \
+#define ENGRAM_STORE_SLICE(b, buf)                                                                 \
   {                                                                                                \
     _Pragma("unroll") for (int i = 0; i < NW; ++i) {                                               \
       const int c = tid + i * kThreads;                                                            \
-      Ws[(buf) * kWChunks + swz(c >> 3, c & 7)] = rw[i];                                           \
+      Ws[(buf) * kWChunks + swz(c >> 3, c & 7)] = rw[b][i];                                        \
     }                                                                                              \
     _Pragma("unroll") for (int i = 0; i < NE; ++i) {                                               \
       const int c = tid + i * kThreads;                                                            \
-      Es[(buf) * kEChunks + swz(c >> 3, c & 7)] = re[i];                                           \
+      Es[(buf) * kEChunks + swz(c >> 3, c & 7)] = re[b][i];                                        \
     }                                                                                              \
   }
 #define ENGRAM_COMPUTE(buf)                                                                        \
@@ -124,59 +126,83 @@ proj_gate_kernel(ProjGateArgs a) {
     }                                                                                              \
   }
 
-  const int ksteps = K / BK;
-  ENGRAM_LOAD_SLICE(0);
-  ENGRAM_STORE_SLICE(0);
+#pragma unroll
+  for (int b = 0; b < PD; ++b) ENGRAM_LOAD_SLICE(b, min(b, ksteps - 1) * BK);
+  ENGRAM_STORE_SLICE(0, 0);
   __syncthreads();
-  for (int kt = 0; kt < ksteps; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < ksteps) ENGRAM_LOAD_SLICE((kt + 1) * BK);
-    ENGRAM_COMPUTE(cur);
-    if (kt + 1 < ksteps) ENGRAM_STORE_SLICE(cur ^ 1);
-    __syncthreads();
+  for (int kt0 = 0; kt0 < ksteps; kt0 += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      const int kt = kt0 + u;
+      ENGRAM_LOAD_SLICE(u, min(kt + PD, ksteps - 1) * BK);   // slice kt + PD (clamped)
+      ENGRAM_COMPUTE(kt & 1);
+      ENGRAM_STORE_SLICE((u + 1) % PD, (kt + 1) & 1);        // slice kt + 1 (unused after the last)
+      __syncthreads();
+    }
   }
 #undef ENGRAM_LOAD_SLICE
 #undef ENGRAM_STORE_SLICE
 #undef ENGRAM_COMPUTE
 
-  // ---- epilogue: acc[i][j][4g + r] is feature wf*64 + i*32 + g*8 + (lane>>5)*4 + r
-  // of token wt*64 + j*32 + (lane & 31) ----
+  // ---- epilogue: acc[i][j][4g + r] is feature wf*TF/WF + i*32 + g*8 + (lane>>5)*4 + r
+  // of token wt*TK/WT + j*32 + (lane & 31) ----
   const int d = a.d;
   const bool is_v = f0 < d;
   const int m = is_v ? 0 : f0 / d - 1;
-  const int c0 = is_v ? f0 : f0 - (1 + m) * d;   // column inside v or inside k^(m)
+  const int c0 = (is_v ? f0 : f0 - (1 + m) * d) + wf * (TF / WF) + (lane >> 5) * 4;
   float4* red = reinterpret_cast<float4*>(lds);   // [TK][WF] partials of the feature wavefronts
+  if (is_v) {
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int tl = wt * (TK / WT) + j * 32 + (lane & 31);
-    const int64_t tok = t0 + tl;
-    const bool valid = tok < a.n_tok;
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    for (int j = 0; j < J; ++j) {
+      const int tl = wt * (TK / WT) + j * 32 + (lane & 31);
+      const int64_t tok = t0 + tl;
+      float s3 = 0.f;
 #pragma unroll
-    for (int i = 0; i < I; ++i) {
+      for (int i = 0; i < I; ++i) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = c0 + wf * (TF / WF) + i * 32 + g * 8 + (lane >> 5) * 4;
-        const float x0 = acc[i][j][4 * g], x1 = acc[i][j][4 * g + 1];
-        const float x2 = acc[i][j][4 * g + 2], x3 = acc[i][j][4 * g + 3];
-        if (is_v) {
-          if (valid) *reinterpret_cast<float4*>(a.v + tok * d + col) = make_float4(x0, x1, x2, x3);
+        for (int g = 0; g < 4; ++g) {
+          const float x0 = acc[i][j][4 * g], x1 = acc[i][j][4 * g + 1];
+          const float x2 = acc[i][j][4 * g + 2], x3 = acc[i][j][4 * g + 3];
+          if (tok < a.n_tok)
+            *reinterpret_cast<float4*>(a.v + tok * d + c0 + i * 32 + g * 8) = make_float4(x0, x1, x2, x3);
           s3 += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
-        } else if (valid) {
-          const uint2 hq = *reinterpret_cast<const uint2*>(a.H + (tok * a.M + m) * d + col);
-          const float h0 = __uint_as_float(hq.x << 16), h1 = __uint_as_float(hq.x & 0xffff0000u);
-          const float h2 = __uint_as_float(hq.y << 16), h3 = __uint_as_float(hq.y & 0xffff0000u);
+        }
+      }
+      s3 += __shfl_xor(s3, 32, 64);
+      if ((lane >> 5) == 0) red[tl * WF + wf] = make_float4(0.f, 0.f, 0.f, s3);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int tl = wt * (TK / WT) + j * 32 + (lane & 31);
+      // this token block's h loads first (row clamped: always a valid address), then the sums
+      const int64_t tok = min(t0 + tl, a.n_tok - 1);
+      const uint16_t* hrow = a.H + (tok * a.M + m) * d + c0;
+      uint2 hq[I][4];
+#pragma unroll
+      for (int i = 0; i < I; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) hq[i][g] = *reinterpret_cast<const uint2*>(hrow + i * 32 + g * 8);
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < I; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float x0 = acc[i][j][4 * g], x1 = acc[i][j][4 * g + 1];
+          const float x2 = acc[i][j][4 * g + 2], x3 = acc[i][j][4 * g + 3];
+          const uint2 q = hq[i][g];
+          const float h0 = __uint_as_float(q.x << 16), h1 = __uint_as_float(q.x & 0xffff0000u);
+          const float h2 = __uint_as_float(q.y << 16), h3 = __uint_as_float(q.y & 0xffff0000u);
           s0 += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
           s1 += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
           s2 += h0 * x0 + h1 * x1 + h2 * x2 + h3 * x3;
         }
       }
+      s0 += __shfl_xor(s0, 32, 64);
+      s1 += __shfl_xor(s1, 32, 64);
+      s2 += __shfl_xor(s2, 32, 64);
+      if ((lane >> 5) == 0) red[tl * WF + wf] = make_float4(s0, s1, s2, 0.f);
     }
-    s0 += __shfl_xor(s0, 32, 64);
-    s1 += __shfl_xor(s1, 32, 64);
-    s2 += __shfl_xor(s2, 32, 64);
-    s3 += __shfl_xor(s3, 32, 64);
-    if ((lane >> 5) == 0) red[tl * WF + wf] = make_float4(s0, s1, s2, s3);
   }
   __syncthreads();
   for (int tl = tid; tl < TK; tl += kThreads) {
@@ -193,31 +219,44 @@ proj_gate_kernel(ProjGateArgs a) {
   }
 }
 
-}  // namespace
-
-size_t proj_gate_lds_bytes() { return static_cast<size_t>(2 * (kWChunks + kEChunks)) * sizeof(u32x4_t); }
-
-hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
-  if (in.n_tok == 0) return hipSuccess;
-  ProjGateArgs a = in;
+template <int TF, int PD>
+hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   a.tiles_f = a.N / TF;
   a.tiles_t = static_cast<int>((a.n_tok + TK - 1) / TK);
-  const size_t lds = proj_gate_lds_bytes();
-  // 96 KiB of dynamic LDS exceeds the default per-workgroup limit; raise it
-  // once per device (gfx950 has 160 KiB of LDS per CU).
+  const size_t lds = static_cast<size_t>(2 * (TF + TK) * BK / 8) * sizeof(u32x4_t);
+  // more than 64 KiB of dynamic LDS exceeds the default per-workgroup limit;
+  // raise it once per device and instantiation (gfx950 has 160 KiB per CU)
   static std::atomic<uint64_t> attr_set{0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if ((attr_set.load() & bit) == 0) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_kernel),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_kernel<TF, PD>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit);
   }
-  hipLaunchKernelGGL(proj_gate_kernel, dim3(a.tiles_f * a.tiles_t), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((proj_gate_kernel<TF, PD>), dim3(a.tiles_f * a.tiles_t), dim3(kThreads), lds, s, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+int proj_gate_tile_f(int64_t n_tok, int N, int d) {
+  // 256-feature tiles halve the LDS traffic per matrix operation but need at
+  // least two tiles per CU (512) to keep the chip busy
+  const int64_t tiles256 = ((n_tok + TK - 1) / TK) * (N / 256);
+  return (d % 256 == 0 && tiles256 >= 512) ? 256 : 128;
+}
+
+hipError_t launch_proj_gate(const ProjGateArgs& a, hipStream_t s) {
+  if (a.n_tok == 0) return hipSuccess;
+  if (a.K % BK != 0 || a.N % 128 != 0) return hipErrorInvalidValue;
+  const bool pd2 = (a.K / BK) % 2 == 0;
+  if (proj_gate_tile_f(a.n_tok, a.N, a.d) == 256)
+    return pd2 ? launch_tf<256, 2>(a, s) : launch_tf<256, 1>(a, s);
+  return pd2 ? launch_tf<128, 2>(a, s) : launch_tf<128, 1>(a, s);
 }
 
 }  // namespace engram

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libengram.so")
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
 F32, BF16, I8 = 0, 1, 2
 MAX_TABLES, MAX_ORDER = 32, 4
+MAX_D, MAX_BRANCHES = 65536, 64
 
 _DT = {"f32": F32, "bf16": BF16, "i8": I8}
 _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}

@@ -55,6 +55,8 @@ extern "C" {
 #define ENGRAM_MAX_ORDER 4   /* N */
 #define ENGRAM_MAX_KERNEL_W 8
 #define ENGRAM_MAX_CONV_SPAN 24 /* (kernel_w - 1) * dilation */
+#define ENGRAM_MAX_D 65536      /* d, hidden width per branch */
+#define ENGRAM_MAX_BRANCHES 64  /* M */
 
 typedef enum engram_status {
   ENGRAM_OK = 0,
@@ -108,8 +110,8 @@ typedef struct engram_tables {
 
 /* Steps 6-8: gate, short conv and residual. */
 typedef struct engram_gate_conv_params {
-  int32_t d;              /* hidden width per branch, a multiple of 64             */
-  int32_t branches;       /* M >= 1 residual branches                              */
+  int32_t d;              /* hidden width per branch, a multiple of 64, <= ENGRAM_MAX_D */
+  int32_t branches;       /* M residual branches, 1..ENGRAM_MAX_BRANCHES            */
   int32_t kernel_w;       /* conv taps w, 1..ENGRAM_MAX_KERNEL_W (pages: 4)         */
   int32_t dilation;       /* conv dilation (pages: N); (w-1)*dilation <= 24         */
   float eps;              /* RMSNorm epsilon                                       */
@@ -173,7 +175,7 @@ engram_status engram_project_kv(const void* e, const void* w, int64_t n_tok, int
                                 hipStream_t stream);
 
 /* Steps 6-8 on precomputed projections.  H: device [B][T][M][d] (hdtype),
- * read as h and overwritten with h + Y.  kv: device [B][T][(1+M)*d]
+ * read as h and overwritten with h + Y (T < 2^31, B <= 65535).  kv: device [B][T][(1+M)*d]
  * (hdtype): v, then k^(0..M-1).  st: NULL for independent sequences starting
  * at t = 0; otherwise B = S sequences continuing from st, which is advanced
  * by T tokens (its ids are left for engram_forward to update: here no tokens
@@ -188,7 +190,7 @@ engram_status engram_gate_conv_forward(void* H, const void* kv, int64_t B, int64
                                        hipStream_t stream);
 
 /* Steps 1-8 for one layer.  tokens: device int32 [B][T]; H: device
- * [B][T][M][d] updated in place.  st: as for engram_gate_conv_forward; when
+ * [B][T][M][d] updated in place (T < 2^31, B <= 65535).  st: as for engram_gate_conv_forward; when
  * given, the hash reads st->ids as the history and the state (ids, conv,
  * pos) is advanced by T tokens.  alpha_out / y_out as above.  ws: device
  * scratch of at least engram_forward_workspace() bytes, 256-byte aligned. */

@@ -192,3 +192,23 @@ def test_host_alloc_rejects_zero_bytes():
     h, d = ctypes.c_void_p(), ctypes.c_void_p()
     assert L.engram_host_alloc(0, ctypes.byref(h), ctypes.byref(d)) == eg.EINVAL
     assert L.engram_host_free(None) == eg.OK
+
+
+def test_size_limits_are_rejected_before_launch():
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    g = _gc()
+    need = L.engram_gate_conv_workspace(2, 10, ctypes.byref(g))
+    for bad in (_gc(d=eg.MAX_D + 64), _gc(branches=eg.MAX_BRANCHES + 1)):
+        assert L.engram_gate_conv_forward(p, p, 2, 10, ctypes.byref(bad), None, None, None, p, need, None) \
+            == eg.EUNSUPPORTED
+    st, msg = _status(L.engram_gate_conv_forward, p, p, 1, 2 ** 31, ctypes.byref(g), None, None, None, p, need, None)
+    assert st == eg.EUNSUPPORTED and "T above" in msg
+    st, msg = _status(L.engram_gate_conv_forward, p, p, 65536, 1, ctypes.byref(g), None, None, None, p, need, None)
+    assert st == eg.EUNSUPPORTED and "B above" in msg
+    hp, keep_h = _hash_params()
+    t, keep_t = _tables()
+    lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=64, hdtype=eg.F32))
+    need = L.engram_forward_workspace(1, 64, ctypes.byref(lay))
+    st, msg = _status(L.engram_forward, p, p, 65536, 1, ctypes.byref(lay), None, None, None, p, need, None)
+    assert st == eg.EUNSUPPORTED and "B above" in msg
