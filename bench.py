@@ -43,6 +43,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--hbm-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
+                         "run with --copy-calibration-mib into the per-kernel HBM bytes table and exit")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB device to device three times "
+                         "(a plain copy kernel of known size for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -123,9 +129,96 @@ def setup(args, torch, eg, inputs):
     calls = [(lambda L=L: eg.forward(tok, H, L, ws=ws)) for L in Ls]
     return calls, w.B * w.T, w, w.layers, {"cache_hit_rate": hits, "_keep": (Ls, bufs)}
 
+# ---- HBM traffic from rocprofv3 counters ----
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+# library stage name -> (pattern of the rocprofv3 kernel name, sources whose text fixes the kernel)
+KERNEL_SOURCES = {
+    "gather_kernel<hashed>": (r"gather_kernel<[^>]*true>", ["gather.hip", "hash_device.h"]),
+    "proj_gate_kernel": (r"proj_gate_kernel<", ["proj_gate.hip"]),
+    "conv_kernel": (r"conv_(strip_)?kernel<", ["gate_conv.hip"]),
+}
+COMMON_SOURCES = ["device_util.h", "engram_internal.h"]
+
+
+def kernel_source_hash(stage):
+    import hashlib
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES[stage][1] + COMMON_SOURCES:
+        with open(os.path.join(ROOT, "hashed_gram_embedding_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+def read_traffic_table():
+    """{(workload, stage): (fetch_bytes, write_bytes, source_hash)} from the committed table."""
+    out = {}
+    if not os.path.exists(TRAFFIC_TABLE):
+        return out
+    import re
+    for line in open(TRAFFIC_TABLE):
+        m = re.match(r"\|\s*([\w-]+)\s*\|\s*`([^`]+)`\s*\|\s*(\d+)\s*\|\s*(\d+)\s*\|\s*\d+\s*\|\s*([0-9a-f]+)\s*\|", line)
+        if m:
+            out[(m.group(1), m.group(2))] = (int(m.group(3)), int(m.group(4)), m.group(5))
+    return out
+
+
+def traffic_for(workload, stage):
+    """Measured HBM bytes per launch, or None when the table has no row for
+    the kernel or its sources changed since the counters were taken."""
+    row = read_traffic_table().get((workload, stage))
+    if row is None or stage not in KERNEL_SOURCES or row[2] != kernel_source_hash(stage):
+        return None
+    return row[0] + row[1]
+
+
+def hbm_summary(fetch_csv, write_csv, workload, n_true):
+    """Per-launch HBM bytes of each library kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) averaged over the run's dispatches, each scaled by the
+    ratio of the true bytes of the calibration copy to what the same counter
+    read for it.  Prints the table rows for this workload."""
+    import csv
+    import re
+
+    def per_kernel(path):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return acc
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+
+    # the calibration copy: the largest copyBuffer dispatch reads and writes n_true bytes
+    def copy_bytes(d):
+        vals = [max(v) for k, v in d.items() if "copyBuffer" in k]
+        return max(vals) if vals else None
+    cf, cw = copy_bytes(fetch), copy_bytes(write)
+    if cf is None or cw is None:
+        raise SystemExit("no calibration copy in the counter files (run with --copy-calibration-mib)")
+    f_scale, w_scale = n_true / cf, n_true / cw
+    rows = []
+    for stage, (pat, _) in KERNEL_SOURCES.items():
+        fk = [v for k, v in fetch.items() if re.search(pat, k)]
+        wk = [v for k, v in write.items() if re.search(pat, k)]
+        if not fk or not wk:
+            continue
+        fb = sum(fk[0]) / len(fk[0]) * f_scale
+        wb = sum(wk[0]) / len(wk[0]) * w_scale
+        rows.append((stage, int(round(fb)), int(round(wb)), len(fk[0])))
+    print(f"calibration: copy of {n_true / 2**20:.0f} MiB; FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}")
+    for stage, fb, wb, n in rows:
+        print(f"| {workload} | `{stage}` | {fb} | {wb} | {n} | {kernel_source_hash(stage)} |")
+
+
 
 def main():
     args = parse()
+    if args.hbm_summary:
+        from hashed_gram_embedding_amd import inputs
+        if args.copy_calibration_mib <= 0:
+            raise SystemExit("--hbm-summary needs --copy-calibration-mib: the size of the calibration copy")
+        hbm_summary(args.hbm_summary[0], args.hbm_summary[1], inputs.CONFIG_NAMES[args.config],
+                    args.copy_calibration_mib << 20)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part "
                                    "of this build (see the design notes on sharding)", "n_gpus": args.gpus}))
@@ -193,11 +286,11 @@ def main():
     if kind == "mfma":
         roof = {"bound": "mfma", "kernel": dominant, "achieved": round(rates[dominant], 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(rates[dominant] / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "units_per_launch": amount}
+                "traffic": traffic_for(w.name, dominant), "units_per_launch": amount}
     else:
         roof = {"bound": "hbm", "kernel": dominant, "achieved": round(rates[dominant], 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(rates[dominant] / PEAK_HBM_GBPS, 4),
-                "traffic": None, "units_per_launch": amount}
+                "traffic": traffic_for(w.name, dominant), "units_per_launch": amount}
     gather_gbps = rates.get("gather_kernel<hashed>")
 
     cpu = None
@@ -232,6 +325,14 @@ def main():
         if not k.startswith("_"):
             out[k] = v
     print(json.dumps(out), flush=True)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 def cpu_baseline(w, budget_s):

@@ -166,26 +166,44 @@ constexpr int kMaxStages = 12;
 struct Profiler {
   bool on = false;
   bool created = false;
-  int n = 0;                        // events recorded by the last profiled call
-  hipEvent_t ev[kMaxStages + 1];
+  int n = 0;                        // stages recorded by the last profiled call
+  const char* pending = nullptr;    // open stage: its kernel has not been launched yet
+  hipEvent_t start[kMaxStages];
+  hipEvent_t stop[kMaxStages];
   const char* names[kMaxStages];
 };
 
 thread_local Profiler g_prof;
 
-// Records the start of a stage (or, with name == nullptr, the end of the last one).
-void prof_mark(hipStream_t s, const char* name) {
+// Opens a stage; the next kernel launched on this thread records its events.
+void prof_mark(hipStream_t, const char* name) {
   Profiler& p = g_prof;
-  if (!p.on || p.n > kMaxStages) return;
-  if (name != nullptr && p.n == kMaxStages) return;
-  (void)hipEventRecord(p.ev[p.n], s);
-  if (name != nullptr) p.names[p.n] = name;
-  ++p.n;
+  if (p.on) p.pending = name;
 }
 
 void prof_begin() {
-  if (g_prof.on) g_prof.n = 0;
+  if (g_prof.on) {
+    g_prof.n = 0;
+    g_prof.pending = nullptr;
+  }
 }
+
+}  // namespace
+
+namespace engram {
+bool prof_take(hipEvent_t* start, hipEvent_t* stop) {
+  Profiler& p = g_prof;
+  if (!p.on || p.pending == nullptr || p.n >= kMaxStages) return false;
+  *start = p.start[p.n];
+  *stop = p.stop[p.n];
+  p.names[p.n] = p.pending;
+  p.pending = nullptr;
+  ++p.n;
+  return true;
+}
+}  // namespace engram
+
+namespace {
 
 // ---- workspace layouts ----
 // A bump allocator over the caller's workspace: every region starts on a
@@ -519,14 +537,16 @@ ENGRAM_API engram_status engram_cache_build(const int32_t* warm_tokens, int64_t 
 ENGRAM_API engram_status engram_profile_enable(int32_t on) {
   Profiler& p = g_prof;
   if (on && !p.created) {
-    for (int i = 0; i <= kMaxStages; ++i) {
-      hipError_t e = hipEventCreate(&p.ev[i]);
+    for (int i = 0; i < kMaxStages; ++i) {
+      hipError_t e = hipEventCreate(&p.start[i]);
+      if (e == hipSuccess) e = hipEventCreate(&p.stop[i]);
       if (e != hipSuccess) return hip_status(e, "hipEventCreate");
     }
     p.created = true;
   }
   p.on = on != 0;
   p.n = 0;
+  p.pending = nullptr;
   return ENGRAM_OK;
 }
 
@@ -535,13 +555,13 @@ ENGRAM_API engram_status engram_profile_read(float* ms, const char** names, int3
   if (n_stages == nullptr || (cap > 0 && ms == nullptr))
     return fail(ENGRAM_EINVAL, "profile_read: n_stages and ms must be non-NULL");
   *n_stages = 0;
-  if (!p.created || p.n < 2) return fail(ENGRAM_EINVAL, "profile_read: no profiled call recorded");
-  hipError_t e = hipEventSynchronize(p.ev[p.n - 1]);
+  if (!p.created || p.n < 1) return fail(ENGRAM_EINVAL, "profile_read: no profiled call recorded");
+  hipError_t e = hipEventSynchronize(p.stop[p.n - 1]);
   if (e != hipSuccess) return hip_status(e, "hipEventSynchronize");
-  const int stages = p.n - 1;
+  const int stages = p.n;
   for (int i = 0; i < stages && i < cap; ++i) {
     float t = 0.f;
-    e = hipEventElapsedTime(&t, p.ev[i], p.ev[i + 1]);
+    e = hipEventElapsedTime(&t, p.start[i], p.stop[i]);
     if (e != hipSuccess) return hip_status(e, "hipEventElapsedTime");
     ms[i] = t;
     if (names != nullptr) names[i] = p.names[i];

@@ -228,24 +228,24 @@ hipError_t launch_cache_build(const int32_t* tokens, int64_t B, int64_t T, const
   p += al(nb * 4);
   int64_t* params = reinterpret_cast<int64_t*>(p);
 
-  hipLaunchKernelGGL(fill_u32, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, counts, total_rows, 0u);
-  hipLaunchKernelGGL(fill_u32, dim3(grid_for(kBins, 256)), dim3(256), 0, s, bins, static_cast<int64_t>(kBins), 0u);
+  launch_k(fill_u32, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, counts, total_rows, 0u);
+  launch_k(fill_u32, dim3(grid_for(kBins, 256)), dim3(256), 0, s, bins, static_cast<int64_t>(kBins), 0u);
   const int64_t pairs = B * T * ha.n_tables;
   if (pairs > 0)
-    hipLaunchKernelGGL(count_kernel, dim3(static_cast<unsigned>((pairs + 255) / 256)), dim3(256), 0, s, tokens, B, T,
+    launch_k(count_kernel, dim3(static_cast<unsigned>((pairs + 255) / 256)), dim3(256), 0, s, tokens, B, T,
                        proj, ha, ta, counts);
-  hipLaunchKernelGGL(histogram_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, counts, total_rows, bins);
-  hipLaunchKernelGGL(threshold_kernel, dim3(1), dim3(1024), 0, s, bins, cache_n, params);
+  launch_k(histogram_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, counts, total_rows, bins);
+  launch_k(threshold_kernel, dim3(1), dim3(1024), 0, s, bins, cache_n, params);
   for (int mode = 0; mode < 2; ++mode) {
     int32_t* out = mode == 0 ? eq_rank : cache_slot;
-    hipLaunchKernelGGL(scan_local_kernel, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0, s, mode, counts,
+    launch_k(scan_local_kernel, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0, s, mode, counts,
                        eq_rank, params, total_rows, out, sums);
-    hipLaunchKernelGGL(scan_sums_kernel, dim3(1), dim3(1024), 0, s, sums, nb);
-    hipLaunchKernelGGL(scan_finish_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, mode, counts, eq_rank,
+    launch_k(scan_sums_kernel, dim3(1), dim3(1024), 0, s, sums, nb);
+    launch_k(scan_finish_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, mode, counts, eq_rank,
                        params, total_rows, out, sums);
   }
   const int64_t work = total_rows * (row_bytes / 8);
-  hipLaunchKernelGGL(copy_rows_kernel, dim3(static_cast<unsigned>((work + 255) / 256)), dim3(256), 0, s, cache_slot,
+  launch_k(copy_rows_kernel, dim3(static_cast<unsigned>((work + 255) / 256)), dim3(256), 0, s, cache_slot,
                      total_rows, static_cast<const uint8_t*>(ta.rows), ta.scale, row_bytes,
                      static_cast<uint8_t*>(cache_rows), cache_scale);
   return hipGetLastError();

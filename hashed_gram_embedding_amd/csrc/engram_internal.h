@@ -2,6 +2,7 @@
 // libengram.so.  Not installed; the public interface is include/engram.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -123,5 +124,21 @@ size_t cache_build_workspace(int64_t total_rows);
 hipError_t launch_cache_build(const int32_t* tokens, int64_t B, int64_t T, const int32_t* proj, const HashArgs& ha,
                               const TableArgs& ta, int64_t total_rows, int row_bytes, int64_t cache_n,
                               int32_t* cache_slot, void* cache_rows, float* cache_scale, void* ws, hipStream_t s);
+
+// Benchmark stage timing: after the library opens a named stage, the next
+// kernel launched through launch_k records start and stop events in its own
+// dispatch packet (hipExtLaunchKernel), so a stage's time is that kernel's
+// execution and not the gaps around it.  prof_take hands out the open stage's
+// events (false when no stage is open).
+bool prof_take(hipEvent_t* start, hipEvent_t* stop);
+
+template <typename F, typename... Args>
+inline void launch_k(F kernel, const dim3& grid, const dim3& block, uint32_t lds, hipStream_t s, Args... args) {
+  hipEvent_t e0, e1;
+  if (prof_take(&e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 }  // namespace engram

@@ -571,13 +571,13 @@ hipError_t launch_gate_stats(const void* H, const void* kv, int64_t n_tok, const
   if (pairs == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((pairs + 3) / 4));
   if (g.hdtype == ENGRAM_BF16 && g.kvdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((gate_stats_kernel<ENGRAM_BF16, ENGRAM_BF16>), grid, dim3(256), 0, s, H, kv, n_tok,
+    launch_k((gate_stats_kernel<ENGRAM_BF16, ENGRAM_BF16>), grid, dim3(256), 0, s, H, kv, n_tok,
                        g.branches, g.d, stats);
   else if (g.hdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((gate_stats_kernel<ENGRAM_BF16, ENGRAM_F32>), grid, dim3(256), 0, s, H, kv, n_tok,
+    launch_k((gate_stats_kernel<ENGRAM_BF16, ENGRAM_F32>), grid, dim3(256), 0, s, H, kv, n_tok,
                        g.branches, g.d, stats);
   else
-    hipLaunchKernelGGL((gate_stats_kernel<ENGRAM_F32, ENGRAM_F32>), grid, dim3(256), 0, s, H, kv, n_tok,
+    launch_k((gate_stats_kernel<ENGRAM_F32, ENGRAM_F32>), grid, dim3(256), 0, s, H, kv, n_tok,
                        g.branches, g.d, stats);
   return hipGetLastError();
 }
@@ -601,11 +601,11 @@ hipError_t launch_conv_cg(const ConvArgs& a, int vdtype, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (a.g.hdtype == ENGRAM_BF16 && vdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((conv_kernel<ENGRAM_BF16, ENGRAM_BF16, CG>), grid, dim3(256), lds, s, a);
+    launch_k((conv_kernel<ENGRAM_BF16, ENGRAM_BF16, CG>), grid, dim3(256), lds, s, a);
   else if (a.g.hdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((conv_kernel<ENGRAM_BF16, ENGRAM_F32, CG>), grid, dim3(256), lds, s, a);
+    launch_k((conv_kernel<ENGRAM_BF16, ENGRAM_F32, CG>), grid, dim3(256), lds, s, a);
   else
-    hipLaunchKernelGGL((conv_kernel<ENGRAM_F32, ENGRAM_F32, CG>), grid, dim3(256), lds, s, a);
+    launch_k((conv_kernel<ENGRAM_F32, ENGRAM_F32, CG>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
@@ -618,11 +618,11 @@ hipError_t launch_conv_strip(const ConvArgs& a, int vdtype, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(a.B),
                   static_cast<unsigned>((a.g.d + 256 * CPT - 1) / (256 * CPT)));
   if (a.g.hdtype == ENGRAM_BF16 && vdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((conv_strip_kernel<ENGRAM_BF16, ENGRAM_BF16, KW, DIL, TS, CPT>), grid, dim3(256), 0, s, a, spx);
+    launch_k((conv_strip_kernel<ENGRAM_BF16, ENGRAM_BF16, KW, DIL, TS, CPT>), grid, dim3(256), 0, s, a, spx);
   else if (a.g.hdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL((conv_strip_kernel<ENGRAM_BF16, ENGRAM_F32, KW, DIL, TS, CPT>), grid, dim3(256), 0, s, a, spx);
+    launch_k((conv_strip_kernel<ENGRAM_BF16, ENGRAM_F32, KW, DIL, TS, CPT>), grid, dim3(256), 0, s, a, spx);
   else
-    hipLaunchKernelGGL((conv_strip_kernel<ENGRAM_F32, ENGRAM_F32, KW, DIL, TS, CPT>), grid, dim3(256), 0, s, a, spx);
+    launch_k((conv_strip_kernel<ENGRAM_F32, ENGRAM_F32, KW, DIL, TS, CPT>), grid, dim3(256), 0, s, a, spx);
   return hipGetLastError();
 }
 
@@ -650,10 +650,10 @@ hipError_t launch_state_commit(const void* v, int64_t v_stride, int vdtype, int6
                                const int32_t* tokens, const int32_t* proj, int32_t max_n, hipStream_t s) {
   if (B == 0 || T == 0) return hipSuccess;
   if (vdtype == ENGRAM_BF16)
-    hipLaunchKernelGGL(state_commit_kernel<ENGRAM_BF16>, dim3(static_cast<unsigned>(B)), dim3(256), 0, s,
+    launch_k(state_commit_kernel<ENGRAM_BF16>, dim3(static_cast<unsigned>(B)), dim3(256), 0, s,
                        v, v_stride, T, g, gamma, st, tokens, proj, max_n);
   else
-    hipLaunchKernelGGL(state_commit_kernel<ENGRAM_F32>, dim3(static_cast<unsigned>(B)), dim3(256), 0, s,
+    launch_k(state_commit_kernel<ENGRAM_F32>, dim3(static_cast<unsigned>(B)), dim3(256), 0, s,
                        v, v_stride, T, g, gamma, st, tokens, proj, max_n);
   return hipGetLastError();
 }

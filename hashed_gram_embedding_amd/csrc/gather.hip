@@ -100,9 +100,9 @@ hipError_t launch_in(const int32_t* z, int64_t n_tok, const TableArgs& ta, int o
   const int threads = 256;
   const dim3 grid(static_cast<unsigned>((total + threads - 1) / threads));
   if (out == ENGRAM_BF16)
-    hipLaunchKernelGGL((gather_kernel<IN, ENGRAM_BF16, HASHED>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
+    launch_k((gather_kernel<IN, ENGRAM_BF16, HASHED>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
   else
-    hipLaunchKernelGGL((gather_kernel<IN, ENGRAM_F32, HASHED>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
+    launch_k((gather_kernel<IN, ENGRAM_F32, HASHED>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
   return hipGetLastError();
 }
 

@@ -175,16 +175,16 @@ hipError_t launch_project_kv(const void* e, const void* w, int64_t n_tok, int64_
     const auto* A = static_cast<const uint16_t*>(e);
     const auto* W = static_cast<const uint16_t*>(w);
     if (out_dtype == ENGRAM_BF16)
-      hipLaunchKernelGGL(gemm_bf16_kernel<uint16_t>, grid, dim3(kThreads), 0, s, A, W,
+      launch_k(gemm_bf16_kernel<uint16_t>, grid, dim3(kThreads), 0, s, A, W,
                          static_cast<uint16_t*>(kv), n_tok, static_cast<int>(n_out),
                          static_cast<int>(d_mem), tiles_m, tiles_n);
     else
-      hipLaunchKernelGGL(gemm_bf16_kernel<float>, grid, dim3(kThreads), 0, s, A, W,
+      launch_k(gemm_bf16_kernel<float>, grid, dim3(kThreads), 0, s, A, W,
                          static_cast<float*>(kv), n_tok, static_cast<int>(n_out),
                          static_cast<int>(d_mem), tiles_m, tiles_n);
   } else {
     const int64_t total = n_tok * n_out;
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,
+    launch_k(gemm_f32_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s,
                        static_cast<const float*>(e), static_cast<const float*>(w),
                        static_cast<float*>(kv), n_tok, static_cast<int>(n_out), static_cast<int>(d_mem));
   }

@@ -34,7 +34,7 @@ hipError_t launch_hash(const int32_t* tokens, int64_t B, int64_t T, const int32_
   if (total == 0) return hipSuccess;
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
-  hipLaunchKernelGGL(hash_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, s,
+  launch_k(hash_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, s,
                      tokens, B, T, hist, proj, a, z);
   return hipGetLastError();
 }

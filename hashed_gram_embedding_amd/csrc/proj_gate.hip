@@ -237,7 +237,7 @@ hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit);
   }
-  hipLaunchKernelGGL((proj_gate_kernel<TF, PD>), dim3(a.tiles_f * a.tiles_t), dim3(kThreads), lds, s, a);
+  launch_k((proj_gate_kernel<TF, PD>), dim3(a.tiles_f * a.tiles_t), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 

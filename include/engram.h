@@ -222,13 +222,14 @@ engram_status engram_cache_build(const int32_t* warm_tokens, int64_t B, int64_t 
                                  hipStream_t stream);
 
 /* Stage timing, for benchmarks.  engram_profile_enable(1) makes later
- * engram_forward calls on the calling thread record a HIP event on their
- * stream before each kernel launch and after the last one (events owned by
- * the library, reused by each call).  engram_profile_read waits for the last
- * event of the most recent profiled call, writes up to `cap` stage durations
- * in milliseconds to ms[] and their kernel names to names[] (static strings;
- * names may be NULL), and returns the stage count in *n_stages.
- * engram_profile_enable(0) stops recording. */
+ * engram_forward and engram_gate_conv_forward calls on the calling thread
+ * time each kernel they launch: the start and stop events are recorded by
+ * the kernel's own dispatch (hipExtLaunchKernel), so a stage is the kernel's
+ * execution interval (events owned by the library, reused by each call).
+ * engram_profile_read waits for the last event of the most recent profiled
+ * call, writes up to `cap` stage durations in milliseconds to ms[] and their
+ * kernel names to names[] (static strings; names may be NULL), and returns
+ * the stage count in *n_stages.  engram_profile_enable(0) stops recording. */
 engram_status engram_profile_enable(int32_t on);
 engram_status engram_profile_read(float* ms, const char** names, int32_t cap, int32_t* n_stages);
 
