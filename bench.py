@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--overlap", action="store_true",
+                    help="also measure retrieval (Steps 1-4) run ahead on a second stream: hidden behind a "
+                         "stand-in for the preceding layers, and pipelined across batches")
     ap.add_argument("--hbm-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                          "run with --copy-calibration-mib into the per-kernel HBM bytes table and exit")
@@ -210,6 +213,132 @@ def hbm_summary(fetch_csv, write_csv, workload, n_true):
 
 
 
+def overlap_report(torch, eg, w, lay, steps, warmup):
+    """Retrieval run ahead of the layer (the pages' prefetch from token ids).
+
+    1. Hidden behind the preceding layers: a stand-in for one dense transformer
+       block at the same batch (bf16 matmuls of d = 1024 with a 4x MLP:
+       x W_qkv, q W_o, x W_up, u W_down; torch / hipBLASLt) runs on the main
+       stream while engram_retrieve runs on a second stream; hidden = (t_block
+       + t_retrieve - t_both) / t_retrieve.
+    2. Pipelined batches: engram_retrieve of batch s+1 on the second stream
+       while engram_forward_retrieved of batch s runs on the main stream (two
+       alternating synthetic batches, each step the whole layer for its
+       batch), captured as a two-step HIP graph.
+    Every variant is captured in a HIP graph and replayed, so the streams'
+    fork and join are graph edges rather than host-side event waits."""
+    dev = "cuda"
+    B, T = w.B, w.T
+    n_tok = B * T
+    L = eg.Layer(lay, w.dtype, dev)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    g = torch.Generator(device=dev).manual_seed(7)
+    x = torch.randn(n_tok, 1024, device=dev, dtype=torch.bfloat16, generator=g)
+    wq = torch.randn(1024, 3072, device=dev, dtype=torch.bfloat16, generator=g) / 32
+    wo = torch.randn(1024, 1024, device=dev, dtype=torch.bfloat16, generator=g) / 32
+    wu = torch.randn(1024, 4096, device=dev, dtype=torch.bfloat16, generator=g) / 32
+    wd = torch.randn(4096, 1024, device=dev, dtype=torch.bfloat16, generator=g) / 64
+    flops = 2.0 * n_tok * 1024 * (3072 + 1024 + 4096 + 4096)
+
+    def block():
+        q = torch.matmul(x, wq)
+        torch.matmul(q[:, :1024].contiguous(), wo)
+        torch.matmul(torch.matmul(x, wu), wd)
+
+    tok = torch.from_numpy(w.tokens).to(dev)
+    rng = __import__("numpy").random.default_rng(11)
+    tok2 = torch.from_numpy(inputs_zipf_like(w.tokens, rng)).to(dev)
+    e = [eg.rows_buffer(B, T, L, dev) for _ in range(2)]
+    H = eg.to_device(w.H, w.dtype, dev)
+    ws = torch.empty(eg.forward_retrieved_workspace(B, T, L), dtype=torch.uint8, device=dev)
+
+    def graph_of(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        torch.cuda.synchronize()
+        return gr
+
+    def timed(gr, reps):
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(main)
+        for _ in range(reps):
+            gr.replay()
+        t1.record(main)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps * 1e3          # us
+
+    # every function launches on the stream current at call time (the capture
+    # stream inside a graph capture) plus the side stream forked from it
+    def retr():
+        eg.retrieve(tok, L, e[0])
+
+    def both():
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            eg.retrieve(tok, L, e[0], stream=side)
+        block()
+        cur.wait_stream(side)
+
+    reps = max(steps, 20)
+    t_block = timed(graph_of(block), reps)
+    t_retr = timed(graph_of(retr), reps)
+    t_both = timed(graph_of(both), reps)
+    hidden = (t_block + t_retr - t_both) / t_retr
+
+    # pipelined: a two-step cycle captured once
+    def cycle():
+        cur = torch.cuda.current_stream()
+        for tc, tn, ec, en in ((tok, tok2, 0, 1), (tok2, tok, 1, 0)):
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                eg.retrieve(tn, L, e[en], stream=side)
+            eg.forward_retrieved(tc, e[ec], H, L, ws=ws, stream=cur)
+            cur.wait_stream(side)
+
+    eg.retrieve(tok, L, e[0])
+    g_cycle = graph_of(cycle)
+    eg.retrieve(tok, L, e[0])
+    t_cycle = timed(g_cycle, max(steps // 2, 10))
+    step_us = t_cycle / 2
+
+    # the same two batches without overlap, for comparison
+    def seq():
+        for tc in (tok, tok2):
+            eg.retrieve(tc, L, e[0])
+            eg.forward_retrieved(tc, e[0], H, L, ws=ws)
+    t_seq = timed(graph_of(seq), max(steps // 2, 10)) / 2
+    return {
+        "standin_block": {"what": "one dense transformer block's matmuls, d=1024, 4x MLP, bf16 (torch)",
+                          "us": round(t_block, 2), "TFLOP/s": round(flops / (t_block * 1e-6) / 1e12, 1)},
+        "retrieve_us": round(t_retr, 2),
+        "block_plus_retrieve_concurrent_us": round(t_both, 2),
+        "retrieve_hidden_fraction": round(hidden, 3),
+        "sequential_two_batch_ms_per_step": round(t_seq / 1e3, 5),
+        "pipelined": {"ms_per_step": round(step_us / 1e3, 5), "tokens_per_s": round(n_tok / (step_us * 1e-6), 1),
+                      "how": "retrieve(batch s+1) on a second stream during forward_retrieved(batch s); "
+                             "two alternating batches; HIP graph of a two-step cycle"},
+    }
+
+
+def inputs_zipf_like(tokens, rng):
+    """A second token batch of the same shape and distribution: the first
+    batch's ids permuted within each sequence."""
+    import numpy as np
+    out = np.array(tokens, copy=True)
+    for b in range(out.shape[0]):
+        out[b] = out[b][rng.permutation(out.shape[1])]
+    return np.ascontiguousarray(out)
+
+
 def main():
     args = parse()
     if args.hbm_summary:
@@ -239,23 +368,28 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # the step is captured once into a HIP graph and replayed, so that host
-    # launch overhead does not pace a step of a few tens of microseconds
+    # Consecutive steps are captured into a HIP graph and replayed, so that
+    # host launch overhead does not pace a step of a few tens of microseconds;
+    # a graph holds several complete steps (as a model forward holds many
+    # layers), which pays the replay's own launch cost once per graph.
     graph = None
+    per_graph = 1
     if not args.eager:
+        per_graph = next(k for k in (10, 5, 2, 1) if args.steps % k == 0)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):           # captures on a side stream
-            step()
+            for _ in range(per_graph):
+                step()
         torch.cuda.synchronize()
         run = graph.replay
     else:
         run = step
-    for _ in range(args.warmup):
+    for _ in range(max(1, args.warmup // per_graph)):
         run()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(args.steps // per_graph):
         run()
     t1.record(stream)
     torch.cuda.synchronize()
@@ -314,7 +448,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "layers_per_step": len(calls), "branches": lay.branches,
                    "d": lay.d, "d_mem": lay.d_mem, "tables": lay.hash.n_tables,
                    "table_rows": int(lay.tables.n_rows.sum()), "table_dtype": lay.tables.dtype},
-        "timing": "HIP graph replay" if graph is not None else "eager launches",
+        "timing": f"HIP graph replay, {per_graph} steps per graph" if graph is not None else "eager launches",
         "gather_GBps": None if gather_gbps is None else round(gather_gbps, 1),
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
         "kernel_rate": {k: round(v, 2) for k, v in rates.items()},
@@ -324,6 +458,8 @@ def main():
     for k, v in extra.items():
         if not k.startswith("_"):
             out[k] = v
+    if args.overlap and args.config in (1, 2):
+        out["retrieval_overlap"] = overlap_report(torch, eg, w, lays[0], args.steps, args.warmup)
     print(json.dumps(out), flush=True)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20

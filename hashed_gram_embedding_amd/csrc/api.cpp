@@ -237,19 +237,17 @@ bool use_fused(const engram_layer* L) {
          (static_cast<int64_t>(L->tables.n_tables) * L->tables.dim) % 64 == 0;
 }
 
-struct ForwardWorkspace {
-  void* e;          // [n_tok][d_mem] (hdtype)
+// Workspace of Steps 5-8 (engram_forward_retrieved); engram_forward puts the
+// gathered rows e in front of it.
+struct ComputeWorkspace {
   float* kv;        // unfused: [n_tok][(1+M)d]; fused: v only, [n_tok][d]
-  float4* stats;    // fused: [n_tok][(1+M)d/128]; unfused: [n_tok][1+M]
+  float4* stats;    // fused: [n_tok][(1+M)d/128] (or fewer tiles); unfused: [n_tok][1+M]
   float* gamma;     // [n_tok][M]
 };
 
-ForwardWorkspace carve_forward(Carve& c, int64_t n_tok, const engram_layer* L) {
+ComputeWorkspace carve_compute(Carve& c, int64_t n_tok, const engram_layer* L) {
   const int M = L->gc.branches, d = L->gc.d;
-  const int64_t d_mem = static_cast<int64_t>(L->tables.n_tables) * L->tables.dim;
-  const size_t es = dtype_size(L->gc.hdtype);
-  ForwardWorkspace f;
-  f.e = c.take<char>(static_cast<size_t>(n_tok) * d_mem * es);
+  ComputeWorkspace f;
   if (use_fused(L)) {
     f.kv = c.take<float>(static_cast<size_t>(n_tok) * d);
     f.stats = c.take<float4>(static_cast<size_t>(n_tok) * (1 + M) * d / engram::kProjGateTileF);
@@ -261,15 +259,26 @@ ForwardWorkspace carve_forward(Carve& c, int64_t n_tok, const engram_layer* L) {
   return f;
 }
 
+size_t rows_bytes(int64_t n_tok, const engram_layer* L) {
+  return static_cast<size_t>(n_tok) * L->tables.n_tables * L->tables.dim * dtype_size(L->gc.hdtype);
+}
+
 size_t gc_ws_bytes(int64_t n_tok, int M) {
   Carve c{nullptr};
   carve_gc(c, n_tok, M);
   return c.used;
 }
 
+size_t compute_ws_bytes(int64_t n_tok, const engram_layer* L) {
+  Carve c{nullptr};
+  carve_compute(c, n_tok, L);
+  return c.used;
+}
+
 size_t forward_ws_bytes(int64_t n_tok, const engram_layer* L) {
   Carve c{nullptr};
-  carve_forward(c, n_tok, L);
+  c.take<char>(rows_bytes(n_tok, L));
+  carve_compute(c, n_tok, L);
   return c.used;
 }
 
@@ -419,49 +428,44 @@ ENGRAM_API engram_status engram_gate_conv_forward(void* H, const void* kv, int64
                          w.gamma, y_out, stream);
 }
 
-ENGRAM_API size_t engram_forward_workspace(int64_t B, int64_t T, const engram_layer* L) {
-  if (L == nullptr || B < 0 || T < 0 || L->gc.branches < 1 || L->tables.n_tables < 1) return 0;
-  return forward_ws_bytes(B * T, L);
+namespace {
+
+// Argument checks shared by the layer entry points (everything host-visible).
+engram_status check_call(const char* who, const engram_layer* L, const engram_decode_state* st, bool state_ids,
+                         int64_t B, int64_t T, engram::HashArgs* ha, engram::TableArgs* ta,
+                         engram::GateConvArgs* g) {
+  engram_status r = check_layer(L, ha, ta, g);
+  if (r != ENGRAM_OK) return r;
+  if ((r = check_state(st, state_ids)) != ENGRAM_OK) return r;
+  if (B < 0 || T < 0) return fail(ENGRAM_EINVAL, "%s: B and T must be >= 0", who);
+  if (T > INT32_MAX) return fail(ENGRAM_EUNSUPPORTED, "%s: T above 2^31-1 tokens per sequence", who);
+  if (B > 65535) return fail(ENGRAM_EUNSUPPORTED, "%s: B above 65535 sequences per call", who);
+  return ENGRAM_OK;
 }
 
-ENGRAM_API engram_status engram_forward(const int32_t* tokens, void* H, int64_t B, int64_t T,
-                                        const engram_layer* L, engram_decode_state* st,
-                                        float* alpha_out, float* y_out, void* ws, size_t ws_bytes,
-                                        hipStream_t stream) {
-  engram::HashArgs ha;
-  engram::TableArgs ta;
-  engram::GateConvArgs g;
-  engram_status r = check_layer(L, &ha, &ta, &g);
-  if (r != ENGRAM_OK) return r;
-  if ((r = check_state(st, true)) != ENGRAM_OK) return r;
-  if (B < 0 || T < 0) return fail(ENGRAM_EINVAL, "forward: B and T must be >= 0");
-  if (T > INT32_MAX) return fail(ENGRAM_EUNSUPPORTED, "forward: T above 2^31-1 tokens per sequence");
-  if (B > 65535) return fail(ENGRAM_EUNSUPPORTED, "forward: B above 65535 sequences per call");
-  const int64_t n_tok = B * T;
-  if (n_tok == 0) return ENGRAM_OK;
-  if (tokens == nullptr || H == nullptr) return fail(ENGRAM_EINVAL, "forward: tokens and H must be non-NULL");
-  if (!aligned(H, 16)) return fail(ENGRAM_EINVAL, "forward: H must be 16-byte aligned");
-  if (y_out != nullptr && !aligned(y_out, 16)) return fail(ENGRAM_EINVAL, "forward: y_out must be 16-byte aligned");
-  const size_t need = forward_ws_bytes(n_tok, L);
-  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
-    return fail(ENGRAM_EINVAL, "forward: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+// Steps 1-4: indices hashed inside the gather.
+engram_status run_retrieve(const int32_t* tokens, int64_t B, int64_t T, const engram_layer* L,
+                           const engram::HashArgs& ha, const engram::TableArgs& ta, int hdtype,
+                           const engram_decode_state* st, void* e, hipStream_t stream) {
+  const int32_t* hist = st != nullptr ? st->ids : nullptr;
+  prof_mark(stream, "gather_kernel<hashed>");
+  return hip_status(engram::launch_hash_gather(tokens, B, T, hist, L->hash.proj, ha, ta, hdtype, e, stream),
+                    "hash+gather launch");
+}
 
-  Carve c{static_cast<char*>(ws)};
-  ForwardWorkspace f = carve_forward(c, n_tok, L);
+// Steps 5-8 on gathered rows e.
+engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t B, int64_t T,
+                          const engram_layer* L, engram::GateConvArgs g, engram_decode_state* st,
+                          float* alpha_out, float* y_out, const ComputeWorkspace& f, hipStream_t stream) {
+  const int64_t n_tok = B * T;
   const int64_t d_mem = static_cast<int64_t>(L->tables.n_tables) * L->tables.dim;
   const int M = g.branches, d = g.d;
   const int64_t n_out = static_cast<int64_t>(1 + M) * d;
-  const int32_t* hist = st != nullptr ? st->ids : nullptr;
-  prof_begin();
-  // Steps 1-4: indices hashed inside the gather
-  prof_mark(stream, "gather_kernel<hashed>");
-  r = hip_status(engram::launch_hash_gather(tokens, B, T, hist, L->hash.proj, ha, ta, g.hdtype, f.e, stream),
-                 "hash+gather launch");
-  if (r != ENGRAM_OK) return r;
+  engram_status r;
   if (use_fused(L)) {
     // Step 5 with the gate's sums folded into the product's epilogue; only v is stored
     engram::ProjGateArgs pa{};
-    pa.e = static_cast<const uint16_t*>(f.e);
+    pa.e = static_cast<const uint16_t*>(e);
     pa.w = static_cast<const uint16_t*>(L->w);
     pa.H = static_cast<const uint16_t*>(H);
     pa.v = f.kv;
@@ -480,7 +484,7 @@ ENGRAM_API engram_status engram_forward(const int32_t* tokens, void* H, int64_t 
   }
   // Step 5 into float32 projections, then whole-row gate statistics
   prof_mark(stream, "gemm_kernel");
-  r = hip_status(engram::launch_project_kv(f.e, L->w, n_tok, d_mem, n_out, g.hdtype, ENGRAM_F32, f.kv, stream),
+  r = hip_status(engram::launch_project_kv(e, L->w, n_tok, d_mem, n_out, g.hdtype, ENGRAM_F32, f.kv, stream),
                  "project_kv launch");
   if (r != ENGRAM_OK) return r;
   g.kvdtype = ENGRAM_F32;
@@ -489,6 +493,86 @@ ENGRAM_API engram_status engram_forward(const int32_t* tokens, void* H, int64_t 
   if (r != ENGRAM_OK) return r;
   return run_conv_commit(H, f.kv, n_out, ENGRAM_F32, f.stats, 1, 1, B, T, g, st, tokens, L->hash.proj,
                          L->hash.max_n, alpha_out, f.gamma, y_out, stream);
+}
+
+}  // namespace
+
+ENGRAM_API size_t engram_forward_workspace(int64_t B, int64_t T, const engram_layer* L) {
+  if (L == nullptr || B < 0 || T < 0 || L->gc.branches < 1 || L->tables.n_tables < 1) return 0;
+  return forward_ws_bytes(B * T, L);
+}
+
+ENGRAM_API engram_status engram_forward(const int32_t* tokens, void* H, int64_t B, int64_t T,
+                                        const engram_layer* L, engram_decode_state* st,
+                                        float* alpha_out, float* y_out, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  engram::HashArgs ha;
+  engram::TableArgs ta;
+  engram::GateConvArgs g;
+  engram_status r = check_call("forward", L, st, true, B, T, &ha, &ta, &g);
+  if (r != ENGRAM_OK) return r;
+  const int64_t n_tok = B * T;
+  if (n_tok == 0) return ENGRAM_OK;
+  if (tokens == nullptr || H == nullptr) return fail(ENGRAM_EINVAL, "forward: tokens and H must be non-NULL");
+  if (!aligned(H, 16)) return fail(ENGRAM_EINVAL, "forward: H must be 16-byte aligned");
+  if (y_out != nullptr && !aligned(y_out, 16)) return fail(ENGRAM_EINVAL, "forward: y_out must be 16-byte aligned");
+  const size_t need = forward_ws_bytes(n_tok, L);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(ENGRAM_EINVAL, "forward: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  Carve c{static_cast<char*>(ws)};
+  void* e = c.take<char>(rows_bytes(n_tok, L));
+  const ComputeWorkspace f = carve_compute(c, n_tok, L);
+  prof_begin();
+  r = run_retrieve(tokens, B, T, L, ha, ta, g.hdtype, st, e, stream);
+  if (r != ENGRAM_OK) return r;
+  return run_compute(tokens, e, H, B, T, L, g, st, alpha_out, y_out, f, stream);
+}
+
+ENGRAM_API engram_status engram_retrieve(const int32_t* tokens, int64_t B, int64_t T, const engram_layer* L,
+                                         const engram_decode_state* st, void* e, hipStream_t stream) {
+  engram::HashArgs ha;
+  engram::TableArgs ta;
+  engram::GateConvArgs g;
+  engram_status r = check_call("retrieve", L, st, true, B, T, &ha, &ta, &g);
+  if (r != ENGRAM_OK) return r;
+  if (B * T == 0) return ENGRAM_OK;
+  if (tokens == nullptr || e == nullptr) return fail(ENGRAM_EINVAL, "retrieve: tokens and e must be non-NULL");
+  if (!aligned(e, 16)) return fail(ENGRAM_EINVAL, "retrieve: e must be 16-byte aligned");
+  prof_begin();
+  return run_retrieve(tokens, B, T, L, ha, ta, g.hdtype, st, e, stream);
+}
+
+ENGRAM_API size_t engram_forward_retrieved_workspace(int64_t B, int64_t T, const engram_layer* L) {
+  if (L == nullptr || B < 0 || T < 0 || L->gc.branches < 1 || L->tables.n_tables < 1) return 0;
+  return compute_ws_bytes(B * T, L);
+}
+
+ENGRAM_API engram_status engram_forward_retrieved(const int32_t* tokens, const void* e, void* H, int64_t B,
+                                                  int64_t T, const engram_layer* L, engram_decode_state* st,
+                                                  float* alpha_out, float* y_out, void* ws, size_t ws_bytes,
+                                                  hipStream_t stream) {
+  engram::HashArgs ha;
+  engram::TableArgs ta;
+  engram::GateConvArgs g;
+  engram_status r = check_call("forward_retrieved", L, st, true, B, T, &ha, &ta, &g);
+  if (r != ENGRAM_OK) return r;
+  const int64_t n_tok = B * T;
+  if (n_tok == 0) return ENGRAM_OK;
+  if (e == nullptr || H == nullptr) return fail(ENGRAM_EINVAL, "forward_retrieved: e and H must be non-NULL");
+  if (st != nullptr && tokens == nullptr)
+    return fail(ENGRAM_EINVAL, "forward_retrieved: tokens must be non-NULL with a decode state");
+  if (!aligned(H, 16) || !aligned(e, 16))
+    return fail(ENGRAM_EINVAL, "forward_retrieved: H and e must be 16-byte aligned");
+  if (y_out != nullptr && !aligned(y_out, 16))
+    return fail(ENGRAM_EINVAL, "forward_retrieved: y_out must be 16-byte aligned");
+  const size_t need = compute_ws_bytes(n_tok, L);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(ENGRAM_EINVAL, "forward_retrieved: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                ws_bytes);
+  Carve c{static_cast<char*>(ws)};
+  const ComputeWorkspace f = carve_compute(c, n_tok, L);
+  prof_begin();
+  return run_compute(tokens, e, H, B, T, L, g, st, alpha_out, y_out, f, stream);
 }
 
 ENGRAM_API size_t engram_cache_build_workspace(int64_t total_rows) {

@@ -85,6 +85,11 @@ def lib():
         "engram_forward_workspace": (sz, [i64, i64, ctypes.POINTER(LayerStruct)]),
         "engram_forward": (i32, [vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
                                  ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
+        "engram_retrieve": (i32, [vp, i64, i64, ctypes.POINTER(LayerStruct), ctypes.POINTER(DecodeStateStruct), vp,
+                                  vp]),
+        "engram_forward_retrieved_workspace": (sz, [i64, i64, ctypes.POINTER(LayerStruct)]),
+        "engram_forward_retrieved": (i32, [vp, vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
+                                           ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
         "engram_cache_build_workspace": (sz, [i64]),
         "engram_cache_build": (i32, [vp, i64, i64, ctypes.POINTER(HashParams), ctypes.POINTER(Tables), i64, vp, vp, vp,
                                      vp, sz, vp]),
@@ -105,7 +110,8 @@ def lib():
 def exported_names():
     return ["engram_abi_version", "engram_last_error", "engram_hash_indices", "engram_gather",
             "engram_project_kv", "engram_gate_conv_workspace", "engram_gate_conv_forward",
-            "engram_forward_workspace", "engram_forward", "engram_cache_build_workspace", "engram_cache_build",
+            "engram_forward_workspace", "engram_forward", "engram_retrieve", "engram_forward_retrieved_workspace",
+            "engram_forward_retrieved", "engram_cache_build_workspace", "engram_cache_build",
             "engram_profile_enable", "engram_profile_read",
             "engram_host_alloc", "engram_host_free"]
 
@@ -210,6 +216,10 @@ class Layer:
     @property
     def d(self):
         return self.li.d
+
+    @property
+    def d_mem(self):
+        return self.li.tables.dim * self.li.tables.n_rows.shape[0]
 
 
 class DecodeState:
@@ -347,4 +357,38 @@ def forward(tokens: torch.Tensor, H: torch.Tensor, layer: Layer, state: Optional
     st = ctypes.byref(state.s) if state is not None else None
     _check(lib().engram_forward(_ptr(tokens), _ptr(H), B, T, ctypes.byref(layer.s), st, _ptr(alpha), _ptr(y),
                                 _ptr(ws), ws.numel(), _stream(stream)))
+    return alpha, y
+
+
+def rows_buffer(B: int, T: int, layer: Layer, device=None) -> torch.Tensor:
+    """A buffer for the gathered rows e of B x T tokens (engram_retrieve)."""
+    dt = torch.bfloat16 if layer.hdtype == BF16 else torch.float32
+    return torch.empty((B * T, layer.d_mem), dtype=dt, device=device)
+
+
+def retrieve(tokens: torch.Tensor, layer: Layer, e: torch.Tensor, state: Optional[DecodeState] = None,
+             stream=None):
+    """Steps 1-4 into e, from the token ids (and the state's id history) only."""
+    B, T = tokens.shape
+    st = ctypes.byref(state.s) if state is not None else None
+    _check(lib().engram_retrieve(_ptr(tokens), B, T, ctypes.byref(layer.s), st, _ptr(e), _stream(stream)))
+
+
+def forward_retrieved_workspace(B: int, T: int, layer: Layer) -> int:
+    return int(lib().engram_forward_retrieved_workspace(B, T, ctypes.byref(layer.s)))
+
+
+def forward_retrieved(tokens: torch.Tensor, e: torch.Tensor, H: torch.Tensor, layer: Layer,
+                      state: Optional[DecodeState] = None, want_alpha: bool = False, want_y: bool = False,
+                      ws: Optional[torch.Tensor] = None, stream=None):
+    """Steps 5-8 on the rows from retrieve(); H is updated in place.  Returns (alpha, y)."""
+    B, T = tokens.shape
+    M, d = layer.M, layer.d
+    alpha = torch.empty((B, T, M), dtype=torch.float32, device=H.device) if want_alpha else None
+    y = torch.empty((B, T, M, d), dtype=torch.float32, device=H.device) if want_y else None
+    if ws is None:
+        ws = torch.empty(max(forward_retrieved_workspace(B, T, layer), 256), dtype=torch.uint8, device=H.device)
+    st = ctypes.byref(state.s) if state is not None else None
+    _check(lib().engram_forward_retrieved(_ptr(tokens), _ptr(e), _ptr(H), B, T, ctypes.byref(layer.s), st,
+                                          _ptr(alpha), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
     return alpha, y

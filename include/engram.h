@@ -200,6 +200,31 @@ engram_status engram_forward(const int32_t* tokens, void* H, int64_t B, int64_t 
                              float* alpha_out, float* y_out, void* ws, size_t ws_bytes,
                              hipStream_t stream);
 
+/* The layer in two halves, so that retrieval can run ahead of the hidden
+ * states.  Steps 1-4 depend on the token ids alone (and, in decode, on the
+ * state's id history), which is why the RecSDK article runs this sparse
+ * retrieval asynchronously as an embedding prefetch that hides the lookup
+ * (cache prefetch section) and the DRAM offload study fetches the rows while
+ * the preceding layers compute (DRAM offload section).
+ *
+ * engram_retrieve: Steps 1-4 into e, device [B*T][n_tables*dim] of the
+ * layer's hdtype, 16-byte aligned, owned by the caller.  st: NULL, or the
+ * decode state whose ids are the history (read only; with a state, call it
+ * after the previous forward on those sequences has committed).
+ *
+ * engram_forward_retrieved: Steps 5-8 on e from engram_retrieve with the same
+ * tokens, B, T and state; arguments otherwise as engram_forward (tokens may be
+ * NULL when st is NULL).  ws: at least engram_forward_retrieved_workspace()
+ * bytes, 256-byte aligned.  engram_forward equals engram_retrieve followed by
+ * engram_forward_retrieved on one stream. */
+engram_status engram_retrieve(const int32_t* tokens, int64_t B, int64_t T, const engram_layer* L,
+                              const engram_decode_state* st, void* e, hipStream_t stream);
+size_t engram_forward_retrieved_workspace(int64_t B, int64_t T, const engram_layer* L);
+engram_status engram_forward_retrieved(const int32_t* tokens, const void* e, void* H, int64_t B,
+                                       int64_t T, const engram_layer* L, engram_decode_state* st,
+                                       float* alpha_out, float* y_out, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
 /* Static LFU admission for the HBM hot-row cache (Ascend RecSDK Engram
  * article, multi-level cache: hot rows by access frequency in fast memory,
  * the full table in host DRAM).  Counts how often each row of `tab` is

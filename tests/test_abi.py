@@ -212,3 +212,28 @@ def test_size_limits_are_rejected_before_launch():
     need = L.engram_forward_workspace(1, 64, ctypes.byref(lay))
     st, msg = _status(L.engram_forward, p, p, 65536, 1, ctypes.byref(lay), None, None, None, p, need, None)
     assert st == eg.EUNSUPPORTED and "B above" in msg
+
+
+def test_retrieve_and_forward_retrieved_reject_bad_arguments():
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    hp, keep_h = _hash_params()
+    t, keep_t = _tables()
+    lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=64, hdtype=eg.F32))
+    assert L.engram_retrieve(p, 0, 5, ctypes.byref(lay), None, None, None) == eg.OK      # empty: no-op
+    st, msg = _status(L.engram_retrieve, p, 1, 5, ctypes.byref(lay), None, None, None)
+    assert st == eg.EINVAL and "e must" in msg
+    assert L.engram_retrieve(p, 1, 5, ctypes.byref(lay), None, ctypes.c_void_p(0x10008), None) == eg.EINVAL
+    assert L.engram_retrieve(p, 1, 5, None, None, p, None) == eg.EINVAL
+    need = L.engram_forward_retrieved_workspace(1, 64, ctypes.byref(lay))
+    assert 0 < need < L.engram_forward_workspace(1, 64, ctypes.byref(lay))
+    st, msg = _status(L.engram_forward_retrieved, p, p, p, 1, 64, ctypes.byref(lay), None, None, None, p, need - 256,
+                      None)
+    assert st == eg.EINVAL and "workspace" in msg
+    st, msg = _status(L.engram_forward_retrieved, p, None, p, 1, 64, ctypes.byref(lay), None, None, None, p, need,
+                      None)
+    assert st == eg.EINVAL and "e and H" in msg
+    sd = eg.DecodeStateStruct(0x20000, 0x30000, 0x40000)
+    st, msg = _status(L.engram_forward_retrieved, None, p, p, 1, 64, ctypes.byref(lay), ctypes.byref(sd), None, None,
+                      p, need, None)
+    assert st == eg.EINVAL and "tokens" in msg
