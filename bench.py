@@ -95,7 +95,7 @@ def setup(args, torch, eg, inputs):
         tok = torch.from_numpy(w.tokens).to(dev)
         H = eg.to_device(w.H, w.dtype, dev)
         ws = torch.empty(eg.forward_workspace(w.B, w.T, L), dtype=torch.uint8, device=dev)
-        return [lambda: eg.forward(tok, H, L, ws=ws)], w.B * w.T, w, [lay], {}
+        return [lambda: eg.forward(tok, H, L, ws=ws)], w.B * w.T, w, [lay], {"_pipe": ([L], tok, H)}
     if cfg == 3:
         w = inputs.make_config(3)
         S = w.B
@@ -130,7 +130,7 @@ def setup(args, torch, eg, inputs):
         Ls.append(L)
     ws = torch.empty(max(eg.forward_workspace(w.B, w.T, L) for L in Ls), dtype=torch.uint8, device=dev)
     calls = [(lambda L=L: eg.forward(tok, H, L, ws=ws)) for L in Ls]
-    return calls, w.B * w.T, w, w.layers, {"cache_hit_rate": hits, "_keep": (Ls, bufs)}
+    return calls, w.B * w.T, w, w.layers, {"cache_hit_rate": hits, "_keep": (Ls, bufs), "_pipe": (Ls, tok, H)}
 
 # ---- HBM traffic from rocprofv3 counters ----
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
@@ -329,6 +329,90 @@ def overlap_report(torch, eg, w, lay, steps, warmup):
     }
 
 
+def pipelined_report(torch, eg, w, pipe, steps):
+    """Steps of all layers with the retrieval of step s+1 (every layer's
+    Steps 1-4, token ids only) on a second stream while step s computes
+    (Steps 5-8 of every layer) on the main stream; two alternating token
+    batches, a two-step cycle captured as a HIP graph.  Compared with the
+    same two batches run in order in one graph."""
+    import numpy as np
+    Ls, tok, H = pipe
+    B, T = tok.shape
+    dev = "cuda"
+    side = torch.cuda.Stream()
+    tok2 = torch.from_numpy(inputs_zipf_like(tok.cpu().numpy(), np.random.default_rng(11))).to(dev)
+    toks = (tok, tok2)
+    e = [[eg.rows_buffer(B, T, L, dev) for L in Ls] for _ in range(2)]
+    ws = torch.empty(max(eg.forward_retrieved_workspace(B, T, L) for L in Ls), dtype=torch.uint8, device=dev)
+
+    def retrieve_all(par, stream=None):
+        for li, L in enumerate(Ls):
+            eg.retrieve(toks[par], L, e[par][li], stream=stream)
+
+    def compute_all(par, stream=None):
+        for li, L in enumerate(Ls):
+            eg.forward_retrieved(toks[par], e[par][li], H, L, ws=ws, stream=stream)
+
+    def cycle():
+        cur = torch.cuda.current_stream()
+        for par in (0, 1):
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                retrieve_all(1 - par, stream=side)
+            compute_all(par, stream=cur)
+            cur.wait_stream(side)
+
+    def seq():
+        for par in (0, 1):
+            retrieve_all(par)
+            compute_all(par)
+
+    def timed_graph(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        torch.cuda.synchronize()
+        retrieve_all(0)
+        for _ in range(2):
+            gr.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            gr.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps / 2 * 1e3       # us per step
+
+    def timed_eager(fn, reps):
+        retrieve_all(0)
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps / 2 * 1e3
+
+    retrieve_all(0)
+    reps = max(steps // 2, 5)
+    t_pipe = timed_graph(cycle, reps)
+    t_seq = timed_graph(seq, reps)
+    t_pipe_eager = timed_eager(cycle, reps)
+    t_seq_eager = timed_eager(seq, reps)
+    return {"layers_per_step": len(Ls), "sequential_us_per_step": round(t_seq, 2),
+            "pipelined_us_per_step": round(t_pipe, 2),
+            "pipelined_tokens_per_s": round(B * T / (t_pipe * 1e-6), 1),
+            "eager_sequential_us_per_step": round(t_seq_eager, 2), "eager_pipelined_us_per_step": round(t_pipe_eager, 2),
+            "how": "retrieval of step s+1 (all layers) on a second stream during the compute of step s; "
+                   "two alternating token batches; HIP graphs of two-step cycles"}
+
+
 def inputs_zipf_like(tokens, rng):
     """A second token batch of the same shape and distribution: the first
     batch's ids permuted within each sequence."""
@@ -337,6 +421,39 @@ def inputs_zipf_like(tokens, rng):
     for b in range(out.shape[0]):
         out[b] = out[b][rng.permutation(out.shape[1])]
     return np.ascontiguousarray(out)
+
+
+def measured_peaks(torch):
+    """The box's practical peaks, re-measured in the same run: a 1 GiB
+    device-to-device copy (bytes read + written per second) and a large bf16
+    matmul through torch (hipBLASLt), 8192 x 8192 x 8192."""
+    main = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(main)
+        for _ in range(reps):
+            fn()
+        t1.record(main)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps * 1e-3          # s
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
+    t_mm = timed(lambda: torch.matmul(a, b), 10)
+    del a, b
+    return {"hbm_copy_GBps": round(2 * n / t_copy / 1e9, 1),
+            "bf16_gemm_TFLOPs": round(2.0 * m ** 3 / t_mm / 1e12, 1),
+            "how": "1 GiB device-to-device copy (read + write bytes); 8192^3 bf16 torch.matmul (hipBLASLt)"}
 
 
 def main():
@@ -426,6 +543,9 @@ def main():
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(rates[dominant] / PEAK_HBM_GBPS, 4),
                 "traffic": traffic_for(w.name, dominant), "units_per_launch": amount}
     gather_gbps = rates.get("gather_kernel<hashed>")
+    peaks = measured_peaks(torch)
+    roof["frac_of_measured_peak"] = round(
+        roof["achieved"] / (peaks["bf16_gemm_TFLOPs"] if kind == "mfma" else peaks["hbm_copy_GBps"]), 4)
 
     cpu = None
     if not args.no_cpu_baseline and args.config in (1, 2):
@@ -453,6 +573,7 @@ def main():
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
         "kernel_rate": {k: round(v, 2) for k, v in rates.items()},
         "roofline": roof,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     for k, v in extra.items():
@@ -460,6 +581,8 @@ def main():
             out[k] = v
     if args.overlap and args.config in (1, 2):
         out["retrieval_overlap"] = overlap_report(torch, eg, w, lays[0], args.steps, args.warmup)
+    if args.overlap and "_pipe" in extra:
+        out["retrieval_pipelined"] = pipelined_report(torch, eg, w, extra["_pipe"], args.steps)
     print(json.dumps(out), flush=True)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20

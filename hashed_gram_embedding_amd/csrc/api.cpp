@@ -233,7 +233,7 @@ GcWorkspace carve_gc(Carve& c, int64_t n_tok, int M) {
 
 // Fused bf16 path: gathered rows, float32 v, per-tile gate statistics.
 bool use_fused(const engram_layer* L) {
-  return L->gc.hdtype == ENGRAM_BF16 && L->gc.d % engram::kProjGateTileF == 0 && L->gc.d <= 4096 &&
+  return L->gc.hdtype == ENGRAM_BF16 && L->gc.d % 128 == 0 && L->gc.d <= 4096 &&
          (static_cast<int64_t>(L->tables.n_tables) * L->tables.dim) % 64 == 0;
 }
 

@@ -87,7 +87,7 @@ struct ProjGateArgs {
   int tiles_f;  // set by the launcher
   int tiles_t;  // set by the launcher
 };
-constexpr int kProjGateTileF = 128;  // narrowest feature tile (bounds the statistics buffer)
+constexpr int kProjGateTileF = 64;   // narrowest feature tile (bounds the statistics buffer)
 int proj_gate_tile_f(int64_t n_tok, int N, int d);   // feature columns per gate-statistics tile
 hipError_t launch_proj_gate(const ProjGateArgs& a, hipStream_t s);
 

@@ -219,6 +219,135 @@ proj_gate_kernel(ProjGateArgs a) {
   }
 }
 
+// Small batches (decode): a 64-feature x 32-token tile per workgroup, so that
+// a few hundred tokens still give hundreds of workgroups.  The four
+// wavefronts split K four ways; each loads its MFMA operands straight from
+// memory (L2) into fragment registers -- a 16-byte run of K per lane for
+// both operands -- in batches of four K16 steps, the next batch in flight
+// while the current one is multiplied, so the whole K range costs a couple
+// of memory round trips instead of one per slice.  The partial tiles are
+// summed through LDS and the epilogue (v store, gate sums per 64 columns)
+// follows the large kernel's.
+constexpr int kSmallTF = 64;
+constexpr int kSmallTK = 32;
+constexpr int kSmallWaves = 4;
+constexpr int kSmallBatch = 4;   // K16 steps per load batch
+
+__global__ void __launch_bounds__(64 * kSmallWaves)
+proj_gate_small_kernel(ProjGateArgs a) {
+  __shared__ float part[kSmallWaves][kSmallTF][kSmallTK + 1];   // +1: no bank conflicts on the sums
+  __shared__ float4 red[kSmallWaves][kSmallTK];
+  const int tf = blockIdx.x % a.tiles_f;
+  const int tt = blockIdx.x / a.tiles_f;
+  const int f0 = tf * kSmallTF;
+  const int64_t t0 = static_cast<int64_t>(tt) * kSmallTK;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int K = a.K;
+  const int kq = K / kSmallWaves;             // this wavefront's K range: [wave*kq, (wave+1)*kq)
+  const int nsteps = kq / 16;                 // K16 steps (K is a multiple of 64: at least one)
+  const int half = lane >> 5;                 // lanes 32-63 hold K elements 8..15 of each step
+  const int64_t tok = min(t0 + (lane & 31), a.n_tok - 1);
+  const uint16_t* wrow0 = a.w + static_cast<int64_t>(f0 + (lane & 31)) * K + wave * kq + half * 8;
+  const uint16_t* wrow1 = wrow0 + static_cast<int64_t>(32) * K;
+  const uint16_t* erow = a.e + tok * K + wave * kq + half * 8;
+
+  f32x16_t acc0, acc1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+
+  u32x4_t fa0[2][kSmallBatch], fa1[2][kSmallBatch], fb[2][kSmallBatch];
+#define ENGRAM_SMALL_LOAD(buf, s0)                                                                 \
+  _Pragma("unroll") for (int j = 0; j < kSmallBatch; ++j) {                                        \
+    const int kk = min((s0) + j, nsteps - 1) * 16;                                                 \
+    fa0[buf][j] = *reinterpret_cast<const u32x4_t*>(wrow0 + kk);                                   \
+    fa1[buf][j] = *reinterpret_cast<const u32x4_t*>(wrow1 + kk);                                   \
+    fb[buf][j] = *reinterpret_cast<const u32x4_t*>(erow + kk);                                     \
+  }
+  ENGRAM_SMALL_LOAD(0, 0);
+  for (int s0 = 0; s0 < nsteps; s0 += 2 * kSmallBatch) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int sb = s0 + u * kSmallBatch;     // first step of the batch in buffer u
+      ENGRAM_SMALL_LOAD(u ^ 1, sb + kSmallBatch);  // next batch (clamped past the end, never used)
+#pragma unroll
+      for (int j = 0; j < kSmallBatch; ++j) {
+        if (sb + j < nsteps) {
+          const bf16x8_t b = __builtin_bit_cast(bf16x8_t, fb[u][j]);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa0[u][j]), b, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa1[u][j]), b, acc1, 0, 0, 0);
+        }
+      }
+    }
+  }
+#undef ENGRAM_SMALL_LOAD
+
+  // acc_i[4g + r]: feature i*32 + g*8 + half*4 + r of the tile, token lane & 31
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      part[wave][g * 8 + half * 4 + r][lane & 31] = acc0[4 * g + r];
+      part[wave][32 + g * 8 + half * 4 + r][lane & 31] = acc1[4 * g + r];
+    }
+  __syncthreads();
+
+  // thread (token tl, feature quarter fq): 16 features of one token, summed over the waves
+  const int tl = threadIdx.x & (kSmallTK - 1);
+  const int fq = threadIdx.x / kSmallTK;      // 0..7, 8 features each
+  const int64_t gt = t0 + tl;
+  const bool valid = gt < a.n_tok;
+  const int64_t ct = valid ? gt : a.n_tok - 1;
+  const int d = a.d;
+  const bool is_v = f0 < d;
+  const int m = is_v ? 0 : f0 / d - 1;
+  const int c0 = (is_v ? f0 : f0 - (1 + m) * d) + fq * 8;
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float sacc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) sacc += part[w][fq * 8 + i][tl];
+    x[i] = sacc;
+  }
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  if (is_v) {
+    if (valid) {
+      float4* vp = reinterpret_cast<float4*>(a.v + gt * d + c0);
+      vp[0] = make_float4(x[0], x[1], x[2], x[3]);
+      vp[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s3 += x[i] * x[i];
+  } else {
+    const uint4 hq = *reinterpret_cast<const uint4*>(a.H + (ct * a.M + m) * d + c0);
+    const uint32_t hw[4] = {hq.x, hq.y, hq.z, hq.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float h = __uint_as_float(i & 1 ? (hw[i >> 1] & 0xffff0000u) : (hw[i >> 1] << 16));
+      s0 += h * h;
+      s1 += x[i] * x[i];
+      s2 += h * x[i];
+    }
+  }
+  // the 8 feature groups of a token sit in lanes tl, tl+32 of waves 0..3
+  s0 += __shfl_xor(s0, 32, 64);
+  s1 += __shfl_xor(s1, 32, 64);
+  s2 += __shfl_xor(s2, 32, 64);
+  s3 += __shfl_xor(s3, 32, 64);
+  if (lane < 32) red[wave][tl] = make_float4(s0, s1, s2, s3);
+  __syncthreads();
+  if (threadIdx.x < kSmallTK && t0 + threadIdx.x < a.n_tok) {
+    float4 p = red[0][threadIdx.x];
+#pragma unroll
+    for (int w = 1; w < kSmallWaves; ++w) {
+      const float4 q = red[w][threadIdx.x];
+      p = make_float4(p.x + q.x, p.y + q.y, p.z + q.z, p.w + q.w);
+    }
+    a.stats[(t0 + threadIdx.x) * a.tiles_f + tf] = p;
+  }
+}
+
 template <int TF, int PD>
 hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   a.tiles_f = a.N / TF;
@@ -243,20 +372,33 @@ hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
 
 }  // namespace
 
+// Few tokens: the small kernel (64-column statistics tiles); otherwise the
+// large one with 256-column tiles when there are enough of them.
+bool proj_gate_small(int64_t n_tok, int N) { return ((n_tok + TK - 1) / TK) * (N / 128) < 128; }
+
 int proj_gate_tile_f(int64_t n_tok, int N, int d) {
+  if (proj_gate_small(n_tok, N)) return kSmallTF;
   // 256-feature tiles halve the LDS traffic per matrix operation but need at
   // least two tiles per CU (512) to keep the chip busy
   const int64_t tiles256 = ((n_tok + TK - 1) / TK) * (N / 256);
   return (d % 256 == 0 && tiles256 >= 512) ? 256 : 128;
 }
 
-hipError_t launch_proj_gate(const ProjGateArgs& a, hipStream_t s) {
-  if (a.n_tok == 0) return hipSuccess;
-  if (a.K % BK != 0 || a.N % 128 != 0) return hipErrorInvalidValue;
-  const bool pd2 = (a.K / BK) % 2 == 0;
-  if (proj_gate_tile_f(a.n_tok, a.N, a.d) == 256)
-    return pd2 ? launch_tf<256, 2>(a, s) : launch_tf<256, 1>(a, s);
-  return pd2 ? launch_tf<128, 2>(a, s) : launch_tf<128, 1>(a, s);
+hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
+  if (in.n_tok == 0) return hipSuccess;
+  if (in.K % BK != 0 || in.N % 128 != 0) return hipErrorInvalidValue;
+  if (proj_gate_small(in.n_tok, in.N)) {
+    ProjGateArgs a = in;
+    a.tiles_f = a.N / kSmallTF;
+    a.tiles_t = static_cast<int>((a.n_tok + kSmallTK - 1) / kSmallTK);
+    launch_k(proj_gate_small_kernel, dim3(static_cast<unsigned>(a.tiles_f * a.tiles_t)), dim3(64 * kSmallWaves), 0,
+             s, a);
+    return hipGetLastError();
+  }
+  const bool pd2 = (in.K / BK) % 2 == 0;
+  if (proj_gate_tile_f(in.n_tok, in.N, in.d) == 256)
+    return pd2 ? launch_tf<256, 2>(in, s) : launch_tf<256, 1>(in, s);
+  return pd2 ? launch_tf<128, 2>(in, s) : launch_tf<128, 1>(in, s);
 }
 
 }  // namespace engram
