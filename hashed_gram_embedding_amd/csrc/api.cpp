@@ -101,6 +101,7 @@ engram_status check_tables(const engram_tables* tab, engram::TableArgs* out) {
   }
   if (tab->dtype == ENGRAM_I8 && tab->row_scale == nullptr)
     return fail(ENGRAM_EINVAL, "tables: int8 rows need row_scale");
+  if (!aligned(tab->access_counts, 4)) return fail(ENGRAM_EINVAL, "tables: access_counts must be 4-byte aligned");
   if (tab->cache_slot != nullptr) {
     if (tab->cache_rows == nullptr || tab->cache_n < 0)
       return fail(ENGRAM_EINVAL, "tables: a cache needs cache_rows and cache_n >= 0");
@@ -117,6 +118,7 @@ engram_status check_tables(const engram_tables* tab, engram::TableArgs* out) {
     out->cache_slot = tab->cache_slot;
     out->cache_rows = tab->cache_rows;
     out->cache_scale = tab->cache_scale;
+    out->counts = tab->access_counts;
     out->n_tables = tab->n_tables;
     out->dim = tab->dim;
     out->dtype = tab->dtype;
@@ -616,6 +618,40 @@ ENGRAM_API engram_status engram_cache_build(const int32_t* warm_tokens, int64_t 
                                                cache_slot, cache_rows, tab->dtype == ENGRAM_I8 ? cache_scale : nullptr,
                                                ws, stream),
                     "cache build launch");
+}
+
+ENGRAM_API size_t engram_cache_update_workspace(int64_t total_rows, int64_t cache_n) {
+  if (total_rows <= 0 || cache_n < 0 || cache_n > total_rows) return 0;
+  return engram::cache_update_workspace(total_rows, cache_n);
+}
+
+ENGRAM_API engram_status engram_cache_update(const engram_tables* tab, int64_t cache_n, int32_t* cache_slot,
+                                             void* cache_rows, float* cache_scale, uint32_t* counts,
+                                             int32_t decay_shift, void* ws, size_t ws_bytes, hipStream_t stream) {
+  engram::TableArgs ta;
+  if (tab == nullptr) return fail(ENGRAM_EINVAL, "cache_update: tables are NULL");
+  engram_tables plain = *tab;   // the cache being updated is passed separately
+  plain.cache_slot = nullptr;
+  plain.access_counts = nullptr;
+  engram_status r = check_tables(&plain, &ta);
+  if (r != ENGRAM_OK) return r;
+  if (cache_n < 0 || cache_n > tab->total_rows || tab->total_rows > 0x7fffffffLL)
+    return fail(ENGRAM_EINVAL, "cache_update: need 0 <= cache_n <= total_rows < 2^31");
+  if (cache_slot == nullptr || counts == nullptr || (cache_n > 0 && cache_rows == nullptr))
+    return fail(ENGRAM_EINVAL, "cache_update: cache_slot, counts and cache_rows must be non-NULL");
+  if (tab->dtype == ENGRAM_I8 && cache_n > 0 && cache_scale == nullptr)
+    return fail(ENGRAM_EINVAL, "cache_update: int8 tables need cache_scale");
+  if (!aligned(cache_rows, 8) || !aligned(counts, 4) || !aligned(cache_slot, 4))
+    return fail(ENGRAM_EINVAL, "cache_update: misaligned cache_rows, counts or cache_slot");
+  if (decay_shift < 0 || decay_shift > 31) return fail(ENGRAM_EINVAL, "cache_update: decay_shift outside [0, 31]");
+  const size_t need = engram::cache_update_workspace(tab->total_rows, cache_n);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(ENGRAM_EINVAL, "cache_update: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  const int row_bytes = tab->dim * static_cast<int>(dtype_size(tab->dtype));
+  return hip_status(engram::launch_cache_update(ta, tab->total_rows, row_bytes, cache_n, cache_slot, cache_rows,
+                                                tab->dtype == ENGRAM_I8 ? cache_scale : nullptr, counts, decay_shift,
+                                                ws, stream),
+                    "cache update launch");
 }
 
 ENGRAM_API engram_status engram_profile_enable(int32_t on) {

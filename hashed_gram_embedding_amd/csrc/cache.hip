@@ -14,6 +14,19 @@
 //   scan x2    rank of each count-c* row among equals, then the slot of each
 //              admitted row (block scans + a scan of the block sums)
 //   copy       admitted rows (and int8 scales) into the cache
+//
+// Real-time LFU (the same article's hot cache kept up to date from access
+// statistics, with admission and eviction): the gathers add 1 per access to a
+// per-row count, and an update between steps re-ranks the rows by their
+// current counts with the same rule.  Rows that stay keep their slots; rows
+// that fall out free theirs; newcomers, in ascending row order, take the free
+// slots in ascending slot order and only their rows are copied.  Counts may
+// then be aged by a right shift.
+//   mark       stayers claim their slot, leavers drop theirs
+//   scan x2    rank of each newcomer (rows) and of each free slot (slots)
+//   assign     newcomer k -> k-th free slot; the newcomer list
+//   copy       newcomer rows (and int8 scales) into their slots
+//   age        counts >>= shift
 #include "device_util.h"
 #include "engram_internal.h"
 #include "hash_device.h"
@@ -92,20 +105,37 @@ threshold_kernel(const uint32_t* __restrict__ bins, int64_t cap, int64_t* __rest
   }
 }
 
-// mode 0: flag = (count == c*);  mode 1: flag = admitted, using eq_rank from mode 0.
-__device__ __forceinline__ int32_t scan_flag(int mode, const uint32_t* counts, const int32_t* eq_rank,
-                                             const int64_t* params, int64_t i) {
-  const uint32_t c = counts[i];
-  const uint32_t cs = static_cast<uint32_t>(params[0]);
+// Inputs of the scan flags.
+struct FlagSrc {
+  const uint32_t* counts;
+  const int32_t* eq_rank;
+  const int64_t* params;
+  const int32_t* slot;    // row -> slot map (mode 2)
+  const int32_t* owned;   // slot -> 1 when a staying row holds it (mode 3)
+};
+
+__device__ __forceinline__ bool admitted(const FlagSrc& f, int64_t i) {
+  const uint32_t c = f.counts[i];
+  const uint32_t cs = static_cast<uint32_t>(f.params[0]);
   const uint32_t cc = c < kBins - 1 ? c : kBins - 1;
-  if (mode == 0) return cc == cs ? 1 : 0;
-  return (cc > cs || (cc == cs && eq_rank[i] < params[1])) ? 1 : 0;
+  return cc > cs || (cc == cs && f.eq_rank[i] < f.params[1]);
+}
+
+// mode 0: row count == c*;  mode 1: row admitted (eq_rank from mode 0);
+// mode 2: row admitted and not cached (a newcomer);  mode 3: slot free.
+__device__ __forceinline__ int32_t scan_flag(int mode, const FlagSrc& f, int64_t i) {
+  if (mode == 0) {
+    const uint32_t c = f.counts[i];
+    return (c < kBins - 1 ? c : kBins - 1) == static_cast<uint32_t>(f.params[0]) ? 1 : 0;
+  }
+  if (mode == 1) return admitted(f, i) ? 1 : 0;
+  if (mode == 2) return (f.slot[i] < 0 && admitted(f, i)) ? 1 : 0;
+  return f.owned[i] == 0 ? 1 : 0;
 }
 
 // Per-block exclusive scan of the flags, block totals to sums[].
 __global__ void __launch_bounds__(kScanThreads)
-scan_local_kernel(int mode, const uint32_t* __restrict__ counts, const int32_t* __restrict__ eq_rank,
-                  const int64_t* __restrict__ params, int64_t n, int32_t* __restrict__ out, int32_t* __restrict__ sums) {
+scan_local_kernel(int mode, FlagSrc f, int64_t n, int32_t* __restrict__ out, int32_t* __restrict__ sums) {
   __shared__ int32_t warp_tot[kScanThreads / 64];
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kScanBlock + threadIdx.x * kScanItems;
   int32_t v[kScanItems];
@@ -113,7 +143,7 @@ scan_local_kernel(int mode, const uint32_t* __restrict__ counts, const int32_t* 
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
     const int64_t i = base + k;
-    v[k] = i < n ? scan_flag(mode, counts, eq_rank, params, i) : 0;
+    v[k] = i < n ? scan_flag(mode, f, i) : 0;
     run += v[k];
   }
   // exclusive scan of the per-thread totals across the block
@@ -166,19 +196,74 @@ __global__ void __launch_bounds__(1024) scan_sums_kernel(int32_t* __restrict__ s
 
 // mode 0: eq_rank[i] = global exclusive rank among equals.
 // mode 1: cache_slot[i] = slot of an admitted row, else -1.
+// modes 2, 3: rank of a flagged row / slot, else -1.
 __global__ void __launch_bounds__(256)
-scan_finish_kernel(int mode, const uint32_t* __restrict__ counts, const int32_t* __restrict__ eq_rank,
-                   const int64_t* __restrict__ params, int64_t n, int32_t* __restrict__ out,
-                   const int32_t* __restrict__ sums) {
+scan_finish_kernel(int mode, FlagSrc f, int64_t n, int32_t* __restrict__ out, const int32_t* __restrict__ sums) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int32_t r = out[i] + sums[i / kScanBlock];
-    if (mode == 0) {
-      out[i] = r;
-    } else {
-      out[i] = scan_flag(1, counts, eq_rank, params, i) ? r : -1;
-    }
+    out[i] = (mode == 0 || scan_flag(mode, f, i)) ? r : -1;
   }
+}
+
+// Stayers claim their slot in owned[]; cached rows that are no longer
+// admitted leave the cache (slot -1).
+__global__ void __launch_bounds__(256)
+mark_kernel(FlagSrc f, int64_t n, int32_t* __restrict__ slot, int32_t* __restrict__ owned) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int32_t s = slot[i];
+    if (s < 0) continue;
+    if (admitted(f, i)) owned[s] = 1;
+    else slot[i] = -1;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+free_list_kernel(const int32_t* __restrict__ free_rank, int64_t n_slots, int32_t* __restrict__ free_list) {
+  for (int64_t s = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; s < n_slots;
+       s += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int32_t r = free_rank[s];
+    if (r >= 0) free_list[r] = static_cast<int32_t>(s);
+  }
+}
+
+// Newcomer k (ascending row order) takes the k-th free slot (ascending slot
+// order); there are never more newcomers than free slots.
+__global__ void __launch_bounds__(256)
+assign_kernel(const int32_t* __restrict__ new_rank, int64_t n, const int32_t* __restrict__ free_list,
+              int32_t* __restrict__ slot, int32_t* __restrict__ new_list) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int32_t r = new_rank[i];
+    if (r < 0) continue;
+    slot[i] = free_list[r];
+    new_list[r] = static_cast<int32_t>(i);
+  }
+}
+
+// One thread per (newcomer, 8-byte chunk); unused list entries hold -1.
+__global__ void __launch_bounds__(256)
+copy_new_kernel(const int32_t* __restrict__ new_list, int64_t n_slots, const int32_t* __restrict__ slot,
+                const uint8_t* __restrict__ rows, const float* __restrict__ scale, int row_bytes,
+                uint8_t* __restrict__ cache, float* __restrict__ cache_scale) {
+  const int chunks = row_bytes / 8;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= n_slots * chunks) return;
+  const int64_t k = gid / chunks;
+  const int c = static_cast<int>(gid - k * chunks);
+  const int32_t r = new_list[k];
+  if (r < 0) return;
+  const int32_t s = slot[r];
+  *reinterpret_cast<uint2*>(cache + static_cast<int64_t>(s) * row_bytes + c * 8) =
+      *reinterpret_cast<const uint2*>(rows + static_cast<int64_t>(r) * row_bytes + c * 8);
+  if (c == 0 && scale != nullptr) cache_scale[s] = scale[r];
+}
+
+__global__ void __launch_bounds__(256) age_kernel(uint32_t* __restrict__ counts, int64_t n, int shift) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    counts[i] >>= shift;
 }
 
 // One thread per (row, 16-byte chunk) of an admitted row.
@@ -201,6 +286,22 @@ copy_rows_kernel(const int32_t* __restrict__ slot, int64_t n, const uint8_t* __r
 unsigned grid_for(int64_t n, int threads) {
   const int64_t b = (n + threads - 1) / threads;
   return static_cast<unsigned>(b < 65535 * 64 ? b : 65535 * 64);
+}
+
+// Exclusive ranks of the flagged items of [0, n) into out (scan_finish_kernel).
+void scan(int mode, const FlagSrc& f, int64_t n, int32_t* out, int32_t* sums, hipStream_t s) {
+  const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
+  launch_k(scan_local_kernel, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0, s, mode, f, n, out, sums);
+  launch_k(scan_sums_kernel, dim3(1), dim3(1024), 0, s, sums, nb);
+  launch_k(scan_finish_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, mode, f, n, out, sums);
+}
+
+// Histogram of the counts and the admission threshold into params.
+void rank_threshold(const uint32_t* counts, int64_t total_rows, int64_t cache_n, uint32_t* bins, int64_t* params,
+                    hipStream_t s) {
+  launch_k(fill_u32, dim3(grid_for(kBins, 256)), dim3(256), 0, s, bins, static_cast<int64_t>(kBins), 0u);
+  launch_k(histogram_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, counts, total_rows, bins);
+  launch_k(threshold_kernel, dim3(1), dim3(1024), 0, s, bins, cache_n, params);
 }
 
 }  // namespace
@@ -229,25 +330,73 @@ hipError_t launch_cache_build(const int32_t* tokens, int64_t B, int64_t T, const
   int64_t* params = reinterpret_cast<int64_t*>(p);
 
   launch_k(fill_u32, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, counts, total_rows, 0u);
-  launch_k(fill_u32, dim3(grid_for(kBins, 256)), dim3(256), 0, s, bins, static_cast<int64_t>(kBins), 0u);
   const int64_t pairs = B * T * ha.n_tables;
   if (pairs > 0)
     launch_k(count_kernel, dim3(static_cast<unsigned>((pairs + 255) / 256)), dim3(256), 0, s, tokens, B, T,
                        proj, ha, ta, counts);
-  launch_k(histogram_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, counts, total_rows, bins);
-  launch_k(threshold_kernel, dim3(1), dim3(1024), 0, s, bins, cache_n, params);
-  for (int mode = 0; mode < 2; ++mode) {
-    int32_t* out = mode == 0 ? eq_rank : cache_slot;
-    launch_k(scan_local_kernel, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0, s, mode, counts,
-                       eq_rank, params, total_rows, out, sums);
-    launch_k(scan_sums_kernel, dim3(1), dim3(1024), 0, s, sums, nb);
-    launch_k(scan_finish_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, mode, counts, eq_rank,
-                       params, total_rows, out, sums);
-  }
+  rank_threshold(counts, total_rows, cache_n, bins, params, s);
+  const FlagSrc f{counts, eq_rank, params, nullptr, nullptr};
+  for (int mode = 0; mode < 2; ++mode) scan(mode, f, total_rows, mode == 0 ? eq_rank : cache_slot, sums, s);
   const int64_t work = total_rows * (row_bytes / 8);
   launch_k(copy_rows_kernel, dim3(static_cast<unsigned>((work + 255) / 256)), dim3(256), 0, s, cache_slot,
                      total_rows, static_cast<const uint8_t*>(ta.rows), ta.scale, row_bytes,
                      static_cast<uint8_t*>(cache_rows), cache_scale);
+  return hipGetLastError();
+}
+
+size_t cache_update_workspace(int64_t total_rows, int64_t cache_n) {
+  const int64_t nb = (total_rows + kScanBlock - 1) / kScanBlock;
+  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  return al(kBins * 4) /*bins*/ + 2 * al(total_rows * 4) /*eq rank, newcomer rank*/ + al(nb * 4) /*block sums*/ +
+         4 * al(cache_n * 4) /*owned, free rank, free list, newcomer list*/ + al(16) /*params*/;
+}
+
+hipError_t launch_cache_update(const TableArgs& ta, int64_t total_rows, int row_bytes, int64_t cache_n,
+                               int32_t* cache_slot, void* cache_rows, float* cache_scale, uint32_t* counts,
+                               int decay_shift, void* ws, hipStream_t s) {
+  const int64_t nb = (total_rows + kScanBlock - 1) / kScanBlock;
+  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  char* p = static_cast<char*>(ws);
+  uint32_t* bins = reinterpret_cast<uint32_t*>(p);
+  p += al(kBins * 4);
+  int32_t* eq_rank = reinterpret_cast<int32_t*>(p);
+  p += al(total_rows * 4);
+  int32_t* new_rank = reinterpret_cast<int32_t*>(p);
+  p += al(total_rows * 4);
+  int32_t* sums = reinterpret_cast<int32_t*>(p);
+  p += al(nb * 4);
+  int32_t* owned = reinterpret_cast<int32_t*>(p);
+  p += al(cache_n * 4);
+  int32_t* free_rank = reinterpret_cast<int32_t*>(p);
+  p += al(cache_n * 4);
+  int32_t* free_list = reinterpret_cast<int32_t*>(p);
+  p += al(cache_n * 4);
+  int32_t* new_list = reinterpret_cast<int32_t*>(p);
+  p += al(cache_n * 4);
+  int64_t* params = reinterpret_cast<int64_t*>(p);
+
+  rank_threshold(counts, total_rows, cache_n, bins, params, s);
+  FlagSrc f{counts, eq_rank, params, cache_slot, owned};
+  scan(0, f, total_rows, eq_rank, sums, s);
+  if (cache_n > 0) {
+    launch_k(fill_u32, dim3(grid_for(cache_n, 256)), dim3(256), 0, s, reinterpret_cast<uint32_t*>(owned), cache_n, 0u);
+    launch_k(fill_u32, dim3(grid_for(cache_n, 256)), dim3(256), 0, s, reinterpret_cast<uint32_t*>(new_list), cache_n,
+             0xffffffffu);
+  }
+  launch_k(mark_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, f, total_rows, cache_slot, owned);
+  scan(2, f, total_rows, new_rank, sums, s);
+  if (cache_n > 0) {
+    scan(3, f, cache_n, free_rank, sums, s);
+    launch_k(free_list_kernel, dim3(grid_for(cache_n, 256)), dim3(256), 0, s, free_rank, cache_n, free_list);
+    launch_k(assign_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, new_rank, total_rows, free_list,
+             cache_slot, new_list);
+    const int64_t work = cache_n * (row_bytes / 8);
+    launch_k(copy_new_kernel, dim3(static_cast<unsigned>((work + 255) / 256)), dim3(256), 0, s, new_list, cache_n,
+             cache_slot, static_cast<const uint8_t*>(ta.rows), ta.scale, row_bytes, static_cast<uint8_t*>(cache_rows),
+             cache_scale);
+  }
+  if (decay_shift > 0)
+    launch_k(age_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, counts, total_rows, decay_shift);
   return hipGetLastError();
 }
 

@@ -36,6 +36,7 @@ struct TableArgs {
   const int32_t* cache_slot;
   const void* cache_rows;
   const float* cache_scale;
+  uint32_t* counts;  // optional per-row access counts
   int32_t n_tables;
   int32_t dim;
   int32_t dtype;  // engram_dtype
@@ -121,6 +122,10 @@ hipError_t launch_state_commit(const void* v, int64_t v_stride, int vdtype, int6
                                const int32_t* tokens, const int32_t* proj, int32_t max_n, hipStream_t s);
 
 size_t cache_build_workspace(int64_t total_rows);
+size_t cache_update_workspace(int64_t total_rows, int64_t cache_n);
+hipError_t launch_cache_update(const TableArgs& ta, int64_t total_rows, int row_bytes, int64_t cache_n,
+                               int32_t* cache_slot, void* cache_rows, float* cache_scale, uint32_t* counts,
+                               int decay_shift, void* ws, hipStream_t s);
 hipError_t launch_cache_build(const int32_t* tokens, int64_t B, int64_t T, const int32_t* proj, const HashArgs& ha,
                               const TableArgs& ta, int64_t total_rows, int row_bytes, int64_t cache_n,
                               int32_t* cache_slot, void* cache_rows, float* cache_scale, void* ws, hipStream_t s);

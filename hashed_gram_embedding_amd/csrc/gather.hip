@@ -14,7 +14,8 @@
 // adjacent and each wavefront writes a contiguous 1 KiB span of e.
 //
 // Inside the layer forward the row index is hashed in the same thread
-// (Steps 1-3), so the indices never go through memory.
+// (Steps 1-3), so the indices never go through memory.  With access counts
+// given, the first thread of each row access adds 1 to the row's count.
 #include "device_util.h"
 #include "engram_internal.h"
 #include "hash_device.h"
@@ -67,6 +68,7 @@ gather_kernel(const int32_t* __restrict__ z, int64_t n_tok, TableArgs ta, void* 
     zj = z[tj];
   }
   int64_t row = ta.row_offset[j] + zj;
+  if (ta.counts != nullptr && c == 0) atomicAdd(ta.counts + row, 1u);   // access statistics (real-time LFU)
   const void* src = ta.rows;
   const float* scale = ta.scale;
   if (ta.cache_slot != nullptr) {

@@ -38,7 +38,8 @@ class Tables(ctypes.Structure):
                 ("rows", ctypes.c_void_p), ("row_offset", ctypes.c_void_p), ("n_rows", ctypes.c_void_p),
                 ("total_rows", ctypes.c_int64), ("row_scale", ctypes.c_void_p),
                 ("cache_slot", ctypes.c_void_p), ("cache_rows", ctypes.c_void_p),
-                ("cache_scale", ctypes.c_void_p), ("cache_n", ctypes.c_int64)]
+                ("cache_scale", ctypes.c_void_p), ("cache_n", ctypes.c_int64),
+                ("access_counts", ctypes.c_void_p)]
 
 
 class GateConvParams(ctypes.Structure):
@@ -90,6 +91,8 @@ def lib():
         "engram_forward_retrieved_workspace": (sz, [i64, i64, ctypes.POINTER(LayerStruct)]),
         "engram_forward_retrieved": (i32, [vp, vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
                                            ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
+        "engram_cache_update_workspace": (sz, [i64, i64]),
+        "engram_cache_update": (i32, [ctypes.POINTER(Tables), i64, vp, vp, vp, vp, i32, vp, sz, vp]),
         "engram_cache_build_workspace": (sz, [i64]),
         "engram_cache_build": (i32, [vp, i64, i64, ctypes.POINTER(HashParams), ctypes.POINTER(Tables), i64, vp, vp, vp,
                                      vp, sz, vp]),
@@ -112,6 +115,7 @@ def exported_names():
             "engram_project_kv", "engram_gate_conv_workspace", "engram_gate_conv_forward",
             "engram_forward_workspace", "engram_forward", "engram_retrieve", "engram_forward_retrieved_workspace",
             "engram_forward_retrieved", "engram_cache_build_workspace", "engram_cache_build",
+            "engram_cache_update_workspace", "engram_cache_update",
             "engram_profile_enable", "engram_profile_read",
             "engram_host_alloc", "engram_host_free"]
 
@@ -189,6 +193,7 @@ class Layer:
         self.w = to_device(li.w, "bf16" if hdtype == "bf16" else "f32", device)
         self.conv_w = to_device(li.conv_w.astype(np.float32), "f32", device)
         self.cache_slot = self.cache_rows = self.cache_scale = None
+        self.access_counts = None
         self.cache_n = 0
         self.s = LayerStruct()
         self.s.hash = self.hs.s
@@ -208,6 +213,12 @@ class Layer:
         t.cache_scale = None if scale is None else scale.data_ptr()
         self.cache_n = 0 if rows is None else rows.shape[0]
         t.cache_n = self.cache_n
+
+    def set_access_counts(self, counts: Optional[torch.Tensor]):
+        """Per-row access counts (uint32 as int32 [total_rows]) that every gather
+        through this layer increments; None stops counting."""
+        self.access_counts = counts
+        self.s.tables.access_counts = None if counts is None else counts.data_ptr()
 
     @property
     def M(self):
@@ -325,6 +336,18 @@ def cache_build(warm_tokens: torch.Tensor, layer: Layer, cache_n: int, stream=No
     _check(lib().engram_cache_build(_ptr(warm_tokens), B, T, ctypes.byref(layer.s.hash), ctypes.byref(tab), cache_n,
                                     _ptr(slot), _ptr(rows), _ptr(scale), _ptr(ws), ws.numel(), _stream(stream)))
     return slot, rows, scale
+
+
+def cache_update(layer: Layer, counts: torch.Tensor, decay_shift: int = 0, stream=None):
+    """Real-time LFU update of the layer's attached cache (set_cache) from the
+    access counts; the slot map and cache rows are updated in place."""
+    t = layer.s.tables
+    n = layer.cache_n
+    ws = torch.empty(max(lib().engram_cache_update_workspace(t.total_rows, n), 256), dtype=torch.uint8,
+                     device=counts.device)
+    _check(lib().engram_cache_update(ctypes.byref(t), n, _ptr(layer.cache_slot), _ptr(layer.cache_rows),
+                                     _ptr(layer.cache_scale), _ptr(counts), decay_shift, _ptr(ws), ws.numel(),
+                                     _stream(stream)))
 
 
 def profile_enable(on: bool = True):

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 1
+#define ENGRAM_ABI_VERSION 2
 #define ENGRAM_MAX_TABLES 32 /* (N-1)*K */
 #define ENGRAM_MAX_ORDER 4   /* N */
 #define ENGRAM_MAX_KERNEL_W 8
@@ -106,6 +106,10 @@ typedef struct engram_tables {
   const void* cache_rows;    /* device [cache_n][dim], same dtype as rows        */
   const float* cache_scale;  /* device [cache_n]; I8 only                        */
   int64_t cache_n;           /* slots in the cache                               */
+  /* optional access statistics for the real-time LFU cache (NULL = none):
+     every gather through these tables adds 1 to the count of each row it
+     reads (global row, before the cache probe; one atomic add per access) */
+  uint32_t* access_counts;   /* device [total_rows]                              */
 } engram_tables;
 
 /* Steps 6-8: gate, short conv and residual. */
@@ -245,6 +249,27 @@ engram_status engram_cache_build(const int32_t* warm_tokens, int64_t B, int64_t 
                                  int64_t cache_n, int32_t* cache_slot, void* cache_rows,
                                  float* cache_scale, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
+
+/* Real-time LFU update of the hot cache between steps: the RecSDK article
+ * keeps the hot cache current from access-frequency statistics, with LFU
+ * admission and eviction (multi-level cache section, real-time update).
+ * counts: device [total_rows], the access_counts the gathers accumulated.
+ * The cache_n rows with the highest counts are admitted (ties: lower global
+ * row first; exact while the threshold count is below 2^20 - 1).  Cached rows
+ * that stay keep their slots; cached rows that are no longer admitted get
+ * slot -1; newly admitted rows, in ascending row order, take the free slots
+ * in ascending slot order, and only their rows (and int8 scales) are copied
+ * from tab->rows (HBM or mapped host memory).  Afterwards every count is
+ * shifted right by decay_shift (0..31; 0 keeps the counts).  cache_slot,
+ * cache_rows and cache_scale are the cache being updated (as returned by
+ * engram_cache_build or a previous update; tab's own cache fields are
+ * ignored).  Asynchronous; must not overlap a gather that reads the cache.
+ * ws: engram_cache_update_workspace() bytes, 256-byte aligned. */
+size_t engram_cache_update_workspace(int64_t total_rows, int64_t cache_n);
+engram_status engram_cache_update(const engram_tables* tab, int64_t cache_n, int32_t* cache_slot,
+                                  void* cache_rows, float* cache_scale, uint32_t* counts,
+                                  int32_t decay_shift, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /* Stage timing, for benchmarks.  engram_profile_enable(1) makes later
  * engram_forward and engram_gate_conv_forward calls on the calling thread

@@ -212,6 +212,31 @@ def lfu_admission(global_rows: np.ndarray, total_rows: int, cache_n: int) -> np.
     return slot
 
 
+def lfu_update(counts: np.ndarray, slot_prev: np.ndarray, cache_n: int, decay_shift: int = 0):
+    """Real-time LFU update of the hot cache (Ascend RecSDK Engram article,
+    multi-level cache: access statistics drive LFU admission and eviction so
+    the hot cache stays current).
+
+    The cache_n rows with the highest counts are admitted (ties: lower row
+    first).  A cached row that is admitted again keeps its slot; a cached row
+    that is not admitted leaves (-1).  The slots nobody keeps, in ascending
+    order, go to the newly admitted rows in ascending row order.  Then every
+    count is shifted right by decay_shift.  Returns (slot, counts)."""
+    counts = np.asarray(counts, dtype=np.int64)
+    slot_prev = np.asarray(slot_prev, dtype=np.int64)
+    total_rows = counts.shape[0]
+    order = np.lexsort((np.arange(total_rows), -counts))     # by count desc, then row asc
+    is_admitted = np.zeros(total_rows, dtype=bool)
+    is_admitted[order[:cache_n]] = True
+    slot = np.where(is_admitted & (slot_prev >= 0), slot_prev, -1)
+    kept = np.zeros(cache_n, dtype=bool)
+    kept[slot[slot >= 0]] = True
+    free_slots = np.nonzero(~kept)[0]                         # ascending
+    newcomers = np.nonzero(is_admitted & (slot_prev < 0))[0]  # ascending rows
+    slot[newcomers] = free_slots[:newcomers.shape[0]]
+    return slot, counts >> decay_shift
+
+
 # --------------------------------------------------------------------------
 # Step 5: key / value projections
 # --------------------------------------------------------------------------

@@ -39,7 +39,7 @@ def test_exports_match_header():
 
 
 def test_abi_version():
-    assert eg.lib().engram_abi_version() == 1
+    assert eg.lib().engram_abi_version() == 2
 
 
 def _hash_params(**over):
@@ -237,3 +237,26 @@ def test_retrieve_and_forward_retrieved_reject_bad_arguments():
     st, msg = _status(L.engram_forward_retrieved, None, p, p, 1, 64, ctypes.byref(lay), ctypes.byref(sd), None, None,
                       p, need, None)
     assert st == eg.EINVAL and "tokens" in msg
+
+
+def test_cache_update_rejects_bad_arguments():
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    t, keep_t = _tables()
+    need = L.engram_cache_update_workspace(4062, 100)
+    assert need > 0 and L.engram_cache_update_workspace(4062, 5000) == 0
+    # (a valid call would launch: only the rejected ones run here)
+    st, msg = _status(L.engram_cache_update, ctypes.byref(t), 100, p, p, None, None, 0, p, need, None)
+    assert st == eg.EINVAL and "counts" in msg
+    st, msg = _status(L.engram_cache_update, ctypes.byref(t), 100, p, p, None, p, 32, p, need, None)
+    assert st == eg.EINVAL and "decay_shift" in msg
+    st, msg = _status(L.engram_cache_update, ctypes.byref(t), 100, p, p, None, p, 1, p, need - 1, None)
+    assert st == eg.EINVAL and "workspace" in msg
+    st, msg = _status(L.engram_cache_update, ctypes.byref(t), 5000, p, p, None, p, 1, p, need, None)
+    assert st == eg.EINVAL and "cache_n" in msg
+    t8, k8 = _tables(dtype=eg.I8, row_scale=0x20000)
+    st, msg = _status(L.engram_cache_update, ctypes.byref(t8), 100, p, p, None, p, 1, p, need, None)
+    assert st == eg.EINVAL and "cache_scale" in msg
+    tc, kc = _tables(access_counts=0x10002)
+    st, msg = _status(L.engram_gather, p, 4, ctypes.byref(tc), eg.F32, p, None)
+    assert st == eg.EINVAL and "access_counts" in msg

@@ -107,3 +107,44 @@ def test_lfu_admission_hand_example():
     assert list(orc.lfu_admission(np.array(rows), 7, 7)) == [0, 1, 2, 3, 4, 5, 6]
     # zero-count rows fill the cache last, lowest first
     assert list(orc.lfu_admission(np.array([6, 6]), 7, 3)) == [0, 1, -1, -1, -1, -1, 2]
+
+
+def test_lfu_update_hand_example():
+    """counts [5, 3, 3, 3, 1, 0, 3]; rows 0, 4, 6 cached in slots 2, 0, 1 of a
+    4-slot cache.  Admitted: row 0 and the three lowest rows of count 3 (1, 2,
+    3).  Row 0 keeps slot 2; rows 4 and 6 leave; the free slots 0, 1, 3 go to
+    rows 1, 2, 3 in that order.  Aging by one bit halves the counts."""
+    counts = np.array([5, 3, 3, 3, 1, 0, 3])
+    prev = np.array([2, -1, -1, -1, 0, -1, 1])
+    slot, aged = orc.lfu_update(counts, prev, 4, decay_shift=1)
+    assert list(slot) == [2, 0, 1, 3, -1, -1, -1]
+    assert list(aged) == [2, 1, 1, 1, 0, 0, 1]
+    slot0, same = orc.lfu_update(counts, prev, 4)
+    assert list(slot0) == list(slot) and list(same) == list(counts)
+
+
+def test_lfu_update_from_empty_equals_static_admission():
+    rng = np.random.default_rng(8)
+    rows = rng.zipf(1.3, 5000) % 400
+    counts = np.bincount(rows, minlength=400)
+    for n in (0, 1, 37, 400):
+        slot, _ = orc.lfu_update(counts, np.full(400, -1), n)
+        assert np.array_equal(slot, orc.lfu_admission(rows, 400, n))
+
+
+def test_lfu_update_invariants_under_drift():
+    """Random drift: the admitted set is the top cache_n by (count, -row);
+    slots form a permutation of 0..n-1; stayers never move."""
+    rng = np.random.default_rng(9)
+    total, n = 300, 40
+    slot = np.full(total, -1)
+    counts = np.zeros(total, dtype=np.int64)
+    for step in range(6):
+        counts = counts + np.bincount(rng.integers(0, total, 500) ** 2 % total, minlength=total)
+        new, counts_after = orc.lfu_update(counts, slot, n, decay_shift=1)
+        order = np.lexsort((np.arange(total), -counts))
+        assert set(np.nonzero(new >= 0)[0]) == set(order[:n])
+        assert sorted(new[new >= 0]) == list(range(n))
+        stay = (slot >= 0) & (new >= 0)
+        assert np.array_equal(new[stay], slot[stay])
+        slot, counts = new, counts_after
