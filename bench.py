@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--overlap", action="store_true",
                     help="also measure retrieval (Steps 1-4) run ahead on a second stream: hidden behind a "
                          "stand-in for the preceding layers, and pipelined across batches")
+    ap.add_argument("--realtime-lfu", action="store_true",
+                    help="host-table workload: drift the token distribution and measure the static cache against "
+                         "the real-time LFU update (hit rate, step time, update time)")
     ap.add_argument("--hbm-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                          "run with --copy-calibration-mib into the per-kernel HBM bytes table and exit")
@@ -413,6 +416,72 @@ def pipelined_report(torch, eg, w, pipe, steps):
                    "two alternating token batches; HIP graphs of two-step cycles"}
 
 
+def realtime_lfu_report(torch, eg, inputs, w, pipe, rounds=4, steps_per_round=8):
+    """The hot cache under a shifted token distribution (the Zipf ranks mapped
+    to ids by a different seeded permutation than the warm-up stream's; fresh
+    batches every round):
+    static LFU cache vs. the real-time LFU update.  Each round runs
+    steps_per_round steps of every layer with access counting on, then
+    updates every layer's cache from its counts (aged by one bit at each
+    update).  Reports
+    per round the hit rate over the round's accesses, the step time and the
+    update time."""
+    import numpy as np
+    Ls, tok, H = pipe
+    B, T = tok.shape
+    dev = "cuda"
+    rng = np.random.default_rng(21)
+    perm = rng.permutation(128_000).astype(np.int32)
+    def new_batches():
+        # every round draws fresh batches from the same shifted distribution
+        return [torch.from_numpy(np.ascontiguousarray(
+            perm[inputs.zipf_tokens(rng, 128_000, 1.1, (B, T))])).to(dev) for _ in range(steps_per_round)]
+    ws = torch.empty(max(eg.forward_workspace(B, T, L) for L in Ls), dtype=torch.uint8, device=dev)
+    counts = [torch.zeros(L.s.tables.total_rows, dtype=torch.int32, device=dev) for L in Ls]
+    for L, c in zip(Ls, counts):
+        L.set_access_counts(c)
+
+    def hit_rate(before):
+        hits = acc = 0
+        for L, c, c0 in zip(Ls, counts, before):
+            delta = (c.to(torch.int64) - c0.to(torch.int64))
+            acc += int(delta.sum().item())
+            hits += int(delta[L.cache_slot >= 0].sum().item())
+        return hits / max(acc, 1)
+
+    out = []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for r in range(rounds + 1):
+        batches = new_batches()
+        before = [c.clone() for c in counts]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for b in batches:
+            for L in Ls:
+                eg.forward(b, H, L, ws=ws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        step_ms = ev[0].elapsed_time(ev[1]) / steps_per_round
+        hr = hit_rate(before)
+        del before
+        upd_ms = None
+        if r < rounds:
+            ev[2].record()
+            for L, c in zip(Ls, counts):
+                eg.cache_update(L, c, decay_shift=1)
+            ev[3].record()
+            torch.cuda.synchronize()
+            upd_ms = ev[2].elapsed_time(ev[3]) / len(Ls)
+        out.append({"round": r, "hit_rate": round(hr, 4), "ms_per_step": round(step_ms, 4),
+                    "update_ms_per_layer": None if upd_ms is None else round(upd_ms, 3)})
+    for L in Ls:
+        L.set_access_counts(None)
+    return {"rounds": out, "steps_per_round": steps_per_round,
+            "how": "round 0 uses the static cache from the warm-up stream; every later round follows an update "
+                   "from the counts so far (aged by one bit at each update); eager steps; hit rate = cached "
+                   "accesses / all accesses of the round"}
+
+
 def inputs_zipf_like(tokens, rng):
     """A second token batch of the same shape and distribution: the first
     batch's ids permuted within each sequence."""
@@ -581,6 +650,8 @@ def main():
             out[k] = v
     if args.overlap and args.config in (1, 2):
         out["retrieval_overlap"] = overlap_report(torch, eg, w, lays[0], args.steps, args.warmup)
+    if args.realtime_lfu and args.config == 4:
+        out["realtime_lfu"] = realtime_lfu_report(torch, eg, inputs, w, extra["_pipe"])
     if args.overlap and "_pipe" in extra:
         out["retrieval_pipelined"] = pipelined_report(torch, eg, w, extra["_pipe"], args.steps)
     print(json.dumps(out), flush=True)

@@ -58,13 +58,38 @@ count_kernel(const int32_t* __restrict__ tokens, int64_t B, int64_t T, const int
   atomicAdd(counts + ta.row_offset[j] + z, 1u);
 }
 
+// Count histogram.  Most rows have tiny counts (almost all zero in a large
+// table), so one global bin would take millions of contended atomics: each
+// workgroup keeps the bins below kLocalBins in LDS, zeros are counted with a
+// wavefront ballot (one LDS add per wavefront), and the workgroup adds its
+// non-empty bins to the global histogram at the end.
+constexpr int kLocalBins = 4096;
+
 __global__ void __launch_bounds__(256)
 histogram_kernel(const uint32_t* __restrict__ counts, int64_t n, uint32_t* __restrict__ bins) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const uint32_t c = counts[i];
-    atomicAdd(bins + (c < kBins - 1 ? c : kBins - 1), 1u);
+  __shared__ uint32_t local[kLocalBins];
+  for (int i = threadIdx.x; i < kLocalBins; i += blockDim.x) local[i] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t start = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  // every lane of a wavefront runs the same number of iterations (the bound
+  // is rounded up to whole strides), so the ballot sees all 64 lanes
+  const int64_t wave_start = start - lane;
+  for (int64_t base = wave_start; base < n; base += stride) {
+    const int64_t i = base + lane;
+    const bool valid = i < n;
+    const uint32_t c = valid ? counts[i] : 0u;
+    const uint64_t zeros = __ballot(valid && c == 0);
+    if (lane == 0 && zeros != 0) atomicAdd(&local[0], static_cast<uint32_t>(__popcll(zeros)));
+    if (valid && c != 0) {
+      if (c < kLocalBins) atomicAdd(&local[c], 1u);
+      else atomicAdd(bins + (c < kBins - 1 ? c : kBins - 1), 1u);
+    }
   }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kLocalBins; i += blockDim.x)
+    if (local[i] != 0) atomicAdd(bins + i, local[i]);
 }
 
 // params[0] = c*, params[1] = rows of count c* that are admitted.
@@ -300,7 +325,9 @@ void scan(int mode, const FlagSrc& f, int64_t n, int32_t* out, int32_t* sums, hi
 void rank_threshold(const uint32_t* counts, int64_t total_rows, int64_t cache_n, uint32_t* bins, int64_t* params,
                     hipStream_t s) {
   launch_k(fill_u32, dim3(grid_for(kBins, 256)), dim3(256), 0, s, bins, static_cast<int64_t>(kBins), 0u);
-  launch_k(histogram_kernel, dim3(grid_for(total_rows, 256)), dim3(256), 0, s, counts, total_rows, bins);
+  const int64_t hist_blocks = (total_rows + 256 * 64 - 1) / (256 * 64);   // ~64 items per thread
+  launch_k(histogram_kernel, dim3(static_cast<unsigned>(hist_blocks < 2048 ? hist_blocks : 2048)), dim3(256), 0, s,
+           counts, total_rows, bins);
   launch_k(threshold_kernel, dim3(1), dim3(1024), 0, s, bins, cache_n, params);
 }
 
