@@ -331,8 +331,91 @@ def gate_conv(H: np.ndarray, kv: np.ndarray, conv_w: np.ndarray, dilation: int, 
     return {"alpha": alpha, "vt": vt, "u": u, "c": c, "Y": Y, "H_out": H + Y}       # Step 8
 
 
+# --------------------------------------------------------------------------
+# Step 5 in MXFP8: the fused W_V / W_K product as one FP8 dense GEMM
+# --------------------------------------------------------------------------
+# The Guide (variant on a multi-branch backbone) suggests fusing W_V with the
+# M keys into one FP8 dense GEMM.  The FP8 format is fixed here as OCP MXFP8:
+# E4M3 elements (bias 7, no infinities, largest finite 448, subnormals down
+# to 2^-9) in blocks of 32 consecutive elements along the contraction axis,
+# each block with a power-of-two scale stored as an 8-bit biased exponent
+# (byte = exponent + 127).  The scale is the smallest power of two that keeps
+# the block's largest magnitude within +-448 (so nothing saturates; OCP's
+# floor(log2 amax) - 8 rule would clip up to 12.5 % off the largest element):
+# with amax = m 2^E, 0.5 <= m < 1, the exponent is E - 9, plus one when
+# m > 0.875.  Elements are v / scale (exact) rounded to nearest-even E4M3.  An
+# all-zero block gets scale byte 0 and zero elements.
+
+E4M3_MAX = 448.0
+
+
+def round_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Nearest-even rounding of float64 values to E4M3, saturated to +-448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    # exponent of the value's binade, never below the smallest normal's (-6)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    quantum = np.ldexp(1.0, (e - 3).astype(np.int64))          # 3 mantissa bits
+    r = np.rint(a / quantum) * quantum                          # ties to even
+    r = np.minimum(r, E4M3_MAX)
+    return np.copysign(r, x)
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Bit patterns of values that are exactly representable in E4M3."""
+    v = np.asarray(v, dtype=np.float64)
+    sign = (np.signbit(v)).astype(np.uint8) << 7
+    a = np.abs(v)
+    out = np.zeros(v.shape, dtype=np.uint8)
+    normal = a >= 2.0 ** -6
+    e = np.floor(np.log2(np.where(normal, a, 1.0))).astype(np.int64)
+    man = np.where(normal, np.rint((a / np.ldexp(1.0, e) - 1.0) * 8), np.rint(a / 2.0 ** -9)).astype(np.int64)
+    out = np.where(normal, ((e + 7) << 3) | man, man).astype(np.uint8)
+    return (out | sign).astype(np.uint8)
+
+
+def e4m3_decode(q: np.ndarray) -> np.ndarray:
+    q = np.asarray(q, dtype=np.uint8).astype(np.int64)
+    s = np.where(q & 0x80, -1.0, 1.0)
+    e = (q >> 3) & 15
+    m = q & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    return s * mag
+
+
+def quantize_mxfp8(x: np.ndarray):
+    """MXFP8 of x [..., K] with K a multiple of 32: returns (elements uint8
+    [..., K], scale bytes uint8 [..., K/32])."""
+    x = np.asarray(x, dtype=np.float64)
+    blocks = x.reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.max(np.abs(blocks), axis=-1)
+    m, E = np.frexp(np.where(amax > 0, amax, 1.0))
+    exp = np.clip(E - 9 + (m > 0.875), -127, 127)
+    scale = np.where(amax > 0, np.ldexp(1.0, exp.astype(np.int64)), 1.0)
+    q = round_to_e4m3(blocks / scale[..., None])
+    q = np.where(amax[..., None] > 0, q, 0.0)
+    sbyte = np.where(amax > 0, exp + 127, 0).astype(np.uint8)
+    return e4m3_encode(q).reshape(x.shape), sbyte
+
+
+def dequantize_mxfp8(q: np.ndarray, sbyte: np.ndarray) -> np.ndarray:
+    v = e4m3_decode(q)
+    blocks = v.reshape(v.shape[:-1] + (v.shape[-1] // 32, 32))
+    scale = np.ldexp(1.0, sbyte.astype(np.int64) - 127)
+    return (blocks * scale[..., None]).reshape(v.shape)
+
+
+def project_kv_mxfp8(e: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Step 5 with both operands in MXFP8 (blocks along d_mem), products and
+    sums exact in float64."""
+    eq, es = quantize_mxfp8(e)
+    wq, ws = quantize_mxfp8(w)
+    return dequantize_mxfp8(eq, es) @ dequantize_mxfp8(wq, ws).T
+
+
 def forward(tokens: np.ndarray, H: np.ndarray, layer, h_dtype: str, state=None,
-            e_dtype=None) -> dict:
+            e_dtype=None, gemm: str = "exact") -> dict:
     """One Engram layer over tokens [B, T] and hidden states H [B, T, M, d].
 
     `layer` is a `LayerInputs`-like object (hash, tables, w, conv_w, eps,
@@ -340,7 +423,7 @@ def forward(tokens: np.ndarray, H: np.ndarray, layer, h_dtype: str, state=None,
     the gathered rows ("f32" or "bf16").  With `state` (see new_state) the
     chunk continues earlier tokens and a new state is returned.
     Returns float64 arrays: z, e, kv, alpha [B,T,M], vt, u, c, Y [B,T,M,d],
-    H_out, and `state`.
+    H_out, and `state`.  gemm="mxfp8" takes Step 5 in MXFP8 (project_kv_mxfp8).
     """
     hp, tab = layer.hash, layer.tables
     B, T = tokens.shape
@@ -350,7 +433,8 @@ def forward(tokens: np.ndarray, H: np.ndarray, layer, h_dtype: str, state=None,
 
     z = hash_indices(tokens, hp.proj, hp.mult, hp.prime, hp.max_n, hp.heads, hist)   # Steps 1-3
     e = gather(z, tab.rows, tab.dtype, tab.row_offset, tab.dim, tab.scale, e_dtype)  # Steps 3-4
-    kv = project_kv(e, storage_to_f64(layer.w, h_dtype))                             # Step 5
+    w64 = storage_to_f64(layer.w, h_dtype)
+    kv = project_kv_mxfp8(e, w64) if gemm == "mxfp8" else project_kv(e, w64)       # Step 5
     out = gate_conv(storage_to_f64(H, h_dtype), kv, layer.conv_w, layer.dilation, layer.eps,
                     None if state is None else state["u"])                           # Steps 6-8
     out.update({"z": z, "e": e, "kv": kv})
