@@ -342,6 +342,15 @@ engram_status check_layer(const engram_layer* L, engram::HashArgs* ha, engram::T
     return fail(ENGRAM_EUNSUPPORTED, "layer: bf16 projections need n_tables*dim (%lld) to be a multiple of 64",
                 static_cast<long long>(d_mem));
   if (!aligned(L->w, 16)) return fail(ENGRAM_EINVAL, "layer: w must be 16-byte aligned");
+  if ((L->w_mx == nullptr) != (L->w_mx_scale == nullptr))
+    return fail(ENGRAM_EINVAL, "layer: w_mx and w_mx_scale must both be set or both be NULL");
+  if (L->w_mx != nullptr) {
+    if (L->gc.hdtype != ENGRAM_BF16 || L->gc.d % 128 != 0 || L->tables.dim % 32 != 0 || d_mem % 128 != 0)
+      return fail(ENGRAM_EUNSUPPORTED,
+                  "layer: MXFP8 needs bf16 H, d a multiple of 128, dim a multiple of 32 and d_mem of 128");
+    if (!aligned(L->w_mx, 16) || !aligned(L->w_mx_scale, 4))
+      return fail(ENGRAM_EINVAL, "layer: w_mx must be 16-byte and w_mx_scale 4-byte aligned");
+  }
   return ENGRAM_OK;
 }
 
@@ -450,8 +459,9 @@ engram_status run_retrieve(const int32_t* tokens, int64_t B, int64_t T, const en
                            const engram::HashArgs& ha, const engram::TableArgs& ta, int hdtype,
                            const engram_decode_state* st, void* e, hipStream_t stream) {
   const int32_t* hist = st != nullptr ? st->ids : nullptr;
+  const int out = L->w_mx != nullptr ? engram::kGatherOutMXFP8 : hdtype;
   prof_mark(stream, "gather_kernel<hashed>");
-  return hip_status(engram::launch_hash_gather(tokens, B, T, hist, L->hash.proj, ha, ta, hdtype, e, stream),
+  return hip_status(engram::launch_hash_gather(tokens, B, T, hist, L->hash.proj, ha, ta, out, e, stream),
                     "hash+gather launch");
 }
 
@@ -467,8 +477,13 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
   if (use_fused(L)) {
     // Step 5 with the gate's sums folded into the product's epilogue; only v is stored
     engram::ProjGateArgs pa{};
+    const bool mx = L->w_mx != nullptr;
     pa.e = static_cast<const uint16_t*>(e);
-    pa.w = static_cast<const uint16_t*>(L->w);
+    pa.w = static_cast<const uint16_t*>(mx ? static_cast<const void*>(L->w_mx) : L->w);
+    if (mx) {
+      pa.e_scale = static_cast<const uint8_t*>(e) + n_tok * d_mem;   // after the codes
+      pa.w_scale = L->w_mx_scale;
+    }
     pa.H = static_cast<const uint16_t*>(H);
     pa.v = f.kv;
     pa.stats = f.stats;
@@ -480,7 +495,7 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
     prof_mark(stream, "proj_gate_kernel");
     r = hip_status(engram::launch_proj_gate(pa, stream), "projection launch");
     if (r != ENGRAM_OK) return r;
-    const int q = d / engram::proj_gate_tile_f(n_tok, static_cast<int>(n_out), d);
+    const int q = d / engram::proj_gate_tile_f(n_tok, static_cast<int>(n_out), d, mx);
     return run_conv_commit(H, f.kv, d, ENGRAM_F32, f.stats, q, q, B, T, g, st, tokens, L->hash.proj,
                            L->hash.max_n, alpha_out, f.gamma, y_out, stream);
   }
@@ -652,6 +667,19 @@ ENGRAM_API engram_status engram_cache_update(const engram_tables* tab, int64_t c
                                                 tab->dtype == ENGRAM_I8 ? cache_scale : nullptr, counts, decay_shift,
                                                 ws, stream),
                     "cache update launch");
+}
+
+ENGRAM_API engram_status engram_quantize_mxfp8(const void* x, engram_dtype dtype, int64_t rows, int64_t cols,
+                                               uint8_t* q, uint8_t* scale, hipStream_t stream) {
+  if (dtype != ENGRAM_F32 && dtype != ENGRAM_BF16) return fail(ENGRAM_EUNSUPPORTED, "quantize_mxfp8: dtype F32 or BF16");
+  if (rows < 0 || cols < 0 || cols % 32 != 0)
+    return fail(ENGRAM_EINVAL, "quantize_mxfp8: rows >= 0 and cols a non-negative multiple of 32");
+  if (rows * cols == 0) return ENGRAM_OK;
+  if (x == nullptr || q == nullptr || scale == nullptr)
+    return fail(ENGRAM_EINVAL, "quantize_mxfp8: x, q and scale must be non-NULL");
+  if (!aligned(x, dtype == ENGRAM_F32 ? 32 : 16) || !aligned(q, 8))
+    return fail(ENGRAM_EINVAL, "quantize_mxfp8: x must be 16-byte (BF16) or 32-byte (F32) aligned, q 8-byte");
+  return hip_status(engram::launch_mx_quantize(x, dtype, rows, cols, q, scale, stream), "quantize launch");
 }
 
 ENGRAM_API engram_status engram_profile_enable(int32_t on) {

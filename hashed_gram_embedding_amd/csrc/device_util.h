@@ -33,6 +33,55 @@ __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * x));
 }
 
+// ---- MXFP8: E4M3 elements (bias 7, largest finite 448, subnormals of 2^-9),
+// one power-of-two scale per 32 consecutive values along the contraction
+// axis, stored as a biased exponent byte.  The scale is the smallest power of
+// two that keeps the block's largest magnitude within 448: with
+// amax = m 2^E (0.5 <= m < 1) the exponent is E - 9, plus one when m > 0.875.
+
+// Nearest-even E4M3 code of x, |x| <= 448.  Below 2^-6 the quantum is 2^-9
+// (the code is the multiple of 2^-9, and 8 is also the smallest normal's
+// code); above, the float's top 3 mantissa bits are rounded in place.
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const uint32_t ab = b & 0x7fffffffu;
+  const float a = __uint_as_float(ab);
+  uint32_t code;
+  if (a < 0.015625f) code = static_cast<uint32_t>(rintf(a * 512.0f));
+  else code = ((ab + 0x7ffffu + ((ab >> 20) & 1u)) >> 20) - (120u << 3);
+  return code | ((b >> 24) & 0x80u);
+}
+
+// Scale exponent of a block whose largest magnitude is amax (> 0), clamped
+// to the byte's range.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  int E;
+  const float m = frexpf(amax, &E);
+  int e = E - 9 + (m > 0.875f ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Quantise 8 values held by each lane of an aligned group of 4 lanes (one
+// 32-value block): returns the 8 codes packed little-endian and sets *sbyte
+// to the block's scale byte (0 for an all-zero block).
+__device__ __forceinline__ uint2 mx_quantize8(const float* f, uint32_t* sbyte) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  if (amax == 0.f) {
+    *sbyte = 0;
+    return make_uint2(0u, 0u);
+  }
+  const int e = mx_scale_exp(amax);
+  *sbyte = static_cast<uint32_t>(e + 127);
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i >> 2] |= e4m3_rne(ldexpf(f[i], -e)) << (8 * (i & 3));
+  return make_uint2(w[0], w[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);

@@ -62,6 +62,13 @@ struct StateArgs {
 hipError_t launch_hash(const int32_t* tokens, int64_t B, int64_t T, const int32_t* hist,
                        const int32_t* proj, const HashArgs& a, int32_t* z, hipStream_t s);
 
+hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scale,
+                              hipStream_t s);
+
+// Gather output in MXFP8: [n_tok][n_tables*dim] E4M3 codes followed by
+// [n_tok][n_tables*dim/32] scale bytes (dim a multiple of 32).
+constexpr int kGatherOutMXFP8 = 3;
+
 hipError_t launch_gather(const int32_t* z, int64_t n_tok, const TableArgs& ta, int out_dtype,
                          void* e, hipStream_t s);
 
@@ -87,9 +94,13 @@ struct ProjGateArgs {
   int M;
   int tiles_f;  // set by the launcher
   int tiles_t;  // set by the launcher
+  // MXFP8 product when non-NULL: e and w hold E4M3 codes ([n_tok][K], [N][K]
+  // bytes) and these their block scale bytes ([n_tok][K/32], [N][K/32])
+  const uint8_t* e_scale;
+  const uint8_t* w_scale;
 };
 constexpr int kProjGateTileF = 64;   // narrowest feature tile (bounds the statistics buffer)
-int proj_gate_tile_f(int64_t n_tok, int N, int d);   // feature columns per gate-statistics tile
+int proj_gate_tile_f(int64_t n_tok, int N, int d, bool mx);   // feature columns per gate-statistics tile
 hipError_t launch_proj_gate(const ProjGateArgs& a, hipStream_t s);
 
 // Whole-row gate statistics from given projections: stats [n_tok][1+M].

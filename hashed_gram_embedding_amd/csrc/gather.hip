@@ -23,6 +23,8 @@
 namespace engram {
 namespace {
 
+constexpr int kOutMXFP8 = kGatherOutMXFP8;
+
 template <int IN>
 __device__ __forceinline__ void load8(const void* base, const float* scale, int64_t row, int dim,
                                       int col, float* f, uint4* raw_bf16) {
@@ -83,7 +85,16 @@ gather_kernel(const int32_t* __restrict__ z, int64_t n_tok, TableArgs ta, void* 
   uint4 raw;
   load8<IN>(src, scale, row, ta.dim, c * 8, f, &raw);
   const int64_t out = tj * ta.dim + c * 8;
-  if constexpr (OUT == ENGRAM_BF16) {
+  if constexpr (OUT == kOutMXFP8) {
+    // MXFP8 e: 8 codes per thread, the block scale from the 4 threads of the
+    // block (rows are whole blocks: dim is a multiple of 32, so the groups
+    // of 4 lanes never straddle rows or the grid's end)
+    uint32_t sb;
+    const uint2 q = mx_quantize8(f, &sb);
+    uint8_t* eq = static_cast<uint8_t*>(e);
+    *reinterpret_cast<uint2*>(eq + out) = q;
+    if ((c & 3) == 0) eq[n_tok * nt * ta.dim + out / 32] = static_cast<uint8_t>(sb);
+  } else if constexpr (OUT == ENGRAM_BF16) {
     uint4 q;
     if constexpr (IN == ENGRAM_BF16) q = raw; else q = pack8(f);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(e) + out) = q;
@@ -101,7 +112,9 @@ hipError_t launch_in(const int32_t* z, int64_t n_tok, const TableArgs& ta, int o
   if (total == 0) return hipSuccess;
   const int threads = 256;
   const dim3 grid(static_cast<unsigned>((total + threads - 1) / threads));
-  if (out == ENGRAM_BF16)
+  if (out == kOutMXFP8)
+    launch_k((gather_kernel<IN, kOutMXFP8, HASHED>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
+  else if (out == ENGRAM_BF16)
     launch_k((gather_kernel<IN, ENGRAM_BF16, HASHED>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
   else
     launch_k((gather_kernel<IN, ENGRAM_F32, HASHED>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);

@@ -37,6 +37,13 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // 16-byte staging type: a native vector (HIP's uint4 struct copies through memory)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// Two 16-byte chunks as the 32-byte MXFP8 operand of one lane.
+__device__ __forceinline__ i32x8_t join16(u32x4_t lo, u32x4_t hi) {
+  return i32x8_t{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                 static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+}
 
 constexpr int TK = 256;        // tokens per workgroup
 constexpr int BK = 64;         // K slice
@@ -47,11 +54,15 @@ constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
-template <int TF, int PD>
+template <int TF, int PD, bool MX>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 proj_gate_kernel(ProjGateArgs a) {
-  constexpr int kWChunks = TF * BK / 8;    // 16-byte chunks of a W slice
-  constexpr int kEChunks = TK * BK / 8;    // 16-byte chunks of an e slice
+  // a K slice is 128 bytes of every row: 64 bf16 values, or 128 MXFP8 codes
+  // (four 32-value scale blocks)
+  constexpr int ESZ = MX ? 1 : 2;          // bytes per element
+  constexpr int BKE = 128 / ESZ;           // elements per K slice
+  constexpr int kWChunks = TF * 8;         // 16-byte chunks of a W slice
+  constexpr int kEChunks = TK * 8;         // 16-byte chunks of an e slice
   constexpr int NW = kWChunks / kThreads;  // W chunks staged per thread
   constexpr int NE = kEChunks / kThreads;  // e chunks staged per thread
   constexpr int I = TF / WF / 32;          // 32-row feature blocks per wavefront
@@ -59,6 +70,8 @@ proj_gate_kernel(ProjGateArgs a) {
   extern __shared__ u32x4_t lds[];
   u32x4_t* Ws = lds;                  // [2][kWChunks]
   u32x4_t* Es = lds + 2 * kWChunks;   // [2][kEChunks]
+  // MXFP8: the slice's scale bytes, one 32-bit word (4 blocks) per W row, then per e row
+  uint32_t* Ss = reinterpret_cast<uint32_t*>(lds + 2 * (kWChunks + kEChunks));   // [2][TF + TK]
 
   const int n_tiles = a.tiles_f * a.tiles_t;
   const int L = blockIdx.x;
@@ -74,7 +87,7 @@ proj_gate_kernel(ProjGateArgs a) {
   const int wf = wave % WF;
   const int wt = wave / WF;
   const int K = a.K;
-  const int ksteps = K / BK;   // a multiple of PD (checked by the launcher)
+  const int ksteps = K / BKE;  // a multiple of PD (checked by the launcher)
 
   f32x16_t acc[I][J];
 #pragma unroll
@@ -87,18 +100,30 @@ proj_gate_kernel(ProjGateArgs a) {
   // global -> register staging, PD slices in flight.  Token rows past the end
   // load the last row instead; their results are never stored.
   u32x4_t rw[PD][NW], re[PD][NE];
-  const uint16_t* wbase = a.w + static_cast<int64_t>(f0) * K;
-#define ENGRAM_LOAD_SLICE(b, k0)                                                                   \
+  uint32_t rs[PD];
+  const char* wbase = reinterpret_cast<const char*>(a.w) + static_cast<int64_t>(f0) * K * ESZ;
+  const char* ebase = reinterpret_cast<const char*>(a.e);
+  // MXFP8 scale word of this thread's row: W rows for tid < TF, then e rows
+  const uint8_t* sbase = nullptr;
+  if constexpr (MX) {
+    const int sr = tid < TF ? tid : (tid < TF + TK ? tid - TF : 0);
+    sbase = tid < TF ? a.w_scale + static_cast<int64_t>(f0 + sr) * (K / 32)
+                     : a.e_scale + min(t0 + sr, a.n_tok - 1) * (K / 32);
+  }
+#define ENGRAM_LOAD_SLICE(b, kt)                                                                   \
   {                                                                                                \
+    const int64_t kb = static_cast<int64_t>(kt) * 128;   /* byte offset of the slice in a row */  \
     _Pragma("unroll") for (int i = 0; i < NW; ++i) {                                               \
       const int c = tid + i * kThreads;                                                            \
-      rw[b][i] = *reinterpret_cast<const u32x4_t*>(wbase + (c >> 3) * K + (k0) + (c & 7) * 8);     \
+      rw[b][i] = *reinterpret_cast<const u32x4_t*>(wbase + static_cast<int64_t>(c >> 3) * K * ESZ + \
+                                                   kb + (c & 7) * 16);                             \
     }                                                                                              \
     _Pragma("unroll") for (int i = 0; i < NE; ++i) {                                               \
       const int c = tid + i * kThreads;                                                            \
       const int64_t tok = min(t0 + (c >> 3), a.n_tok - 1);                                         \
-      re[b][i] = *reinterpret_cast<const u32x4_t*>(a.e + tok * K + (k0) + (c & 7) * 8);            \
+      re[b][i] = *reinterpret_cast<const u32x4_t*>(ebase + tok * K * ESZ + kb + (c & 7) * 16);     \
     }                                                                                              \
+    if constexpr (MX) rs[b] = *reinterpret_cast<const uint32_t*>(sbase + (kt) * 4);                \
   }
 #define ENGRAM_STORE_SLICE(b, buf)                                                                 \
   {                                                                                                \
@@ -110,31 +135,62 @@ proj_gate_kernel(ProjGateArgs a) {
       const int c = tid + i * kThreads;                                                            \
       Es[(buf) * kEChunks + swz(c >> 3, c & 7)] = re[b][i];                                        \
     }                                                                                              \
+    if constexpr (MX) {                                                                            \
+      if (tid < TF + TK) Ss[(buf) * (TF + TK) + tid] = rs[b];                                      \
+    }                                                                                              \
   }
+  // bf16: K16 steps, lane half h holds K elements 8h..8h+7 (one chunk).
+  // MXFP8: K64 steps; lane r (< 32) holds bytes 0-15 and 32-47 of its row's
+  // 64-byte run and the scale of its first 32-value block, lane r + 32 bytes
+  // 16-31 and 48-63 and the second block's scale (the layout of
+  // v_mfma_scale_f32_32x32x64_f8f6f4, checked by a probe against exact sums).
 #define ENGRAM_COMPUTE(buf)                                                                        \
   {                                                                                                \
     __builtin_amdgcn_iglp_opt(0);                                                                  \
-    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                                       \
-      const int kc = ks * 2 + (lane >> 5);                                                         \
-      bf16x8_t fa[I], fb[J];                                                                       \
-      _Pragma("unroll") for (int i = 0; i < I; ++i) fa[i] = __builtin_bit_cast(                    \
-          bf16x8_t, Ws[(buf) * kWChunks + swz(wf * (TF / WF) + i * 32 + (lane & 31), kc)]);        \
-      _Pragma("unroll") for (int j = 0; j < J; ++j) fb[j] = __builtin_bit_cast(                    \
-          bf16x8_t, Es[(buf) * kEChunks + swz(wt * (TK / WT) + j * 32 + (lane & 31), kc)]);        \
-      _Pragma("unroll") for (int i = 0; i < I; ++i) _Pragma("unroll") for (int j = 0; j < J; ++j)  \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);   \
+    if constexpr (!MX) {                                                                           \
+      _Pragma("unroll") for (int ks = 0; ks < BKE / 16; ++ks) {                                    \
+        const int kc = ks * 2 + (lane >> 5);                                                       \
+        bf16x8_t fa[I], fb[J];                                                                     \
+        _Pragma("unroll") for (int i = 0; i < I; ++i) fa[i] = __builtin_bit_cast(                  \
+            bf16x8_t, Ws[(buf) * kWChunks + swz(wf * (TF / WF) + i * 32 + (lane & 31), kc)]);      \
+        _Pragma("unroll") for (int j = 0; j < J; ++j) fb[j] = __builtin_bit_cast(                  \
+            bf16x8_t, Es[(buf) * kEChunks + swz(wt * (TK / WT) + j * 32 + (lane & 31), kc)]);      \
+        _Pragma("unroll") for (int i = 0; i < I; ++i) _Pragma("unroll") for (int j = 0; j < J; ++j) \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0); \
+      }                                                                                            \
+    } else {                                                                                       \
+      const int h = lane >> 5;                                                                     \
+      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                           \
+        i32x8_t fa[I], fb[J];                                                                      \
+        int sa[I], sb[J];                                                                          \
+        _Pragma("unroll") for (int i = 0; i < I; ++i) {                                            \
+          const int row = wf * (TF / WF) + i * 32 + (lane & 31);                                   \
+          fa[i] = join16(Ws[(buf) * kWChunks + swz(row, 4 * ks + h)],                              \
+                         Ws[(buf) * kWChunks + swz(row, 4 * ks + 2 + h)]);                         \
+          sa[i] = static_cast<int>((Ss[(buf) * (TF + TK) + row] >> (8 * (2 * ks + h))) & 0xffu);    \
+        }                                                                                          \
+        _Pragma("unroll") for (int j = 0; j < J; ++j) {                                            \
+          const int row = wt * (TK / WT) + j * 32 + (lane & 31);                                   \
+          fb[j] = join16(Es[(buf) * kEChunks + swz(row, 4 * ks + h)],                              \
+                         Es[(buf) * kEChunks + swz(row, 4 * ks + 2 + h)]);                         \
+          sb[j] = static_cast<int>((Ss[(buf) * (TF + TK) + TF + row] >> (8 * (2 * ks + h))) & 0xffu); \
+        }                                                                                          \
+        _Pragma("unroll") for (int i = 0; i < I; ++i) _Pragma("unroll") for (int j = 0; j < J; ++j) \
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, \
+                                                                        0, sa[i], 0, sb[j]);       \
+      }                                                                                            \
     }                                                                                              \
   }
 
 #pragma unroll
-  for (int b = 0; b < PD; ++b) ENGRAM_LOAD_SLICE(b, min(b, ksteps - 1) * BK);
+  for (int b = 0; b < PD; ++b) ENGRAM_LOAD_SLICE(b, min(b, ksteps - 1));
   ENGRAM_STORE_SLICE(0, 0);
   __syncthreads();
   for (int kt0 = 0; kt0 < ksteps; kt0 += PD) {
 #pragma unroll
     for (int u = 0; u < PD; ++u) {
       const int kt = kt0 + u;
-      ENGRAM_LOAD_SLICE(u, min(kt + PD, ksteps - 1) * BK);   // slice kt + PD (clamped)
+      ENGRAM_LOAD_SLICE(u, min(kt + PD, ksteps - 1));        // slice kt + PD (clamped)
       ENGRAM_COMPUTE(kt & 1);
       ENGRAM_STORE_SLICE((u + 1) % PD, (kt + 1) & 1);        // slice kt + 1 (unused after the last)
       __syncthreads();
@@ -348,11 +404,12 @@ proj_gate_small_kernel(ProjGateArgs a) {
   }
 }
 
-template <int TF, int PD>
+template <int TF, int PD, bool MX>
 hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   a.tiles_f = a.N / TF;
   a.tiles_t = static_cast<int>((a.n_tok + TK - 1) / TK);
-  const size_t lds = static_cast<size_t>(2 * (TF + TK) * BK / 8) * sizeof(u32x4_t);
+  const size_t lds = static_cast<size_t>(2 * (TF + TK) * 8) * sizeof(u32x4_t) +
+                     (MX ? static_cast<size_t>(2 * (TF + TK)) * sizeof(uint32_t) : 0);
   // more than 64 KiB of dynamic LDS exceeds the default per-workgroup limit;
   // raise it once per device and instantiation (gfx950 has 160 KiB per CU)
   static std::atomic<uint64_t> attr_set{0};
@@ -361,22 +418,24 @@ hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if ((attr_set.load() & bit) == 0) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_kernel<TF, PD>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_kernel<TF, PD, MX>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit);
   }
-  launch_k((proj_gate_kernel<TF, PD>), dim3(a.tiles_f * a.tiles_t), dim3(kThreads), lds, s, a);
+  launch_k((proj_gate_kernel<TF, PD, MX>), dim3(a.tiles_f * a.tiles_t), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 // Few tokens: the small kernel (64-column statistics tiles); otherwise the
-// large one with 256-column tiles when there are enough of them.
+// large one with 256-column tiles when there are enough of them.  The MXFP8
+// product always takes the large kernel with 128-column tiles.
 bool proj_gate_small(int64_t n_tok, int N) { return ((n_tok + TK - 1) / TK) * (N / 128) < 128; }
 
-int proj_gate_tile_f(int64_t n_tok, int N, int d) {
+int proj_gate_tile_f(int64_t n_tok, int N, int d, bool mx) {
+  if (mx) return 128;
   if (proj_gate_small(n_tok, N)) return kSmallTF;
   // 256-feature tiles halve the LDS traffic per matrix operation but need at
   // least two tiles per CU (512) to keep the chip busy
@@ -386,7 +445,15 @@ int proj_gate_tile_f(int64_t n_tok, int N, int d) {
 
 hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
   if (in.n_tok == 0) return hipSuccess;
-  if (in.K % BK != 0 || in.N % 128 != 0) return hipErrorInvalidValue;
+  if (in.N % 128 != 0) return hipErrorInvalidValue;
+  const bool mx = in.e_scale != nullptr;
+  if (mx) {
+    // 128-feature tiles, one slice in flight: the FP8 operands of two slices
+    // and the 256-feature tile's accumulators do not fit the register budget
+    if (in.K % 128 != 0 || in.w_scale == nullptr) return hipErrorInvalidValue;
+    return launch_tf<128, 1, true>(in, s);
+  }
+  if (in.K % BK != 0) return hipErrorInvalidValue;
   if (proj_gate_small(in.n_tok, in.N)) {
     ProjGateArgs a = in;
     a.tiles_f = a.N / kSmallTF;
@@ -396,9 +463,9 @@ hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
     return hipGetLastError();
   }
   const bool pd2 = (in.K / BK) % 2 == 0;
-  if (proj_gate_tile_f(in.n_tok, in.N, in.d) == 256)
-    return pd2 ? launch_tf<256, 2>(in, s) : launch_tf<256, 1>(in, s);
-  return pd2 ? launch_tf<128, 2>(in, s) : launch_tf<128, 1>(in, s);
+  if (proj_gate_tile_f(in.n_tok, in.N, in.d, false) == 256)
+    return pd2 ? launch_tf<256, 2, false>(in, s) : launch_tf<256, 1, false>(in, s);
+  return pd2 ? launch_tf<128, 2, false>(in, s) : launch_tf<128, 1, false>(in, s);
 }
 
 }  // namespace engram

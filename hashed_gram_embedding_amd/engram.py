@@ -49,7 +49,8 @@ class GateConvParams(ctypes.Structure):
 
 
 class LayerStruct(ctypes.Structure):
-    _fields_ = [("hash", HashParams), ("tables", Tables), ("w", ctypes.c_void_p), ("gc", GateConvParams)]
+    _fields_ = [("hash", HashParams), ("tables", Tables), ("w", ctypes.c_void_p), ("gc", GateConvParams),
+                ("w_mx", ctypes.c_void_p), ("w_mx_scale", ctypes.c_void_p)]
 
 
 class DecodeStateStruct(ctypes.Structure):
@@ -91,6 +92,7 @@ def lib():
         "engram_forward_retrieved_workspace": (sz, [i64, i64, ctypes.POINTER(LayerStruct)]),
         "engram_forward_retrieved": (i32, [vp, vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
                                            ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
+        "engram_quantize_mxfp8": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "engram_cache_update_workspace": (sz, [i64, i64]),
         "engram_cache_update": (i32, [ctypes.POINTER(Tables), i64, vp, vp, vp, vp, i32, vp, sz, vp]),
         "engram_cache_build_workspace": (sz, [i64]),
@@ -115,7 +117,7 @@ def exported_names():
             "engram_project_kv", "engram_gate_conv_workspace", "engram_gate_conv_forward",
             "engram_forward_workspace", "engram_forward", "engram_retrieve", "engram_forward_retrieved_workspace",
             "engram_forward_retrieved", "engram_cache_build_workspace", "engram_cache_build",
-            "engram_cache_update_workspace", "engram_cache_update",
+            "engram_cache_update_workspace", "engram_cache_update", "engram_quantize_mxfp8",
             "engram_profile_enable", "engram_profile_read",
             "engram_host_alloc", "engram_host_free"]
 
@@ -175,7 +177,7 @@ class Layer:
     be the device alias of pinned host memory from HostBuffer."""
 
     def __init__(self, li, hdtype: str, device="cuda", rows_device: Optional[torch.Tensor] = None,
-                 rows_ptr: Optional[int] = None, scale_ptr: Optional[int] = None):
+                 rows_ptr: Optional[int] = None, scale_ptr: Optional[int] = None, mxfp8: bool = False):
         hp, tab = li.hash, li.tables
         self.li = li
         self.hdtype = _DT[hdtype]
@@ -203,6 +205,14 @@ class Layer:
         self.s.w = self.w.data_ptr()
         self.s.gc = GateConvParams(li.d, li.branches, li.kernel_w, li.dilation, li.eps, self.hdtype,
                                    self.conv_w.data_ptr())
+        self.mxfp8 = mxfp8
+        if mxfp8:
+            n, k = self.w.shape
+            self.w_mx = torch.empty((n, k), dtype=torch.uint8, device=device)
+            self.w_mx_scale = torch.empty((n, k // 32), dtype=torch.uint8, device=device)
+            quantize_mxfp8(self.w, self.w_mx, self.w_mx_scale)
+            self.s.w_mx = self.w_mx.data_ptr()
+            self.s.w_mx_scale = self.w_mx_scale.data_ptr()
 
     def set_cache(self, slot: Optional[torch.Tensor], rows: Optional[torch.Tensor],
                   scale: Optional[torch.Tensor] = None):
@@ -384,9 +394,20 @@ def forward(tokens: torch.Tensor, H: torch.Tensor, layer: Layer, state: Optional
 
 
 def rows_buffer(B: int, T: int, layer: Layer, device=None) -> torch.Tensor:
-    """A buffer for the gathered rows e of B x T tokens (engram_retrieve)."""
+    """A buffer for the gathered rows e of B x T tokens (engram_retrieve); for
+    an MXFP8 layer the E4M3 codes followed by the block scale bytes."""
+    if layer.mxfp8:
+        n = B * T * layer.d_mem
+        return torch.empty(n + n // 32, dtype=torch.uint8, device=device)
     dt = torch.bfloat16 if layer.hdtype == BF16 else torch.float32
     return torch.empty((B * T, layer.d_mem), dtype=dt, device=device)
+
+
+def quantize_mxfp8(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream=None):
+    """MXFP8 of the rows of x (float32 or bfloat16 [rows, cols], cols % 32 == 0)."""
+    rows, cols = x.shape
+    dt = BF16 if x.dtype == torch.bfloat16 else F32
+    _check(lib().engram_quantize_mxfp8(_ptr(x), dt, rows, cols, _ptr(q), _ptr(scale), _stream(stream)))
 
 
 def retrieve(tokens: torch.Tensor, layer: Layer, e: torch.Tensor, state: Optional[DecodeState] = None,

@@ -135,6 +135,14 @@ typedef struct engram_layer {
                              W_K^(m) (Step 5; the multi-branch variant fuses the
                              shared W_V with the M keys into one product)          */
   engram_gate_conv_params gc;
+  /* optional MXFP8 Step 5 (the Guide's multi-branch variant suggests one FP8
+     dense GEMM for W_V and the M keys): W in MXFP8 from engram_quantize_mxfp8
+     of w.  When both are set (bf16 layers, tables with dim a multiple of 32,
+     n_tables*dim a multiple of 128), the gathered rows are quantised to
+     MXFP8 in the gather and the product runs on the FP8 matrix cores with
+     per-block scales; NULL = bf16 product.                                      */
+  const uint8_t* w_mx;        /* device [(1+M)*d][n_tables*dim] E4M3 codes        */
+  const uint8_t* w_mx_scale;  /* device [(1+M)*d][n_tables*dim/32] scale bytes    */
 } engram_layer;
 
 /* Decode / chunked-prefill state of S sequences (not on the pages; it is
@@ -212,7 +220,9 @@ engram_status engram_forward(const int32_t* tokens, void* H, int64_t B, int64_t 
  * the preceding layers compute (DRAM offload section).
  *
  * engram_retrieve: Steps 1-4 into e, device [B*T][n_tables*dim] of the
- * layer's hdtype, 16-byte aligned, owned by the caller.  st: NULL, or the
+ * layer's hdtype, 16-byte aligned, owned by the caller (for an MXFP8 layer:
+ * [B*T][n_tables*dim] E4M3 codes followed by [B*T][n_tables*dim/32] scale
+ * bytes).  st: NULL, or the
  * decode state whose ids are the history (read only; with a state, call it
  * after the previous forward on those sequences has committed).
  *
@@ -270,6 +280,15 @@ engram_status engram_cache_update(const engram_tables* tab, int64_t cache_n, int
                                   void* cache_rows, float* cache_scale, uint32_t* counts,
                                   int32_t decay_shift, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/* MXFP8 quantisation (used for W of the FP8 product): x [rows][cols] (F32 or
+ * BF16 on the device, cols a multiple of 32) -> q [rows][cols] E4M3 codes and
+ * scale [rows][cols/32] biased-exponent bytes.  Blocks are 32 consecutive
+ * values of a row; the scale is the smallest power of two keeping the block's
+ * largest magnitude within 448 (E4M3's largest finite value), elements are
+ * x / scale rounded to nearest-even E4M3, an all-zero block has scale byte 0. */
+engram_status engram_quantize_mxfp8(const void* x, engram_dtype dtype, int64_t rows, int64_t cols,
+                                    uint8_t* q, uint8_t* scale, hipStream_t stream);
 
 /* Stage timing, for benchmarks.  engram_profile_enable(1) makes later
  * engram_forward and engram_gate_conv_forward calls on the calling thread

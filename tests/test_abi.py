@@ -19,7 +19,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(eg.LIB_PATH), reason="libengr
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(engram_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(engram_[a-z0-9_]+)\s*\(", text)))
 
 
 def exported_functions():

@@ -1,0 +1,79 @@
+"""GPU: the MXFP8 Step 5 (the Guide's FP8 fused W_V / W_K product).  The
+quantiser and the gather's MXFP8 output are bit-exact against the oracle;
+the layer with the FP8 product matches the oracle's MXFP8 forward at the
+bf16 tolerances (only the float32 accumulation order differs)."""
+import numpy as np
+import pytest
+import torch
+
+from hashed_gram_embedding_amd import engram as eg
+from hashed_gram_embedding_amd import inputs
+from oracle import engram_oracle as orc
+
+from parity import check_bf16_layer, log, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_bit_exact(dtype):
+    log(f"mxfp8 quantize {dtype}")
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((70, 256)) * np.exp2(rng.integers(-30, 30, (70, 1)))).astype(np.float32)
+    x[3, :32] = 0.0                          # all-zero block
+    x[4, 32:64] = 0.0
+    x[4, 40] = 448.0                         # amax exactly 448: scale byte 127
+    x[5, :32] = rng.standard_normal(32).astype(np.float32) * 1e-3
+    x[5, 7] = np.float32(-449.0) * 2.0 ** -20
+    x[6, :] = 2.0 ** -140                    # float32 subnormals
+    if dtype == "bf16":
+        xt = torch.from_numpy(x).to(DEV).to(torch.bfloat16)
+        x64 = xt.float().cpu().numpy().astype(np.float64)
+    else:
+        xt = torch.from_numpy(x).to(DEV)
+        x64 = x.astype(np.float64)
+    q = torch.empty((70, 256), dtype=torch.uint8, device=DEV)
+    s = torch.empty((70, 8), dtype=torch.uint8, device=DEV)
+    eg.quantize_mxfp8(xt, q, s)
+    torch.cuda.synchronize()
+    rq, rs = orc.quantize_mxfp8(x64)
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
+def _mx_layer(config, **kw):
+    w = inputs.make_config(config, rows_per_table=997, **kw)
+    lay = w.layers[0]
+    return w, lay, eg.Layer(lay, "bf16", DEV, mxfp8=True)
+
+
+def test_retrieve_emits_mxfp8_rows_bit_exact():
+    log("mxfp8 gather")
+    w, lay, L = _mx_layer(1, B=2, T=90)
+    tok = torch.from_numpy(w.tokens).to(DEV)
+    e = eg.rows_buffer(2, 90, L, DEV)
+    eg.retrieve(tok, L, e)
+    torch.cuda.synchronize()
+    hp, tab = lay.hash, lay.tables
+    z = orc.hash_indices(w.tokens, hp.proj, hp.mult, hp.prime, hp.max_n, hp.heads)
+    ref = orc.gather(z, tab.rows, tab.dtype, tab.row_offset, tab.dim, tab.scale, out_dtype="bf16").reshape(180, -1)
+    rq, rs = orc.quantize_mxfp8(ref)
+    got = e.cpu().numpy()
+    n = ref.size
+    assert np.array_equal(got[:n].reshape(rq.shape), rq)
+    assert np.array_equal(got[n:n + n // 32].reshape(rs.shape), rs)
+
+
+@pytest.mark.parametrize("config,B,T", [(1, 2, 300), (1, 1, 5), (2, 2, 130), (1, 3, 700)])
+def test_forward_mxfp8_matches_oracle(config, B, T):
+    log(f"mxfp8 forward config={config} B={B} T={T}")
+    w, lay, L = _mx_layer(config, B=B, T=T)
+    tok = torch.from_numpy(w.tokens).to(DEV)
+    H = eg.to_device(w.H, "bf16", DEV)
+    alpha, y = eg.forward(tok, H, L, want_alpha=True, want_y=True)
+    torch.cuda.synchronize()
+    ref = orc.forward(w.tokens, w.H, lay, "bf16", gemm="mxfp8")
+    check_bf16_layer(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.bf16_to_f64(w.H),
+                     tag=f"mxfp8 c{config}")
