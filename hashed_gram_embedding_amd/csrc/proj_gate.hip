@@ -47,16 +47,15 @@ __device__ __forceinline__ i32x8_t join16(u32x4_t lo, u32x4_t hi) {
 
 constexpr int TK = 256;        // tokens per workgroup
 constexpr int BK = 64;         // K slice
-constexpr int WF = 2;          // wavefronts along features
-constexpr int WT = 4;          // wavefronts along tokens
-constexpr int kThreads = 64 * WF * WT;
+constexpr int WF = 2;          // wavefronts along features (wavefronts along tokens: WT, 4 or 2)
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
-template <int TF, int PD, bool MX>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int TF, int PD, bool MX, int WT>
+__global__ void __launch_bounds__(64 * WF * WT) __attribute__((amdgpu_waves_per_eu(WF * WT / 4, WF * WT / 4)))
 proj_gate_kernel(ProjGateArgs a) {
+  constexpr int kThreads = 64 * WF * WT;
   // a K slice is 128 bytes of every row: 64 bf16 values, or 128 MXFP8 codes
   // (four 32-value scale blocks)
   constexpr int ESZ = MX ? 1 : 2;          // bytes per element
@@ -100,15 +99,19 @@ proj_gate_kernel(ProjGateArgs a) {
   // global -> register staging, PD slices in flight.  Token rows past the end
   // load the last row instead; their results are never stored.
   u32x4_t rw[PD][NW], re[PD][NE];
-  uint32_t rs[PD];
+  constexpr int NS = MX ? (TF + TK + kThreads - 1) / kThreads : 1;   // scale words staged per thread
+  uint32_t rs[PD][NS];
   const char* wbase = reinterpret_cast<const char*>(a.w) + static_cast<int64_t>(f0) * K * ESZ;
   const char* ebase = reinterpret_cast<const char*>(a.e);
   // MXFP8 scale word of this thread's row: W rows for tid < TF, then e rows
-  const uint8_t* sbase = nullptr;
+  const uint8_t* sbase[NS];
   if constexpr (MX) {
-    const int sr = tid < TF ? tid : (tid < TF + TK ? tid - TF : 0);
-    sbase = tid < TF ? a.w_scale + static_cast<int64_t>(f0 + sr) * (K / 32)
-                     : a.e_scale + min(t0 + sr, a.n_tok - 1) * (K / 32);
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+      const int r = tid + q * kThreads;
+      sbase[q] = r < TF ? a.w_scale + static_cast<int64_t>(f0 + r) * (K / 32)
+                        : a.e_scale + min(t0 + (r < TF + TK ? r - TF : 0), a.n_tok - 1) * (K / 32);
+    }
   }
 #define ENGRAM_LOAD_SLICE(b, kt)                                                                   \
   {                                                                                                \
@@ -123,7 +126,10 @@ proj_gate_kernel(ProjGateArgs a) {
       const int64_t tok = min(t0 + (c >> 3), a.n_tok - 1);                                         \
       re[b][i] = *reinterpret_cast<const u32x4_t*>(ebase + tok * K * ESZ + kb + (c & 7) * 16);     \
     }                                                                                              \
-    if constexpr (MX) rs[b] = *reinterpret_cast<const uint32_t*>(sbase + (kt) * 4);                \
+    if constexpr (MX) {                                                                            \
+      _Pragma("unroll") for (int q = 0; q < NS; ++q)                                               \
+        rs[b][q] = *reinterpret_cast<const uint32_t*>(sbase[q] + (kt) * 4);                        \
+    }                                                                                              \
   }
 #define ENGRAM_STORE_SLICE(b, buf)                                                                 \
   {                                                                                                \
@@ -136,7 +142,8 @@ proj_gate_kernel(ProjGateArgs a) {
       Es[(buf) * kEChunks + swz(c >> 3, c & 7)] = re[b][i];                                        \
     }                                                                                              \
     if constexpr (MX) {                                                                            \
-      if (tid < TF + TK) Ss[(buf) * (TF + TK) + tid] = rs[b];                                      \
+      _Pragma("unroll") for (int q = 0; q < NS; ++q)                                               \
+        if (tid + q * kThreads < TF + TK) Ss[(buf) * (TF + TK) + tid + q * kThreads] = rs[b][q];   \
     }                                                                                              \
   }
   // bf16: K16 steps, lane half h holds K elements 8h..8h+7 (one chunk).
@@ -404,7 +411,7 @@ proj_gate_small_kernel(ProjGateArgs a) {
   }
 }
 
-template <int TF, int PD, bool MX>
+template <int TF, int PD, bool MX, int WT = 4>
 hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   a.tiles_f = a.N / TF;
   a.tiles_t = static_cast<int>((a.n_tok + TK - 1) / TK);
@@ -418,12 +425,12 @@ hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if ((attr_set.load() & bit) == 0) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_kernel<TF, PD, MX>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_kernel<TF, PD, MX, WT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit);
   }
-  launch_k((proj_gate_kernel<TF, PD, MX>), dim3(a.tiles_f * a.tiles_t), dim3(kThreads), lds, s, a);
+  launch_k((proj_gate_kernel<TF, PD, MX, WT>), dim3(a.tiles_f * a.tiles_t), dim3(64 * WF * WT), lds, s, a);
   return hipGetLastError();
 }
 
