@@ -325,3 +325,45 @@ def test_graph_replays_match_eager():
         eg.forward(tok, other, L, ws=ws)          # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(other.view(torch.int16), ref.view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# Other conv widths and dilations (the LDS-tiled conv kernel)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,kw,dil,M,d,B,T", [("f32", 3, 2, 1, 64, 2, 40), ("bf16", 2, 1, 2, 128, 2, 33),
+                                                  ("bf16", 8, 3, 1, 256, 1, 90), ("f32", 5, 6, 1, 64, 1, 70)])
+def test_forward_other_conv_shapes(dtype, kw, dil, M, d, B, T):
+    log(f"conv shape dtype={dtype} w={kw} dilation={dil} M={M} d={d}")
+    w = small(0 if dtype == "f32" else 1, B=B, T=T, d=d, branches=M)
+    lay = w.layers[0]
+    lay.kernel_w, lay.dilation = kw, dil
+    lay.conv_w = inputs.normal_f32(inputs.rng_for(98, kw, dil), M * d * kw, 0.1).reshape(M, d, kw)
+    L = eg.Layer(lay, dtype, DEV)
+    H = dev_H(w)
+    alpha, y = eg.forward(dev_tokens(w), H, L, want_alpha=True, want_y=True)
+    ref = orc.forward(w.tokens, w.H, lay, dtype)
+    chk = check_f32_layer if dtype == "f32" else check_bf16_layer
+    chk(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.storage_to_f64(w.H, dtype),
+        tag=f"w{kw} dil{dil}")
+
+
+def test_decode_other_conv_shape():
+    """w = 3, dilation 2 (span 4): prefill then token-by-token decode equals the oracle."""
+    log("decode conv w3 dil2")
+    w = small(1, B=3, T=12, rows_per_table=997)
+    lay = w.layers[0]
+    lay.kernel_w, lay.dilation = 3, 2
+    lay.conv_w = inputs.normal_f32(inputs.rng_for(99, 3, 2), lay.d * 3, 0.1).reshape(1, lay.d, 3)
+    L = eg.Layer(lay, "bf16", DEV)
+    st = eg.DecodeState(3, 3, 1, 4, lay.d, DEV)
+    ost = orc.new_state(3, 3, 1, 4, lay.d)
+    chunks = [(w.tokens[:, :7], w.H[:, :7])] + [(w.tokens[:, t:t + 1], w.H[:, t:t + 1]) for t in range(7, 12)]
+    for ci, (tok, Hn) in enumerate(chunks):
+        H = eg.to_device(Hn, "bf16", DEV)
+        alpha, y = eg.forward(torch.from_numpy(np.ascontiguousarray(tok)).to(DEV), H, L, state=st,
+                              want_alpha=True, want_y=True)
+        ref = orc.forward(tok, Hn, lay, "bf16", state=ost)
+        ost = ref["state"]
+        check_bf16_layer(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.bf16_to_f64(Hn),
+                         tag=f"chunk{ci}")
