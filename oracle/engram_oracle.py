@@ -40,6 +40,10 @@ Readings where the pages are silent (all listed in the design notes):
     (nearest-even) when the gathered rows are bfloat16.
   * Decode state: the last N-1 compressed ids, and the last (w-1)*N conv
     inputs u = RMSNorm(v~), oldest first.
+  * Engram-Nine hot tier (experiment 3 of the guide): the hot set is given
+    per order n as a list of n-grams; a hit replaces the K heads of order n,
+    i.e. K*d_head columns of e_t, by one hot row ("a single K x d table");
+    the fingerprint is read as exact, so membership is exact set membership.
 
 All floating-point arithmetic is float64 on values upcast exactly from their
 storage type; hashing is uint64 with wraparound.
@@ -238,6 +242,70 @@ def lfu_update(counts: np.ndarray, slot_prev: np.ndarray, cache_n: int, decay_sh
 
 
 # --------------------------------------------------------------------------
+# Engram-Nine: a collision-free hot tier over the most frequent n-grams
+# ("DeepSeek Engram series guide", experiment 3 "Engram-Nine", its Figure 1:
+# two-tier retrieval).  An n-gram g_{t,n} that belongs to the hot set of its
+# order n takes one hot row of width K*d_head in place of its K hashed rows;
+# every other n-gram keeps the K-head cold lookup.  The page builds the hot
+# set's index with a minimal perfect hash plus a fingerprint; what that
+# computes is exact set membership and a distinct row per hot n-gram, which
+# is what is written out here (a dictionary from n-gram to row).
+# --------------------------------------------------------------------------
+
+def hot_index(keys) -> dict:
+    """Row of every hot n-gram: keys is a sequence of n-tuples (oldest id
+    first); key r gets hot row r.  Duplicate keys are an error."""
+    index = {}
+    for r, key in enumerate(keys):
+        key = tuple(int(v) for v in key)
+        if key in index:
+            raise ValueError(f"duplicate hot key {key}")
+        index[key] = r
+    return index
+
+
+def hot_lookup(tokens: np.ndarray, proj: np.ndarray, max_n: int, hot_keys: dict, hist=None) -> np.ndarray:
+    """r[b, t, n-2] = hot row of g_{t,n} in the hot set of order n, or -1 when
+    g_{t,n} is not hot (or order n has no hot tier).
+
+    hot_keys maps an order n to its sequence of hot n-tuples (oldest first);
+    g_{t,n} is formed exactly as in Step 2, with history / pad for t < n-1."""
+    xc = compress(tokens, proj)
+    B, T = xc.shape
+    out = np.full((B, T, max_n - 1), -1, dtype=np.int64)
+    for n in range(2, max_n + 1):
+        keys = hot_keys.get(n)
+        if keys is None or len(keys) == 0:
+            continue
+        index = hot_index(keys)
+        for b in range(B):
+            for t in range(T):
+                out[b, t, n - 2] = index.get(suffix_ngram(xc, b, t, n, hist), -1)
+    return out
+
+
+def gather_two_tier(z: np.ndarray, hot_idx: np.ndarray, rows: np.ndarray, dtype: str, row_offset: np.ndarray,
+                    dim: int, heads: int, hot_rows: dict, scale=None, out_dtype: str = "bf16") -> np.ndarray:
+    """e_t with the hot tier: for order n the K*dim columns of its K heads,
+    columns (n-2)*K*dim .. (n-1)*K*dim - 1 of e_t, are the hot row
+    hot_rows[n][hot_idx[..., n-2]] when that index is >= 0 and the
+    concatenated cold rows E_{n,k}[z_{t,n,k}] otherwise.  Hot rows are stored
+    like the cold tables (f32 or bf16 bits)."""
+    if dtype == "i8":
+        raise ValueError("the hot tier holds f32 or bf16 rows")
+    e = gather(z, rows, dtype, row_offset, dim, scale, out_dtype)
+    width = heads * dim
+    for o in range(hot_idx.shape[-1]):
+        hit = hot_idx[..., o] >= 0
+        if not hit.any():
+            continue
+        n = o + 2
+        vals = table_rows_f64(hot_rows[n], dtype, hot_idx[..., o][hit], None, out_dtype)
+        e[..., o * width:(o + 1) * width][hit] = vals
+    return e
+
+
+# --------------------------------------------------------------------------
 # Step 5: key / value projections
 # --------------------------------------------------------------------------
 
@@ -415,7 +483,7 @@ def project_kv_mxfp8(e: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 
 def forward(tokens: np.ndarray, H: np.ndarray, layer, h_dtype: str, state=None,
-            e_dtype=None, gemm: str = "exact") -> dict:
+            e_dtype=None, gemm: str = "exact", hot=None) -> dict:
     """One Engram layer over tokens [B, T] and hidden states H [B, T, M, d].
 
     `layer` is a `LayerInputs`-like object (hash, tables, w, conv_w, eps,
@@ -424,6 +492,8 @@ def forward(tokens: np.ndarray, H: np.ndarray, layer, h_dtype: str, state=None,
     chunk continues earlier tokens and a new state is returned.
     Returns float64 arrays: z, e, kv, alpha [B,T,M], vt, u, c, Y [B,T,M,d],
     H_out, and `state`.  gemm="mxfp8" takes Step 5 in MXFP8 (project_kv_mxfp8).
+    hot = {"keys": {n: n-tuples}, "rows": {n: [n_hot, K*dim] rows}} adds the
+    Engram-Nine hot tier (gather_two_tier); the result then also holds hot_idx.
     """
     hp, tab = layer.hash, layer.tables
     B, T = tokens.shape
@@ -432,12 +502,19 @@ def forward(tokens: np.ndarray, H: np.ndarray, layer, h_dtype: str, state=None,
     e_dtype = e_dtype or h_dtype
 
     z = hash_indices(tokens, hp.proj, hp.mult, hp.prime, hp.max_n, hp.heads, hist)   # Steps 1-3
-    e = gather(z, tab.rows, tab.dtype, tab.row_offset, tab.dim, tab.scale, e_dtype)  # Steps 3-4
+    if hot is None:
+        e = gather(z, tab.rows, tab.dtype, tab.row_offset, tab.dim, tab.scale, e_dtype)  # Steps 3-4
+    else:
+        hot_idx = hot_lookup(tokens, hp.proj, hp.max_n, hot["keys"], hist)
+        e = gather_two_tier(z, hot_idx, tab.rows, tab.dtype, tab.row_offset, tab.dim, hp.heads, hot["rows"],
+                            tab.scale, e_dtype)
     w64 = storage_to_f64(layer.w, h_dtype)
     kv = project_kv_mxfp8(e, w64) if gemm == "mxfp8" else project_kv(e, w64)       # Step 5
     out = gate_conv(storage_to_f64(H, h_dtype), kv, layer.conv_w, layer.dilation, layer.eps,
                     None if state is None else state["u"])                           # Steps 6-8
     out.update({"z": z, "e": e, "kv": kv})
+    if hot is not None:
+        out["hot_idx"] = hot_idx
     if state is not None:
         xc = compress(tokens, hp.proj)
         ids = np.concatenate([state["ids"], xc], axis=1)[:, -(hp.max_n - 1):]
