@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--mxfp8", action="store_true",
                     help="configs 1-2: Step 5 as the MXFP8 product (E4M3 operands with 32-value block scales) "
                          "instead of bf16")
+    ap.add_argument("--hot-tier", type=int, default=0, metavar="N",
+                    help="configs 1-2: attach an Engram-Nine hot tier holding the N most frequent 2-grams and the "
+                         "N most frequent 3-grams of a seeded 2M-token Zipf(1.1) warm-up stream")
     ap.add_argument("--realtime-lfu", action="store_true",
                     help="host-table workload: drift the token distribution and measure the static cache against "
                          "the real-time LFU update (hit rate, step time, update time)")
@@ -62,10 +65,13 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_units(n_tok, lay, hdtype):
+def kernel_units(n_tok, lay, hdtype, hot_hit=None):
     """Algorithmic bytes (HBM-bound kernels) or flops (matrix-core kernels)
     per launch of each kernel of one layer forward over n_tok tokens, keyed by
-    the kernel names the library reports."""
+    the kernel names the library reports.  hot_hit: the fraction of hot
+    n-grams per order when the Engram-Nine tier is attached (a hit reads one
+    pilot, one 32-byte slot and its K*dim row; a miss reads its K cold rows
+    after the same pilot and slot)."""
     nt = lay.hash.n_tables
     dim = lay.tables.dim
     d, M = lay.d, lay.branches
@@ -76,7 +82,7 @@ def kernel_units(n_tok, lay, hdtype):
     fused = hdtype == "bf16" and d % 128 == 0
     n_stat = (1 + M) * d // 128 if fused else 1 + M
     flops = 2.0 * n_tok * (1 + M) * d * d_mem
-    return {
+    units = {
         # token ids in; rows in; e out
         "gather_kernel<hashed>": ("hbm", n_tok * (4 + nt * (row_bytes + dim * es))),
         "proj_gate_kernel": ("mfma", flops),
@@ -88,6 +94,13 @@ def kernel_units(n_tok, lay, hdtype):
         # v and gamma in; conv input of the newest position out; ids, pos
         "state_commit_kernel": ("hbm", n_tok * (d * 4 + M * (d * 4 + 4) + 16)),
     }
+    if hot_hit is not None:
+        K = lay.hash.heads
+        per_tok = 4 + nt * dim * es
+        for h in hot_hit:
+            per_tok += 36 + h * K * dim * es + (1 - h) * K * row_bytes
+        units["gather_kernel<hashed,hot>"] = ("hbm", n_tok * per_tok)
+    return units
 
 
 def setup(args, torch, eg, inputs):
@@ -102,7 +115,10 @@ def setup(args, torch, eg, inputs):
         tok = torch.from_numpy(w.tokens).to(dev)
         H = eg.to_device(w.H, w.dtype, dev)
         ws = torch.empty(eg.forward_workspace(w.B, w.T, L), dtype=torch.uint8, device=dev)
-        return [lambda: eg.forward(tok, H, L, ws=ws)], w.B * w.T, w, [lay], {"_pipe": ([L], tok, H)}
+        extra = {"_pipe": ([L], tok, H)}
+        if args.hot_tier > 0:
+            extra.update(hot_tier_setup(args, torch, eg, inputs, w, lay, L, tok))
+        return [lambda: eg.forward(tok, H, L, ws=ws)], w.B * w.T, w, [lay], extra
     if cfg == 3:
         w = inputs.make_config(3)
         S = w.B
@@ -139,11 +155,39 @@ def setup(args, torch, eg, inputs):
     calls = [(lambda L=L: eg.forward(tok, H, L, ws=ws)) for L in Ls]
     return calls, w.B * w.T, w, w.layers, {"cache_hit_rate": hits, "_keep": (Ls, bufs), "_pipe": (Ls, tok, H)}
 
+def hot_tier_setup(args, torch, eg, inputs, w, lay, L, tok):
+    """Engram-Nine hot tier for configs 1-2: per order the args.hot_tier most
+    frequent n-grams of a seeded warm-up stream (projected with the layer's
+    P on the host, as part of building the workload) with N(0, 0.02) rows."""
+    hp, tab = lay.hash, lay.tables
+    warm = inputs.hot_warmup_tokens(w.config, 0)
+    xc = hp.proj[warm]
+    keys, rows, dev_rows = {}, {}, {}
+    t0 = time.perf_counter()
+    for n in range(2, hp.max_n + 1):
+        keys[n] = inputs.frequent_ngrams(xc, n, args.hot_tier)
+        rows[n] = inputs.hot_rows(w.config, 0, n, keys[n].shape[0], hp.heads * tab.dim, tab.dtype)
+        dev_rows[n] = eg.to_device(rows[n], tab.dtype, "cuda")
+    t_sel = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    hot = eg.HotTier(keys, dev_rows, device="cuda")
+    t_build = time.perf_counter() - t0
+    L.set_hot(hot)
+    hit = (eg.hot_lookup(tok, L, hot) >= 0).float().mean(dim=(0, 1)).cpu().numpy()
+    info = {"n_hot_per_order": {str(n): int(k.shape[0]) for n, k in keys.items()},
+            "warm_tokens": int(warm.size),
+            "hit_rate_per_order": {str(n): round(float(hit[n - 2]), 4) for n in keys},
+            "hot_rows_MiB": round(sum(r.nbytes for r in rows.values()) / 2 ** 20, 1),
+            "host_select_s": round(t_sel, 2), "host_mphf_build_s": round(t_build, 2)}
+    return {"hot_tier": info, "_hot": (hot, keys, rows, [float(h) for h in hit])}
+
+
 # ---- HBM traffic from rocprofv3 counters ----
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 # library stage name -> (pattern of the rocprofv3 kernel name, sources whose text fixes the kernel)
 KERNEL_SOURCES = {
-    "gather_kernel<hashed>": (r"gather_kernel<[^>]*true>", ["gather.hip", "hash_device.h"]),
+    "gather_kernel<hashed>": (r"gather_kernel<[^>]*true, false>", ["gather.hip", "hash_device.h", "hot_device.h"]),
+    "gather_kernel<hashed,hot>": (r"gather_kernel<[^>]*true, true>", ["gather.hip", "hash_device.h", "hot_device.h"]),
     "proj_gate_kernel": (r"proj_gate_kernel<", ["proj_gate.hip"]),
     "conv_kernel": (r"conv_(strip_)?kernel<", ["gate_conv.hip"]),
 }
@@ -599,7 +643,7 @@ def main():
     eg.profile_enable(False)
     kernel_ms = {k: acc[k] / cnt[k] for k in acc}
 
-    units = kernel_units(n_tok, lays[0], w.dtype)
+    units = kernel_units(n_tok, lays[0], w.dtype, extra["_hot"][3] if "_hot" in extra else None)
     rates = {}
     for k, t in kernel_ms.items():
         if k in units:
@@ -616,14 +660,18 @@ def main():
         roof = {"bound": "hbm", "kernel": dominant, "achieved": round(rates[dominant], 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(rates[dominant] / PEAK_HBM_GBPS, 4),
                 "traffic": traffic_for(w.name, dominant), "units_per_launch": amount}
-    gather_gbps = rates.get("gather_kernel<hashed>")
+    gather_gbps = rates.get("gather_kernel<hashed>", rates.get("gather_kernel<hashed,hot>"))
     peaks = measured_peaks(torch)
     roof["frac_of_measured_peak"] = round(
         roof["achieved"] / (peaks["bf16_gemm_TFLOPs"] if kind == "mfma" else peaks["hbm_copy_GBps"]), 4)
 
     cpu = None
     if not args.no_cpu_baseline and args.config in (1, 2):
-        cpu = cpu_baseline(w, args.cpu_budget_s)
+        hot = None
+        if "_hot" in extra:
+            _, keys, rows, _ = extra["_hot"]
+            hot = {"keys": {n: [tuple(int(v) for v in r) for r in k] for n, k in keys.items()}, "rows": rows}
+        cpu = cpu_baseline(w, args.cpu_budget_s, hot)
 
     lay = lays[0]
     out = {
@@ -641,7 +689,8 @@ def main():
         "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) tables, N(0,1) hidden states)",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "layers_per_step": len(calls), "branches": lay.branches,
                    "d": lay.d, "d_mem": lay.d_mem, "tables": lay.hash.n_tables,
-                   "table_rows": int(lay.tables.n_rows.sum()), "table_dtype": lay.tables.dtype},
+                   "table_rows": int(lay.tables.n_rows.sum()), "table_dtype": lay.tables.dtype,
+                   "hot_ngrams_per_order": args.hot_tier if args.config in (1, 2) else 0},
         "timing": f"HIP graph replay, {per_graph} steps per graph" if graph is not None else "eager launches",
         "gather_GBps": None if gather_gbps is None else round(gather_gbps, 1),
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
@@ -670,10 +719,11 @@ def main():
         torch.cuda.synchronize()
 
 
-def cpu_baseline(w, budget_s):
+def cpu_baseline(w, budget_s, hot=None):
     """The CPU oracle (float64, numpy) on a bounded sample of the same workload:
     whole forward passes over the first 1024 tokens of sequence 0, repeated
-    until the time budget is used; reported as tokens/s."""
+    until the time budget is used; reported as tokens/s.  hot: the oracle's
+    form of the Engram-Nine tier when the workload has one."""
     from oracle import engram_oracle as orc
     try:
         from threadpoolctl import threadpool_info
@@ -687,7 +737,7 @@ def cpu_baseline(w, budget_s):
     n = 0
     t0 = time.perf_counter()
     while True:
-        orc.forward(tok, Hs, lay, w.dtype)
+        orc.forward(tok, Hs, lay, w.dtype, hot=hot)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s:

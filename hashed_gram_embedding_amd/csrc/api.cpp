@@ -10,6 +10,7 @@
 
 #include "engram.h"
 #include "engram_internal.h"
+#include "hot_device.h"
 
 #define ENGRAM_API extern "C" __attribute__((visibility("default")))
 
@@ -319,6 +320,44 @@ engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdty
   return r;
 }
 
+// The Engram-Nine hot tier.  tab = NULL when only the lookup runs (then the
+// rows are not read and may be NULL).  *any is set when some order has a
+// hot set.
+engram_status check_hot(const engram_hot_tier* hot, const engram_hash_params* hp, const engram_tables* tab,
+                        engram::HotArgs* out, bool* any) {
+  *any = false;
+  if (out != nullptr) *out = engram::HotArgs{};
+  if (hot == nullptr) return ENGRAM_OK;
+  for (int o = 0; o < ENGRAM_MAX_ORDER - 1; ++o) {
+    const int n = o + 2;
+    const int64_t nh = hot->n_hot[o];
+    if (nh < 0 || nh > INT32_MAX) return fail(ENGRAM_EINVAL, "hot tier: n_hot of order %d outside [0, 2^31)", n);
+    if (nh == 0) continue;
+    if (n > hp->max_n) return fail(ENGRAM_EINVAL, "hot tier: order %d has a hot set but max_n is %d", n, hp->max_n);
+    if (hot->pilots[o] == nullptr || hot->slots[o] == nullptr || (tab != nullptr && hot->rows[o] == nullptr))
+      return fail(ENGRAM_EINVAL, "hot tier: order %d needs pilots, slots and rows", n);
+    if (!aligned(hot->slots[o], 32) || !aligned(hot->pilots[o], 4) || !aligned(hot->rows[o], 16))
+      return fail(ENGRAM_EINVAL, "hot tier: order %d slots must be 32-byte, pilots 4-byte, rows 16-byte aligned", n);
+    *any = true;
+    if (out != nullptr) {
+      engram::HotOrderArgs& a = out->o[o];
+      a.pilots = hot->pilots[o];
+      a.slots = reinterpret_cast<const uint4*>(hot->slots[o]);
+      a.rows = hot->rows[o];
+      a.seed = hot->seed[o];
+      a.n_hot = static_cast<uint64_t>(nh);
+      a.n_buckets = engram::hot_buckets(static_cast<uint64_t>(nh));
+    }
+  }
+  if (*any && tab != nullptr && tab->dtype != ENGRAM_F32 && tab->dtype != ENGRAM_BF16)
+    return fail(ENGRAM_EUNSUPPORTED, "hot tier: needs F32 or BF16 tables");
+  if (out != nullptr) {
+    out->heads = hp->heads;
+    out->width = tab != nullptr ? hp->heads * tab->dim : 0;
+  }
+  return ENGRAM_OK;
+}
+
 engram_status check_layer(const engram_layer* L, engram::HashArgs* ha, engram::TableArgs* ta,
                           engram::GateConvArgs* ga) {
   if (L == nullptr) return fail(ENGRAM_EINVAL, "layer is NULL");
@@ -351,7 +390,8 @@ engram_status check_layer(const engram_layer* L, engram::HashArgs* ha, engram::T
     if (!aligned(L->w_mx, 16) || !aligned(L->w_mx_scale, 4))
       return fail(ENGRAM_EINVAL, "layer: w_mx must be 16-byte and w_mx_scale 4-byte aligned");
   }
-  return ENGRAM_OK;
+  bool any_hot;
+  return check_hot(L->hot, &L->hash, &L->tables, nullptr, &any_hot);
 }
 
 }  // namespace
@@ -460,8 +500,13 @@ engram_status run_retrieve(const int32_t* tokens, int64_t B, int64_t T, const en
                            const engram_decode_state* st, void* e, hipStream_t stream) {
   const int32_t* hist = st != nullptr ? st->ids : nullptr;
   const int out = L->w_mx != nullptr ? engram::kGatherOutMXFP8 : hdtype;
-  prof_mark(stream, "gather_kernel<hashed>");
-  return hip_status(engram::launch_hash_gather(tokens, B, T, hist, L->hash.proj, ha, ta, out, e, stream),
+  engram::HotArgs hot;
+  bool any_hot;
+  const engram_status r = check_hot(L->hot, &L->hash, &L->tables, &hot, &any_hot);
+  if (r != ENGRAM_OK) return r;
+  prof_mark(stream, any_hot ? "gather_kernel<hashed,hot>" : "gather_kernel<hashed>");
+  return hip_status(engram::launch_hash_gather(tokens, B, T, hist, L->hash.proj, ha, ta, any_hot ? &hot : nullptr,
+                                               out, e, stream),
                     "hash+gather launch");
 }
 
@@ -740,4 +785,49 @@ ENGRAM_API engram_status engram_host_alloc(size_t bytes, void** host_ptr, void**
 ENGRAM_API engram_status engram_host_free(void* host_ptr) {
   if (host_ptr == nullptr) return ENGRAM_OK;
   return hip_status(hipHostFree(host_ptr), "hipHostFree");
+}
+
+ENGRAM_API size_t engram_hot_buckets(int64_t n_hot) {
+  return n_hot <= 0 ? 0 : static_cast<size_t>(engram::hot_buckets(static_cast<uint64_t>(n_hot)));
+}
+
+ENGRAM_API engram_status engram_hot_build(const int32_t* keys, int64_t n_hot, int32_t n, uint64_t seed,
+                                          uint32_t* pilots, engram_hot_slot* slots, uint64_t* seed_used) {
+  static_assert(sizeof(engram_hot_slot) == 32, "a hot slot is 32 bytes");
+  if (n < 2 || n > ENGRAM_MAX_ORDER) return fail(ENGRAM_EINVAL, "hot build: n=%d outside [2, %d]", n, ENGRAM_MAX_ORDER);
+  if (n_hot < 1 || n_hot > INT32_MAX) return fail(ENGRAM_EINVAL, "hot build: n_hot must be in [1, 2^31)");
+  if (keys == nullptr || pilots == nullptr || slots == nullptr || seed_used == nullptr)
+    return fail(ENGRAM_EINVAL, "hot build: keys, pilots, slots and seed_used must be non-NULL");
+  for (int64_t q = 0; q < n_hot * n; ++q)
+    if (keys[q] < 0) return fail(ENGRAM_EINVAL, "hot build: n-gram %lld holds a negative id", static_cast<long long>(q / n));
+  for (int attempt = 0; attempt < 16; ++attempt) {
+    const uint64_t s = seed + static_cast<uint64_t>(attempt);
+    const engram::HotBuild b = engram::hot_build(keys, n_hot, n, s, pilots, reinterpret_cast<int32_t*>(slots));
+    if (b.status == engram::HotBuild::kOk) {
+      *seed_used = s;
+      return ENGRAM_OK;
+    }
+    if (b.status == engram::HotBuild::kDuplicate)
+      return fail(ENGRAM_EINVAL, "hot build: n-grams %u and %u are equal", b.a, b.b);
+  }
+  return fail(ENGRAM_EUNSUPPORTED, "hot build: no seed in [seed, seed+15] gave a perfect hash");
+}
+
+ENGRAM_API engram_status engram_hot_lookup(const int32_t* tokens, int64_t B, int64_t T, const int32_t* hist,
+                                           const engram_hash_params* hp, const engram_hot_tier* hot,
+                                           int32_t* hot_row, hipStream_t stream) {
+  engram::HashArgs ha;
+  engram_status r = check_hash(hp, &ha);
+  if (r != ENGRAM_OK) return r;
+  if (hot == nullptr) return fail(ENGRAM_EINVAL, "hot lookup: hot is NULL");
+  engram::HotArgs h;
+  bool any;
+  if ((r = check_hot(hot, hp, nullptr, &h, &any)) != ENGRAM_OK) return r;
+  if (B < 0 || T < 0) return fail(ENGRAM_EINVAL, "hot lookup: B and T must be >= 0");
+  if (B * T == 0) return ENGRAM_OK;
+  if (tokens == nullptr || hot_row == nullptr) return fail(ENGRAM_EINVAL, "hot lookup: tokens and hot_row must be non-NULL");
+  prof_begin();
+  prof_mark(stream, "hot_lookup_kernel");
+  return hip_status(engram::launch_hot_lookup(tokens, B, T, hist, hp->proj, hp->max_n, h, hot_row, stream),
+                    "hot lookup launch");
 }

@@ -12,7 +12,7 @@ namespace engram {
 
 // Hash parameters by value: they travel in the kernel-argument segment.
 struct HashArgs {
-  uint64_t mult[ENGRAM_MAX_TABLES][ENGRAM_MAX_ORDER];  // per table j: m_{n,k,i}
+  uint64_t mult[ENGRAM_MAX_TABLES][ENGRAM_MAX_ORDER];  // per table j: m_{n,k,i}; 0 for i >= n
   uint64_t inv[ENGRAM_MAX_TABLES];                     // floor((2^64-1) / p_j)
   uint32_t prime[ENGRAM_MAX_TABLES];
   int32_t order[ENGRAM_MAX_TABLES];                    // n of table j
@@ -20,14 +20,6 @@ struct HashArgs {
   int32_t max_n;
 };
 
-// Where the fused hash+gather reads its ids.
-struct HashSrc {
-  const int32_t* tokens;
-  const int32_t* proj;
-  const int32_t* hist;
-  int64_t T;
-  HashArgs a;
-};
 
 struct TableArgs {
   int64_t row_offset[ENGRAM_MAX_TABLES];
@@ -40,6 +32,34 @@ struct TableArgs {
   int32_t n_tables;
   int32_t dim;
   int32_t dtype;  // engram_dtype
+};
+
+// Engram-Nine hot tier of one order on the device.  A slot is 32 bytes:
+// ids[4] with ids[i] = x'_{t-i} for i < n and 0 above, then the hot row,
+// then padding.
+struct HotOrderArgs {
+  const uint32_t* pilots;  // [n_buckets]
+  const uint4* slots;      // [n_hot][2]
+  const void* rows;        // [n_hot][width]
+  uint64_t seed;
+  uint64_t n_hot;          // 0 = no hot tier for this order
+  uint64_t n_buckets;
+};
+
+struct HotArgs {
+  HotOrderArgs o[ENGRAM_MAX_ORDER - 1];  // order n at [n-2]
+  int32_t width;                         // K * dim: columns of a hot row
+  int32_t heads;                         // K
+};
+
+// Where the fused hash+gather reads its ids.
+struct HashSrc {
+  const int32_t* tokens;
+  const int32_t* proj;
+  const int32_t* hist;
+  int64_t T;
+  HashArgs a;
+  HotArgs hot;  // used by the hot-tier variant only
 };
 
 struct GateConvArgs {
@@ -73,9 +93,22 @@ hipError_t launch_gather(const int32_t* z, int64_t n_tok, const TableArgs& ta, i
                          void* e, hipStream_t s);
 
 // Steps 1-4 in one kernel: rows are addressed by indices hashed in-thread.
+// hot: the Engram-Nine hot tier, or null for the cold lookup alone.
 hipError_t launch_hash_gather(const int32_t* tokens, int64_t B, int64_t T, const int32_t* hist,
                               const int32_t* proj, const HashArgs& a, const TableArgs& ta,
-                              int out_dtype, void* e, hipStream_t s);
+                              const HotArgs* hot, int out_dtype, void* e, hipStream_t s);
+
+hipError_t launch_hot_lookup(const int32_t* tokens, int64_t B, int64_t T, const int32_t* hist,
+                             const int32_t* proj, int max_n, const HotArgs& h, int32_t* out, hipStream_t s);
+
+// Host build of one order's minimal perfect hash (pilots, and 8 int32 per
+// slot: ids newest first, row, padding).  a, b name the n-grams behind a
+// duplicate or a retry.
+struct HotBuild {
+  enum Status { kOk, kDuplicate, kRetry } status;
+  uint32_t a, b;
+};
+HotBuild hot_build(const int32_t* keys, int64_t n_hot, int n, uint64_t seed, uint32_t* pilots, int32_t* slots);
 
 hipError_t launch_project_kv(const void* e, const void* w, int64_t n_tok, int64_t d_mem,
                              int64_t n_out, int in_dtype, int out_dtype, void* kv, hipStream_t s);

@@ -16,9 +16,17 @@
 // Inside the layer forward the row index is hashed in the same thread
 // (Steps 1-3), so the indices never go through memory.  With access counts
 // given, the first thread of each row access adds 1 to the row's count.
+//
+// With the Engram-Nine hot tier ("DeepSeek Engram series guide", experiment
+// 3, Figure 1) the same thread first looks its n-gram up in the hot set of
+// its order; on a hit it copies its 8 elements from the n-gram's hot row
+// (head k of order n covers columns k*dim .. k*dim+dim-1 of that row) and
+// reads no cold row.  With K*dim/8 = 64 a wavefront holds exactly one
+// (token, order), so the lookup is uniform across it.
 #include "device_util.h"
 #include "engram_internal.h"
 #include "hash_device.h"
+#include "hot_device.h"
 
 namespace engram {
 namespace {
@@ -29,12 +37,16 @@ template <int IN>
 __device__ __forceinline__ void load8(const void* base, const float* scale, int64_t row, int dim,
                                       int col, float* f, uint4* raw_bf16) {
   if constexpr (IN == ENGRAM_BF16) {
-    const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * dim + col);
+    const uint4 q = global_load16(static_cast<const uint16_t*>(base) + row * dim + col);
     *raw_bf16 = q;
     unpack8(q, f);
   } else if constexpr (IN == ENGRAM_F32) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + row * dim + col);
-    const float4 a = p[0], b = p[1];
+    const float* p = static_cast<const float*>(base) + row * dim + col;
+    const uint4 qa = global_load16(p), qb = global_load16(p + 4);
+    const float4 a = make_float4(__uint_as_float(qa.x), __uint_as_float(qa.y), __uint_as_float(qa.z),
+                                 __uint_as_float(qa.w));
+    const float4 b = make_float4(__uint_as_float(qb.x), __uint_as_float(qb.y), __uint_as_float(qb.z),
+                                 __uint_as_float(qb.w));
     f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
   } else {
@@ -49,7 +61,7 @@ __device__ __forceinline__ void load8(const void* base, const float* scale, int6
   }
 }
 
-template <int IN, int OUT, bool HASHED>
+template <int IN, int OUT, bool HASHED, bool HOT>
 __global__ void __launch_bounds__(256)
 gather_kernel(const int32_t* __restrict__ z, int64_t n_tok, TableArgs ta, void* __restrict__ e,
               HashSrc hs) {
@@ -61,29 +73,54 @@ gather_kernel(const int32_t* __restrict__ z, int64_t n_tok, TableArgs ta, void* 
   const int c = static_cast<int>(gid % chunks);
   const int64_t tj = gid / chunks;
   const int j = static_cast<int>(tj % nt);
+  // per-table arguments first: their loads overlap the id loads
+  const int64_t row_offset = ta.row_offset[j];
   int32_t zj;
+  int32_t hot_row = -1;
+  const void* hot_src = nullptr;
+  int hot_col = 0;
   if constexpr (HASHED) {
+    const TableHash th = table_hash(hs.a, j);
     const int64_t bt = tj / nt;
     const int64_t b = bt / hs.T;
-    zj = hash_index(hs.tokens, hs.proj, hs.hist, hs.a, j, b, bt - b * hs.T, hs.T);
+    uint32_t x[ENGRAM_MAX_ORDER];
+    window_ids(hs.tokens, hs.proj, hs.hist, hs.a.max_n, b, bt - b * hs.T, hs.T, x);
+    zj = hash_of_ids(x, th);
+    if constexpr (HOT) {
+      const int n = th.n;
+      const HotOrderArgs o = hot_order(hs.hot, n);
+      hot_row = hot_find(x, n, o);
+      hot_src = o.rows;
+      hot_col = (j - (n - 2) * hs.hot.heads) * ta.dim + c * 8;
+    }
   } else {
     zj = z[tj];
   }
-  int64_t row = ta.row_offset[j] + zj;
-  if (ta.counts != nullptr && c == 0) atomicAdd(ta.counts + row, 1u);   // access statistics (real-time LFU)
   const void* src = ta.rows;
   const float* scale = ta.scale;
-  if (ta.cache_slot != nullptr) {
-    const int32_t slot = ta.cache_slot[row];
-    if (slot >= 0) {
-      src = ta.cache_rows;
-      scale = ta.cache_scale;
-      row = slot;
+  int64_t row;
+  int row_len = ta.dim;
+  int col = c * 8;
+  if (HOT && hot_row >= 0) {
+    src = hot_src;
+    row = hot_row;
+    row_len = hs.hot.width;
+    col = hot_col;
+  } else {
+    row = row_offset + zj;
+    if (ta.counts != nullptr && c == 0) atomicAdd(ta.counts + row, 1u);   // access statistics (real-time LFU)
+    if (ta.cache_slot != nullptr) {
+      const int32_t slot = ta.cache_slot[row];
+      if (slot >= 0) {
+        src = ta.cache_rows;
+        scale = ta.cache_scale;
+        row = slot;
+      }
     }
   }
   float f[8];
   uint4 raw;
-  load8<IN>(src, scale, row, ta.dim, c * 8, f, &raw);
+  load8<IN>(src, scale, row, row_len, col, f, &raw);
   const int64_t out = tj * ta.dim + c * 8;
   if constexpr (OUT == kOutMXFP8) {
     // MXFP8 e: 8 codes per thread, the block scale from the 4 threads of the
@@ -105,7 +142,7 @@ gather_kernel(const int32_t* __restrict__ z, int64_t n_tok, TableArgs ta, void* 
   }
 }
 
-template <int IN, bool HASHED>
+template <int IN, bool HASHED, bool HOT>
 hipError_t launch_in(const int32_t* z, int64_t n_tok, const TableArgs& ta, int out, void* e,
                      const HashSrc& hs, hipStream_t s) {
   const int64_t total = n_tok * ta.n_tables * (ta.dim / 8);
@@ -113,21 +150,25 @@ hipError_t launch_in(const int32_t* z, int64_t n_tok, const TableArgs& ta, int o
   const int threads = 256;
   const dim3 grid(static_cast<unsigned>((total + threads - 1) / threads));
   if (out == kOutMXFP8)
-    launch_k((gather_kernel<IN, kOutMXFP8, HASHED>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
+    launch_k((gather_kernel<IN, kOutMXFP8, HASHED, HOT>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
   else if (out == ENGRAM_BF16)
-    launch_k((gather_kernel<IN, ENGRAM_BF16, HASHED>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
+    launch_k((gather_kernel<IN, ENGRAM_BF16, HASHED, HOT>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
   else
-    launch_k((gather_kernel<IN, ENGRAM_F32, HASHED>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
+    launch_k((gather_kernel<IN, ENGRAM_F32, HASHED, HOT>), grid, dim3(threads), 0, s, z, n_tok, ta, e, hs);
   return hipGetLastError();
 }
 
-template <bool HASHED>
+// The hot tier holds F32 or BF16 rows only (checked by the caller), so int8
+// tables have no hot variant.
+template <bool HASHED, bool HOT>
 hipError_t dispatch(const int32_t* z, int64_t n_tok, const TableArgs& ta, int out_dtype, void* e,
                     const HashSrc& hs, hipStream_t s) {
   switch (ta.dtype) {
-    case ENGRAM_BF16: return launch_in<ENGRAM_BF16, HASHED>(z, n_tok, ta, out_dtype, e, hs, s);
-    case ENGRAM_F32: return launch_in<ENGRAM_F32, HASHED>(z, n_tok, ta, out_dtype, e, hs, s);
-    default: return launch_in<ENGRAM_I8, HASHED>(z, n_tok, ta, out_dtype, e, hs, s);
+    case ENGRAM_BF16: return launch_in<ENGRAM_BF16, HASHED, HOT>(z, n_tok, ta, out_dtype, e, hs, s);
+    case ENGRAM_F32: return launch_in<ENGRAM_F32, HASHED, HOT>(z, n_tok, ta, out_dtype, e, hs, s);
+    default:
+      if constexpr (HOT) return hipErrorInvalidValue;
+      else return launch_in<ENGRAM_I8, HASHED, false>(z, n_tok, ta, out_dtype, e, hs, s);
   }
 }
 
@@ -135,14 +176,15 @@ hipError_t dispatch(const int32_t* z, int64_t n_tok, const TableArgs& ta, int ou
 
 hipError_t launch_gather(const int32_t* z, int64_t n_tok, const TableArgs& ta, int out_dtype,
                          void* e, hipStream_t s) {
-  return dispatch<false>(z, n_tok, ta, out_dtype, e, HashSrc{}, s);
+  return dispatch<false, false>(z, n_tok, ta, out_dtype, e, HashSrc{}, s);
 }
 
 hipError_t launch_hash_gather(const int32_t* tokens, int64_t B, int64_t T, const int32_t* hist,
                               const int32_t* proj, const HashArgs& a, const TableArgs& ta,
-                              int out_dtype, void* e, hipStream_t s) {
-  HashSrc hs{tokens, proj, hist, T, a};
-  return dispatch<true>(nullptr, B * T, ta, out_dtype, e, hs, s);
+                              const HotArgs* hot, int out_dtype, void* e, hipStream_t s) {
+  HashSrc hs{tokens, proj, hist, T, a, hot != nullptr ? *hot : HotArgs{}};
+  if (hot != nullptr) return dispatch<true, true>(nullptr, B * T, ta, out_dtype, e, hs, s);
+  return dispatch<true, false>(nullptr, B * T, ta, out_dtype, e, hs, s);
 }
 
 }  // namespace engram

@@ -20,15 +20,13 @@ __device__ __forceinline__ uint32_t mod_prime(uint64_t x, uint32_t p, uint64_t i
   return static_cast<uint32_t>(r >= p ? r - p : r);
 }
 
-// z of table j at position t of sequence b: XOR over i < n of
-// x'_{t-i} * m_{j,i} (wrapping in 64 bits), then mod p_j.  Positions before the
+// Compressed ids of the suffix window at position t of sequence b, newest
+// first: x[i] = x'_{t-i} for i < ENGRAM_MAX_ORDER.  Positions before the
 // sequence start read the history (oldest first) or the pad id 0.
-__device__ __forceinline__ int32_t hash_index(const int32_t* __restrict__ tokens,
-                                              const int32_t* __restrict__ proj,
-                                              const int32_t* __restrict__ hist, const HashArgs& a,
-                                              int j, int64_t b, int64_t t, int64_t T) {
-  const int n = a.order[j];
-  const int hist_len = a.max_n - 1;
+__device__ __forceinline__ void window_ids(const int32_t* __restrict__ tokens, const int32_t* __restrict__ proj,
+                                           const int32_t* __restrict__ hist, int max_n, int64_t b, int64_t t,
+                                           int64_t T, uint32_t (&x)[ENGRAM_MAX_ORDER]) {
+  const int hist_len = max_n - 1;
   // Unrolled to the largest order, with clamped (always valid) positions, so
   // that the token loads of all positions and then their P lookups are each
   // issued together; positions before the sequence start are patched from
@@ -39,7 +37,6 @@ __device__ __forceinline__ int32_t hash_index(const int32_t* __restrict__ tokens
     const int64_t p = t - i;
     tok[i] = tokens[b * T + (p >= 0 ? p : 0)];
   }
-  uint32_t x[ENGRAM_MAX_ORDER];
 #pragma unroll
   for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) x[i] = static_cast<uint32_t>(proj[tok[i]]);
   if (t < hist_len) {
@@ -49,11 +46,47 @@ __device__ __forceinline__ int32_t hash_index(const int32_t* __restrict__ tokens
       if (p < 0) x[i] = hist != nullptr && hist_len + p >= 0 ? static_cast<uint32_t>(hist[b * hist_len + hist_len + p]) : 0u;
     }
   }
+}
+
+// Hash constants of table j.  Kernels read them before the token ids, so
+// that these argument loads and the id loads are in flight together.  The
+// multipliers of positions i >= n are 0, so every position can be taken
+// unconditionally.
+struct TableHash {
+  uint64_t m[ENGRAM_MAX_ORDER];
+  uint64_t inv;
+  uint32_t prime;
+  int32_t n;
+};
+
+__device__ __forceinline__ TableHash table_hash(const HashArgs& a, int j) {
+  TableHash th;
+#pragma unroll
+  for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) th.m[i] = a.mult[j][i];
+  th.inv = a.inv[j];
+  th.prime = a.prime[j];
+  th.n = a.order[j];
+  return th;
+}
+
+// z of a table from the window ids: XOR over i < n of x'_{t-i} * m_i
+// (wrapping in 64 bits), then mod p.
+__device__ __forceinline__ int32_t hash_of_ids(const uint32_t (&x)[ENGRAM_MAX_ORDER], const TableHash& th) {
   uint64_t acc = 0;
 #pragma unroll
-  for (int i = 0; i < ENGRAM_MAX_ORDER; ++i)
-    if (i < n) acc ^= static_cast<uint64_t>(x[i]) * a.mult[j][i];
-  return static_cast<int32_t>(mod_prime(acc, a.prime[j], a.inv[j]));
+  for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) acc ^= static_cast<uint64_t>(x[i]) * th.m[i];
+  return static_cast<int32_t>(mod_prime(acc, th.prime, th.inv));
+}
+
+// z of table j at position t of sequence b.
+__device__ __forceinline__ int32_t hash_index(const int32_t* __restrict__ tokens,
+                                              const int32_t* __restrict__ proj,
+                                              const int32_t* __restrict__ hist, const HashArgs& a,
+                                              int j, int64_t b, int64_t t, int64_t T) {
+  const TableHash th = table_hash(a, j);
+  uint32_t x[ENGRAM_MAX_ORDER];
+  window_ids(tokens, proj, hist, a.max_n, b, t, T, x);
+  return hash_of_ids(x, th);
 }
 
 }  // namespace engram

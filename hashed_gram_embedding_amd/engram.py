@@ -48,9 +48,16 @@ class GateConvParams(ctypes.Structure):
                 ("conv_w", ctypes.c_void_p)]
 
 
+class HotTierStruct(ctypes.Structure):
+    _fields_ = [("n_hot", ctypes.c_int64 * (MAX_ORDER - 1)), ("seed", ctypes.c_uint64 * (MAX_ORDER - 1)),
+                ("pilots", ctypes.c_void_p * (MAX_ORDER - 1)), ("slots", ctypes.c_void_p * (MAX_ORDER - 1)),
+                ("rows", ctypes.c_void_p * (MAX_ORDER - 1))]
+
+
 class LayerStruct(ctypes.Structure):
     _fields_ = [("hash", HashParams), ("tables", Tables), ("w", ctypes.c_void_p), ("gc", GateConvParams),
-                ("w_mx", ctypes.c_void_p), ("w_mx_scale", ctypes.c_void_p)]
+                ("w_mx", ctypes.c_void_p), ("w_mx_scale", ctypes.c_void_p),
+                ("hot", ctypes.POINTER(HotTierStruct))]
 
 
 class DecodeStateStruct(ctypes.Structure):
@@ -98,6 +105,10 @@ def lib():
         "engram_cache_build_workspace": (sz, [i64]),
         "engram_cache_build": (i32, [vp, i64, i64, ctypes.POINTER(HashParams), ctypes.POINTER(Tables), i64, vp, vp, vp,
                                      vp, sz, vp]),
+        "engram_hot_buckets": (sz, [i64]),
+        "engram_hot_build": (i32, [vp, i64, i32, ctypes.c_uint64, vp, vp, ctypes.POINTER(ctypes.c_uint64)]),
+        "engram_hot_lookup": (i32, [vp, i64, i64, vp, ctypes.POINTER(HashParams), ctypes.POINTER(HotTierStruct),
+                                    vp, vp]),
         "engram_profile_enable": (i32, [i32]),
         "engram_profile_read": (i32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), i32,
                                       ctypes.POINTER(i32)]),
@@ -118,6 +129,7 @@ def exported_names():
             "engram_forward_workspace", "engram_forward", "engram_retrieve", "engram_forward_retrieved_workspace",
             "engram_forward_retrieved", "engram_cache_build_workspace", "engram_cache_build",
             "engram_cache_update_workspace", "engram_cache_update", "engram_quantize_mxfp8",
+            "engram_hot_buckets", "engram_hot_build", "engram_hot_lookup",
             "engram_profile_enable", "engram_profile_read",
             "engram_host_alloc", "engram_host_free"]
 
@@ -196,6 +208,7 @@ class Layer:
         self.conv_w = to_device(li.conv_w.astype(np.float32), "f32", device)
         self.cache_slot = self.cache_rows = self.cache_scale = None
         self.access_counts = None
+        self.hot = None
         self.cache_n = 0
         self.s = LayerStruct()
         self.s.hash = self.hs.s
@@ -224,6 +237,20 @@ class Layer:
         self.cache_n = 0 if rows is None else rows.shape[0]
         t.cache_n = self.cache_n
 
+    def set_hot(self, hot: Optional["HotTier"]):
+        """Attach an Engram-Nine hot tier (built for this layer's K and dim) or
+        detach it (None)."""
+        if hot is not None:
+            width = self.li.hash.heads * self.li.tables.dim
+            for n, k in hot.keys.items():
+                r = hot.rows.get(n)
+                if r is None or r.dtype != _TORCH_DT[self.table_dtype] or tuple(r.shape) != (k.shape[0], width) \
+                        or not r.is_contiguous():
+                    raise ValueError(f"hot rows of order {n} must be a contiguous {_TORCH_DT[self.table_dtype]} "
+                                     f"tensor [{k.shape[0]}, {width}]")
+        self.hot = hot
+        self.s.hot = None if hot is None else ctypes.pointer(hot.s)
+
     def set_access_counts(self, counts: Optional[torch.Tensor]):
         """Per-row access counts (uint32 as int32 [total_rows]) that every gather
         through this layer increments; None stops counting."""
@@ -241,6 +268,50 @@ class Layer:
     @property
     def d_mem(self):
         return self.li.tables.dim * self.li.tables.n_rows.shape[0]
+
+
+def hot_build(keys: np.ndarray, seed: int = 0):
+    """Minimal perfect hash of one order's hot n-grams (host only).
+
+    keys: int [n_hot, n], n-gram r oldest id first.  Returns (pilots uint32
+    [engram_hot_buckets(n_hot)], slots int32 [n_hot, 8], seed_used)."""
+    keys = np.ascontiguousarray(keys, dtype=np.int32)
+    n_hot, n = keys.shape
+    pilots = np.zeros(max(int(lib().engram_hot_buckets(n_hot)), 1), dtype=np.uint32)
+    slots = np.zeros((max(n_hot, 1), 8), dtype=np.int32)
+    used = ctypes.c_uint64(0)
+    _check(lib().engram_hot_build(keys.ctypes.data, n_hot, n, ctypes.c_uint64(seed), pilots.ctypes.data,
+                                  slots.ctypes.data, ctypes.byref(used)))
+    return pilots, slots, int(used.value)
+
+
+class HotTier:
+    """Device copy of an Engram-Nine hot tier: per order n, the hot n-grams
+    (keys[n]: int [n_hot, n], oldest id first) and their rows (rows[n]: a
+    device tensor [n_hot, K*dim] of the cold tables' dtype, row r for key r).
+    Orders absent from `keys` have no hot set."""
+
+    def __init__(self, keys: dict, rows: Optional[dict] = None, seed: int = 0, device="cuda"):
+        self.s = HotTierStruct()
+        self.pilots, self.slots, self.rows, self.keys = {}, {}, {}, {}
+        for n, k in keys.items():
+            k = np.ascontiguousarray(k, dtype=np.int32).reshape(-1, n)
+            if k.shape[0] == 0:
+                continue
+            pilots, slots, used = hot_build(k, seed)
+            o = n - 2
+            self.keys[n] = k
+            self.pilots[n] = to_device(pilots.view(np.int32), "i32", device)
+            self.slots[n] = to_device(slots, "i32", device)
+            self.s.n_hot[o] = k.shape[0]
+            self.s.seed[o] = used
+            self.s.pilots[o] = self.pilots[n].data_ptr()
+            self.s.slots[o] = self.slots[n].data_ptr()
+            if rows is not None:
+                r = rows[n]
+                assert r.is_contiguous() and r.shape[0] == k.shape[0]
+                self.rows[n] = r
+                self.s.rows[o] = r.data_ptr()
 
 
 class DecodeState:
@@ -408,6 +479,18 @@ def quantize_mxfp8(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream
     rows, cols = x.shape
     dt = BF16 if x.dtype == torch.bfloat16 else F32
     _check(lib().engram_quantize_mxfp8(_ptr(x), dt, rows, cols, _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def hot_lookup(tokens: torch.Tensor, spec, hot: HotTier, hist: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Hot row of every suffix n-gram, int32 [B, T, N-1] (-1 = cold)."""
+    hs = spec.hs if isinstance(spec, Layer) else spec
+    B, T = tokens.shape
+    if out is None:
+        out = torch.empty((B, T, hs.hp.max_n - 1), dtype=torch.int32, device=tokens.device)
+    _check(lib().engram_hot_lookup(_ptr(tokens), B, T, _ptr(hist), ctypes.byref(hs.s), ctypes.byref(hot.s),
+                                   _ptr(out), _stream(stream)))
+    return out
 
 
 def retrieve(tokens: torch.Tensor, layer: Layer, e: torch.Tensor, state: Optional[DecodeState] = None,

@@ -2,8 +2,8 @@
 
 This module draws every input the layer consumes -- token ids, the vocabulary
 projection table, hash multipliers, prime table sizes, embedding tables,
-hidden states, projection and conv weights, decode context and LFU warm-up
-streams -- and nothing else.  It holds none of the layer's arithmetic (no
+hidden states, projection and conv weights, decode context, LFU warm-up
+streams and the hot tier's n-gram choice and rows -- and nothing else.  It holds none of the layer's arithmetic (no
 hashing, gathering, projection, gating or convolution), so the CPU oracle and
 the GPU library can both be fed from it without sharing any of the method.
 
@@ -30,7 +30,7 @@ from typing import List, Optional
 import numpy as np
 
 # stream ids inside SeedSequence([config, layer, stream])
-S_TOKENS, S_PROJ, S_MULT, S_TABLES, S_H, S_W, S_CONV, S_LFU, S_CONTEXT = range(9)
+S_TOKENS, S_PROJ, S_MULT, S_TABLES, S_H, S_W, S_CONV, S_LFU, S_CONTEXT, S_HOT = range(10)
 
 F32, BF16, I8 = "f32", "bf16", "i8"
 
@@ -358,3 +358,48 @@ def lfu_warmup_tokens(config: int, layer: int, n: int = 1 << 24, vocab: int = 12
     """Seeded Zipf(1.1) warm-up stream, shape [1, n], whose row-access counts
     decide the static LFU admission of the HBM hot cache."""
     return zipf_tokens(rng_for(config, layer, S_LFU), vocab, 1.1, (1, n))
+
+
+# --------------------------------------------------------------------------
+# Engram-Nine hot tier ("DeepSeek Engram series guide", experiment 3): the
+# hot set is the most frequent n-grams of the training text.  Here it is the
+# most frequent windows of a seeded Zipf(1.1) warm-up stream, counted on ids
+# the caller has already projected; the hot rows are drawn like table rows.
+# --------------------------------------------------------------------------
+
+def hot_warmup_tokens(config: int, layer: int, n: int = 1 << 21, vocab: int = 128_000) -> np.ndarray:
+    """Seeded Zipf(1.1) warm-up stream, shape [1, n], whose most frequent
+    n-grams form the hot set."""
+    return zipf_tokens(rng_for(config, layer, S_HOT), vocab, 1.1, (1, n))
+
+
+def frequent_ngrams(ids: np.ndarray, n: int, n_hot: int) -> np.ndarray:
+    """The n_hot most frequent length-n windows of the rows of ids (int [R, L]);
+    windows stay inside a row.  Ties go to the smaller window in lexicographic
+    order.  Returns int32 [min(n_hot, distinct), n], most frequent first,
+    each window oldest id first."""
+    ids = np.asarray(ids, dtype=np.int64)
+    rows = [np.lib.stride_tricks.sliding_window_view(r, n) for r in ids if r.shape[0] >= n]
+    if not rows or n_hot <= 0:
+        return np.zeros((0, n), dtype=np.int32)
+    wins = np.concatenate(rows, axis=0)
+    if n <= 3 and ids.size and 0 <= ids.min() and ids.max() < (1 << 21):
+        # 21 bits per id, oldest id most significant: numeric order of the
+        # packed words is the lexicographic order of the windows
+        packed = np.zeros(wins.shape[0], dtype=np.int64)
+        for i in range(n):
+            packed = (packed << 21) | wins[:, i]
+        uk, counts = np.unique(packed, return_counts=True)
+        uniq = np.stack([(uk >> (21 * (n - 1 - i))) & ((1 << 21) - 1) for i in range(n)], axis=1)
+    else:
+        uniq, counts = np.unique(wins, axis=0, return_counts=True)     # lexicographic order
+    order = np.argsort(-counts, kind="stable")[:n_hot]
+    return np.ascontiguousarray(uniq[order].astype(np.int32))
+
+
+def hot_rows(config: int, layer: int, n: int, n_hot: int, width: int, dtype: str, std: float = 0.02):
+    """Hot rows of order n: [n_hot, width] N(0, std), as bf16 bits or float32."""
+    rng = rng_for(config, layer, S_HOT * 16 + n)
+    if dtype == BF16:
+        return normal_bf16_bits(rng, n_hot * width, std).reshape(n_hot, width)
+    return normal_f32(rng, n_hot * width, std).reshape(n_hot, width)

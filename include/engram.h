@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 2
+#define ENGRAM_ABI_VERSION 3
 #define ENGRAM_MAX_TABLES 32 /* (N-1)*K */
 #define ENGRAM_MAX_ORDER 4   /* N */
 #define ENGRAM_MAX_KERNEL_W 8
@@ -126,6 +126,42 @@ typedef struct engram_gate_conv_params {
                              (kernel_w-1-j)*dilation steps back                     */
 } engram_gate_conv_params;
 
+/* Engram-Nine hot tier ("DeepSeek Engram series guide", experiment 3
+ * "Engram-Nine", Figure 1: two-tier retrieval).  Per order n an optional set
+ * of hot n-grams (the most frequent ones), each with a row of its own of
+ * width K*dim.  A hot n-gram g_{t,n} takes its row for the K heads of order
+ * n, columns (n-2)*K*dim .. (n-1)*K*dim - 1 of e_t; every other n-gram keeps
+ * the K-head cold lookup of Steps 3-4.  The set is indexed by a minimal
+ * perfect hash and every slot keeps its whole n-gram as the fingerprint, so
+ * a lookup is exact: an n-gram outside the set is never taken for a hot one.
+ *
+ * The hash (hash-and-displace with one pilot per bucket, after PTHash,
+ * Pibiri and Trani, SIGIR 2021), for an n-gram with ids x_i = x'_{t-i}:
+ *   mix(v)  = the SplitMix64 finaliser: v ^= v >> 30; v *= 0xbf58476d1ce4e5b9;
+ *             v ^= v >> 27; v *= 0x94d049bb133111eb; v ^= v >> 31
+ *   h       = mix(seed ^ n), then h = mix(h ^ x_i) for i = 0, 1, .., n-1
+ *   range(a, r) = floor(a * r / 2^64)
+ *   bucket  = range(h, engram_hot_buckets(n_hot))
+ *   slot    = range(mix(h ^ mix(pilots[bucket] + 1)), n_hot)
+ * and g_{t,n} is hot, with row slots[slot].row, iff slots[slot].ids equals
+ * (x_0, .., x_{n-1}, 0, ..). */
+typedef struct engram_hot_slot {
+  int32_t ids[ENGRAM_MAX_ORDER]; /* ids[i] = x'_{t-i} for i < n (newest first), 0 above */
+  int32_t row;                   /* the n-gram's row in engram_hot_tier.rows             */
+  int32_t reserved[3];           /* 0                                                    */
+} engram_hot_slot;               /* 32 bytes                                             */
+
+typedef struct engram_hot_tier {
+  int64_t n_hot[ENGRAM_MAX_ORDER - 1];                /* hot n-grams of order n at [n-2],
+                                                         0..2^31-1; 0 = no hot tier for n */
+  uint64_t seed[ENGRAM_MAX_ORDER - 1];                /* seed_used of engram_hot_build     */
+  const uint32_t* pilots[ENGRAM_MAX_ORDER - 1];       /* device [engram_hot_buckets(n_hot)]*/
+  const engram_hot_slot* slots[ENGRAM_MAX_ORDER - 1]; /* device [n_hot], 32-byte aligned   */
+  const void* rows[ENGRAM_MAX_ORDER - 1];             /* device [*][K*dim] of the cold
+                                                         tables' dtype (F32 or BF16),
+                                                         16-byte aligned                  */
+} engram_hot_tier;
+
 /* One Engram layer. */
 typedef struct engram_layer {
   engram_hash_params hash;
@@ -143,6 +179,10 @@ typedef struct engram_layer {
      per-block scales; NULL = bf16 product.                                      */
   const uint8_t* w_mx;        /* device [(1+M)*d][n_tables*dim] E4M3 codes        */
   const uint8_t* w_mx_scale;  /* device [(1+M)*d][n_tables*dim/32] scale bytes    */
+  /* optional Engram-Nine hot tier (read on the host during each call; NULL =
+     none): used by engram_forward and engram_retrieve.  Needs F32 or BF16
+     tables; a hot hit reads no cold row and counts no access.                  */
+  const engram_hot_tier* hot;
 } engram_layer;
 
 /* Decode / chunked-prefill state of S sequences (not on the pages; it is
@@ -289,6 +329,34 @@ engram_status engram_cache_update(const engram_tables* tab, int64_t cache_n, int
  * x / scale rounded to nearest-even E4M3, an all-zero block has scale byte 0. */
 engram_status engram_quantize_mxfp8(const void* x, engram_dtype dtype, int64_t rows, int64_t cols,
                                     uint8_t* q, uint8_t* scale, hipStream_t stream);
+
+/* Engram-Nine hot tier set-up and lookup (see engram_hot_tier).
+ *
+ * engram_hot_buckets: pilots of a hot set of n_hot n-grams, ceil(n_hot / 4)
+ * (1 for 1 <= n_hot <= 4, 0 for n_hot <= 0).
+ *
+ * engram_hot_build (host only, touches no device): the minimal perfect hash
+ * of one order's hot set.  keys: host int32 [n_hot][n], n-gram r oldest id
+ * first (as in Step 2), ids >= 0, no n-gram twice; 1 <= n_hot < 2^31,
+ * 2 <= n <= ENGRAM_MAX_ORDER.  Writes host pilots [engram_hot_buckets(n_hot)]
+ * and host slots [n_hot], where n-gram r sits in the slot the hash gives it,
+ * with row = r (so the tier's rows are in the caller's key order), and
+ * *seed_used: the first of seed, seed+1, .., seed+15 for which every bucket
+ * got a pilot.  Pilots are searched per bucket, largest bucket first, from 0
+ * upward.  EINVAL: bad arguments or a repeated n-gram; EUNSUPPORTED: no seed
+ * of the 16 worked (two n-grams with one 64-bit hash, or a bucket with no
+ * pilot below max(2^24, 16 n_hot)).  Deterministic.
+ *
+ * engram_hot_lookup: hot_row device int32 [B][T][N-1], hot_row[b][t][n-2] =
+ * the hot row of g_{t,n} (n-grams formed as in engram_hash_indices, with
+ * hist or pad 0 before the start), or -1 when g_{t,n} is not hot or order n
+ * has no hot tier.  hot: host-read descriptor as in engram_layer. */
+size_t engram_hot_buckets(int64_t n_hot);
+engram_status engram_hot_build(const int32_t* keys, int64_t n_hot, int32_t n, uint64_t seed,
+                               uint32_t* pilots, engram_hot_slot* slots, uint64_t* seed_used);
+engram_status engram_hot_lookup(const int32_t* tokens, int64_t B, int64_t T, const int32_t* hist,
+                                const engram_hash_params* hp, const engram_hot_tier* hot,
+                                int32_t* hot_row, hipStream_t stream);
 
 /* Stage timing, for benchmarks.  engram_profile_enable(1) makes later
  * engram_forward and engram_gate_conv_forward calls on the calling thread

@@ -39,7 +39,7 @@ def test_exports_match_header():
 
 
 def test_abi_version():
-    assert eg.lib().engram_abi_version() == 2
+    assert eg.lib().engram_abi_version() == 3
 
 
 def _hash_params(**over):
@@ -260,3 +260,50 @@ def test_cache_update_rejects_bad_arguments():
     tc, kc = _tables(access_counts=0x10002)
     st, msg = _status(L.engram_gather, p, 4, ctypes.byref(tc), eg.F32, p, None)
     assert st == eg.EINVAL and "access_counts" in msg
+
+
+def test_hot_tier_is_validated_before_launch():
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    hp, keep_h = _hash_params()
+    t, keep_t = _tables()
+    hot = eg.HotTierStruct()
+    hot.n_hot[0] = 10
+    hot.pilots[0], hot.slots[0], hot.rows[0] = 0x20000, 0x30000, 0x40000
+    lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=64, hdtype=eg.F32))
+    lay.hot = ctypes.pointer(hot)
+    need = L.engram_forward_workspace(1, 64, ctypes.byref(lay))
+    z = ctypes.c_void_p(0x50000)
+    # a well-formed tier passes every check (empty call)
+    assert L.engram_forward(p, p, 0, 64, ctypes.byref(lay), None, None, None, None, 0, None) == eg.OK
+    assert L.engram_hot_lookup(p, 0, 64, None, ctypes.byref(hp), ctypes.byref(hot), z, None) == eg.OK
+    cases = [
+        (("slots", 0, 0x30010), eg.EINVAL, "aligned"),     # slots not 32-byte aligned
+        (("rows", 0, 0x40008), eg.EINVAL, "aligned"),
+        (("pilots", 0, None), eg.EINVAL, "pilots"),
+        (("n_hot", 0, -1), eg.EINVAL, "n_hot"),
+        (("n_hot", 2, 5), eg.EINVAL, "max_n"),             # order 4 beyond max_n = 3
+    ]
+    for (field, o, v), status, text in cases:
+        bad = eg.HotTierStruct()
+        ctypes.pointer(bad)[0] = hot
+        getattr(bad, field)[o] = v
+        if field == "n_hot" and o == 2:
+            bad.pilots[2], bad.slots[2], bad.rows[2] = 0x20000, 0x30000, 0x40000
+        lay.hot = ctypes.pointer(bad)
+        st, msg = _status(L.engram_forward, p, p, 1, 64, ctypes.byref(lay), None, None, None, p, need, None)
+        assert st == status and text in msg, (field, msg)
+        st, msg = _status(L.engram_retrieve, p, 1, 64, ctypes.byref(lay), None, p, None)
+        assert st == status and text in msg, (field, msg)
+    # int8 tables have no hot tier
+    t8, keep_8 = _tables(dtype=eg.I8, row_scale=0x60000)
+    lay8 = eg.LayerStruct(hp, t8, 0x10000, _gc(d=64, hdtype=eg.F32))
+    lay8.hot = ctypes.pointer(hot)
+    st, msg = _status(L.engram_forward, p, p, 1, 64, ctypes.byref(lay8), None, None, None, p, need, None)
+    assert st == eg.EUNSUPPORTED and "hot" in msg
+    # the lookup alone needs no rows, but a tier and output
+    nor = eg.HotTierStruct()
+    ctypes.pointer(nor)[0] = hot
+    nor.rows[0] = None
+    assert L.engram_hot_lookup(p, 1, 64, None, ctypes.byref(hp), ctypes.byref(nor), None, None) == eg.EINVAL
+    assert L.engram_hot_lookup(p, 1, 64, None, ctypes.byref(hp), None, z, None) == eg.EINVAL

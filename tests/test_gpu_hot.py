@@ -1,0 +1,235 @@
+"""GPU: the Engram-Nine hot tier ("DeepSeek Engram series guide", experiment
+3 "Engram-Nine", Figure 1: two-tier retrieval) against the oracle.
+
+The device lookup (a minimal perfect hash and a whole-n-gram fingerprint)
+must give exactly the oracle's set membership and rows; with the tier
+attached, the gathered rows equal the oracle's two-tier e bit for bit (also
+in MXFP8), the layer matches the oracle's forward at the stated tolerances,
+retrieval split from compute and chunked prefill with a decode state agree,
+and access counts cover exactly the cold rows read."""
+import numpy as np
+import pytest
+import torch
+
+from hashed_gram_embedding_amd import engram as eg
+from hashed_gram_embedding_amd import inputs
+from oracle import engram_oracle as orc
+
+from parity import check_bf16_layer, check_f32_layer, log, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def hot_sets(w, lay, n_hot, seed, orders=None, absent=7, corpus=None):
+    """Hot n-grams: the n_hot most frequent n-grams of `corpus` (raw tokens,
+    default the workload's own, then also the padded n-grams at the start of
+    each sequence), plus `absent` random n-grams; rows drawn in the tables'
+    storage type.  Returns (oracle dict, HotTier)."""
+    hp, tab = lay.hash, lay.tables
+    rng = np.random.default_rng(seed)
+    xc = orc.compress(w.tokens if corpus is None else corpus, hp.proj)
+    keys, rows, dev_rows = {}, {}, {}
+    for n in (orders or range(2, hp.max_n + 1)):
+        k = inputs.frequent_ngrams(xc, n, n_hot)
+        if corpus is None and n_hot > 0:
+            pads = [orc.suffix_ngram(xc, b, t, n) for b in range(xc.shape[0]) for t in range(min(n - 1, xc.shape[1]))]
+            k = np.concatenate([k, np.array(pads, dtype=np.int32).reshape(-1, n)])
+        extra = rng.integers(0, hp.vocab_c, size=(absent, n)).astype(np.int32)
+        k = np.concatenate([k, extra]) if absent else k
+        _, first = np.unique(k, axis=0, return_index=True)
+        k = k[np.sort(first)]
+        keys[n] = k
+        rows[n] = inputs.hot_rows(w.config, 0, n, k.shape[0], hp.heads * tab.dim, tab.dtype)
+        dev_rows[n] = eg.to_device(rows[n], tab.dtype, DEV)
+    ref = {"keys": {n: [tuple(int(v) for v in r) for r in k] for n, k in keys.items()}, "rows": rows}
+    return ref, eg.HotTier(keys, dev_rows, seed=seed, device=DEV)
+
+
+def two_tier_e(w, lay, ref, out, tokens=None, hist=None):
+    hp, tab = lay.hash, lay.tables
+    tokens = w.tokens if tokens is None else tokens
+    z = orc.hash_indices(tokens, hp.proj, hp.mult, hp.prime, hp.max_n, hp.heads, hist)
+    idx = orc.hot_lookup(tokens, hp.proj, hp.max_n, ref["keys"], hist)
+    e = orc.gather_two_tier(z, idx, tab.rows, tab.dtype, tab.row_offset, tab.dim, hp.heads, ref["rows"],
+                            tab.scale, out)
+    return e, idx
+
+
+@pytest.mark.parametrize("config,B,T,n_hot,hist", [(0, 2, 40, 30, False), (1, 2, 300, 200, True),
+                                                    (1, 1, 1, 3, True), (2, 1, 130, 1, False)])
+def test_lookup_bit_exact(config, B, T, n_hot, hist):
+    log(f"hot lookup config={config} B={B} T={T} n_hot={n_hot} hist={hist}")
+    w = inputs.make_config(config, B=B, T=T, rows_per_table=997)
+    lay = w.layers[0]
+    ref, hot = hot_sets(w, lay, n_hot, seed=config * 10 + B)
+    L = eg.Layer(lay, w.dtype, DEV)
+    h = None
+    if hist:
+        h = np.random.default_rng(9).integers(0, lay.hash.vocab_c, size=(B, lay.hash.max_n - 1)).astype(np.int32)
+    got = eg.hot_lookup(torch.from_numpy(w.tokens).to(DEV), L, hot,
+                        None if h is None else torch.from_numpy(h).to(DEV))
+    torch.cuda.synchronize()
+    want = orc.hot_lookup(w.tokens, lay.hash.proj, lay.hash.max_n, ref["keys"], h)
+    assert np.array_equal(got.cpu().numpy(), want)
+    if B * T > 1:
+        assert np.any(want >= 0) and np.any(want < 0)
+
+
+@pytest.mark.parametrize("config,B,T", [(0, 2, 40), (1, 2, 300), (2, 1, 130), (1, 1, 1)])
+def test_forward_and_rows_match_oracle(config, B, T):
+    log(f"hot forward config={config} B={B} T={T}")
+    w = inputs.make_config(config, B=B, T=T, rows_per_table=997)
+    lay = w.layers[0]
+    ref, hot = hot_sets(w, lay, max(1, B * T // 3), seed=5)
+    L = eg.Layer(lay, w.dtype, DEV)
+    L.set_hot(hot)
+    tok = torch.from_numpy(w.tokens).to(DEV)
+    e = eg.rows_buffer(B, T, L, DEV)
+    eg.retrieve(tok, L, e)
+    H1 = eg.to_device(w.H, w.dtype, DEV)
+    H2 = H1.clone()
+    a1, y1 = eg.forward(tok, H1, L, want_alpha=True, want_y=True)
+    a2, y2 = eg.forward_retrieved(tok, e, H2, L, want_alpha=True, want_y=True)
+    torch.cuda.synchronize()
+    bits = (lambda x: x.view(torch.int16)) if w.dtype == "bf16" else (lambda x: x.view(torch.int32))
+    assert torch.equal(bits(H1), bits(H2)) and torch.equal(a1, a2) and torch.equal(y1, y2)
+    out = "bf16" if w.dtype == "bf16" else "f32"
+    ref_e, idx = two_tier_e(w, lay, ref, out)
+    assert np.array_equal(to_f64(e).reshape(ref_e.shape), ref_e)
+    assert np.any(idx >= 0)
+    r = orc.forward(w.tokens, w.H, lay, w.dtype, hot=ref)
+    chk = check_f32_layer if w.dtype == "f32" else check_bf16_layer
+    chk(to_f64(a1), r["alpha"], to_f64(y1), r["Y"], to_f64(H1), orc.storage_to_f64(w.H, w.dtype), tag="hot")
+
+
+def test_edge_cases():
+    log("hot edge cases")
+    w = inputs.make_config(1, B=2, T=200, rows_per_table=997)
+    lay = w.layers[0]
+    L = eg.Layer(lay, w.dtype, DEV)
+    tok = torch.from_numpy(w.tokens).to(DEV)
+    cold = eg.rows_buffer(2, 200, L, DEV)
+    eg.retrieve(tok, L, cold)
+    cases = {
+        "order 3 only, one n-gram": dict(n_hot=1, orders=[3], absent=0),
+        "every n-gram hot": dict(n_hot=10 ** 6, absent=0),
+        "no hot n-gram occurs": dict(n_hot=0, absent=50),
+    }
+    for name, kw in cases.items():
+        log(f"  {name}")
+        ref, hot = hot_sets(w, lay, seed=3, **kw)
+        L.set_hot(hot)
+        e = eg.rows_buffer(2, 200, L, DEV)
+        eg.retrieve(tok, L, e)
+        torch.cuda.synchronize()
+        ref_e, idx = two_tier_e(w, lay, ref, "bf16")
+        assert np.array_equal(to_f64(e).reshape(ref_e.shape), ref_e), name
+        if name.startswith("every"):
+            assert np.all(idx >= 0)
+        if name.startswith("no hot"):
+            assert np.all(idx < 0) and torch.equal(e.view(torch.int16), cold.view(torch.int16))
+    eg.retrieve(tok[:, :0].contiguous(), L, e)        # empty call: no-op
+    L.set_hot(None)
+
+
+def test_mxfp8_rows_and_access_counts():
+    log("hot mxfp8 rows + access counts")
+    w = inputs.make_config(1, B=2, T=150, rows_per_table=997)
+    lay = w.layers[0]
+    ref, hot = hot_sets(w, lay, 100, seed=8)
+    L = eg.Layer(lay, "bf16", DEV, mxfp8=True)
+    L.set_hot(hot)
+    counts = torch.zeros(lay.tables.total_rows, dtype=torch.int32, device=DEV)
+    L.set_access_counts(counts)
+    tok = torch.from_numpy(w.tokens).to(DEV)
+    e = eg.rows_buffer(2, 150, L, DEV)
+    eg.retrieve(tok, L, e)
+    torch.cuda.synchronize()
+    ref_e, idx = two_tier_e(w, lay, ref, "bf16")
+    rq, rs = orc.quantize_mxfp8(ref_e.reshape(300, -1))
+    got = e.cpu().numpy()
+    n = rq.size
+    assert np.array_equal(got[:n].reshape(rq.shape), rq)
+    assert np.array_equal(got[n:n + n // 32].reshape(rs.shape), rs)
+    # counts: one per cold row read; a hot n-gram reads none of its K rows
+    hp, tab = lay.hash, lay.tables
+    z = orc.hash_indices(w.tokens, hp.proj, hp.mult, hp.prime, hp.max_n, hp.heads)
+    order_of_table = np.repeat(np.arange(hp.max_n - 1), hp.heads)
+    cold = idx[:, :, order_of_table] < 0
+    want = np.bincount((z + tab.row_offset)[cold], minlength=tab.total_rows)
+    assert np.array_equal(counts.cpu().numpy().view(np.uint32).astype(np.int64), want)
+    assert 0 < cold.sum() < cold.size
+
+
+def test_chunked_prefill_with_state():
+    """The hot lookup across a chunk boundary reads the decode state's ids."""
+    log("hot chunked prefill")
+    w = inputs.make_config(1, B=3, T=96, rows_per_table=997)
+    lay = w.layers[0]
+    ref, hot = hot_sets(w, lay, 150, seed=12)
+    L = eg.Layer(lay, w.dtype, DEV)
+    L.set_hot(hot)
+    span = (lay.kernel_w - 1) * lay.dilation
+    st = eg.DecodeState(3, lay.hash.max_n, lay.branches, span, lay.d, DEV)
+    H = eg.to_device(w.H, w.dtype, DEV)
+    tok = torch.from_numpy(w.tokens).to(DEV)
+    oracle_state = orc.new_state(3, lay.hash.max_n, lay.branches, span, lay.d)
+    for lo, hi in ((0, 37), (37, 38), (38, 96)):
+        t_chunk = tok[:, lo:hi].contiguous()
+        e = eg.rows_buffer(3, hi - lo, L, DEV)
+        eg.retrieve(t_chunk, L, e, state=st)
+        Hc = H[:, lo:hi].contiguous()
+        a, y = eg.forward_retrieved(t_chunk, e, Hc, L, state=st, want_alpha=True, want_y=True)
+        torch.cuda.synchronize()
+        ref_e, _ = two_tier_e(w, lay, ref, "bf16", tokens=w.tokens[:, lo:hi], hist=oracle_state["ids"])
+        assert np.array_equal(to_f64(e).reshape(ref_e.shape), ref_e), (lo, hi)
+        r = orc.forward(w.tokens[:, lo:hi], w.H[:, lo:hi], lay, w.dtype, state=oracle_state, hot=ref)
+        oracle_state = r["state"]
+        check_bf16_layer(to_f64(a), r["alpha"], to_f64(y), r["Y"], to_f64(Hc),
+                         orc.storage_to_f64(w.H[:, lo:hi], w.dtype), tag=f"chunk {lo}:{hi}")
+
+
+def test_full_size_single_branch_sampled():
+    """T = 4096 with the full 10.3M-row tables and the benchmark's hot tier:
+    100,000 2-grams and 100,000 3-grams, the most frequent of a 2M-token
+    warm-up stream.  Every hot lookup and the rows of sampled windows are
+    bit-exact; the forward matches the oracle on those windows."""
+    log("hot full size: inputs")
+    w = inputs.make_config(1)
+    lay = w.layers[0]
+    hp, tab = lay.hash, lay.tables
+    warm = inputs.hot_warmup_tokens(1, 0)
+    xc = hp.proj[warm]
+    keys = {n: inputs.frequent_ngrams(xc, n, 100_000) for n in (2, 3)}
+    rows = {n: inputs.hot_rows(1, 0, n, 100_000, hp.heads * tab.dim, "bf16") for n in (2, 3)}
+    hot = eg.HotTier(keys, {n: eg.to_device(r, "bf16", DEV) for n, r in rows.items()}, device=DEV)
+    L = eg.Layer(lay, "bf16", DEV)
+    L.set_hot(hot)
+    tok = torch.from_numpy(w.tokens).to(DEV)
+    log("hot full size: lookup + retrieve + forward")
+    got_idx = eg.hot_lookup(tok, L, hot).cpu().numpy()
+    e = eg.rows_buffer(1, 4096, L, DEV)
+    eg.retrieve(tok, L, e)
+    H = eg.to_device(w.H, "bf16", DEV)
+    alpha, y = eg.forward(tok, H, L, want_alpha=True, want_y=True)
+    torch.cuda.synchronize()
+    ref = {"keys": {n: [tuple(int(v) for v in r) for r in k] for n, k in keys.items()}, "rows": rows}
+    log("hot full size: oracle")
+    idx = orc.hot_lookup(w.tokens, hp.proj, hp.max_n, ref["keys"])
+    assert np.array_equal(got_idx, idx)
+    hit = (idx >= 0).mean(axis=(0, 1))
+    log(f"  hit rate per order {hit}")
+    assert np.all(hit > 0.05)
+    starts = [0, 1000, 2500, 4096 - 64]
+    h_in = orc.storage_to_f64(w.H, "bf16")
+    e_g = e.view(1, 4096, -1)
+    for s in starts:
+        lo = max(0, s - 11)
+        sl = slice(lo, s + 64)
+        r = orc.forward(w.tokens[:, sl], w.H[:, sl], lay, "bf16", hot=ref)
+        k = s - lo
+        assert np.array_equal(to_f64(e_g[:, s:s + 64]), r["e"][:, k:]), s
+        check_bf16_layer(to_f64(alpha[:, s:s + 64]), r["alpha"][:, k:], to_f64(y[:, s:s + 64]), r["Y"][:, k:],
+                         to_f64(H[:, s:s + 64]), h_in[:, s:s + 64], tag=f"hot full s{s}")
