@@ -233,3 +233,38 @@ def test_full_size_single_branch_sampled():
         assert np.array_equal(to_f64(e_g[:, s:s + 64]), r["e"][:, k:]), s
         check_bf16_layer(to_f64(alpha[:, s:s + 64]), r["alpha"][:, k:], to_f64(y[:, s:s + 64]), r["Y"][:, k:],
                          to_f64(H[:, s:s + 64]), h_in[:, s:s + 64], tag=f"hot full s{s}")
+
+
+@pytest.mark.parametrize("B,T", [(1, 2049), (3, 2731)])
+def test_gather_items_per_thread_ragged(B, T):
+    """Sizes where a thread serves 2 (2049 tokens) or 4 (8193 tokens)
+    consecutive tokens with a ragged last group and groups that straddle
+    sequence boundaries: the rows (bf16 and MXFP8, cold and two-tier) are the
+    oracle's, bit for bit."""
+    log(f"gather items ragged B={B} T={T}")
+    w = inputs.make_config(1, B=B, T=T, rows_per_table=997)
+    lay = w.layers[0]
+    hp, tab = lay.hash, lay.tables
+    tok = torch.from_numpy(w.tokens).to(DEV)
+    ref_hot, hot = hot_sets(w, lay, 300, seed=21)
+    z = orc.hash_indices(w.tokens, hp.proj, hp.mult, hp.prime, hp.max_n, hp.heads)
+    for mx in (False, True):
+        L = eg.Layer(lay, "bf16", DEV, mxfp8=mx)
+        for use_hot in (False, True):
+            L.set_hot(hot if use_hot else None)
+            e = eg.rows_buffer(B, T, L, DEV)
+            eg.retrieve(tok, L, e)
+            torch.cuda.synchronize()
+            if use_hot:
+                ref, idx = two_tier_e(w, lay, ref_hot, "bf16")
+                assert np.any(idx >= 0)
+            else:
+                ref = orc.gather(z, tab.rows, tab.dtype, tab.row_offset, tab.dim, tab.scale, out_dtype="bf16")
+            ref = ref.reshape(B * T, -1)
+            if mx:
+                rq, rs = orc.quantize_mxfp8(ref)
+                got = e.cpu().numpy()
+                assert np.array_equal(got[:rq.size].reshape(rq.shape), rq), (mx, use_hot)
+                assert np.array_equal(got[rq.size:rq.size + rs.size].reshape(rs.shape), rs), (mx, use_hot)
+            else:
+                assert np.array_equal(to_f64(e).reshape(ref.shape), ref), (mx, use_hot)
