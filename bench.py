@@ -26,6 +26,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -59,6 +61,9 @@ def parse():
     ap.add_argument("--hbm-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                          "run with --copy-calibration-mib into the per-kernel HBM bytes table and exit")
+    ap.add_argument("--no-controls", action="store_true",
+                    help="configs 1-2: skip the control measurements (a cold-cache pass that overwrites 512 MiB "
+                         "between steps, and the gather over uniform tokens)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB device to device three times "
                          "(a plain copy kernel of known size for scaling HBM byte counters)")
@@ -540,10 +545,14 @@ def inputs_zipf_like(tokens, rng):
     return np.ascontiguousarray(out)
 
 
-def measured_peaks(torch):
+def measured_peaks(torch, shape=None):
     """The box's practical peaks, re-measured in the same run: a 1 GiB
     device-to-device copy (bytes read + written per second) and a large bf16
-    matmul through torch (hipBLASLt), 8192 x 8192 x 8192."""
+    matmul through torch (hipBLASLt), 8192 x 8192 x 8192, with its operands in
+    the layer's layout (both K-contiguous: C = A B^T) and, for reference, in
+    the plain layout (C = A B).  shape = (tokens, N, K) adds the library's
+    matmul at the layer's own product shape, timed as a replayed graph of 20
+    back-to-back calls."""
     main = torch.cuda.current_stream()
 
     def timed(fn, reps):
@@ -566,11 +575,30 @@ def measured_peaks(torch):
     m = 8192
     a = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
     b = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
-    t_mm = timed(lambda: torch.matmul(a, b), 10)
-    del a, b
-    return {"hbm_copy_GBps": round(2 * n / t_copy / 1e9, 1),
-            "bf16_gemm_TFLOPs": round(2.0 * m ** 3 / t_mm / 1e12, 1),
-            "how": "1 GiB device-to-device copy (read + write bytes); 8192^3 bf16 torch.matmul (hipBLASLt)"}
+    bt = b.t()
+    t_nt = timed(lambda: torch.matmul(a, bt), 10)
+    t_nn = timed(lambda: torch.matmul(a, b), 10)
+    del a, b, bt
+    out = {"hbm_copy_GBps": round(2 * n / t_copy / 1e9, 1),
+           "bf16_gemm_TFLOPs": round(2.0 * m ** 3 / t_nt / 1e12, 1),
+           "bf16_gemm_plain_layout_TFLOPs": round(2.0 * m ** 3 / t_nn / 1e12, 1),
+           "how": "1 GiB device-to-device copy (read + write bytes); 8192^3 bf16 torch.matmul (hipBLASLt), "
+                  "A B^T with both operands K-contiguous as in the layer, and A B"}
+    if shape is not None:
+        M, N, K = shape
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        bt = torch.randn(N, K, device="cuda", dtype=torch.bfloat16).t()
+        for _ in range(3):
+            torch.matmul(a, bt)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(20):
+                torch.matmul(a, bt)
+        t = timed(g.replay, 3) / 20
+        out["library_gemm_at_layer_shape"] = {"M": M, "N": N, "K": K, "us": round(t * 1e6, 2),
+                                              "TFLOPs": round(2.0 * M * N * K / t / 1e12, 1)}
+        del a, bt, g
+    return out
 
 
 def main():
@@ -631,17 +659,29 @@ def main():
 
     # per-kernel durations: HIP events that the library records on the launch
     # stream around each kernel of the same forward calls (eager launches)
+    # (the same loop also times each eager layer call with events on the stream)
     eg.profile_enable(True)
-    acc, cnt = {}, {}
+    samples, layer_ms = {}, []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for it in range(args.warmup + args.steps):
         for c in calls:
+            e0.record(stream)
             c()
+            e1.record(stream)
             for name, t in eg.profile_read():
                 if it >= args.warmup:
-                    acc[name] = acc.get(name, 0.0) + t
-                    cnt[name] = cnt.get(name, 0) + 1
+                    samples.setdefault(name, []).append(t)
+            if it >= args.warmup:
+                e1.synchronize()
+                layer_ms.append(e0.elapsed_time(e1))
     eg.profile_enable(False)
-    kernel_ms = {k: acc[k] / cnt[k] for k in acc}
+    kernel_ms = {k: sum(v) / len(v) for k, v in samples.items()}
+
+    def pcts(v):
+        q = np.percentile(np.asarray(v) * 1000.0, [10, 50, 90])
+        return [round(float(x), 2) for x in q]
+    kernel_us_p10_p50_p90 = {k: pcts(v) for k, v in samples.items()}
+    layer_us_p10_p50_p90 = pcts(layer_ms)
 
     units = kernel_units(n_tok, lays[0], w.dtype, extra["_hot"][3] if "_hot" in extra else None)
     rates = {}
@@ -661,7 +701,9 @@ def main():
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(rates[dominant] / PEAK_HBM_GBPS, 4),
                 "traffic": traffic_for(w.name, dominant), "units_per_launch": amount}
     gather_gbps = rates.get("gather_kernel<hashed>", rates.get("gather_kernel<hashed,hot>"))
-    peaks = measured_peaks(torch)
+    lay0 = lays[0]
+    peaks = measured_peaks(torch, (n_tok // len(calls), (1 + lay0.branches) * lay0.d, lay0.d_mem)
+                           if args.config in (1, 2) else None)
     roof["frac_of_measured_peak"] = round(
         roof["achieved"] / (peaks["bf16_gemm_TFLOPs"] if kind == "mfma" else peaks["hbm_copy_GBps"]), 4)
 
@@ -694,6 +736,8 @@ def main():
         "timing": f"HIP graph replay, {per_graph} steps per graph" if graph is not None else "eager launches",
         "gather_GBps": None if gather_gbps is None else round(gather_gbps, 1),
         "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
+        "kernel_us_p10_p50_p90": kernel_us_p10_p50_p90,
+        "eager_layer_call_us_p10_p50_p90": layer_us_p10_p50_p90,
         "kernel_rate": {k: round(v, 2) for k, v in rates.items()},
         "roofline": roof,
         "measured_peaks": peaks,
@@ -702,6 +746,10 @@ def main():
     for k, v in extra.items():
         if not k.startswith("_"):
             out[k] = v
+    if args.config in (1, 2) and not args.no_controls:
+        out["controls"] = control_report(torch, eg, inputs, args, w, lays[0], extra["_pipe"], units)
+    if args.config == 3:
+        out["tokens_per_s_per_layer"] = round(n_tok * len(calls) / (ms * 1e-3), 1)
     if args.overlap and args.config in (1, 2):
         out["retrieval_overlap"] = overlap_report(torch, eg, w, lays[0], args.steps, args.warmup)
     if args.realtime_lfu and args.config == 4:
@@ -717,6 +765,50 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+
+
+def control_report(torch, eg, inputs, args, w, lay, pipe, units, steps=20):
+    """Two controls of the measured kernel rates.
+    cold: before every eager layer call a 512 MiB buffer is overwritten (more
+    than the 256 MB Infinity Cache), so tables, W and e start outside the
+    on-chip caches; per-kernel times from the dispatch events.
+    uniform tokens: the gather alone over tokens drawn uniformly from the raw
+    vocabulary instead of Zipf(1.1), i.e. with almost no row reuse."""
+    Ls, tok, H = pipe
+    L = Ls[0]
+    ws = torch.empty(eg.forward_workspace(w.B, w.T, L), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    eg.profile_enable(True)
+    cold = {}
+    for it in range(3 + steps):
+        flush.fill_(it & 0xff)
+        eg.forward(tok, H, L, ws=ws)
+        for name, t in eg.profile_read():
+            if it >= 3:
+                cold.setdefault(name, []).append(t)
+    del flush
+    utok = torch.from_numpy(inputs.uniform_control_tokens(w.config, w.B, w.T, lay.hash.vocab)).to("cuda")
+    e = eg.rows_buffer(w.B, w.T, L, "cuda")
+    uni = []
+    for it in range(3 + steps):
+        eg.retrieve(utok, L, e)
+        for name, t in eg.profile_read():
+            if it >= 3:
+                uni.append(t)
+    eg.profile_enable(False)
+    cold_ms = {k: sum(v) / len(v) for k, v in cold.items()}
+
+    def rate(name, ms):
+        kind, amount = units[name]
+        return round(amount / (ms * 1e-3) / (1e9 if kind == "hbm" else 1e12), 1)
+    g_name = next(k for k in cold_ms if k.startswith("gather"))
+    uni_ms = sum(uni) / len(uni)
+    return {"cold_kernel_us": {k: round(v * 1000, 2) for k, v in cold_ms.items()},
+            "cold_rate": {k: rate(k, v) for k, v in cold_ms.items() if k in units},
+            "uniform_tokens_gather_us": round(uni_ms * 1000, 2),
+            "uniform_tokens_gather_GBps": rate(g_name, uni_ms),
+            "how": "cold: a 512 MiB buffer overwritten before each of 20 eager layer calls; uniform: "
+                   "engram_retrieve over seeded uniform raw ids, 20 calls; rates are algorithmic units per second"}
 
 
 def cpu_baseline(w, budget_s, hot=None):

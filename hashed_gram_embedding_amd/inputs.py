@@ -30,7 +30,7 @@ from typing import List, Optional
 import numpy as np
 
 # stream ids inside SeedSequence([config, layer, stream])
-S_TOKENS, S_PROJ, S_MULT, S_TABLES, S_H, S_W, S_CONV, S_LFU, S_CONTEXT, S_HOT = range(10)
+S_TOKENS, S_PROJ, S_MULT, S_TABLES, S_H, S_W, S_CONV, S_LFU, S_CONTEXT, S_HOT, S_UNIFORM = range(11)
 
 F32, BF16, I8 = "f32", "bf16", "i8"
 
@@ -352,6 +352,12 @@ def hash_inputs_for(config: int, layer: int = 0) -> HashInputs:
         return _hash_inputs(0, 0, 1000, 770, 3, 2, 1000, [1009, 1013, 1019, 1021])
     start = C4_PRIME_START if config == 4 else C1_PRIME_START
     return _hash_inputs(config, layer, 128_000, 98_560, 3, 8, start)
+
+
+def uniform_control_tokens(config: int, B: int, T: int, vocab: int = 128_000) -> np.ndarray:
+    """Raw ids drawn uniformly from the vocabulary, [B, T]: the no-reuse
+    control of the gather's bandwidth."""
+    return rng_for(config, 0, S_UNIFORM).integers(0, vocab, size=(B, T), dtype=np.int32)
 
 
 def lfu_warmup_tokens(config: int, layer: int, n: int = 1 << 24, vocab: int = 128_000) -> np.ndarray:
