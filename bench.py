@@ -70,27 +70,36 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_units(n_tok, lay, hdtype, hot_hit=None):
+def kernel_units(n_tok, lay, hdtype, hot_hit=None, mx=False):
     """Algorithmic bytes (HBM-bound kernels) or flops (matrix-core kernels)
     per launch of each kernel of one layer forward over n_tok tokens, keyed by
     the kernel names the library reports.  hot_hit: the fraction of hot
     n-grams per order when the Engram-Nine tier is attached (a hit reads one
     pilot, one 32-byte slot and its K*dim row; a miss reads its K cold rows
-    after the same pilot and slot)."""
+    after the same pilot and slot).  mx: the layer runs the MXFP8 product, so
+    the gather writes one E4M3 code per element plus a scale byte per 32."""
     nt = lay.hash.n_tables
     dim = lay.tables.dim
     d, M = lay.d, lay.branches
     es = 2 if hdtype == "bf16" else 4
     i8 = lay.tables.dtype == "i8"
     row_bytes = dim * (1 if i8 else es) + (4 if i8 else 0)
+    e_bytes = dim + dim // 32 if mx else dim * es     # gathered bytes per row
     d_mem = nt * dim
     fused = hdtype == "bf16" and d % 128 == 0
     n_stat = (1 + M) * d // 128 if fused else 1 + M
-    flops = 2.0 * n_tok * (1 + M) * d * d_mem
+    N = (1 + M) * d
+    flops = 2.0 * n_tok * N * d_mem
+    # Below the matrix cores' ridge (the library's small-batch projection, used
+    # while fewer than 128 tiles of 256 tokens x 128 features exist) the
+    # projection is bound by reading W: W, e and h in, v and statistics out.
+    small = fused and ((n_tok + 255) // 256) * (N // 128) < 128
+    proj = ("hbm", N * d_mem * es + n_tok * (d_mem * es + M * d * es + d * 4 + 16 * N // 64)) if small \
+        else ("mfma", flops)
     units = {
         # token ids in; rows in; e out
-        "gather_kernel<hashed>": ("hbm", n_tok * (4 + nt * (row_bytes + dim * es))),
-        "proj_gate_kernel": ("mfma", flops),
+        "gather_kernel<hashed>": ("hbm", n_tok * (4 + nt * (row_bytes + e_bytes))),
+        "proj_gate_kernel": proj,
         "gemm_kernel": ("mfma", flops),
         # h, k, v in; statistics out
         "gate_stats_kernel": ("hbm", n_tok * (M * 2 * d * 4 + d * 4 + M * d * es + 16 * n_stat)),
@@ -101,7 +110,7 @@ def kernel_units(n_tok, lay, hdtype, hot_hit=None):
     }
     if hot_hit is not None:
         K = lay.hash.heads
-        per_tok = 4 + nt * dim * es
+        per_tok = 4 + nt * e_bytes
         for h in hot_hit:
             per_tok += 36 + h * K * dim * es + (1 - h) * K * row_bytes
         units["gather_kernel<hashed,hot>"] = ("hbm", n_tok * per_tok)
@@ -607,7 +616,8 @@ def main():
         from hashed_gram_embedding_amd import inputs
         if args.copy_calibration_mib <= 0:
             raise SystemExit("--hbm-summary needs --copy-calibration-mib: the size of the calibration copy")
-        hbm_summary(args.hbm_summary[0], args.hbm_summary[1], inputs.CONFIG_NAMES[args.config],
+        hbm_summary(args.hbm_summary[0], args.hbm_summary[1],
+                    inputs.CONFIG_NAMES[args.config] + ("-mxfp8" if args.mxfp8 else ""),
                     args.copy_calibration_mib << 20)
         return
     if args.gpus != 1:
@@ -683,7 +693,8 @@ def main():
     kernel_us_p10_p50_p90 = {k: pcts(v) for k, v in samples.items()}
     layer_us_p10_p50_p90 = pcts(layer_ms)
 
-    units = kernel_units(n_tok, lays[0], w.dtype, extra["_hot"][3] if "_hot" in extra else None)
+    units = kernel_units(n_tok, lays[0], w.dtype, extra["_hot"][3] if "_hot" in extra else None,
+                         mx=args.mxfp8 and args.config in (1, 2))
     rates = {}
     for k, t in kernel_ms.items():
         if k in units:
@@ -695,7 +706,8 @@ def main():
         peak = PEAK_FP8_TFLOPS if args.mxfp8 else PEAK_BF16_TFLOPS
         roof = {"bound": "mfma", "kernel": dominant, "achieved": round(rates[dominant], 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(rates[dominant] / peak, 4),
-                "traffic": traffic_for(w.name, dominant), "units_per_launch": amount}
+                "traffic": traffic_for(w.name + ("-mxfp8" if args.mxfp8 else ""), dominant),
+                "units_per_launch": amount}
     else:
         roof = {"bound": "hbm", "kernel": dominant, "achieved": round(rates[dominant], 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(rates[dominant] / PEAK_HBM_GBPS, 4),
@@ -704,8 +716,10 @@ def main():
     lay0 = lays[0]
     peaks = measured_peaks(torch, (n_tok // len(calls), (1 + lay0.branches) * lay0.d, lay0.d_mem)
                            if args.config in (1, 2) else None)
-    roof["frac_of_measured_peak"] = round(
-        roof["achieved"] / (peaks["bf16_gemm_TFLOPs"] if kind == "mfma" else peaks["hbm_copy_GBps"]), 4)
+    # (no FP8 matmul is re-measured, so an MXFP8 product has no measured peak)
+    ref = None if (kind == "mfma" and args.mxfp8) else \
+        (peaks["bf16_gemm_TFLOPs"] if kind == "mfma" else peaks["hbm_copy_GBps"])
+    roof["frac_of_measured_peak"] = None if ref is None else round(roof["achieved"] / ref, 4)
 
     cpu = None
     if not args.no_cpu_baseline and args.config in (1, 2):
