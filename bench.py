@@ -432,6 +432,22 @@ def pipelined_report(torch, eg, w, pipe, steps):
             retrieve_all(par)
             compute_all(par)
 
+    def compute_only():
+        for par in (0, 1):
+            compute_all(par)
+
+    def fused():
+        # each layer's compute carries the next retrieval in its conv launch
+        # (engram_forward_retrieved_prefetch): the next layer's rows of the same
+        # batch, and after the last layer the first layer's rows of the next batch
+        for par in (0, 1):
+            for li, L in enumerate(Ls):
+                if li + 1 < len(Ls):
+                    nl, nt, ne = Ls[li + 1], toks[par], e[par][li + 1]
+                else:
+                    nl, nt, ne = Ls[0], toks[1 - par], e[1 - par][0]
+                eg.forward_retrieved_prefetch(toks[par], e[par][li], H, L, nt, ne, ws=ws, next_layer=nl)
+
     def timed_graph(fn, reps):
         for _ in range(2):
             fn()
@@ -470,12 +486,22 @@ def pipelined_report(torch, eg, w, pipe, steps):
     t_seq = timed_graph(seq, reps)
     t_pipe_eager = timed_eager(cycle, reps)
     t_seq_eager = timed_eager(seq, reps)
+    t_fused = timed_graph(fused, reps)
+    t_compute = timed_graph(compute_only, reps)
+    t_retr = t_seq - t_compute
     return {"layers_per_step": len(Ls), "sequential_us_per_step": round(t_seq, 2),
             "pipelined_us_per_step": round(t_pipe, 2),
             "pipelined_tokens_per_s": round(B * T / (t_pipe * 1e-6), 1),
             "eager_sequential_us_per_step": round(t_seq_eager, 2), "eager_pipelined_us_per_step": round(t_pipe_eager, 2),
+            "fused_us_per_step": round(t_fused, 2), "fused_tokens_per_s": round(B * T / (t_fused * 1e-6), 1),
+            "compute_only_us_per_step": round(t_compute, 2),
+            "fused_retrieval_hidden_fraction": round((t_seq - t_fused) / t_retr, 3) if t_retr > 0 else None,
             "how": "retrieval of step s+1 (all layers) on a second stream during the compute of step s; "
-                   "two alternating token batches; HIP graphs of two-step cycles"}
+                   "two alternating token batches; HIP graphs of two-step cycles.  fused: the same two "
+                   "batches, one stream, each layer call carrying the next retrieval (the next layer's rows, "
+                   "or after the last layer the next batch's) inside its conv launch "
+                   "(engram_forward_retrieved_prefetch); hidden fraction = (sequential - fused) "
+                   "/ (sequential - compute only)"}
 
 
 def realtime_lfu_report(torch, eg, inputs, w, pipe, rounds=4, steps_per_round=8):

@@ -287,10 +287,12 @@ size_t forward_ws_bytes(int64_t n_tok, const engram_layer* L) {
 
 // Steps 6-8 once the gate statistics are in `stats`: conv (+ residual), then
 // the decode-state commit.
+// next: a hashed gather of another batch to run with this conv (in the same
+// launch where a fused form exists, else right after it), or null.
 engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdtype, const float4* stats, int qv,
                               int qk, int64_t B, int64_t T, const engram::GateConvArgs& g, engram_decode_state* st,
                               const int32_t* tokens, const int32_t* proj, int32_t max_n, float* alpha_out,
-                              float* gamma, float* y_out, hipStream_t s) {
+                              float* gamma, float* y_out, hipStream_t s, const engram::GatherJob* next = nullptr) {
   engram::ConvArgs ca{};
   ca.H = H;
   ca.v = v;
@@ -307,9 +309,28 @@ engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdty
   ca.alpha_out = alpha_out;
   ca.gamma_out = gamma;
   ca.y_out = y_out;
-  prof_mark(s, "conv_kernel");
-  engram_status r = hip_status(engram::launch_conv(ca, vdtype, s), "conv launch");
-  if (r != ENGRAM_OK) return r;
+  engram_status r;
+  bool fused = false;
+  if (next != nullptr && st == nullptr) {
+    prof_mark(s, "conv_gather_kernel");
+    const hipError_t e = engram::launch_conv_gather(ca, vdtype, *next, s);
+    if (e != hipErrorNotSupported) {
+      if ((r = hip_status(e, "conv+gather launch")) != ENGRAM_OK) return r;
+      fused = true;
+    }
+  }
+  if (!fused) {
+    prof_mark(s, "conv_kernel");
+    if ((r = hip_status(engram::launch_conv(ca, vdtype, s), "conv launch")) != ENGRAM_OK) return r;
+    if (next != nullptr) {
+      const engram::HashSrc& hs = next->hs;
+      prof_mark(s, next->hot ? "gather_kernel<hashed,hot>" : "gather_kernel<hashed>");
+      r = hip_status(engram::launch_hash_gather(hs.tokens, next->n_tok / hs.T, hs.T, hs.hist, hs.proj, hs.a, next->ta,
+                                                next->hot ? &hs.hot : nullptr, next->out_dtype, next->e, s),
+                     "hash+gather launch");
+      if (r != ENGRAM_OK) return r;
+    }
+  }
   if (st != nullptr) {
     engram::StateArgs sa{tokens != nullptr ? st->ids : nullptr, st->conv, st->pos};
     prof_mark(s, "state_commit_kernel");
@@ -513,7 +534,8 @@ engram_status run_retrieve(const int32_t* tokens, int64_t B, int64_t T, const en
 // Steps 5-8 on gathered rows e.
 engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t B, int64_t T,
                           const engram_layer* L, engram::GateConvArgs g, engram_decode_state* st,
-                          float* alpha_out, float* y_out, const ComputeWorkspace& f, hipStream_t stream) {
+                          float* alpha_out, float* y_out, const ComputeWorkspace& f, hipStream_t stream,
+                          const engram::GatherJob* next = nullptr) {
   const int64_t n_tok = B * T;
   const int64_t d_mem = static_cast<int64_t>(L->tables.n_tables) * L->tables.dim;
   const int M = g.branches, d = g.d;
@@ -542,7 +564,7 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
     if (r != ENGRAM_OK) return r;
     const int q = d / engram::proj_gate_tile_f(n_tok, static_cast<int>(n_out), d, mx);
     return run_conv_commit(H, f.kv, d, ENGRAM_F32, f.stats, q, q, B, T, g, st, tokens, L->hash.proj,
-                           L->hash.max_n, alpha_out, f.gamma, y_out, stream);
+                           L->hash.max_n, alpha_out, f.gamma, y_out, stream, next);
   }
   // Step 5 into float32 projections, then whole-row gate statistics
   prof_mark(stream, "gemm_kernel");
@@ -554,7 +576,7 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
   r = hip_status(engram::launch_gate_stats(H, f.kv, n_tok, g, f.stats, stream), "gate statistics launch");
   if (r != ENGRAM_OK) return r;
   return run_conv_commit(H, f.kv, n_out, ENGRAM_F32, f.stats, 1, 1, B, T, g, st, tokens, L->hash.proj,
-                         L->hash.max_n, alpha_out, f.gamma, y_out, stream);
+                         L->hash.max_n, alpha_out, f.gamma, y_out, stream, next);
 }
 
 }  // namespace
@@ -635,6 +657,69 @@ ENGRAM_API engram_status engram_forward_retrieved(const int32_t* tokens, const v
   const ComputeWorkspace f = carve_compute(c, n_tok, L);
   prof_begin();
   return run_compute(tokens, e, H, B, T, L, g, st, alpha_out, y_out, f, stream);
+}
+
+ENGRAM_API engram_status engram_forward_retrieved_prefetch(const int32_t* tokens, const void* e, void* H, int64_t B,
+                                                           int64_t T, const engram_layer* L, float* alpha_out,
+                                                           float* y_out, void* ws, size_t ws_bytes,
+                                                           const engram_layer* next_L, const int32_t* next_tokens,
+                                                           int64_t next_B, int64_t next_T, void* next_e,
+                                                           hipStream_t stream) {
+  engram::HashArgs ha;
+  engram::TableArgs ta;
+  engram::GateConvArgs g;
+  engram_status r = check_call("forward_retrieved_prefetch", L, nullptr, false, B, T, &ha, &ta, &g);
+  if (r != ENGRAM_OK) return r;
+  // the next retrieval's layer (its hash, tables and row format)
+  const engram_layer* NL = next_L != nullptr ? next_L : L;
+  engram::HashArgs nha;
+  engram::TableArgs nta;
+  engram::GateConvArgs ng;
+  if (NL != L && (r = check_layer(NL, &nha, &nta, &ng)) != ENGRAM_OK) return r;
+  if (NL == L) {
+    nha = ha;
+    nta = ta;
+    ng = g;
+  }
+  if (next_B < 0 || next_T < 0 || next_T > INT32_MAX || next_B > 65535)
+    return fail(ENGRAM_EINVAL, "forward_retrieved_prefetch: next_B and next_T outside [0, 65535] x [0, 2^31)");
+  const int64_t n_tok = B * T, n_next = next_B * next_T;
+  if (n_next > 0) {
+    if (next_tokens == nullptr || next_e == nullptr)
+      return fail(ENGRAM_EINVAL, "forward_retrieved_prefetch: next_tokens and next_e must be non-NULL");
+    if (!aligned(next_e, 16)) return fail(ENGRAM_EINVAL, "forward_retrieved_prefetch: next_e must be 16-byte aligned");
+    if (next_e == e) return fail(ENGRAM_EINVAL, "forward_retrieved_prefetch: next_e must not be e");
+  }
+  engram::GatherJob job{};
+  job.ta = nta;
+  engram::HotArgs hot;
+  bool any_hot;
+  if ((r = check_hot(NL->hot, &NL->hash, &NL->tables, &hot, &any_hot)) != ENGRAM_OK) return r;
+  job.hs = engram::HashSrc{next_tokens, NL->hash.proj, nullptr, next_T, nha, hot};
+  job.e = next_e;
+  job.n_tok = static_cast<uint32_t>(n_next);
+  job.out_dtype = NL->w_mx != nullptr ? engram::kGatherOutMXFP8 : ng.hdtype;
+  job.hot = any_hot;
+  if (n_next >= (1ll << 31)) return fail(ENGRAM_EUNSUPPORTED, "forward_retrieved_prefetch: next batch too large");
+  if (n_tok == 0) {
+    if (n_next == 0) return ENGRAM_OK;
+    prof_begin();
+    return run_retrieve(next_tokens, next_B, next_T, NL, nha, nta, ng.hdtype, nullptr, next_e, stream);
+  }
+  if (e == nullptr || H == nullptr)
+    return fail(ENGRAM_EINVAL, "forward_retrieved_prefetch: e and H must be non-NULL");
+  if (!aligned(H, 16) || !aligned(e, 16))
+    return fail(ENGRAM_EINVAL, "forward_retrieved_prefetch: H and e must be 16-byte aligned");
+  if (y_out != nullptr && !aligned(y_out, 16))
+    return fail(ENGRAM_EINVAL, "forward_retrieved_prefetch: y_out must be 16-byte aligned");
+  const size_t need = compute_ws_bytes(n_tok, L);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(ENGRAM_EINVAL, "forward_retrieved_prefetch: workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                need, ws_bytes);
+  Carve c{static_cast<char*>(ws)};
+  const ComputeWorkspace f = carve_compute(c, n_tok, L);
+  prof_begin();
+  return run_compute(tokens, e, H, B, T, L, g, nullptr, alpha_out, y_out, f, stream, n_next > 0 ? &job : nullptr);
 }
 
 ENGRAM_API size_t engram_cache_build_workspace(int64_t total_rows) {

@@ -159,6 +159,19 @@ struct ConvArgs {
 };
 hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s);
 
+// A hashed gather (Steps 1-4) to run inside another launch.
+struct GatherJob {
+  TableArgs ta;
+  HashSrc hs;
+  void* e;
+  uint32_t n_tok;
+  int out_dtype;
+  bool hot;  // a hot tier is attached (hs.hot)
+};
+// The strip conv of a with gj's gather in one launch; hipErrorNotSupported
+// (nothing launched) when the pair has no fused form.
+hipError_t launch_conv_gather(const ConvArgs& a, int vdtype, const GatherJob& gj, hipStream_t s);
+
 // Writes the chunk's last conv inputs into the circular state, shifts ids
 // (when tokens/proj are given) and advances pos.
 hipError_t launch_state_commit(const void* v, int64_t v_stride, int vdtype, int64_t B, int64_t T,

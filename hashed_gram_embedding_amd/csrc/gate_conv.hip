@@ -24,6 +24,7 @@
 // cannot feed another token's gate.
 #include "device_util.h"
 #include "engram_internal.h"
+#include "gather_device.h"
 
 namespace engram {
 namespace {
@@ -335,8 +336,7 @@ conv_kernel(ConvArgs a) {
 // shared by a strip's M branches are read through one L2.  spx == 0 (fewer
 // strips than XCDs) keeps the plain order.
 template <int HT, int VT, int KW, int DIL, int TS, int CPT>
-__global__ void __launch_bounds__(256)
-conv_strip_kernel(ConvArgs a, int spx) {
+__device__ __forceinline__ void conv_strip_body(const ConvArgs& a, int spx, int bx, int by, int bz) {
   constexpr int SPAN = (KW - 1) * DIL;
   constexpr int R = TS + SPAN;                 // rows this strip reads
   constexpr int kStatLanes = 16;               // lanes reducing one row's statistics
@@ -349,7 +349,7 @@ conv_strip_kernel(ConvArgs a, int spx) {
   const int64_t T = a.T;
   int strip, m;
   {
-    const int L = blockIdx.x;
+    const int L = bx;
     if (spx > 0) {
       const int k = L >> 3;
       m = k % M;
@@ -367,9 +367,9 @@ conv_strip_kernel(ConvArgs a, int spx) {
   constexpr int kHB = HT == ENGRAM_BF16 ? 2 : 4;
   const int Ti = static_cast<int>(T);
   const int t0 = strip * TS;
-  const int b = blockIdx.y;
+  const int b = by;
   const int tid = threadIdx.x;
-  const uint32_t c = (blockIdx.z * 256 + tid) * CPT;  // this thread's CPT channels
+  const uint32_t c = (bz * 256 + tid) * CPT;  // this thread's CPT channels
   const bool active = c < static_cast<uint32_t>(d);
   const uint32_t cc = active ? c : 0;                 // a valid column for idle threads' loads
   const int64_t row0 = static_cast<int64_t>(b) * T;
@@ -469,7 +469,7 @@ conv_strip_kernel(ConvArgs a, int spx) {
         const float logit = shk * rh * rk / sqrtf(static_cast<float>(d));
         al = 1.0f / (1.0f + expf(-logit));
         gm = al / sqrtf(al * al * (svv * inv_d) + g.eps);
-        if (blockIdx.z == 0 && r >= SPAN) {
+        if (bz == 0 && r >= SPAN) {
           const int64_t o = (row0 + t) * M + m;
           if (a.alpha_out != nullptr) a.alpha_out[o] = al;
           if (a.gamma_out != nullptr) a.gamma_out[o] = gm;
@@ -509,6 +509,36 @@ conv_strip_kernel(ConvArgs a, int spx) {
       storec<HT, CPT>(hseq + static_cast<int64_t>(t) * hrow, c, hn);
       if (a.y_out != nullptr) storec<ENGRAM_F32, CPT>(a.y_out + ((row0 + t) * M + m) * d, c, y);
     }
+  }
+}
+
+template <int HT, int VT, int KW, int DIL, int TS, int CPT>
+__global__ void __launch_bounds__(256)
+conv_strip_kernel(ConvArgs a, int spx) {
+  conv_strip_body<HT, VT, KW, DIL, TS, CPT>(a, spx, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// One launch with two kinds of workgroups: the first n_conv run this batch's
+// strip conv (the 3-D grid flattened x fastest, so workgroup i still runs on
+// XCD i % 8 and keeps the strips' XCD order), the rest run the next batch's
+// hashed gather (Steps 1-4 from token ids alone).  The two share no data;
+// both are bound by memory latency at these sizes, so each fills the other's
+// wait cycles on the same CUs -- the pages' prefetch of the next retrieval
+// behind the current computation, without a second stream.
+template <int KW, int DIL, int TS, int CPT, int GOUT, int ITEMS>
+__global__ void __launch_bounds__(256)
+conv_gather_kernel(ConvArgs a, int spx, uint32_t n_conv, uint32_t gx, GatherJob gj) {
+  const uint32_t flat = blockIdx.x;
+  if (flat < n_conv) {
+    const uint32_t plane = gx * static_cast<uint32_t>(a.B);
+    const uint32_t bz = flat / plane;
+    const uint32_t rem = flat - bz * plane;
+    const uint32_t by = rem / gx;
+    conv_strip_body<ENGRAM_BF16, ENGRAM_F32, KW, DIL, TS, CPT>(a, spx, static_cast<int>(rem - by * gx),
+                                                                static_cast<int>(by), static_cast<int>(bz));
+  } else {
+    hashed_gather_body<ENGRAM_BF16, GOUT, false, ITEMS>((flat - n_conv) * 256 + threadIdx.x, gj.n_tok, gj.ta,
+                                                         gj.e, gj.hs);
   }
 }
 
@@ -626,17 +656,65 @@ hipError_t launch_conv_strip(const ConvArgs& a, int vdtype, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Strip shape of the pages' conv (w = 4, dilation 3): decode steps get
+// 1-token strips; otherwise 16-token strips of 512 channels when that gives
+// at least 4 workgroups per CU, else 4-token strips of 1024 channels (4x the
+// workgroups, more halo re-reads, which hit L2).  Returns TS (CPT = 4 for
+// TS <= 4, else 2), or 0 when the strip kernel does not apply.
+int conv_strip_ts(const ConvArgs& a) {
+  if (a.g.kernel_w != 4 || a.g.dilation != 3 || a.qv + a.qk > 64) return 0;
+  if (a.T == 1) return 1;
+  const int64_t wg16 = a.B * a.g.branches * ((a.T + 15) / 16) * ((a.g.d + 511) / 512);
+  return wg16 < 1024 ? 4 : 16;
+}
+
+template <int TS, int CPT>
+hipError_t launch_conv_gather_ts(const ConvArgs& a, const GatherJob& gj, hipStream_t s) {
+  const int64_t n_strips = (a.T + TS - 1) / TS;
+  const int spx = static_cast<int>((n_strips + 7) / 8);
+  const int64_t gx = 8 * static_cast<int64_t>(spx) * a.g.branches;
+  const int64_t gz = (a.g.d + 256 * CPT - 1) / (256 * CPT);
+  const int64_t n_conv = gx * a.B * gz;
+  const int64_t per_group = static_cast<int64_t>(gj.ta.n_tables) * (gj.ta.dim / 8);
+  // 4 tokens per gather thread: the fewest wavefronts, so that the gather and
+  // the conv fit on the CUs together
+  constexpr int items = 4;
+  const int64_t g_threads = (static_cast<int64_t>(gj.n_tok) + items - 1) / items * per_group;
+  const int64_t n_blocks = n_conv + (g_threads + 255) / 256;
+  if (n_blocks >= (1ll << 31) || g_threads >= (1ll << 31)) return hipErrorNotSupported;
+  const dim3 grid(static_cast<unsigned>(n_blocks));
+  const uint32_t nc = static_cast<uint32_t>(n_conv), ux = static_cast<uint32_t>(gx);
+  if (gj.out_dtype == kGatherOutMXFP8)
+    launch_k((conv_gather_kernel<4, 3, TS, CPT, kGatherOutMXFP8, items>), grid, dim3(256), 0, s, a, spx, nc, ux, gj);
+  else
+    launch_k((conv_gather_kernel<4, 3, TS, CPT, ENGRAM_BF16, items>), grid, dim3(256), 0, s, a, spx, nc, ux, gj);
+  return hipGetLastError();
+}
+
+// The strip conv of this batch with the next batch's gather in the same
+// launch, the conv in exactly the shape launch_conv would give it (so the
+// results are bit-identical to the two launches).  Only for the layer
+// forward's own case: bf16 H, float32 v from the fused projection, no decode
+// state, bf16 tables, bf16 or MXFP8 rows out, no hot tier, at least 8 strips;
+// anything else returns hipErrorNotSupported before launching, and the caller
+// launches the two kernels one after the other.
+hipError_t launch_conv_gather(const ConvArgs& a, int vdtype, const GatherJob& gj, hipStream_t s) {
+  if (a.g.hdtype != ENGRAM_BF16 || vdtype != ENGRAM_F32 || a.has_state || gj.ta.dtype != ENGRAM_BF16 || gj.hot ||
+      (gj.out_dtype != ENGRAM_BF16 && gj.out_dtype != kGatherOutMXFP8) || a.B * a.T == 0 || gj.n_tok == 0)
+    return hipErrorNotSupported;
+  const int ts = conv_strip_ts(a);
+  if (ts != 4 && ts != 16) return hipErrorNotSupported;
+  if ((a.T + ts - 1) / ts < 8) return hipErrorNotSupported;   // fewer strips than XCDs: plain order
+  return ts == 4 ? launch_conv_gather_ts<4, 4>(a, gj, s) : launch_conv_gather_ts<16, 2>(a, gj, s);
+}
+
 hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
-  // the pages' conv (w = 4, dilation 3): strip kernel; decode steps get 1-token strips
-  if (a.g.kernel_w == 4 && a.g.dilation == 3 && a.qv + a.qk <= 64) {
-    if (a.T == 1) return launch_conv_strip<4, 3, 1, 4>(a, vdtype, s);
-    // 16-token strips of 512 channels when that gives at least 4 workgroups
-    // per CU; otherwise 4-token strips of 1024 channels (4x the workgroups,
-    // more halo re-reads, which hit L2)
-    const int64_t wg16 = a.B * a.g.branches * ((a.T + 15) / 16) * ((a.g.d + 511) / 512);
-    if (wg16 < 1024) return launch_conv_strip<4, 3, 4, 4>(a, vdtype, s);
-    return launch_conv_strip<4, 3, 16, 2>(a, vdtype, s);
+  switch (conv_strip_ts(a)) {   // the pages' conv (w = 4, dilation 3): strip kernel
+    case 1: return launch_conv_strip<4, 3, 1, 4>(a, vdtype, s);
+    case 4: return launch_conv_strip<4, 3, 4, 4>(a, vdtype, s);
+    case 16: return launch_conv_strip<4, 3, 16, 2>(a, vdtype, s);
+    default: break;
   }
   switch (conv_channels(a.g.d)) {
     case 256: return launch_conv_cg<64>(a, vdtype, s);
