@@ -200,8 +200,10 @@ def hot_tier_setup(args, torch, eg, inputs, w, lay, L, tok):
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 # library stage name -> (pattern of the rocprofv3 kernel name, sources whose text fixes the kernel)
 KERNEL_SOURCES = {
-    "gather_kernel<hashed>": (r"hashed_gather_kernel<[^>]*false, \d>", ["gather.hip", "hash_device.h", "hot_device.h"]),
-    "gather_kernel<hashed,hot>": (r"hashed_gather_kernel<[^>]*true, \d>", ["gather.hip", "hash_device.h", "hot_device.h"]),
+    "gather_kernel<hashed>": (r"hashed_gather_kernel<[^>]*false, \d>",
+                              ["gather.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
+    "gather_kernel<hashed,hot>": (r"hashed_gather_kernel<[^>]*true, \d>",
+                                  ["gather.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
     "proj_gate_kernel": (r"proj_gate_kernel<", ["proj_gate.hip"]),
     "conv_kernel": (r"conv_(strip_)?kernel<", ["gate_conv.hip"]),
 }
