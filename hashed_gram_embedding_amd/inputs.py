@@ -346,6 +346,20 @@ def make_config(config: int, *, B: Optional[int] = None, T: Optional[int] = None
     raise ValueError(f"unknown config {config}")
 
 
+def make_order4(B: int, T: int, *, heads: int = 4, dim: int = 32, d: int = 128, branches: int = 1,
+                rows_per_table: int = 1009, layers: int = 1) -> Workload:
+    """A bf16 variant with n-gram orders 2..4 (N = 4, the largest the library
+    takes): K = 4 heads of 32 dims per order (d_mem = 384), prime tables from
+    rows_per_table up, hidden width d; tokens Zipf(1.1) over 128,000 raw ids
+    projected to 98,560.  Seeds under configuration id 5."""
+    lays = [_layer(5, l, vocab=128_000, vocab_c=98_560, max_n=4, heads=heads, prime_start=rows_per_table, dim=dim,
+                   table_dtype=BF16, d=d, branches=branches, store_dtype=BF16, w_std=1.0 / 20)
+            for l in range(layers)]
+    tokens = zipf_tokens(rng_for(5, 0, S_TOKENS), 128_000, 1.1, (B, T))
+    H = _hidden(5, (B, T, branches, d), BF16)
+    return Workload("order-4-bf16", 5, BF16, B, T, tokens, H, lays)
+
+
 def hash_inputs_for(config: int, layer: int = 0) -> HashInputs:
     """Only the hash inputs of a configuration (no tables), for index tests."""
     if config == 0:
