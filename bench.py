@@ -789,7 +789,7 @@ def main():
         if not k.startswith("_"):
             out[k] = v
     if args.config in (1, 2) and not args.no_controls:
-        out["controls"] = control_report(torch, eg, inputs, args, w, lays[0], extra["_pipe"], units)
+        out["controls"] = control_report(torch, eg, inputs, w, lays[0], extra["_pipe"], units)
     if args.config == 3:
         out["tokens_per_s_per_layer"] = round(n_tok * len(calls) / (ms * 1e-3), 1)
     if args.overlap and args.config in (1, 2):
@@ -809,7 +809,7 @@ def main():
         torch.cuda.synchronize()
 
 
-def control_report(torch, eg, inputs, args, w, lay, pipe, units, steps=20):
+def control_report(torch, eg, inputs, w, lay, pipe, units, steps=20):
     """Two controls of the measured kernel rates.
     cold: before every eager layer call a 512 MiB buffer is overwritten (more
     than the 256 MB Infinity Cache), so tables, W and e start outside the

@@ -1,0 +1,61 @@
+"""Host-side logic of bench.py: the one-GPU contract, the algorithmic units
+the roofline divides by, and the HBM byte counter scaling (no GPU needed)."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from hashed_gram_embedding_amd import inputs  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+def test_kernel_units_of_the_single_branch_layer():
+    lay = inputs.make_config(1, T=8, rows_per_table=997).layers[0]
+    u = bench.kernel_units(4096, lay, "bf16")
+    # 4 B of token id, then 16 rows of 128 B in and 128 B out per token
+    assert u["gather_kernel<hashed>"] == ("hbm", 4096 * (4 + 16 * 256))
+    assert u["proj_gate_kernel"] == ("mfma", 2.0 * 4096 * 2048 * 1024)
+    # v (fp32) and 16 statistics tiles in; H in and out; alpha and gamma out
+    assert u["conv_kernel"] == ("hbm", 4096 * (4096 + 16 * 16 + 2 * 2048 + 8))
+    # MXFP8 rows: a code per element and a scale byte per 32
+    assert bench.kernel_units(4096, lay, "bf16", mx=True)["gather_kernel<hashed>"][1] == 4096 * (4 + 16 * (128 + 66))
+    # hot tier: every order adds a pilot and a 32-byte slot; a hit reads its 1 KiB row, a miss 8 cold rows
+    hot = bench.kernel_units(4096, lay, "bf16", hot_hit=[1.0, 0.0])["gather_kernel<hashed,hot>"][1]
+    assert hot == 4096 * (4 + 16 * 128 + 2 * 36 + 1024 + 8 * 128)
+    # decode: below the ridge the projection is priced by the bytes it moves
+    small = bench.kernel_units(256, lay, "bf16")["proj_gate_kernel"]
+    assert small[0] == "hbm" and small[1] > 2048 * 1024 * 2
+
+
+def test_hbm_summary_scales_counters_by_the_calibration_copy(tmp_path, capsys):
+    def write(path, rows):
+        with open(path, "w") as f:
+            f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+            for k, c, v in rows:
+                f.write(f'"{k}",{c},{v}\n')
+    n = 1 << 30
+    gather = "void engram::(anonymous namespace)::hashed_gather_kernel<1, 1, false, 2>(unsigned int)"
+    fetch = [(gather, "FETCH_SIZE", 4000.0), (gather, "FETCH_SIZE", 6000.0),
+             ("__amd_rocclr_copyBuffer", "FETCH_SIZE", n / 1024 / 2)]          # the counter reads half
+    write_ = [(gather, "WRITE_SIZE", 8192.0), ("__amd_rocclr_copyBuffer", "WRITE_SIZE", n / 1024)]
+    write(tmp_path / "f.csv", fetch)
+    write(tmp_path / "w.csv", write_)
+    bench.hbm_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "wl", n)
+    out = capsys.readouterr().out
+    row = next(l for l in out.splitlines() if "`gather_kernel<hashed>`" in l)
+    cells = [c.strip() for c in row.strip().strip("|").split("|")]
+    assert cells[0] == "wl" and int(cells[2]) == 2 * 5000 * 1024 and int(cells[3]) == 8192 * 1024
+    assert cells[4] == "2" and cells[5] == bench.kernel_source_hash("gather_kernel<hashed>")
