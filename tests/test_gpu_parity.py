@@ -220,6 +220,23 @@ def test_forward_bf16(config, B, T):
     _forward_check(w, tag=f"c{config}")
 
 
+# Hidden widths off the fused path (d not a multiple of 128: the separate
+# product, then whole-row gate statistics) and several branches in fp32.
+@pytest.mark.parametrize("dtype,d,M,B,T", [("bf16", 192, 2, 2, 50), ("bf16", 64, 3, 1, 70), ("f32", 128, 2, 2, 33)])
+def test_forward_unfused_widths(dtype, d, M, B, T):
+    log(f"forward unfused dtype={dtype} d={d} M={M} B={B} T={T}")
+    w = small(0 if dtype == "f32" else 1, B=B, T=T, d=d, branches=M)
+    names = []
+    eg.profile_enable(True)
+    try:
+        ref = _forward_check(w, tag=f"unfused d={d}")
+        names = [n for n, _ in eg.profile_read()]
+    finally:
+        eg.profile_enable(False)
+    assert "gemm_kernel" in names and "gate_stats_kernel" in names, names
+    assert ref["Y"].shape == (B, T, M, d)
+
+
 def test_forward_empty_is_noop():
     log("forward empty")
     w = small(1, B=1, T=4)
