@@ -292,7 +292,8 @@ size_t forward_ws_bytes(int64_t n_tok, const engram_layer* L) {
 engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdtype, const float4* stats, int qv,
                               int qk, int64_t B, int64_t T, const engram::GateConvArgs& g, engram_decode_state* st,
                               const int32_t* tokens, const int32_t* proj, int32_t max_n, float* alpha_out,
-                              float* gamma, float* y_out, hipStream_t s, const engram::GatherJob* next = nullptr) {
+                              float* gamma, float* y_out, hipStream_t s, const engram::GatherJob* next = nullptr,
+                              bool state_folded = false) {
   engram::ConvArgs ca{};
   ca.H = H;
   ca.v = v;
@@ -306,6 +307,10 @@ engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdty
   ca.g = g;
   ca.has_state = st != nullptr;
   if (st != nullptr) ca.st = engram::StateArgs{st->ids, st->conv, st->pos};
+  // decode with the state advance already done by the projection launch: the
+  // conv reads pos - T and writes the new conv input itself
+  ca.pos_advanced = state_folded;
+  ca.commit_u = state_folded;
   ca.alpha_out = alpha_out;
   ca.gamma_out = gamma;
   ca.y_out = y_out;
@@ -331,7 +336,7 @@ engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdty
       if (r != ENGRAM_OK) return r;
     }
   }
-  if (st != nullptr) {
+  if (st != nullptr && !state_folded) {
     engram::StateArgs sa{tokens != nullptr ? st->ids : nullptr, st->conv, st->pos};
     prof_mark(s, "state_commit_kernel");
     r = hip_status(engram::launch_state_commit(v, v_stride, vdtype, B, T, g, gamma, sa, tokens, proj, max_n, s),
@@ -559,12 +564,32 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
     pa.N = static_cast<int>(n_out);
     pa.d = d;
     pa.M = M;
+    const int q = d / engram::proj_gate_tile_f(n_tok, static_cast<int>(n_out), d, mx);
+    // Decode step (T = 1, the strip conv): the state's ids and pos advance in
+    // this launch and the conv writes the new ring row, so no commit kernel
+    bool fold = false;
+    if (st != nullptr && T == 1 && tokens != nullptr && st->ids != nullptr) {
+      engram::ConvArgs probe{};
+      probe.g = g;
+      probe.qv = probe.qk = q;
+      probe.B = B;
+      probe.T = T;
+      fold = engram::conv_strip_ts(probe) == 1;
+    }
+    if (fold) {
+      pa.st_ids = st->ids;
+      pa.st_pos = st->pos;
+      pa.tokens = tokens;
+      pa.proj = L->hash.proj;
+      pa.max_n = L->hash.max_n;
+      pa.adv_T = static_cast<int32_t>(T);
+      pa.adv_B = static_cast<int32_t>(B);
+    }
     prof_mark(stream, "proj_gate_kernel");
     r = hip_status(engram::launch_proj_gate(pa, stream), "projection launch");
     if (r != ENGRAM_OK) return r;
-    const int q = d / engram::proj_gate_tile_f(n_tok, static_cast<int>(n_out), d, mx);
     return run_conv_commit(H, f.kv, d, ENGRAM_F32, f.stats, q, q, B, T, g, st, tokens, L->hash.proj,
-                           L->hash.max_n, alpha_out, f.gamma, y_out, stream, next);
+                           L->hash.max_n, alpha_out, f.gamma, y_out, stream, next, fold);
   }
   // Step 5 into float32 projections, then whole-row gate statistics
   prof_mark(stream, "gemm_kernel");

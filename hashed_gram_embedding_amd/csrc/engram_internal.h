@@ -131,6 +131,17 @@ struct ProjGateArgs {
   // bytes) and these their block scale bytes ([n_tok][K/32], [N][K/32])
   const uint8_t* e_scale;
   const uint8_t* w_scale;
+  // Decode-state advance folded into this launch (adv_B > 0): workgroup 0
+  // shifts the last N-1 compressed ids of every sequence's T = adv_T new
+  // tokens into st_ids and adds adv_T to st_pos.  Nothing in the launch reads
+  // them; the conv that follows knows pos has moved (ConvArgs.pos_advanced).
+  int32_t* st_ids;        // [adv_B][max_n-1]
+  int32_t* st_pos;        // [adv_B]
+  const int32_t* tokens;  // [adv_B][adv_T] raw ids
+  const int32_t* proj;    // P
+  int32_t max_n;
+  int32_t adv_T;
+  int32_t adv_B;
 };
 constexpr int kProjGateTileF = 64;   // narrowest feature tile (bounds the statistics buffer)
 int proj_gate_tile_f(int64_t n_tok, int N, int d, bool mx);   // feature columns per gate-statistics tile
@@ -153,11 +164,16 @@ struct ConvArgs {
   GateConvArgs g;
   StateArgs st;
   int has_state;
+  int pos_advanced;     // st.pos already holds pos + T (advanced by the projection launch)
+  int commit_u;         // T = 1 strip conv: also write the new conv input u into the ring
   float* alpha_out;     // [B*T][M] or null
   float* gamma_out;     // [B*T][M] or null
   float* y_out;         // [B][T][M][d] or null
 };
 hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s);
+// Token strip of the conv launch_conv runs for a (1, 4 or 16), or 0 when it
+// runs the LDS-tiled conv kernel instead.
+int conv_strip_ts(const ConvArgs& a);
 
 // A hashed gather (Steps 1-4) to run inside another launch.
 struct GatherJob {

@@ -386,7 +386,8 @@ __device__ __forceinline__ void conv_strip_body(const ConvArgs& a, int spx, int 
     const int t = t0 - SPAN + r;
     if (r < SPAN && t < 0 && a.has_state) {
       // halo before the chunk: the state's circular slot of position pos + t
-      int slot = static_cast<int>((static_cast<int64_t>(a.st.pos[b]) + t) % SPAN);
+      const int64_t pos = static_cast<int64_t>(a.st.pos[b]) - (a.pos_advanced ? T : 0);
+      int slot = static_cast<int>((pos + t) % SPAN);
       if (slot < 0) slot += SPAN;
       loadc<ENGRAM_F32, CPT>(a.st.conv + ((static_cast<int64_t>(b) * M + m) * SPAN + slot) * d, cc, v[r]);
     } else {
@@ -508,6 +509,20 @@ __device__ __forceinline__ void conv_strip_body(const ConvArgs& a, int spx, int 
     if (active && t < Ti) {
       storec<HT, CPT>(hseq + static_cast<int64_t>(t) * hrow, c, hn);
       if (a.y_out != nullptr) storec<ENGRAM_F32, CPT>(a.y_out + ((row0 + t) * M + m) * d, c, y);
+    }
+  }
+  // Decode (T = 1 strips): the new position's conv input u goes to its ring
+  // slot (pos % SPAN, which held position pos - SPAN: this workgroup read that
+  // row for its oldest tap above and owns these channels, so no other
+  // workgroup reads the slot).
+  if constexpr (TS == 1) {
+    if (a.commit_u && active) {
+      const int64_t pos = static_cast<int64_t>(a.st.pos[b]) - (a.pos_advanced ? T : 0);
+      const int slot = static_cast<int>(pos % SPAN);
+      float uc[CPT];
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) uc[i] = u[SPAN][i];
+      storec<ENGRAM_F32, CPT>(a.st.conv + ((static_cast<int64_t>(b) * M + m) * SPAN + slot) * d, c, uc);
     }
   }
 }

@@ -52,6 +52,28 @@ constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
+// Decode-state advance (ProjGateArgs.adv_B > 0), by the threads of
+// workgroup 0: ids <- last N-1 of (ids ++ P(tokens)), pos += T.
+__device__ __forceinline__ void advance_state(const ProjGateArgs& a) {
+  if (a.adv_B <= 0 || blockIdx.x != 0) return;
+  const int hl = a.max_n - 1;
+  for (int b = threadIdx.x; b < a.adv_B; b += blockDim.x) {
+    int32_t next[ENGRAM_MAX_ORDER];
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDER - 1; ++i) {
+      if (i < hl) {
+        const int64_t idx = static_cast<int64_t>(a.adv_T) + i;   // index in (old ids ++ chunk ids)
+        next[i] = idx < hl ? a.st_ids[static_cast<int64_t>(b) * hl + idx]
+                           : a.proj[a.tokens[static_cast<int64_t>(b) * a.adv_T + idx - hl]];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDER - 1; ++i)
+      if (i < hl) a.st_ids[static_cast<int64_t>(b) * hl + i] = next[i];
+    a.st_pos[b] += a.adv_T;
+  }
+}
+
 template <int TF, int PD, bool MX, int WT>
 __global__ void __launch_bounds__(64 * WF * WT) __attribute__((amdgpu_waves_per_eu(WF * WT / 4, WF * WT / 4)))
 proj_gate_kernel(ProjGateArgs a) {
@@ -280,6 +302,7 @@ proj_gate_kernel(ProjGateArgs a) {
       a.stats[tok * a.tiles_f + tf] = p;
     }
   }
+  advance_state(a);
 }
 
 // Small batches (decode): a 64-feature x 32-token tile per workgroup, so that
@@ -409,6 +432,7 @@ proj_gate_small_kernel(ProjGateArgs a) {
     }
     a.stats[(t0 + threadIdx.x) * a.tiles_f + tf] = p;
   }
+  advance_state(a);
 }
 
 template <int TF, int PD, bool MX, int WT = 4>
