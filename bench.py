@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--hbm-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                          "run with --copy-calibration-mib into the per-kernel HBM bytes table and exit")
+    ap.add_argument("--no-layer-prefetch", action="store_true",
+                    help="config 3: run each layer as a plain engram_forward instead of carrying the next layer's "
+                         "retrieval in the conv launch (engram_forward_retrieved_prefetch)")
     ap.add_argument("--no-controls", action="store_true",
                     help="configs 1-2: skip the control measurements (a cold-cache pass that overwrites 512 MiB "
                          "between steps, and the gather over uniform tokens)")
@@ -118,8 +121,10 @@ def kernel_units(n_tok, lay, hdtype, hot_hit=None, mx=False):
 
 
 def setup(args, torch, eg, inputs):
-    """Returns (layer_calls, n_tok, workload, layer_inputs, extra); layer_calls
-    holds one zero-argument callable per layer forward of a step."""
+    """Returns (calls, n_tok, workload, layer_inputs, extra); calls holds one
+    zero-argument callable per library call of a step (one per layer forward;
+    in decode with the next layer's retrieval prefetched, layer 0's retrieval
+    and then one per layer, with extra["_layers"] the layer count)."""
     dev = "cuda"
     cfg = args.config
     if cfg in (1, 2):
@@ -145,10 +150,27 @@ def setup(args, torch, eg, inputs):
         tok = torch.from_numpy(w.tokens).to(dev)
         H = eg.to_device(w.H, "bf16", dev)
         wss = [torch.empty(eg.forward_workspace(S, 1, L), dtype=torch.uint8, device=dev) for L in Ls]
-        calls = [(lambda L=L, st=st, ws=ws: eg.forward(tok, H, L, state=st, ws=ws))
-                 for L, st, ws in zip(Ls, states, wss)]
-        return calls, S, w, w.layers, {"decode": "256 sequences x 1 token, 2 layers, after a 16-token prefill",
-                                       "_keep": (Ls, states)}
+        if args.no_layer_prefetch:
+            calls = [(lambda L=L, st=st, ws=ws: eg.forward(tok, H, L, state=st, ws=ws))
+                     for L, st, ws in zip(Ls, states, wss)]
+        else:
+            # every layer but the last carries the next layer's retrieval (same
+            # tokens, that layer's id history) in its conv launch
+            es = [eg.rows_buffer(S, 1, L, dev) for L in Ls]
+
+            def call(i):
+                if i + 1 < len(Ls):
+                    eg.forward_retrieved_prefetch(tok, es[i], H, Ls[i], tok, es[i + 1], ws=wss[i], next_layer=Ls[i + 1],
+                                                  state=states[i], next_state=states[i + 1])
+                else:
+                    eg.forward_retrieved(tok, es[i], H, Ls[i], state=states[i], ws=wss[i])
+            # library calls of one step: layer 0's retrieval, then the layers
+            calls = [lambda: eg.retrieve(tok, Ls[0], es[0], state=states[0])] + \
+                [(lambda i=i: call(i)) for i in range(len(Ls))]
+        return calls, S, w, w.layers, {"decode": "256 sequences x 1 token, 2 layers, after a 16-token prefill"
+                                                 + ("" if args.no_layer_prefetch else
+                                                    "; layer 1's retrieval runs inside layer 0's conv launch"),
+                                       "_keep": (Ls, states), "_layers": len(Ls)}
     # cfg == 4: host tables + HBM cache
     w = inputs.make_config(4)
     tok = torch.from_numpy(w.tokens).to(dev)
@@ -742,7 +764,8 @@ def main():
                 "traffic": traffic_for(w.name, dominant), "units_per_launch": amount}
     gather_gbps = rates.get("gather_kernel<hashed>", rates.get("gather_kernel<hashed,hot>"))
     lay0 = lays[0]
-    peaks = measured_peaks(torch, (n_tok // len(calls), (1 + lay0.branches) * lay0.d, lay0.d_mem)
+    n_layers = extra.get("_layers", len(calls))
+    peaks = measured_peaks(torch, (n_tok // n_layers, (1 + lay0.branches) * lay0.d, lay0.d_mem)
                            if args.config in (1, 2) else None)
     # (no FP8 matmul is re-measured, so an MXFP8 product has no measured peak)
     ref = None if (kind == "mfma" and args.mxfp8) else \
@@ -771,7 +794,7 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp8 projection, bf16 storage" if args.mxfp8 else w.dtype,
         "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) tables, N(0,1) hidden states)",
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "layers_per_step": len(calls), "branches": lay.branches,
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "layers_per_step": n_layers, "branches": lay.branches,
                    "d": lay.d, "d_mem": lay.d_mem, "tables": lay.hash.n_tables,
                    "table_rows": int(lay.tables.n_rows.sum()), "table_dtype": lay.tables.dtype,
                    "hot_ngrams_per_order": args.hot_tier if args.config in (1, 2) else 0},
@@ -791,7 +814,7 @@ def main():
     if args.config in (1, 2) and not args.no_controls:
         out["controls"] = control_report(torch, eg, inputs, w, lays[0], extra["_pipe"], units)
     if args.config == 3:
-        out["tokens_per_s_per_layer"] = round(n_tok * len(calls) / (ms * 1e-3), 1)
+        out["tokens_per_s_per_layer"] = round(n_tok * n_layers / (ms * 1e-3), 1)
     if args.overlap and args.config in (1, 2):
         out["retrieval_overlap"] = overlap_report(torch, eg, w, lays[0], args.steps, args.warmup)
     if args.realtime_lfu and args.config == 4:

@@ -316,7 +316,7 @@ engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdty
   ca.y_out = y_out;
   engram_status r;
   bool fused = false;
-  if (next != nullptr && st == nullptr) {
+  if (next != nullptr) {
     prof_mark(s, "conv_gather_kernel");
     const hipError_t e = engram::launch_conv_gather(ca, vdtype, *next, s);
     if (e != hipErrorNotSupported) {
@@ -685,16 +685,19 @@ ENGRAM_API engram_status engram_forward_retrieved(const int32_t* tokens, const v
 }
 
 ENGRAM_API engram_status engram_forward_retrieved_prefetch(const int32_t* tokens, const void* e, void* H, int64_t B,
-                                                           int64_t T, const engram_layer* L, float* alpha_out,
-                                                           float* y_out, void* ws, size_t ws_bytes,
-                                                           const engram_layer* next_L, const int32_t* next_tokens,
-                                                           int64_t next_B, int64_t next_T, void* next_e,
-                                                           hipStream_t stream) {
+                                                           int64_t T, const engram_layer* L, engram_decode_state* st,
+                                                           float* alpha_out, float* y_out, void* ws, size_t ws_bytes,
+                                                           const engram_layer* next_L,
+                                                           const engram_decode_state* next_st,
+                                                           const int32_t* next_tokens, int64_t next_B, int64_t next_T,
+                                                           void* next_e, hipStream_t stream) {
   engram::HashArgs ha;
   engram::TableArgs ta;
   engram::GateConvArgs g;
-  engram_status r = check_call("forward_retrieved_prefetch", L, nullptr, false, B, T, &ha, &ta, &g);
+  engram_status r = check_call("forward_retrieved_prefetch", L, st, true, B, T, &ha, &ta, &g);
   if (r != ENGRAM_OK) return r;
+  if (next_st != nullptr && (next_st == st || next_st->ids == nullptr))
+    return fail(ENGRAM_EINVAL, "forward_retrieved_prefetch: next_st must have ids and must not be st");
   // the next retrieval's layer (its hash, tables and row format)
   const engram_layer* NL = next_L != nullptr ? next_L : L;
   engram::HashArgs nha;
@@ -720,7 +723,7 @@ ENGRAM_API engram_status engram_forward_retrieved_prefetch(const int32_t* tokens
   engram::HotArgs hot;
   bool any_hot;
   if ((r = check_hot(NL->hot, &NL->hash, &NL->tables, &hot, &any_hot)) != ENGRAM_OK) return r;
-  job.hs = engram::HashSrc{next_tokens, NL->hash.proj, nullptr, next_T, nha, hot};
+  job.hs = engram::HashSrc{next_tokens, NL->hash.proj, next_st != nullptr ? next_st->ids : nullptr, next_T, nha, hot};
   job.e = next_e;
   job.n_tok = static_cast<uint32_t>(n_next);
   job.out_dtype = NL->w_mx != nullptr ? engram::kGatherOutMXFP8 : ng.hdtype;
@@ -729,10 +732,12 @@ ENGRAM_API engram_status engram_forward_retrieved_prefetch(const int32_t* tokens
   if (n_tok == 0) {
     if (n_next == 0) return ENGRAM_OK;
     prof_begin();
-    return run_retrieve(next_tokens, next_B, next_T, NL, nha, nta, ng.hdtype, nullptr, next_e, stream);
+    return run_retrieve(next_tokens, next_B, next_T, NL, nha, nta, ng.hdtype, next_st, next_e, stream);
   }
   if (e == nullptr || H == nullptr)
     return fail(ENGRAM_EINVAL, "forward_retrieved_prefetch: e and H must be non-NULL");
+  if (st != nullptr && tokens == nullptr)
+    return fail(ENGRAM_EINVAL, "forward_retrieved_prefetch: tokens must be non-NULL with a decode state");
   if (!aligned(H, 16) || !aligned(e, 16))
     return fail(ENGRAM_EINVAL, "forward_retrieved_prefetch: H and e must be 16-byte aligned");
   if (y_out != nullptr && !aligned(y_out, 16))
@@ -744,7 +749,7 @@ ENGRAM_API engram_status engram_forward_retrieved_prefetch(const int32_t* tokens
   Carve c{static_cast<char*>(ws)};
   const ComputeWorkspace f = carve_compute(c, n_tok, L);
   prof_begin();
-  return run_compute(tokens, e, H, B, T, L, g, nullptr, alpha_out, y_out, f, stream, n_next > 0 ? &job : nullptr);
+  return run_compute(tokens, e, H, B, T, L, g, st, alpha_out, y_out, f, stream, n_next > 0 ? &job : nullptr);
 }
 
 ENGRAM_API size_t engram_cache_build_workspace(int64_t total_rows) {

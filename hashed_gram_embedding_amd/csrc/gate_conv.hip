@@ -533,14 +533,15 @@ conv_strip_kernel(ConvArgs a, int spx) {
   conv_strip_body<HT, VT, KW, DIL, TS, CPT>(a, spx, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// One launch with two kinds of workgroups: the first n_conv run this batch's
+// One launch with two kinds of workgroups: the first n_conv run this call's
 // strip conv (the 3-D grid flattened x fastest, so workgroup i still runs on
-// XCD i % 8 and keeps the strips' XCD order), the rest run the next batch's
-// hashed gather (Steps 1-4 from token ids alone).  The two share no data;
-// both are bound by memory latency at these sizes, so each fills the other's
-// wait cycles on the same CUs -- the pages' prefetch of the next retrieval
-// behind the current computation, without a second stream.
-template <int KW, int DIL, int TS, int CPT, int GOUT, int ITEMS>
+// XCD i % 8 and keeps the strips' XCD order), the rest run the next
+// retrieval's hashed gather (Steps 1-4 from token ids and, in decode, the next
+// layer's id history).  The two share no data; both are bound by memory
+// latency at these sizes, so each fills the other's wait cycles on the same
+// CUs -- the pages' prefetch of the next retrieval behind the current
+// computation, without a second stream.
+template <int KW, int DIL, int TS, int CPT, int GIN, int GOUT, int ITEMS>
 __global__ void __launch_bounds__(256)
 conv_gather_kernel(ConvArgs a, int spx, uint32_t n_conv, uint32_t gx, GatherJob gj) {
   const uint32_t flat = blockIdx.x;
@@ -552,8 +553,8 @@ conv_gather_kernel(ConvArgs a, int spx, uint32_t n_conv, uint32_t gx, GatherJob 
     conv_strip_body<ENGRAM_BF16, ENGRAM_F32, KW, DIL, TS, CPT>(a, spx, static_cast<int>(rem - by * gx),
                                                                 static_cast<int>(by), static_cast<int>(bz));
   } else {
-    hashed_gather_body<ENGRAM_BF16, GOUT, false, ITEMS>((flat - n_conv) * 256 + threadIdx.x, gj.n_tok, gj.ta,
-                                                         gj.e, gj.hs);
+    hashed_gather_body<GIN, GOUT, false, ITEMS>((flat - n_conv) * 256 + threadIdx.x, gj.n_tok, gj.ta, gj.e,
+                                                 gj.hs);
   }
 }
 
@@ -683,11 +684,12 @@ int conv_strip_ts(const ConvArgs& a) {
   return wg16 < 1024 ? 4 : 16;
 }
 
-template <int TS, int CPT>
+template <int TS, int CPT, int GIN>
 hipError_t launch_conv_gather_ts(const ConvArgs& a, const GatherJob& gj, hipStream_t s) {
+  // the strip grid of launch_conv_strip: XCD order from 8 strips up, else plain
   const int64_t n_strips = (a.T + TS - 1) / TS;
-  const int spx = static_cast<int>((n_strips + 7) / 8);
-  const int64_t gx = 8 * static_cast<int64_t>(spx) * a.g.branches;
+  const int spx = n_strips >= 8 ? static_cast<int>((n_strips + 7) / 8) : 0;
+  const int64_t gx = (spx > 0 ? 8 * static_cast<int64_t>(spx) : n_strips) * a.g.branches;
   const int64_t gz = (a.g.d + 256 * CPT - 1) / (256 * CPT);
   const int64_t n_conv = gx * a.B * gz;
   const int64_t per_group = static_cast<int64_t>(gj.ta.n_tables) * (gj.ta.dim / 8);
@@ -700,27 +702,39 @@ hipError_t launch_conv_gather_ts(const ConvArgs& a, const GatherJob& gj, hipStre
   const dim3 grid(static_cast<unsigned>(n_blocks));
   const uint32_t nc = static_cast<uint32_t>(n_conv), ux = static_cast<uint32_t>(gx);
   if (gj.out_dtype == kGatherOutMXFP8)
-    launch_k((conv_gather_kernel<4, 3, TS, CPT, kGatherOutMXFP8, items>), grid, dim3(256), 0, s, a, spx, nc, ux, gj);
+    launch_k((conv_gather_kernel<4, 3, TS, CPT, GIN, kGatherOutMXFP8, items>), grid, dim3(256), 0, s, a, spx, nc, ux,
+             gj);
   else
-    launch_k((conv_gather_kernel<4, 3, TS, CPT, ENGRAM_BF16, items>), grid, dim3(256), 0, s, a, spx, nc, ux, gj);
+    launch_k((conv_gather_kernel<4, 3, TS, CPT, GIN, ENGRAM_BF16, items>), grid, dim3(256), 0, s, a, spx, nc, ux, gj);
   return hipGetLastError();
 }
 
-// The strip conv of this batch with the next batch's gather in the same
+template <int GIN>
+hipError_t launch_conv_gather_in(int ts, const ConvArgs& a, const GatherJob& gj, hipStream_t s) {
+  switch (ts) {
+    case 1: return launch_conv_gather_ts<1, 4, GIN>(a, gj, s);
+    case 4: return launch_conv_gather_ts<4, 4, GIN>(a, gj, s);
+    default: return launch_conv_gather_ts<16, 2, GIN>(a, gj, s);
+  }
+}
+
+// The strip conv of this call with the next retrieval's gather in the same
 // launch, the conv in exactly the shape launch_conv would give it (so the
-// results are bit-identical to the two launches).  Only for the layer
-// forward's own case: bf16 H, float32 v from the fused projection, no decode
-// state, bf16 tables, bf16 or MXFP8 rows out, no hot tier, at least 8 strips;
-// anything else returns hipErrorNotSupported before launching, and the caller
-// launches the two kernels one after the other.
+// results are bit-identical to the two launches), with or without a decode
+// state.  Only for the layer forward's own case: bf16 H and float32 v from
+// the fused projection, the strip conv (w = 4, dilation 3), bf16 or int8
+// tables without a hot tier, bf16 or MXFP8 rows out; anything else returns
+// hipErrorNotSupported before launching, and the caller launches the two
+// kernels one after the other.
 hipError_t launch_conv_gather(const ConvArgs& a, int vdtype, const GatherJob& gj, hipStream_t s) {
-  if (a.g.hdtype != ENGRAM_BF16 || vdtype != ENGRAM_F32 || a.has_state || gj.ta.dtype != ENGRAM_BF16 || gj.hot ||
+  if (a.g.hdtype != ENGRAM_BF16 || vdtype != ENGRAM_F32 || gj.hot ||
+      (gj.ta.dtype != ENGRAM_BF16 && gj.ta.dtype != ENGRAM_I8) ||
       (gj.out_dtype != ENGRAM_BF16 && gj.out_dtype != kGatherOutMXFP8) || a.B * a.T == 0 || gj.n_tok == 0)
     return hipErrorNotSupported;
   const int ts = conv_strip_ts(a);
-  if (ts != 4 && ts != 16) return hipErrorNotSupported;
-  if ((a.T + ts - 1) / ts < 8) return hipErrorNotSupported;   // fewer strips than XCDs: plain order
-  return ts == 4 ? launch_conv_gather_ts<4, 4>(a, gj, s) : launch_conv_gather_ts<16, 2>(a, gj, s);
+  if (ts == 0) return hipErrorNotSupported;
+  return gj.ta.dtype == ENGRAM_I8 ? launch_conv_gather_in<ENGRAM_I8>(ts, a, gj, s)
+                                  : launch_conv_gather_in<ENGRAM_BF16>(ts, a, gj, s);
 }
 
 hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s) {

@@ -100,8 +100,10 @@ def lib():
         "engram_forward_retrieved": (i32, [vp, vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
                                            ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
         "engram_quantize_mxfp8": (i32, [vp, i32, i64, i64, vp, vp, vp]),
-        "engram_forward_retrieved_prefetch": (i32, [vp, vp, vp, i64, i64, ctypes.POINTER(LayerStruct), vp, vp, vp,
-                                                    sz, ctypes.POINTER(LayerStruct), vp, i64, i64, vp, vp]),
+        "engram_forward_retrieved_prefetch": (i32, [vp, vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
+                                                    ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz,
+                                                    ctypes.POINTER(LayerStruct), ctypes.POINTER(DecodeStateStruct),
+                                                    vp, i64, i64, vp, vp]),
         "engram_cache_update_workspace": (sz, [i64, i64]),
         "engram_cache_update": (i32, [ctypes.POINTER(Tables), i64, vp, vp, vp, vp, i32, vp, sz, vp]),
         "engram_cache_build_workspace": (sz, [i64]),
@@ -526,10 +528,12 @@ def forward_retrieved(tokens: torch.Tensor, e: torch.Tensor, H: torch.Tensor, la
 def forward_retrieved_prefetch(tokens: torch.Tensor, e: torch.Tensor, H: torch.Tensor, layer: Layer,
                                next_tokens: Optional[torch.Tensor], next_e: Optional[torch.Tensor],
                                want_alpha: bool = False, want_y: bool = False, ws: Optional[torch.Tensor] = None,
-                               next_layer: Optional[Layer] = None, stream=None):
-    """Steps 5-8 on e (rows of `tokens`) and Steps 1-4 of next_tokens with
-    next_layer's tables (default: this layer) into next_e, in the same
-    launches where the layers allow.  Returns (alpha, y)."""
+                               next_layer: Optional[Layer] = None, state: Optional[DecodeState] = None,
+                               next_state: Optional[DecodeState] = None, stream=None):
+    """Steps 5-8 on e (rows of `tokens`, continuing `state` if given) and
+    Steps 1-4 of next_tokens with next_layer's tables (default: this layer)
+    and next_state's id history into next_e, in the same launches where the
+    layers allow.  Returns (alpha, y)."""
     B, T = tokens.shape
     nB, nT = (0, 0) if next_tokens is None else next_tokens.shape
     M, d = layer.M, layer.d
@@ -538,7 +542,9 @@ def forward_retrieved_prefetch(tokens: torch.Tensor, e: torch.Tensor, H: torch.T
     if ws is None:
         ws = torch.empty(max(forward_retrieved_workspace(B, T, layer), 256), dtype=torch.uint8, device=H.device)
     nl = None if next_layer is None else ctypes.byref(next_layer.s)
-    _check(lib().engram_forward_retrieved_prefetch(_ptr(tokens), _ptr(e), _ptr(H), B, T, ctypes.byref(layer.s),
-                                                   _ptr(alpha), _ptr(y), _ptr(ws), ws.numel(), nl,
+    st = None if state is None else ctypes.byref(state.s)
+    nst = None if next_state is None else ctypes.byref(next_state.s)
+    _check(lib().engram_forward_retrieved_prefetch(_ptr(tokens), _ptr(e), _ptr(H), B, T, ctypes.byref(layer.s), st,
+                                                   _ptr(alpha), _ptr(y), _ptr(ws), ws.numel(), nl, nst,
                                                    _ptr(next_tokens), nB, nT, _ptr(next_e), _stream(stream)))
     return alpha, y

@@ -283,25 +283,26 @@ engram_status engram_forward_retrieved(const int32_t* tokens, const void* e, voi
  * launches: the prefetch of the next embeddings behind the current
  * computation that the RecSDK article (cache prefetch section) and the DRAM
  * offload study (DRAM offload section) describe.  The next retrieval is that
- * of next_L (NULL = L: the same layer, e.g. for the next batch; another layer:
- * that layer's rows for the same or another batch) over next_tokens
- * [next_B][next_T].  The results are those of engram_forward_retrieved(tokens,
- * e, H, B, T, L, NULL, alpha_out, y_out, ws, ws_bytes) followed by
- * engram_retrieve(next_tokens, next_B, next_T, next_L, NULL, next_e), bit for
- * bit; where the layers allow it (L: bf16 H with the fused projection, w = 4
- * and dilation 3, at least 8 conv strips of 4 or 16 tokens; next_L: bf16
- * tables, no hot tier) the next gather
- * runs inside this call's conv launch, so that the two memory-latency-bound
- * kernels share the CUs.  No decode state (independent sequences).  next_e:
- * device, laid out as e of engram_retrieve for next_L, 16-byte aligned, not
- * overlapping e; next_B * next_T = 0 skips the prefetch, B * T = 0 leaves only
- * it.  ws as for engram_forward_retrieved. */
+ * of next_L (NULL = L) over next_tokens [next_B][next_T], with next_st's ids
+ * as its history (NULL = pad 0): the same layer's next batch, or the next
+ * layer's rows of the same tokens (in decode, with that layer's state).  The
+ * results are those of engram_forward_retrieved(tokens, e, H, B, T, L, st,
+ * alpha_out, y_out, ws, ws_bytes) followed by engram_retrieve(next_tokens,
+ * next_B, next_T, next_L, next_st, next_e), bit for bit; where the layers
+ * allow it (L: bf16 H with the fused projection, w = 4 and dilation 3;
+ * next_L: bf16 or int8 tables, no hot tier) the next gather runs inside this
+ * call's conv launch, so that the two memory-latency-bound kernels share the
+ * CUs.  st: as for engram_forward_retrieved (advanced by T tokens).  next_st:
+ * read only, must not be st.  next_e: device, laid out as e of
+ * engram_retrieve for next_L, 16-byte aligned, not overlapping e;
+ * next_B * next_T = 0 skips the prefetch, B * T = 0 leaves only it.  ws as for
+ * engram_forward_retrieved. */
 engram_status engram_forward_retrieved_prefetch(const int32_t* tokens, const void* e, void* H, int64_t B,
-                                                int64_t T, const engram_layer* L, float* alpha_out,
-                                                float* y_out, void* ws, size_t ws_bytes,
-                                                const engram_layer* next_L, const int32_t* next_tokens,
-                                                int64_t next_B, int64_t next_T, void* next_e,
-                                                hipStream_t stream);
+                                                int64_t T, const engram_layer* L, engram_decode_state* st,
+                                                float* alpha_out, float* y_out, void* ws, size_t ws_bytes,
+                                                const engram_layer* next_L, const engram_decode_state* next_st,
+                                                const int32_t* next_tokens, int64_t next_B, int64_t next_T,
+                                                void* next_e, hipStream_t stream);
 
 /* Static LFU admission for the HBM hot-row cache (Ascend RecSDK Engram
  * article, multi-level cache: hot rows by access frequency in fast memory,

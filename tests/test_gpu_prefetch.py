@@ -36,7 +36,7 @@ def stage_names(fn):
     (1, 1, 512, 3, 77, False, True),     # next batch of another shape
     (2, 1, 200, 1, 200, False, True),    # four branches
     (1, 2, 300, 1, 260, True, True),     # MXFP8 rows for the next batch
-    (1, 1, 20, 1, 20, False, False),     # fewer than 8 strips: conv, then gather
+    (1, 1, 20, 1, 20, False, True),      # fewer strips than XCDs: the plain strip order
 ])
 def test_prefetch_equals_separate_calls(config, B, T, nB, nT, mx, fused):
     log(f"prefetch config={config} B={B} T={T} next={nB}x{nT} mx={mx}")
@@ -116,9 +116,8 @@ def test_prefetch_with_empty_halves_and_hot_tier():
 
 @pytest.mark.parametrize("config,table", [(4, "bf16"), (3, "i8")])
 def test_prefetch_of_the_next_layer(config, table):
-    """Layer 0's compute carrying layer 1's retrieval of the same tokens (fused
-    for bf16 tables; int8 tables have no fused form and run the two kernels in
-    turn): equal to the separate calls, bit for bit."""
+    """Layer 0's compute carrying layer 1's retrieval of the same tokens (bf16
+    or int8 tables): equal to the separate calls, bit for bit."""
     log(f"prefetch next layer config={config}")
     kw = dict(B=1, T=300, layers=2) if config == 4 else dict(B=16, T=1, layers=2)
     w = inputs.make_config(config, rows_per_table=997, **kw)
@@ -136,5 +135,44 @@ def test_prefetch_of_the_next_layer(config, table):
     got = eg.rows_buffer(B, T, L1, DEV)
     names = stage_names(lambda: eg.forward_retrieved_prefetch(tok, e0, H2, L0, tok, got, next_layer=L1))
     torch.cuda.synchronize()
-    assert ("conv_gather_kernel" in names) == (table == "bf16" and T >= 32), names
+    assert "conv_gather_kernel" in names, names
     assert torch.equal(_bits(H1), _bits(H2)) and torch.equal(ref, got)
+
+
+def test_decode_steps_with_the_next_layer_prefetched():
+    """Two-layer decode: after a 16-token prefill, each single-token step runs
+    layer 0 with layer 1's retrieval (its own id history) inside layer 0's conv
+    launch, then layer 1 on those rows.  Hidden states, the rows and both
+    decode states equal plain per-layer forwards, bit for bit."""
+    log("prefetch decode")
+    w = inputs.make_config(3, B=32, rows_per_table=997)
+    lays = w.layers
+    Ls = [eg.Layer(l, "bf16", DEV) for l in lays]
+    S, span, d = w.B, (lays[0].kernel_w - 1) * lays[0].dilation, lays[0].d
+    states = {k: [eg.DecodeState(S, 3, 1, span, d, DEV) for _ in Ls] for k in ("plain", "fused")}
+    ctx = torch.from_numpy(w.context).to(DEV)
+    for k in states:
+        Hc = eg.to_device(w.H_context, "bf16", DEV)
+        for L, st in zip(Ls, states[k]):
+            eg.forward(ctx, Hc, L, state=st)
+    rng = np.random.default_rng(21)
+    Hp = eg.to_device(w.H, "bf16", DEV)
+    Hf = Hp.clone()
+    e0 = eg.rows_buffer(S, 1, Ls[0], DEV)
+    e1 = eg.rows_buffer(S, 1, Ls[1], DEV)
+    fused_seen = False
+    for step in range(4):
+        tok = torch.from_numpy(inputs.zipf_tokens(rng, 128_000, 1.1, (S, 1))).to(DEV)
+        for L, st in zip(Ls, states["plain"]):
+            eg.forward(tok, Hp, L, state=st)
+        s0, s1 = states["fused"]
+        eg.retrieve(tok, Ls[0], e0, state=s0)
+        names = stage_names(lambda: eg.forward_retrieved_prefetch(tok, e0, Hf, Ls[0], tok, e1, next_layer=Ls[1],
+                                                                  state=s0, next_state=s1))
+        fused_seen |= "conv_gather_kernel" in names and "state_commit_kernel" not in names
+        eg.forward_retrieved(tok, e1, Hf, Ls[1], state=s1)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(Hp), _bits(Hf)), step
+        for a, b in zip(states["plain"], states["fused"]):
+            assert torch.equal(a.ids, b.ids) and torch.equal(a.pos, b.pos) and torch.equal(a.conv, b.conv), step
+    assert fused_seen
