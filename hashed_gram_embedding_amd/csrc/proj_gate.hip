@@ -17,11 +17,13 @@
 // enough tiles to give every CU two) with eight wavefronts (two per SIMD, so
 // one wavefront's matrix work overlaps another's LDS traffic); K advances 64
 // per step through double-buffered LDS with the 16-byte chunk c of row r
-// stored at chunk c ^ ((r >> 1) & 7).  Global loads run PD slices ahead in
-// registers.  Every load is issued unconditionally (ragged token rows and
-// slices past the end re-read a valid row or slice that is never stored), so
-// the compiler's memory-counter waits stay exact and a wait for one slice
-// never drains the loads of the next.  The epilogue issues all of a token
+// stored at chunk c ^ ((r >> 1) & 7).  bf16 slices go from memory straight
+// into LDS (global_load_lds_dwordx4, one slice in flight while the other
+// buffer is multiplied; ragged token rows re-read the last valid row).  The
+// MXFP8 product stages its slice and scale bytes through registers instead,
+// every load issued unconditionally (slices past the end re-read a valid
+// slice that is never used) so that the compiler's memory-counter waits stay
+// exact.  The epilogue issues all of a token
 // block's h loads before it uses any.  Tiles are ordered XCD by XCD
 // (workgroup i runs on XCD i % 8) with the feature tile fastest, so the
 // workgroups that read the same e rows share an L2.
@@ -74,7 +76,13 @@ __device__ __forceinline__ void advance_state(const ProjGateArgs& a) {
   }
 }
 
-template <int TF, int PD, bool MX, int WT>
+// Main loop variants: DMA = false stages each slice through registers (PD
+// slices in flight) and writes it to LDS; DMA = true loads it straight into
+// the other of two LDS buffers (global_load_lds_dwordx4) while this one is
+// multiplied.  Measured on gfx950 against register staging with two slices
+// in flight: 3-5 % faster, and three LDS buffers (two slices in flight,
+// 128-column tiles only) no faster than two.
+template <int TF, int PD, bool MX, int WT, bool DMA = false>
 __global__ void __launch_bounds__(64 * WF * WT) __attribute__((amdgpu_waves_per_eu(WF * WT / 4, WF * WT / 4)))
 proj_gate_kernel(ProjGateArgs a) {
   constexpr int kThreads = 64 * WF * WT;
@@ -88,6 +96,7 @@ proj_gate_kernel(ProjGateArgs a) {
   constexpr int NE = kEChunks / kThreads;  // e chunks staged per thread
   constexpr int I = TF / WF / 32;          // 32-row feature blocks per wavefront
   constexpr int J = TK / WT / 32;          // 32-row token blocks per wavefront
+  static_assert(!(DMA && MX), "direct-to-LDS loads: bf16 operands only");
   extern __shared__ u32x4_t lds[];
   u32x4_t* Ws = lds;                  // [2][kWChunks]
   u32x4_t* Es = lds + 2 * kWChunks;   // [2][kEChunks]
@@ -211,18 +220,67 @@ proj_gate_kernel(ProjGateArgs a) {
     }                                                                                              \
   }
 
+  if constexpr (DMA) {
+    // Each wavefront instruction fills 64 consecutive 16-byte LDS slots (8
+    // rows of a slice).  Slot s of row r holds chunk s ^ ((r >> 1) & 7), so
+    // lane l, landing in slot c = l & 7 of row l >> 3, fetches that chunk;
+    // the fragment reads are the same as with staged stores.
+    auto issue = [&](int kt, int buf) {
+      const int64_t kb = static_cast<int64_t>(kt) * 128;
 #pragma unroll
-  for (int b = 0; b < PD; ++b) ENGRAM_LOAD_SLICE(b, min(b, ksteps - 1));
-  ENGRAM_STORE_SLICE(0, 0);
-  __syncthreads();
-  for (int kt0 = 0; kt0 < ksteps; kt0 += PD) {
+      for (int i = 0; i < NW; ++i) {
+        const int c = tid + i * kThreads;
+        const int r = c >> 3;
+        const char* src = wbase + static_cast<int64_t>(r) * K * 2 + kb + (((c & 7) ^ ((r >> 1) & 7)) * 16);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                         (__attribute__((address_space(3))) void*)(Ws + buf * kWChunks + i * kThreads + wave * 64),
+                                         16, 0, 0);
+      }
 #pragma unroll
-    for (int u = 0; u < PD; ++u) {
-      const int kt = kt0 + u;
-      ENGRAM_LOAD_SLICE(u, min(kt + PD, ksteps - 1));        // slice kt + PD (clamped)
-      ENGRAM_COMPUTE(kt & 1);
-      ENGRAM_STORE_SLICE((u + 1) % PD, (kt + 1) & 1);        // slice kt + 1 (unused after the last)
-      __syncthreads();
+      for (int i = 0; i < NE; ++i) {
+        const int c = tid + i * kThreads;
+        const int r = c >> 3;
+        const int64_t tok = min(t0 + r, a.n_tok - 1);
+        const char* src = ebase + tok * K * 2 + kb + (((c & 7) ^ ((r >> 1) & 7)) * 16);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                         (__attribute__((address_space(3))) void*)(Es + buf * kEChunks + i * kThreads + wave * 64),
+                                         16, 0, 0);
+      }
+    };
+    issue(0, 0);
+    // unrolled by two so that the buffer indices are constants
+    for (int kt0 = 0; kt0 < ksteps; kt0 += 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int kt = kt0 + u;
+        if (kt < ksteps) {
+          // this lane's loads of slice kt have landed and its fragment reads
+          // of slice kt - 1 have returned; after the barrier, every lane's
+          // have.  (A fence in place of the bare barrier would do the same,
+          // but the compiler then also waits for all outstanding loads.)
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          // into the buffer of slice kt - 1, which every wavefront has read
+          if (kt + 1 < ksteps) issue(kt + 1, u ^ 1);
+          ENGRAM_COMPUTE(u);
+        }
+      }
+    }
+    // the epilogue reuses the LDS: all fragment reads done, no load in flight
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
+#pragma unroll
+    for (int b = 0; b < PD; ++b) ENGRAM_LOAD_SLICE(b, min(b, ksteps - 1));
+    ENGRAM_STORE_SLICE(0, 0);
+    __syncthreads();
+    for (int kt0 = 0; kt0 < ksteps; kt0 += PD) {
+#pragma unroll
+      for (int u = 0; u < PD; ++u) {
+        const int kt = kt0 + u;
+        ENGRAM_LOAD_SLICE(u, min(kt + PD, ksteps - 1));        // slice kt + PD (clamped)
+        ENGRAM_COMPUTE(kt & 1);
+        ENGRAM_STORE_SLICE((u + 1) % PD, (kt + 1) & 1);        // slice kt + 1 (unused after the last)
+        __syncthreads();
+      }
     }
   }
 #undef ENGRAM_LOAD_SLICE
@@ -435,7 +493,7 @@ proj_gate_small_kernel(ProjGateArgs a) {
   advance_state(a);
 }
 
-template <int TF, int PD, bool MX, int WT = 4>
+template <int TF, int PD, bool MX, int WT = 4, bool DMA = false>
 hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   a.tiles_f = a.N / TF;
   a.tiles_t = static_cast<int>((a.n_tok + TK - 1) / TK);
@@ -449,12 +507,12 @@ hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if ((attr_set.load() & bit) == 0) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_kernel<TF, PD, MX, WT>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_kernel<TF, PD, MX, WT, DMA>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit);
   }
-  launch_k((proj_gate_kernel<TF, PD, MX, WT>), dim3(a.tiles_f * a.tiles_t), dim3(64 * WF * WT), lds, s, a);
+  launch_k((proj_gate_kernel<TF, PD, MX, WT, DMA>), dim3(a.tiles_f * a.tiles_t), dim3(64 * WF * WT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -463,7 +521,12 @@ hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
 // Few tokens: the small kernel (64-column statistics tiles); otherwise the
 // large one with 256-column tiles when there are enough of them.  The MXFP8
 // product always takes the large kernel with 128-column tiles.
-bool proj_gate_small(int64_t n_tok, int N) { return ((n_tok + TK - 1) / TK) * (N / 128) < 128; }
+//
+// The small kernel's time grows with tokens x features; the large one costs
+// about the same (its K loop's latency) until its tiles fill the chip.  On
+// gfx950 at K = 1024 the two meet near 2^20 token-features (512 tokens at
+// N = 2048, 200 at N = 5120); past that the large kernel wins.
+bool proj_gate_small(int64_t n_tok, int N) { return n_tok * static_cast<int64_t>(N) <= (int64_t{1} << 20); }
 
 int proj_gate_tile_f(int64_t n_tok, int N, int d, bool mx) {
   if (mx) return 128;
@@ -493,10 +556,8 @@ hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
              s, a);
     return hipGetLastError();
   }
-  const bool pd2 = (in.K / BK) % 2 == 0;
-  if (proj_gate_tile_f(in.n_tok, in.N, in.d, false) == 256)
-    return pd2 ? launch_tf<256, 2, false>(in, s) : launch_tf<256, 1, false>(in, s);
-  return pd2 ? launch_tf<128, 2, false>(in, s) : launch_tf<128, 1, false>(in, s);
+  if (proj_gate_tile_f(in.n_tok, in.N, in.d, false) == 256) return launch_tf<256, 1, false, 4, true>(in, s);
+  return launch_tf<128, 1, false, 4, true>(in, s);
 }
 
 }  // namespace engram
