@@ -27,6 +27,7 @@
 // block's h loads before it uses any.  Tiles are ordered XCD by XCD
 // (workgroup i runs on XCD i % 8) with the feature tile fastest, so the
 // workgroups that read the same e rows share an L2.
+#include <algorithm>
 #include <atomic>
 
 #include "device_util.h"
@@ -293,7 +294,9 @@ proj_gate_kernel(ProjGateArgs a) {
   const bool is_v = f0 < d;
   const int m = is_v ? 0 : f0 / d - 1;
   const int c0 = (is_v ? f0 : f0 - (1 + m) * d) + wf * (TF / WF) + (lane >> 5) * 4;
-  float4* red = reinterpret_cast<float4*>(lds);   // [TK][WF] partials of the feature wavefronts
+  // the main loop's LDS is free now: the h tile of a key tile goes at its
+  // start ([TK][TF] bf16), the per-token partials after it
+  float4* red = reinterpret_cast<float4*>(lds + TK * TF / 8);   // [TK][WF] partials of the feature wavefronts
   if (is_v) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -315,36 +318,62 @@ proj_gate_kernel(ProjGateArgs a) {
       if ((lane >> 5) == 0) red[tl * WF + wf] = make_float4(0.f, 0.f, 0.f, s3);
     }
   } else {
+    // The tile's h rows ([TK][TF] bf16, 2*TF contiguous bytes per token) go
+    // into LDS with 16-byte direct loads, a wavefront instruction covering
+    // whole rows; chunk c of row r lands in slot c ^ (r & 15), so that the
+    // reads below (32 rows, one chunk each) spread over all banks.  Token
+    // rows past the end re-read the last valid row.  Sum k^2 meanwhile.
+    constexpr int HC = TF / 8;                 // 16-byte chunks per h row
+    constexpr int NH = TK * HC / kThreads;     // loads per thread
+    u32x4_t* Hs = lds;
+    const int fb = f0 - (1 + m) * d;           // the tile's first feature within branch m
+#pragma unroll
+    for (int q = 0; q < NH; ++q) {
+      const int u = q * kThreads + wave * 64 + lane;   // LDS slot this lane fills
+      const int r = u / HC, sl = u % HC;
+      const int64_t tok = min(t0 + r, a.n_tok - 1);
+      const uint16_t* src = a.H + (tok * a.M + m) * d + fb + (sl ^ (r & 15)) * 8;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                       (__attribute__((address_space(3))) void*)(Hs + q * kThreads + wave * 64),
+                                       16, 0, 0);
+    }
+    float s1[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int tl = wt * (TK / WT) + j * 32 + (lane & 31);
-      // this token block's h loads first (row clamped: always a valid address), then the sums
-      const int64_t tok = min(t0 + tl, a.n_tok - 1);
-      const uint16_t* hrow = a.H + (tok * a.M + m) * d + c0;
-      uint2 hq[I][4];
+      s1[j] = 0.f;
 #pragma unroll
       for (int i = 0; i < I; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) hq[i][g] = *reinterpret_cast<const uint2*>(hrow + i * 32 + g * 8);
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+        for (int g = 0; g < 4; ++g)
+          s1[j] += acc[i][j][4 * g] * acc[i][j][4 * g] + acc[i][j][4 * g + 1] * acc[i][j][4 * g + 1] +
+                   acc[i][j][4 * g + 2] * acc[i][j][4 * g + 2] + acc[i][j][4 * g + 3] * acc[i][j][4 * g + 3];
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const uint2* Hs2 = reinterpret_cast<const uint2*>(lds);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int tl = wt * (TK / WT) + j * 32 + (lane & 31);
+      float s0 = 0.f, s2 = 0.f;
 #pragma unroll
       for (int i = 0; i < I; ++i) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          // features wf*TF/WF + i*32 + g*8 + (lane>>5)*4 .. +3: half (lane>>5) of one chunk
+          const int c = wf * (TF / WF) / 8 + i * 4 + g;
+          const uint2 q = Hs2[(tl * HC + (c ^ (tl & 15))) * 2 + (lane >> 5)];
           const float x0 = acc[i][j][4 * g], x1 = acc[i][j][4 * g + 1];
           const float x2 = acc[i][j][4 * g + 2], x3 = acc[i][j][4 * g + 3];
-          const uint2 q = hq[i][g];
           const float h0 = __uint_as_float(q.x << 16), h1 = __uint_as_float(q.x & 0xffff0000u);
           const float h2 = __uint_as_float(q.y << 16), h3 = __uint_as_float(q.y & 0xffff0000u);
           s0 += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
-          s1 += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
           s2 += h0 * x0 + h1 * x1 + h2 * x2 + h3 * x3;
         }
       }
+      float s1j = s1[j];
       s0 += __shfl_xor(s0, 32, 64);
-      s1 += __shfl_xor(s1, 32, 64);
+      s1j += __shfl_xor(s1j, 32, 64);
       s2 += __shfl_xor(s2, 32, 64);
-      if ((lane >> 5) == 0) red[tl * WF + wf] = make_float4(s0, s1, s2, 0.f);
+      if ((lane >> 5) == 0) red[tl * WF + wf] = make_float4(s0, s1j, s2, 0.f);
     }
   }
   __syncthreads();
@@ -497,8 +526,11 @@ template <int TF, int PD, bool MX, int WT = 4, bool DMA = false>
 hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   a.tiles_f = a.N / TF;
   a.tiles_t = static_cast<int>((a.n_tok + TK - 1) / TK);
-  const size_t lds = static_cast<size_t>(2 * (TF + TK) * 8) * sizeof(u32x4_t) +
-                     (MX ? static_cast<size_t>(2 * (TF + TK)) * sizeof(uint32_t) : 0);
+  // main loop: two slices (and MXFP8 scale words); epilogue: the h tile and
+  // the per-token partials
+  const size_t lds = std::max(static_cast<size_t>(2 * (TF + TK) * 8) * sizeof(u32x4_t) +
+                                  (MX ? static_cast<size_t>(2 * (TF + TK)) * sizeof(uint32_t) : 0),
+                              static_cast<size_t>(TK * TF) * 2 + static_cast<size_t>(TK * WF) * sizeof(float4));
   // more than 64 KiB of dynamic LDS exceeds the default per-workgroup limit;
   // raise it once per device and instantiation (gfx950 has 160 KiB per CU)
   static std::atomic<uint64_t> attr_set{0};
