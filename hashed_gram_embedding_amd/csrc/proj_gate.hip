@@ -23,8 +23,8 @@
 // MXFP8 product stages its slice and scale bytes through registers instead,
 // every load issued unconditionally (slices past the end re-read a valid
 // slice that is never used) so that the compiler's memory-counter waits stay
-// exact.  The epilogue issues all of a token
-// block's h loads before it uses any.  Tiles are ordered XCD by XCD
+// exact.  The epilogue stages a key tile's h rows and a value tile's v
+// through LDS, so that both move as whole rows.  Tiles are ordered XCD by XCD
 // (workgroup i runs on XCD i % 8) with the feature tile fastest, so the
 // workgroups that read the same e rows share an L2.
 #include <algorithm>
@@ -293,15 +293,23 @@ proj_gate_kernel(ProjGateArgs a) {
   const int d = a.d;
   const bool is_v = f0 < d;
   const int m = is_v ? 0 : f0 / d - 1;
-  const int c0 = (is_v ? f0 : f0 - (1 + m) * d) + wf * (TF / WF) + (lane >> 5) * 4;
-  // the main loop's LDS is free now: the h tile of a key tile goes at its
-  // start ([TK][TF] bf16), the per-token partials after it
+  // the main loop's LDS is free now: a value tile turns v around in its
+  // first 4*TK*TF/WT bytes and a key tile holds its h rows ([TK][TF] bf16)
+  // there; the per-token partials go after them
   float4* red = reinterpret_cast<float4*>(lds + TK * TF / 8);   // [TK][WF] partials of the feature wavefronts
   if (is_v) {
+    // Each wavefront turns its 32-token x TF/WF-feature block of v around in
+    // a private LDS region ([32][VC] 16-byte chunks, chunk c of row r at
+    // c ^ (r & 15), so that both the accumulator-layout writes and the row
+    // reads spread over all banks) and stores whole rows: half a wavefront
+    // writes 4*TF/WF contiguous bytes of one token.
+    constexpr int VC = TF / WF / 4;                      // 16-byte chunks per row of the block
+    float4* Vs = reinterpret_cast<float4*>(lds) + wave * 32 * VC;
+    float* vrow0 = a.v + t0 * d + f0 + wf * (TF / WF);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int tl = wt * (TK / WT) + j * 32 + (lane & 31);
-      const int64_t tok = t0 + tl;
+      const int r = lane & 31;
+      const int tl = wt * (TK / WT) + j * 32 + r;
       float s3 = 0.f;
 #pragma unroll
       for (int i = 0; i < I; ++i) {
@@ -309,13 +317,23 @@ proj_gate_kernel(ProjGateArgs a) {
         for (int g = 0; g < 4; ++g) {
           const float x0 = acc[i][j][4 * g], x1 = acc[i][j][4 * g + 1];
           const float x2 = acc[i][j][4 * g + 2], x3 = acc[i][j][4 * g + 3];
-          if (tok < a.n_tok)
-            *reinterpret_cast<float4*>(a.v + tok * d + c0 + i * 32 + g * 8) = make_float4(x0, x1, x2, x3);
+          // features i*32 + g*8 + (lane>>5)*4 .. +3 of the block: chunk i*8 + g*2 + (lane>>5)
+          Vs[r * VC + ((i * 8 + g * 2 + (lane >> 5)) ^ (r & 15))] = make_float4(x0, x1, x2, x3);
           s3 += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
         }
       }
       s3 += __shfl_xor(s3, 32, 64);
       if ((lane >> 5) == 0) red[tl * WF + wf] = make_float4(0.f, 0.f, 0.f, s3);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wavefront's block is in LDS
+#pragma unroll
+      for (int it = 0; it < 32 * VC / 64; ++it) {
+        const int u = it * 64 + lane;
+        const int rr = u / VC, c = u % VC;
+        const int64_t trow = wt * (TK / WT) + j * 32 + rr;
+        const float4 x = Vs[rr * VC + (c ^ (rr & 15))];
+        if (t0 + trow < a.n_tok) *reinterpret_cast<float4*>(vrow0 + trow * d + c * 4) = x;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next block's writes
     }
   } else {
     // The tile's h rows ([TK][TF] bf16, 2*TF contiguous bytes per token) go
