@@ -412,11 +412,14 @@ proj_gate_kernel(ProjGateArgs a) {
 
 // Small batches (decode): a 64-feature x 32-token tile per workgroup, so that
 // a few hundred tokens still give hundreds of workgroups.  The four
-// wavefronts split K four ways; each loads its MFMA operands straight from
-// memory (L2) into fragment registers -- a 16-byte run of K per lane for
-// both operands -- in batches of four K16 steps, the next batch in flight
-// while the current one is multiplied, so the whole K range costs a couple
-// of memory round trips instead of one per slice.  The partial tiles are
+// wavefronts split K four ways.  Each stages its operands for four K16 steps
+// (a 128-byte run of every W and e row) in a private pair of LDS buffers with
+// 16-byte direct loads, a wavefront instruction covering 8 whole runs, the
+// next batch in flight while the current one is multiplied; the MFMA
+// fragments are read from LDS.  (Loading fragments straight from memory, each
+// load instruction touches 32 rows at 32 bytes apiece, and the kernel took
+// twice as long.)  Only the wavefront itself writes and reads its buffers, so
+// the loop needs memory-counter waits but no barrier.  The partial tiles are
 // summed through LDS and the epilogue (v store, gate sums per 64 columns)
 // follows the large kernel's.
 constexpr int kSmallTF = 64;
@@ -424,10 +427,19 @@ constexpr int kSmallTK = 32;
 constexpr int kSmallWaves = 4;
 constexpr int kSmallBatch = 4;   // K16 steps per load batch
 
+// one wavefront's staging buffer: 64 W rows and 32 e rows of a batch's
+// 128-byte run, chunk c of row r at slot c ^ (r & 7)
+constexpr int kSmallRows = kSmallTF + kSmallTK;
+constexpr int kSmallStage = kSmallRows * 8;   // 16-byte slots per buffer
+constexpr int kSmallLds = kSmallWaves * 2 * kSmallStage * 16;   // bytes of staging (the partial sums reuse it)
+
 __global__ void __launch_bounds__(64 * kSmallWaves)
 proj_gate_small_kernel(ProjGateArgs a) {
-  __shared__ float part[kSmallWaves][kSmallTF][kSmallTK + 1];   // +1: no bank conflicts on the sums
+  extern __shared__ u32x4_t small_lds[];
+  // after the main loop: the partial tiles, +1 column so that the sums are conflict free
+  auto part = reinterpret_cast<float (*)[kSmallTF][kSmallTK + 1]>(small_lds);
   __shared__ float4 red[kSmallWaves][kSmallTK];
+  static_assert(kSmallWaves * kSmallTF * (kSmallTK + 1) * 4 <= kSmallLds, "partial sums fit the staging LDS");
   const int tf = blockIdx.x % a.tiles_f;
   const int tt = blockIdx.x / a.tiles_f;
   const int f0 = tf * kSmallTF;
@@ -438,40 +450,78 @@ proj_gate_small_kernel(ProjGateArgs a) {
   const int kq = K / kSmallWaves;             // this wavefront's K range: [wave*kq, (wave+1)*kq)
   const int nsteps = kq / 16;                 // K16 steps (K is a multiple of 64: at least one)
   const int half = lane >> 5;                 // lanes 32-63 hold K elements 8..15 of each step
-  const int64_t tok = min(t0 + (lane & 31), a.n_tok - 1);
-  const uint16_t* wrow0 = a.w + static_cast<int64_t>(f0 + (lane & 31)) * K + wave * kq + half * 8;
-  const uint16_t* wrow1 = wrow0 + static_cast<int64_t>(32) * K;
-  const uint16_t* erow = a.e + tok * K + wave * kq + half * 8;
+
+  // epilogue thread (token tl, feature eighth fq): a key tile's 8 h values
+  // are loaded now, alongside the first operand batch, not after the loop
+  const int tl = threadIdx.x & (kSmallTK - 1);
+  const int fq = threadIdx.x / kSmallTK;      // 0..7, 8 features each
+  const int64_t gt = t0 + tl;
+  const bool valid = gt < a.n_tok;
+  const int64_t ct = valid ? gt : a.n_tok - 1;
+  const int d = a.d;
+  const bool is_v = f0 < d;
+  const int m = is_v ? 0 : f0 / d - 1;
+  const int c0 = (is_v ? f0 : f0 - (1 + m) * d) + fq * 8;
+  uint4 hq = make_uint4(0u, 0u, 0u, 0u);
+  if (!is_v) hq = *reinterpret_cast<const uint4*>(a.H + (ct * a.M + m) * d + c0);
 
   f32x16_t acc0, acc1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
 
-  u32x4_t fa0[2][kSmallBatch], fa1[2][kSmallBatch], fb[2][kSmallBatch];
-#define ENGRAM_SMALL_LOAD(buf, s0)                                                                 \
-  _Pragma("unroll") for (int j = 0; j < kSmallBatch; ++j) {                                        \
-    const int kk = min((s0) + j, nsteps - 1) * 16;                                                 \
-    fa0[buf][j] = *reinterpret_cast<const u32x4_t*>(wrow0 + kk);                                   \
-    fa1[buf][j] = *reinterpret_cast<const u32x4_t*>(wrow1 + kk);                                   \
-    fb[buf][j] = *reinterpret_cast<const u32x4_t*>(erow + kk);                                     \
-  }
-  ENGRAM_SMALL_LOAD(0, 0);
-  for (int s0 = 0; s0 < nsteps; s0 += 2 * kSmallBatch) {
+  // Batch b covers K elements [b*64, b*64 + 64) of this wavefront's range:
+  // 12 instructions, 8 rows each (lane l: row 8i + (l >> 3), slot l & 7,
+  // which fetches chunk (l & 7) ^ (row & 7)).  Chunks past the range (K/4 not
+  // a multiple of 64) re-read the range's last chunk and are never used.
+  u32x4_t* stg = small_lds + wave * 2 * kSmallStage;
+  const char* wbase = reinterpret_cast<const char*>(a.w + static_cast<int64_t>(f0) * K + wave * kq);
+  const char* ebase = reinterpret_cast<const char*>(a.e + wave * kq);
+  const int nb = (nsteps + kSmallBatch - 1) / kSmallBatch;
+  auto issue = [&](int b, int buf) {
+#pragma unroll
+    for (int i = 0; i < kSmallRows / 8; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      const int ch = (lane & 7) ^ (r & 7);
+      const int ke = min(b * 64 + ch * 8, kq - 8);            // element offset in the range
+      const int64_t row = r < kSmallTF ? static_cast<int64_t>(r) : min(t0 + (r - kSmallTF), a.n_tok - 1);
+      const char* src = (r < kSmallTF ? wbase : ebase) + (row * K + ke) * 2;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                       (__attribute__((address_space(3))) void*)(stg + buf * kSmallStage + i * 64),
+                                       16, 0, 0);
+    }
+  };
+  issue(0, 0);
+  for (int b0 = 0; b0 < nb; b0 += 2) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int sb = s0 + u * kSmallBatch;     // first step of the batch in buffer u
-      ENGRAM_SMALL_LOAD(u ^ 1, sb + kSmallBatch);  // next batch (clamped past the end, never used)
+      const int b = b0 + u;
+      if (b < nb) {
+        // this wavefront's fragment reads of buffer u ^ 1 (batch b - 1) are done
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (b + 1 < nb) {
+          issue(b + 1, u ^ 1);
+          asm volatile("s_waitcnt vmcnt(12)" ::: "memory");   // batch b has landed, b + 1 in flight
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        const u32x4_t* sb = stg + u * kSmallStage;
 #pragma unroll
-      for (int j = 0; j < kSmallBatch; ++j) {
-        if (sb + j < nsteps) {
-          const bf16x8_t b = __builtin_bit_cast(bf16x8_t, fb[u][j]);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa0[u][j]), b, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa1[u][j]), b, acc1, 0, 0, 0);
+        for (int j = 0; j < kSmallBatch; ++j) {
+          if (b * kSmallBatch + j < nsteps) {
+            const int c = 2 * j + half;          // this lane's chunk of the run
+            const int r = lane & 31;
+            const bf16x8_t fa0 = __builtin_bit_cast(bf16x8_t, sb[r * 8 + (c ^ (r & 7))]);
+            const bf16x8_t fa1 = __builtin_bit_cast(bf16x8_t, sb[(32 + r) * 8 + (c ^ (r & 7))]);
+            const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, sb[(kSmallTF + r) * 8 + (c ^ (r & 7))]);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb, acc1, 0, 0, 0);
+          }
         }
       }
     }
   }
-#undef ENGRAM_SMALL_LOAD
+  // every wavefront's fragment reads are done before the partial sums reuse the LDS
+  __syncthreads();
 
   // acc_i[4g + r]: feature i*32 + g*8 + half*4 + r of the tile, token lane & 31
 #pragma unroll
@@ -483,16 +533,7 @@ proj_gate_small_kernel(ProjGateArgs a) {
     }
   __syncthreads();
 
-  // thread (token tl, feature quarter fq): 16 features of one token, summed over the waves
-  const int tl = threadIdx.x & (kSmallTK - 1);
-  const int fq = threadIdx.x / kSmallTK;      // 0..7, 8 features each
-  const int64_t gt = t0 + tl;
-  const bool valid = gt < a.n_tok;
-  const int64_t ct = valid ? gt : a.n_tok - 1;
-  const int d = a.d;
-  const bool is_v = f0 < d;
-  const int m = is_v ? 0 : f0 / d - 1;
-  const int c0 = (is_v ? f0 : f0 - (1 + m) * d) + fq * 8;
+  // thread (token tl, feature eighth fq): 8 features of one token, summed over the waves
   float x[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -511,7 +552,6 @@ proj_gate_small_kernel(ProjGateArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) s3 += x[i] * x[i];
   } else {
-    const uint4 hq = *reinterpret_cast<const uint4*>(a.H + (ct * a.M + m) * d + c0);
     const uint32_t hw[4] = {hq.x, hq.y, hq.z, hq.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -602,8 +642,19 @@ hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
     ProjGateArgs a = in;
     a.tiles_f = a.N / kSmallTF;
     a.tiles_t = static_cast<int>((a.n_tok + kSmallTK - 1) / kSmallTK);
-    launch_k(proj_gate_small_kernel, dim3(static_cast<unsigned>(a.tiles_f * a.tiles_t)), dim3(64 * kSmallWaves), 0,
-             s, a);
+    static std::atomic<uint64_t> attr_set{0};   // > 64 KiB of dynamic LDS, raised once per device
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = 1ull << (dev & 63);
+    if ((attr_set.load() & bit) == 0) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_small_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kSmallLds);
+      if (e != hipSuccess) return e;
+      attr_set.fetch_or(bit);
+    }
+    launch_k(proj_gate_small_kernel, dim3(static_cast<unsigned>(a.tiles_f * a.tiles_t)), dim3(64 * kSmallWaves),
+             kSmallLds, s, a);
     return hipGetLastError();
   }
   if (proj_gate_tile_f(in.n_tok, in.N, in.d, false) == 256) return launch_tf<256, 1, false, 4, true>(in, s);
