@@ -94,9 +94,9 @@ def kernel_units(n_tok, lay, hdtype, hot_hit=None, mx=False):
     N = (1 + M) * d
     flops = 2.0 * n_tok * N * d_mem
     # Below the matrix cores' ridge (the library's small-batch projection, used
-    # while fewer than 128 tiles of 256 tokens x 128 features exist) the
-    # projection is bound by reading W: W, e and h in, v and statistics out.
-    small = fused and ((n_tok + 255) // 256) * (N // 128) < 128
+    # up to 7 * 2^18 token-features) the projection is bound by reading W:
+    # W, e and h in, v and statistics out.
+    small = fused and n_tok * N <= 7 << 18
     proj = ("hbm", N * d_mem * es + n_tok * (d_mem * es + M * d * es + d * 4 + 16 * N // 64)) if small \
         else ("mfma", flops)
     units = {

@@ -613,10 +613,11 @@ hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
 // product always takes the large kernel with 128-column tiles.
 //
 // The small kernel's time grows with tokens x features; the large one costs
-// about the same (its K loop's latency) until its tiles fill the chip.  On
-// gfx950 at K = 1024 the two meet near 2^20 token-features (512 tokens at
-// N = 2048, 200 at N = 5120); past that the large kernel wins.
-bool proj_gate_small(int64_t n_tok, int N) { return n_tok * static_cast<int64_t>(N) <= (int64_t{1} << 20); }
+// about the same (its K loop's latency) until its tiles fill the chip.
+// Measured on gfx950 at K = 1024 (small / large, us): N = 2048, 768 tokens
+// 14.4 / 17.5 and 1,024 tokens 18.3 / 17.7; N = 5120, 256 tokens 13.3 / 16.8
+// and 384 tokens 17.7 / 17.3.  The two meet near 1.9 M token-features.
+bool proj_gate_small(int64_t n_tok, int N) { return n_tok * static_cast<int64_t>(N) <= (int64_t{7} << 18); }
 
 int proj_gate_tile_f(int64_t n_tok, int N, int d, bool mx) {
   if (mx) return 128;

@@ -209,10 +209,11 @@ def test_forward_fp32(B, T, dim):
     _forward_check(w, tag="c0")
 
 
-# Up to 2^20 token-features (512 tokens at N = 2048) the projection runs the
-# small-batch kernel (64 x 32 tiles, K split over wavefronts): (1, 1, 1),
-# (1, 3, 11) and (2, 1, 40); (1, 2, 300), (2, 2, 130), (1, 2, 1100) and
-# (2, 1, 900) run the large-tile kernel with a ragged last token tile.
+# Up to 7 * 2^18 token-features (896 tokens at N = 2048, 358 at N = 5120) the
+# projection runs the small-batch kernel (64 x 32 tiles, K split over
+# wavefronts): (1, 1, 1), (1, 3, 11), (2, 1, 40), (1, 2, 300) and (2, 2, 130);
+# (1, 2, 1100) and (2, 1, 900) run the large-tile kernel with a ragged last
+# token tile.
 @pytest.mark.parametrize("config,B,T", [(1, 2, 300), (1, 1, 1), (1, 3, 11), (2, 1, 40), (2, 2, 130), (1, 2, 1100),
                                         (2, 1, 900)])
 def test_forward_bf16(config, B, T):
