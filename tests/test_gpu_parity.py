@@ -222,6 +222,17 @@ def test_forward_bf16(config, B, T):
     _forward_check(w, tag=f"c{config}")
 
 
+
+# Narrow tables: d_mem = 16 x 8 = 128 or 16 x 32 = 512 (K of the projection).
+# The small-batch kernel's K range per wavefront is then 32 or 128 elements,
+# a partial or a whole number of its 64-element load batches; 1,100 tokens at
+# d_mem = 128 take the large-tile kernel with two K slices.
+@pytest.mark.parametrize("table_dim,B,T", [(8, 2, 40), (32, 1, 300), (8, 1, 1100)])
+def test_forward_bf16_narrow_tables(table_dim, B, T):
+    log(f"forward bf16 narrow tables table_dim={table_dim} B={B} T={T}")
+    w = small(1, B=B, T=T, table_dim=table_dim)
+    _forward_check(w, tag=f"c1 table_dim={table_dim}")
+
 # Hidden widths off the fused path (d not a multiple of 128: the separate
 # product, then whole-row gate statistics) and several branches in fp32.
 @pytest.mark.parametrize("dtype,d,M,B,T", [("bf16", 192, 2, 2, 50), ("bf16", 64, 3, 1, 70), ("f32", 128, 2, 2, 33)])
