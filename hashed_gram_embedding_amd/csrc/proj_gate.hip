@@ -438,7 +438,6 @@ proj_gate_small_kernel(ProjGateArgs a) {
   extern __shared__ u32x4_t small_lds[];
   // after the main loop: the partial tiles, +1 column so that the sums are conflict free
   auto part = reinterpret_cast<float (*)[kSmallTF][kSmallTK + 1]>(small_lds);
-  __shared__ float4 red[kSmallWaves][kSmallTK];
   static_assert(kSmallWaves * kSmallTF * (kSmallTK + 1) * 4 <= kSmallLds, "partial sums fit the staging LDS");
   const int tf = blockIdx.x % a.tiles_f;
   const int tt = blockIdx.x / a.tiles_f;
@@ -451,10 +450,11 @@ proj_gate_small_kernel(ProjGateArgs a) {
   const int nsteps = kq / 16;                 // K16 steps (K is a multiple of 64: at least one)
   const int half = lane >> 5;                 // lanes 32-63 hold K elements 8..15 of each step
 
-  // epilogue thread (token tl, feature eighth fq): a key tile's 8 h values
-  // are loaded now, alongside the first operand batch, not after the loop
-  const int tl = threadIdx.x & (kSmallTK - 1);
-  const int fq = threadIdx.x / kSmallTK;      // 0..7, 8 features each
+  // epilogue thread (token tl, feature eighth fq; the 8 threads of a token are
+  // consecutive lanes, so that v stores and h loads move whole row runs): a
+  // key tile's 8 h values are loaded now, alongside the first operand batch
+  const int tl = threadIdx.x >> 3;
+  const int fq = threadIdx.x & 7;             // 8 features each
   const int64_t gt = t0 + tl;
   const bool valid = gt < a.n_tok;
   const int64_t ct = valid ? gt : a.n_tok - 1;
@@ -561,22 +561,15 @@ proj_gate_small_kernel(ProjGateArgs a) {
       s2 += h * x[i];
     }
   }
-  // the 8 feature groups of a token sit in lanes tl, tl+32 of waves 0..3
-  s0 += __shfl_xor(s0, 32, 64);
-  s1 += __shfl_xor(s1, 32, 64);
-  s2 += __shfl_xor(s2, 32, 64);
-  s3 += __shfl_xor(s3, 32, 64);
-  if (lane < 32) red[wave][tl] = make_float4(s0, s1, s2, s3);
-  __syncthreads();
-  if (threadIdx.x < kSmallTK && t0 + threadIdx.x < a.n_tok) {
-    float4 p = red[0][threadIdx.x];
+  // the 8 feature groups of a token are lanes 8k .. 8k+7 of one wavefront
 #pragma unroll
-    for (int w = 1; w < kSmallWaves; ++w) {
-      const float4 q = red[w][threadIdx.x];
-      p = make_float4(p.x + q.x, p.y + q.y, p.z + q.z, p.w + q.w);
-    }
-    a.stats[(t0 + threadIdx.x) * a.tiles_f + tf] = p;
+  for (int off = 1; off < 8; off <<= 1) {
+    s0 += __shfl_xor(s0, off, 64);
+    s1 += __shfl_xor(s1, off, 64);
+    s2 += __shfl_xor(s2, off, 64);
+    s3 += __shfl_xor(s3, off, 64);
   }
+  if (fq == 0 && valid) a.stats[gt * a.tiles_f + tf] = make_float4(s0, s1, s2, s3);
   advance_state(a);
 }
 
