@@ -17,13 +17,11 @@
 // enough tiles to give every CU two) with eight wavefronts (two per SIMD, so
 // one wavefront's matrix work overlaps another's LDS traffic); K advances 64
 // per step through double-buffered LDS with the 16-byte chunk c of row r
-// stored at chunk c ^ ((r >> 1) & 7).  bf16 slices go from memory straight
-// into LDS (global_load_lds_dwordx4, one slice in flight while the other
-// buffer is multiplied; ragged token rows re-read the last valid row).  The
-// MXFP8 product stages its slice and scale bytes through registers instead,
-// every load issued unconditionally (slices past the end re-read a valid
-// slice that is never used) so that the compiler's memory-counter waits stay
-// exact.  The epilogue stages a key tile's h rows and a value tile's v
+// stored at chunk c ^ ((r >> 1) & 7).  Slices go from memory straight into
+// LDS (global_load_lds_dwordx4, one slice in flight while the other buffer
+// is multiplied; ragged token rows re-read the last valid row); an MXFP8
+// slice is 128 codes per row, the same 128 bytes, and its per-row scale
+// words follow with 4-byte direct loads.  The epilogue stages a key tile's h rows and a value tile's v
 // through LDS, so that both move as whole rows.  Tiles are ordered XCD by XCD
 // (workgroup i runs on XCD i % 8) with the feature tile fastest, so the
 // workgroups that read the same e rows share an L2.
@@ -97,7 +95,6 @@ proj_gate_kernel(ProjGateArgs a) {
   constexpr int NE = kEChunks / kThreads;  // e chunks staged per thread
   constexpr int I = TF / WF / 32;          // 32-row feature blocks per wavefront
   constexpr int J = TK / WT / 32;          // 32-row token blocks per wavefront
-  static_assert(!(DMA && MX), "direct-to-LDS loads: bf16 operands only");
   extern __shared__ u32x4_t lds[];
   u32x4_t* Ws = lds;                  // [2][kWChunks]
   u32x4_t* Es = lds + 2 * kWChunks;   // [2][kEChunks]
@@ -232,7 +229,7 @@ proj_gate_kernel(ProjGateArgs a) {
       for (int i = 0; i < NW; ++i) {
         const int c = tid + i * kThreads;
         const int r = c >> 3;
-        const char* src = wbase + static_cast<int64_t>(r) * K * 2 + kb + (((c & 7) ^ ((r >> 1) & 7)) * 16);
+        const char* src = wbase + static_cast<int64_t>(r) * K * ESZ + kb + (((c & 7) ^ ((r >> 1) & 7)) * 16);
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
                                          (__attribute__((address_space(3))) void*)(Ws + buf * kWChunks + i * kThreads + wave * 64),
                                          16, 0, 0);
@@ -242,10 +239,24 @@ proj_gate_kernel(ProjGateArgs a) {
         const int c = tid + i * kThreads;
         const int r = c >> 3;
         const int64_t tok = min(t0 + r, a.n_tok - 1);
-        const char* src = ebase + tok * K * 2 + kb + (((c & 7) ^ ((r >> 1) & 7)) * 16);
+        const char* src = ebase + tok * K * ESZ + kb + (((c & 7) ^ ((r >> 1) & 7)) * 16);
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
                                          (__attribute__((address_space(3))) void*)(Es + buf * kEChunks + i * kThreads + wave * 64),
                                          16, 0, 0);
+      }
+      if constexpr (MX) {
+        // the slice's scale word of every row (4 blocks of 32 codes): W rows,
+        // then e rows, 64 rows per wavefront instruction, one instruction
+        // for each of the first (TF + TK) / 64 wavefronts
+        static_assert((TF + TK) % 64 == 0 && (TF + TK) / 64 <= WF * WT, "one scale instruction per wavefront");
+        if (wave < (TF + TK) / 64) {
+          const int r = wave * 64 + lane;
+          const uint8_t* src = r < TF ? a.w_scale + static_cast<int64_t>(f0 + r) * (K / 32) + kt * 4
+                                      : a.e_scale + min(t0 + (r - TF), a.n_tok - 1) * (K / 32) + kt * 4;
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                           (__attribute__((address_space(3))) void*)(Ss + buf * (TF + TK) + wave * 64),
+                                           4, 0, 0);
+        }
       }
     };
     issue(0, 0);
@@ -626,10 +637,10 @@ hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
   if (in.N % 128 != 0) return hipErrorInvalidValue;
   const bool mx = in.e_scale != nullptr;
   if (mx) {
-    // 128-feature tiles, one slice in flight: the FP8 operands of two slices
-    // and the 256-feature tile's accumulators do not fit the register budget
+    // 128-feature tiles, slices straight into LDS like the bf16 product
+    // (the 256-feature tile's accumulators and FP8 operands spill registers)
     if (in.K % 128 != 0 || in.w_scale == nullptr) return hipErrorInvalidValue;
-    return launch_tf<128, 1, true>(in, s);
+    return launch_tf<128, 1, true, 4, true>(in, s);
   }
   if (in.K % BK != 0) return hipErrorInvalidValue;
   if (proj_gate_small(in.n_tok, in.N)) {
