@@ -223,6 +223,22 @@ def test_forward_bf16(config, B, T):
 
 
 
+
+# Either side of the switch between the two projection kernels (7 * 2^18
+# token-features): 896 / 897 tokens at N = 2048, 358 / 359 at N = 5120.
+@pytest.mark.parametrize("config,B,T", [(1, 1, 896), (1, 1, 897), (2, 2, 179), (2, 1, 359)])
+def test_forward_bf16_kernel_switch(config, B, T):
+    log(f"forward bf16 kernel switch config={config} B={B} T={T}")
+    w = small(config, B=B, T=T)
+    names = []
+    eg.profile_enable(True)
+    try:
+        _forward_check(w, tag=f"c{config} switch")
+        names = [n for n, _ in eg.profile_read()]
+    finally:
+        eg.profile_enable(False)
+    assert "proj_gate_kernel" in names, names
+
 # Narrow tables: d_mem = 16 x 8 = 128 or 16 x 32 = 512 (K of the projection).
 # The small-batch kernel's K range per wavefront is then 32 or 128 elements,
 # a partial or a whole number of its 64-element load batches; 1,100 tokens at
