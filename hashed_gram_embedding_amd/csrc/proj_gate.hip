@@ -75,13 +75,12 @@ __device__ __forceinline__ void advance_state(const ProjGateArgs& a) {
   }
 }
 
-// Main loop variants: DMA = false stages each slice through registers (PD
-// slices in flight) and writes it to LDS; DMA = true loads it straight into
-// the other of two LDS buffers (global_load_lds_dwordx4) while this one is
-// multiplied.  Measured on gfx950 against register staging with two slices
-// in flight: 3-5 % faster, and three LDS buffers (two slices in flight,
-// 128-column tiles only) no faster than two.
-template <int TF, int PD, bool MX, int WT, bool DMA = false>
+// Main loop: each slice goes straight into the other of two LDS buffers
+// (global_load_lds_dwordx4) while this one is multiplied.  Measured on
+// gfx950 against staging through registers with two slices in flight: 3-5 %
+// faster for bf16 and 11 % for MXFP8; three LDS buffers (two slices in
+// flight, 128-column tiles only) were no faster than two.
+template <int TF, bool MX, int WT>
 __global__ void __launch_bounds__(64 * WF * WT) __attribute__((amdgpu_waves_per_eu(WF * WT / 4, WF * WT / 4)))
 proj_gate_kernel(ProjGateArgs a) {
   constexpr int kThreads = 64 * WF * WT;
@@ -91,8 +90,8 @@ proj_gate_kernel(ProjGateArgs a) {
   constexpr int BKE = 128 / ESZ;           // elements per K slice
   constexpr int kWChunks = TF * 8;         // 16-byte chunks of a W slice
   constexpr int kEChunks = TK * 8;         // 16-byte chunks of an e slice
-  constexpr int NW = kWChunks / kThreads;  // W chunks staged per thread
-  constexpr int NE = kEChunks / kThreads;  // e chunks staged per thread
+  constexpr int NW = kWChunks / kThreads;  // W chunks loaded per thread and slice
+  constexpr int NE = kEChunks / kThreads;  // e chunks loaded per thread and slice
   constexpr int I = TF / WF / 32;          // 32-row feature blocks per wavefront
   constexpr int J = TK / WT / 32;          // 32-row token blocks per wavefront
   extern __shared__ u32x4_t lds[];
@@ -115,7 +114,7 @@ proj_gate_kernel(ProjGateArgs a) {
   const int wf = wave % WF;
   const int wt = wave / WF;
   const int K = a.K;
-  const int ksteps = K / BKE;  // a multiple of PD (checked by the launcher)
+  const int ksteps = K / BKE;
 
   f32x16_t acc[I][J];
 #pragma unroll
@@ -125,56 +124,8 @@ proj_gate_kernel(ProjGateArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // global -> register staging, PD slices in flight.  Token rows past the end
-  // load the last row instead; their results are never stored.
-  u32x4_t rw[PD][NW], re[PD][NE];
-  constexpr int NS = MX ? (TF + TK + kThreads - 1) / kThreads : 1;   // scale words staged per thread
-  uint32_t rs[PD][NS];
   const char* wbase = reinterpret_cast<const char*>(a.w) + static_cast<int64_t>(f0) * K * ESZ;
   const char* ebase = reinterpret_cast<const char*>(a.e);
-  // MXFP8 scale word of this thread's row: W rows for tid < TF, then e rows
-  const uint8_t* sbase[NS];
-  if constexpr (MX) {
-#pragma unroll
-    for (int q = 0; q < NS; ++q) {
-      const int r = tid + q * kThreads;
-      sbase[q] = r < TF ? a.w_scale + static_cast<int64_t>(f0 + r) * (K / 32)
-                        : a.e_scale + min(t0 + (r < TF + TK ? r - TF : 0), a.n_tok - 1) * (K / 32);
-    }
-  }
-#define ENGRAM_LOAD_SLICE(b, kt)                                                                   \
-  {                                                                                                \
-    const int64_t kb = static_cast<int64_t>(kt) * 128;   /* byte offset of the slice in a row */  \
-    _Pragma("unroll") for (int i = 0; i < NW; ++i) {                                               \
-      const int c = tid + i * kThreads;                                                            \
-      rw[b][i] = *reinterpret_cast<const u32x4_t*>(wbase + static_cast<int64_t>(c >> 3) * K * ESZ + \
-                                                   kb + (c & 7) * 16);                             \
-    }                                                                                              \
-    _Pragma("unroll") for (int i = 0; i < NE; ++i) {                                               \
-      const int c = tid + i * kThreads;                                                            \
-      const int64_t tok = min(t0 + (c >> 3), a.n_tok - 1);                                         \
-      re[b][i] = *reinterpret_cast<const u32x4_t*>(ebase + tok * K * ESZ + kb + (c & 7) * 16);     \
-    }                                                                                              \
-    if constexpr (MX) {                                                                            \
-      _Pragma("unroll") for (int q = 0; q < NS; ++q)                                               \
-        rs[b][q] = *reinterpret_cast<const uint32_t*>(sbase[q] + (kt) * 4);                        \
-    }                                                                                              \
-  }
-#define ENGRAM_STORE_SLICE(b, buf)                                                                 \
-  {                                                                                                \
-    _Pragma("unroll") for (int i = 0; i < NW; ++i) {                                               \
-      const int c = tid + i * kThreads;                                                            \
-      Ws[(buf) * kWChunks + swz(c >> 3, c & 7)] = rw[b][i];                                        \
-    }                                                                                              \
-    _Pragma("unroll") for (int i = 0; i < NE; ++i) {                                               \
-      const int c = tid + i * kThreads;                                                            \
-      Es[(buf) * kEChunks + swz(c >> 3, c & 7)] = re[b][i];                                        \
-    }                                                                                              \
-    if constexpr (MX) {                                                                            \
-      _Pragma("unroll") for (int q = 0; q < NS; ++q)                                               \
-        if (tid + q * kThreads < TF + TK) Ss[(buf) * (TF + TK) + tid + q * kThreads] = rs[b][q];   \
-    }                                                                                              \
-  }
   // bf16: K16 steps, lane half h holds K elements 8h..8h+7 (one chunk).
   // MXFP8: K64 steps; lane r (< 32) holds bytes 0-15 and 32-47 of its row's
   // 64-byte run and the scale of its first 32-value block, lane r + 32 bytes
@@ -218,11 +169,12 @@ proj_gate_kernel(ProjGateArgs a) {
     }                                                                                              \
   }
 
-  if constexpr (DMA) {
+  {
     // Each wavefront instruction fills 64 consecutive 16-byte LDS slots (8
     // rows of a slice).  Slot s of row r holds chunk s ^ ((r >> 1) & 7), so
-    // lane l, landing in slot c = l & 7 of row l >> 3, fetches that chunk;
-    // the fragment reads are the same as with staged stores.
+    // lane l, landing in slot c = l & 7 of row l >> 3, fetches that chunk
+    // (the layout that swz() reads).  Token rows past the end re-read the
+    // last row; their results are never stored.
     auto issue = [&](int kt, int buf) {
       const int64_t kb = static_cast<int64_t>(kt) * 128;
 #pragma unroll
@@ -279,24 +231,7 @@ proj_gate_kernel(ProjGateArgs a) {
     }
     // the epilogue reuses the LDS: all fragment reads done, no load in flight
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  } else {
-#pragma unroll
-    for (int b = 0; b < PD; ++b) ENGRAM_LOAD_SLICE(b, min(b, ksteps - 1));
-    ENGRAM_STORE_SLICE(0, 0);
-    __syncthreads();
-    for (int kt0 = 0; kt0 < ksteps; kt0 += PD) {
-#pragma unroll
-      for (int u = 0; u < PD; ++u) {
-        const int kt = kt0 + u;
-        ENGRAM_LOAD_SLICE(u, min(kt + PD, ksteps - 1));        // slice kt + PD (clamped)
-        ENGRAM_COMPUTE(kt & 1);
-        ENGRAM_STORE_SLICE((u + 1) % PD, (kt + 1) & 1);        // slice kt + 1 (unused after the last)
-        __syncthreads();
-      }
-    }
   }
-#undef ENGRAM_LOAD_SLICE
-#undef ENGRAM_STORE_SLICE
 #undef ENGRAM_COMPUTE
 
   // ---- epilogue: acc[i][j][4g + r] is feature wf*TF/WF + i*32 + g*8 + (lane>>5)*4 + r
@@ -584,7 +519,7 @@ proj_gate_small_kernel(ProjGateArgs a) {
   advance_state(a);
 }
 
-template <int TF, int PD, bool MX, int WT = 4, bool DMA = false>
+template <int TF, bool MX, int WT = 4>
 hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   a.tiles_f = a.N / TF;
   a.tiles_t = static_cast<int>((a.n_tok + TK - 1) / TK);
@@ -601,12 +536,12 @@ hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if ((attr_set.load() & bit) == 0) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_kernel<TF, PD, MX, WT, DMA>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_kernel<TF, MX, WT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit);
   }
-  launch_k((proj_gate_kernel<TF, PD, MX, WT, DMA>), dim3(a.tiles_f * a.tiles_t), dim3(64 * WF * WT), lds, s, a);
+  launch_k((proj_gate_kernel<TF, MX, WT>), dim3(a.tiles_f * a.tiles_t), dim3(64 * WF * WT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -640,7 +575,7 @@ hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
     // 128-feature tiles, slices straight into LDS like the bf16 product
     // (the 256-feature tile's accumulators and FP8 operands spill registers)
     if (in.K % 128 != 0 || in.w_scale == nullptr) return hipErrorInvalidValue;
-    return launch_tf<128, 1, true, 4, true>(in, s);
+    return launch_tf<128, true>(in, s);
   }
   if (in.K % BK != 0) return hipErrorInvalidValue;
   if (proj_gate_small(in.n_tok, in.N)) {
@@ -662,8 +597,8 @@ hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
              kSmallLds, s, a);
     return hipGetLastError();
   }
-  if (proj_gate_tile_f(in.n_tok, in.N, in.d, false) == 256) return launch_tf<256, 1, false, 4, true>(in, s);
-  return launch_tf<128, 1, false, 4, true>(in, s);
+  if (proj_gate_tile_f(in.n_tok, in.N, in.d, false) == 256) return launch_tf<256, false>(in, s);
+  return launch_tf<128, false>(in, s);
 }
 
 }  // namespace engram
