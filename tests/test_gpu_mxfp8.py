@@ -77,3 +77,18 @@ def test_forward_mxfp8_matches_oracle(config, B, T):
     ref = orc.forward(w.tokens, w.H, lay, "bf16", gemm="mxfp8")
     check_bf16_layer(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.bf16_to_f64(w.H),
                      tag=f"mxfp8 c{config}")
+
+
+# Narrower tables (16 x 32 dims: K = 512, four 128-code slices of the FP8
+# product; MXFP8 rows need whole 32-value blocks, so 32 dims is the narrowest).
+@pytest.mark.parametrize("config,B,T", [(1, 1, 300), (2, 1, 200)])
+def test_forward_mxfp8_narrow_tables(config, B, T):
+    log(f"mxfp8 forward narrow tables config={config} B={B} T={T}")
+    w, lay, L = _mx_layer(config, B=B, T=T, table_dim=32)
+    tok = torch.from_numpy(w.tokens).to(DEV)
+    H = eg.to_device(w.H, "bf16", DEV)
+    alpha, y = eg.forward(tok, H, L, want_alpha=True, want_y=True)
+    torch.cuda.synchronize()
+    ref = orc.forward(w.tokens, w.H, lay, "bf16", gemm="mxfp8")
+    check_bf16_layer(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.bf16_to_f64(w.H),
+                     tag=f"mxfp8 narrow c{config}")
