@@ -92,3 +92,24 @@ def test_forward_mxfp8_narrow_tables(config, B, T):
     ref = orc.forward(w.tokens, w.H, lay, "bf16", gemm="mxfp8")
     check_bf16_layer(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.bf16_to_f64(w.H),
                      tag=f"mxfp8 narrow c{config}")
+
+
+@pytest.mark.parametrize("config", [1, 2])
+def test_decode_mxfp8_matches_oracle(config):
+    """A 7-token prefill with a decode state, then 5 single-token steps, with
+    the FP8 product (one ragged token tile per call); every call matches the
+    oracle's MXFP8 forward carrying the same state."""
+    log(f"mxfp8 decode config={config}")
+    w, lay, L = _mx_layer(config, B=3, T=12)
+    M, d = lay.branches, lay.d
+    st = eg.DecodeState(3, 3, M, 9, d, DEV)
+    ost = orc.new_state(3, 3, M, 9, d)
+    chunks = [(w.tokens[:, :7], w.H[:, :7])] + [(w.tokens[:, t:t + 1], w.H[:, t:t + 1]) for t in range(7, 12)]
+    for ci, (tok, Hn) in enumerate(chunks):
+        H = eg.to_device(Hn, "bf16", DEV)
+        alpha, y = eg.forward(torch.from_numpy(np.ascontiguousarray(tok)).to(DEV), H, L, state=st,
+                              want_alpha=True, want_y=True)
+        ref = orc.forward(tok, Hn, lay, "bf16", state=ost, gemm="mxfp8")
+        ost = ref["state"]
+        check_bf16_layer(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.bf16_to_f64(Hn),
+                         tag=f"mxfp8 decode c{config} chunk{ci}")
