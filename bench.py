@@ -102,8 +102,11 @@ def kernel_units(n_tok, lay, hdtype, hot_hit=None, mx=False):
     # Below the matrix cores' ridge (the library's small-batch projection, used
     # up to 7 * 2^18 token-features) the projection is bound by reading W:
     # W, e and h in, v and statistics out.
-    small = fused and n_tok * N <= 7 << 18
-    proj = ("hbm", N * d_mem * es + n_tok * (d_mem * es + M * d * es + d * 4 + 16 * N // 64)) if small \
+    # (the FP8 product takes it only when K is a multiple of 512; its W and e
+    # are one byte per value plus a scale byte per 32)
+    small = fused and n_tok * N <= 7 << 18 and (not mx or d_mem % 512 == 0)
+    op = 1 + 1 / 32 if mx else es
+    proj = ("hbm", N * d_mem * op + n_tok * (d_mem * op + M * d * es + d * 4 + 16 * N // 64)) if small \
         else ("mfma", flops)
     units = {
         # token ids in; rows in; e out
@@ -147,7 +150,7 @@ def setup(args, torch, eg, inputs):
     if cfg == 3:
         w = inputs.make_config(3)
         S = w.B
-        Ls = [eg.Layer(l, "bf16", dev) for l in w.layers]
+        Ls = [eg.Layer(l, "bf16", dev, mxfp8=args.mxfp8) for l in w.layers]
         states = [eg.DecodeState(S, 3, 1, 9, 1024, dev) for _ in Ls]
         ctx = torch.from_numpy(w.context).to(dev)
         Hc = eg.to_device(w.H_context, "bf16", dev)
@@ -763,7 +766,7 @@ def main():
     layer_us_p10_p50_p90 = pcts(layer_ms)
 
     units = kernel_units(n_tok, lays[0], w.dtype, extra["_hot"][3] if "_hot" in extra else None,
-                         mx=args.mxfp8 and args.config in (1, 2))
+                         mx=args.mxfp8)
     rates = {}
     for k, t in kernel_ms.items():
         if k in units:

@@ -564,7 +564,7 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
     pa.N = static_cast<int>(n_out);
     pa.d = d;
     pa.M = M;
-    const int q = d / engram::proj_gate_tile_f(n_tok, static_cast<int>(n_out), d, mx);
+    const int q = d / engram::proj_gate_tile_f(n_tok, static_cast<int>(n_out), d, static_cast<int>(d_mem), mx);
     // Decode step (T = 1, the strip conv): the state's ids and pos advance in
     // this launch and the conv writes the new ring row, so no commit kernel
     bool fold = false;

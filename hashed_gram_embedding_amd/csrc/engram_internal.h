@@ -119,7 +119,7 @@ struct ProjGateArgs {
   const uint16_t* w;  // [N][K] bf16, N = (1+M)*d
   const uint16_t* H;  // [n_tok][M][d] bf16 (read only)
   float* v;           // [n_tok][d]
-  float4* stats;      // [n_tok][N/TF], TF = proj_gate_tile_f(n_tok, N, d)
+  float4* stats;      // [n_tok][N/TF], TF = proj_gate_tile_f(n_tok, N, d, K, mx)
   int64_t n_tok;
   int K;
   int N;
@@ -144,7 +144,7 @@ struct ProjGateArgs {
   int32_t adv_B;
 };
 constexpr int kProjGateTileF = 64;   // narrowest feature tile (bounds the statistics buffer)
-int proj_gate_tile_f(int64_t n_tok, int N, int d, bool mx);   // feature columns per gate-statistics tile
+int proj_gate_tile_f(int64_t n_tok, int N, int d, int K, bool mx);   // feature columns per gate-statistics tile
 hipError_t launch_proj_gate(const ProjGateArgs& a, hipStream_t s);
 
 // Whole-row gate statistics from given projections: stats [n_tok][1+M].

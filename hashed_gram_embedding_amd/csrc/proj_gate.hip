@@ -376,15 +376,22 @@ constexpr int kSmallBatch = 4;   // K16 steps per load batch
 // one wavefront's staging buffer: 64 W rows and 32 e rows of a batch's
 // 128-byte run, chunk c of row r at slot c ^ (r & 7)
 constexpr int kSmallRows = kSmallTF + kSmallTK;
-constexpr int kSmallStage = kSmallRows * 8;   // 16-byte slots per buffer
-constexpr int kSmallLds = kSmallWaves * 2 * kSmallStage * 16;   // bytes of staging (the partial sums reuse it)
+// (MXFP8: the 128-byte run is 128 codes, and the rows' scale words of the
+// batch follow, 128 words, the last 32 re-reading a valid row)
+template <bool MX>
+constexpr int small_stage() { return kSmallRows * 8 + (MX ? 128 / 4 : 0); }   // 16-byte slots per buffer
+template <bool MX>
+constexpr int small_lds_bytes() { return kSmallWaves * 2 * small_stage<MX>() * 16; }   // staging bytes (reused for the partial sums)
 
+template <bool MX>
 __global__ void __launch_bounds__(64 * kSmallWaves)
 proj_gate_small_kernel(ProjGateArgs a) {
-  extern __shared__ u32x4_t small_lds[];
+  constexpr int kSmallStage = small_stage<MX>();
+  extern __shared__ u32x4_t small_lds_buf[];
+  u32x4_t* small_lds = small_lds_buf;
   // after the main loop: the partial tiles, +1 column so that the sums are conflict free
   auto part = reinterpret_cast<float (*)[kSmallTF][kSmallTK + 1]>(small_lds);
-  static_assert(kSmallWaves * kSmallTF * (kSmallTK + 1) * 4 <= kSmallLds, "partial sums fit the staging LDS");
+  static_assert(kSmallWaves * kSmallTF * (kSmallTK + 1) * 4 <= small_lds_bytes<MX>(), "partial sums fit the staging LDS");
   const int tf = blockIdx.x % a.tiles_f;
   const int tt = blockIdx.x / a.tiles_f;
   const int f0 = tf * kSmallTF;
@@ -393,8 +400,10 @@ proj_gate_small_kernel(ProjGateArgs a) {
   const int wave = threadIdx.x >> 6;
   const int K = a.K;
   const int kq = K / kSmallWaves;             // this wavefront's K range: [wave*kq, (wave+1)*kq)
-  const int nsteps = kq / 16;                 // K16 steps (K is a multiple of 64: at least one)
-  const int half = lane >> 5;                 // lanes 32-63 hold K elements 8..15 of each step
+  // bf16: K16 steps (K a multiple of 64: at least one), 4 per batch; MXFP8:
+  // K64 steps, 2 per batch (K a multiple of 512: whole batches only)
+  const int nsteps = MX ? kq / 64 : kq / 16;
+  const int half = lane >> 5;                 // lanes 32-63 hold the second half of each step's run
 
   // epilogue thread (token tl, feature eighth fq; the 8 threads of a token are
   // consecutive lanes, so that v stores and h loads move whole row runs): a
@@ -420,20 +429,36 @@ proj_gate_small_kernel(ProjGateArgs a) {
   // which fetches chunk (l & 7) ^ (row & 7)).  Chunks past the range (K/4 not
   // a multiple of 64) re-read the range's last chunk and are never used.
   u32x4_t* stg = small_lds + wave * 2 * kSmallStage;
-  const char* wbase = reinterpret_cast<const char*>(a.w + static_cast<int64_t>(f0) * K + wave * kq);
-  const char* ebase = reinterpret_cast<const char*>(a.e + wave * kq);
-  const int nb = (nsteps + kSmallBatch - 1) / kSmallBatch;
+  constexpr int ESZ = MX ? 1 : 2;             // bytes per element
+  constexpr int SPB = MX ? 2 : kSmallBatch;   // steps per batch (a 128-byte run)
+  const char* wbase = reinterpret_cast<const char*>(a.w) + (static_cast<int64_t>(f0) * K + wave * kq) * ESZ;
+  const char* ebase = reinterpret_cast<const char*>(a.e) + static_cast<int64_t>(wave) * kq * ESZ;
+  const int nb = (nsteps + SPB - 1) / SPB;
   auto issue = [&](int b, int buf) {
 #pragma unroll
     for (int i = 0; i < kSmallRows / 8; ++i) {
       const int r = 8 * i + (lane >> 3);
       const int ch = (lane & 7) ^ (r & 7);
-      const int ke = min(b * 64 + ch * 8, kq - 8);            // element offset in the range
+      const int kb = min(b * 128 + ch * 16, kq * ESZ - 16);   // byte offset in the range
       const int64_t row = r < kSmallTF ? static_cast<int64_t>(r) : min(t0 + (r - kSmallTF), a.n_tok - 1);
-      const char* src = (r < kSmallTF ? wbase : ebase) + (row * K + ke) * 2;
+      const char* src = (r < kSmallTF ? wbase : ebase) + row * K * ESZ + kb;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
                                        (__attribute__((address_space(3))) void*)(stg + buf * kSmallStage + i * 64),
                                        16, 0, 0);
+    }
+    if constexpr (MX) {
+      // the batch's scale word of every row (blocks 4b .. 4b+3 of the range)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = min(i * 64 + lane, kSmallRows - 1);
+        const int64_t col = (static_cast<int64_t>(wave) * kq) / 32 + b * 4;
+        const uint8_t* src = r < kSmallTF ? a.w_scale + static_cast<int64_t>(f0 + r) * (K / 32) + col
+                                          : a.e_scale + min(t0 + (r - kSmallTF), a.n_tok - 1) * (K / 32) + col;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                         (__attribute__((address_space(3))) void*)(reinterpret_cast<uint32_t*>(
+                                             stg + buf * kSmallStage + kSmallRows * 8) + i * 64),
+                                         4, 0, 0);
+      }
     }
   };
   issue(0, 0);
@@ -446,21 +471,46 @@ proj_gate_small_kernel(ProjGateArgs a) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (b + 1 < nb) {
           issue(b + 1, u ^ 1);
-          asm volatile("s_waitcnt vmcnt(12)" ::: "memory");   // batch b has landed, b + 1 in flight
+          // batch b has landed, b + 1 (12 or, with scale words, 14 loads) in flight
+          if constexpr (MX)
+            asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         const u32x4_t* sb = stg + u * kSmallStage;
+        const int r = lane & 31;
+        if constexpr (!MX) {
 #pragma unroll
-        for (int j = 0; j < kSmallBatch; ++j) {
-          if (b * kSmallBatch + j < nsteps) {
-            const int c = 2 * j + half;          // this lane's chunk of the run
-            const int r = lane & 31;
-            const bf16x8_t fa0 = __builtin_bit_cast(bf16x8_t, sb[r * 8 + (c ^ (r & 7))]);
-            const bf16x8_t fa1 = __builtin_bit_cast(bf16x8_t, sb[(32 + r) * 8 + (c ^ (r & 7))]);
-            const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, sb[(kSmallTF + r) * 8 + (c ^ (r & 7))]);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb, acc1, 0, 0, 0);
+          for (int j = 0; j < kSmallBatch; ++j) {
+            if (b * kSmallBatch + j < nsteps) {
+              const int c = 2 * j + half;          // this lane's chunk of the run
+              const bf16x8_t fa0 = __builtin_bit_cast(bf16x8_t, sb[r * 8 + (c ^ (r & 7))]);
+              const bf16x8_t fa1 = __builtin_bit_cast(bf16x8_t, sb[(32 + r) * 8 + (c ^ (r & 7))]);
+              const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, sb[(kSmallTF + r) * 8 + (c ^ (r & 7))]);
+              acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb, acc0, 0, 0, 0);
+              acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb, acc1, 0, 0, 0);
+            }
+          }
+        } else {
+          // K64 step ks: lane r holds bytes 0-15 and 32-47 of its row's 64-byte
+          // run and block 2ks's scale, lane r + 32 bytes 16-31 and 48-63 and
+          // block 2ks+1's (the large kernel's MXFP8 operand layout)
+          const uint32_t* sw = reinterpret_cast<const uint32_t*>(sb + kSmallRows * 8);
+          const uint32_t wa0 = sw[r], wa1 = sw[32 + r], wb = sw[kSmallTF + r];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int c0c = 4 * ks + half, c1c = 4 * ks + 2 + half;
+            const i32x8_t fa0 = join16(sb[r * 8 + (c0c ^ (r & 7))], sb[r * 8 + (c1c ^ (r & 7))]);
+            const i32x8_t fa1 = join16(sb[(32 + r) * 8 + (c0c ^ (r & 7))], sb[(32 + r) * 8 + (c1c ^ (r & 7))]);
+            const i32x8_t fb = join16(sb[(kSmallTF + r) * 8 + (c0c ^ (r & 7))],
+                                      sb[(kSmallTF + r) * 8 + (c1c ^ (r & 7))]);
+            const int sh = 8 * (2 * ks + half);
+            const int sa0 = static_cast<int>((wa0 >> sh) & 0xffu), sa1 = static_cast<int>((wa1 >> sh) & 0xffu);
+            const int sbb = static_cast<int>((wb >> sh) & 0xffu);
+            acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0, fb, acc0, 0, 0, 0, sa0, 0, sbb);
+            acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1, fb, acc1, 0, 0, 0, sa1, 0, sbb);
           }
         }
       }
@@ -558,13 +608,40 @@ hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
 // and 384 tokens 17.7 / 17.3.  The two meet near 1.9 M token-features.
 bool proj_gate_small(int64_t n_tok, int N) { return n_tok * static_cast<int64_t>(N) <= (int64_t{7} << 18); }
 
-int proj_gate_tile_f(int64_t n_tok, int N, int d, bool mx) {
+// The FP8 product takes the small kernel only with whole 512-code K ranges
+// per wavefront batch pair (K a multiple of 512), else the large kernel.
+bool proj_gate_small_for(int64_t n_tok, int N, int K, bool mx) {
+  return proj_gate_small(n_tok, N) && (!mx || K % 512 == 0);
+}
+
+int proj_gate_tile_f(int64_t n_tok, int N, int d, int K, bool mx) {
+  if (proj_gate_small_for(n_tok, N, K, mx)) return kSmallTF;
   if (mx) return 128;
-  if (proj_gate_small(n_tok, N)) return kSmallTF;
   // 256-feature tiles halve the LDS traffic per matrix operation but need at
   // least two tiles per CU (512) to keep the chip busy
   const int64_t tiles256 = ((n_tok + TK - 1) / TK) * (N / 256);
   return (d % 256 == 0 && tiles256 >= 512) ? 256 : 128;
+}
+
+template <bool MX>
+hipError_t launch_small(const ProjGateArgs& in, hipStream_t s) {
+  ProjGateArgs a = in;
+  a.tiles_f = a.N / kSmallTF;
+  a.tiles_t = static_cast<int>((a.n_tok + kSmallTK - 1) / kSmallTK);
+  static std::atomic<uint64_t> attr_set{0};   // > 64 KiB of dynamic LDS, raised once per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if ((attr_set.load() & bit) == 0) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_small_kernel<MX>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, small_lds_bytes<MX>());
+    if (e != hipSuccess) return e;
+    attr_set.fetch_or(bit);
+  }
+  launch_k(proj_gate_small_kernel<MX>, dim3(static_cast<unsigned>(a.tiles_f * a.tiles_t)), dim3(64 * kSmallWaves),
+           small_lds_bytes<MX>(), s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
@@ -572,32 +649,15 @@ hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
   if (in.N % 128 != 0) return hipErrorInvalidValue;
   const bool mx = in.e_scale != nullptr;
   if (mx) {
+    if (in.K % 128 != 0 || in.w_scale == nullptr) return hipErrorInvalidValue;
+    if (proj_gate_small_for(in.n_tok, in.N, in.K, true)) return launch_small<true>(in, s);
     // 128-feature tiles, slices straight into LDS like the bf16 product
     // (the 256-feature tile's accumulators and FP8 operands spill registers)
-    if (in.K % 128 != 0 || in.w_scale == nullptr) return hipErrorInvalidValue;
     return launch_tf<128, true>(in, s);
   }
   if (in.K % BK != 0) return hipErrorInvalidValue;
-  if (proj_gate_small(in.n_tok, in.N)) {
-    ProjGateArgs a = in;
-    a.tiles_f = a.N / kSmallTF;
-    a.tiles_t = static_cast<int>((a.n_tok + kSmallTK - 1) / kSmallTK);
-    static std::atomic<uint64_t> attr_set{0};   // > 64 KiB of dynamic LDS, raised once per device
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    const uint64_t bit = 1ull << (dev & 63);
-    if ((attr_set.load() & bit) == 0) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_small_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kSmallLds);
-      if (e != hipSuccess) return e;
-      attr_set.fetch_or(bit);
-    }
-    launch_k(proj_gate_small_kernel, dim3(static_cast<unsigned>(a.tiles_f * a.tiles_t)), dim3(64 * kSmallWaves),
-             kSmallLds, s, a);
-    return hipGetLastError();
-  }
-  if (proj_gate_tile_f(in.n_tok, in.N, in.d, false) == 256) return launch_tf<256, false>(in, s);
+  if (proj_gate_small(in.n_tok, in.N)) return launch_small<false>(in, s);
+  if (proj_gate_tile_f(in.n_tok, in.N, in.d, in.K, false) == 256) return launch_tf<256, false>(in, s);
   return launch_tf<128, false>(in, s);
 }
 

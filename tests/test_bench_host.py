@@ -38,6 +38,11 @@ def test_kernel_units_of_the_single_branch_layer():
     # decode: below the ridge the projection is priced by the bytes it moves
     small = bench.kernel_units(256, lay, "bf16")["proj_gate_kernel"]
     assert small[0] == "hbm" and small[1] > 2048 * 1024 * 2
+    # the FP8 small-batch product moves W as one byte per value plus a scale byte per 32
+    small_mx = bench.kernel_units(256, lay, "bf16", mx=True)["proj_gate_kernel"]
+    assert small_mx[0] == "hbm" and 2048 * 1024 * 33 / 32 < small_mx[1] < small[1]
+    # past the switch the FP8 product is priced by its flops
+    assert bench.kernel_units(4096, lay, "bf16", mx=True)["proj_gate_kernel"] == ("mfma", 2.0 * 4096 * 2048 * 1024)
 
 
 def test_hbm_summary_scales_counters_by_the_calibration_copy(tmp_path, capsys):
