@@ -102,9 +102,9 @@ def kernel_units(n_tok, lay, hdtype, hot_hit=None, mx=False):
     # Below the matrix cores' ridge (the library's small-batch projection, used
     # up to 7 * 2^18 token-features) the projection is bound by reading W:
     # W, e and h in, v and statistics out.
-    # (the FP8 product takes it only when K is a multiple of 512; its W and e
-    # are one byte per value plus a scale byte per 32)
-    small = fused and n_tok * N <= 7 << 18 and (not mx or d_mem % 512 == 0)
+    # (the FP8 product takes it up to 3 * 2^19 and only when K is a multiple of
+    # 512; its W and e are one byte per value plus a scale byte per 32)
+    small = fused and n_tok * N <= (3 << 19 if mx else 7 << 18) and (not mx or d_mem % 512 == 0)
     op = 1 + 1 / 32 if mx else es
     proj = ("hbm", N * d_mem * op + n_tok * (d_mem * op + M * d * es + d * 4 + 16 * N // 64)) if small \
         else ("mfma", flops)

@@ -608,10 +608,15 @@ hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
 // and 384 tokens 17.7 / 17.3.  The two meet near 1.9 M token-features.
 bool proj_gate_small(int64_t n_tok, int N) { return n_tok * static_cast<int64_t>(N) <= (int64_t{7} << 18); }
 
-// The FP8 product takes the small kernel only with whole 512-code K ranges
-// per wavefront batch pair (K a multiple of 512), else the large kernel.
+// The FP8 product takes the small kernel only with whole 128-code batches per
+// wavefront (K a multiple of 512), and only up to 3 * 2^19 token-features: its
+// large kernel is faster than the bf16 one (12.3-13.5 us from 256 to 2,048
+// tokens at N = 2048), so the two meet earlier (small / large at K = 1024:
+// N = 2048, 768 tokens 12.4 / 12.8 us, 1,024 tokens 16.2 / 12.7; N = 5120,
+// 256 tokens 11.3 / 12.3, 384 tokens 14.9 / 12.7).
 bool proj_gate_small_for(int64_t n_tok, int N, int K, bool mx) {
-  return proj_gate_small(n_tok, N) && (!mx || K % 512 == 0);
+  if (!mx) return proj_gate_small(n_tok, N);
+  return K % 512 == 0 && n_tok * static_cast<int64_t>(N) <= (int64_t{3} << 19);
 }
 
 int proj_gate_tile_f(int64_t n_tok, int N, int d, int K, bool mx) {
