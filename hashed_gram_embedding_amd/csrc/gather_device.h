@@ -51,8 +51,22 @@ __device__ __forceinline__ void store8(void* e, int64_t out, int64_t mx_scale_ba
     // block (rows are whole blocks: dim is a multiple of 32, so the groups
     // of 4 lanes never straddle rows or the grid's end; every lane of the
     // group takes part in the shuffle, stores are predicated)
+    // the codes quantise the bf16 row values the bf16 product would read:
+    // int8 and float32 rows are rounded to bf16 (RNE) first
+    float fb[8];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      if constexpr (IN == ENGRAM_BF16) {
+        fb[i] = f[i];
+        fb[i + 1] = f[i + 1];
+      } else {
+        const uint32_t b = pack_bf16x2(f[i], f[i + 1]);
+        fb[i] = __uint_as_float(b << 16);
+        fb[i + 1] = __uint_as_float(b & 0xffff0000u);
+      }
+    }
     uint32_t sb;
-    const uint2 q = mx_quantize8(f, &sb);
+    const uint2 q = mx_quantize8(fb, &sb);
     uint8_t* eq = static_cast<uint8_t*>(e);
     if (live) {
       *reinterpret_cast<uint2*>(eq + out) = q;

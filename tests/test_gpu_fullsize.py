@@ -18,24 +18,43 @@ DEV = "cuda"
 HALO = 11   # (N-1) + (w-1)*N positions of history determine a position's output
 
 
-def check_windows(w, lay, a_g, y_g, h_g, starts, rows, L=64, tag=""):
+def check_windows(w, lay, a_g, y_g, h_g, starts, rows, L=64, tag="", gemm="exact"):
     h_in = orc.storage_to_f64(w.H, w.dtype)
     for b in rows:
         for s in starts:
             lo = max(0, s - HALO)
-            ref = orc.forward(w.tokens[b:b + 1, lo:s + L], w.H[b:b + 1, lo:s + L], lay, w.dtype)
+            ref = orc.forward(w.tokens[b:b + 1, lo:s + L], w.H[b:b + 1, lo:s + L], lay, w.dtype, gemm=gemm)
             k = s - lo
             check_bf16_layer(a_g[b:b + 1, s:s + L], ref["alpha"][:, k:], y_g[b:b + 1, s:s + L], ref["Y"][:, k:],
                              h_g[b:b + 1, s:s + L], h_in[b:b + 1, s:s + L], tag=f"{tag} b{b} s{s}")
 
 
-def test_multi_branch_full_size_sampled():
+def test_single_branch_full_size_sampled():
+    """The single-branch workload the benchmark's headline line times: B = 1,
+    T = 4096, the full 10.3M-row tables, bf16 and the MXFP8 product."""
+    log("single-branch full size: inputs")
+    w = inputs.make_config(1)
+    lay = w.layers[0]
+    starts = [0, 1000, 2048, 4096 - 64]
+    for mx in (False, True):
+        log(f"single-branch full size: forward mxfp8={mx}")
+        L = eg.Layer(lay, "bf16", DEV, mxfp8=mx)
+        H = eg.to_device(w.H, "bf16", DEV)
+        alpha, y = eg.forward(torch.from_numpy(w.tokens).to(DEV), H, L, want_alpha=True, want_y=True)
+        torch.cuda.synchronize()
+        a_g, y_g, h_g = to_f64(alpha), to_f64(y), to_f64(H)
+        log(f"single-branch full size: oracle windows mxfp8={mx}")
+        check_windows(w, lay, a_g, y_g, h_g, starts, [0], tag=f"c1 mx={mx}", gemm="mxfp8" if mx else "exact")
+
+
+@pytest.mark.parametrize("mx", [False, True])
+def test_multi_branch_full_size_sampled(mx):
     """B = 8, T = 4096, M = 4 branches (shared W_V, four W_K^(m), per-branch
-    gate and conv), the full 10.3M-row tables."""
-    log("multi-branch full size: inputs")
+    gate and conv), the full 10.3M-row tables; bf16 and the MXFP8 product."""
+    log(f"multi-branch full size: inputs mxfp8={mx}")
     w = inputs.make_config(2)
     lay = w.layers[0]
-    L = eg.Layer(lay, "bf16", DEV)
+    L = eg.Layer(lay, "bf16", DEV, mxfp8=mx)
     H = eg.to_device(w.H, "bf16", DEV)
     log("multi-branch full size: forward")
     alpha, y = eg.forward(torch.from_numpy(w.tokens).to(DEV), H, L, want_alpha=True, want_y=True)
@@ -52,21 +71,22 @@ def test_multi_branch_full_size_sampled():
             y_g[b, s:s + 64] = to_f64(y[b, s:s + 64])
             h_g[b, s:s + 64] = to_f64(H[b, s:s + 64])
     log("multi-branch full size: oracle windows")
-    check_windows(w, lay, a_g, y_g, h_g, starts, rows, tag="c2")
+    check_windows(w, lay, a_g, y_g, h_g, starts, rows, tag=f"c2 mx={mx}", gemm="mxfp8" if mx else "exact")
 
 
-def test_decode_full_size_sampled():
+@pytest.mark.parametrize("mx", [False, True])
+def test_decode_full_size_sampled(mx):
     """256 sequences, int8 rows with per-row scales (703 MB per layer), each
     of the 2 layers: a 16-token prefill with state, then 3 single-token decode
     steps; sampled sequences match the oracle at every step and the state's
-    ids and positions match exactly."""
-    log("decode full size: inputs")
+    ids and positions match exactly (bf16 and the MXFP8 product)."""
+    log(f"decode full size: inputs mxfp8={mx}")
     w = inputs.make_config(3, T=3)
     S = w.B
     sample = [0, 1, 100, 255]
     for li, lay in enumerate(w.layers):
         log(f"decode full size: layer {li}")
-        L = eg.Layer(lay, "bf16", DEV)
+        L = eg.Layer(lay, "bf16", DEV, mxfp8=mx)
         st = eg.DecodeState(S, 3, 1, 9, 1024, DEV)
         ost = orc.new_state(len(sample), 3, 1, 9, 1024)
         chunks = [(w.context, w.H_context)] + [(w.tokens[:, t:t + 1], w.H[:, t:t + 1]) for t in range(3)]
@@ -74,7 +94,7 @@ def test_decode_full_size_sampled():
             H = eg.to_device(Hn, "bf16", DEV)
             alpha, y = eg.forward(torch.from_numpy(np.ascontiguousarray(tok)).to(DEV), H, L, state=st,
                                   want_alpha=True, want_y=True)
-            ref = orc.forward(tok[sample], Hn[sample], lay, "bf16", state=ost)
+            ref = orc.forward(tok[sample], Hn[sample], lay, "bf16", state=ost, gemm="mxfp8" if mx else "exact")
             ost = ref["state"]
             check_bf16_layer(to_f64(alpha[sample]), ref["alpha"], to_f64(y[sample]), ref["Y"], to_f64(H[sample]),
                              orc.bf16_to_f64(Hn[sample]), tag=f"layer{li} chunk{ci}")

@@ -49,9 +49,14 @@ def _mx_layer(config, **kw):
     return w, lay, eg.Layer(lay, "bf16", DEV, mxfp8=True)
 
 
-def test_retrieve_emits_mxfp8_rows_bit_exact():
-    log("mxfp8 gather")
-    w, lay, L = _mx_layer(1, B=2, T=90)
+@pytest.mark.parametrize("config", [1, 3])
+def test_retrieve_emits_mxfp8_rows_bit_exact(config):
+    """MXFP8 codes and scale bytes of the gathered rows equal the oracle's
+    quantisation of the bf16 rows (bf16 tables, and int8 tables whose rows are
+    dequantised and rounded to bf16 first)."""
+    log(f"mxfp8 gather config={config}")
+    w, lay, L = _mx_layer(config, B=2, T=90)
+    assert lay.tables.dtype == ("i8" if config == 3 else "bf16")
     tok = torch.from_numpy(w.tokens).to(DEV)
     e = eg.rows_buffer(2, 90, L, DEV)
     eg.retrieve(tok, L, e)
