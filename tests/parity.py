@@ -60,6 +60,7 @@ def check_bf16_layer(alpha_gpu, alpha_ref, y_gpu, y_ref, h_gpu, h_in, tag=""):
     bound = 0.5 * bf16_ulp(np.abs(target) + tol_y) + tol_y
     dh = np.abs(h_gpu - target)
     assert np.all(dh <= bound), f"{tag} H_out err {float(np.max(dh - bound)):.3e} over bound"
+    log(f"{tag} margins: alpha {da / BF16_ALPHA_ABS:.3f}, Y {dy / max(tol_y, 1e-30):.3f} of the tolerance")
     return da, dy / max(tol_y, 1e-30)
 
 
