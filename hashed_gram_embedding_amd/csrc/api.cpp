@@ -51,6 +51,7 @@ engram_status check_hash(const engram_hash_params* hp, engram::HashArgs* out) {
   if (hp->proj == nullptr || hp->mult == nullptr || hp->prime == nullptr)
     return fail(ENGRAM_EINVAL, "hash params: proj, mult and prime must be non-NULL");
   if (hp->vocab <= 0) return fail(ENGRAM_EINVAL, "hash params: vocab must be positive");
+  if (hp->vocab > INT32_MAX) return fail(ENGRAM_EUNSUPPORTED, "hash params: vocab above 2^31-1");
   if (hp->max_n < 2 || hp->max_n > ENGRAM_MAX_ORDER)
     return fail(ENGRAM_EUNSUPPORTED, "hash params: max_n=%d outside [2, %d]", hp->max_n, ENGRAM_MAX_ORDER);
   const int nt = (hp->max_n - 1) * hp->heads;
@@ -75,6 +76,7 @@ engram_status check_hash(const engram_hash_params* hp, engram::HashArgs* out) {
   if (out != nullptr) {
     out->n_tables = nt;
     out->max_n = hp->max_n;
+    out->vocab = static_cast<int32_t>(hp->vocab);
   }
   return ENGRAM_OK;
 }
@@ -291,8 +293,9 @@ size_t forward_ws_bytes(int64_t n_tok, const engram_layer* L) {
 // launch where a fused form exists, else right after it), or null.
 engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdtype, const float4* stats, int qv,
                               int qk, int64_t B, int64_t T, const engram::GateConvArgs& g, engram_decode_state* st,
-                              const int32_t* tokens, const int32_t* proj, int32_t max_n, float* alpha_out,
-                              float* gamma, float* y_out, hipStream_t s, const engram::GatherJob* next = nullptr,
+                              const int32_t* tokens, const int32_t* proj, int32_t max_n, int32_t vocab,
+                              float* alpha_out, float* gamma, float* y_out, hipStream_t s,
+                              const engram::GatherJob* next = nullptr,
                               bool state_folded = false) {
   engram::ConvArgs ca{};
   ca.H = H;
@@ -339,7 +342,7 @@ engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdty
   if (st != nullptr && !state_folded) {
     engram::StateArgs sa{tokens != nullptr ? st->ids : nullptr, st->conv, st->pos};
     prof_mark(s, "state_commit_kernel");
-    r = hip_status(engram::launch_state_commit(v, v_stride, vdtype, B, T, g, gamma, sa, tokens, proj, max_n, s),
+    r = hip_status(engram::launch_state_commit(v, v_stride, vdtype, B, T, g, gamma, sa, tokens, proj, max_n, vocab, s),
                    "state commit launch");
   }
   prof_mark(s, nullptr);
@@ -410,9 +413,11 @@ engram_status check_layer(const engram_layer* L, engram::HashArgs* ha, engram::T
   if ((L->w_mx == nullptr) != (L->w_mx_scale == nullptr))
     return fail(ENGRAM_EINVAL, "layer: w_mx and w_mx_scale must both be set or both be NULL");
   if (L->w_mx != nullptr) {
-    if (L->gc.hdtype != ENGRAM_BF16 || L->gc.d % 128 != 0 || L->tables.dim % 32 != 0 || d_mem % 128 != 0)
+    // (the MXFP8 rows are read only by the fused projection, which takes d <= 4096)
+    if (L->gc.hdtype != ENGRAM_BF16 || L->gc.d % 128 != 0 || L->gc.d > 4096 || L->tables.dim % 32 != 0 ||
+        d_mem % 128 != 0)
       return fail(ENGRAM_EUNSUPPORTED,
-                  "layer: MXFP8 needs bf16 H, d a multiple of 128, dim a multiple of 32 and d_mem of 128");
+                  "layer: MXFP8 needs bf16 H, d a multiple of 128 up to 4096, dim a multiple of 32 and d_mem of 128");
     if (!aligned(L->w_mx, 16) || !aligned(L->w_mx_scale, 4))
       return fail(ENGRAM_EINVAL, "layer: w_mx must be 16-byte and w_mx_scale 4-byte aligned");
   }
@@ -501,7 +506,7 @@ ENGRAM_API engram_status engram_gate_conv_forward(void* H, const void* kv, int64
   r = hip_status(engram::launch_gate_stats(H, kv, B * T, g, w.stats, stream), "gate statistics launch");
   if (r != ENGRAM_OK) return r;
   const int64_t stride = static_cast<int64_t>(1 + p->branches) * p->d;
-  return run_conv_commit(H, kv, stride, g.kvdtype, w.stats, 1, 1, B, T, g, st, nullptr, nullptr, 0, alpha_out,
+  return run_conv_commit(H, kv, stride, g.kvdtype, w.stats, 1, 1, B, T, g, st, nullptr, nullptr, 0, 1, alpha_out,
                          w.gamma, y_out, stream);
 }
 
@@ -581,6 +586,7 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
       pa.st_pos = st->pos;
       pa.tokens = tokens;
       pa.proj = L->hash.proj;
+      pa.vocab = static_cast<int32_t>(L->hash.vocab);
       pa.max_n = L->hash.max_n;
       pa.adv_T = static_cast<int32_t>(T);
       pa.adv_B = static_cast<int32_t>(B);
@@ -589,7 +595,7 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
     r = hip_status(engram::launch_proj_gate(pa, stream), "projection launch");
     if (r != ENGRAM_OK) return r;
     return run_conv_commit(H, f.kv, d, ENGRAM_F32, f.stats, q, q, B, T, g, st, tokens, L->hash.proj,
-                           L->hash.max_n, alpha_out, f.gamma, y_out, stream, next, fold);
+                           L->hash.max_n, static_cast<int32_t>(L->hash.vocab), alpha_out, f.gamma, y_out, stream, next, fold);
   }
   // Step 5 into float32 projections, then whole-row gate statistics
   prof_mark(stream, "gemm_kernel");
@@ -601,7 +607,7 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
   r = hip_status(engram::launch_gate_stats(H, f.kv, n_tok, g, f.stats, stream), "gate statistics launch");
   if (r != ENGRAM_OK) return r;
   return run_conv_commit(H, f.kv, n_out, ENGRAM_F32, f.stats, 1, 1, B, T, g, st, tokens, L->hash.proj,
-                         L->hash.max_n, alpha_out, f.gamma, y_out, stream, next);
+                         L->hash.max_n, static_cast<int32_t>(L->hash.vocab), alpha_out, f.gamma, y_out, stream, next);
 }
 
 }  // namespace
@@ -943,6 +949,6 @@ ENGRAM_API engram_status engram_hot_lookup(const int32_t* tokens, int64_t B, int
   if (tokens == nullptr || hot_row == nullptr) return fail(ENGRAM_EINVAL, "hot lookup: tokens and hot_row must be non-NULL");
   prof_begin();
   prof_mark(stream, "hot_lookup_kernel");
-  return hip_status(engram::launch_hot_lookup(tokens, B, T, hist, hp->proj, hp->max_n, h, hot_row, stream),
+  return hip_status(engram::launch_hot_lookup(tokens, B, T, hist, hp->proj, hp->max_n, ha.vocab, h, hot_row, stream),
                     "hot lookup launch");
 }

@@ -18,6 +18,7 @@ struct HashArgs {
   int32_t order[ENGRAM_MAX_TABLES];                    // n of table j
   int32_t n_tables;
   int32_t max_n;
+  int32_t vocab;                                       // raw ids are clamped into [0, vocab)
 };
 
 
@@ -99,7 +100,8 @@ hipError_t launch_hash_gather(const int32_t* tokens, int64_t B, int64_t T, const
                               const HotArgs* hot, int out_dtype, void* e, hipStream_t s);
 
 hipError_t launch_hot_lookup(const int32_t* tokens, int64_t B, int64_t T, const int32_t* hist,
-                             const int32_t* proj, int max_n, const HotArgs& h, int32_t* out, hipStream_t s);
+                             const int32_t* proj, int max_n, int32_t vocab, const HotArgs& h, int32_t* out,
+                             hipStream_t s);
 
 // Host build of one order's minimal perfect hash (pilots, and 8 int32 per
 // slot: ids newest first, row, padding).  a, b name the n-grams behind a
@@ -139,11 +141,15 @@ struct ProjGateArgs {
   int32_t* st_pos;        // [adv_B]
   const int32_t* tokens;  // [adv_B][adv_T] raw ids
   const int32_t* proj;    // P
+  int32_t vocab;          // raw ids are clamped into [0, vocab)
   int32_t max_n;
   int32_t adv_T;
   int32_t adv_B;
 };
 constexpr int kProjGateTileF = 64;   // narrowest feature tile (bounds the statistics buffer)
+// Gate statistics per (token, branch) that the conv kernels take: the value
+// tiles plus one branch's key tiles, qv + qk <= kConvMaxStats.
+constexpr int kConvMaxStats = 64;
 int proj_gate_tile_f(int64_t n_tok, int N, int d, int K, bool mx);   // feature columns per gate-statistics tile
 hipError_t launch_proj_gate(const ProjGateArgs& a, hipStream_t s);
 
@@ -192,7 +198,8 @@ hipError_t launch_conv_gather(const ConvArgs& a, int vdtype, const GatherJob& gj
 // (when tokens/proj are given) and advances pos.
 hipError_t launch_state_commit(const void* v, int64_t v_stride, int vdtype, int64_t B, int64_t T,
                                const GateConvArgs& g, const float* gamma, const StateArgs& st,
-                               const int32_t* tokens, const int32_t* proj, int32_t max_n, hipStream_t s);
+                               const int32_t* tokens, const int32_t* proj, int32_t max_n, int32_t vocab,
+                               hipStream_t s);
 
 size_t cache_build_workspace(int64_t total_rows);
 size_t cache_update_workspace(int64_t total_rows, int64_t cache_n);

@@ -173,7 +173,7 @@ conv_kernel(ConvArgs a) {
   // are unrolled, so every load is in flight before the first one is waited on.
   constexpr int kMaxRows = TT + ENGRAM_MAX_CONV_SPAN;
   constexpr int kTileIters = (kMaxRows * CG + 255) / 256;
-  constexpr int kStatIters = (kMaxRows * 64 + 255) / 256;  // up to 64 statistics per row
+  constexpr int kStatIters = (kMaxRows * kConvMaxStats + 255) / 256;  // up to kConvMaxStats per row (launch_conv checks)
   const int64_t row0 = static_cast<int64_t>(b) * T;
   {
     // v rows of this chunk: the address is clamped into the chunk (always a
@@ -572,7 +572,7 @@ template <int VT>
 __global__ void __launch_bounds__(256)
 state_commit_kernel(const void* __restrict__ v, int64_t v_stride, int64_t T, GateConvArgs g,
                     const float* __restrict__ gamma, StateArgs st, const int32_t* __restrict__ tokens,
-                    const int32_t* __restrict__ proj, int32_t max_n) {
+                    const int32_t* __restrict__ proj, int32_t max_n, int32_t vocab) {
   const int64_t b = blockIdx.x;
   const int M = g.branches;
   const int d = g.d;
@@ -604,7 +604,7 @@ state_commit_kernel(const void* __restrict__ v, int64_t v_stride, int64_t T, Gat
     for (int i = 0; i < ENGRAM_MAX_ORDER - 1; ++i) {
       if (i < hl) {
         const int64_t idx = T + i;  // index in (old ids ++ chunk ids)
-        next[i] = idx < hl ? st.ids[b * hl + idx] : proj[tokens[b * T + idx - hl]];
+        next[i] = idx < hl ? st.ids[b * hl + idx] : proj[token_in_vocab(tokens[b * T + idx - hl], vocab)];
       }
     }
 #pragma unroll
@@ -684,7 +684,7 @@ hipError_t launch_conv_strip(const ConvArgs& a, int vdtype, hipStream_t s) {
 // workgroups, more halo re-reads, which hit L2).  Returns TS (CPT = 4 for
 // TS <= 4, else 2), or 0 when the strip kernel does not apply.
 int conv_strip_ts(const ConvArgs& a) {
-  if (a.g.kernel_w != 4 || a.g.dilation != 3 || a.qv + a.qk > 64) return 0;
+  if (a.g.kernel_w != 4 || a.g.dilation != 3 || a.qv + a.qk > kConvMaxStats) return 0;
   if (a.T == 1) return 1;
   const int64_t wg16 = a.B * a.g.branches * ((a.T + 15) / 16) * ((a.g.d + 511) / 512);
   return wg16 < 1024 ? 4 : 16;
@@ -745,6 +745,9 @@ hipError_t launch_conv_gather(const ConvArgs& a, int vdtype, const GatherJob& gj
 
 hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
+  // both conv kernels stage at most kConvMaxStats statistics per row (the
+  // projection launchers never produce more)
+  if (a.qv < 1 || a.qk < 1 || a.qv + a.qk > kConvMaxStats) return hipErrorInvalidValue;
   switch (conv_strip_ts(a)) {   // the pages' conv (w = 4, dilation 3): strip kernel
     case 1: return launch_conv_strip<4, 3, 1, 4>(a, vdtype, s);
     case 4: return launch_conv_strip<4, 3, 4, 4>(a, vdtype, s);
@@ -760,14 +763,15 @@ hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s) {
 
 hipError_t launch_state_commit(const void* v, int64_t v_stride, int vdtype, int64_t B, int64_t T,
                                const GateConvArgs& g, const float* gamma, const StateArgs& st,
-                               const int32_t* tokens, const int32_t* proj, int32_t max_n, hipStream_t s) {
+                               const int32_t* tokens, const int32_t* proj, int32_t max_n, int32_t vocab,
+                               hipStream_t s) {
   if (B == 0 || T == 0) return hipSuccess;
   if (vdtype == ENGRAM_BF16)
     launch_k(state_commit_kernel<ENGRAM_BF16>, dim3(static_cast<unsigned>(B)), dim3(256), 0, s,
-                       v, v_stride, T, g, gamma, st, tokens, proj, max_n);
+                       v, v_stride, T, g, gamma, st, tokens, proj, max_n, vocab);
   else
     launch_k(state_commit_kernel<ENGRAM_F32>, dim3(static_cast<unsigned>(B)), dim3(256), 0, s,
-                       v, v_stride, T, g, gamma, st, tokens, proj, max_n);
+                       v, v_stride, T, g, gamma, st, tokens, proj, max_n, vocab);
   return hipGetLastError();
 }
 

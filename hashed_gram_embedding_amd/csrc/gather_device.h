@@ -131,7 +131,8 @@ __device__ __forceinline__ void hashed_gather_body(uint32_t gid, uint32_t n_tok,
 #pragma unroll
   for (int q = 0; q < ITEMS; ++q)
 #pragma unroll
-    for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) x[q][i] = static_cast<uint32_t>(hs.proj[tk[q][i]]);
+    for (int i = 0; i < ENGRAM_MAX_ORDER; ++i)
+      x[q][i] = static_cast<uint32_t>(hs.proj[token_in_vocab(tk[q][i], hs.a.vocab)]);
 #pragma unroll
   for (int q = 0; q < ITEMS; ++q) {
     if (t[q] < static_cast<uint32_t>(hist_len)) {

@@ -30,6 +30,7 @@
 
 #include "device_util.h"
 #include "engram_internal.h"
+#include "hash_device.h"
 
 namespace engram {
 namespace {
@@ -65,7 +66,7 @@ __device__ __forceinline__ void advance_state(const ProjGateArgs& a) {
       if (i < hl) {
         const int64_t idx = static_cast<int64_t>(a.adv_T) + i;   // index in (old ids ++ chunk ids)
         next[i] = idx < hl ? a.st_ids[static_cast<int64_t>(b) * hl + idx]
-                           : a.proj[a.tokens[static_cast<int64_t>(b) * a.adv_T + idx - hl]];
+                           : a.proj[token_in_vocab(a.tokens[static_cast<int64_t>(b) * a.adv_T + idx - hl], a.vocab)];
       }
     }
 #pragma unroll
@@ -606,7 +607,13 @@ hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
 // Measured on gfx950 at K = 1024 (small / large, us): N = 2048, 768 tokens
 // 14.4 / 17.5 and 1,024 tokens 18.3 / 17.7; N = 5120, 256 tokens 13.3 / 16.8
 // and 384 tokens 17.7 / 17.3.  The two meet near 1.9 M token-features.
-bool proj_gate_small(int64_t n_tok, int N) { return n_tok * static_cast<int64_t>(N) <= (int64_t{7} << 18); }
+//
+// The small kernel's statistics come in 64-column tiles, 2d/64 per token and
+// branch (one value tile set and one key tile set); the conv takes at most
+// kConvMaxStats of them per row, so the small kernel serves d <= 2048 only.
+bool proj_gate_small(int64_t n_tok, int N, int d) {
+  return 2 * d / kSmallTF <= kConvMaxStats && n_tok * static_cast<int64_t>(N) <= (int64_t{7} << 18);
+}
 
 // The FP8 product takes the small kernel only with whole 128-code batches per
 // wavefront (K a multiple of 512), and only up to 3 * 2^19 token-features: its
@@ -614,13 +621,13 @@ bool proj_gate_small(int64_t n_tok, int N) { return n_tok * static_cast<int64_t>
 // tokens at N = 2048), so the two meet earlier (small / large at K = 1024:
 // N = 2048, 768 tokens 12.4 / 12.8 us, 1,024 tokens 16.2 / 12.7; N = 5120,
 // 256 tokens 11.3 / 12.3, 384 tokens 14.9 / 12.7).
-bool proj_gate_small_for(int64_t n_tok, int N, int K, bool mx) {
-  if (!mx) return proj_gate_small(n_tok, N);
-  return K % 512 == 0 && n_tok * static_cast<int64_t>(N) <= (int64_t{3} << 19);
+bool proj_gate_small_for(int64_t n_tok, int N, int d, int K, bool mx) {
+  if (!mx) return proj_gate_small(n_tok, N, d);
+  return 2 * d / kSmallTF <= kConvMaxStats && K % 512 == 0 && n_tok * static_cast<int64_t>(N) <= (int64_t{3} << 19);
 }
 
 int proj_gate_tile_f(int64_t n_tok, int N, int d, int K, bool mx) {
-  if (proj_gate_small_for(n_tok, N, K, mx)) return kSmallTF;
+  if (proj_gate_small_for(n_tok, N, d, K, mx)) return kSmallTF;
   if (mx) return 128;
   // 256-feature tiles halve the LDS traffic per matrix operation but need at
   // least two tiles per CU (512) to keep the chip busy
@@ -655,13 +662,13 @@ hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
   const bool mx = in.e_scale != nullptr;
   if (mx) {
     if (in.K % 128 != 0 || in.w_scale == nullptr) return hipErrorInvalidValue;
-    if (proj_gate_small_for(in.n_tok, in.N, in.K, true)) return launch_small<true>(in, s);
+    if (proj_gate_small_for(in.n_tok, in.N, in.d, in.K, true)) return launch_small<true>(in, s);
     // 128-feature tiles, slices straight into LDS like the bf16 product
     // (the 256-feature tile's accumulators and FP8 operands spill registers)
     return launch_tf<128, true>(in, s);
   }
   if (in.K % BK != 0) return hipErrorInvalidValue;
-  if (proj_gate_small(in.n_tok, in.N)) return launch_small<false>(in, s);
+  if (proj_gate_small(in.n_tok, in.N, in.d)) return launch_small<false>(in, s);
   if (proj_gate_tile_f(in.n_tok, in.N, in.d, in.K, false) == 256) return launch_tf<256, false>(in, s);
   return launch_tf<128, false>(in, s);
 }

@@ -24,7 +24,9 @@ bf16 arrays are carried as uint16 bit patterns (numpy has no bfloat16).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import List, Optional
 
 import numpy as np
@@ -112,19 +114,52 @@ def make_multipliers(rng: np.random.Generator, max_n: int, heads: int) -> np.nda
     return m | np.uint64(1)
 
 
-def normal_bf16_bits(rng: np.random.Generator, n: int, std: float, chunk: int = 1 << 26) -> np.ndarray:
+# Large arrays are drawn in fixed chunks of GEN_CHUNK values, chunk i from the
+# i-th child generator of `rng` (Generator.spawn), and the chunks are filled by
+# a thread pool (numpy's generators and ufuncs release the GIL).  The values
+# depend only on the seed and the array size, not on the thread count.
+GEN_CHUNK = 1 << 22
+
+
+def gen_threads() -> int:
+    """Threads for input generation: the CPUs this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def fill_chunks(rng: np.random.Generator, n: int, chunk: int, fill) -> None:
+    """Calls fill(child_rng, start, end) for consecutive chunks of [0, n), each
+    with its own spawned child generator, on a thread pool."""
+    if n <= 0:
+        return
+    bounds = [(s, min(n, s + chunk)) for s in range(0, n, chunk)]
+    kids = rng.spawn(len(bounds))
+    if len(bounds) == 1:
+        fill(kids[0], *bounds[0])
+        return
+    with concurrent.futures.ThreadPoolExecutor(max_workers=gen_threads()) as ex:
+        list(ex.map(lambda a: fill(a[0], *a[1]), zip(kids, bounds)))
+
+
+def normal_bf16_bits(rng: np.random.Generator, n: int, std: float) -> np.ndarray:
     out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        out[s:e] = to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32) * np.float32(std))
+
+    def fill(g, s, e):
+        out[s:e] = to_bf16_bits(g.standard_normal(e - s, dtype=np.float32) * np.float32(std))
+    fill_chunks(rng, n, GEN_CHUNK, fill)
     return out
 
 
-def normal_f32(rng: np.random.Generator, n: int, std: float, chunk: int = 1 << 26) -> np.ndarray:
+def normal_f32(rng: np.random.Generator, n: int, std: float) -> np.ndarray:
     out = np.empty(n, dtype=np.float32)
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        out[s:e] = rng.standard_normal(e - s, dtype=np.float32) * np.float32(std)
+
+    def fill(g, s, e):
+        g.standard_normal(e - s, dtype=np.float32, out=out[s:e])
+        out[s:e] *= np.float32(std)
+    fill_chunks(rng, n, GEN_CHUNK, fill)
     return out
 
 
@@ -232,12 +267,11 @@ def _tables(config, layer, prime, dim, dtype, std=0.02):
     if dtype == I8:
         q = np.empty((total, dim), dtype=np.int8)
         scale = np.empty(total, dtype=np.float32)
-        chunk = 1 << 20
-        for s in range(0, total, chunk):
-            e = min(total, s + chunk)
-            qq, sc = quantize_rows_int8(normal_f32(rng, (e - s) * dim, std).reshape(e - s, dim))
-            q[s:e] = qq
-            scale[s:e] = sc
+
+        def fill(g, s, e):
+            x = g.standard_normal((e - s) * dim, dtype=np.float32) * np.float32(std)
+            q[s:e], scale[s:e] = quantize_rows_int8(x.reshape(e - s, dim))
+        fill_chunks(rng, total, max(1, GEN_CHUNK // dim), fill)
         return TableInputs(dim, I8, q, row_offset, n_rows, scale)
     raise ValueError(dtype)
 

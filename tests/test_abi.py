@@ -307,3 +307,21 @@ def test_hot_tier_is_validated_before_launch():
     nor.rows[0] = None
     assert L.engram_hot_lookup(p, 1, 64, None, ctypes.byref(hp), ctypes.byref(nor), None, None) == eg.EINVAL
     assert L.engram_hot_lookup(p, 1, 64, None, ctypes.byref(hp), None, z, None) == eg.EINVAL
+
+
+def test_mxfp8_layer_outside_the_fused_projection_is_rejected():
+    """MXFP8 rows are read only by the fused projection (d <= 4096): a wider
+    MXFP8 layer is refused before anything launches."""
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    hp, keep_h = _hash_params()
+    t, keep_t = _tables(dtype=eg.BF16, dim=32)       # d_mem = 4 x 32 = 128
+    for d, want in ((4096 + 128, eg.EUNSUPPORTED), (4096 * 2, eg.EUNSUPPORTED)):
+        lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=d), 0x20000, 0x30000, None)
+        need = L.engram_forward_workspace(1, 64, ctypes.byref(lay))
+        st, msg = _status(L.engram_forward, p, p, 1, 64, ctypes.byref(lay), None, None, None, p, need, None)
+        assert st == want and "MXFP8" in msg
+        assert L.engram_retrieve(p, 1, 64, ctypes.byref(lay), None, p, None) == want
+    lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=4096), 0x20000, 0x30000, None)
+    assert L.engram_retrieve(p, 0, 64, ctypes.byref(lay), None, p, None) == eg.OK     # d = 4096 passes the checks
+

@@ -266,6 +266,31 @@ def test_forward_unfused_widths(dtype, d, M, B, T):
     assert ref["Y"].shape == (B, T, M, d)
 
 
+# Hidden widths above 2048 on the fused path, bf16 and MXFP8 products, at
+# token counts that the small-batch projection would take for narrower
+# layers: its 64-column statistics tiles would give the conv more than its
+# 64 statistics per row, so these run 128-column tiles.
+@pytest.mark.parametrize("d,B,T,mx", [(3072, 2, 75, False), (4096, 1, 150, False), (3072, 3, 40, True),
+                                      (4096, 2, 64, True)])
+def test_forward_wide_hidden(d, B, T, mx):
+    log(f"forward wide hidden d={d} B={B} T={T} mxfp8={mx}")
+    w = small(1, B=B, T=T, d=d)
+    lay = w.layers[0]
+    L = eg.Layer(lay, "bf16", DEV, mxfp8=mx)
+    H = dev_H(w)
+    names = []
+    eg.profile_enable(True)
+    try:
+        alpha, y = eg.forward(dev_tokens(w), H, L, want_alpha=True, want_y=True)
+        names = [n for n, _ in eg.profile_read()]
+    finally:
+        eg.profile_enable(False)
+    assert "proj_gate_kernel" in names, names
+    ref = orc.forward(w.tokens, w.H, lay, "bf16", gemm="mxfp8" if mx else "exact")
+    check_bf16_layer(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.bf16_to_f64(w.H),
+                     tag=f"wide d={d} mx={mx}")
+
+
 def test_forward_empty_is_noop():
     log("forward empty")
     w = small(1, B=1, T=4)
