@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "engram.h"
@@ -641,6 +642,59 @@ ENGRAM_API engram_status engram_forward(const int32_t* tokens, void* H, int64_t 
   r = run_retrieve(tokens, B, T, L, ha, ta, g.hdtype, st, e, stream);
   if (r != ENGRAM_OK) return r;
   return run_compute(tokens, e, H, B, T, L, g, st, alpha_out, y_out, f, stream);
+}
+
+namespace {
+
+// Scratch of engram_forward_noalloc: a device global, so each GPU holds its
+// own copy (at its own address) from the moment the library's code is loaded
+// there until the process ends.  On the host `scratch` names a stand-in, not
+// device memory: host code takes the array's device address from
+// hipGetSymbolAddress, once per device with that device current, and passes
+// only that address on.
+static __device__ __align__(256) unsigned char scratch[ENGRAM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch.
+engram_status current_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ENGRAM_EUNSUPPORTED, "forward_noalloc: device %d above %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || !aligned(p, 256)) return fail(ENGRAM_EHIP, "forward_noalloc: scratch address not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ENGRAM_OK;
+}
+
+}  // namespace
+
+ENGRAM_API engram_status engram_forward_noalloc(const int32_t* tokens, void* H, int64_t B, int64_t T,
+                                                const engram_layer* L, engram_decode_state* st, float* alpha_out,
+                                                float* y_out, hipStream_t stream) {
+  engram::HashArgs ha;
+  engram::TableArgs ta;
+  engram::GateConvArgs g;
+  engram_status r = check_call("forward_noalloc", L, st, true, B, T, &ha, &ta, &g);
+  if (r != ENGRAM_OK) return r;
+  const int64_t n_tok = B * T;
+  if (n_tok == 0) return ENGRAM_OK;
+  const size_t need = forward_ws_bytes(n_tok, L);
+  if (need > ENGRAM_NOALLOC_SCRATCH_BYTES)
+    return fail(ENGRAM_EINVAL, "forward_noalloc: the call needs %zu bytes of workspace, above the %u-byte scratch",
+                need, ENGRAM_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((r = current_scratch(&ws)) != ENGRAM_OK) return r;
+  return engram_forward(tokens, H, B, T, L, st, alpha_out, y_out, ws, ENGRAM_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 ENGRAM_API engram_status engram_retrieve(const int32_t* tokens, int64_t B, int64_t T, const engram_layer* L,

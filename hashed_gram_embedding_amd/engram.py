@@ -94,6 +94,8 @@ def lib():
         "engram_forward_workspace": (sz, [i64, i64, ctypes.POINTER(LayerStruct)]),
         "engram_forward": (i32, [vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
                                  ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
+        "engram_forward_noalloc": (i32, [vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
+                                         ctypes.POINTER(DecodeStateStruct), vp, vp, vp]),
         "engram_retrieve": (i32, [vp, i64, i64, ctypes.POINTER(LayerStruct), ctypes.POINTER(DecodeStateStruct), vp,
                                   vp]),
         "engram_forward_retrieved_workspace": (sz, [i64, i64, ctypes.POINTER(LayerStruct)]),
@@ -130,7 +132,7 @@ def lib():
 def exported_names():
     return ["engram_abi_version", "engram_last_error", "engram_hash_indices", "engram_gather",
             "engram_project_kv", "engram_gate_conv_workspace", "engram_gate_conv_forward",
-            "engram_forward_workspace", "engram_forward", "engram_retrieve", "engram_forward_retrieved_workspace",
+            "engram_forward_workspace", "engram_forward", "engram_forward_noalloc", "engram_retrieve", "engram_forward_retrieved_workspace",
             "engram_forward_retrieved", "engram_cache_build_workspace", "engram_cache_build",
             "engram_cache_update_workspace", "engram_cache_update", "engram_quantize_mxfp8",
             "engram_hot_buckets", "engram_hot_build", "engram_hot_lookup", "engram_forward_retrieved_prefetch",
@@ -466,6 +468,19 @@ def forward(tokens: torch.Tensor, H: torch.Tensor, layer: Layer, state: Optional
     _check(lib().engram_forward(_ptr(tokens), _ptr(H), B, T, ctypes.byref(layer.s), st, _ptr(alpha), _ptr(y),
                                 _ptr(ws), ws.numel(), _stream(stream)))
     return alpha, y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # ENGRAM_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(tokens: torch.Tensor, H: torch.Tensor, layer: Layer, state: Optional[DecodeState] = None,
+                    alpha: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None, stream=None):
+    """engram_forward_noalloc: the layer with the library's own scratch (no
+    device allocation in the call; alpha / y are optional caller buffers)."""
+    B, T = tokens.shape
+    st = ctypes.byref(state.s) if state is not None else None
+    _check(lib().engram_forward_noalloc(_ptr(tokens), _ptr(H), B, T, ctypes.byref(layer.s), st, _ptr(alpha),
+                                        _ptr(y), _stream(stream)))
 
 
 def rows_buffer(B: int, T: int, layer: Layer, device=None) -> torch.Tensor:

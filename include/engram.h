@@ -22,7 +22,8 @@
  *    alias of mapped pinned host memory); "host" pointers are read on the
  *    host during the call only.  The caller owns every buffer; the library
  *    keeps no pointer after a call returns and allocates no device memory
- *    (scratch comes in through `ws`).
+ *    (scratch comes in through `ws`; engram_forward_noalloc uses a scratch
+ *    array of the library's code instead).
  *  - Every compute call is asynchronous on `stream` (0 = the null stream)
  *    and never synchronises.  Calls are reentrant; calls that write the same
  *    buffers must be ordered by the caller.
@@ -251,6 +252,26 @@ engram_status engram_forward(const int32_t* tokens, void* H, int64_t B, int64_t 
                              const engram_layer* L, engram_decode_state* st,
                              float* alpha_out, float* y_out, void* ws, size_t ws_bytes,
                              hipStream_t stream);
+
+/* engram_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same layer, the same kernels and the same results bit for bit, with
+ * the workspace taken from scratch memory that the library holds, one array
+ * of ENGRAM_NOALLOC_SCRATCH_BYTES per GPU, created with the library's code on
+ * that GPU and kept until the process ends.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine); the caller still passes
+ * tokens, H, the layer's memory and the optional outputs.  Nothing in the
+ * scratch needs to start at zero: every call writes what it reads there.
+ * Calls that overlap on one GPU (on different streams, or from several
+ * threads without ordering) share that GPU's scratch and race; order them.
+ * EINVAL when the call needs more than ENGRAM_NOALLOC_SCRATCH_BYTES of
+ * workspace (engram_forward_workspace(B, T, L) above it: 4,096 tokens of a
+ * single-branch d = 1024 layer need 26 MiB); other arguments as for
+ * engram_forward. */
+#define ENGRAM_NOALLOC_SCRATCH_BYTES (32u << 20)
+engram_status engram_forward_noalloc(const int32_t* tokens, void* H, int64_t B, int64_t T,
+                                     const engram_layer* L, engram_decode_state* st,
+                                     float* alpha_out, float* y_out, hipStream_t stream);
 
 /* The layer in two halves, so that retrieval can run ahead of the hidden
  * states.  Steps 1-4 depend on the token ids alone (and, in decode, on the

@@ -325,3 +325,24 @@ def test_mxfp8_layer_outside_the_fused_projection_is_rejected():
     lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=4096), 0x20000, 0x30000, None)
     assert L.engram_retrieve(p, 0, 64, ctypes.byref(lay), None, p, None) == eg.OK     # d = 4096 passes the checks
 
+
+def test_forward_noalloc_rejects_calls_beyond_its_scratch():
+    """engram_forward_noalloc checks every host-visible argument, and that the
+    call fits the library's fixed scratch, before it touches any device."""
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    hp, keep_h = _hash_params()
+    t, keep_t = _tables()
+    lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=64, hdtype=eg.F32))
+    per_tok = L.engram_forward_workspace(1, 1024, ctypes.byref(lay)) / 1024
+    T_big = int(eg.NOALLOC_SCRATCH_BYTES / per_tok) + 1024
+    assert L.engram_forward_workspace(1, T_big, ctypes.byref(lay)) > eg.NOALLOC_SCRATCH_BYTES
+    st, msg = _status(L.engram_forward_noalloc, p, p, 1, T_big, ctypes.byref(lay), None, None, None, None)
+    assert st == eg.EINVAL and "scratch" in msg
+    assert L.engram_forward_noalloc(p, p, 0, 64, ctypes.byref(lay), None, None, None, None) == eg.OK   # empty
+    assert L.engram_forward_noalloc(p, p, 1, 64, None, None, None, None, None) == eg.EINVAL
+    st_bad = eg.DecodeStateStruct(None, 0x20000, 0x30000)
+    assert L.engram_forward_noalloc(p, p, 1, 64, ctypes.byref(lay), ctypes.byref(st_bad), None, None, None) \
+        == eg.EINVAL
+    text = open(HEADER).read()
+    assert f"#define ENGRAM_NOALLOC_SCRATCH_BYTES (32u << 20)" in text and eg.NOALLOC_SCRATCH_BYTES == 32 << 20
