@@ -4,13 +4,19 @@
 
 One step is one pass of the whole layer path (hash, gather, projections,
 gate, conv and residual) over one batch, with every input already resident
-(in HBM, or in pinned host memory for the host-table configuration).  Prints
-one JSON line.
+(in HBM, or in pinned host memory for the host-table configuration).  The
+timed steps go round a rotation of distinct seeded batches (token ids and
+hidden states), enough of them that the table rows one batch reads have left
+the 256 MB Infinity Cache before that batch comes round again; rows shared
+between batches (frequent n-grams) stay cached as they would in a stream of
+real text.  Prints one JSON line.
 
 --config 1 (default; the metric's workload): single-branch bf16 layer, B = 1
     sequence of T = 4096 tokens (Zipf(1.1) ids over a 128,000-id vocabulary,
     projected to 98,560), 2 orders x 8 heads of 64-dim bf16 rows in 16
-    prime-sized tables (10,344,164 rows, 1.32 GB), d = d_mem = 1024.
+    prime-sized tables (10,344,164 rows, 1.32 GB), d = d_mem = 1024.  The
+    line also carries the other workloads under "secondary" (--no-secondary
+    skips them).
 --config 2: the same tables with M = 4 branches, B = 8, T = 4096.
 --config 3: decode: 256 sequences x 1 new token through 2 layers with int8
     rows (+ float32 row scales), after a 16-token prefill of each sequence.
@@ -22,6 +28,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -35,23 +42,28 @@ METRIC = "Engram layer tokens/s at T=4096 (lookup+gate+conv); gather HBM GB/s"
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
-
+PEAK_PCIE_GBPS = 64.0        # PCIe Gen5 x16, one direction (host-resident table rows)
 
 WARMUP_FLOOR_MS = 100.0   # least untimed warm-up before the timed steps
+ROTATION_BYTES = 512 << 20   # table rows a rotation of batches touches: twice the Infinity Cache
+CPU_HALO = 11                # positions before a token that its layer output depends on: (N-1) + (w-1)*N
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # defaults: the first few milliseconds of back-to-back steps on a fresh GPU
-    # run up to 7 % slower (clocks and caches settling), so the timed steps
-    # follow 200 eager and 200 graph-replayed warm-up steps
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
-    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="config 1: skip the other workloads (multi-branch, decode, host tables) in the line")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of HIP graphs")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0,
+                    help="CPU time of the oracle baseline (whole batch on every core, then one core)")
+    ap.add_argument("--ring", type=int, default=0,
+                    help="distinct batches in the timed rotation (default: enough to touch 512 MiB of rows; "
+                         "1 replays one batch, the cache-resident control)")
     ap.add_argument("--overlap", action="store_true",
                     help="also measure retrieval (Steps 1-4) run ahead on a second stream: hidden behind a "
                          "stand-in for the preceding layers, and pipelined across batches")
@@ -71,12 +83,30 @@ def parse():
                     help="config 3: run each layer as a plain engram_forward instead of carrying the next layer's "
                          "retrieval in the conv launch (engram_forward_retrieved_prefetch)")
     ap.add_argument("--no-controls", action="store_true",
-                    help="configs 1-2: skip the control measurements (a cold-cache pass that overwrites 512 MiB "
-                         "between steps, and the gather over uniform tokens)")
+                    help="configs 1-2: skip the control measurements (one batch replayed, a cold-cache pass that "
+                         "overwrites 512 MiB between steps, and the gather over uniform tokens)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB device to device three times "
                          "(a plain copy kernel of known size for scaling HBM byte counters)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
+
+
+def log(msg):
+    """Progress to stderr (the JSON line alone goes to stdout)."""
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def rotation_size(rows_bytes_per_batch, per_graph, override=0, least=8):
+    """Distinct batches in the timed rotation: enough that they touch
+    ROTATION_BYTES of table rows (at least `least`), rounded up to whole
+    graphs of per_graph steps."""
+    if override > 0:
+        n = override
+    else:
+        n = max(least, math.ceil(ROTATION_BYTES / max(rows_bytes_per_batch, 1)))
+    return per_graph * math.ceil(n / per_graph)
+
 
 
 def kernel_units(n_tok, lay, hdtype, hot_hit=None, mx=False):
@@ -129,61 +159,139 @@ def kernel_units(n_tok, lay, hdtype, hot_hit=None, mx=False):
     return units
 
 
-def setup(args, torch, eg, inputs):
-    """Returns (calls, n_tok, workload, layer_inputs, extra); calls holds one
-    zero-argument callable per library call of a step (one per layer forward;
-    in decode with the next layer's retrieval prefetched, layer 0's retrieval
-    and then one per layer, with extra["_layers"] the layer count)."""
+class Case:
+    """One workload on the device, ready to time.
+
+    calls(i): the library calls (zero-argument callables, launched on the
+    current stream) of step i, which runs batch i % ring of the rotation."""
+
+    def __init__(self, w, lays, n_tok, n_layers, ring, calls):
+        self.w, self.lays, self.n_tok, self.n_layers = w, lays, n_tok, n_layers
+        self.ring, self.calls = ring, calls
+        self.extra = {}      # reported keys
+        self.pipe = None     # (layers, tokens, H) of batch 0, for the overlap and LFU reports
+        self.hot = None      # (hot tier, keys, rows, hit rate per order)
+        self.keep = []       # device objects kept alive with the case
+
+
+def hot_tier_host(n_hot, inputs, w, lay):
+    """Engram-Nine hot tier on the host: per order the n_hot most frequent
+    n-grams of a seeded warm-up stream (projected with the layer's P, as
+    part of building the workload) and their N(0, 0.02) rows."""
+    hp, tab = lay.hash, lay.tables
+    warm = inputs.hot_warmup_tokens(w.config, 0)
+    xc = hp.proj[warm]
+    t0 = time.perf_counter()
+    keys, rows = {}, {}
+    for n in range(2, hp.max_n + 1):
+        keys[n] = inputs.frequent_ngrams(xc, n, n_hot)
+        rows[n] = inputs.hot_rows(w.config, 0, n, keys[n].shape[0], hp.heads * tab.dim, tab.dtype)
+    return keys, rows, {"warm_tokens": int(warm.size), "host_select_s": round(time.perf_counter() - t0, 2)}
+
+
+def hot_tier_device(eg, L, tok, tab_dtype, keys, rows, info):
+    dev_rows = {n: eg.to_device(r, tab_dtype, "cuda") for n, r in rows.items()}
+    t0 = time.perf_counter()
+    hot = eg.HotTier(keys, dev_rows, device="cuda")
+    t_build = time.perf_counter() - t0
+    L.set_hot(hot)
+    hit = (eg.hot_lookup(tok, L, hot) >= 0).float().mean(dim=(0, 1)).cpu().numpy()
+    info = dict(info)
+    info.update({"n_hot_per_order": {str(n): int(k.shape[0]) for n, k in keys.items()},
+                 "hit_rate_per_order": {str(n): round(float(hit[n - 2]), 4) for n in keys},
+                 "hot_rows_MiB": round(sum(r.nbytes for r in rows.values()) / 2 ** 20, 1),
+                 "host_mphf_build_s": round(t_build, 2)})
+    return (hot, keys, rows, [float(h) for h in hit]), info
+
+
+def rows_per_batch(lays, n_tok):
+    """Bytes of table rows one batch reads (every layer)."""
+    out = 0
+    for lay in lays:
+        tab = lay.tables
+        row = tab.dim * {"f32": 4, "bf16": 2, "i8": 1}[tab.dtype] + (4 if tab.dtype == "i8" else 0)
+        out += n_tok * lay.hash.n_tables * row
+    return out
+
+
+def build_case(args, cfg, torch, eg, inputs, w=None, per_graph=10, hot_host=None, mxfp8=False):
+    """Workload cfg on the device with its rotation of batches."""
     dev = "cuda"
-    cfg = args.config
     if cfg in (1, 2):
-        w = inputs.make_config(cfg)
+        w = w if w is not None else inputs.make_config(cfg)
         lay = w.layers[0]
-        L = eg.Layer(lay, w.dtype, dev, mxfp8=args.mxfp8)
-        tok = torch.from_numpy(w.tokens).to(dev)
-        H = eg.to_device(w.H, w.dtype, dev)
+        L = eg.Layer(lay, w.dtype, dev, mxfp8=mxfp8)
+        n_tok = w.B * w.T
+        ring = rotation_size(rows_per_batch([lay], n_tok), per_graph, args.ring, least=8)
+        h_bytes = w.H.nbytes
+        ring_h = min(ring, max(2, math.ceil(ROTATION_BYTES / h_bytes))) if ring > 1 else 1
+        log(f"{w.name}: {ring} token batches, {ring_h} hidden-state batches in the rotation")
+        toks = [torch.from_numpy(w.tokens).to(dev)] + \
+            [torch.from_numpy(inputs.token_batch(cfg, i, (w.B, w.T))).to(dev) for i in range(1, ring)]
+        Hs = [eg.to_device(w.H, w.dtype, dev)] + \
+            [eg.to_device(inputs.hidden_batch(cfg, i, w.H.shape, w.dtype), w.dtype, dev) for i in range(1, ring_h)]
         ws = torch.empty(eg.forward_workspace(w.B, w.T, L), dtype=torch.uint8, device=dev)
-        extra = {"_pipe": ([L], tok, H)}
-        if args.hot_tier > 0:
-            extra.update(hot_tier_setup(args, torch, eg, inputs, w, lay, L, tok))
-        return [lambda: eg.forward(tok, H, L, ws=ws)], w.B * w.T, w, [lay], extra
+        case = Case(w, [lay], n_tok, 1, ring,
+                    lambda i: [lambda: eg.forward(toks[i % ring], Hs[i % ring_h], L, ws=ws)])
+        case.extra["rotation"] = {"token_batches": ring, "hidden_batches": ring_h,
+                                  "table_row_bytes_per_batch": rows_per_batch([lay], n_tok)}
+        case.pipe = ([L], toks[0], Hs[0])
+        case.keep = [L, toks, Hs, ws]
+        if hot_host is not None:
+            keys, rows, info = hot_host
+            case.hot, case.extra["hot_tier"] = hot_tier_device(eg, L, toks[0], lay.tables.dtype, keys, rows, info)
+        return case
     if cfg == 3:
-        w = inputs.make_config(3)
+        w = w if w is not None else inputs.make_config(3)
         S = w.B
-        Ls = [eg.Layer(l, "bf16", dev, mxfp8=args.mxfp8) for l in w.layers]
+        Ls = [eg.Layer(l, "bf16", dev, mxfp8=mxfp8) for l in w.layers]
         states = [eg.DecodeState(S, 3, 1, 9, 1024, dev) for _ in Ls]
         ctx = torch.from_numpy(w.context).to(dev)
         Hc = eg.to_device(w.H_context, "bf16", dev)
         for L, st in zip(Ls, states):               # prefill the context (not timed)
             eg.forward(ctx, Hc, L, state=st)
-        tok = torch.from_numpy(w.tokens).to(dev)
-        H = eg.to_device(w.H, "bf16", dev)
+        ring = rotation_size(rows_per_batch(w.layers, S), per_graph, args.ring, least=64)
+        log(f"{w.name}: {ring} decode batches in the rotation")
+        toks = [torch.from_numpy(w.tokens).to(dev)] + \
+            [torch.from_numpy(inputs.token_batch(3, i, (S, 1))).to(dev) for i in range(1, ring)]
+        Hs = [eg.to_device(w.H, "bf16", dev)] + \
+            [eg.to_device(inputs.hidden_batch(3, i, w.H.shape), "bf16", dev) for i in range(1, ring)]
         wss = [torch.empty(eg.forward_workspace(S, 1, L), dtype=torch.uint8, device=dev) for L in Ls]
-        if args.no_layer_prefetch:
-            calls = [(lambda L=L, st=st, ws=ws: eg.forward(tok, H, L, state=st, ws=ws))
-                     for L, st, ws in zip(Ls, states, wss)]
-        else:
+        es = [eg.rows_buffer(S, 1, L, dev) for L in Ls]
+
+        def calls(i):
+            tok, H = toks[i % ring], Hs[i % ring]
+            if args.no_layer_prefetch:
+                return [(lambda L=L, st=st, ws=ws: eg.forward(tok, H, L, state=st, ws=ws))
+                        for L, st, ws in zip(Ls, states, wss)]
+
             # every layer but the last carries the next layer's retrieval (same
             # tokens, that layer's id history) in its conv launch
-            es = [eg.rows_buffer(S, 1, L, dev) for L in Ls]
-
-            def call(i):
-                if i + 1 < len(Ls):
-                    eg.forward_retrieved_prefetch(tok, es[i], H, Ls[i], tok, es[i + 1], ws=wss[i], next_layer=Ls[i + 1],
-                                                  state=states[i], next_state=states[i + 1])
+            def layer(j):
+                if j + 1 < len(Ls):
+                    eg.forward_retrieved_prefetch(tok, es[j], H, Ls[j], tok, es[j + 1], ws=wss[j],
+                                                  next_layer=Ls[j + 1], state=states[j], next_state=states[j + 1])
                 else:
-                    eg.forward_retrieved(tok, es[i], H, Ls[i], state=states[i], ws=wss[i])
-            # library calls of one step: layer 0's retrieval, then the layers
-            calls = [lambda: eg.retrieve(tok, Ls[0], es[0], state=states[0])] + \
-                [(lambda i=i: call(i)) for i in range(len(Ls))]
-        return calls, S, w, w.layers, {"decode": "256 sequences x 1 token, 2 layers, after a 16-token prefill"
-                                                 + ("" if args.no_layer_prefetch else
-                                                    "; layer 1's retrieval runs inside layer 0's conv launch"),
-                                       "_keep": (Ls, states), "_layers": len(Ls)}
+                    eg.forward_retrieved(tok, es[j], H, Ls[j], state=states[j], ws=wss[j])
+            return [lambda: eg.retrieve(tok, Ls[0], es[0], state=states[0])] + \
+                [(lambda j=j: layer(j)) for j in range(len(Ls))]
+        case = Case(w, w.layers, S, len(Ls), ring, calls)
+        case.extra["decode"] = "256 sequences x 1 token, 2 layers, after a 16-token prefill" + \
+            ("" if args.no_layer_prefetch else "; layer 1's retrieval runs inside layer 0's conv launch")
+        case.extra["rotation"] = {"token_batches": ring, "hidden_batches": ring,
+                                  "table_row_bytes_per_batch": rows_per_batch(w.layers, S)}
+        case.keep = [Ls, states, toks, Hs, wss, es]
+        return case
     # cfg == 4: host tables + HBM cache
-    w = inputs.make_config(4)
-    tok = torch.from_numpy(w.tokens).to(dev)
-    H = eg.to_device(w.H, "bf16", dev)
+    w = w if w is not None else inputs.make_config(4)
+    n_tok = w.B * w.T
+    ring = rotation_size(rows_per_batch(w.layers, n_tok), per_graph, args.ring, least=8)
+    ring_h = min(ring, max(2, math.ceil(ROTATION_BYTES / w.H.nbytes))) if ring > 1 else 1
+    log(f"{w.name}: {ring} token batches, {ring_h} hidden-state batches in the rotation")
+    toks = [torch.from_numpy(w.tokens).to(dev)] + \
+        [torch.from_numpy(inputs.token_batch(4, i, (w.B, w.T))).to(dev) for i in range(1, ring)]
+    Hs = [eg.to_device(w.H, "bf16", dev)] + \
+        [eg.to_device(inputs.hidden_batch(4, i, w.H.shape), "bf16", dev) for i in range(1, ring_h)]
     Ls, bufs, hits = [], [], []
     for li, lay in enumerate(w.layers):
         hb = eg.HostBuffer(lay.tables.rows.nbytes)
@@ -193,38 +301,19 @@ def setup(args, torch, eg, inputs):
         warm = torch.from_numpy(inputs.lfu_warmup_tokens(4, li).reshape(16, -1)).to(dev)
         slot, rows, _ = eg.cache_build(warm, L, lay.tables.total_rows // 10)
         L.set_cache(slot, rows)
-        z = eg.hash_indices(tok, L).long() + torch.from_numpy(lay.tables.row_offset).to(dev)
+        z = eg.hash_indices(toks[0], L).long() + torch.from_numpy(lay.tables.row_offset).to(dev)
         hits.append(round(float((slot[z] >= 0).float().mean().item()), 4))
         Ls.append(L)
     ws = torch.empty(max(eg.forward_workspace(w.B, w.T, L) for L in Ls), dtype=torch.uint8, device=dev)
-    calls = [(lambda L=L: eg.forward(tok, H, L, ws=ws)) for L in Ls]
-    return calls, w.B * w.T, w, w.layers, {"cache_hit_rate": hits, "_keep": (Ls, bufs), "_pipe": (Ls, tok, H)}
+    case = Case(w, w.layers, n_tok, len(Ls), ring,
+                lambda i: [(lambda L=L: eg.forward(toks[i % ring], Hs[i % ring_h], L, ws=ws)) for L in Ls])
+    case.extra["cache_hit_rate"] = hits
+    case.extra["rotation"] = {"token_batches": ring, "hidden_batches": ring_h,
+                              "table_row_bytes_per_batch": rows_per_batch(w.layers, n_tok)}
+    case.pipe = (Ls, toks[0], Hs[0])
+    case.keep = [Ls, bufs, toks, Hs, ws]
+    return case
 
-def hot_tier_setup(args, torch, eg, inputs, w, lay, L, tok):
-    """Engram-Nine hot tier for configs 1-2: per order the args.hot_tier most
-    frequent n-grams of a seeded warm-up stream (projected with the layer's
-    P on the host, as part of building the workload) with N(0, 0.02) rows."""
-    hp, tab = lay.hash, lay.tables
-    warm = inputs.hot_warmup_tokens(w.config, 0)
-    xc = hp.proj[warm]
-    keys, rows, dev_rows = {}, {}, {}
-    t0 = time.perf_counter()
-    for n in range(2, hp.max_n + 1):
-        keys[n] = inputs.frequent_ngrams(xc, n, args.hot_tier)
-        rows[n] = inputs.hot_rows(w.config, 0, n, keys[n].shape[0], hp.heads * tab.dim, tab.dtype)
-        dev_rows[n] = eg.to_device(rows[n], tab.dtype, "cuda")
-    t_sel = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    hot = eg.HotTier(keys, dev_rows, device="cuda")
-    t_build = time.perf_counter() - t0
-    L.set_hot(hot)
-    hit = (eg.hot_lookup(tok, L, hot) >= 0).float().mean(dim=(0, 1)).cpu().numpy()
-    info = {"n_hot_per_order": {str(n): int(k.shape[0]) for n, k in keys.items()},
-            "warm_tokens": int(warm.size),
-            "hit_rate_per_order": {str(n): round(float(hit[n - 2]), 4) for n in keys},
-            "hot_rows_MiB": round(sum(r.nbytes for r in rows.values()) / 2 ** 20, 1),
-            "host_select_s": round(t_sel, 2), "host_mphf_build_s": round(t_build, 2)}
-    return {"hot_tier": info, "_hot": (hot, keys, rows, [float(h) for h in hit])}
 
 
 # ---- HBM traffic from rocprofv3 counters ----
@@ -669,8 +758,263 @@ def measured_peaks(torch, shape=None):
     return out
 
 
-def main():
-    args = parse()
+def time_case(torch, eg, case, steps, warmup, eager=False, per_graph=10):
+    """Times `steps` steps of the case (HIP graphs of per_graph consecutive
+    steps, one graph per stretch of the rotation, replayed in rotation
+    order), then each kernel's duration from events its own dispatch records
+    (eager launches over the same rotation), and the eager step with host
+    launches.  Returns a dict of measurements."""
+    stream = torch.cuda.current_stream()
+    R = case.ring
+
+    def step(i):
+        for c in case.calls(i):
+            c()                                 # on the current stream
+
+    for i in range(max(warmup, min(R, 200))):
+        step(i)
+    torch.cuda.synchronize()
+    n_graphs = R // math.gcd(R, per_graph)      # graph g runs steps g*per_graph .. (g+1)*per_graph - 1
+    graphs = []
+    if not eager:
+        for g in range(n_graphs):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):          # captures on a side stream
+                for s in range(per_graph):
+                    step(g * per_graph + s)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+    pos = [0]
+
+    def run():                                  # the next per_graph steps of the rotation
+        if eager:
+            for s in range(per_graph):
+                step(pos[0] * per_graph + s)
+        else:
+            graphs[pos[0] % n_graphs].replay()
+        pos[0] += 1
+
+    # warm-up: whole cycles of the rotation, at least `warmup` steps and
+    # WARMUP_FLOOR_MS of back-to-back work (the first ~100 ms on a fresh GPU
+    # run up to 7 % slower while clocks and caches settle)
+    warm_steps = 0
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    warm_ms = 0.0
+    while warm_steps < warmup or warm_ms < WARMUP_FLOOR_MS or pos[0] % n_graphs != 0:
+        w0.record(stream)
+        run()
+        w1.record(stream)
+        w1.synchronize()
+        warm_ms += w0.elapsed_time(w1)
+        warm_steps += per_graph
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps // per_graph):
+        run()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del graphs
+
+    # eager steps with host launches (no profiling), the same rotation
+    n_eager = max(min(R, 200), 20)
+    t0.record(stream)
+    for i in range(n_eager):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = t0.elapsed_time(t1) / n_eager
+
+    # per-kernel durations: events recorded by each kernel's own dispatch
+    # (the library's stage timing), eager steps over the same rotation
+    eg.profile_enable(True)
+    samples = {}
+    for i in range(n_eager):
+        for c in case.calls(i):
+            c()
+            for name, t in eg.profile_read():
+                samples.setdefault(name, []).append(t)
+    eg.profile_enable(False)
+    per_step = {k: len(v) / n_eager for k, v in samples.items()}   # launches of each kernel per step
+    kernel_ms = {k: sum(v) / len(v) for k, v in samples.items()}
+
+    def pcts(v):
+        q = np.percentile(np.asarray(v) * 1000.0, [10, 50, 90])
+        return [round(float(x), 2) for x in q]
+    return {"ms_per_step": ms, "warmup_steps_run": warm_steps, "graphs": 0 if eager else n_graphs,
+            "eager_ms_per_step": eager_ms, "kernel_ms": kernel_ms,
+            "kernel_launches_per_step": per_step,
+            "kernel_us_p10_p50_p90": {k: pcts(v) for k, v in samples.items()}}
+
+
+def rates_and_roofline(t, case, mxfp8=False, workload=None):
+    """Kernel rates (algorithmic units per second) and the roofline of the
+    longest kernel."""
+    lay = case.lays[0]
+    n_per_layer = case.n_tok
+    units = kernel_units(n_per_layer, lay, case.w.dtype, case.hot[3] if case.hot else None, mx=mxfp8)
+    rates = {}
+    for k, ms in t["kernel_ms"].items():
+        if k in units:
+            kind, amount = units[k]
+            rates[k] = amount / (ms * 1e-3) / (1e9 if kind == "hbm" else 1e12)
+    dominant = max((k for k in t["kernel_ms"] if k in units), key=lambda k: t["kernel_ms"][k])
+    kind, amount = units[dominant]
+    wl = workload or case.w.name
+    if kind == "mfma":
+        peak = PEAK_FP8_TFLOPS if mxfp8 else PEAK_BF16_TFLOPS
+        roof = {"bound": "mfma", "kernel": dominant, "achieved": round(rates[dominant], 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(rates[dominant] / peak, 4),
+                "traffic": traffic_for(wl, dominant), "units_per_launch": amount}
+    else:
+        roof = {"bound": "hbm", "kernel": dominant, "achieved": round(rates[dominant], 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(rates[dominant] / PEAK_HBM_GBPS, 4),
+                "traffic": traffic_for(wl, dominant), "units_per_launch": amount}
+    return units, rates, roof
+
+
+def kernel_block(t, rates, case):
+    """The per-kernel part of a report: mean durations, percentiles, rates,
+    and the sum of one step's kernel durations beside the graph step time."""
+    ks = sum(t["kernel_ms"][k] * t["kernel_launches_per_step"][k] for k in t["kernel_ms"])
+    return {"kernel_ms": {k: round(v, 5) for k, v in t["kernel_ms"].items()},
+            "kernel_us_p10_p50_p90": t["kernel_us_p10_p50_p90"],
+            "kernel_rate": {k: round(v, 2) for k, v in rates.items()},
+            "kernel_timing": {"how": "events recorded by each kernel's own dispatch, eager steps over the same "
+                                     "rotation of batches",
+                              "sum_of_kernels_ms_per_step": round(ks, 5),
+                              "graph_step_minus_kernel_sum_ms": round(t["ms_per_step"] - ks, 5),
+                              "eager_ms_per_step": round(t["eager_ms_per_step"], 5)}}
+
+
+def config_block(w, case, args, mxfp8):
+    lay = case.lays[0]
+    return {"workload": w.name, "B": w.B, "T": w.T, "layers_per_step": case.n_layers, "branches": lay.branches,
+            "d": lay.d, "d_mem": lay.d_mem, "tables": lay.hash.n_tables,
+            "table_rows": int(lay.tables.n_rows.sum()), "table_dtype": lay.tables.dtype,
+            "product": "mxfp8" if mxfp8 else w.dtype,
+            "hot_ngrams_per_order": args.hot_tier if w.config in (1, 2) else 0}
+
+
+_CPU_JOB = None   # (workload, hot tier) for the forked oracle workers
+
+
+def _cpu_chunk(bounds):
+    """The oracle's layer forward on tokens [lo, hi) of every sequence, with the
+    CPU_HALO positions before lo that the outputs there depend on."""
+    from oracle import engram_oracle as orc
+    lo, hi = bounds
+    w, hot = _CPU_JOB
+    s = max(0, lo - CPU_HALO)
+    orc.forward(w.tokens[:, s:hi], w.H[:, s:hi], w.layers[0], w.dtype, hot=hot)
+    return w.B * (hi - lo)
+
+
+def cpu_baseline(w, budget_s, hot=None):
+    """The CPU oracle (float64 numpy) on the whole batch of the workload, on
+    every core this process may use (at most 16): the batch's positions are
+    split into chunks (each with the 11 positions before it that its outputs
+    depend on) over one forked worker process per core, each with one BLAS
+    thread; whole-batch passes repeat for about 2/3 of the budget.  Then the
+    same oracle on one core (one process, one BLAS thread) over the whole
+    batch for the rest.  Runs before the GPU is touched (the workers are
+    forked)."""
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
+    global _CPU_JOB
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        cores = os.cpu_count() or 1
+    cores = max(1, min(16, cores))
+    T = w.T
+    n_chunks = cores * 2
+    step = max(CPU_HALO + 1, math.ceil(T / n_chunks))
+    chunks = [(lo, min(T, lo + step)) for lo in range(0, T, step)]
+    _CPU_JOB = (w, hot)
+    n_tok = w.B * w.T
+    with threadpool_limits(1):
+        ctx = mp.get_context("fork")
+        with ctx.Pool(cores) as pool:
+            pool.map(_cpu_chunk, chunks[:cores])          # workers started and warm
+            passes, t0 = 0, time.perf_counter()
+            while True:
+                done = sum(pool.map(_cpu_chunk, chunks, chunksize=1))
+                assert done == n_tok
+                passes += 1
+                el = time.perf_counter() - t0
+                if el >= budget_s * 2 / 3:
+                    break
+        one, t1 = 0, time.perf_counter()
+        while True:
+            _cpu_chunk((0, T))
+            one += 1
+            el1 = time.perf_counter() - t1
+            if el1 >= budget_s / 3:
+                break
+    _CPU_JOB = None
+    return {"value": round(passes * n_tok / el, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole batch ({w.B} x {w.T} tokens) per pass, {passes} passes in {el:.1f} s over "
+                      f"{cores} forked worker processes (one BLAS thread each; {len(chunks)} chunks of <= {step} "
+                      f"positions, each with the {CPU_HALO} positions before it)",
+            "single_core": {"value": round(one * n_tok / el1, 1), "unit": "tokens/s", "cores": 1,
+                            "sample": f"{one} whole-batch passes in {el1:.1f} s, one process, one BLAS thread"}}
+
+
+def report_case(args, torch, eg, case, steps, warmup, eager, mxfp8, per_graph):
+    t = time_case(torch, eg, case, steps, warmup, eager=eager, per_graph=per_graph)
+    wl = case.w.name + ("-mxfp8" if mxfp8 else "")
+    units, rates, roof = rates_and_roofline(t, case, mxfp8=mxfp8, workload=wl)
+    out = {"value": round(case.n_tok / (t["ms_per_step"] * 1e-3), 1), "unit": "tokens/s",
+           "ms_per_step": round(t["ms_per_step"], 5), "steps": steps, "warmup_steps_run": t["warmup_steps_run"],
+           "timing": (f"HIP graph replay, {per_graph} steps per graph, {t['graphs']} graphs over the rotation"
+                      if not eager else "eager launches")}
+    out.update(kernel_block(t, rates, case))
+    out["roofline"] = roof
+    g = rates.get("gather_kernel<hashed>", rates.get("gather_kernel<hashed,hot>"))
+    out["gather_GBps"] = None if g is None else round(g, 1)
+    if case.n_layers > 1:
+        out["tokens_per_s_per_layer"] = round(case.n_tok * case.n_layers / (t["ms_per_step"] * 1e-3), 1)
+    return out, units
+
+
+def secondary_report(args, torch, eg, inputs):
+    """The other workloads, each timed like the headline one (20 steps over its
+    rotation of batches, HIP graphs of 10 steps) with its kernels' rates and
+    the roofline of its longest kernel."""
+    out = {}
+    for cfg in (2, 3, 4):
+        log(f"secondary: building {inputs.CONFIG_NAMES[cfg]}")
+        t0 = time.perf_counter()
+        case = build_case(args, cfg, torch, eg, inputs)
+        log(f"secondary: {inputs.CONFIG_NAMES[cfg]} ready in {time.perf_counter() - t0:.1f} s; timing")
+        rep, _ = report_case(args, torch, eg, case, 20, 5, False, False, 10)
+        rep["config"] = config_block(case.w, case, args, False)
+        if cfg == 4:
+            # rows missing from the HBM cache cross PCIe: the gather's bound
+            hit = sum(case.extra["cache_hit_rate"]) / len(case.extra["cache_hit_rate"])
+            lay = case.lays[0]
+            miss_bytes = case.n_tok * lay.hash.n_tables * lay.tables.dim * 2 * (1 - hit)
+            g_ms = rep["kernel_ms"]["gather_kernel<hashed>"]
+            rep["roofline"] = {"bound": "pcie", "kernel": "gather_kernel<hashed>",
+                               "achieved": round(miss_bytes / (g_ms * 1e-3) / 1e9, 1), "peak": PEAK_PCIE_GBPS,
+                               "unit": "GB/s", "frac": round(miss_bytes / (g_ms * 1e-3) / 1e9 / PEAK_PCIE_GBPS, 4),
+                               "traffic": None, "units_per_launch": round(miss_bytes),
+                               "note": "bytes of the rows that miss the HBM cache (host rows read over PCIe) per "
+                                       "launch, over the gather's duration"}
+        for k, v in case.extra.items():
+            rep[k] = v
+        out[case.w.name] = rep
+        log(f"secondary: {case.w.name} {rep['ms_per_step'] * 1e3:.1f} us per step, {rep['value'] / 1e6:.2f} M tokens/s")
+        del case, rep
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.hbm_summary:
         from hashed_gram_embedding_amd import inputs
         if args.copy_calibration_mib <= 0:
@@ -683,167 +1027,81 @@ def main():
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part "
                                    "of this build (see the design notes on sharding)", "n_gpus": args.gpus}))
         sys.exit(2)
-
-    import torch
-    from hashed_gram_embedding_amd import engram as eg
     from hashed_gram_embedding_amd import inputs
 
-    calls, n_tok, w, lays, extra = setup(args, torch, eg, inputs)
-    stream = torch.cuda.current_stream()
-
-    def step():
-        for c in calls:
-            c()                                 # on the current stream
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Consecutive steps are captured into a HIP graph and replayed, so that
-    # host launch overhead does not pace a step of a few tens of microseconds;
-    # a graph holds several complete steps (as a model forward holds many
-    # layers), which pays the replay's own launch cost once per graph.
-    graph = None
-    per_graph = 1
-    if not args.eager:
-        per_graph = next(k for k in (10, 5, 2, 1) if args.steps % k == 0)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):           # captures on a side stream
-            for _ in range(per_graph):
-                step()
-        torch.cuda.synchronize()
-        run = graph.replay
-    else:
-        run = step
-    for _ in range(max(1, args.warmup // per_graph)):
-        run()
-    torch.cuda.synchronize()
-    # Warm-up floor: the first ~100 ms of back-to-back steps on a fresh GPU run
-    # up to 7 % slower (clocks and caches settling), so untimed replays go on
-    # until at least that much warm-up has run, whatever --warmup asked for.
-    warm_steps = args.warmup + max(1, args.warmup // per_graph) * per_graph
-    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    warm_ms = 0.0
-    while warm_ms < WARMUP_FLOOR_MS:
-        w0.record(stream)
-        run()
-        w1.record(stream)
-        w1.synchronize()
-        warm_ms += w0.elapsed_time(w1)
-        warm_steps += per_graph
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps // per_graph):
-        run()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-
-    # per-kernel durations: HIP events that the library records on the launch
-    # stream around each kernel of the same forward calls (eager launches)
-    # (the same loop also times each eager layer call with events on the stream)
-    eg.profile_enable(True)
-    samples, layer_ms = {}, []
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for it in range(args.warmup + args.steps):
-        for c in calls:
-            e0.record(stream)
-            c()
-            e1.record(stream)
-            for name, t in eg.profile_read():
-                if it >= args.warmup:
-                    samples.setdefault(name, []).append(t)
-            if it >= args.warmup:
-                e1.synchronize()
-                layer_ms.append(e0.elapsed_time(e1))
-    eg.profile_enable(False)
-    kernel_ms = {k: sum(v) / len(v) for k, v in samples.items()}
-
-    def pcts(v):
-        q = np.percentile(np.asarray(v) * 1000.0, [10, 50, 90])
-        return [round(float(x), 2) for x in q]
-    kernel_us_p10_p50_p90 = {k: pcts(v) for k, v in samples.items()}
-    layer_us_p10_p50_p90 = pcts(layer_ms)
-
-    units = kernel_units(n_tok, lays[0], w.dtype, extra["_hot"][3] if "_hot" in extra else None,
-                         mx=args.mxfp8)
-    rates = {}
-    for k, t in kernel_ms.items():
-        if k in units:
-            kind, amount = units[k]
-            rates[k] = amount / (t * 1e-3) / (1e9 if kind == "hbm" else 1e12)
-    dominant = max((k for k in kernel_ms if k in units), key=lambda k: kernel_ms[k])
-    kind, amount = units[dominant]
-    if kind == "mfma":
-        peak = PEAK_FP8_TFLOPS if args.mxfp8 else PEAK_BF16_TFLOPS
-        roof = {"bound": "mfma", "kernel": dominant, "achieved": round(rates[dominant], 2),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(rates[dominant] / peak, 4),
-                "traffic": traffic_for(w.name + ("-mxfp8" if args.mxfp8 else ""), dominant),
-                "units_per_launch": amount}
-    else:
-        roof = {"bound": "hbm", "kernel": dominant, "achieved": round(rates[dominant], 1),
-                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(rates[dominant] / PEAK_HBM_GBPS, 4),
-                "traffic": traffic_for(w.name, dominant), "units_per_launch": amount}
-    gather_gbps = rates.get("gather_kernel<hashed>", rates.get("gather_kernel<hashed,hot>"))
-    lay0 = lays[0]
-    n_layers = extra.get("_layers", len(calls))
-    peaks = measured_peaks(torch, (n_tok // n_layers, (1 + lay0.branches) * lay0.d, lay0.d_mem)
-                           if args.config in (1, 2) else None)
-    # (no FP8 matmul is re-measured, so an MXFP8 product has no measured peak)
-    ref = None if (kind == "mfma" and args.mxfp8) else \
-        (peaks["bf16_gemm_TFLOPs"] if kind == "mfma" else peaks["hbm_copy_GBps"])
-    roof["frac_of_measured_peak"] = None if ref is None else round(roof["achieved"] / ref, 4)
-
+    per_graph = next(k for k in (10, 5, 2, 1) if args.steps % k == 0)
+    log(f"building {inputs.CONFIG_NAMES[args.config]}")
+    w = inputs.make_config(args.config)
+    hot_host = None
+    if args.hot_tier > 0 and args.config in (1, 2):
+        hot_host = hot_tier_host(args.hot_tier, inputs, w, w.layers[0])
     cpu = None
     if not args.no_cpu_baseline and args.config in (1, 2):
+        log("CPU oracle baseline")
         hot = None
-        if "_hot" in extra:
-            _, keys, rows, _ = extra["_hot"]
+        if hot_host is not None:
+            keys, rows, _ = hot_host
             hot = {"keys": {n: [tuple(int(v) for v in r) for r in k] for n, k in keys.items()}, "rows": rows}
         cpu = cpu_baseline(w, args.cpu_budget_s, hot)
 
-    lay = lays[0]
+    import torch
+    from hashed_gram_embedding_amd import engram as eg
+
+    log("device setup")
+    case = build_case(args, args.config, torch, eg, inputs, w=w, per_graph=per_graph, hot_host=hot_host,
+                      mxfp8=args.mxfp8)
+    log("timing")
+    rep, units = report_case(args, torch, eg, case, args.steps, args.warmup, args.eager, args.mxfp8, per_graph)
+    lay0 = case.lays[0]
+    peaks = measured_peaks(torch, (case.n_tok, (1 + lay0.branches) * lay0.d, lay0.d_mem)
+                           if args.config in (1, 2) else None)
+    roof = rep["roofline"]
+    # (no FP8 matmul is re-measured, so an MXFP8 product has no measured peak)
+    ref = None if (roof["bound"] == "mfma" and args.mxfp8) else \
+        (peaks["bf16_gemm_TFLOPs"] if roof["bound"] == "mfma" else peaks["hbm_copy_GBps"])
+    roof["frac_of_measured_peak"] = None if ref is None else round(roof["achieved"] / ref, 4)
+
     out = {
         "metric": METRIC,
-        "value": round(n_tok / (ms * 1e-3), 1),
+        "value": rep["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_steps_run": warm_steps,
-        "ms_per_step": round(ms, 5),
+        "warmup_steps_run": rep["warmup_steps_run"],
+        "ms_per_step": rep["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "mxfp8 projection, bf16 storage" if args.mxfp8 else w.dtype,
-        "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) tables, N(0,1) hidden states)",
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "layers_per_step": n_layers, "branches": lay.branches,
-                   "d": lay.d, "d_mem": lay.d_mem, "tables": lay.hash.n_tables,
-                   "table_rows": int(lay.tables.n_rows.sum()), "table_dtype": lay.tables.dtype,
-                   "hot_ngrams_per_order": args.hot_tier if args.config in (1, 2) else 0},
-        "timing": f"HIP graph replay, {per_graph} steps per graph" if graph is not None else "eager launches",
-        "gather_GBps": None if gather_gbps is None else round(gather_gbps, 1),
-        "kernel_ms": {k: round(v, 5) for k, v in kernel_ms.items()},
-        "kernel_us_p10_p50_p90": kernel_us_p10_p50_p90,
-        "eager_layer_call_us_p10_p50_p90": layer_us_p10_p50_p90,
-        "kernel_rate": {k: round(v, 2) for k, v in rates.items()},
-        "roofline": roof,
-        "measured_peaks": peaks,
-        "cpu_baseline": cpu,
+        "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) tables, N(0,1) hidden states); a rotation of "
+                "distinct batches so that table rows come from HBM",
+        "config": config_block(w, case, args, args.mxfp8),
+        "timing": rep["timing"],
+        "gather_GBps": rep["gather_GBps"],
     }
-    for k, v in extra.items():
-        if not k.startswith("_"):
-            out[k] = v
+    for k in ("kernel_ms", "kernel_us_p10_p50_p90", "kernel_rate", "kernel_timing", "tokens_per_s_per_layer"):
+        if k in rep:
+            out[k] = rep[k]
+    out["roofline"] = roof
+    out["measured_peaks"] = peaks
+    out["cpu_baseline"] = cpu
+    for k, v in case.extra.items():
+        out[k] = v
     if args.config in (1, 2) and not args.no_controls:
-        out["controls"] = control_report(torch, eg, inputs, w, lays[0], extra["_pipe"], units)
-    if args.config == 3:
-        out["tokens_per_s_per_layer"] = round(n_tok * n_layers / (ms * 1e-3), 1)
+        log("controls")
+        out["controls"] = control_report(torch, eg, inputs, w, lay0, case.pipe, units)
     if args.overlap and args.config in (1, 2):
-        out["retrieval_overlap"] = overlap_report(torch, eg, w, lays[0], args.steps, args.warmup)
+        out["retrieval_overlap"] = overlap_report(torch, eg, w, lay0, args.steps, args.warmup)
     if args.realtime_lfu and args.config == 4:
-        out["realtime_lfu"] = realtime_lfu_report(torch, eg, inputs, w, extra["_pipe"])
-    if args.overlap and "_pipe" in extra:
-        out["retrieval_pipelined"] = pipelined_report(torch, eg, w, extra["_pipe"], args.steps)
+        out["realtime_lfu"] = realtime_lfu_report(torch, eg, inputs, w, case.pipe)
+    if args.overlap and case.pipe is not None:
+        out["retrieval_pipelined"] = pipelined_report(torch, eg, w, case.pipe, args.steps)
+    if args.config == 1 and not args.no_secondary and not args.mxfp8 and args.hot_tier == 0:
+        del case
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out["secondary"] = secondary_report(args, torch, eg, inputs)
     print(json.dumps(out), flush=True)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -856,7 +1114,9 @@ def main():
 
 
 def control_report(torch, eg, inputs, w, lay, pipe, units, steps=20):
-    """Two controls of the measured kernel rates.
+    """Three controls of the measured kernel rates.
+    one batch: the rotation's first batch replayed, so that its rows stay in
+    the on-chip caches (what a benchmark that reuses one batch measures).
     cold: before every eager layer call a 512 MiB buffer is overwritten (more
     than the 256 MB Infinity Cache), so tables, W and e start outside the
     on-chip caches; per-kernel times from the dispatch events.
@@ -867,6 +1127,12 @@ def control_report(torch, eg, inputs, w, lay, pipe, units, steps=20):
     ws = torch.empty(eg.forward_workspace(w.B, w.T, L), dtype=torch.uint8, device="cuda")
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     eg.profile_enable(True)
+    one = {}
+    for it in range(3 + steps):
+        eg.forward(tok, H, L, ws=ws)
+        for name, t in eg.profile_read():
+            if it >= 3:
+                one.setdefault(name, []).append(t)
     cold = {}
     for it in range(3 + steps):
         flush.fill_(it & 0xff)
@@ -885,46 +1151,23 @@ def control_report(torch, eg, inputs, w, lay, pipe, units, steps=20):
                 uni.append(t)
     eg.profile_enable(False)
     cold_ms = {k: sum(v) / len(v) for k, v in cold.items()}
+    one_ms = {k: sum(v) / len(v) for k, v in one.items()}
 
     def rate(name, ms):
         kind, amount = units[name]
         return round(amount / (ms * 1e-3) / (1e9 if kind == "hbm" else 1e12), 1)
     g_name = next(k for k in cold_ms if k.startswith("gather"))
     uni_ms = sum(uni) / len(uni)
-    return {"cold_kernel_us": {k: round(v * 1000, 2) for k, v in cold_ms.items()},
+    return {"one_batch_kernel_us": {k: round(v * 1000, 2) for k, v in one_ms.items()},
+            "one_batch_rate": {k: rate(k, v) for k, v in one_ms.items() if k in units},
+            "cold_kernel_us": {k: round(v * 1000, 2) for k, v in cold_ms.items()},
             "cold_rate": {k: rate(k, v) for k, v in cold_ms.items() if k in units},
             "uniform_tokens_gather_us": round(uni_ms * 1000, 2),
             "uniform_tokens_gather_GBps": rate(g_name, uni_ms),
-            "how": "cold: a 512 MiB buffer overwritten before each of 20 eager layer calls; uniform: "
+            "how": "one batch: the first batch of the rotation 20 times in a row (its rows stay in the caches); "
+                   "cold: a 512 MiB buffer overwritten before each of 20 eager layer calls; uniform: "
                    "engram_retrieve over seeded uniform raw ids, 20 calls; rates are algorithmic units per second"}
 
-
-def cpu_baseline(w, budget_s, hot=None):
-    """The CPU oracle (float64, numpy) on a bounded sample of the same workload:
-    whole forward passes over the first 1024 tokens of sequence 0, repeated
-    until the time budget is used; reported as tokens/s.  hot: the oracle's
-    form of the Engram-Nine tier when the workload has one."""
-    from oracle import engram_oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    lay = w.layers[0]
-    Ts = min(w.T, 1024)
-    tok = w.tokens[:1, :Ts]
-    Hs = w.H[:1, :Ts]
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        orc.forward(tok, Hs, lay, w.dtype, hot=hot)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": round(n * Ts / el, 1), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} forward passes of the float64 oracle over the first {Ts} tokens of sequence 0 "
-                      f"({el:.1f} s); cores = BLAS threads (the rest of the oracle is single-threaded numpy)"}
 
 
 if __name__ == "__main__":

@@ -32,7 +32,7 @@ from typing import List, Optional
 import numpy as np
 
 # stream ids inside SeedSequence([config, layer, stream])
-S_TOKENS, S_PROJ, S_MULT, S_TABLES, S_H, S_W, S_CONV, S_LFU, S_CONTEXT, S_HOT, S_UNIFORM = range(11)
+S_TOKENS, S_PROJ, S_MULT, S_TABLES, S_H, S_W, S_CONV, S_LFU, S_CONTEXT, S_HOT, S_UNIFORM, S_RING = range(12)
 
 F32, BF16, I8 = "f32", "bf16", "i8"
 
@@ -457,3 +457,23 @@ def hot_rows(config: int, layer: int, n: int, n_hot: int, width: int, dtype: str
     if dtype == BF16:
         return normal_bf16_bits(rng, n_hot * width, std).reshape(n_hot, width)
     return normal_f32(rng, n_hot * width, std).reshape(n_hot, width)
+
+
+# --------------------------------------------------------------------------
+# Rotations of distinct batches for timing: batch 0 is the workload's own;
+# batch i > 0 is drawn like it from SeedSequence([config, i, S_RING]) (token
+# ids) or SeedSequence([config, i, S_RING + 1]) (hidden states).
+# --------------------------------------------------------------------------
+
+def token_batch(config: int, i: int, shape, vocab: int = 128_000) -> np.ndarray:
+    """Batch i of a rotation of Zipf(1.1) token batches of `shape`."""
+    return zipf_tokens(rng_for(config, i, S_RING), vocab, 1.1, shape)
+
+
+def hidden_batch(config: int, i: int, shape, dtype: str = BF16) -> np.ndarray:
+    """Hidden states of batch i of a rotation, N(0, 1), as bf16 bits or float32."""
+    rng = rng_for(config, i, S_RING + 1)
+    n = int(np.prod(shape))
+    if dtype == BF16:
+        return normal_bf16_bits(rng, n, 1.0).reshape(shape)
+    return normal_f32(rng, n, 1.0).reshape(shape)

@@ -64,3 +64,39 @@ def test_hbm_summary_scales_counters_by_the_calibration_copy(tmp_path, capsys):
     cells = [c.strip() for c in row.strip().strip("|").split("|")]
     assert cells[0] == "wl" and int(cells[2]) == 2 * 5000 * 1024 and int(cells[3]) == 8192 * 1024
     assert cells[4] == "2" and cells[5] == bench.kernel_source_hash("gather_kernel<hashed>")
+
+
+def test_rotation_touches_twice_the_infinity_cache():
+    """The timed rotation holds whole graphs of batches and enough batches that
+    their table rows add up to 512 MiB: 70 single-branch batches (8 MiB of
+    rows each), 10 four-branch batches (64 MiB each)."""
+    lay = inputs.make_config(1, T=8, rows_per_table=997).layers[0]
+    assert bench.rows_per_batch([lay], 4096) == 4096 * 16 * 128
+    assert bench.rotation_size(bench.rows_per_batch([lay], 4096), 10) == 70
+    assert bench.rotation_size(bench.rows_per_batch([lay], 32768), 10) == 10
+    assert bench.rotation_size(bench.rows_per_batch([lay], 32768), 10, override=1) == 10
+    assert bench.rotation_size(123, 5, override=7) == 10
+    # batches of the rotation are seeded: the same draw twice, different batches differ
+    a, b = inputs.token_batch(1, 3, (1, 64)), inputs.token_batch(1, 3, (1, 64))
+    assert np.array_equal(a, b) and not np.array_equal(a, inputs.token_batch(1, 4, (1, 64)))
+    assert np.array_equal(inputs.hidden_batch(1, 2, (1, 4, 1, 8)), inputs.hidden_batch(1, 2, (1, 4, 1, 8)))
+
+
+def test_cpu_baseline_covers_the_whole_batch_on_every_core():
+    w = inputs.make_config(1, B=2, T=100, rows_per_table=997)
+    r = bench.cpu_baseline(w, 0.3)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0
+    assert 1 <= r["cores"] <= 16 and r["single_core"]["cores"] == 1 and r["single_core"]["value"] > 0
+    assert "2 x 100 tokens" in r["sample"]
+
+
+def test_chunked_oracle_with_halo_equals_the_whole_batch():
+    """The CPU baseline's chunks (each with the 11 positions before it) give
+    exactly the outputs of the oracle over the whole batch."""
+    from oracle import engram_oracle as orc
+    w = inputs.make_config(1, B=2, T=60, rows_per_table=997)
+    full = orc.forward(w.tokens, w.H, w.layers[0], "bf16")
+    for lo, hi in ((0, 13), (13, 30), (30, 60)):
+        s = max(0, lo - bench.CPU_HALO)
+        part = orc.forward(w.tokens[:, s:hi], w.H[:, s:hi], w.layers[0], "bf16")
+        assert np.array_equal(part["Y"][:, lo - s:], full["Y"][:, lo:hi])
