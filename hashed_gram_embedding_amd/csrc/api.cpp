@@ -293,7 +293,7 @@ size_t forward_ws_bytes(int64_t n_tok, const engram_layer* L) {
 // next: a hashed gather of another batch to run with this conv (in the same
 // launch where a fused form exists, else right after it), or null.
 engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdtype, const float4* stats, int qv,
-                              int qk, int64_t B, int64_t T, const engram::GateConvArgs& g, engram_decode_state* st,
+                              int qk, bool mixed, int64_t B, int64_t T, const engram::GateConvArgs& g, engram_decode_state* st,
                               const int32_t* tokens, const int32_t* proj, int32_t max_n, int32_t vocab,
                               float* alpha_out, float* gamma, float* y_out, hipStream_t s,
                               const engram::GatherJob* next = nullptr,
@@ -305,6 +305,8 @@ engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdty
   ca.stats = stats;
   ca.qv = qv;
   ca.qk = qk;
+  ca.mixed = mixed;
+  ca.kq0 = mixed ? 0 : qv;
   ca.nq = qv + g.branches * qk;
   ca.B = B;
   ca.T = T;
@@ -507,7 +509,7 @@ ENGRAM_API engram_status engram_gate_conv_forward(void* H, const void* kv, int64
   r = hip_status(engram::launch_gate_stats(H, kv, B * T, g, w.stats, stream), "gate statistics launch");
   if (r != ENGRAM_OK) return r;
   const int64_t stride = static_cast<int64_t>(1 + p->branches) * p->d;
-  return run_conv_commit(H, kv, stride, g.kvdtype, w.stats, 1, 1, B, T, g, st, nullptr, nullptr, 0, 1, alpha_out,
+  return run_conv_commit(H, kv, stride, g.kvdtype, w.stats, 1, 1, false, B, T, g, st, nullptr, nullptr, 0, 1, alpha_out,
                          w.gamma, y_out, stream);
 }
 
@@ -570,14 +572,17 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
     pa.N = static_cast<int>(n_out);
     pa.d = d;
     pa.M = M;
-    const int q = d / engram::proj_gate_tile_f(n_tok, static_cast<int>(n_out), d, static_cast<int>(d_mem), mx);
+    const engram::ProjGateLayout pl =
+        engram::proj_gate_layout(n_tok, static_cast<int>(n_out), d, static_cast<int>(d_mem), M, mx);
     // Decode step (T = 1, the strip conv): the state's ids and pos advance in
     // this launch and the conv writes the new ring row, so no commit kernel
     bool fold = false;
     if (st != nullptr && T == 1 && tokens != nullptr && st->ids != nullptr) {
       engram::ConvArgs probe{};
       probe.g = g;
-      probe.qv = probe.qk = q;
+      probe.qv = pl.qv;
+      probe.qk = pl.qk;
+      probe.mixed = pl.mixed;
       probe.B = B;
       probe.T = T;
       fold = engram::conv_strip_ts(probe) == 1;
@@ -595,7 +600,7 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
     prof_mark(stream, "proj_gate_kernel");
     r = hip_status(engram::launch_proj_gate(pa, stream), "projection launch");
     if (r != ENGRAM_OK) return r;
-    return run_conv_commit(H, f.kv, d, ENGRAM_F32, f.stats, q, q, B, T, g, st, tokens, L->hash.proj,
+    return run_conv_commit(H, f.kv, d, ENGRAM_F32, f.stats, pl.qv, pl.qk, pl.mixed, B, T, g, st, tokens, L->hash.proj,
                            L->hash.max_n, static_cast<int32_t>(L->hash.vocab), alpha_out, f.gamma, y_out, stream, next, fold);
   }
   // Step 5 into float32 projections, then whole-row gate statistics
@@ -607,7 +612,7 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
   prof_mark(stream, "gate_stats_kernel");
   r = hip_status(engram::launch_gate_stats(H, f.kv, n_tok, g, f.stats, stream), "gate statistics launch");
   if (r != ENGRAM_OK) return r;
-  return run_conv_commit(H, f.kv, n_out, ENGRAM_F32, f.stats, 1, 1, B, T, g, st, tokens, L->hash.proj,
+  return run_conv_commit(H, f.kv, n_out, ENGRAM_F32, f.stats, 1, 1, false, B, T, g, st, tokens, L->hash.proj,
                          L->hash.max_n, static_cast<int32_t>(L->hash.vocab), alpha_out, f.gamma, y_out, stream, next);
 }
 

@@ -151,6 +151,17 @@ constexpr int kProjGateTileF = 64;   // narrowest feature tile (bounds the stati
 // tiles plus one branch's key tiles, qv + qk <= kConvMaxStats.
 constexpr int kConvMaxStats = 64;
 int proj_gate_tile_f(int64_t n_tok, int N, int d, int K, bool mx);   // feature columns per gate-statistics tile
+// Gate statistics of a projection launch: qv tiles feed v.v; qk tiles per
+// branch feed h.h, k.k, h.k (after the qv ones); mixed = every one of the
+// qv tiles feeds all four sums (qk = 0).
+struct ProjGateLayout {
+  int tf;
+  bool small;
+  bool mixed;
+  int qv;
+  int qk;
+};
+ProjGateLayout proj_gate_layout(int64_t n_tok, int N, int d, int K, int M, bool mx);
 hipError_t launch_proj_gate(const ProjGateArgs& a, hipStream_t s);
 
 // Whole-row gate statistics from given projections: stats [n_tok][1+M].
@@ -165,6 +176,8 @@ struct ConvArgs {
   int qv;
   int qk;
   int nq;
+  int mixed;            // each of the qv statistics also carries the key sums (qk = 0)
+  int kq0;              // first statistic of a row that carries key sums: 0 when mixed, else qv
   int64_t B;
   int64_t T;
   GateConvArgs g;

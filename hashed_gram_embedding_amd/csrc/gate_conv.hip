@@ -244,7 +244,7 @@ conv_kernel(ConvArgs a) {
       const float4* st = sstat + tid * nqb;
       float svv = 0.f, shh = 0.f, skk = 0.f, shk = 0.f;
       for (int q = 0; q < a.qv; ++q) svv += st[q].w;
-      for (int q = a.qv; q < nqb; ++q) {
+      for (int q = a.kq0; q < nqb; ++q) {
         shh += st[q].x;
         skk += st[q].y;
         shk += st[q].z;
@@ -452,13 +452,12 @@ __device__ __forceinline__ void conv_strip_body(const ConvArgs& a, int spx, int 
     for (int i = 0; i < kMaxQ; ++i) {
       const int q = q0 + i * kStatLanes;
       const float4 p = sp[pass][i];
-      if (q < a.qv) {
-        svv += p.w;
-      } else if (q < nqb) {
-        shh += p.x;
-        skk += p.y;
-        shk += p.z;
-      }
+      // a.kq0 = 0 (mixed statistics): the value statistics carry the key sums too
+      const bool key = q < a.qv ? q >= a.kq0 : q < nqb;
+      if (q < a.qv) svv += p.w;
+      shh += key ? p.x : 0.f;
+      skk += key ? p.y : 0.f;
+      shk += key ? p.z : 0.f;
     }
 #pragma unroll
     for (int off = 1; off < kStatLanes; off <<= 1) {
@@ -747,7 +746,8 @@ hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
   // both conv kernels stage at most kConvMaxStats statistics per row (the
   // projection launchers never produce more)
-  if (a.qv < 1 || a.qk < 1 || a.qv + a.qk > kConvMaxStats) return hipErrorInvalidValue;
+  if (a.qv < 1 || (a.qk < 1 && !a.mixed) || (a.mixed && a.qk != 0) || a.qv + a.qk > kConvMaxStats)
+    return hipErrorInvalidValue;
   switch (conv_strip_ts(a)) {   // the pages' conv (w = 4, dilation 3): strip kernel
     case 1: return launch_conv_strip<4, 3, 1, 4>(a, vdtype, s);
     case 4: return launch_conv_strip<4, 3, 4, 4>(a, vdtype, s);

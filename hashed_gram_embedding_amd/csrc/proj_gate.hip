@@ -76,14 +76,23 @@ __device__ __forceinline__ void advance_state(const ProjGateArgs& a) {
   }
 }
 
-// Main loop: each slice goes straight into the other of two LDS buffers
-// (global_load_lds_dwordx4) while this one is multiplied.  Measured on
-// gfx950 against staging through registers with two slices in flight: 3-5 %
-// faster for bf16 and 11 % for MXFP8; three LDS buffers (two slices in
-// flight, 128-column tiles only) were no faster than two.
-template <int TF, bool MX, int WT>
+// Main loop: slices go straight into LDS (global_load_lds_dwordx4), NBUF - 1
+// of them in flight while the oldest landed one is multiplied.  With one
+// slice in flight (NBUF = 2) the loop waits about as long for each slice as
+// it multiplies (matrix cores busy 27 % at 4096 tokens, waves waiting on
+// their loads 40 % of their cycles); three buffers (144 KiB of LDS at 128
+// columns) keep two slices in flight.
+//
+// MIXED (single-branch layers): a tile's W rows are TF/2 rows of W_V and the
+// same TF/2 rows of W_K, so the feature wavefront wf = 0 holds v and wf = 1
+// holds k for the same columns.  Every tile then stores half a tile of v and
+// reads half a tile of h, instead of value tiles storing whole v tiles while
+// key tiles only read h, and each token's statistics tile carries all four
+// sums (h.h, k.k, h.k of the key half, v.v of the value half).
+template <int TF, bool MX, int WT, int NBUF, bool MIXED>
 __global__ void __launch_bounds__(64 * WF * WT) __attribute__((amdgpu_waves_per_eu(WF * WT / 4, WF * WT / 4)))
 proj_gate_kernel(ProjGateArgs a) {
+  static_assert(NBUF == 2 || NBUF == 3, "two or three slice buffers");
   constexpr int kThreads = 64 * WF * WT;
   // a K slice is 128 bytes of every row: 64 bf16 values, or 128 MXFP8 codes
   // (four 32-value scale blocks)
@@ -95,18 +104,22 @@ proj_gate_kernel(ProjGateArgs a) {
   constexpr int NE = kEChunks / kThreads;  // e chunks loaded per thread and slice
   constexpr int I = TF / WF / 32;          // 32-row feature blocks per wavefront
   constexpr int J = TK / WT / 32;          // 32-row token blocks per wavefront
+  constexpr int kScaleWaves = (TF + TK) / 64;   // MXFP8: wavefronts that load a slice's scale words
   extern __shared__ u32x4_t lds[];
-  u32x4_t* Ws = lds;                  // [2][kWChunks]
-  u32x4_t* Es = lds + 2 * kWChunks;   // [2][kEChunks]
+  u32x4_t* Ws = lds;                     // [NBUF][kWChunks]
+  u32x4_t* Es = lds + NBUF * kWChunks;   // [NBUF][kEChunks]
   // MXFP8: the slice's scale bytes, one 32-bit word (4 blocks) per W row, then per e row
-  uint32_t* Ss = reinterpret_cast<uint32_t*>(lds + 2 * (kWChunks + kEChunks));   // [2][TF + TK]
+  uint32_t* Ss = reinterpret_cast<uint32_t*>(lds + NBUF * (kWChunks + kEChunks));   // [NBUF][TF + TK]
 
   const int n_tiles = a.tiles_f * a.tiles_t;
   const int L = blockIdx.x;
   const int tile = (n_tiles % kXcds == 0) ? (L % kXcds) * (n_tiles / kXcds) + L / kXcds : L;
   const int tf = tile % a.tiles_f;
   const int tt = tile / a.tiles_f;
-  const int f0 = tf * TF;
+  const int d = a.d;
+  const int f0 = MIXED ? tf * (TF / 2) : tf * TF;   // first feature (MIXED: first v and k column)
+  // W row of LDS row r of this tile's slices, counted from row f0
+  auto wrow = [&](int r) { return MIXED && r >= TF / 2 ? r + (d - TF / 2) : r; };
   const int64_t t0 = static_cast<int64_t>(tt) * TK;
 
   const int tid = threadIdx.x;
@@ -182,7 +195,7 @@ proj_gate_kernel(ProjGateArgs a) {
       for (int i = 0; i < NW; ++i) {
         const int c = tid + i * kThreads;
         const int r = c >> 3;
-        const char* src = wbase + static_cast<int64_t>(r) * K * ESZ + kb + (((c & 7) ^ ((r >> 1) & 7)) * 16);
+        const char* src = wbase + static_cast<int64_t>(wrow(r)) * K * ESZ + kb + (((c & 7) ^ ((r >> 1) & 7)) * 16);
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
                                          (__attribute__((address_space(3))) void*)(Ws + buf * kWChunks + i * kThreads + wave * 64),
                                          16, 0, 0);
@@ -201,10 +214,10 @@ proj_gate_kernel(ProjGateArgs a) {
         // the slice's scale word of every row (4 blocks of 32 codes): W rows,
         // then e rows, 64 rows per wavefront instruction, one instruction
         // for each of the first (TF + TK) / 64 wavefronts
-        static_assert((TF + TK) % 64 == 0 && (TF + TK) / 64 <= WF * WT, "one scale instruction per wavefront");
-        if (wave < (TF + TK) / 64) {
+        static_assert(kScaleWaves * 64 == TF + TK && kScaleWaves <= WF * WT, "one scale instruction per wavefront");
+        if (wave < kScaleWaves) {
           const int r = wave * 64 + lane;
-          const uint8_t* src = r < TF ? a.w_scale + static_cast<int64_t>(f0 + r) * (K / 32) + kt * 4
+          const uint8_t* src = r < TF ? a.w_scale + static_cast<int64_t>(f0 + wrow(r)) * (K / 32) + kt * 4
                                       : a.e_scale + min(t0 + (r - TF), a.n_tok - 1) * (K / 32) + kt * 4;
           __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
                                            (__attribute__((address_space(3))) void*)(Ss + buf * (TF + TK) + wave * 64),
@@ -212,23 +225,57 @@ proj_gate_kernel(ProjGateArgs a) {
         }
       }
     };
-    issue(0, 0);
-    // unrolled by two so that the buffer indices are constants
-    for (int kt0 = 0; kt0 < ksteps; kt0 += 2) {
+    // Wait until this wavefront's loads of slice kt have landed while the
+    // younger slices stay in flight (vmcnt counts this wavefront's loads:
+    // NW + NE per slice, one more for the scale words of an MXFP8 slice).
+    auto wait_slice = [&](int younger) {
+      if constexpr (NBUF == 3) {
+        if (younger > 0) {
+          if (MX && wave < kScaleWaves)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NW + NE + 1) : "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NW + NE) : "memory");
+          return;
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    if constexpr (NBUF == 2) {
+      // one slice in flight (the form the compiler allocates best for two
+      // buffers: 210 rather than 256 VGPRs at 256 columns)
+      issue(0, 0);
+      for (int kt0 = 0; kt0 < ksteps; kt0 += 2) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 2; ++u) {
+          const int kt = kt0 + u;
+          if (kt < ksteps) {
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (kt + 1 < ksteps) issue(kt + 1, u ^ 1);
+            ENGRAM_COMPUTE(u);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+    for (int p = 0; p < NBUF - 1; ++p)
+      if (p < ksteps) issue(p, p);
+    // unrolled by NBUF so that the buffer indices are constants
+    for (int kt0 = 0; kt0 < ksteps; kt0 += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
         const int kt = kt0 + u;
         if (kt < ksteps) {
           // this lane's loads of slice kt have landed and its fragment reads
           // of slice kt - 1 have returned; after the barrier, every lane's
           // have.  (A fence in place of the bare barrier would do the same,
           // but the compiler then also waits for all outstanding loads.)
-          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          wait_slice(min(NBUF - 2, ksteps - 1 - kt));
           // into the buffer of slice kt - 1, which every wavefront has read
-          if (kt + 1 < ksteps) issue(kt + 1, u ^ 1);
+          if (kt + NBUF - 1 < ksteps) issue(kt + NBUF - 1, (u + NBUF - 1) % NBUF);
           ENGRAM_COMPUTE(u);
         }
       }
+    }
     }
     // the epilogue reuses the LDS: all fragment reads done, no load in flight
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -236,14 +283,16 @@ proj_gate_kernel(ProjGateArgs a) {
 #undef ENGRAM_COMPUTE
 
   // ---- epilogue: acc[i][j][4g + r] is feature wf*TF/WF + i*32 + g*8 + (lane>>5)*4 + r
-  // of token wt*TK/WT + j*32 + (lane & 31) ----
-  const int d = a.d;
-  const bool is_v = f0 < d;
-  const int m = is_v ? 0 : f0 / d - 1;
-  // the main loop's LDS is free now: a value tile turns v around in its
-  // first 4*TK*TF/WT bytes and a key tile holds its h rows ([TK][TF] bf16)
-  // there; the per-token partials go after them
+  // of the tile's LDS rows, token wt*TK/WT + j*32 + (lane & 31) ----
+  // value or key columns: per wavefront (MIXED) or per tile
+  const bool is_v = MIXED ? wf == 0 : f0 < d;
+  const int m = MIXED ? 0 : (is_v ? 0 : f0 / d - 1);
+  // the main loop's LDS is free now: a value wavefront turns its v block
+  // around in a private region, a key tile (or key wavefront) holds its h
+  // rows; the per-token partials go after them
   float4* red = reinterpret_cast<float4*>(lds + TK * TF / 8);   // [TK][WF] partials of the feature wavefronts
+  // first column of this wavefront's block: within v, or within branch m's h
+  const int fcol = MIXED ? f0 : (is_v ? f0 + wf * (TF / WF) : f0 - (1 + m) * d);
   if (is_v) {
     // Each wavefront turns its 32-token x TF/WF-feature block of v around in
     // a private LDS region ([32][VC] 16-byte chunks, chunk c of row r at
@@ -252,7 +301,7 @@ proj_gate_kernel(ProjGateArgs a) {
     // writes 4*TF/WF contiguous bytes of one token.
     constexpr int VC = TF / WF / 4;                      // 16-byte chunks per row of the block
     float4* Vs = reinterpret_cast<float4*>(lds) + wave * 32 * VC;
-    float* vrow0 = a.v + t0 * d + f0 + wf * (TF / WF);
+    float* vrow0 = a.v + t0 * d + fcol;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int r = lane & 31;
@@ -283,23 +332,32 @@ proj_gate_kernel(ProjGateArgs a) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next block's writes
     }
   } else {
-    // The tile's h rows ([TK][TF] bf16, 2*TF contiguous bytes per token) go
-    // into LDS with 16-byte direct loads, a wavefront instruction covering
-    // whole rows; chunk c of row r lands in slot c ^ (r & 15), so that the
-    // reads below (32 rows, one chunk each) spread over all banks.  Token
-    // rows past the end re-read the last valid row.  Sum k^2 meanwhile.
-    constexpr int HC = TF / 8;                 // 16-byte chunks per h row
-    constexpr int NH = TK * HC / kThreads;     // loads per thread
-    u32x4_t* Hs = lds;
-    const int fb = f0 - (1 + m) * d;           // the tile's first feature within branch m
+    // The h values of this block go into LDS with 16-byte direct loads, a
+    // wavefront instruction covering whole row runs; the chunks of a row are
+    // rotated by its row number, so that the reads below (32 rows, one
+    // chunk each) spread over the banks.  MIXED: each key wavefront loads its own
+    // TK/WT tokens x TF/2 columns into a private region and waits for its
+    // own loads only; otherwise the workgroup loads the tile's [TK][TF] h
+    // rows together (chunk c of row r in slot c ^ (r & HSW), HSW < HC).
+    // Token rows past the end re-read the last valid row.
+    // Sum k^2 meanwhile.
+    constexpr int HC = MIXED ? TF / 16 : TF / 8;                // 16-byte chunks per staged h row
+    constexpr int HROWS = MIXED ? TK / WT : TK;                 // rows staged by one loader
+    constexpr int HLOADERS = MIXED ? 64 : kThreads;             // threads sharing the loads
+    constexpr int NH = HROWS * HC / HLOADERS;                   // loads per thread
+    constexpr int HSW = HC < 16 ? HC - 1 : 15;                  // row bits in the chunk swizzle (< HC)
+    static_assert(NH * HLOADERS == HROWS * HC && (HC & (HC - 1)) == 0, "whole loads, power-of-two rows");
+    u32x4_t* Hs = MIXED ? lds + wave * (HROWS * HC) : lds;
+    const int hl_tid = MIXED ? lane : tid;
+    const int64_t hrow0 = MIXED ? t0 + wt * (TK / WT) : t0;
 #pragma unroll
     for (int q = 0; q < NH; ++q) {
-      const int u = q * kThreads + wave * 64 + lane;   // LDS slot this lane fills
+      const int u = q * HLOADERS + hl_tid;   // LDS slot this lane fills (64 consecutive per instruction)
       const int r = u / HC, sl = u % HC;
-      const int64_t tok = min(t0 + r, a.n_tok - 1);
-      const uint16_t* src = a.H + (tok * a.M + m) * d + fb + (sl ^ (r & 15)) * 8;
+      const int64_t tok = min(hrow0 + r, a.n_tok - 1);
+      const uint16_t* src = a.H + (tok * a.M + m) * d + fcol + (sl ^ (r & HSW)) * 8;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
-                                       (__attribute__((address_space(3))) void*)(Hs + q * kThreads + wave * 64),
+                                       (__attribute__((address_space(3))) void*)(Hs + q * HLOADERS + (MIXED ? 0 : wave * 64)),
                                        16, 0, 0);
     }
     float s1[J];
@@ -313,19 +371,23 @@ proj_gate_kernel(ProjGateArgs a) {
           s1[j] += acc[i][j][4 * g] * acc[i][j][4 * g] + acc[i][j][4 * g + 1] * acc[i][j][4 * g + 1] +
                    acc[i][j][4 * g + 2] * acc[i][j][4 * g + 2] + acc[i][j][4 * g + 3] * acc[i][j][4 * g + 3];
     }
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    const uint2* Hs2 = reinterpret_cast<const uint2*>(lds);
+    if constexpr (MIXED)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");              // this wavefront's own h block
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");   // every wavefront's part of the tile
+    const uint2* Hs2 = reinterpret_cast<const uint2*>(Hs);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int tl = wt * (TK / WT) + j * 32 + (lane & 31);
+      const int hr = MIXED ? j * 32 + (lane & 31) : tl;    // row in the staged h block
       float s0 = 0.f, s2 = 0.f;
 #pragma unroll
       for (int i = 0; i < I; ++i) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          // features wf*TF/WF + i*32 + g*8 + (lane>>5)*4 .. +3: half (lane>>5) of one chunk
-          const int c = wf * (TF / WF) / 8 + i * 4 + g;
-          const uint2 q = Hs2[(tl * HC + (c ^ (tl & 15))) * 2 + (lane >> 5)];
+          // features i*32 + g*8 + (lane>>5)*4 .. +3 of the block: half (lane>>5) of one chunk
+          const int c = (MIXED ? 0 : wf * (TF / WF) / 8) + i * 4 + g;
+          const uint2 q = Hs2[(hr * HC + (c ^ (hr & HSW))) * 2 + (lane >> 5)];
           const float x0 = acc[i][j][4 * g], x1 = acc[i][j][4 * g + 1];
           const float x2 = acc[i][j][4 * g + 2], x3 = acc[i][j][4 * g + 3];
           const float h0 = __uint_as_float(q.x << 16), h1 = __uint_as_float(q.x & 0xffff0000u);
@@ -570,15 +632,16 @@ proj_gate_small_kernel(ProjGateArgs a) {
   advance_state(a);
 }
 
-template <int TF, bool MX, int WT = 4>
+template <int TF, bool MX, int NBUF, bool MIXED, int WT = 4>
 hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   a.tiles_f = a.N / TF;
   a.tiles_t = static_cast<int>((a.n_tok + TK - 1) / TK);
-  // main loop: two slices (and MXFP8 scale words); epilogue: the h tile and
+  // main loop: NBUF slices (and MXFP8 scale words); epilogue: the h tile and
   // the per-token partials
-  const size_t lds = std::max(static_cast<size_t>(2 * (TF + TK) * 8) * sizeof(u32x4_t) +
-                                  (MX ? static_cast<size_t>(2 * (TF + TK)) * sizeof(uint32_t) : 0),
+  const size_t lds = std::max(static_cast<size_t>(NBUF * (TF + TK) * 8) * sizeof(u32x4_t) +
+                                  (MX ? static_cast<size_t>(NBUF * (TF + TK)) * sizeof(uint32_t) : 0),
                               static_cast<size_t>(TK * TF) * 2 + static_cast<size_t>(TK * WF) * sizeof(float4));
+  static_assert(NBUF * (TF + TK) * 8 * 16 + (MX ? NBUF * (TF + TK) * 4 : 0) <= 160 * 1024, "fits gfx950's LDS");
   // more than 64 KiB of dynamic LDS exceeds the default per-workgroup limit;
   // raise it once per device and instantiation (gfx950 has 160 KiB per CU)
   static std::atomic<uint64_t> attr_set{0};
@@ -587,12 +650,12 @@ hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if ((attr_set.load() & bit) == 0) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_kernel<TF, MX, WT>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_kernel<TF, MX, WT, NBUF, MIXED>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit);
   }
-  launch_k((proj_gate_kernel<TF, MX, WT>), dim3(a.tiles_f * a.tiles_t), dim3(64 * WF * WT), lds, s, a);
+  launch_k((proj_gate_kernel<TF, MX, WT, NBUF, MIXED>), dim3(a.tiles_f * a.tiles_t), dim3(64 * WF * WT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -624,6 +687,19 @@ bool proj_gate_small(int64_t n_tok, int N, int d) {
 bool proj_gate_small_for(int64_t n_tok, int N, int d, int K, bool mx) {
   if (!mx) return proj_gate_small(n_tok, N, d);
   return 2 * d / kSmallTF <= kConvMaxStats && K % 512 == 0 && n_tok * static_cast<int64_t>(N) <= (int64_t{3} << 19);
+}
+
+// The statistics layout of the launch that launch_proj_gate makes.  The
+// large kernel on a single-branch layer pairs value and key columns in each
+// tile (MIXED), so that every token's statistics tile holds all four sums.
+ProjGateLayout proj_gate_layout(int64_t n_tok, int N, int d, int K, int M, bool mx) {
+  ProjGateLayout l;
+  l.tf = proj_gate_tile_f(n_tok, N, d, K, mx);
+  l.small = l.tf == kSmallTF;
+  l.mixed = !l.small && M == 1;
+  l.qv = l.mixed ? 2 * d / l.tf : d / l.tf;
+  l.qk = l.mixed ? 0 : d / l.tf;
+  return l;
 }
 
 int proj_gate_tile_f(int64_t n_tok, int N, int d, int K, bool mx) {
@@ -665,12 +741,13 @@ hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
     if (proj_gate_small_for(in.n_tok, in.N, in.d, in.K, true)) return launch_small<true>(in, s);
     // 128-feature tiles, slices straight into LDS like the bf16 product
     // (the 256-feature tile's accumulators and FP8 operands spill registers)
-    return launch_tf<128, true>(in, s);
+    return in.M == 1 ? launch_tf<128, true, 3, true>(in, s) : launch_tf<128, true, 3, false>(in, s);
   }
   if (in.K % BK != 0) return hipErrorInvalidValue;
   if (proj_gate_small(in.n_tok, in.N, in.d)) return launch_small<false>(in, s);
-  if (proj_gate_tile_f(in.n_tok, in.N, in.d, in.K, false) == 256) return launch_tf<256, false>(in, s);
-  return launch_tf<128, false>(in, s);
+  if (proj_gate_tile_f(in.n_tok, in.N, in.d, in.K, false) == 256)
+    return in.M == 1 ? launch_tf<256, false, 2, true>(in, s) : launch_tf<256, false, 2, false>(in, s);
+  return in.M == 1 ? launch_tf<128, false, 3, true>(in, s) : launch_tf<128, false, 3, false>(in, s);
 }
 
 }  // namespace engram
