@@ -1,7 +1,7 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times.  The oracle recomputes sampled windows (with the 11-position
-halo that makes a window exact), sampled decode sequences, and the exact LFU
-admission; everything else is compared element by element on those samples."""
+benchmark times, on every token: the gathered rows bit for bit (MXFP8 codes
+and scale bytes too), and alpha, Y and H_out element by element against the
+oracle, sequence by sequence (the oracle runs each whole sequence)."""
 import numpy as np
 import pytest
 import torch
@@ -10,96 +10,103 @@ from hashed_gram_embedding_amd import engram as eg
 from hashed_gram_embedding_amd import inputs
 from oracle import engram_oracle as orc
 
-from parity import check_bf16_layer, log, to_f64
+from parity import bits_equal, check_bf16_layer, log, to_f64
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-HALO = 11   # (N-1) + (w-1)*N positions of history determine a position's output
 
 
-def check_windows(w, lay, a_g, y_g, h_g, starts, rows, L=64, tag="", gemm="exact"):
-    h_in = orc.storage_to_f64(w.H, w.dtype)
-    for b in rows:
-        for s in starts:
-            lo = max(0, s - HALO)
-            ref = orc.forward(w.tokens[b:b + 1, lo:s + L], w.H[b:b + 1, lo:s + L], lay, w.dtype, gemm=gemm)
-            k = s - lo
-            check_bf16_layer(a_g[b:b + 1, s:s + L], ref["alpha"][:, k:], y_g[b:b + 1, s:s + L], ref["Y"][:, k:],
-                             h_g[b:b + 1, s:s + L], h_in[b:b + 1, s:s + L], tag=f"{tag} b{b} s{s}")
+def check_rows(e_dev, ref_e, mx, tag):
+    """Gathered rows of one sequence: bf16 bit for bit, or the MXFP8 codes and
+    scale bytes of the oracle's quantisation of its bf16 rows."""
+    if not mx:
+        assert bits_equal(to_f64(e_dev), ref_e), f"{tag}: gathered rows differ"
+        return
+    codes, scales = e_dev
+    rq, rs = orc.quantize_mxfp8(ref_e)
+    assert np.array_equal(codes.cpu().numpy(), rq), f"{tag}: MXFP8 codes differ"
+    assert np.array_equal(scales.cpu().numpy(), rs), f"{tag}: MXFP8 scale bytes differ"
 
 
-def test_single_branch_full_size_sampled():
-    """The single-branch workload the benchmark's headline line times: B = 1,
-    T = 4096, the full 10.3M-row tables, bf16 and the MXFP8 product."""
-    log("single-branch full size: inputs")
-    w = inputs.make_config(1)
-    lay = w.layers[0]
-    starts = [0, 1000, 2048, 4096 - 64]
-    for mx in (False, True):
-        log(f"single-branch full size: forward mxfp8={mx}")
-        L = eg.Layer(lay, "bf16", DEV, mxfp8=mx)
-        H = eg.to_device(w.H, "bf16", DEV)
-        alpha, y = eg.forward(torch.from_numpy(w.tokens).to(DEV), H, L, want_alpha=True, want_y=True)
-        torch.cuda.synchronize()
-        a_g, y_g, h_g = to_f64(alpha), to_f64(y), to_f64(H)
-        log(f"single-branch full size: oracle windows mxfp8={mx}")
-        check_windows(w, lay, a_g, y_g, h_g, starts, [0], tag=f"c1 mx={mx}", gemm="mxfp8" if mx else "exact")
+def run_and_check(w, lay, L, tag, mx=False):
+    """engram_retrieve (rows) and engram_forward (alpha, Y, H_out) on the whole
+    workload, then every sequence against the oracle."""
+    B, T = w.B, w.T
+    tok = torch.from_numpy(w.tokens).to(DEV)
+    e = eg.rows_buffer(B, T, L, DEV)
+    eg.retrieve(tok, L, e)
+    H = eg.to_device(w.H, "bf16", DEV)
+    alpha, y = eg.forward(tok, H, L, want_alpha=True, want_y=True)
+    torch.cuda.synchronize()
+    d_mem = lay.d_mem
+    worst = [0.0, 0.0]
+    for b in range(B):
+        log(f"{tag}: oracle, sequence {b} of {B}")
+        ref = orc.forward(w.tokens[b:b + 1], w.H[b:b + 1], lay, "bf16", gemm="mxfp8" if mx else "exact")
+        if mx:
+            n = B * T * d_mem
+            codes = e[:n].view(B * T, d_mem)[b * T:(b + 1) * T]
+            scales = e[n:].view(B * T, d_mem // 32)[b * T:(b + 1) * T]
+            check_rows((codes, scales), ref["e"].reshape(T, d_mem), True, f"{tag} b{b}")
+        else:
+            check_rows(e[b * T:(b + 1) * T], ref["e"].reshape(T, d_mem), False, f"{tag} b{b}")
+        da, dy = check_bf16_layer(to_f64(alpha[b:b + 1]), ref["alpha"], to_f64(y[b:b + 1]), ref["Y"],
+                                  to_f64(H[b:b + 1]), orc.bf16_to_f64(w.H[b:b + 1]), tag=f"{tag} b{b}")
+        worst = [max(worst[0], da), max(worst[1], dy)]
+        del ref
+    log(f"{tag}: all {B * T} tokens checked; worst alpha err {worst[0]:.2e}, worst Y err {worst[1]:.3f} of tol")
 
 
 @pytest.mark.parametrize("mx", [False, True])
-def test_multi_branch_full_size_sampled(mx):
+def test_single_branch_full_size_every_token(mx):
+    """The single-branch workload the benchmark's headline line times: B = 1,
+    T = 4096, the full 10.3M-row tables; bf16 and the MXFP8 product."""
+    log(f"single-branch full size: inputs mxfp8={mx}")
+    w = inputs.make_config(1)
+    lay = w.layers[0]
+    run_and_check(w, lay, eg.Layer(lay, "bf16", DEV, mxfp8=mx), f"c1 mx={mx}", mx)
+
+
+@pytest.mark.parametrize("mx", [False, True])
+def test_multi_branch_full_size_every_token(mx):
     """B = 8, T = 4096, M = 4 branches (shared W_V, four W_K^(m), per-branch
     gate and conv), the full 10.3M-row tables; bf16 and the MXFP8 product."""
     log(f"multi-branch full size: inputs mxfp8={mx}")
     w = inputs.make_config(2)
     lay = w.layers[0]
-    L = eg.Layer(lay, "bf16", DEV, mxfp8=mx)
-    H = eg.to_device(w.H, "bf16", DEV)
-    log("multi-branch full size: forward")
-    alpha, y = eg.forward(torch.from_numpy(w.tokens).to(DEV), H, L, want_alpha=True, want_y=True)
-    torch.cuda.synchronize()
-    starts = [0, 777, 2048, 4096 - 64]
-    rows = [0, 3, 7]
-    # bring only the sampled windows to the host
-    a_g = np.zeros((8, 4096, 4))
-    y_g = np.zeros((8, 4096, 4, 1024))
-    h_g = np.zeros((8, 4096, 4, 1024))
-    for b in rows:
-        for s in starts:
-            a_g[b, s:s + 64] = to_f64(alpha[b, s:s + 64])
-            y_g[b, s:s + 64] = to_f64(y[b, s:s + 64])
-            h_g[b, s:s + 64] = to_f64(H[b, s:s + 64])
-    log("multi-branch full size: oracle windows")
-    check_windows(w, lay, a_g, y_g, h_g, starts, rows, tag=f"c2 mx={mx}", gemm="mxfp8" if mx else "exact")
+    run_and_check(w, lay, eg.Layer(lay, "bf16", DEV, mxfp8=mx), f"c2 mx={mx}", mx)
 
 
 @pytest.mark.parametrize("mx", [False, True])
-def test_decode_full_size_sampled(mx):
+def test_decode_full_size_every_sequence(mx):
     """256 sequences, int8 rows with per-row scales (703 MB per layer), each
     of the 2 layers: a 16-token prefill with state, then 3 single-token decode
-    steps; sampled sequences match the oracle at every step and the state's
-    ids and positions match exactly (bf16 and the MXFP8 product)."""
+    steps; every sequence matches the oracle at every step, and the state's
+    ids, positions and conv ring match (bf16 and the MXFP8 product)."""
     log(f"decode full size: inputs mxfp8={mx}")
     w = inputs.make_config(3, T=3)
     S = w.B
-    sample = [0, 1, 100, 255]
     for li, lay in enumerate(w.layers):
         log(f"decode full size: layer {li}")
         L = eg.Layer(lay, "bf16", DEV, mxfp8=mx)
         st = eg.DecodeState(S, 3, 1, 9, 1024, DEV)
-        ost = orc.new_state(len(sample), 3, 1, 9, 1024)
+        ost = orc.new_state(S, 3, 1, 9, 1024)
         chunks = [(w.context, w.H_context)] + [(w.tokens[:, t:t + 1], w.H[:, t:t + 1]) for t in range(3)]
         for ci, (tok, Hn) in enumerate(chunks):
             H = eg.to_device(Hn, "bf16", DEV)
             alpha, y = eg.forward(torch.from_numpy(np.ascontiguousarray(tok)).to(DEV), H, L, state=st,
                                   want_alpha=True, want_y=True)
-            ref = orc.forward(tok[sample], Hn[sample], lay, "bf16", state=ost, gemm="mxfp8" if mx else "exact")
+            ref = orc.forward(tok, Hn, lay, "bf16", state=ost, gemm="mxfp8" if mx else "exact")
             ost = ref["state"]
-            check_bf16_layer(to_f64(alpha[sample]), ref["alpha"], to_f64(y[sample]), ref["Y"], to_f64(H[sample]),
-                             orc.bf16_to_f64(Hn[sample]), tag=f"layer{li} chunk{ci}")
-        assert np.array_equal(st.ids.cpu().numpy()[sample], ost["ids"])
+            check_bf16_layer(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.bf16_to_f64(Hn),
+                             tag=f"layer{li} chunk{ci}")
+        assert np.array_equal(st.ids.cpu().numpy(), ost["ids"])
         assert np.all(st.pos.cpu().numpy() == 16 + 3)
+        conv = st.conv.cpu().numpy().astype(np.float64)           # [S, 1, 9, d], position p in slot p % 9
+        pos = 16 + 3
+        chrono = np.stack([conv[:, :, (pos - 9 + i) % 9] for i in range(9)], axis=2)
+        assert np.max(np.abs(chrono - ost["u"])) <= 1e-2 * np.max(np.abs(ost["u"]))
 
 
 def test_host_table_full_size_with_cache():
@@ -107,7 +114,7 @@ def test_host_table_full_size_with_cache():
     HBM cache of 10 % of the rows admitted from a 2^22-token warm-up (exact
     LFU ranking checked against the oracle), and a B = 4, T = 4096 forward
     that equals the HBM-table forward bit for bit and matches the oracle on
-    sampled windows."""
+    every token."""
     log("host table full size: inputs")
     w = inputs.make_config(4, layers=1)
     lay = w.layers[0]
@@ -127,25 +134,16 @@ def test_host_table_full_size_with_cache():
         L.set_cache(slot, rows)
         tok = torch.from_numpy(w.tokens).to(DEV)
         H0 = eg.to_device(w.H, "bf16", DEV)
-        H = H0.clone()
-        log("host table full size: forward")
-        alpha, y = eg.forward(tok, H, L, want_alpha=True, want_y=True)
-        L_dev = eg.Layer(lay, "bf16", DEV)
         H2 = H0.clone()
+        L_dev = eg.Layer(lay, "bf16", DEV)
         eg.forward(tok, H2, L_dev)
+        log("host table full size: forward through the cache, every token against the oracle")
+        run_and_check(w, lay, L, "c4")
+        H = H0.clone()
+        eg.forward(tok, H, L)
         torch.cuda.synchronize()
         assert torch.equal(H.view(torch.int16), H2.view(torch.int16))
         del L_dev
-        starts, rows_b = [0, 1500, 4096 - 64], [0, 3]
-        a_g = np.zeros((4, 4096, 1))
-        y_g = np.zeros((4, 4096, 1, 1024))
-        h_g = np.zeros((4, 4096, 1, 1024))
-        for b in rows_b:
-            for s in starts:
-                a_g[b, s:s + 64] = to_f64(alpha[b, s:s + 64])
-                y_g[b, s:s + 64] = to_f64(y[b, s:s + 64])
-                h_g[b, s:s + 64] = to_f64(H[b, s:s + 64])
-        check_windows(w, lay, a_g, y_g, h_g, starts, rows_b, tag="c4")
     finally:
         torch.cuda.synchronize()
         hb.free()

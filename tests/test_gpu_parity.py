@@ -343,30 +343,17 @@ def test_decode_steps_match_oracle(config):
     assert np.max(np.abs(chrono - ost["u"])) <= tol * np.max(np.abs(ost["u"]))
 
 
-def test_forward_full_size_single_branch_sampled():
-    """T = 4096 single-branch bf16 with the full 10.3M-row tables, in the
-    launch configuration the benchmark times; the oracle recomputes sampled
-    windows (with an 11-position halo) and compares them element by element;
-    the hash indices are compared on the whole sequence."""
-    log("forward full-size single-branch: building inputs")
+def test_hash_indices_full_size_single_branch():
+    """T = 4096 tokens hashed into the full 10.3M-row tables: every index
+    equals the oracle's (the layer forward at this size is compared on every
+    token in test_gpu_fullsize.py)."""
+    log("hash indices full-size single-branch")
     w = inputs.make_config(1)
     lay = w.layers[0]
     L = eg.Layer(lay, "bf16", DEV)
-    H = dev_H(w)
-    tok = dev_tokens(w)
-    z_gpu = eg.hash_indices(tok, L).cpu().numpy()
+    z_gpu = eg.hash_indices(dev_tokens(w), L).cpu().numpy()
     hp = lay.hash
     assert np.array_equal(z_gpu, orc.hash_indices(w.tokens, hp.proj, hp.mult, hp.prime, 3, hp.heads))
-    log("forward full-size single-branch: running")
-    alpha, y = eg.forward(tok, H, L, want_alpha=True, want_y=True)
-    a_g, y_g, h_g = to_f64(alpha), to_f64(y), to_f64(H)
-    h_in = orc.storage_to_f64(w.H, "bf16")
-    for s in (0, 5, 1000, 2047, 3333, 4096 - 64):
-        lo = max(0, s - 11)
-        ref = orc.forward(w.tokens[:, lo:s + 64], w.H[:, lo:s + 64], lay, "bf16")
-        k = s - lo
-        check_bf16_layer(a_g[:, s:s + 64], ref["alpha"][:, k:], y_g[:, s:s + 64], ref["Y"][:, k:],
-                         h_g[:, s:s + 64], h_in[:, s:s + 64], tag=f"window{s}")
 
 
 def test_graph_replays_match_eager():
