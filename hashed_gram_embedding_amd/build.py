@@ -3,7 +3,10 @@
     python -m hashed_gram_embedding_amd.build
 
 Compiles every source under csrc/ with hipcc for gfx950 only and links them
-into hashed_gram_embedding_amd/libengram.so.  Packed-FP32 instructions are
+into hashed_gram_embedding_amd/libengram.so, and a second time with
+ENGRAM_DEBUG_CHECKS defined into libengram_debug.so (the kernels check the
+device-resident preconditions into the caller's error word; see
+engram_debug_checks in include/engram.h).  Packed-FP32 instructions are
 disabled in device code (-packed-fp32-ops); hipcc's host pass warns that it
 does not know that feature, which is harmless.
 """
@@ -20,6 +23,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libengram.so")
+LIB_DEBUG = os.path.join(PKG, "libengram_debug.so")
 ARCH = "gfx950"
 
 
@@ -41,9 +45,9 @@ def common_flags():
             "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", src, "-o", obj]
+def _compile(src: str, out_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + common_flags() + list(extra) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = (r.stdout + r.stderr).strip()
     noise = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
@@ -55,19 +59,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """Builds libengram.so and libengram_debug.so; returns the release path."""
+    debug_dir = os.path.join(BUILD, "debug")
+    os.makedirs(debug_dir, exist_ok=True)
+    srcs = sources()
+    jobs = [(src, BUILD, ()) for src in srcs] + [(src, debug_dir, ("-DENGRAM_DEBUG_CHECKS",)) for src in srcs]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], LIB_DEBUG)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {LIB_DEBUG}")
     return LIB
 
 

@@ -3,6 +3,7 @@
 // here touches device data or synchronises, except engram_host_alloc/free.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -18,6 +19,10 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Debug build: the caller's device error word (engram_debug_set_error_word),
+// passed to every kernel launched after it is set.
+std::atomic<uint32_t*> g_err_word{nullptr};
 
 engram_status fail(engram_status st, const char* fmt, ...) {
   char buf[512];
@@ -78,6 +83,7 @@ engram_status check_hash(const engram_hash_params* hp, engram::HashArgs* out) {
     out->n_tables = nt;
     out->max_n = hp->max_n;
     out->vocab = static_cast<int32_t>(hp->vocab);
+    out->err = g_err_word.load();
   }
   return ENGRAM_OK;
 }
@@ -116,7 +122,12 @@ engram_status check_tables(const engram_tables* tab, engram::TableArgs* out) {
   }
   if (out != nullptr) {
     *out = engram::TableArgs{};
-    for (int j = 0; j < tab->n_tables; ++j) out->row_offset[j] = tab->row_offset[j];
+    for (int j = 0; j < tab->n_tables; ++j) {
+      out->row_offset[j] = tab->row_offset[j];
+      out->n_rows[j] = static_cast<int32_t>(tab->n_rows[j]);
+    }
+    out->cache_n = tab->cache_slot != nullptr ? tab->cache_n : 0;
+    out->err = g_err_word.load();
     out->rows = tab->rows;
     out->scale = tab->row_scale;
     out->cache_slot = tab->cache_slot;
@@ -345,7 +356,8 @@ engram_status run_conv_commit(void* H, const void* v, int64_t v_stride, int vdty
   if (st != nullptr && !state_folded) {
     engram::StateArgs sa{tokens != nullptr ? st->ids : nullptr, st->conv, st->pos};
     prof_mark(s, "state_commit_kernel");
-    r = hip_status(engram::launch_state_commit(v, v_stride, vdtype, B, T, g, gamma, sa, tokens, proj, max_n, vocab, s),
+    r = hip_status(engram::launch_state_commit(v, v_stride, vdtype, B, T, g, gamma, sa, tokens, proj, max_n, vocab,
+                                                    g_err_word.load(), s),
                    "state commit launch");
   }
   prof_mark(s, nullptr);
@@ -593,6 +605,7 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
       pa.tokens = tokens;
       pa.proj = L->hash.proj;
       pa.vocab = static_cast<int32_t>(L->hash.vocab);
+      pa.err = g_err_word.load();
       pa.max_n = L->hash.max_n;
       pa.adv_T = static_cast<int32_t>(T);
       pa.adv_B = static_cast<int32_t>(B);
@@ -1008,6 +1021,31 @@ ENGRAM_API engram_status engram_hot_lookup(const int32_t* tokens, int64_t B, int
   if (tokens == nullptr || hot_row == nullptr) return fail(ENGRAM_EINVAL, "hot lookup: tokens and hot_row must be non-NULL");
   prof_begin();
   prof_mark(stream, "hot_lookup_kernel");
-  return hip_status(engram::launch_hot_lookup(tokens, B, T, hist, hp->proj, hp->max_n, ha.vocab, h, hot_row, stream),
+  return hip_status(engram::launch_hot_lookup(tokens, B, T, hist, hp->proj, hp->max_n, ha.vocab, h, hot_row,
+                                                 g_err_word.load(), stream),
                     "hot lookup launch");
+}
+
+ENGRAM_API int32_t engram_debug_checks(void) { return engram::kDebugChecks ? 1 : 0; }
+
+ENGRAM_API engram_status engram_debug_set_error_word(uint32_t* word) {
+  if (!engram::kDebugChecks)
+    return fail(ENGRAM_EUNSUPPORTED, "debug_set_error_word: this is the release build (use libengram_debug.so)");
+  if (!aligned(word, 4)) return fail(ENGRAM_EINVAL, "debug_set_error_word: word must be 4-byte aligned");
+  g_err_word.store(word);
+  return ENGRAM_OK;
+}
+
+ENGRAM_API engram_status engram_debug_read_errors(uint32_t* bits) {
+  if (!engram::kDebugChecks)
+    return fail(ENGRAM_EUNSUPPORTED, "debug_read_errors: this is the release build (use libengram_debug.so)");
+  if (bits == nullptr) return fail(ENGRAM_EINVAL, "debug_read_errors: bits is NULL");
+  *bits = 0;
+  uint32_t* word = g_err_word.load();
+  if (word == nullptr) return fail(ENGRAM_EINVAL, "debug_read_errors: no error word is set");
+  engram_status r = hip_status(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  if (r != ENGRAM_OK) return r;
+  if ((r = hip_status(hipMemcpy(bits, word, sizeof(uint32_t), hipMemcpyDeviceToHost), "hipMemcpy")) != ENGRAM_OK)
+    return r;
+  return hip_status(hipMemset(word, 0, sizeof(uint32_t)), "hipMemset");
 }

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "debug_checks.h"
 #include "engram.h"
 
 namespace engram {
@@ -19,11 +20,15 @@ struct HashArgs {
   int32_t n_tables;
   int32_t max_n;
   int32_t vocab;                                       // raw ids are clamped into [0, vocab)
+  uint32_t* err;                                       // debug build: the caller's error word, or null
 };
 
 
 struct TableArgs {
   int64_t row_offset[ENGRAM_MAX_TABLES];
+  int32_t n_rows[ENGRAM_MAX_TABLES];   // rows of table j (debug build: row indices are checked against it)
+  int64_t cache_n;                     // slots in the cache (debug build: slots are checked against it)
+  uint32_t* err;                       // debug build: the caller's error word, or null
   const void* rows;
   const float* scale;
   const int32_t* cache_slot;
@@ -101,7 +106,7 @@ hipError_t launch_hash_gather(const int32_t* tokens, int64_t B, int64_t T, const
 
 hipError_t launch_hot_lookup(const int32_t* tokens, int64_t B, int64_t T, const int32_t* hist,
                              const int32_t* proj, int max_n, int32_t vocab, const HotArgs& h, int32_t* out,
-                             hipStream_t s);
+                             uint32_t* err, hipStream_t s);
 
 // Host build of one order's minimal perfect hash (pilots, and 8 int32 per
 // slot: ids newest first, row, padding).  a, b name the n-grams behind a
@@ -142,6 +147,7 @@ struct ProjGateArgs {
   const int32_t* tokens;  // [adv_B][adv_T] raw ids
   const int32_t* proj;    // P
   int32_t vocab;          // raw ids are clamped into [0, vocab)
+  uint32_t* err;          // debug build: the caller's error word, or null
   int32_t max_n;
   int32_t adv_T;
   int32_t adv_B;
@@ -212,7 +218,7 @@ hipError_t launch_conv_gather(const ConvArgs& a, int vdtype, const GatherJob& gj
 hipError_t launch_state_commit(const void* v, int64_t v_stride, int vdtype, int64_t B, int64_t T,
                                const GateConvArgs& g, const float* gamma, const StateArgs& st,
                                const int32_t* tokens, const int32_t* proj, int32_t max_n, int32_t vocab,
-                               hipStream_t s);
+                               uint32_t* err, hipStream_t s);
 
 size_t cache_build_workspace(int64_t total_rows);
 size_t cache_update_workspace(int64_t total_rows, int64_t cache_n);

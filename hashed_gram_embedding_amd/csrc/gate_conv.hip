@@ -571,7 +571,7 @@ template <int VT>
 __global__ void __launch_bounds__(256)
 state_commit_kernel(const void* __restrict__ v, int64_t v_stride, int64_t T, GateConvArgs g,
                     const float* __restrict__ gamma, StateArgs st, const int32_t* __restrict__ tokens,
-                    const int32_t* __restrict__ proj, int32_t max_n, int32_t vocab) {
+                    const int32_t* __restrict__ proj, int32_t max_n, int32_t vocab, uint32_t* err) {
   const int64_t b = blockIdx.x;
   const int M = g.branches;
   const int d = g.d;
@@ -603,7 +603,7 @@ state_commit_kernel(const void* __restrict__ v, int64_t v_stride, int64_t T, Gat
     for (int i = 0; i < ENGRAM_MAX_ORDER - 1; ++i) {
       if (i < hl) {
         const int64_t idx = T + i;  // index in (old ids ++ chunk ids)
-        next[i] = idx < hl ? st.ids[b * hl + idx] : proj[token_in_vocab(tokens[b * T + idx - hl], vocab)];
+        next[i] = idx < hl ? st.ids[b * hl + idx] : proj[token_in_vocab(tokens[b * T + idx - hl], vocab, err)];
       }
     }
 #pragma unroll
@@ -764,14 +764,14 @@ hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s) {
 hipError_t launch_state_commit(const void* v, int64_t v_stride, int vdtype, int64_t B, int64_t T,
                                const GateConvArgs& g, const float* gamma, const StateArgs& st,
                                const int32_t* tokens, const int32_t* proj, int32_t max_n, int32_t vocab,
-                               hipStream_t s) {
+                               uint32_t* err, hipStream_t s) {
   if (B == 0 || T == 0) return hipSuccess;
   if (vdtype == ENGRAM_BF16)
     launch_k(state_commit_kernel<ENGRAM_BF16>, dim3(static_cast<unsigned>(B)), dim3(256), 0, s,
-                       v, v_stride, T, g, gamma, st, tokens, proj, max_n, vocab);
+                       v, v_stride, T, g, gamma, st, tokens, proj, max_n, vocab, err);
   else
     launch_k(state_commit_kernel<ENGRAM_F32>, dim3(static_cast<unsigned>(B)), dim3(256), 0, s,
-                       v, v_stride, T, g, gamma, st, tokens, proj, max_n, vocab);
+                       v, v_stride, T, g, gamma, st, tokens, proj, max_n, vocab, err);
   return hipGetLastError();
 }
 

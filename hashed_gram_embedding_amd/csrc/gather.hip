@@ -45,12 +45,22 @@ gather_kernel(const int32_t* __restrict__ z, int64_t n_tok, TableArgs ta, void* 
   const int64_t tj = gid / chunks;
   const int j = static_cast<int>(tj % nt);
   const int64_t row_offset = ta.row_offset[j];
-  int64_t row = row_offset + z[tj];
+  int64_t zj = z[tj];
+  if constexpr (kDebugChecks) {
+    debug_record(ta.err, range_bit(zj, ta.n_rows[j], kErrRow));
+    zj = clamp_index(zj, ta.n_rows[j]);
+  }
+  int64_t row = row_offset + zj;
   const void* src = ta.rows;
   const float* scale = ta.scale;
   if (ta.counts != nullptr && c == 0) atomicAdd(ta.counts + row, 1u);   // access statistics (real-time LFU)
   if (ta.cache_slot != nullptr) {
-    const int32_t slot = ta.cache_slot[row];
+    int32_t slot = ta.cache_slot[row];
+    if constexpr (kDebugChecks) {
+      uint32_t bits = 0;
+      slot = checked_slot(slot, ta.cache_n, &bits);
+      debug_record(ta.err, bits);
+    }
     if (slot >= 0) {
       src = ta.cache_rows;
       scale = ta.cache_scale;

@@ -132,7 +132,7 @@ __device__ __forceinline__ void hashed_gather_body(uint32_t gid, uint32_t n_tok,
   for (int q = 0; q < ITEMS; ++q)
 #pragma unroll
     for (int i = 0; i < ENGRAM_MAX_ORDER; ++i)
-      x[q][i] = static_cast<uint32_t>(hs.proj[token_in_vocab(tk[q][i], hs.a.vocab)]);
+      x[q][i] = static_cast<uint32_t>(hs.proj[token_in_vocab(tk[q][i], hs.a.vocab, hs.a.err)]);
 #pragma unroll
   for (int q = 0; q < ITEMS; ++q) {
     if (t[q] < static_cast<uint32_t>(hist_len)) {
@@ -148,7 +148,11 @@ __device__ __forceinline__ void hashed_gather_body(uint32_t gid, uint32_t n_tok,
   // Step 3: cold row of every item
   int64_t crow[ITEMS];
 #pragma unroll
-  for (int q = 0; q < ITEMS; ++q) crow[q] = row_offset + hash_of_ids(x[q], th);
+  for (int q = 0; q < ITEMS; ++q) {
+    const int32_t z = hash_of_ids(x[q], th);
+    if constexpr (kDebugChecks) debug_record(hs.a.err, range_bit(z, th.prime, kErrRow));   // z < p by construction
+    crow[q] = row_offset + z;
+  }
 
   // Engram-Nine: hot row of every item (-1 = cold)
   int32_t hot[ITEMS];
@@ -183,6 +187,12 @@ __device__ __forceinline__ void hashed_gather_body(uint32_t gid, uint32_t n_tok,
         for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) xm[i] = i < n ? x[q][i] : 0u;
         const bool match = sa[q].x == xm[0] && sa[q].y == xm[1] && sa[q].z == xm[2] && sa[q].w == xm[3];
         hot[q] = match ? static_cast<int32_t>(sb[q].x) : -1;
+        if constexpr (kDebugChecks) {
+          if (hot[q] >= 0 && !in_range(hot[q], static_cast<int64_t>(o.n_hot))) {
+            debug_record(hs.a.err, kErrHotRow);
+            hot[q] = -1;   // read as cold
+          }
+        }
       }
     }
   }
@@ -198,6 +208,12 @@ __device__ __forceinline__ void hashed_gather_body(uint32_t gid, uint32_t n_tok,
   if (ta.cache_slot != nullptr) {
 #pragma unroll
     for (int q = 0; q < ITEMS; ++q) slot[q] = ta.cache_slot[crow[q]];
+    if constexpr (kDebugChecks) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int q = 0; q < ITEMS; ++q) slot[q] = checked_slot(slot[q], ta.cache_n, &bits);
+      debug_record(ta.err, bits);
+    }
   }
 #pragma unroll
   for (int q = 0; q < ITEMS; ++q) {

@@ -22,15 +22,20 @@ __device__ __forceinline__ uint32_t mod_prime(uint64_t x, uint32_t p, uint64_t i
 
 // Raw token ids are the caller's contract (0 <= id < vocab); an id outside
 // that range is clamped into it, so that P is never read out of bounds (the
-// result for such a token is then that of the clamped id).
-__device__ __forceinline__ int32_t token_in_vocab(int32_t tk, int32_t vocab) { return min(max(tk, 0), vocab - 1); }
+// result for such a token is then that of the clamped id), and the debug
+// build reports it in the error word.
+__device__ __forceinline__ int32_t token_in_vocab(int32_t tk, int32_t vocab, uint32_t* err) {
+  debug_record(err, range_bit(tk, vocab, kErrToken));
+  return min(max(tk, 0), vocab - 1);
+}
 
 // Compressed ids of the suffix window at position t of sequence b, newest
 // first: x[i] = x'_{t-i} for i < ENGRAM_MAX_ORDER.  Positions before the
 // sequence start read the history (oldest first) or the pad id 0.
 __device__ __forceinline__ void window_ids(const int32_t* __restrict__ tokens, const int32_t* __restrict__ proj,
-                                           const int32_t* __restrict__ hist, int max_n, int32_t vocab, int64_t b,
-                                           int64_t t, int64_t T, uint32_t (&x)[ENGRAM_MAX_ORDER]) {
+                                           const int32_t* __restrict__ hist, int max_n, int32_t vocab,
+                                           uint32_t* err, int64_t b, int64_t t, int64_t T,
+                                           uint32_t (&x)[ENGRAM_MAX_ORDER]) {
   const int hist_len = max_n - 1;
   // Unrolled to the largest order, with clamped (always valid) positions, so
   // that the token loads of all positions and then their P lookups are each
@@ -43,7 +48,7 @@ __device__ __forceinline__ void window_ids(const int32_t* __restrict__ tokens, c
     tok[i] = tokens[b * T + (p >= 0 ? p : 0)];
   }
 #pragma unroll
-  for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) x[i] = static_cast<uint32_t>(proj[token_in_vocab(tok[i], vocab)]);
+  for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) x[i] = static_cast<uint32_t>(proj[token_in_vocab(tok[i], vocab, err)]);
   if (t < hist_len) {
 #pragma unroll
     for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) {
@@ -90,7 +95,7 @@ __device__ __forceinline__ int32_t hash_index(const int32_t* __restrict__ tokens
                                               int j, int64_t b, int64_t t, int64_t T) {
   const TableHash th = table_hash(a, j);
   uint32_t x[ENGRAM_MAX_ORDER];
-  window_ids(tokens, proj, hist, a.max_n, a.vocab, b, t, T, x);
+  window_ids(tokens, proj, hist, a.max_n, a.vocab, a.err, b, t, T, x);
   return hash_of_ids(x, th);
 }
 

@@ -108,7 +108,7 @@ __device__ __forceinline__ uint4 global_load16(const void* p) {
 
 // Hot row of the n-gram whose ids are x (newest first), or -1.
 __device__ __forceinline__ int32_t hot_find(const uint32_t (&x)[ENGRAM_MAX_ORDER], int n,
-                                            const HotOrderArgs& o) {
+                                            const HotOrderArgs& o, uint32_t* err = nullptr) {
   if (o.n_hot == 0) return -1;
   const uint64_t h = hot_key_hash(x, n, o.seed);
   const uint32_t pilot = global_load(o.pilots + hot_range(h, o.n_buckets));
@@ -120,7 +120,14 @@ __device__ __forceinline__ int32_t hot_find(const uint32_t (&x)[ENGRAM_MAX_ORDER
   for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) xm[i] = i < n ? x[i] : 0u;
   static_assert(ENGRAM_MAX_ORDER == 4, "a slot holds four ids");
   const bool match = a.x == xm[0] && a.y == xm[1] && a.z == xm[2] && a.w == xm[3];
-  return match ? static_cast<int32_t>(b.x) : -1;
+  const int32_t row = match ? static_cast<int32_t>(b.x) : -1;
+  if constexpr (kDebugChecks) {
+    if (row >= 0 && !in_range(row, static_cast<int64_t>(o.n_hot))) {
+      debug_record(err, kErrHotRow);
+      return -1;
+    }
+  }
+  return row;
 }
 
 }  // namespace engram

@@ -21,7 +21,8 @@ namespace {
 
 __global__ void __launch_bounds__(256)
 hot_lookup_kernel(const int32_t* __restrict__ tokens, int64_t B, int64_t T, const int32_t* __restrict__ hist,
-                  const int32_t* __restrict__ proj, int max_n, int32_t vocab, HotArgs h, int32_t* __restrict__ out) {
+                  const int32_t* __restrict__ proj, int max_n, int32_t vocab, HotArgs h, int32_t* __restrict__ out,
+                  uint32_t* err) {
   const int no = max_n - 1;
   const int64_t total = B * T * no;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -30,21 +31,21 @@ hot_lookup_kernel(const int32_t* __restrict__ tokens, int64_t B, int64_t T, cons
   const int64_t bt = gid / no;
   const int64_t b = bt / T;
   uint32_t x[ENGRAM_MAX_ORDER];
-  window_ids(tokens, proj, hist, max_n, vocab, b, bt - b * T, T, x);
-  out[gid] = hot_find(x, o + 2, hot_order(h, o + 2));
+  window_ids(tokens, proj, hist, max_n, vocab, err, b, bt - b * T, T, x);
+  out[gid] = hot_find(x, o + 2, hot_order(h, o + 2), err);
 }
 
 }  // namespace
 
 hipError_t launch_hot_lookup(const int32_t* tokens, int64_t B, int64_t T, const int32_t* hist,
                              const int32_t* proj, int max_n, int32_t vocab, const HotArgs& h, int32_t* out,
-                             hipStream_t s) {
+                             uint32_t* err, hipStream_t s) {
   const int64_t total = B * T * (max_n - 1);
   if (total == 0) return hipSuccess;
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
   launch_k(hot_lookup_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, s, tokens, B, T, hist, proj,
-           max_n, vocab, h, out);
+           max_n, vocab, h, out, err);
   return hipGetLastError();
 }
 

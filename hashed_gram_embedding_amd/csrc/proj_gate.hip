@@ -66,7 +66,8 @@ __device__ __forceinline__ void advance_state(const ProjGateArgs& a) {
       if (i < hl) {
         const int64_t idx = static_cast<int64_t>(a.adv_T) + i;   // index in (old ids ++ chunk ids)
         next[i] = idx < hl ? a.st_ids[static_cast<int64_t>(b) * hl + idx]
-                           : a.proj[token_in_vocab(a.tokens[static_cast<int64_t>(b) * a.adv_T + idx - hl], a.vocab)];
+                           : a.proj[token_in_vocab(a.tokens[static_cast<int64_t>(b) * a.adv_T + idx - hl], a.vocab,
+                                                   a.err)];
       }
     }
 #pragma unroll

@@ -15,7 +15,10 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libengram.so")
+# ENGRAM_DEBUG_CHECKS=1 in the environment loads the debug build instead
+# (device-resident preconditions checked into an error word).
+LIB_PATH = os.path.join(_HERE, "libengram_debug.so" if os.environ.get("ENGRAM_DEBUG_CHECKS") == "1"
+                        else "libengram.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
 F32, BF16, I8 = 0, 1, 2
@@ -76,11 +79,17 @@ class EngramError(RuntimeError):
 def lib():
     """Load libengram.so (raises if it has not been built)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m hashed_gram_embedding_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """A build of the library (release or debug) with every entry point's
+    signature set; raises if it has not been built."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m hashed_gram_embedding_amd.build`")
+    L = ctypes.CDLL(path)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     sig = {
         "engram_abi_version": (i32, []),
@@ -119,13 +128,15 @@ def lib():
         "engram_profile_read": (i32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), i32,
                                       ctypes.POINTER(i32)]),
         "engram_host_alloc": (i32, [sz, ctypes.POINTER(vp), ctypes.POINTER(vp)]),
+        "engram_debug_checks": (i32, []),
+        "engram_debug_set_error_word": (i32, [vp]),
+        "engram_debug_read_errors": (i32, [ctypes.POINTER(ctypes.c_uint32)]),
         "engram_host_free": (i32, [vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = L
     return L
 
 
@@ -137,7 +148,8 @@ def exported_names():
             "engram_cache_update_workspace", "engram_cache_update", "engram_quantize_mxfp8",
             "engram_hot_buckets", "engram_hot_build", "engram_hot_lookup", "engram_forward_retrieved_prefetch",
             "engram_profile_enable", "engram_profile_read",
-            "engram_host_alloc", "engram_host_free"]
+            "engram_host_alloc", "engram_host_free", "engram_debug_checks", "engram_debug_set_error_word",
+            "engram_debug_read_errors"]
 
 
 def last_error() -> str:
@@ -563,3 +575,24 @@ def forward_retrieved_prefetch(tokens: torch.Tensor, e: torch.Tensor, H: torch.T
                                                    _ptr(alpha), _ptr(y), _ptr(ws), ws.numel(), nl, nst,
                                                    _ptr(next_tokens), nB, nT, _ptr(next_e), _stream(stream)))
     return alpha, y
+
+
+ERR_TOKEN, ERR_ROW, ERR_SLOT, ERR_HOT_ROW = 1, 2, 4, 8
+
+
+def debug_checks() -> bool:
+    """True when the loaded library is the debug build."""
+    return bool(lib().engram_debug_checks())
+
+
+def debug_set_error_word(word: Optional[torch.Tensor]):
+    """Debug build: kernels OR their precondition violations into `word` (a
+    zeroed int32 device tensor of one element); None stops recording."""
+    _check(lib().engram_debug_set_error_word(_ptr(word)))
+
+
+def debug_read_errors() -> int:
+    """Debug build: the error word's bits (ERR_*), cleared afterwards."""
+    bits = ctypes.c_uint32(0)
+    _check(lib().engram_debug_read_errors(ctypes.byref(bits)))
+    return int(bits.value)

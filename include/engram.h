@@ -31,7 +31,8 @@
  *    launch; on failure nothing is launched and a message is kept for
  *    engram_last_error() (per calling thread).  Device-resident values are
  *    the caller's contract: 0 <= token < vocab, 0 <= z < n_rows[j],
- *    cache slots < cache_n.
+ *    -1 <= cache slots < cache_n (the debug build checks them; see
+ *    engram_debug_checks).
  *  - Status codes: ENGRAM_OK, ENGRAM_EINVAL (null or misaligned pointer, bad
  *    size, inconsistent descriptors, workspace too small),
  *    ENGRAM_EUNSUPPORTED (dtype combination or shape outside the supported
@@ -415,6 +416,33 @@ engram_status engram_hot_lookup(const int32_t* tokens, int64_t B, int64_t T, con
  * the stage count in *n_stages.  engram_profile_enable(0) stops recording. */
 engram_status engram_profile_enable(int32_t on);
 engram_status engram_profile_read(float* ms, const char** names, int32_t cap, int32_t* n_stages);
+
+/* Debug build (libengram_debug.so, compiled with ENGRAM_DEBUG_CHECKS): the
+ * device-resident preconditions of the conventions above are checked by the
+ * kernels before the load that uses each value.  A raw token id outside
+ * [0, vocab), a row index outside [0, rows of its table) (engram_gather's z;
+ * hashed indices are in range by construction and are checked too), a cache
+ * slot outside [-1, cache_n) or a hot-tier row outside [0, n_hot) sets its
+ * bit in the error word and is replaced by an in-range value (a token or
+ * index clamped into its range, a bad slot or hot row read as a miss), so
+ * that no access leaves its buffer.  Raw token ids are clamped into the
+ * vocabulary in the release build too, without the report.
+ *
+ * engram_debug_checks: 1 in the debug build, 0 in the release build.
+ * engram_debug_set_error_word: word is a device uint32, 4-byte aligned, that
+ * later calls (from any thread) OR their violation bits into with one global
+ * atomic each; NULL stops recording.  The caller zeroes it first and keeps it
+ * allocated while kernels may write it.  EUNSUPPORTED in the release build.
+ * engram_debug_read_errors: waits for the device, returns the word's bits and
+ * clears it (synchronous).  EINVAL when no word is set; EUNSUPPORTED in the
+ * release build. */
+#define ENGRAM_ERR_TOKEN 1u    /* raw token id outside [0, vocab)             */
+#define ENGRAM_ERR_ROW 2u      /* row index outside its table                 */
+#define ENGRAM_ERR_SLOT 4u     /* cache slot outside [-1, cache_n)            */
+#define ENGRAM_ERR_HOT_ROW 8u  /* hot-tier row outside [0, n_hot)             */
+int32_t engram_debug_checks(void);
+engram_status engram_debug_set_error_word(uint32_t* word);
+engram_status engram_debug_read_errors(uint32_t* bits);
 
 /* Pinned host memory that kernels read directly over PCIe (tables kept in
  * host DRAM; the DRAM-offload study reads them through unified addressing).
