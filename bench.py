@@ -45,6 +45,8 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_PCIE_GBPS = 64.0        # PCIe Gen5 x16, one direction (host-resident table rows)
 
 WARMUP_FLOOR_MS = 100.0   # least untimed warm-up before the timed steps
+PROFILE_CHUNK_STEPS = 10  # steps launched back to back between reads of the kernel events (a graph's length)
+QUEUE_AHEAD_MS = 2.0      # spin ahead of each such run, while the host queues its launches
 ROTATION_BYTES = 512 << 20   # table rows a rotation of batches touches: twice the Infinity Cache
 CPU_HALO = 11                # positions before a token that its layer output depends on: (N-1) + (w-1)*N
 
@@ -758,6 +760,26 @@ def measured_peaks(torch, shape=None):
     return out
 
 
+
+_SPIN = {}
+
+
+def queue_ahead(torch, ms):
+    """Puts a spin kernel of about `ms` milliseconds on the current stream,
+    so that the host has queued the launches that follow before the GPU
+    reaches them: they then run back to back, as in a graph replay, instead
+    of waiting on host launch overhead."""
+    if "cycles_per_ms" not in _SPIN:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(1 << 22)
+        b.record()
+        b.synchronize()
+        _SPIN["cycles_per_ms"] = (1 << 22) / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(ms * _SPIN["cycles_per_ms"]))
+
+
 def time_case(torch, eg, case, steps, warmup, eager=False, per_graph=10):
     """Times `steps` steps of the case (HIP graphs of per_graph consecutive
     steps, one graph per stretch of the rotation, replayed in rotation
@@ -826,16 +848,27 @@ def time_case(torch, eg, case, steps, warmup, eager=False, per_graph=10):
     eager_ms = t0.elapsed_time(t1) / n_eager
 
     # per-kernel durations: events recorded by each kernel's own dispatch
-    # (the library's stage timing), eager steps over the same rotation
-    eg.profile_enable(True)
+    # (the library's stage timing), eager steps over the same rotation run
+    # back to back and read every `chunk` steps; the first step of a chunk
+    # starts on an idle GPU and is left out
+    eg.profile_enable(2)
+    step(0)
+    per_call = len(eg.profile_read())           # stages of one step
+    chunk = max(2, min(PROFILE_CHUNK_STEPS, eg.PROFILE_MAX_STAGES // max(per_call, 1)))
     samples = {}
-    for i in range(n_eager):
-        for c in case.calls(i):
-            c()
-            for name, t in eg.profile_read():
-                samples.setdefault(name, []).append(t)
+    n_timed = 0
+    i = 0
+    while n_timed < n_eager:
+        queue_ahead(torch, QUEUE_AHEAD_MS)
+        for s in range(chunk):
+            step(i + s)
+        for name, t in eg.profile_read()[per_call:]:
+            samples.setdefault(name, []).append(t)
+        n_timed += chunk - 1
+        i += chunk
     eg.profile_enable(False)
-    per_step = {k: len(v) / n_eager for k, v in samples.items()}   # launches of each kernel per step
+    n_eager_timed = n_timed
+    per_step = {k: len(v) / n_eager_timed for k, v in samples.items()}   # launches of each kernel per step
     kernel_ms = {k: sum(v) / len(v) for k, v in samples.items()}
 
     def pcts(v):
@@ -880,8 +913,10 @@ def kernel_block(t, rates, case):
     return {"kernel_ms": {k: round(v, 5) for k, v in t["kernel_ms"].items()},
             "kernel_us_p10_p50_p90": t["kernel_us_p10_p50_p90"],
             "kernel_rate": {k: round(v, 2) for k, v in rates.items()},
-            "kernel_timing": {"how": "events recorded by each kernel's own dispatch, eager steps over the same "
-                                     "rotation of batches",
+            "kernel_timing": {"how": "events recorded by each kernel's own dispatch over eager steps of the same "
+                                     f"rotation, queued behind a {QUEUE_AHEAD_MS:g} ms spin kernel so that they run back to "
+                                     f"back, read every {PROFILE_CHUNK_STEPS} steps (the first step after each read "
+                                     "left out)",
                               "sum_of_kernels_ms_per_step": round(ks, 5),
                               "graph_step_minus_kernel_sum_ms": round(t["ms_per_step"] - ks, 5),
                               "eager_ms_per_step": round(t["eager_ms_per_step"], 5)}}
@@ -1115,7 +1150,7 @@ def main(argv=None):
 
 def control_report(torch, eg, inputs, w, lay, pipe, units, steps=20):
     """Three controls of the measured kernel rates.
-    one batch: the rotation's first batch replayed, so that its rows stay in
+    one batch: the rotation's first batch called back to back, so that its rows stay in
     the on-chip caches (what a benchmark that reuses one batch measures).
     cold: before every eager layer call a 512 MiB buffer is overwritten (more
     than the 256 MB Infinity Cache), so tables, W and e start outside the
@@ -1126,13 +1161,24 @@ def control_report(torch, eg, inputs, w, lay, pipe, units, steps=20):
     L = Ls[0]
     ws = torch.empty(eg.forward_workspace(w.B, w.T, L), dtype=torch.uint8, device="cuda")
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    eg.profile_enable(True)
-    one = {}
-    for it in range(3 + steps):
-        eg.forward(tok, H, L, ws=ws)
+
+    def back_to_back(call):
+        """Stage durations of `steps` back-to-back calls after 3 untimed ones."""
+        eg.profile_enable(2)
+        for _ in range(3):
+            call()
+        eg.profile_read()
+        queue_ahead(torch, QUEUE_AHEAD_MS)
+        for _ in range(steps):
+            call()
+        got = {}
         for name, t in eg.profile_read():
-            if it >= 3:
-                one.setdefault(name, []).append(t)
+            got.setdefault(name, []).append(t)
+        eg.profile_enable(False)
+        return got
+
+    one = back_to_back(lambda: eg.forward(tok, H, L, ws=ws))
+    eg.profile_enable(True)
     cold = {}
     for it in range(3 + steps):
         flush.fill_(it & 0xff)
@@ -1143,13 +1189,8 @@ def control_report(torch, eg, inputs, w, lay, pipe, units, steps=20):
     del flush
     utok = torch.from_numpy(inputs.uniform_control_tokens(w.config, w.B, w.T, lay.hash.vocab)).to("cuda")
     e = eg.rows_buffer(w.B, w.T, L, "cuda")
-    uni = []
-    for it in range(3 + steps):
-        eg.retrieve(utok, L, e)
-        for name, t in eg.profile_read():
-            if it >= 3:
-                uni.append(t)
     eg.profile_enable(False)
+    uni = [t for v in back_to_back(lambda: eg.retrieve(utok, L, e)).values() for t in v]
     cold_ms = {k: sum(v) / len(v) for k, v in cold.items()}
     one_ms = {k: sum(v) / len(v) for k, v in one.items()}
 
@@ -1164,9 +1205,10 @@ def control_report(torch, eg, inputs, w, lay, pipe, units, steps=20):
             "cold_rate": {k: rate(k, v) for k, v in cold_ms.items() if k in units},
             "uniform_tokens_gather_us": round(uni_ms * 1000, 2),
             "uniform_tokens_gather_GBps": rate(g_name, uni_ms),
-            "how": "one batch: the first batch of the rotation 20 times in a row (its rows stay in the caches); "
-                   "cold: a 512 MiB buffer overwritten before each of 20 eager layer calls; uniform: "
-                   "engram_retrieve over seeded uniform raw ids, 20 calls; rates are algorithmic units per second"}
+            "how": "one batch: the first batch of the rotation, 20 back-to-back calls (its rows stay in the "
+                   "caches); cold: a 512 MiB buffer overwritten before each of 20 eager layer calls; uniform: "
+                   "engram_retrieve over seeded uniform raw ids, 20 back-to-back calls; rates are algorithmic "
+                   "units per second"}
 
 
 

@@ -178,12 +178,17 @@ engram_status check_state(const engram_decode_state* st, bool need_ids) {
 }
 
 // ---- stage timing (per calling thread) ----
-constexpr int kMaxStages = 12;
+// Mode 1 keeps the stages of the last call (kCallStages); mode 2 keeps every
+// stage since the last read, up to kMaxStages (later ones are dropped and
+// counted).
+constexpr int kCallStages = 12;
+constexpr int kMaxStages = 2048;
 
 struct Profiler {
-  bool on = false;
-  bool created = false;
-  int n = 0;                        // stages recorded by the last profiled call
+  int mode = 0;                     // 0 off, 1 last call, 2 accumulate until read
+  int created = 0;                  // event pairs created
+  int n = 0;                        // stages recorded
+  int dropped = 0;                  // stages not recorded since the last read (no free event pair)
   const char* pending = nullptr;    // open stage: its kernel has not been launched yet
   hipEvent_t start[kMaxStages];
   hipEvent_t stop[kMaxStages];
@@ -195,14 +200,16 @@ thread_local Profiler g_prof;
 // Opens a stage; the next kernel launched on this thread records its events.
 void prof_mark(hipStream_t, const char* name) {
   Profiler& p = g_prof;
-  if (p.on) p.pending = name;
+  if (p.mode != 0) p.pending = name;
 }
 
 void prof_begin() {
-  if (g_prof.on) {
-    g_prof.n = 0;
-    g_prof.pending = nullptr;
+  Profiler& p = g_prof;
+  if (p.mode == 1) {
+    p.n = 0;
+    p.dropped = 0;
   }
+  p.pending = nullptr;
 }
 
 }  // namespace
@@ -210,7 +217,12 @@ void prof_begin() {
 namespace engram {
 bool prof_take(hipEvent_t* start, hipEvent_t* stop) {
   Profiler& p = g_prof;
-  if (!p.on || p.pending == nullptr || p.n >= kMaxStages) return false;
+  if (p.mode == 0 || p.pending == nullptr) return false;
+  if (p.n >= p.created) {
+    ++p.dropped;
+    p.pending = nullptr;
+    return false;
+  }
   *start = p.start[p.n];
   *stop = p.stop[p.n];
   p.names[p.n] = p.pending;
@@ -921,17 +933,17 @@ ENGRAM_API engram_status engram_quantize_mxfp8(const void* x, engram_dtype dtype
 }
 
 ENGRAM_API engram_status engram_profile_enable(int32_t on) {
+  if (on < 0 || on > 2) return fail(ENGRAM_EINVAL, "profile_enable: mode must be 0, 1 or 2");
   Profiler& p = g_prof;
-  if (on && !p.created) {
-    for (int i = 0; i < kMaxStages; ++i) {
-      hipError_t e = hipEventCreate(&p.start[i]);
-      if (e == hipSuccess) e = hipEventCreate(&p.stop[i]);
-      if (e != hipSuccess) return hip_status(e, "hipEventCreate");
-    }
-    p.created = true;
+  const int want = on == 2 ? kMaxStages : (on == 1 ? kCallStages : 0);
+  for (; p.created < want; ++p.created) {
+    hipError_t e = hipEventCreate(&p.start[p.created]);
+    if (e == hipSuccess) e = hipEventCreate(&p.stop[p.created]);
+    if (e != hipSuccess) return hip_status(e, "hipEventCreate");
   }
-  p.on = on != 0;
+  p.mode = on;
   p.n = 0;
+  p.dropped = 0;
   p.pending = nullptr;
   return ENGRAM_OK;
 }
@@ -941,7 +953,12 @@ ENGRAM_API engram_status engram_profile_read(float* ms, const char** names, int3
   if (n_stages == nullptr || (cap > 0 && ms == nullptr))
     return fail(ENGRAM_EINVAL, "profile_read: n_stages and ms must be non-NULL");
   *n_stages = 0;
-  if (!p.created || p.n < 1) return fail(ENGRAM_EINVAL, "profile_read: no profiled call recorded");
+  if (p.mode == 0 || p.n < 1) return fail(ENGRAM_EINVAL, "profile_read: no profiled call recorded");
+  if (p.dropped != 0) {
+    p.n = 0;
+    p.dropped = 0;
+    return fail(ENGRAM_EINVAL, "profile_read: more stages than the profiler holds since the last read");
+  }
   hipError_t e = hipEventSynchronize(p.stop[p.n - 1]);
   if (e != hipSuccess) return hip_status(e, "hipEventSynchronize");
   const int stages = p.n;
@@ -953,6 +970,7 @@ ENGRAM_API engram_status engram_profile_read(float* ms, const char** names, int3
     if (names != nullptr) names[i] = p.names[i];
   }
   *n_stages = stages;
+  if (p.mode == 2) p.n = 0;
   return ENGRAM_OK;
 }
 

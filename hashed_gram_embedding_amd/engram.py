@@ -449,13 +449,19 @@ def cache_update(layer: Layer, counts: torch.Tensor, decay_shift: int = 0, strea
                                      _stream(stream)))
 
 
-def profile_enable(on: bool = True):
-    _check(lib().engram_profile_enable(1 if on else 0))
+def profile_enable(on=True):
+    """on = True / 1: keep the stages of the last call; 2: accumulate the
+    stages of back-to-back calls until profile_read; False / 0: off."""
+    _check(lib().engram_profile_enable(int(on)))
+
+
+PROFILE_MAX_STAGES = 2048
 
 
 def profile_read():
-    """[(kernel name, ms)] of the stages of the last profiled forward call."""
-    cap = 16
+    """[(kernel name, ms)] of the recorded stages (mode 1: the last profiled
+    call; mode 2: every call since the previous read)."""
+    cap = PROFILE_MAX_STAGES
     ms = (ctypes.c_float * cap)()
     names = (ctypes.c_char_p * cap)()
     n = ctypes.c_int32()

@@ -405,15 +405,24 @@ engram_status engram_hot_lookup(const int32_t* tokens, int64_t B, int64_t T, con
                                 const engram_hash_params* hp, const engram_hot_tier* hot,
                                 int32_t* hot_row, hipStream_t stream);
 
-/* Stage timing, for benchmarks.  engram_profile_enable(1) makes later
- * engram_forward and engram_gate_conv_forward calls on the calling thread
- * time each kernel they launch: the start and stop events are recorded by
- * the kernel's own dispatch (hipExtLaunchKernel), so a stage is the kernel's
- * execution interval (events owned by the library, reused by each call).
- * engram_profile_read waits for the last event of the most recent profiled
- * call, writes up to `cap` stage durations in milliseconds to ms[] and their
- * kernel names to names[] (static strings; names may be NULL), and returns
- * the stage count in *n_stages.  engram_profile_enable(0) stops recording. */
+/* Stage timing, for benchmarks.  While profiling is on, calls of
+ * engram_forward (and engram_forward_noalloc), engram_retrieve,
+ * engram_forward_retrieved(_prefetch), engram_gate_conv_forward and
+ * engram_hot_lookup on the calling thread time each kernel they launch: the start and stop events are recorded by the kernel's own
+ * dispatch (hipExtLaunchKernel), so a stage is the kernel's execution
+ * interval (events owned by the library and reused).
+ *   on = 1: engram_profile_read returns the stages of the most recent call
+ *           (at most 12).
+ *   on = 2: stages accumulate over calls until engram_profile_read, which
+ *           returns all of them (at most 2048) and starts a new series, so
+ *           calls can run back to back without a host wait between them.
+ *           Stages beyond 2048 are not recorded; the read then fails with
+ *           ENGRAM_EINVAL and starts a new series.
+ *   on = 0: stops recording.
+ * engram_profile_read waits for the last recorded event, writes up to `cap`
+ * stage durations in milliseconds to ms[] and their kernel names to names[]
+ * (static strings; names may be NULL), and returns the stage count in
+ * *n_stages.  Other values of `on` return ENGRAM_EINVAL. */
 engram_status engram_profile_enable(int32_t on);
 engram_status engram_profile_read(float* ms, const char** names, int32_t cap, int32_t* n_stages);
 

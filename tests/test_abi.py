@@ -346,3 +346,18 @@ def test_forward_noalloc_rejects_calls_beyond_its_scratch():
         == eg.EINVAL
     text = open(HEADER).read()
     assert f"#define ENGRAM_NOALLOC_SCRATCH_BYTES (32u << 20)" in text and eg.NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
+def test_profile_modes_are_checked():
+    """engram_profile_enable accepts modes 0, 1 and 2 only; reading with
+    profiling off, or before any profiled call, is an error (no GPU work)."""
+    L = eg.lib()
+    st, msg = _status(L.engram_profile_enable, 3)
+    assert st == eg.EINVAL and "mode" in msg
+    assert L.engram_profile_enable(-1) == eg.EINVAL
+    assert L.engram_profile_enable(0) == eg.OK
+    ms = (ctypes.c_float * 4)()
+    n = ctypes.c_int32(7)
+    st, msg = _status(L.engram_profile_read, ms, None, 4, ctypes.byref(n))
+    assert st == eg.EINVAL and n.value == 0
+    assert L.engram_profile_read(ms, None, 4, None) == eg.EINVAL

@@ -239,6 +239,31 @@ def test_forward_bf16_kernel_switch(config, B, T):
         eg.profile_enable(False)
     assert "proj_gate_kernel" in names, names
 
+def test_profile_accumulates_back_to_back_calls():
+    """Mode 2 keeps the stages of several calls until one read, in launch
+    order; the next read starts a new series; mode 1 keeps the last call's."""
+    w = small(1, B=1, T=300)
+    lay = w.layers[0]
+    L = eg.Layer(lay, "bf16", DEV)
+    tok, H = dev_tokens(w), dev_H(w)
+    try:
+        eg.profile_enable(1)
+        eg.forward(tok, H, L)
+        one = [n for n, _ in eg.profile_read()]
+        eg.profile_enable(2)
+        for _ in range(3):
+            eg.forward(tok, H, L)
+        three = eg.profile_read()
+        eg.forward(tok, H, L)
+        again = eg.profile_read()
+    finally:
+        eg.profile_enable(False)
+    assert one == ["gather_kernel<hashed>", "proj_gate_kernel", "conv_kernel"], one
+    assert [n for n, _ in three] == one * 3
+    assert [n for n, _ in again] == one
+    assert all(t > 0 for _, t in three + again)
+
+
 # Narrow tables: d_mem = 16 x 8 = 128 or 16 x 32 = 512 (K of the projection).
 # The small-batch kernel's K range per wavefront is then 32 or 128 elements,
 # a partial or a whole number of its 64-element load batches; 1,100 tokens at
