@@ -326,8 +326,10 @@ KERNEL_SOURCES = {
                               ["gather.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
     "gather_kernel<hashed,hot>": (r"hashed_gather_kernel<[^>]*true, \d>",
                                   ["gather.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
-    "proj_gate_kernel": (r"proj_gate_kernel<", ["proj_gate.hip"]),
+    "proj_gate_kernel": (r"proj_gate(_small)?_kernel<", ["proj_gate.hip"]),
     "conv_kernel": (r"conv_(strip_)?kernel<", ["gate_conv.hip"]),
+    "conv_gather_kernel": (r"conv_gather_kernel<",
+                           ["gate_conv.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
 }
 COMMON_SOURCES = ["device_util.h", "engram_internal.h"]
 
@@ -389,13 +391,15 @@ def hbm_summary(fetch_csv, write_csv, workload, n_true):
     f_scale, w_scale = n_true / cf, n_true / cw
     rows = []
     for stage, (pat, _) in KERNEL_SOURCES.items():
-        fk = [v for k, v in fetch.items() if re.search(pat, k)]
-        wk = [v for k, v in write.items() if re.search(pat, k)]
-        if not fk or not wk:
+        # of the kernel's instantiations in the run, the one dispatched most
+        # often (the timed workload's, not e.g. a decode prefill's)
+        names = [k for k in fetch if re.search(pat, k) and k in write]
+        if not names:
             continue
-        fb = sum(fk[0]) / len(fk[0]) * f_scale
-        wb = sum(wk[0]) / len(wk[0]) * w_scale
-        rows.append((stage, int(round(fb)), int(round(wb)), len(fk[0])))
+        k = max(names, key=lambda n: len(fetch[n]))
+        fb = sum(fetch[k]) / len(fetch[k]) * f_scale
+        wb = sum(write[k]) / len(write[k]) * w_scale
+        rows.append((stage, int(round(fb)), int(round(wb)), len(fetch[k])))
     print(f"calibration: copy of {n_true / 2**20:.0f} MiB; FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}")
     for stage, fb, wb, n in rows:
         print(f"| {workload} | `{stage}` | {fb} | {wb} | {n} | {kernel_source_hash(stage)} |")
