@@ -394,6 +394,20 @@ def make_order4(B: int, T: int, *, heads: int = 4, dim: int = 32, d: int = 128, 
     return Workload("order-4-bf16", 5, BF16, B, T, tokens, H, lays)
 
 
+def make_shape(B: int, T: int, *, max_n: int = 3, heads: int = 8, dim: int = 64, d: int = 1024,
+               branches: int = 1, rows_per_table: int = 997, w_std: float = 1.0 / 32) -> Workload:
+    """A bf16 layer of any shape the library takes (n-gram orders 2..max_n,
+    `heads` tables of `dim` columns per order, hidden width d, `branches`
+    branches), for the tests at the library's limits: Zipf(1.1) tokens over
+    128,000 raw ids projected to 98,560, prime tables from rows_per_table up.
+    Seeds under configuration id 6."""
+    lay = _layer(6, 0, vocab=128_000, vocab_c=98_560, max_n=max_n, heads=heads, prime_start=rows_per_table,
+                 dim=dim, table_dtype=BF16, d=d, branches=branches, store_dtype=BF16, w_std=w_std)
+    tokens = zipf_tokens(rng_for(6, 0, S_TOKENS), 128_000, 1.1, (B, T))
+    H = _hidden(6, (B, T, branches, d), BF16)
+    return Workload("shape-bf16", 6, BF16, B, T, tokens, H, [lay])
+
+
 def hash_inputs_for(config: int, layer: int = 0) -> HashInputs:
     """Only the hash inputs of a configuration (no tables), for index tests."""
     if config == 0:
