@@ -66,6 +66,31 @@ def test_hbm_summary_scales_counters_by_the_calibration_copy(tmp_path, capsys):
     assert cells[4] == "2" and cells[5] == bench.kernel_source_hash("gather_kernel<hashed>")
 
 
+
+def test_hbm_summary_takes_the_most_dispatched_instantiation(tmp_path, capsys):
+    """A kernel with several instantiations in one run (a decode prefill and
+    its single-token steps; the small-batch and the large projection) is
+    summarised by the one dispatched most often."""
+    def write(path, rows):
+        with open(path, "w") as f:
+            f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+            for k, c, v in rows:
+                f.write(f'"{k}",{c},{v}\n')
+    n = 1 << 30
+    prefill = "void engram::(anonymous namespace)::proj_gate_kernel<128, false, 4, 3, true>(engram::ProjGateArgs)"
+    steps = "void engram::(anonymous namespace)::proj_gate_small_kernel<false>(engram::ProjGateArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    fetch = [(prefill, "FETCH_SIZE", 90000.0)] * 2 + [(steps, "FETCH_SIZE", 4000.0)] * 5 + \
+            [(copy, "FETCH_SIZE", n / 1024)]
+    write_ = [(prefill, "WRITE_SIZE", 70000.0)] * 2 + [(steps, "WRITE_SIZE", 1000.0)] * 5 + \
+             [(copy, "WRITE_SIZE", n / 1024)]
+    write(tmp_path / "f.csv", fetch)
+    write(tmp_path / "w.csv", write_)
+    bench.hbm_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "wl", n)
+    row = next(l for l in capsys.readouterr().out.splitlines() if "`proj_gate_kernel`" in l)
+    cells = [c.strip() for c in row.strip().strip("|").split("|")]
+    assert int(cells[2]) == 4000 * 1024 and int(cells[3]) == 1000 * 1024 and cells[4] == "5"
+
 def test_rotation_touches_twice_the_infinity_cache():
     """The timed rotation holds whole graphs of batches and enough batches that
     their table rows add up to 512 MiB: 70 single-branch batches (8 MiB of
