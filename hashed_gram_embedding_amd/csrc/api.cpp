@@ -556,6 +556,9 @@ engram_status check_call(const char* who, const engram_layer* L, const engram_de
 engram_status run_retrieve(const int32_t* tokens, int64_t B, int64_t T, const engram_layer* L,
                            const engram::HashArgs& ha, const engram::TableArgs& ta, int hdtype,
                            const engram_decode_state* st, void* e, hipStream_t stream) {
+  // the hashed gather indexes tokens and (token, table) groups in 32 bits
+  if (B * T >= (int64_t{1} << 31))
+    return fail(ENGRAM_EUNSUPPORTED, "retrieve: B*T = %lld tokens, above 2^31-1 per call", static_cast<long long>(B * T));
   const int32_t* hist = st != nullptr ? st->ids : nullptr;
   const int out = L->w_mx != nullptr ? engram::kGatherOutMXFP8 : hdtype;
   engram::HotArgs hot;

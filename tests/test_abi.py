@@ -212,6 +212,13 @@ def test_size_limits_are_rejected_before_launch():
     need = L.engram_forward_workspace(1, 64, ctypes.byref(lay))
     st, msg = _status(L.engram_forward, p, p, 65536, 1, ctypes.byref(lay), None, None, None, p, need, None)
     assert st == eg.EUNSUPPORTED and "B above" in msg
+    # 2 x 2^30 tokens: B and T are each within their limits, but the hashed gather's 2^31
+    # tokens per call is not (refused before any launch; the workspace size is only claimed)
+    big = L.engram_forward_workspace(2, 2 ** 30, ctypes.byref(lay))
+    st, msg = _status(L.engram_forward, p, p, 2, 2 ** 30, ctypes.byref(lay), None, None, None, p, big, None)
+    assert st == eg.EUNSUPPORTED and "2^31" in msg
+    st, msg = _status(L.engram_retrieve, p, 2, 2 ** 30, ctypes.byref(lay), None, p, None)
+    assert st == eg.EUNSUPPORTED and "2^31" in msg
 
 
 def test_retrieve_and_forward_retrieved_reject_bad_arguments():
