@@ -244,7 +244,8 @@ engram_status engram_gate_conv_forward(void* H, const void* kv, int64_t B, int64
                                        hipStream_t stream);
 
 /* Steps 1-8 for one layer.  tokens: device int32 [B][T]; H: device
- * [B][T][M][d] updated in place (T < 2^31, B <= 65535).  st: as for engram_gate_conv_forward; when
+ * [B][T][M][d] updated in place (T < 2^31, B <= 65535, and B*T < 2^31 for
+ * the hashed gather: ENGRAM_EUNSUPPORTED otherwise).  st: as for engram_gate_conv_forward; when
  * given, the hash reads st->ids as the history and the state (ids, conv,
  * pos) is advanced by T tokens.  alpha_out / y_out as above.  ws: device
  * scratch of at least engram_forward_workspace() bytes, 256-byte aligned. */
@@ -281,7 +282,7 @@ engram_status engram_forward_noalloc(const int32_t* tokens, void* H, int64_t B, 
  * (cache prefetch section) and the DRAM offload study fetches the rows while
  * the preceding layers compute (DRAM offload section).
  *
- * engram_retrieve: Steps 1-4 into e, device [B*T][n_tables*dim] of the
+ * engram_retrieve: Steps 1-4 into e (B*T < 2^31), device [B*T][n_tables*dim] of the
  * layer's hdtype, 16-byte aligned, owned by the caller (for an MXFP8 layer:
  * [B*T][n_tables*dim] E4M3 codes followed by [B*T][n_tables*dim/32] scale
  * bytes).  st: NULL, or the
