@@ -47,6 +47,7 @@ PEAK_PCIE_GBPS = 64.0        # PCIe Gen5 x16, one direction (host-resident table
 WARMUP_FLOOR_MS = 100.0   # least untimed warm-up before the timed steps
 PROFILE_CHUNK_STEPS = 10  # steps launched back to back between reads of the kernel events (a graph's length)
 QUEUE_AHEAD_MS = 2.0      # spin ahead of each such run, while the host queues its launches
+QUEUE_AHEAD_MAX_STEP_MS = 0.2   # ... for steps shorter than this (longer ones keep the queue full)
 ROTATION_BYTES = 512 << 20   # table rows a rotation of batches touches: twice the Infinity Cache
 CPU_HALO = 11                # positions before a token that its layer output depends on: (N-1) + (w-1)*N
 
@@ -862,8 +863,13 @@ def time_case(torch, eg, case, steps, warmup, eager=False, per_graph=10):
     samples = {}
     n_timed = 0
     i = 0
+    # a spin ahead only where the host could fall behind: steps longer than
+    # QUEUE_AHEAD_MAX_STEP_MS keep the queue full by themselves, and an idle
+    # spin before them would let the clocks drop for the steps that follow
+    spin = ms < QUEUE_AHEAD_MAX_STEP_MS
     while n_timed < n_eager:
-        queue_ahead(torch, QUEUE_AHEAD_MS)
+        if spin:
+            queue_ahead(torch, QUEUE_AHEAD_MS)
         for s in range(chunk):
             step(i + s)
         for name, t in eg.profile_read()[per_call:]:
@@ -918,9 +924,9 @@ def kernel_block(t, rates, case):
             "kernel_us_p10_p50_p90": t["kernel_us_p10_p50_p90"],
             "kernel_rate": {k: round(v, 2) for k, v in rates.items()},
             "kernel_timing": {"how": "events recorded by each kernel's own dispatch over eager steps of the same "
-                                     f"rotation, queued behind a {QUEUE_AHEAD_MS:g} ms spin kernel so that they run back to "
-                                     f"back, read every {PROFILE_CHUNK_STEPS} steps (the first step after each read "
-                                     "left out)",
+                                     f"rotation, run back to back (steps under {QUEUE_AHEAD_MAX_STEP_MS:g} ms queued behind a "
+                                     f"{QUEUE_AHEAD_MS:g} ms spin kernel so that the host stays ahead), read every "
+                                     f"{PROFILE_CHUNK_STEPS} steps (the first step after each read left out)",
                               "sum_of_kernels_ms_per_step": round(ks, 5),
                               "graph_step_minus_kernel_sum_ms": round(t["ms_per_step"] - ks, 5),
                               "eager_ms_per_step": round(t["eager_ms_per_step"], 5)}}
