@@ -448,6 +448,10 @@ engram_status check_layer(const engram_layer* L, engram::HashArgs* ha, engram::T
     if (!aligned(L->w_mx, 16) || !aligned(L->w_mx_scale, 4))
       return fail(ENGRAM_EINVAL, "layer: w_mx must be 16-byte and w_mx_scale 4-byte aligned");
   }
+  if (L->w_mx_packed != nullptr) {
+    if (L->w_mx == nullptr) return fail(ENGRAM_EINVAL, "layer: w_mx_packed needs w_mx");
+    if (!aligned(L->w_mx_packed, 16)) return fail(ENGRAM_EINVAL, "layer: w_mx_packed must be 16-byte aligned");
+  }
   bool any_hot;
   return check_hot(L->hot, &L->hash, &L->tables, nullptr, &any_hot);
 }
@@ -590,6 +594,7 @@ engram_status run_compute(const int32_t* tokens, const void* e, void* H, int64_t
     if (mx) {
       pa.e_scale = static_cast<const uint8_t*>(e) + n_tok * d_mem;   // after the codes
       pa.w_scale = L->w_mx_scale;
+      pa.w_packed = L->w_mx_packed;
     }
     pa.H = static_cast<const uint16_t*>(H);
     pa.v = f.kv;
@@ -933,6 +938,18 @@ ENGRAM_API engram_status engram_quantize_mxfp8(const void* x, engram_dtype dtype
   if (!aligned(x, dtype == ENGRAM_F32 ? 32 : 16) || !aligned(q, 8))
     return fail(ENGRAM_EINVAL, "quantize_mxfp8: x must be 16-byte (BF16) or 32-byte (F32) aligned, q 8-byte");
   return hip_status(engram::launch_mx_quantize(x, dtype, rows, cols, q, scale, stream), "quantize launch");
+}
+
+ENGRAM_API engram_status engram_pack_mxfp8(const uint8_t* q, const uint8_t* scale, int64_t rows, int64_t cols,
+                                           uint8_t* packed, hipStream_t stream) {
+  if (rows < 0 || cols < 0 || rows % 32 != 0 || cols % 256 != 0)
+    return fail(ENGRAM_EINVAL, "pack_mxfp8: rows a non-negative multiple of 32 and cols of 256");
+  if (rows * cols == 0) return ENGRAM_OK;
+  if (q == nullptr || scale == nullptr || packed == nullptr)
+    return fail(ENGRAM_EINVAL, "pack_mxfp8: q, scale and packed must be non-NULL");
+  if (!aligned(q, 16) || !aligned(packed, 16))
+    return fail(ENGRAM_EINVAL, "pack_mxfp8: q and packed must be 16-byte aligned");
+  return hip_status(engram::launch_mx_pack(q, scale, rows, cols, packed, stream), "pack launch");
 }
 
 ENGRAM_API engram_status engram_profile_enable(int32_t on) {

@@ -90,6 +90,10 @@ hipError_t launch_hash(const int32_t* tokens, int64_t B, int64_t T, const int32_
 
 hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scale,
                               hipStream_t s);
+// MXFP8 W (codes [rows][cols], scales [rows][cols/32]) in the fragment order
+// of the FP8 matrix cores; rows a multiple of 32, cols of 256.
+hipError_t launch_mx_pack(const uint8_t* q, const uint8_t* scale, int64_t rows, int64_t cols, uint8_t* packed,
+                          hipStream_t s);
 
 // Gather output in MXFP8: [n_tok][n_tables*dim] E4M3 codes followed by
 // [n_tok][n_tables*dim/32] scale bytes (dim a multiple of 32).
@@ -138,6 +142,9 @@ struct ProjGateArgs {
   // bytes) and these their block scale bytes ([n_tok][K/32], [N][K/32])
   const uint8_t* e_scale;
   const uint8_t* w_scale;
+  // optional MXFP8 W in matrix-core fragment order (engram_pack_mxfp8): the
+  // resident-token kernel streams it straight into registers
+  const uint8_t* w_packed;
   // Decode-state advance folded into this launch (adv_B > 0): workgroup 0
   // shifts the last N-1 compressed ids of every sequence's T = adv_T new
   // tokens into st_ids and adds adv_T to st_pos.  Nothing in the launch reads

@@ -28,7 +28,58 @@ mx_quantize_kernel(const void* __restrict__ x, int64_t n8, uint8_t* __restrict__
   if ((gid & 3) == 0) scale[gid >> 2] = static_cast<uint8_t>(sb);
 }
 
+// Fragment order of a 32-row block of W for v_mfma_scale_f32_32x32x64_f8f6f4
+// (the A-operand layout the projection kernels read out of LDS): for K64
+// step kk, lane l = 32h + r holds bytes 16h..16h+15 and 32+16h..32+16h+15 of
+// row r's 64-byte run, and its operand scale is that of block 2kk + h.  The
+// packed copy stores, per (block, step), the 64 lanes' 32 bytes one after the
+// other, then per (block, group of four steps) one 32-bit word per lane with
+// the lane's four scale bytes (byte s for step 4kq + s).  A wavefront then
+// loads its operand for a step with two fully coalesced 16-byte loads.
+// One thread per (block, step, lane) and, in the scale part, per (block,
+// step group, lane).
+__global__ void __launch_bounds__(256)
+mx_pack_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ scale, int64_t rows, int cols,
+               uint8_t* __restrict__ packed) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int kk_n = cols / 64;
+  const int64_t n_frag = rows / 32 * kk_n * 64;   // fragment-lane slots
+  const int64_t n_word = rows / 32 * (kk_n / 4) * 64;
+  if (gid < n_frag) {
+    const int lane = static_cast<int>(gid & 63);
+    const int64_t rest = gid >> 6;
+    const int kk = static_cast<int>(rest % kk_n);
+    const int64_t row = rest / kk_n * 32 + (lane & 31);
+    const int hh = lane >> 5;
+    const uint8_t* src = q + row * cols + kk * 64 + hh * 16;
+    uint4* dst = reinterpret_cast<uint4*>(packed + gid * 32);
+    dst[0] = *reinterpret_cast<const uint4*>(src);
+    dst[1] = *reinterpret_cast<const uint4*>(src + 32);
+  } else if (gid < n_frag + n_word) {
+    const int64_t w = gid - n_frag;
+    const int lane = static_cast<int>(w & 63);
+    const int64_t rest = w >> 6;
+    const int kq = static_cast<int>(rest % (kk_n / 4));
+    const int64_t row = rest / (kk_n / 4) * 32 + (lane & 31);
+    const int hh = lane >> 5;
+    const uint8_t* src = scale + row * (cols / 32) + kq * 8 + hh;   // block 2 * (4kq + s) + hh
+    const uint32_t word = static_cast<uint32_t>(src[0]) | static_cast<uint32_t>(src[2]) << 8 |
+                          static_cast<uint32_t>(src[4]) << 16 | static_cast<uint32_t>(src[6]) << 24;
+    reinterpret_cast<uint32_t*>(packed + rows * cols)[w] = word;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_mx_pack(const uint8_t* q, const uint8_t* scale, int64_t rows, int64_t cols, uint8_t* packed,
+                          hipStream_t s) {
+  if (rows % 32 != 0 || cols % 256 != 0) return hipErrorInvalidValue;
+  const int64_t n = rows / 32 * (cols / 64) * 64 + rows / 32 * (cols / 256) * 64;
+  if (n == 0) return hipSuccess;
+  launch_k(mx_pack_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, q, scale, rows,
+           static_cast<int>(cols), packed);
+  return hipGetLastError();
+}
 
 hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scale,
                               hipStream_t s) {

@@ -41,6 +41,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+// The same, as one vector shuffle (the halves can land in place).
+__device__ __forceinline__ i32x8_t cat16(u32x4_t lo, u32x4_t hi) {
+  return __builtin_bit_cast(i32x8_t, static_cast<u32x8_t>(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)));
+}
+
 // Two 16-byte chunks as the 32-byte MXFP8 operand of one lane.
 __device__ __forceinline__ i32x8_t join16(u32x4_t lo, u32x4_t hi) {
   return i32x8_t{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
@@ -633,6 +639,388 @@ proj_gate_small_kernel(ProjGateArgs a) {
   advance_state(a);
 }
 
+// Many tokens of a multi-branch FP8 product, with W in fragment order
+// (engram_pack_mxfp8): a workgroup keeps the e codes of 128 tokens resident
+// in LDS for the whole launch (128 KiB at K = 1024) and sweeps the feature
+// columns in passes of 256, one 32-column block per wavefront.  A
+// wavefront's W operand comes straight from memory into registers, two
+// coalesced 16-byte loads per K64 step, kResDepth steps ahead and across pass
+// boundaries, so the main loop has no barrier at all; the four token blocks
+// of its 32 x 128 output tile reuse each W operand four times.  Per
+// multiply-accumulate the L2-to-CU traffic is then W's alone, 1/128 byte,
+// against 3/256 for the 128 x 256 tiles that stream both operands.  A key
+// pass loads its h values into registers before its K loop, so their latency
+// hides behind the matrix work; the per-token partial sums of each 128-column
+// statistics tile (four wavefronts) meet in LDS at the end of the pass.
+constexpr int kResTK = 128;                // tokens per workgroup, resident in LDS
+constexpr int kResWaves = 8;               // wavefront w: 32 features x 128 tokens
+constexpr int kResPass = 32 * kResWaves;   // features per pass
+constexpr int kResDepth = 4;               // K64 W operands in flight per wavefront
+constexpr int kVmcnt0 = 0x0f70;            // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt unbounded
+
+// LDS: e codes [K/16][128] 16-byte chunks, e scale words [K/128][128], and
+// a pass's partial sums: per statistics tile and 64-column half, the first
+// wavefront's per-lane sums [4][64] and the per-token sums [128]
+constexpr int kResRed = 2 * 2 * 4 * 64 + 2 * 2 * kResTK;   // float4 slots
+size_t res_lds_bytes(int K) {
+  return static_cast<size_t>(kResTK) * K + static_cast<size_t>(kResTK) * (K / 32) +
+         static_cast<size_t>(kResRed) * sizeof(float4);
+}
+
+template <int KK>   // K64 steps: K = 64 * KK, a multiple of 256 up to 1024
+__global__ void __launch_bounds__(64 * kResWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+proj_gate_mx_resident_kernel(ProjGateArgs a) {
+  static_assert(KK % 4 == 0 && KK <= 16, "K a multiple of 256 up to 1024");
+  extern __shared__ u32x4_t res_lds[];
+  constexpr int K = KK * 64;
+  constexpr int nch = K / 16;   // 16-byte chunks of an e row
+  u32x4_t* Ec = res_lds;                                                // chunk c of token t at c * 128 + t
+  uint32_t* Es = reinterpret_cast<uint32_t*>(res_lds + nch * kResTK);   // scale word w of token t at w * 128 + t
+  float4* red = reinterpret_cast<float4*>(Es + (K / 128) * kResTK);     // kResRed partial sums
+
+  const int groups = static_cast<int>(gridDim.x) / a.tiles_t;   // workgroups sharing a token tile
+  const int tt = blockIdx.x / groups;
+  const int grp = blockIdx.x % groups;
+  const int passes = a.N / kResPass;
+  const int p0 = grp * passes / groups, p1 = (grp + 1) * passes / groups;
+  const int64_t t0 = static_cast<int64_t>(tt) * kResTK;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hh = lane >> 5;
+  const int r = lane & 31;
+  const int d = a.d;
+
+  // e codes and scale words of the tile: one wavefront instruction fills 64
+  // consecutive LDS slots, chunk c (or word w) of 64 consecutive tokens;
+  // token rows past the end re-read the last valid row
+  {
+    const uint8_t* ecodes = reinterpret_cast<const uint8_t*>(a.e);
+    for (int q = wave; q < 2 * nch; q += kResWaves) {
+      const int c = q >> 1;
+      const int64_t tok = min(t0 + ((q & 1) << 6) + lane, a.n_tok - 1);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(ecodes + tok * K + c * 16),
+                                       (__attribute__((address_space(3))) void*)(Ec + c * kResTK + (q & 1) * 64),
+                                       16, 0, 0);
+    }
+    for (int q = wave; q < 2 * (K / 128); q += kResWaves) {
+      const int w = q >> 1;
+      const int64_t tok = min(t0 + ((q & 1) << 6) + lane, a.n_tok - 1);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.e_scale + tok * (K / 32) + 4 * w),
+                                       (__attribute__((address_space(3))) void*)(Es + w * kResTK + (q & 1) * 64),
+                                       4, 0, 0);
+    }
+  }
+
+  // Pass order: the eight XCDs start at passes np/8 apart, so that the
+  // chip's h loads (key passes) and v stores (value passes) do not all fall
+  // on HBM at once; the workgroups of one XCD keep one order and share W in
+  // their L2.
+  const int np = p1 - p0;
+  const int off = ((blockIdx.x & (kXcds - 1)) * np) / kXcds;
+  auto pass_at = [&](int i) { return p0 + (i + off) % np; };
+
+  // this wavefront's W operands: (block b, step kk) is lane slot
+  // (b*KK + kk)*64 + lane, its scale word (b*KK/4 + kk/4)*64 + lane; the
+  // wavefront's block of pass p is p*8 + wave.  kResDepth steps are in
+  // flight, the first ones of the next pass while a pass ends (after the
+  // last pass the loads repeat the last block's first steps, unused).  Each
+  // ring slot is refilled right after the multiplies that read it, and the
+  // e operands of a step are read one step ahead, two register sets in turn.
+  const i32x8_t* wop = reinterpret_cast<const i32x8_t*>(a.w_packed);
+  const uint32_t* wword = reinterpret_cast<const uint32_t*>(a.w_packed + static_cast<int64_t>(a.N) * K);
+  i32x8_t wring[kResDepth];
+  {
+    const int64_t slot0 = static_cast<int64_t>(pass_at(0) * kResWaves + wave) * KK * 64;
+#pragma unroll
+    for (int u = 0; u < kResDepth; ++u) wring[u] = wop[slot0 + u * 64 + lane];   // KK >= kResDepth
+  }
+  uint32_t wsc_next = wword[static_cast<int64_t>(pass_at(0) * kResWaves + wave) * (KK / 4) * 64 + lane];
+  // the e tile has landed (every wavefront's part); a wait the compiler
+  // sees, so that it counts the operand loads after it exactly
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __builtin_amdgcn_s_barrier();
+
+  auto read_e = [&](int kk, i32x8_t (&fb)[4], int (&sb)[4]) {
+    // (the lane index through an empty asm, so that the addresses are formed
+    // where they are used: hoisted out of the pass loop, they stay live
+    // across it and spill)
+    int rr = r;
+    asm volatile("" : "+v"(rr));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tr = j * 32 + rr;
+      fb[j] = cat16(Ec[(4 * kk + hh) * kResTK + tr], Ec[(4 * kk + 2 + hh) * kResTK + tr]);
+      sb[j] = static_cast<int>((Es[(kk >> 1) * kResTK + tr] >> (8 * (2 * (kk & 1) + hh))) & 0xffu);
+    }
+  };
+  i32x8_t fbA[4], fbB[4];
+  int sbA[4], sbB[4];
+  read_e(0, fbA, sbA);
+
+  // A key pass's 16 h loads per lane are spread over its first kHSteps
+  // steps, each after that step's operand loads.  The memory counter
+  // retires loads in order, so a wait for an operand load also waits for
+  // every load issued before it: an h load issued at step s is waited for
+  // at step s + kResDepth + 1 at the latest, and the whole set arrives by the
+  // epilogue, instead of the first operand wait of the pass waiting for all
+  // of them.
+  constexpr int kHSteps = KK < 8 ? KK : 8;
+  constexpr int kHPerStep = 8 / kHSteps;
+  for (int i = 0; i < np; ++i) {
+    const int p = pass_at(i);
+    const int fp = p * kResPass;
+    const bool is_v = fp < d;
+    const int m = is_v ? 0 : fp / d - 1;
+    const int fcol = (is_v ? fp : fp - (1 + m) * d) + wave * 32;   // this block's first column of v or of h
+    // A key block's h values.  Lane half hh loads columns 16hh .. 16hh+15
+    // of its token's 32 (two 16-byte loads, half as many instructions as
+    // the accumulator layout's 8-byte pieces), and the epilogue trades half
+    // of them with the partner lane (v_permlane32_swap) to reach that
+    // layout.  The loads are unconditional (a branch around them inside the
+    // unrolled loop costs registers); a value pass reads the first 64 bytes
+    // of H instead, unused.  Byte offsets of H fit 32 bits (checked by the
+    // launcher).
+    u32x4_t hA[4], hB[4];
+    uint32_t hoff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      hoff[j] = static_cast<uint32_t>(hh * 32) +
+                (is_v ? 0u : static_cast<uint32_t>(((min(t0 + j * 32 + r, a.n_tok - 1) * a.M + m) * d + fcol) * 2));
+    f32x16_t acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc[j][c] = 0.f;
+
+    const int64_t blk = static_cast<int64_t>(p) * kResWaves + wave;
+    const int64_t nblk = i + 1 < np ? static_cast<int64_t>(pass_at(i + 1)) * kResWaves + wave : blk;
+    // the whole K loop of a pass unrolled: every wait on an operand load is
+    // then counted exactly (through a loop back-edge the compiler waits for
+    // all loads)
+#pragma unroll
+    for (int kk0 = 0; kk0 < KK; kk0 += kResDepth) {
+      const uint32_t wsc = wsc_next;   // scale bytes of this group of four steps
+      // where the operands kResDepth steps ahead come from: later steps of
+      // this block, or the first steps of the next pass's block
+      const bool in_pass = kk0 + kResDepth < KK;
+      // (uniform bases; the lane offset is added per load)
+      const i32x8_t* tslot = wop + (in_pass ? blk * KK + kk0 + kResDepth : nblk * KK) * 64;
+      const uint32_t* tword = wword + (in_pass ? blk * (KK / 4) + kk0 / 4 + 1 : nblk * (KK / 4)) * 64;
+      const int kn = in_pass ? kk0 + kResDepth : 0;   // the step after this group
+#pragma unroll
+      for (int u = 0; u < kResDepth; ++u) {
+        const int kk = kk0 + u;
+        const int sa = static_cast<int>((wsc >> (8 * u)) & 0xffu);
+        i32x8_t (&fc)[4] = (u & 1) ? fbB : fbA;   // this step's e operands
+        int (&sc)[4] = (u & 1) ? sbB : sbA;
+        i32x8_t (&fn)[4] = (u & 1) ? fbA : fbB;   // the next step's
+        int (&sn)[4] = (u & 1) ? sbA : sbB;
+        read_e(u + 1 < kResDepth ? kk + 1 : kn, fn, sn);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wring[u], fc[j], acc[j], 0, 0, 0, sa, 0, sc[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        wring[u] = tslot[u * 64 + lane];
+        if (u == 0) wsc_next = tword[lane];
+        if (kk < kHSteps) {
+#pragma unroll
+          for (int c = 0; c < kHPerStep; ++c) {
+            const int idx = kk * kHPerStep + c;
+            const u32x4_t hv = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(a.H) +
+                                                                 hoff[idx >> 1] + (idx & 1) * 16);
+            if (idx & 1)
+              hB[idx >> 1] = hv;
+            else
+              hA[idx >> 1] = hv;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // epilogue: acc[j][4g + i] is feature g*8 + hh*4 + i of the block, token
+    // j*32 + r.  The gate sums of each 128-column statistics tile are formed
+    // in exactly the order of the 128 x 256 tile kernel (whose wavefront
+    // holds 64 columns): the first 32-column wavefront of each 64-column
+    // half leaves its per-lane running sums in LDS, the second continues
+    // them and halves them across the lane halves, and the two halves are
+    // added last.  The results are then identical bit for bit.
+    const int qd = wave >> 2;          // 128-column statistics tile of the pass
+    const int half64 = (wave >> 1) & 1;   // 64-column half of the tile
+    const bool first = (wave & 1) == 0;   // first 32-column block of the half
+    float4* lane_part = red + ((qd * 2 + half64) * 4) * 64;   // [4 token blocks][64 lanes]
+    float4* tok_part = red + 2 * 2 * 4 * 64 + (qd * 2 + half64) * kResTK;   // [128 tokens]
+    // the previous pass's partial sums have been read (LDS only: the operand
+    // loads in flight stay in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // h in the accumulator layout: after the swaps (in place), lane (hh, r)
+    // holds columns g*8 + hh*4 .. +3 in hA[j].xy (g = 0), hB[j].xy (g = 1),
+    // hA[j].zw (g = 2) and hB[j].zw (g = 3)
+    if (!is_v) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const auto a0 = __builtin_amdgcn_permlane32_swap(hA[j].x, hA[j].z, false, false);
+        const auto a1 = __builtin_amdgcn_permlane32_swap(hA[j].y, hA[j].w, false, false);
+        const auto b0 = __builtin_amdgcn_permlane32_swap(hB[j].x, hB[j].z, false, false);
+        const auto b1 = __builtin_amdgcn_permlane32_swap(hB[j].y, hB[j].w, false, false);
+        hA[j] = u32x4_t{a0[0], a1[0], a0[1], a1[1]};
+        hB[j] = u32x4_t{b0[0], b1[0], b0[1], b1[1]};
+      }
+    }
+    auto hq = [&](int j, int g) {
+      const u32x4_t& v = (g & 1) ? hB[j] : hA[j];
+      return g < 2 ? make_uint2(v.x, v.y) : make_uint2(v.z, v.w);
+    };
+    float4 part[4];
+    if (is_v) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t tok = t0 + j * 32 + r;
+        float s3 = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float x0 = acc[j][4 * g], x1 = acc[j][4 * g + 1], x2 = acc[j][4 * g + 2], x3 = acc[j][4 * g + 3];
+          if (tok < a.n_tok) *reinterpret_cast<float4*>(a.v + tok * d + fcol + g * 8 + hh * 4) = make_float4(x0, x1, x2, x3);
+        }
+        if (first) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float x0 = acc[j][4 * g], x1 = acc[j][4 * g + 1], x2 = acc[j][4 * g + 2], x3 = acc[j][4 * g + 3];
+            s3 += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+          }
+        }
+        part[j] = make_float4(0.f, 0.f, 0.f, s3);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+        if (first) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float x0 = acc[j][4 * g], x1 = acc[j][4 * g + 1], x2 = acc[j][4 * g + 2], x3 = acc[j][4 * g + 3];
+            s1 += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint2 q = hq(j, g);
+            const float x0 = acc[j][4 * g], x1 = acc[j][4 * g + 1], x2 = acc[j][4 * g + 2], x3 = acc[j][4 * g + 3];
+            const float h0 = __uint_as_float(q.x << 16), h1 = __uint_as_float(q.x & 0xffff0000u);
+            const float h2 = __uint_as_float(q.y << 16), h3 = __uint_as_float(q.y & 0xffff0000u);
+            s0 += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
+            s2 += h0 * x0 + h1 * x1 + h2 * x2 + h3 * x3;
+          }
+        }
+        part[j] = make_float4(s0, s1, s2, 0.f);
+      }
+    }
+    if (first) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lane_part[j * 64 + lane] = part[j];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (!first) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 c = lane_part[j * 64 + lane];
+        float s0 = c.x, s1 = c.y, s2 = c.z, s3 = c.w;
+        if (is_v) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float x0 = acc[j][4 * g], x1 = acc[j][4 * g + 1], x2 = acc[j][4 * g + 2], x3 = acc[j][4 * g + 3];
+            s3 += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+          }
+          s3 += __shfl_xor(s3, 32, 64);
+          if (hh == 0) tok_part[j * 32 + r] = make_float4(0.f, 0.f, 0.f, s3);
+        } else {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float x0 = acc[j][4 * g], x1 = acc[j][4 * g + 1], x2 = acc[j][4 * g + 2], x3 = acc[j][4 * g + 3];
+            s1 += x0 * x0 + x1 * x1 + x2 * x2 + x3 * x3;
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint2 q = hq(j, g);
+            const float x0 = acc[j][4 * g], x1 = acc[j][4 * g + 1], x2 = acc[j][4 * g + 2], x3 = acc[j][4 * g + 3];
+            const float h0 = __uint_as_float(q.x << 16), h1 = __uint_as_float(q.x & 0xffff0000u);
+            const float h2 = __uint_as_float(q.y << 16), h3 = __uint_as_float(q.y & 0xffff0000u);
+            s0 += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
+            s2 += h0 * x0 + h1 * x1 + h2 * x2 + h3 * x3;
+          }
+          s0 += __shfl_xor(s0, 32, 64);
+          s1 += __shfl_xor(s1, 32, 64);
+          s2 += __shfl_xor(s2, 32, 64);
+          if (hh == 0) tok_part[j * 32 + r] = make_float4(s0, s1, s2, 0.f);
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (tid < 2 * kResTK) {
+      const int q2 = tid >> 7, t = tid & (kResTK - 1);
+      const int64_t tok = t0 + t;
+      if (tok < a.n_tok) {
+        const float4* tp = red + 2 * 2 * 4 * 64 + q2 * 2 * kResTK;
+        const float4 x = tp[t], y = tp[kResTK + t];
+        a.stats[tok * a.tiles_f + p * 2 + q2] = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+      }
+    }
+    // Drain this pass's stores here.  The memory counter mixes loads and
+    // stores, which do not finish in order, so with stores in flight every
+    // later wait on an operand load would be a wait for all memory work,
+    // the next pass's h loads included.
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  }
+  advance_state(a);
+}
+
+// Workgroups per token tile for the resident-token FP8 kernel, or 0 where it
+// does not apply: multi-branch layers (whose statistics tiles are plain
+// 128-column ones), d a multiple of 256, K a multiple of 256 up to 1024 (the
+// e tile in LDS), H below 4 GiB, and enough token tiles that at most
+// passes / 4 workgroups per tile fill the 256 CUs.
+int res_groups(int64_t n_tok, int N, int d, int K, int M) {
+  if (M < 2 || d % kResPass != 0 || N % kResPass != 0 || K % 256 != 0 || K > 1024) return 0;
+  if (n_tok * M * d * 2 > int64_t{0xffffffff}) return 0;   // byte offsets of H in 32 bits
+  const int64_t tiles_t = (n_tok + kResTK - 1) / kResTK;
+  const int passes = N / kResPass;
+  for (int g = 1; g <= passes / 4; ++g)
+    if (tiles_t * g >= 256) return g;
+  return 0;
+}
+
+template <int KK>
+hipError_t launch_resident_k(const ProjGateArgs& a, dim3 grid, size_t lds, hipStream_t s) {
+  static std::atomic<uint64_t> attr_set{0};   // > 64 KiB of dynamic LDS, raised once per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if ((attr_set.load() & bit) == 0) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_mx_resident_kernel<KK>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set.fetch_or(bit);
+  }
+  launch_k(proj_gate_mx_resident_kernel<KK>, grid, dim3(64 * kResWaves), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_resident(const ProjGateArgs& in, int groups, hipStream_t s) {
+  ProjGateArgs a = in;
+  a.tiles_f = a.N / 128;
+  a.tiles_t = static_cast<int>((a.n_tok + kResTK - 1) / kResTK);
+  const size_t lds = res_lds_bytes(a.K);
+  const dim3 grid(static_cast<unsigned>(a.tiles_t * groups));
+  switch (a.K) {
+    case 256: return launch_resident_k<4>(a, grid, lds, s);
+    case 512: return launch_resident_k<8>(a, grid, lds, s);
+    case 768: return launch_resident_k<12>(a, grid, lds, s);
+    case 1024: return launch_resident_k<16>(a, grid, lds, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int TF, bool MX, int NBUF, bool MIXED, int WT = 4>
 hipError_t launch_tf(ProjGateArgs a, hipStream_t s) {
   a.tiles_f = a.N / TF;
@@ -740,6 +1128,10 @@ hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {
   if (mx) {
     if (in.K % 128 != 0 || in.w_scale == nullptr) return hipErrorInvalidValue;
     if (proj_gate_small_for(in.n_tok, in.N, in.d, in.K, true)) return launch_small<true>(in, s);
+    if (in.w_packed != nullptr) {
+      const int g = res_groups(in.n_tok, in.N, in.d, in.K, in.M);
+      if (g > 0) return launch_resident(in, g, s);
+    }
     // 128-feature tiles, slices straight into LDS like the bf16 product
     // (the 256-feature tile's accumulators and FP8 operands spill registers)
     return in.M == 1 ? launch_tf<128, true, 3, true>(in, s) : launch_tf<128, true, 3, false>(in, s);

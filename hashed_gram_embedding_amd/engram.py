@@ -59,7 +59,7 @@ class HotTierStruct(ctypes.Structure):
 
 class LayerStruct(ctypes.Structure):
     _fields_ = [("hash", HashParams), ("tables", Tables), ("w", ctypes.c_void_p), ("gc", GateConvParams),
-                ("w_mx", ctypes.c_void_p), ("w_mx_scale", ctypes.c_void_p),
+                ("w_mx", ctypes.c_void_p), ("w_mx_scale", ctypes.c_void_p), ("w_mx_packed", ctypes.c_void_p),
                 ("hot", ctypes.POINTER(HotTierStruct))]
 
 
@@ -111,6 +111,7 @@ def load_library(path: str) -> ctypes.CDLL:
         "engram_forward_retrieved": (i32, [vp, vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
                                            ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
         "engram_quantize_mxfp8": (i32, [vp, i32, i64, i64, vp, vp, vp]),
+        "engram_pack_mxfp8": (i32, [vp, vp, i64, i64, vp, vp]),
         "engram_forward_retrieved_prefetch": (i32, [vp, vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
                                                     ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz,
                                                     ctypes.POINTER(LayerStruct), ctypes.POINTER(DecodeStateStruct),
@@ -145,7 +146,7 @@ def exported_names():
             "engram_project_kv", "engram_gate_conv_workspace", "engram_gate_conv_forward",
             "engram_forward_workspace", "engram_forward", "engram_forward_noalloc", "engram_retrieve", "engram_forward_retrieved_workspace",
             "engram_forward_retrieved", "engram_cache_build_workspace", "engram_cache_build",
-            "engram_cache_update_workspace", "engram_cache_update", "engram_quantize_mxfp8",
+            "engram_cache_update_workspace", "engram_cache_update", "engram_quantize_mxfp8", "engram_pack_mxfp8",
             "engram_hot_buckets", "engram_hot_build", "engram_hot_lookup", "engram_forward_retrieved_prefetch",
             "engram_profile_enable", "engram_profile_read",
             "engram_host_alloc", "engram_host_free", "engram_debug_checks", "engram_debug_set_error_word",
@@ -207,7 +208,8 @@ class Layer:
     be the device alias of pinned host memory from HostBuffer."""
 
     def __init__(self, li, hdtype: str, device="cuda", rows_device: Optional[torch.Tensor] = None,
-                 rows_ptr: Optional[int] = None, scale_ptr: Optional[int] = None, mxfp8: bool = False):
+                 rows_ptr: Optional[int] = None, scale_ptr: Optional[int] = None, mxfp8: bool = False,
+                 mx_packed: bool = True):
         hp, tab = li.hash, li.tables
         self.li = li
         self.hdtype = _DT[hdtype]
@@ -244,6 +246,12 @@ class Layer:
             quantize_mxfp8(self.w, self.w_mx, self.w_mx_scale)
             self.s.w_mx = self.w_mx.data_ptr()
             self.s.w_mx_scale = self.w_mx_scale.data_ptr()
+            self.w_mx_packed = None
+            if mx_packed and n % 32 == 0 and k % 256 == 0:
+                # the fragment-ordered copy that the resident-token FP8 kernel streams
+                self.w_mx_packed = torch.empty(n * k + n * k // 32, dtype=torch.uint8, device=device)
+                pack_mxfp8(self.w_mx, self.w_mx_scale, self.w_mx_packed)
+                self.s.w_mx_packed = self.w_mx_packed.data_ptr()
 
     def set_cache(self, slot: Optional[torch.Tensor], rows: Optional[torch.Tensor],
                   scale: Optional[torch.Tensor] = None):
@@ -516,6 +524,13 @@ def quantize_mxfp8(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream
     rows, cols = x.shape
     dt = BF16 if x.dtype == torch.bfloat16 else F32
     _check(lib().engram_quantize_mxfp8(_ptr(x), dt, rows, cols, _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def pack_mxfp8(q: torch.Tensor, scale: torch.Tensor, packed: torch.Tensor, stream=None):
+    """The MXFP8 codes q [rows, cols] and scales [rows, cols/32] in the
+    matrix cores' operand order (uint8 [rows*cols + rows*cols/32])."""
+    rows, cols = q.shape
+    _check(lib().engram_pack_mxfp8(_ptr(q), _ptr(scale), rows, cols, _ptr(packed), _stream(stream)))
 
 
 def hot_lookup(tokens: torch.Tensor, spec, hot: HotTier, hist: Optional[torch.Tensor] = None,

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 3
+#define ENGRAM_ABI_VERSION 4
 #define ENGRAM_MAX_TABLES 32 /* (N-1)*K */
 #define ENGRAM_MAX_ORDER 4   /* N */
 #define ENGRAM_MAX_KERNEL_W 8
@@ -181,6 +181,13 @@ typedef struct engram_layer {
      per-block scales; NULL = bf16 product.                                      */
   const uint8_t* w_mx;        /* device [(1+M)*d][n_tables*dim] E4M3 codes        */
   const uint8_t* w_mx_scale;  /* device [(1+M)*d][n_tables*dim/32] scale bytes    */
+  /* optional (NULL = none; needs w_mx): the same MXFP8 W in matrix-core
+     fragment order from engram_pack_mxfp8, 16-byte aligned.  Multi-branch
+     layers (M >= 2) with d a multiple of 256 and n_tables*dim a multiple of
+     256 up to 1024 then run the product, at enough tokens, with each
+     workgroup's token rows held on chip while W streams past them; results
+     are identical to those without it.                                       */
+  const uint8_t* w_mx_packed;
   /* optional Engram-Nine hot tier (read on the host during each call; NULL =
      none): used by engram_forward and engram_retrieve.  Needs F32 or BF16
      tables; a hot hit reads no cold row and counts no access.                  */
@@ -377,6 +384,19 @@ engram_status engram_cache_update(const engram_tables* tab, int64_t cache_n, int
  * x / scale rounded to nearest-even E4M3, an all-zero block has scale byte 0. */
 engram_status engram_quantize_mxfp8(const void* x, engram_dtype dtype, int64_t rows, int64_t cols,
                                     uint8_t* q, uint8_t* scale, hipStream_t stream);
+
+/* The MXFP8 W of engram_quantize_mxfp8 (q [rows][cols] codes, scale
+ * [rows][cols/32] bytes, device) rearranged into the operand order of the FP8
+ * matrix cores, for engram_layer.w_mx_packed: packed (device, 16-byte
+ * aligned, rows*cols + rows*cols/32 bytes, owned by the caller) holds, for
+ * each 32-row block b and K64 step kk, 64 lane slots of 32 bytes (lane
+ * l = 32h + r: bytes 64kk+16h .. +15 and 64kk+32+16h .. +15 of row 32b + r),
+ * then, for each block b and group kq of four steps, 64 lane words whose
+ * byte s is the scale of block 2(4kq+s)+h of row 32b + r.  rows a multiple
+ * of 32, cols a multiple of 256 (EINVAL otherwise); rows*cols = 0 is a
+ * no-op. */
+engram_status engram_pack_mxfp8(const uint8_t* q, const uint8_t* scale, int64_t rows, int64_t cols,
+                                uint8_t* packed, hipStream_t stream);
 
 /* Engram-Nine hot tier set-up and lookup (see engram_hot_tier).
  *

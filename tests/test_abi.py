@@ -39,7 +39,7 @@ def test_exports_match_header():
 
 
 def test_abi_version():
-    assert eg.lib().engram_abi_version() == 3
+    assert eg.lib().engram_abi_version() == 4
 
 
 def _hash_params(**over):
@@ -324,13 +324,36 @@ def test_mxfp8_layer_outside_the_fused_projection_is_rejected():
     hp, keep_h = _hash_params()
     t, keep_t = _tables(dtype=eg.BF16, dim=32)       # d_mem = 4 x 32 = 128
     for d, want in ((4096 + 128, eg.EUNSUPPORTED), (4096 * 2, eg.EUNSUPPORTED)):
-        lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=d), 0x20000, 0x30000, None)
+        lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=d), 0x20000, 0x30000)
         need = L.engram_forward_workspace(1, 64, ctypes.byref(lay))
         st, msg = _status(L.engram_forward, p, p, 1, 64, ctypes.byref(lay), None, None, None, p, need, None)
         assert st == want and "MXFP8" in msg
         assert L.engram_retrieve(p, 1, 64, ctypes.byref(lay), None, p, None) == want
-    lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=4096), 0x20000, 0x30000, None)
+    lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=4096), 0x20000, 0x30000)
     assert L.engram_retrieve(p, 0, 64, ctypes.byref(lay), None, p, None) == eg.OK     # d = 4096 passes the checks
+
+
+def test_packed_mxfp8_weights_are_checked():
+    """engram_pack_mxfp8 takes whole 32-row blocks and 256-column step
+    groups, and a layer's packed W needs its MXFP8 W and 16-byte alignment;
+    all refused before anything launches."""
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    for rows, cols in ((33, 256), (32, 128), (-32, 256), (64, 300)):
+        st, msg = _status(L.engram_pack_mxfp8, p, p, rows, cols, p, None)
+        assert st == eg.EINVAL and "pack_mxfp8" in msg, (rows, cols)
+    assert L.engram_pack_mxfp8(None, None, 0, 256, None, None) == eg.OK          # empty: a no-op
+    st, msg = _status(L.engram_pack_mxfp8, None, p, 32, 256, p, None)
+    assert st == eg.EINVAL and "non-NULL" in msg
+    st, msg = _status(L.engram_pack_mxfp8, ctypes.c_void_p(0x10008), p, 32, 256, p, None)
+    assert st == eg.EINVAL and "aligned" in msg
+    hp, keep_h = _hash_params()
+    t, keep_t = _tables(dtype=eg.BF16, dim=32)
+    for w_mx, packed, text in ((None, 0x40000, "needs w_mx"), (0x20000, 0x40008, "aligned")):
+        lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=256), w_mx, 0x30000 if w_mx else None, packed)
+        need = L.engram_forward_workspace(1, 64, ctypes.byref(lay))
+        st, msg = _status(L.engram_forward, p, p, 1, 64, ctypes.byref(lay), None, None, None, p, need, None)
+        assert st == eg.EINVAL and text in msg, msg
 
 
 def test_forward_noalloc_rejects_calls_beyond_its_scratch():

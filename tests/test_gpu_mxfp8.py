@@ -118,3 +118,78 @@ def test_decode_mxfp8_matches_oracle(config):
         ost = ref["state"]
         check_bf16_layer(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.bf16_to_f64(Hn),
                          tag=f"mxfp8 decode c{config} chunk{ci}")
+
+
+def test_pack_mxfp8_layout():
+    """engram_pack_mxfp8 writes the operand order that include/engram.h
+    documents, built here index by index from the codes and scales."""
+    log("mxfp8 pack layout")
+    rng = np.random.default_rng(37)
+    rows, cols = 96, 768
+    q = rng.integers(0, 256, (rows, cols), dtype=np.uint8)
+    s = rng.integers(0, 256, (rows, cols // 32), dtype=np.uint8)
+    packed = torch.empty(rows * cols + rows * cols // 32, dtype=torch.uint8, device=DEV)
+    eg.pack_mxfp8(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), packed)
+    got = packed.cpu().numpy()
+    kk_n = cols // 64
+    want = np.empty(rows * cols + rows * cols // 32, dtype=np.uint8)
+    for b in range(rows // 32):
+        for kk in range(kk_n):
+            for lane in range(64):
+                row, h = 32 * b + (lane & 31), lane >> 5
+                o = ((b * kk_n + kk) * 64 + lane) * 32
+                want[o:o + 16] = q[row, 64 * kk + 16 * h:64 * kk + 16 * h + 16]
+                want[o + 16:o + 32] = q[row, 64 * kk + 32 + 16 * h:64 * kk + 48 + 16 * h]
+        for kq in range(kk_n // 4):
+            for lane in range(64):
+                row, h = 32 * b + (lane & 31), lane >> 5
+                o = rows * cols + ((b * (kk_n // 4) + kq) * 64 + lane) * 4
+                for st in range(4):
+                    want[o + st] = s[row, 2 * (4 * kq + st) + h]
+    assert np.array_equal(got, want)
+
+
+def _forward(w, L, **kw):
+    tok = torch.from_numpy(w.tokens).to(DEV)
+    H = eg.to_device(w.H, "bf16", DEV)
+    alpha, y = eg.forward(tok, H, L, want_alpha=True, want_y=True, **kw)
+    torch.cuda.synchronize()
+    return H, alpha, y
+
+
+# Token counts that give the resident-token FP8 product enough token tiles
+# (at most a quarter of the 256-column passes per workgroup), each with a
+# ragged last tile, at every K it is built for.
+RESIDENT_CASES = [
+    ("K1024 M4", lambda: inputs.make_config(2, B=2, T=3500, rows_per_table=997)),
+    ("K512 M4", lambda: inputs.make_config(2, B=2, T=3500, rows_per_table=997, table_dim=32)),
+    ("K768 M2", lambda: inputs.make_shape(1, 11000, heads=6, dim=64, d=1024, branches=2)),
+    ("K256 M3", lambda: inputs.make_shape(2, 8200, heads=4, dim=32, d=512, branches=3)),
+]
+
+
+@pytest.mark.parametrize("name,make", RESIDENT_CASES, ids=[c[0] for c in RESIDENT_CASES])
+def test_resident_fp8_product_is_bit_identical(name, make):
+    """With the packed W, multi-branch FP8 layers run the resident-token
+    product, whose v and gate sums are formed in the same order as the 128 x
+    256 tile kernel's: H, alpha and Y equal the layer without the packed W
+    bit for bit, and match the oracle's MXFP8 forward.  A packed W of zeros
+    changes the result, so the packed path is the one that ran."""
+    log(f"resident fp8 product {name}")
+    w = make()
+    lay = w.layers[0]
+    L = eg.Layer(lay, "bf16", DEV, mxfp8=True)
+    assert L.w_mx_packed is not None
+    L0 = eg.Layer(lay, "bf16", DEV, mxfp8=True, mx_packed=False)
+    H, alpha, y = _forward(w, L)
+    H0, alpha0, y0 = _forward(w, L0)
+    assert torch.equal(H, H0) and torch.equal(alpha, alpha0) and torch.equal(y, y0), name
+    zero = torch.zeros_like(L.w_mx_packed)
+    L.s.w_mx_packed = zero.data_ptr()
+    Hz, _, _ = _forward(w, L)
+    assert not torch.equal(Hz, H0), f"{name}: the packed W was not read"
+    L.s.w_mx_packed = L.w_mx_packed.data_ptr()
+    log(f"{name}: oracle")
+    ref = orc.forward(w.tokens, w.H, lay, "bf16", gemm="mxfp8")
+    check_bf16_layer(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.bf16_to_f64(w.H),
+                     tag=f"resident {name}")
