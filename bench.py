@@ -327,7 +327,7 @@ KERNEL_SOURCES = {
                               ["gather.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
     "gather_kernel<hashed,hot>": (r"hashed_gather_kernel<[^>]*true, \d>",
                                   ["gather.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
-    "proj_gate_kernel": (r"proj_gate(_small)?_kernel<", ["proj_gate.hip"]),
+    "proj_gate_kernel": (r"proj_gate(_small|_mx_resident)?_kernel<", ["proj_gate.hip"]),
     "conv_kernel": (r"conv_(strip_)?kernel<", ["gate_conv.hip"]),
     "conv_gather_kernel": (r"conv_gather_kernel<",
                            ["gate_conv.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
