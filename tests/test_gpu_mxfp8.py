@@ -193,3 +193,36 @@ def test_resident_fp8_product_is_bit_identical(name, make):
     ref = orc.forward(w.tokens, w.H, lay, "bf16", gemm="mxfp8")
     check_bf16_layer(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.bf16_to_f64(w.H),
                      tag=f"resident {name}")
+
+
+def test_resident_fp8_decode_with_state_is_bit_identical():
+    """A multi-branch FP8 decode over 6,600 sequences (a 3-token prefill, then
+    single tokens) runs the resident-token product, the single-token steps
+    with the decode state's advance folded into that launch: H, alpha, Y and
+    the whole state equal the run without the packed W bit for bit, and the
+    first sequences match the oracle carrying the same state."""
+    S, T = 6600, 5
+    log(f"resident fp8 decode S={S}")
+    w = inputs.make_config(2, B=S, T=T, rows_per_table=997)
+    lay = w.layers[0]
+    M, d = lay.branches, lay.d
+    L = eg.Layer(lay, "bf16", DEV, mxfp8=True)
+    L0 = eg.Layer(lay, "bf16", DEV, mxfp8=True, mx_packed=False)
+    st, st0 = eg.DecodeState(S, 3, M, 9, d, DEV), eg.DecodeState(S, 3, M, 9, d, DEV)
+    ns = 4
+    ost = orc.new_state(ns, 3, M, 9, d)
+    chunks = [(0, 3), (3, 4), (4, 5)]
+    for a, b in chunks:
+        tok = torch.from_numpy(np.ascontiguousarray(w.tokens[:, a:b])).to(DEV)
+        Hn = np.ascontiguousarray(w.H[:, a:b])
+        H, H0 = eg.to_device(Hn, "bf16", DEV), eg.to_device(Hn, "bf16", DEV)
+        alpha, y = eg.forward(tok, H, L, state=st, want_alpha=True, want_y=True)
+        alpha0, y0 = eg.forward(tok, H0, L0, state=st0, want_alpha=True, want_y=True)
+        torch.cuda.synchronize()
+        tag = f"tokens {a}..{b}"
+        assert torch.equal(H, H0) and torch.equal(alpha, alpha0) and torch.equal(y, y0), tag
+        assert torch.equal(st.ids, st0.ids) and torch.equal(st.conv, st0.conv) and torch.equal(st.pos, st0.pos), tag
+        ref = orc.forward(w.tokens[:ns, a:b], Hn[:ns], lay, "bf16", state=ost, gemm="mxfp8")
+        ost = ref["state"]
+        check_bf16_layer(to_f64(alpha[:ns]), ref["alpha"], to_f64(y[:ns]), ref["Y"], to_f64(H[:ns]),
+                         orc.bf16_to_f64(Hn[:ns]), tag=f"resident decode {tag}")
