@@ -83,8 +83,12 @@ def parse(argv=None):
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                          "run with --copy-calibration-mib into the per-kernel HBM bytes table and exit")
     ap.add_argument("--no-layer-prefetch", action="store_true",
-                    help="config 3: run each layer as a plain engram_forward instead of carrying the next layer's "
-                         "retrieval in the conv launch (engram_forward_retrieved_prefetch)")
+                    help="config 3: the same as --decode-schedule plain")
+    ap.add_argument("--decode-schedule", choices=["ahead", "prefetch", "plain"], default="ahead",
+                    help="config 3: 'ahead' runs both layers' Steps 1-5 in two launches (engram_project_ahead) and "
+                         "each layer's Steps 6-8 in one (engram_forward_projected); 'prefetch' carries the next "
+                         "layer's retrieval in the conv launch (engram_forward_retrieved_prefetch); 'plain' is "
+                         "engram_forward per layer")
     ap.add_argument("--no-controls", action="store_true",
                     help="configs 1-2: skip the control measurements (one batch replayed, a cold-cache pass that "
                          "overwrites 512 MiB between steps, and the gather over uniform tokens)")
@@ -152,6 +156,11 @@ def kernel_units(n_tok, lay, hdtype, hot_hit=None, mx=False):
         "conv_kernel": ("hbm", n_tok * (d * 4 + 16 * n_stat + M * (2 * d * es + 8))),
         # v and gamma in; conv input of the newest position out; ids, pos
         "state_commit_kernel": ("hbm", n_tok * (d * 4 + M * (d * 4 + 4) + 16)),
+        # two identical layers per launch (engram_project_ahead): both layers'
+        # gathers; both layers' small-batch products (W and e in, the float32
+        # product out)
+        "gather2_kernel": ("hbm", 2 * n_tok * (4 + nt * (row_bytes + e_bytes))),
+        "proj_kv_kernel": ("hbm", 2 * (N * d_mem * op + n_tok * (d_mem * op + N * 4))),
     }
     if hot_hit is not None:
         K = lay.hash.heads
@@ -261,10 +270,19 @@ def build_case(args, cfg, torch, eg, inputs, w=None, per_graph=10, hot_host=None
             [eg.to_device(inputs.hidden_batch(3, i, w.H.shape), "bf16", dev) for i in range(1, ring)]
         wss = [torch.empty(eg.forward_workspace(S, 1, L), dtype=torch.uint8, device=dev) for L in Ls]
         es = [eg.rows_buffer(S, 1, L, dev) for L in Ls]
+        schedule = "plain" if args.no_layer_prefetch else args.decode_schedule
+        kvs = [eg.kv_buffer(S, 1, L, dev) for L in Ls]
+        ws_ahead = torch.empty(max(eg.project_ahead_workspace(S, 1, Ls), 256), dtype=torch.uint8, device=dev)
 
         def calls(i):
             tok, H = toks[i % ring], Hs[i % ring]
-            if args.no_layer_prefetch:
+            if schedule == "ahead":
+                # both layers' Steps 1-5 as soon as the token is known, then
+                # each layer's Steps 6-8 on its hidden state
+                return [lambda: eg.project_ahead(tok, Ls, kv=kvs, states=states, ws=ws_ahead)] + \
+                    [(lambda j=j: eg.forward_projected(kvs[j], H, Ls[j], S, 1, state=states[j], ws=wss[j]))
+                     for j in range(len(Ls))]
+            if schedule == "plain":
                 return [(lambda L=L, st=st, ws=ws: eg.forward(tok, H, L, state=st, ws=ws))
                         for L, st, ws in zip(Ls, states, wss)]
 
@@ -279,11 +297,14 @@ def build_case(args, cfg, torch, eg, inputs, w=None, per_graph=10, hot_host=None
             return [lambda: eg.retrieve(tok, Ls[0], es[0], state=states[0])] + \
                 [(lambda j=j: layer(j)) for j in range(len(Ls))]
         case = Case(w, w.layers, S, len(Ls), ring, calls)
-        case.extra["decode"] = "256 sequences x 1 token, 2 layers, after a 16-token prefill" + \
-            ("" if args.no_layer_prefetch else "; layer 1's retrieval runs inside layer 0's conv launch")
+        case.extra["decode"] = "256 sequences x 1 token, 2 layers, after a 16-token prefill" + {
+            "plain": "; engram_forward per layer",
+            "prefetch": "; layer 1's retrieval runs inside layer 0's conv launch",
+            "ahead": "; both layers' Steps 1-5 in two launches ahead of the hidden states, then one gate+conv "
+                     "launch per layer"}[schedule]
         case.extra["rotation"] = {"token_batches": ring, "hidden_batches": ring,
                                   "table_row_bytes_per_batch": rows_per_batch(w.layers, S)}
-        case.keep = [Ls, states, toks, Hs, wss, es]
+        case.keep = [Ls, states, toks, Hs, wss, es, kvs, ws_ahead]
         return case
     # cfg == 4: host tables + HBM cache
     w = w if w is not None else inputs.make_config(4)
@@ -328,6 +349,8 @@ KERNEL_SOURCES = {
     "gather_kernel<hashed,hot>": (r"hashed_gather_kernel<[^>]*true, \d>",
                                   ["gather.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
     "proj_gate_kernel": (r"proj_gate(_small|_mx_resident)?_kernel<", ["proj_gate.hip"]),
+    "gather2_kernel": (r"hashed_gather2_kernel<", ["gather.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
+    "proj_kv_kernel": (r"proj_gate_small2_kernel<", ["proj_gate.hip"]),
     "conv_kernel": (r"conv_(strip_)?kernel<", ["gate_conv.hip"]),
     "conv_gather_kernel": (r"conv_gather_kernel<",
                            ["gate_conv.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),

@@ -850,6 +850,235 @@ ENGRAM_API engram_status engram_forward_retrieved_prefetch(const int32_t* tokens
   return run_compute(tokens, e, H, B, T, L, g, st, alpha_out, y_out, f, stream, n_next > 0 ? &job : nullptr);
 }
 
+// ---- Steps 1-5 ahead of the hidden states ----
+
+namespace {
+
+size_t ahead_ws_bytes(int64_t n_tok, int32_t n_layers, const engram_layer* const* layers) {
+  Carve c{nullptr};
+  for (int l = 0; l < n_layers; ++l) c.take<char>(rows_bytes(n_tok, layers[l]));
+  return c.used;
+}
+
+// The gather job of one layer (cold rows; the hot tier is not supported here).
+engram::GatherJob gather_job(const int32_t* tokens, int64_t T, int64_t n_tok, const engram_layer* L,
+                             const engram::HashArgs& ha, const engram::TableArgs& ta, int hdtype,
+                             const engram_decode_state* st, void* e) {
+  engram::GatherJob j{};
+  j.ta = ta;
+  j.hs = engram::HashSrc{tokens, L->hash.proj, st != nullptr ? st->ids : nullptr, T, ha, engram::HotArgs{}};
+  j.e = e;
+  j.n_tok = static_cast<uint32_t>(n_tok);
+  j.out_dtype = L->w_mx != nullptr ? engram::kGatherOutMXFP8 : hdtype;
+  j.hot = false;
+  return j;
+}
+
+}  // namespace
+
+ENGRAM_API size_t engram_project_ahead_workspace(int64_t B, int64_t T, int32_t n_layers,
+                                                 const engram_layer* const* layers) {
+  if (layers == nullptr || B < 0 || T < 0 || n_layers < 1 || n_layers > ENGRAM_MAX_AHEAD_LAYERS) return 0;
+  for (int l = 0; l < n_layers; ++l)
+    if (layers[l] == nullptr || layers[l]->tables.n_tables < 1) return 0;
+  return ahead_ws_bytes(B * T, n_layers, layers);
+}
+
+ENGRAM_API engram_status engram_project_ahead(const int32_t* tokens, int64_t B, int64_t T, int32_t n_layers,
+                                              const engram_layer* const* layers, engram_decode_state* const* states,
+                                              float* const* kv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (n_layers < 1 || n_layers > ENGRAM_MAX_AHEAD_LAYERS)
+    return fail(ENGRAM_EINVAL, "project_ahead: n_layers must be 1..%d", ENGRAM_MAX_AHEAD_LAYERS);
+  if (layers == nullptr || kv == nullptr) return fail(ENGRAM_EINVAL, "project_ahead: layers and kv must be non-NULL");
+  engram::HashArgs ha[ENGRAM_MAX_AHEAD_LAYERS];
+  engram::TableArgs ta[ENGRAM_MAX_AHEAD_LAYERS];
+  engram::GateConvArgs g[ENGRAM_MAX_AHEAD_LAYERS];
+  const int64_t n_tok = B * T;
+  engram_status r;
+  for (int l = 0; l < n_layers; ++l) {
+    const engram_layer* L = layers[l];
+    if (L == nullptr) return fail(ENGRAM_EINVAL, "project_ahead: layers[%d] is NULL", l);
+    engram_decode_state* st = states != nullptr ? states[l] : nullptr;
+    if (states != nullptr && st == nullptr)
+      return fail(ENGRAM_EINVAL, "project_ahead: states[%d] is NULL (give a state for every layer or none)", l);
+    if ((r = check_call("project_ahead", L, st, true, B, T, &ha[l], &ta[l], &g[l])) != ENGRAM_OK) return r;
+    if (!use_fused(L))
+      return fail(ENGRAM_EUNSUPPORTED, "project_ahead: layer %d needs bf16 H, d a multiple of 128 up to 4096", l);
+    if (L->hot != nullptr) return fail(ENGRAM_EUNSUPPORTED, "project_ahead: layer %d has a hot tier", l);
+    if (st != nullptr && T != 1) return fail(ENGRAM_EUNSUPPORTED, "project_ahead: with decode states T must be 1");
+    if (n_tok > 0 && (kv[l] == nullptr || !aligned(kv[l], 16)))
+      return fail(ENGRAM_EINVAL, "project_ahead: kv[%d] must be non-NULL and 16-byte aligned", l);
+  }
+  if (n_tok == 0) return ENGRAM_OK;
+  if (tokens == nullptr) return fail(ENGRAM_EINVAL, "project_ahead: tokens must be non-NULL");
+  if (n_tok >= (int64_t{1} << 31))
+    return fail(ENGRAM_EUNSUPPORTED, "project_ahead: B*T = %lld tokens, above 2^31-1 per call",
+                static_cast<long long>(n_tok));
+  const size_t need = ahead_ws_bytes(n_tok, n_layers, layers);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(ENGRAM_EINVAL, "project_ahead: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  // the product of each layer, and whether it takes the small-batch kernel
+  engram::ProjGateArgs pa[ENGRAM_MAX_AHEAD_LAYERS];
+  bool small[ENGRAM_MAX_AHEAD_LAYERS];
+  void* e[ENGRAM_MAX_AHEAD_LAYERS];
+  Carve c{static_cast<char*>(ws)};
+  for (int l = 0; l < n_layers; ++l) {
+    const engram_layer* L = layers[l];
+    engram_decode_state* st = states != nullptr ? states[l] : nullptr;
+    e[l] = c.take<char>(rows_bytes(n_tok, L));
+    const int64_t d_mem = static_cast<int64_t>(L->tables.n_tables) * L->tables.dim;
+    const int M = g[l].branches, d = g[l].d;
+    const bool mx = L->w_mx != nullptr;
+    engram::ProjGateArgs& p = pa[l];
+    p = engram::ProjGateArgs{};
+    p.e = static_cast<const uint16_t*>(e[l]);
+    p.w = static_cast<const uint16_t*>(mx ? static_cast<const void*>(L->w_mx) : L->w);
+    if (mx) {
+      p.e_scale = static_cast<const uint8_t*>(e[l]) + n_tok * d_mem;
+      p.w_scale = L->w_mx_scale;
+    }
+    p.kv_out = kv[l];
+    p.n_tok = n_tok;
+    p.K = static_cast<int>(d_mem);
+    p.N = static_cast<int>(static_cast<int64_t>(1 + M) * d);
+    p.d = d;
+    p.M = M;
+    if (st != nullptr) {
+      p.st_ids = st->ids;
+      p.st_pos = st->pos;
+      p.tokens = tokens;
+      p.proj = L->hash.proj;
+      p.vocab = static_cast<int32_t>(L->hash.vocab);
+      p.err = g_err_word.load();
+      p.max_n = L->hash.max_n;
+      p.adv_T = static_cast<int32_t>(T);
+      p.adv_B = static_cast<int32_t>(B);
+    }
+    small[l] = engram::proj_gate_small_for(n_tok, p.N, d, p.K, mx) && p.K % (mx ? 512 : 64) == 0;
+    if (!small[l] && (mx || st != nullptr))
+      return fail(ENGRAM_EUNSUPPORTED,
+                  "project_ahead: layer %d's product (%lld tokens x %d columns) is above the small-batch range, which "
+                  "MXFP8 layers and decode states need",
+                  l, static_cast<long long>(n_tok), p.N);
+  }
+  prof_begin();
+  for (int l = 0; l < n_layers; l += 2) {
+    const bool pair = l + 1 < n_layers;
+    // Steps 1-4 of the pair in one launch where the formats match
+    const engram::GatherJob ja = gather_job(tokens, T, n_tok, layers[l], ha[l], ta[l], g[l].hdtype,
+                                            states != nullptr ? states[l] : nullptr, e[l]);
+    bool gathered = false;
+    if (pair) {
+      const engram::GatherJob jb = gather_job(tokens, T, n_tok, layers[l + 1], ha[l + 1], ta[l + 1], g[l + 1].hdtype,
+                                              states != nullptr ? states[l + 1] : nullptr, e[l + 1]);
+      prof_mark(stream, "gather2_kernel");
+      const hipError_t he = engram::launch_hash_gather2(ja, jb, stream);
+      if (he != hipErrorNotSupported) {
+        if ((r = hip_status(he, "two-layer gather launch")) != ENGRAM_OK) return r;
+        gathered = true;
+      }
+    }
+    if (!gathered) {
+      for (int k = l; k < l + (pair ? 2 : 1); ++k) {
+        engram_decode_state* st = states != nullptr ? states[k] : nullptr;
+        if ((r = run_retrieve(tokens, B, T, layers[k], ha[k], ta[k], g[k].hdtype, st, e[k], stream)) != ENGRAM_OK)
+          return r;
+      }
+    }
+    // Step 5 of the pair
+    if (small[l] && (!pair || small[l + 1])) {
+      prof_mark(stream, "proj_kv_kernel");
+      const hipError_t he = engram::launch_project_layers(pa[l], pair ? &pa[l + 1] : nullptr, stream);
+      if (he != hipErrorNotSupported) {
+        if ((r = hip_status(he, "projection launch")) != ENGRAM_OK) return r;
+        continue;
+      }
+    }
+    for (int k = l; k < l + (pair ? 2 : 1); ++k) {
+      if (small[k]) {
+        prof_mark(stream, "proj_kv_kernel");
+        r = hip_status(engram::launch_project_layers(pa[k], nullptr, stream), "projection launch");
+      } else {
+        prof_mark(stream, "gemm_kernel");
+        r = hip_status(engram::launch_project_kv(e[k], layers[k]->w, n_tok, pa[k].K, pa[k].N, ENGRAM_BF16, ENGRAM_F32,
+                                                 kv[k], stream),
+                       "project_kv launch");
+      }
+      if (r != ENGRAM_OK) return r;
+    }
+  }
+  prof_mark(stream, nullptr);
+  return ENGRAM_OK;
+}
+
+ENGRAM_API size_t engram_forward_projected_workspace(int64_t B, int64_t T, const engram_layer* L) {
+  if (L == nullptr || B < 0 || T < 0 || L->gc.branches < 1) return 0;
+  return gc_ws_bytes(B * T, L->gc.branches);
+}
+
+ENGRAM_API engram_status engram_forward_projected(const float* kv, void* H, int64_t B, int64_t T,
+                                                  const engram_layer* L, engram_decode_state* st, float* alpha_out,
+                                                  float* y_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  engram::HashArgs ha;
+  engram::TableArgs ta;
+  engram::GateConvArgs g;
+  engram_status r = check_call("forward_projected", L, st, false, B, T, &ha, &ta, &g);
+  if (r != ENGRAM_OK) return r;
+  if (!use_fused(L))
+    return fail(ENGRAM_EUNSUPPORTED, "forward_projected: the layer needs bf16 H, d a multiple of 128 up to 4096");
+  const int64_t n_tok = B * T;
+  const int M = g.branches, d = g.d;
+  // one launch: a single-token chunk whose rows fit one conv workgroup
+  const bool one = T == 1 && d <= 1024 && g.kernel_w == 4 && g.dilation == 3;
+  if (st != nullptr && !one)
+    return fail(ENGRAM_EUNSUPPORTED,
+                "forward_projected: with a decode state, T = 1, d <= 1024 and the conv w = 4, dilation 3");
+  if (n_tok == 0) return ENGRAM_OK;
+  if (kv == nullptr || H == nullptr) return fail(ENGRAM_EINVAL, "forward_projected: kv and H must be non-NULL");
+  if (!aligned(H, 16) || !aligned(kv, 16)) return fail(ENGRAM_EINVAL, "forward_projected: H and kv must be 16-byte aligned");
+  if (y_out != nullptr && !aligned(y_out, 16))
+    return fail(ENGRAM_EINVAL, "forward_projected: y_out must be 16-byte aligned");
+  const size_t need = gc_ws_bytes(n_tok, M);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256))
+    return fail(ENGRAM_EINVAL, "forward_projected: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                ws_bytes);
+  Carve c{static_cast<char*>(ws)};
+  const GcWorkspace w = carve_gc(c, n_tok, M);
+  const int64_t n_out = static_cast<int64_t>(1 + M) * d;
+  g.kvdtype = ENGRAM_F32;
+  prof_begin();
+  if (one) {
+    engram::ConvArgs ca{};
+    ca.H = H;
+    ca.v = kv;
+    ca.v_stride = n_out;
+    ca.qv = 1;
+    ca.qk = 1;
+    ca.kq0 = 1;
+    ca.nq = 1 + M;
+    ca.B = B;
+    ca.T = T;
+    ca.g = g;
+    ca.has_state = st != nullptr;
+    if (st != nullptr) ca.st = engram::StateArgs{st->ids, st->conv, st->pos};
+    ca.pos_advanced = st != nullptr;   // advanced by engram_project_ahead
+    ca.commit_u = st != nullptr;
+    ca.sums_from_kv = 1;
+    ca.alpha_out = alpha_out;
+    ca.gamma_out = w.gamma;
+    ca.y_out = y_out;
+    prof_mark(stream, "conv_kernel");
+    r = hip_status(engram::launch_conv(ca, ENGRAM_F32, stream), "conv launch");
+    prof_mark(stream, nullptr);
+    return r;
+  }
+  prof_mark(stream, "gate_stats_kernel");
+  r = hip_status(engram::launch_gate_stats(H, kv, n_tok, g, w.stats, stream), "gate statistics launch");
+  if (r != ENGRAM_OK) return r;
+  return run_conv_commit(H, kv, n_out, ENGRAM_F32, w.stats, 1, 1, false, B, T, g, nullptr, nullptr, L->hash.proj,
+                         L->hash.max_n, static_cast<int32_t>(L->hash.vocab), alpha_out, w.gamma, y_out, stream);
+}
+
 ENGRAM_API size_t engram_cache_build_workspace(int64_t total_rows) {
   if (total_rows <= 0) return 0;
   return engram::cache_build_workspace(total_rows);

@@ -145,6 +145,10 @@ struct ProjGateArgs {
   // optional MXFP8 W in matrix-core fragment order (engram_pack_mxfp8): the
   // resident-token kernel streams it straight into registers
   const uint8_t* w_packed;
+  // small-batch kernel only: store every column of the product here
+  // ([n_tok][N] float32: v, then the keys) instead of v and the gate sums; H
+  // is then not read
+  float* kv_out;
   // Decode-state advance folded into this launch (adv_B > 0): workgroup 0
   // shifts the last N-1 compressed ids of every sequence's T = adv_T new
   // tokens into st_ids and adds adv_T to st_pos.  Nothing in the launch reads
@@ -164,6 +168,7 @@ constexpr int kProjGateTileF = 64;   // narrowest feature tile (bounds the stati
 // tiles plus one branch's key tiles, qv + qk <= kConvMaxStats.
 constexpr int kConvMaxStats = 64;
 int proj_gate_tile_f(int64_t n_tok, int N, int d, int K, bool mx);   // feature columns per gate-statistics tile
+bool proj_gate_small_for(int64_t n_tok, int N, int d, int K, bool mx);   // the small-batch kernel serves this product
 // Gate statistics of a projection launch: qv tiles feed v.v; qk tiles per
 // branch feed h.h, k.k, h.k (after the qv ones); mixed = every one of the
 // qv tiles feeds all four sums (qk = 0).
@@ -176,6 +181,11 @@ struct ProjGateLayout {
 };
 ProjGateLayout proj_gate_layout(int64_t n_tok, int N, int d, int K, int M, bool mx);
 hipError_t launch_proj_gate(const ProjGateArgs& a, hipStream_t s);
+// Step 5 of up to two layers into float32 rows (ProjGateArgs.kv_out set on
+// both) with the small-batch kernel, in one launch; hipErrorNotSupported
+// (nothing launched) when a layer's size or format does not take that kernel
+// or the two differ in format.  b may be null.
+hipError_t launch_project_layers(const ProjGateArgs& a, const ProjGateArgs* b, hipStream_t s);
 
 // Whole-row gate statistics from given projections: stats [n_tok][1+M].
 hipError_t launch_gate_stats(const void* H, const void* kv, int64_t n_tok, const GateConvArgs& g, float4* stats,
@@ -198,6 +208,8 @@ struct ConvArgs {
   int has_state;
   int pos_advanced;     // st.pos already holds pos + T (advanced by the projection launch)
   int commit_u;         // T = 1 strip conv: also write the new conv input u into the ring
+  int sums_from_kv;     // T = 1 strip conv on float32 [v | k^(0..M-1)] rows (v_stride = (1+M)d, d <= 1024):
+                        // the gate sums come from the rows themselves, stats is unused
   float* alpha_out;     // [B*T][M] or null
   float* gamma_out;     // [B*T][M] or null
   float* y_out;         // [B][T][M][d] or null
@@ -219,6 +231,10 @@ struct GatherJob {
 // The strip conv of a with gj's gather in one launch; hipErrorNotSupported
 // (nothing launched) when the pair has no fused form.
 hipError_t launch_conv_gather(const ConvArgs& a, int vdtype, const GatherJob& gj, hipStream_t s);
+// Two hashed gathers (no hot tier, one table and row format) in one launch;
+// hipErrorNotSupported (nothing launched) otherwise.  The two jobs travel in
+// the kernel-argument segment (about 4.4 KiB).
+hipError_t launch_hash_gather2(const GatherJob& a, const GatherJob& b, hipStream_t s);
 
 // Writes the chunk's last conv inputs into the circular state, shifts ids
 // (when tokens/proj are given) and advances pos.

@@ -422,6 +422,58 @@ __device__ __forceinline__ void conv_strip_body(const ConvArgs& a, int spx, int 
     }
   }
 
+  bool from_kv = false;
+  if constexpr (TS == 1) from_kv = a.sums_from_kv != 0;
+  if (from_kv) {
+    // ---- a single-token chunk on given float32 projections (v, then the M
+    // keys, in one row): the workgroup holds its token's whole row (d <=
+    // 256 * CPT, checked by the launcher), so it forms the gate's four sums
+    // itself, by a block reduction, instead of reading per-tile statistics.
+    // The halo rows are the state's conv inputs (gamma 1) or padding. ----
+    __shared__ float4 wsum[4];
+    float kk[CPT];
+    loadc<VT, CPT>(vseq, static_cast<uint32_t>((1 + m) * d) + cc, kk);
+    float s_hh = 0.f, s_kk = 0.f, s_hk = 0.f, s_vv = 0.f;
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        s_hh += h[0][i] * h[0][i];
+        s_kk += kk[i] * kk[i];
+        s_hk += h[0][i] * kk[i];
+        s_vv += v[SPAN][i] * v[SPAN][i];
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      s_hh += __shfl_xor(s_hh, off, 64);
+      s_kk += __shfl_xor(s_kk, off, 64);
+      s_hk += __shfl_xor(s_hk, off, 64);
+      s_vv += __shfl_xor(s_vv, off, 64);
+    }
+    if ((tid & 63) == 0) wsum[tid >> 6] = make_float4(s_hh, s_kk, s_hk, s_vv);
+    __syncthreads();
+    if (tid < R) {
+      float al = 0.f, gm = 0.f;
+      if (tid == SPAN) {
+        float4 q = wsum[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) q = make_float4(q.x + wsum[w].x, q.y + wsum[w].y, q.z + wsum[w].z, q.w + wsum[w].w);
+        const float inv_d = 1.0f / static_cast<float>(d);
+        const float rh = 1.0f / sqrtf(q.x * inv_d + g.eps);
+        const float rk = 1.0f / sqrtf(q.y * inv_d + g.eps);
+        const float logit = q.z * rh * rk / sqrtf(static_cast<float>(d));
+        al = 1.0f / (1.0f + expf(-logit));
+        gm = al / sqrtf(al * al * (q.w * inv_d) + g.eps);
+        const int64_t o = row0 * M + m;
+        if (a.alpha_out != nullptr) a.alpha_out[o] = al;
+        if (a.gamma_out != nullptr) a.gamma_out[o] = gm;
+      } else if (a.has_state) {
+        gm = 1.0f;  // the state holds u itself
+      }
+      alpha_s[tid] = al;
+      gamma_s[tid] = gm;
+    }
+  } else {
   // ---- alpha and gamma of the R rows: 16 lanes per row, shuffle reduction.
   // A lane loads up to kMaxQ statistics per pass (nqb <= 16 * kMaxQ = 64); all
   // passes' loads are issued before any is used. ----
@@ -486,6 +538,7 @@ __device__ __forceinline__ void conv_strip_body(const ConvArgs& a, int spx, int 
       alpha_s[r] = al;
       gamma_s[r] = gm;
     }
+  }
   }
   __syncthreads();
 
@@ -744,6 +797,11 @@ hipError_t launch_conv_gather(const ConvArgs& a, int vdtype, const GatherJob& gj
 
 hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
+  if (a.sums_from_kv) {
+    // the single-token strip conv with the whole row in one workgroup
+    if (conv_strip_ts(a) != 1 || a.g.d > 256 * 4 || vdtype != ENGRAM_F32) return hipErrorInvalidValue;
+    return launch_conv_strip<4, 3, 1, 4>(a, vdtype, s);
+  }
   // both conv kernels stage at most kConvMaxStats statistics per row (the
   // projection launchers never produce more)
   if (a.qv < 1 || (a.qk < 1 && !a.mixed) || (a.mixed && a.qk != 0) || a.qv + a.qk > kConvMaxStats)

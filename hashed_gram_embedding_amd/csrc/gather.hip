@@ -80,6 +80,40 @@ hashed_gather_kernel(uint32_t n_tok, TableArgs ta, void* __restrict__ e, HashSrc
   hashed_gather_body<IN, OUT, HOT, ITEMS>(blockIdx.x * blockDim.x + threadIdx.x, n_tok, ta, e, hs);
 }
 
+// Two layers' hashed gathers in one launch (the retrieval of several layers
+// ahead of their hidden states): workgroups below split serve job a, the rest
+// job b.  Both have the same table and row formats.
+template <int IN, int OUT, int ITEMS>
+__global__ void __launch_bounds__(256)
+hashed_gather2_kernel(GatherJob a, GatherJob b, uint32_t split) {
+  if (blockIdx.x < split)
+    hashed_gather_body<IN, OUT, false, ITEMS>(blockIdx.x * blockDim.x + threadIdx.x, a.n_tok, a.ta, a.e, a.hs);
+  else
+    hashed_gather_body<IN, OUT, false, ITEMS>((blockIdx.x - split) * blockDim.x + threadIdx.x, b.n_tok, b.ta, b.e,
+                                              b.hs);
+}
+
+template <int IN, int OUT>
+hipError_t launch_gather2_t(const GatherJob& a, const GatherJob& b, hipStream_t s) {
+  // one item count for both (layer a's choice; any count is correct)
+  const int items = gather_items(a.n_tok, static_cast<int64_t>(a.ta.n_tables) * (a.ta.dim / 8));
+  auto blocks = [&](const GatherJob& j) {
+    const int64_t per_group = static_cast<int64_t>(j.ta.n_tables) * (j.ta.dim / 8);
+    return ((static_cast<int64_t>(j.n_tok) + items - 1) / items * per_group + 255) / 256;
+  };
+  const int64_t na = blocks(a), nb = blocks(b);
+  if (na + nb >= (int64_t{1} << 31) / 256) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(na + nb));
+  const uint32_t split = static_cast<uint32_t>(na);
+  if (items == 4)
+    launch_k((hashed_gather2_kernel<IN, OUT, 4>), grid, dim3(256), 0, s, a, b, split);
+  else if (items == 2)
+    launch_k((hashed_gather2_kernel<IN, OUT, 2>), grid, dim3(256), 0, s, a, b, split);
+  else
+    launch_k((hashed_gather2_kernel<IN, OUT, 1>), grid, dim3(256), 0, s, a, b, split);
+  return hipGetLastError();
+}
+
 template <int IN>
 hipError_t launch_in(const int32_t* z, int64_t n_tok, const TableArgs& ta, int out, void* e, hipStream_t s) {
   const int64_t total = n_tok * ta.n_tables * (ta.dim / 8);
@@ -119,7 +153,24 @@ hipError_t launch_hashed(int64_t n_tok, const TableArgs& ta, int out, void* e, c
   return launch_hashed_items<IN, ENGRAM_F32, HOT>(n_tok, ta, e, hs, s);
 }
 
+template <int IN>
+hipError_t launch_gather2_in(const GatherJob& a, const GatherJob& b, hipStream_t s) {
+  if (a.out_dtype == kOutMXFP8) return launch_gather2_t<IN, kOutMXFP8>(a, b, s);
+  if (a.out_dtype == ENGRAM_BF16) return launch_gather2_t<IN, ENGRAM_BF16>(a, b, s);
+  return launch_gather2_t<IN, ENGRAM_F32>(a, b, s);
+}
+
 }  // namespace
+
+hipError_t launch_hash_gather2(const GatherJob& a, const GatherJob& b, hipStream_t s) {
+  if (a.hot || b.hot || a.ta.dtype != b.ta.dtype || a.out_dtype != b.out_dtype) return hipErrorNotSupported;
+  if (a.n_tok == 0 && b.n_tok == 0) return hipSuccess;
+  switch (a.ta.dtype) {
+    case ENGRAM_BF16: return launch_gather2_in<ENGRAM_BF16>(a, b, s);
+    case ENGRAM_F32: return launch_gather2_in<ENGRAM_F32>(a, b, s);
+    default: return launch_gather2_in<ENGRAM_I8>(a, b, s);
+  }
+}
 
 hipError_t launch_gather(const int32_t* z, int64_t n_tok, const TableArgs& ta, int out_dtype,
                          void* e, hipStream_t s) {

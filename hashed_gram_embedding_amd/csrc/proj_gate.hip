@@ -62,8 +62,8 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk
 
 // Decode-state advance (ProjGateArgs.adv_B > 0), by the threads of
 // workgroup 0: ids <- last N-1 of (ids ++ P(tokens)), pos += T.
-__device__ __forceinline__ void advance_state(const ProjGateArgs& a) {
-  if (a.adv_B <= 0 || blockIdx.x != 0) return;
+__device__ __forceinline__ void advance_state(const ProjGateArgs& a, uint32_t bid) {
+  if (a.adv_B <= 0 || bid != 0) return;
   const int hl = a.max_n - 1;
   for (int b = threadIdx.x; b < a.adv_B; b += blockDim.x) {
     int32_t next[ENGRAM_MAX_ORDER];
@@ -423,7 +423,7 @@ proj_gate_kernel(ProjGateArgs a) {
       a.stats[tok * a.tiles_f + tf] = p;
     }
   }
-  advance_state(a);
+  advance_state(a, blockIdx.x);
 }
 
 // Small batches (decode): a 64-feature x 32-token tile per workgroup, so that
@@ -443,29 +443,33 @@ constexpr int kSmallTK = 32;
 constexpr int kSmallWaves = 4;
 constexpr int kSmallBatch = 4;   // K16 steps per load batch
 
-// one wavefront's staging buffer: 64 W rows and 32 e rows of a batch's
-// 128-byte run, chunk c of row r at slot c ^ (r & 7)
-constexpr int kSmallRows = kSmallTF + kSmallTK;
+// one wavefront's staging buffer: 64 W rows and STK (32, or 64 for the
+// float32-output launch of two layers) e rows of a batch's 128-byte run,
+// chunk c of row r at slot c ^ (r & 7)
+template <int STK>
+constexpr int small_rows() { return kSmallTF + STK; }
 // (MXFP8: the 128-byte run is 128 codes, and the rows' scale words of the
-// batch follow, 128 words, the last 32 re-reading a valid row)
-template <bool MX>
-constexpr int small_stage() { return kSmallRows * 8 + (MX ? 128 / 4 : 0); }   // 16-byte slots per buffer
-template <bool MX>
-constexpr int small_lds_bytes() { return kSmallWaves * 2 * small_stage<MX>() * 16; }   // staging bytes (reused for the partial sums)
+// batch follow, 128 words, re-reading a valid row past the last)
+template <bool MX, int STK = kSmallTK>
+constexpr int small_stage() { return small_rows<STK>() * 8 + (MX ? 128 / 4 : 0); }   // 16-byte slots per buffer
+template <bool MX, int STK = kSmallTK>
+constexpr int small_lds_bytes() { return kSmallWaves * 2 * small_stage<MX, STK>() * 16; }   // staging bytes (reused for the partial sums)
 
-template <bool MX>
-__global__ void __launch_bounds__(64 * kSmallWaves)
-proj_gate_small_kernel(ProjGateArgs a) {
-  constexpr int kSmallStage = small_stage<MX>();
+template <bool MX, int STK = kSmallTK>
+__device__ __forceinline__ void proj_gate_small_body(const ProjGateArgs& a, uint32_t bid) {
+  static_assert(STK == kSmallTK || STK == 2 * kSmallTK, "32 or 64 tokens per tile");
+  constexpr int kSmallRows = small_rows<STK>();
+  constexpr int JB = STK / 32;                 // 32-token blocks of the tile
+  constexpr int kSmallStage = small_stage<MX, STK>();
   extern __shared__ u32x4_t small_lds_buf[];
   u32x4_t* small_lds = small_lds_buf;
   // after the main loop: the partial tiles, +1 column so that the sums are conflict free
-  auto part = reinterpret_cast<float (*)[kSmallTF][kSmallTK + 1]>(small_lds);
-  static_assert(kSmallWaves * kSmallTF * (kSmallTK + 1) * 4 <= small_lds_bytes<MX>(), "partial sums fit the staging LDS");
-  const int tf = blockIdx.x % a.tiles_f;
-  const int tt = blockIdx.x / a.tiles_f;
+  auto part = reinterpret_cast<float (*)[kSmallTF][STK + 1]>(small_lds);
+  static_assert(kSmallWaves * kSmallTF * (STK + 1) * 4 <= small_lds_bytes<MX, STK>(), "partial sums fit the staging LDS");
+  const int tf = bid % a.tiles_f;
+  const int tt = bid / a.tiles_f;
   const int f0 = tf * kSmallTF;
-  const int64_t t0 = static_cast<int64_t>(tt) * kSmallTK;
+  const int64_t t0 = static_cast<int64_t>(tt) * STK;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int K = a.K;
@@ -488,11 +492,13 @@ proj_gate_small_kernel(ProjGateArgs a) {
   const int m = is_v ? 0 : f0 / d - 1;
   const int c0 = (is_v ? f0 : f0 - (1 + m) * d) + fq * 8;
   uint4 hq = make_uint4(0u, 0u, 0u, 0u);
-  if (!is_v) hq = *reinterpret_cast<const uint4*>(a.H + (ct * a.M + m) * d + c0);
+  if (!is_v && a.kv_out == nullptr) hq = *reinterpret_cast<const uint4*>(a.H + (ct * a.M + m) * d + c0);
 
-  f32x16_t acc0, acc1;
+  f32x16_t acc0[JB], acc1[JB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+  for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc0[jb][r] = acc1[jb][r] = 0.f;
 
   // Batch b covers K elements [b*64, b*64 + 64) of this wavefront's range:
   // 12 instructions, 8 rows each (lane l: row 8i + (l >> 3), slot l & 7,
@@ -541,11 +547,9 @@ proj_gate_small_kernel(ProjGateArgs a) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (b + 1 < nb) {
           issue(b + 1, u ^ 1);
-          // batch b has landed, b + 1 (12 or, with scale words, 14 loads) in flight
-          if constexpr (MX)
-            asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
-          else
-            asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+          // batch b has landed, b + 1 (a load per 8 rows, two more for the
+          // scale words) in flight
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSmallRows / 8 + (MX ? 2 : 0)) : "memory");
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
@@ -558,9 +562,13 @@ proj_gate_small_kernel(ProjGateArgs a) {
               const int c = 2 * j + half;          // this lane's chunk of the run
               const bf16x8_t fa0 = __builtin_bit_cast(bf16x8_t, sb[r * 8 + (c ^ (r & 7))]);
               const bf16x8_t fa1 = __builtin_bit_cast(bf16x8_t, sb[(32 + r) * 8 + (c ^ (r & 7))]);
-              const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, sb[(kSmallTF + r) * 8 + (c ^ (r & 7))]);
-              acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb, acc0, 0, 0, 0);
-              acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb, acc1, 0, 0, 0);
+#pragma unroll
+              for (int jb = 0; jb < JB; ++jb) {
+                const int er = kSmallTF + jb * 32 + r;
+                const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, sb[er * 8 + (c ^ (er & 7))]);
+                acc0[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb, acc0[jb], 0, 0, 0);
+                acc1[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb, acc1[jb], 0, 0, 0);
+              }
             }
           }
         } else {
@@ -568,19 +576,22 @@ proj_gate_small_kernel(ProjGateArgs a) {
           // run and block 2ks's scale, lane r + 32 bytes 16-31 and 48-63 and
           // block 2ks+1's (the large kernel's MXFP8 operand layout)
           const uint32_t* sw = reinterpret_cast<const uint32_t*>(sb + kSmallRows * 8);
-          const uint32_t wa0 = sw[r], wa1 = sw[32 + r], wb = sw[kSmallTF + r];
+          const uint32_t wa0 = sw[r], wa1 = sw[32 + r];
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             const int c0c = 4 * ks + half, c1c = 4 * ks + 2 + half;
             const i32x8_t fa0 = join16(sb[r * 8 + (c0c ^ (r & 7))], sb[r * 8 + (c1c ^ (r & 7))]);
             const i32x8_t fa1 = join16(sb[(32 + r) * 8 + (c0c ^ (r & 7))], sb[(32 + r) * 8 + (c1c ^ (r & 7))]);
-            const i32x8_t fb = join16(sb[(kSmallTF + r) * 8 + (c0c ^ (r & 7))],
-                                      sb[(kSmallTF + r) * 8 + (c1c ^ (r & 7))]);
             const int sh = 8 * (2 * ks + half);
             const int sa0 = static_cast<int>((wa0 >> sh) & 0xffu), sa1 = static_cast<int>((wa1 >> sh) & 0xffu);
-            const int sbb = static_cast<int>((wb >> sh) & 0xffu);
-            acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0, fb, acc0, 0, 0, 0, sa0, 0, sbb);
-            acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1, fb, acc1, 0, 0, 0, sa1, 0, sbb);
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) {
+              const int er = kSmallTF + jb * 32 + r;
+              const i32x8_t fb = join16(sb[er * 8 + (c0c ^ (er & 7))], sb[er * 8 + (c1c ^ (er & 7))]);
+              const int sbb = static_cast<int>((sw[er] >> sh) & 0xffu);
+              acc0[jb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0, fb, acc0[jb], 0, 0, 0, sa0, 0, sbb);
+              acc1[jb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1, fb, acc1[jb], 0, 0, 0, sa1, 0, sbb);
+            }
           }
         }
       }
@@ -589,15 +600,40 @@ proj_gate_small_kernel(ProjGateArgs a) {
   // every wavefront's fragment reads are done before the partial sums reuse the LDS
   __syncthreads();
 
-  // acc_i[4g + r]: feature i*32 + g*8 + half*4 + r of the tile, token lane & 31
+  // acc_i[jb][4g + r]: feature i*32 + g*8 + half*4 + r of the tile, token jb*32 + (lane & 31)
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      part[wave][g * 8 + half * 4 + r][lane & 31] = acc0[4 * g + r];
-      part[wave][32 + g * 8 + half * 4 + r][lane & 31] = acc1[4 * g + r];
-    }
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        part[wave][g * 8 + half * 4 + r][jb * 32 + (lane & 31)] = acc0[jb][4 * g + r];
+        part[wave][32 + g * 8 + half * 4 + r][jb * 32 + (lane & 31)] = acc1[jb][4 * g + r];
+      }
   __syncthreads();
+
+  if constexpr (JB == 2) {
+    // the float32 product only (engram_project_ahead): two tokens per thread
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+      const int tk = tl + 32 * tp;
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float sacc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kSmallWaves; ++w) sacc += part[w][fq * 8 + i][tk];
+        y[i] = sacc;
+      }
+      if (t0 + tk < a.n_tok) {
+        float4* kp = reinterpret_cast<float4*>(a.kv_out + (t0 + tk) * a.N + f0 + fq * 8);
+        kp[0] = make_float4(y[0], y[1], y[2], y[3]);
+        kp[1] = make_float4(y[4], y[5], y[6], y[7]);
+      }
+    }
+    advance_state(a, bid);
+    return;
+  }
 
   // thread (token tl, feature eighth fq): 8 features of one token, summed over the waves
   float x[8];
@@ -607,6 +643,16 @@ proj_gate_small_kernel(ProjGateArgs a) {
 #pragma unroll
     for (int w = 0; w < kSmallWaves; ++w) sacc += part[w][fq * 8 + i][tl];
     x[i] = sacc;
+  }
+  if (a.kv_out != nullptr) {
+    // the product's columns f0 + fq*8 .. +7 of this token, as they are
+    if (valid) {
+      float4* kp = reinterpret_cast<float4*>(a.kv_out + gt * a.N + f0 + fq * 8);
+      kp[0] = make_float4(x[0], x[1], x[2], x[3]);
+      kp[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+    advance_state(a, bid);
+    return;
   }
   float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
   if (is_v) {
@@ -636,7 +682,25 @@ proj_gate_small_kernel(ProjGateArgs a) {
     s3 += __shfl_xor(s3, off, 64);
   }
   if (fq == 0 && valid) a.stats[gt * a.tiles_f + tf] = make_float4(s0, s1, s2, s3);
-  advance_state(a);
+  advance_state(a, bid);
+}
+
+template <bool MX>
+__global__ void __launch_bounds__(64 * kSmallWaves)
+proj_gate_small_kernel(ProjGateArgs a) {
+  proj_gate_small_body<MX>(a, blockIdx.x);
+}
+
+// Two layers' small-batch products in one launch: workgroups below split
+// serve a, the rest b (each layer's first workgroup advances its decode
+// state).
+template <bool MX, int STK>
+__global__ void __launch_bounds__(64 * kSmallWaves)
+proj_gate_small2_kernel(ProjGateArgs a, ProjGateArgs b, uint32_t split) {
+  if (blockIdx.x < split)
+    proj_gate_small_body<MX, STK>(a, blockIdx.x);
+  else
+    proj_gate_small_body<MX, STK>(b, blockIdx.x - split);
 }
 
 // Many tokens of a multi-branch FP8 product, with W in fragment order
@@ -971,7 +1035,7 @@ proj_gate_mx_resident_kernel(ProjGateArgs a) {
     // the next pass's h loads included.
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
   }
-  advance_state(a);
+  advance_state(a, blockIdx.x);
 }
 
 // Workgroups per token tile for the resident-token FP8 kernel, or 0 where it
@@ -1119,6 +1183,57 @@ hipError_t launch_small(const ProjGateArgs& in, hipStream_t s) {
   launch_k(proj_gate_small_kernel<MX>, dim3(static_cast<unsigned>(a.tiles_f * a.tiles_t)), dim3(64 * kSmallWaves),
            small_lds_bytes<MX>(), s, a);
   return hipGetLastError();
+}
+
+// a and b shaped for STK-token tiles (tiles_t counted in STK)
+template <bool MX, int STK>
+hipError_t launch_small2(const ProjGateArgs& a, const ProjGateArgs& b, hipStream_t s) {
+  static std::atomic<uint64_t> attr_set{0};   // > 64 KiB of dynamic LDS, raised once per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if ((attr_set.load() & bit) == 0) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(proj_gate_small2_kernel<MX, STK>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, small_lds_bytes<MX, STK>());
+    if (e != hipSuccess) return e;
+    attr_set.fetch_or(bit);
+  }
+  const uint32_t na = static_cast<uint32_t>(a.tiles_f * a.tiles_t), nb = static_cast<uint32_t>(b.tiles_f * b.tiles_t);
+  launch_k((proj_gate_small2_kernel<MX, STK>), dim3(na + nb), dim3(64 * kSmallWaves), small_lds_bytes<MX, STK>(), s,
+           a, b, na);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_layers(const ProjGateArgs& in_a, const ProjGateArgs* in_b, hipStream_t s) {
+  const bool mx = in_a.e_scale != nullptr;
+  auto fits = [&](const ProjGateArgs& x) {
+    return x.kv_out != nullptr && (x.e_scale != nullptr) == mx && x.N % kSmallTF == 0 &&
+           x.K % (mx ? 512 : BK) == 0 && proj_gate_small_for(x.n_tok, x.N, x.d, x.K, mx);
+  };
+  if (!fits(in_a) || (in_b != nullptr && !fits(*in_b))) return hipErrorNotSupported;
+  auto shaped = [](const ProjGateArgs& x, int tk) {
+    ProjGateArgs y = x;
+    y.tiles_f = y.N / kSmallTF;
+    y.tiles_t = static_cast<int>((y.n_tok + tk - 1) / tk);
+    return y;
+  };
+  if (in_b == nullptr || in_b->n_tok == 0 || in_a.n_tok == 0) {
+    const ProjGateArgs a = shaped(in_a.n_tok == 0 && in_b != nullptr ? *in_b : in_a, kSmallTK);
+    if (a.n_tok == 0) return hipSuccess;
+    return mx ? launch_small<true>(a, s) : launch_small<false>(a, s);
+  }
+  // Two layers: 64-token tiles while the two layers' tiles still fill the
+  // chip once (one workgroup of 128 KiB of LDS per CU), so that the launch
+  // runs in one round; otherwise the single layer's 32-token tiles.
+  const int64_t wg64 = shaped(in_a, 2 * kSmallTK).tiles_f * static_cast<int64_t>(shaped(in_a, 2 * kSmallTK).tiles_t) +
+                       shaped(*in_b, 2 * kSmallTK).tiles_f * static_cast<int64_t>(shaped(*in_b, 2 * kSmallTK).tiles_t);
+  if (wg64 <= 256) {
+    const ProjGateArgs a = shaped(in_a, 2 * kSmallTK), b = shaped(*in_b, 2 * kSmallTK);
+    return mx ? launch_small2<true, 2 * kSmallTK>(a, b, s) : launch_small2<false, 2 * kSmallTK>(a, b, s);
+  }
+  const ProjGateArgs a = shaped(in_a, kSmallTK), b = shaped(*in_b, kSmallTK);
+  return mx ? launch_small2<true, kSmallTK>(a, b, s) : launch_small2<false, kSmallTK>(a, b, s);
 }
 
 hipError_t launch_proj_gate(const ProjGateArgs& in, hipStream_t s) {

@@ -112,6 +112,13 @@ def load_library(path: str) -> ctypes.CDLL:
                                            ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
         "engram_quantize_mxfp8": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "engram_pack_mxfp8": (i32, [vp, vp, i64, i64, vp, vp]),
+        "engram_project_ahead_workspace": (sz, [i64, i64, i32, ctypes.POINTER(ctypes.POINTER(LayerStruct))]),
+        "engram_project_ahead": (i32, [vp, i64, i64, i32, ctypes.POINTER(ctypes.POINTER(LayerStruct)),
+                                       ctypes.POINTER(ctypes.POINTER(DecodeStateStruct)), ctypes.POINTER(vp), vp, sz,
+                                       vp]),
+        "engram_forward_projected_workspace": (sz, [i64, i64, ctypes.POINTER(LayerStruct)]),
+        "engram_forward_projected": (i32, [vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
+                                           ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
         "engram_forward_retrieved_prefetch": (i32, [vp, vp, vp, i64, i64, ctypes.POINTER(LayerStruct),
                                                     ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz,
                                                     ctypes.POINTER(LayerStruct), ctypes.POINTER(DecodeStateStruct),
@@ -147,6 +154,8 @@ def exported_names():
             "engram_forward_workspace", "engram_forward", "engram_forward_noalloc", "engram_retrieve", "engram_forward_retrieved_workspace",
             "engram_forward_retrieved", "engram_cache_build_workspace", "engram_cache_build",
             "engram_cache_update_workspace", "engram_cache_update", "engram_quantize_mxfp8", "engram_pack_mxfp8",
+            "engram_project_ahead_workspace", "engram_project_ahead", "engram_forward_projected_workspace",
+            "engram_forward_projected",
             "engram_hot_buckets", "engram_hot_build", "engram_hot_lookup", "engram_forward_retrieved_prefetch",
             "engram_profile_enable", "engram_profile_read",
             "engram_host_alloc", "engram_host_free", "engram_debug_checks", "engram_debug_set_error_word",
@@ -507,6 +516,60 @@ def forward_noalloc(tokens: torch.Tensor, H: torch.Tensor, layer: Layer, state: 
     st = ctypes.byref(state.s) if state is not None else None
     _check(lib().engram_forward_noalloc(_ptr(tokens), _ptr(H), B, T, ctypes.byref(layer.s), st, _ptr(alpha),
                                         _ptr(y), _stream(stream)))
+
+
+def _layer_array(layers):
+    arr = (ctypes.POINTER(LayerStruct) * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i] = ctypes.pointer(L.s)
+    return arr
+
+
+def project_ahead_workspace(B: int, T: int, layers) -> int:
+    return lib().engram_project_ahead_workspace(B, T, len(layers), _layer_array(layers))
+
+
+def kv_buffer(B: int, T: int, layer: Layer, device=None) -> torch.Tensor:
+    """float32 [B*T, (1+M)*d]: v, then the M keys (engram_project_ahead)."""
+    return torch.empty((B * T, (1 + layer.li.branches) * layer.li.d), dtype=torch.float32, device=device)
+
+
+def project_ahead(tokens: torch.Tensor, layers, kv=None, states=None, ws: Optional[torch.Tensor] = None,
+                  stream=None):
+    """Steps 1-5 of several layers over the same tokens [B, T]; returns the
+    float32 [v | k] rows of each (engram_project_ahead).  With states, T = 1
+    and each state's ids and pos advance here."""
+    B, T = tokens.shape
+    if kv is None:
+        kv = [kv_buffer(B, T, L, tokens.device) for L in layers]
+    if ws is None:
+        ws = torch.empty(max(project_ahead_workspace(B, T, layers), 256), dtype=torch.uint8, device=tokens.device)
+    kv_arr = (ctypes.c_void_p * len(layers))(*[_ptr(k) for k in kv])
+    st_arr = None
+    if states is not None:
+        st_arr = (ctypes.POINTER(DecodeStateStruct) * len(layers))()
+        for i, st in enumerate(states):
+            st_arr[i] = ctypes.pointer(st.s)
+    _check(lib().engram_project_ahead(_ptr(tokens), B, T, len(layers), _layer_array(layers), st_arr, kv_arr,
+                                      _ptr(ws), ws.numel(), _stream(stream)))
+    return kv
+
+
+def forward_projected(kv: torch.Tensor, H: torch.Tensor, layer: Layer, B: int, T: int, state=None,
+                      want_alpha: bool = False, want_y: bool = False, ws: Optional[torch.Tensor] = None,
+                      stream=None):
+    """Steps 6-8 of one layer on kv from project_ahead (H updated in place);
+    returns (alpha, y) when asked."""
+    M, d = layer.li.branches, layer.li.d
+    alpha = torch.empty((B, T, M), dtype=torch.float32, device=H.device) if want_alpha else None
+    y = torch.empty((B, T, M, d), dtype=torch.float32, device=H.device) if want_y else None
+    if ws is None:
+        n = lib().engram_forward_projected_workspace(B, T, ctypes.byref(layer.s))
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=H.device)
+    st = ctypes.byref(state.s) if state is not None else None
+    _check(lib().engram_forward_projected(_ptr(kv), _ptr(H), B, T, ctypes.byref(layer.s), st, _ptr(alpha), _ptr(y),
+                                          _ptr(ws), ws.numel(), _stream(stream)))
+    return alpha, y
 
 
 def rows_buffer(B: int, T: int, layer: Layer, device=None) -> torch.Tensor:

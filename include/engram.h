@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 4
+#define ENGRAM_ABI_VERSION 5
 #define ENGRAM_MAX_TABLES 32 /* (N-1)*K */
 #define ENGRAM_MAX_ORDER 4   /* N */
 #define ENGRAM_MAX_KERNEL_W 8
@@ -333,6 +333,48 @@ engram_status engram_forward_retrieved_prefetch(const int32_t* tokens, const voi
                                                 const engram_layer* next_L, const engram_decode_state* next_st,
                                                 const int32_t* next_tokens, int64_t next_B, int64_t next_T,
                                                 void* next_e, hipStream_t stream);
+
+/* Step 5 ahead of the hidden states as well.  Steps 1-5 read the token ids
+ * (and the decode history) alone: v = W_V e and k^(m) = W_K^(m) e ("DeepSeek
+ * Engram series guide", Step 5 and its multi-branch variant) do not depend on
+ * h, which first enters at Step 6's gate.  So a caller can run Steps 1-5 of
+ * several layers together as soon as the tokens are known (a decode step's
+ * sampled token), as the retrieval-ahead calls above do for Steps 1-4, and
+ * run each layer's Steps 6-8 when its hidden state arrives.
+ *
+ * engram_project_ahead: Steps 1-5 of n_layers layers (1 <= n_layers <=
+ * ENGRAM_MAX_AHEAD_LAYERS) over the same tokens [B][T] into kv[l], device
+ * float32 [B*T][(1+M_l)*d_l], 16-byte aligned, owned by the caller: v, then
+ * k^(0..M-1) (the product in float32, unrounded).  layers[l]: bf16 H layers
+ * with the fused projection (d a multiple of 128 up to 4096); with states
+ * (states[l] non-NULL for every layer, with ids), T must be 1 and each
+ * state's ids and pos advance by that token here, so that the matching
+ * engram_forward_projected reads them as advanced.  Layers go in pairs: one
+ * launch gathers both layers' rows, one launch multiplies both (the
+ * small-batch product; n_tok*(1+M)*d within its range, which a decode batch
+ * of a few hundred sequences is).  Larger bf16 products without states run
+ * the general product per layer; larger ones with states, or MXFP8 ones, are
+ * ENGRAM_EUNSUPPORTED.  ws: at least engram_project_ahead_workspace() bytes,
+ * 256-byte aligned (the gathered rows).
+ *
+ * engram_forward_projected: Steps 6-8 of layer L on kv from
+ * engram_project_ahead with the same B, T and state; H as for engram_forward
+ * (updated in place), alpha_out / y_out as there.  With st (T = 1) the conv
+ * reads the state's ring at the advanced pos and writes the new conv input
+ * into it.  For T = 1 and d <= 1024 one launch forms the gate's sums and runs
+ * the conv; otherwise (no state) a gate-statistics launch comes first.  The
+ * gate's sums are then formed over whole rows, so results agree with
+ * engram_forward's to rounding, not bit for bit.  ws: at least
+ * engram_forward_projected_workspace() bytes, 256-byte aligned. */
+#define ENGRAM_MAX_AHEAD_LAYERS 8
+size_t engram_project_ahead_workspace(int64_t B, int64_t T, int32_t n_layers, const engram_layer* const* layers);
+engram_status engram_project_ahead(const int32_t* tokens, int64_t B, int64_t T, int32_t n_layers,
+                                   const engram_layer* const* layers, engram_decode_state* const* states,
+                                   float* const* kv, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t engram_forward_projected_workspace(int64_t B, int64_t T, const engram_layer* L);
+engram_status engram_forward_projected(const float* kv, void* H, int64_t B, int64_t T, const engram_layer* L,
+                                       engram_decode_state* st, float* alpha_out, float* y_out, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
 
 /* Static LFU admission for the HBM hot-row cache (Ascend RecSDK Engram
  * article, multi-level cache: hot rows by access frequency in fast memory,

@@ -39,7 +39,7 @@ def test_exports_match_header():
 
 
 def test_abi_version():
-    assert eg.lib().engram_abi_version() == 4
+    assert eg.lib().engram_abi_version() == 5
 
 
 def _hash_params(**over):
@@ -391,3 +391,45 @@ def test_profile_modes_are_checked():
     st, msg = _status(L.engram_profile_read, ms, None, 4, ctypes.byref(n))
     assert st == eg.EINVAL and n.value == 0
     assert L.engram_profile_read(ms, None, 4, None) == eg.EINVAL
+
+
+def test_project_ahead_and_forward_projected_are_checked():
+    """engram_project_ahead takes 1..ENGRAM_MAX_AHEAD_LAYERS fused bf16 layers,
+    a state for every layer or none, and T = 1 with states;
+    engram_forward_projected takes a state only for T = 1; all refused before
+    anything launches."""
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    hp, keep_h = _hash_params()
+    t, keep_t = _tables(dtype=eg.BF16, dim=32)
+    lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=256))
+    arr = (ctypes.POINTER(eg.LayerStruct) * 2)(ctypes.pointer(lay), ctypes.pointer(lay))
+    kv = (ctypes.c_void_p * 2)(0x20000, 0x30000)
+    need = L.engram_project_ahead_workspace(1, 1, 2, arr)
+    assert need > 0
+    for n in (0, 9):
+        st, msg = _status(L.engram_project_ahead, p, 1, 1, n, arr, None, kv, p, need, None)
+        assert st == eg.EINVAL and "n_layers" in msg
+    st, msg = _status(L.engram_project_ahead, p, 1, 1, 2, None, None, kv, p, need, None)
+    assert st == eg.EINVAL and "non-NULL" in msg
+    ids = ctypes.c_void_p(0x40000)
+    ds = eg.DecodeStateStruct(ids, 0x50000, 0x60000)
+    sts = (ctypes.POINTER(eg.DecodeStateStruct) * 2)(ctypes.pointer(ds), None)
+    st, msg = _status(L.engram_project_ahead, p, 1, 1, 2, arr, sts, kv, p, need, None)
+    assert st == eg.EINVAL and "every layer or none" in msg
+    sts[1] = ctypes.pointer(ds)
+    st, msg = _status(L.engram_project_ahead, p, 1, 2, 2, arr, sts, kv, p, need, None)
+    assert st == eg.EUNSUPPORTED and "T must be 1" in msg
+    f32 = eg.LayerStruct(hp, t, 0x10000, _gc(d=256, hdtype=eg.F32))
+    arr_f = (ctypes.POINTER(eg.LayerStruct) * 1)(ctypes.pointer(f32))
+    st, msg = _status(L.engram_project_ahead, p, 1, 1, 1, arr_f, None, kv, p, need, None)
+    assert st == eg.EUNSUPPORTED and "bf16 H" in msg
+    st, msg = _status(L.engram_project_ahead, p, 1, 1, 2, arr, None, kv, p, 0, None)
+    assert st == eg.EINVAL and "workspace" in msg
+    assert L.engram_project_ahead(p, 0, 1, 2, arr, None, kv, None, 0, None) == eg.OK     # no tokens: a no-op
+    need_f = L.engram_forward_projected_workspace(1, 2, ctypes.byref(lay))
+    st, msg = _status(L.engram_forward_projected, p, p, 1, 2, ctypes.byref(lay), ctypes.byref(ds), None, None, p,
+                      need_f, None)
+    assert st == eg.EUNSUPPORTED and "decode state" in msg
+    st, msg = _status(L.engram_forward_projected, p, p, 1, 2, ctypes.byref(lay), None, None, None, p, 0, None)
+    assert st == eg.EINVAL and "workspace" in msg
