@@ -161,6 +161,9 @@ def kernel_units(n_tok, lay, hdtype, hot_hit=None, mx=False):
         # product out)
         "gather2_kernel": ("hbm", 2 * n_tok * (4 + nt * (row_bytes + e_bytes))),
         "proj_kv_kernel": ("hbm", 2 * (N * d_mem * op + n_tok * (d_mem * op + N * 4))),
+        # both layers' Steps 1-5 in one launch: token ids and rows in, W in,
+        # the float32 product out (the gathered rows stay on chip)
+        "gather_proj_kernel": ("hbm", 2 * (N * d_mem * op + n_tok * (4 + nt * row_bytes + N * 4))),
     }
     if hot_hit is not None:
         K = lay.hash.heads
@@ -350,7 +353,8 @@ KERNEL_SOURCES = {
                                   ["gather.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
     "proj_gate_kernel": (r"proj_gate(_small|_mx_resident)?_kernel<", ["proj_gate.hip"]),
     "gather2_kernel": (r"hashed_gather2_kernel<", ["gather.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
-    "proj_kv_kernel": (r"proj_gate_small2_kernel<", ["proj_gate.hip"]),
+    "proj_kv_kernel": (r"proj_(gate_small2|frag2)_kernel<", ["proj_gate.hip", "ahead.hip"]),
+    "gather_proj_kernel": (r"ahead_fused_kernel<", ["ahead.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
     "conv_kernel": (r"conv_(strip_)?kernel<", ["gate_conv.hip"]),
     "conv_gather_kernel": (r"conv_gather_kernel<",
                            ["gate_conv.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),

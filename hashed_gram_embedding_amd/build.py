@@ -45,9 +45,18 @@ def common_flags():
             "-Wall", "-Wno-unused-function"]
 
 
+# Per-source flags.  ahead.hip: the compiler's wave-level atomic combining
+# would read the arrival count's return value at once (to spread it over the
+# lanes), so the count's round trip to memory would stall the wavefront
+# instead of overlapping the loads that follow it; its one atomic comes from
+# a single lane anyway.
+FILE_FLAGS = {"ahead.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _compile(src: str, out_dir: str = BUILD, extra=()) -> str:
     obj = os.path.join(out_dir, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + common_flags() + list(extra) + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + common_flags() + FILE_FLAGS.get(os.path.basename(src), []) + list(extra) + \
+        ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = (r.stdout + r.stderr).strip()
     noise = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"

@@ -1,0 +1,543 @@
+// Steps 1-5 of decode-size batches ahead of the hidden states ("DeepSeek
+// Engram series guide", section "Engram working principle": Steps 1-4 and
+// the products v = W_V e, k^(m) = W_K^(m) e of Step 5 read only the token ids
+// and the decode history), into float32 rows of [v | k].
+//
+// At a few hundred tokens the product is a chain of memory latencies, not a
+// bandwidth or matrix-core problem, so both kernels here are built to wait
+// on memory as few times as possible:
+//   proj_frag2_kernel   both operands in the matrix cores' fragment order (W
+//                       from launch_bf16_pack, e from the gather's
+//                       kGatherOutFrag16 output): every operand is one
+//                       coalesced 1 KiB load straight into registers, all of
+//                       a wavefront's loads are issued before its first
+//                       matrix operation, and nothing is staged in LDS.
+//   ahead_fused_kernel  the same product whose wavefronts hash their tokens
+//                       and read their own table rows (Steps 1-4) instead of
+//                       loading gathered rows: the gather's launch and its
+//                       round trip through memory go, the W loads overlap the
+//                       id -> hash -> row chain, and int8 rows are dequantised
+//                       in registers (the select-and-dequantise-in-one-kernel
+//                       design of the DRAM offload study, "Engram embedding
+//                       extension: co-design for efficient DRAM/SSD offload",
+//                       decode section).
+// A workgroup's 64 x 64 output tile is split over its 8 wavefronts along K
+// (K/8 each); the 8 partial tiles meet in LDS (128 KiB) at the end.  Tiles run
+// feature tile fastest, so the token tiles that share a W tile share the
+// workgroup index modulo 8, and so an XCD and its L2.
+//
+// The K order inside the matrix operations: lane l = 32h + r of K16 step ks
+// takes columns 32(ks/2) + 16h + 8(ks%2) .. +7, so that a lane's two steps of
+// a 32-column group read 16 consecutive values of one table row (16 bytes of
+// an int8 row); W is packed the same way, so the sum is that of W e in
+// another order.
+#include <algorithm>
+#include <atomic>
+
+#include "device_util.h"
+#include "engram_internal.h"
+#include "gather_device.h"
+#include "hash_device.h"
+
+namespace engram {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kFragTile = 64;   // features and tokens per workgroup
+constexpr int kFragWaves = 8;
+constexpr int kFragLds = kFragWaves * 16 * 64 * 16;   // [wave][16 float4][64 lanes]
+
+static_assert(sizeof(AheadJob::Head) == 128, "the head is two scalar loads");
+
+// Arrival counts of the fused launches that advance decode states, one per
+// token tile of each layer: zero at load, and put back to zero by the last
+// workgroup of each tile.
+__device__ uint32_t ahead_arrivals[kAheadSlots];
+constexpr int kAheadTiles = 32;   // token tiles per layer that a launch with states may have (2048 sequences)
+
+// The 64 x 64 tile of the 8 wavefronts' partial products acc (K split 8
+// ways): summed through LDS and stored as float32 rows of kv_out.
+__device__ __forceinline__ void frag_epilogue(float* kv_out, int N, int64_t n_tok, int tf, int tt,
+                                              f32x16_t (&acc)[2][2]) {
+  extern __shared__ float4 frag_part[];   // [wave][j][lane]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // acc[fb][tb][4g + r]: feature 32fb + 8g + 4(lane / 32) + r, token 32tb + lane % 32
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        frag_part[(wave * 16 + (fb * 2 + tb) * 4 + g) * 64 + lane] =
+            make_float4(acc[fb][tb][4 * g], acc[fb][tb][4 * g + 1], acc[fb][tb][4 * g + 2], acc[fb][tb][4 * g + 3]);
+  __syncthreads();
+  // thread (j, r): fragment j's float4s of lanes r and r + 32, i.e. 8
+  // consecutive features of one token, summed over the wavefronts
+  const int j = threadIdx.x >> 5, r = threadIdx.x & 31;
+  float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
+#pragma unroll
+  for (int w = 0; w < kFragWaves; ++w) {
+    const float4 x = frag_part[(w * 16 + j) * 64 + r], y = frag_part[(w * 16 + j) * 64 + 32 + r];
+    lo.x += x.x; lo.y += x.y; lo.z += x.z; lo.w += x.w;
+    hi.x += y.x; hi.y += y.y; hi.z += y.z; hi.w += y.w;
+  }
+  const int fb = j >> 3, tb = (j >> 2) & 1, g = j & 3;
+  const int64_t tok = static_cast<int64_t>(tt) * kFragTile + tb * 32 + r;
+  if (tok < n_tok) {
+    float4* kp = reinterpret_cast<float4*>(kv_out + tok * N + tf * kFragTile + fb * 32 + g * 8);
+    kp[0] = lo;
+    kp[1] = hi;
+  }
+}
+
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[2][2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+// This wavefront's W operands: K16 steps wave*SPW .. +SPW-1 of the 32-row
+// blocks 2tf and 2tf+1, step by step, so that step s waits only for its own.
+// The wavefront index, known to the compiler as uniform (so that what it
+// selects, table arguments and base addresses, stays in scalar registers).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+template <int SPW>
+__device__ __forceinline__ void load_w(const uint16_t* w_frag, int tf, u32x4_t (&wa)[2][SPW]) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  constexpr int64_t ks_n = 8 * SPW;   // K / 16
+  const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(w_frag) + ((2 * tf) * ks_n + wave * SPW) * 64 + lane;
+#pragma unroll
+  for (int st = 0; st < SPW; ++st) {
+    wa[0][st] = wp[st * 64];
+    wa[1][st] = wp[(ks_n + st) * 64];
+  }
+}
+
+template <int SPW>
+__device__ __forceinline__ void proj_frag_body(const ProjGateArgs& a, uint32_t bid) {
+  const int tf = static_cast<int>(bid % static_cast<uint32_t>(a.tiles_f));
+  const int tt = static_cast<int>(bid / static_cast<uint32_t>(a.tiles_f));
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int64_t ks_n = a.K / 16;
+  const u32x4_t* ep = reinterpret_cast<const u32x4_t*>(a.e) + ((2 * tt) * ks_n + wave * SPW) * 64 + lane;
+  u32x4_t wa[2][SPW], eb[2][SPW];
+  load_w<SPW>(a.w_frag, tf, wa);
+#pragma unroll
+  for (int st = 0; st < SPW; ++st) {
+    eb[0][st] = ep[st * 64];
+    eb[1][st] = ep[(ks_n + st) * 64];
+  }
+  // keep the scheduler from sinking the loads next to their first use
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16_t acc[2][2];
+  zero_acc(acc);
+#pragma unroll
+  for (int st = 0; st < SPW; ++st)
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wa[fb][st]),
+                                                              __builtin_bit_cast(bf16x8_t, eb[tb][st]), acc[fb][tb],
+                                                              0, 0, 0);
+  frag_epilogue(a.kv_out, a.N, a.n_tok, tf, tt, acc);
+  advance_state(a, bid);
+}
+
+// One or two layers (workgroups below split serve a, the rest b).
+template <int SPW>
+__global__ void __launch_bounds__(64 * kFragWaves)
+proj_frag2_kernel(ProjGateArgs a, ProjGateArgs b, uint32_t split) {
+  if (blockIdx.x < split)
+    proj_frag_body<SPW>(a, blockIdx.x);
+  else
+    proj_frag_body<SPW>(b, blockIdx.x - split);
+}
+
+// Row values of the fused kernel: a lane's 16 consecutive values of a
+// 32-column group, as loaded (int8 codes with the row's scale, or bf16).
+template <int IN>
+struct RowRun;
+template <>
+struct RowRun<ENGRAM_I8> {
+  u32x4_t q;
+  float s;
+};
+template <>
+struct RowRun<ENGRAM_BF16> {
+  u32x4_t lo, hi;
+};
+
+// The bf16 operand of half `s` (values 8s .. 8s+7) of a run: int8 codes are
+// dequantised as the gather does (one float32 multiply by the row's scale,
+// then round to nearest even bf16), bf16 values pass as they are.
+template <int IN>
+__device__ __forceinline__ u32x4_t run_operand(const RowRun<IN>& v, int s) {
+  if constexpr (IN == ENGRAM_I8) {
+    const uint32_t w0 = s == 0 ? v.q[0] : v.q[2], w1 = s == 0 ? v.q[1] : v.q[3];
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = static_cast<float>(static_cast<int8_t>((w0 >> (8 * i)) & 0xffu)) * v.s;
+      f[4 + i] = static_cast<float>(static_cast<int8_t>((w1 >> (8 * i)) & 0xffu)) * v.s;
+    }
+    u32x4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return o;
+  } else {
+    return s == 0 ? v.lo : v.hi;
+  }
+}
+
+// Steps 1-5 of one workgroup tile of one layer; tables of dim 32 GPT.
+template <int IN, int SPW, bool HIST_ALL, int GPT>
+__device__ __forceinline__ void ahead_fused_body(const AheadJob& J, int tf, int tt) {
+  constexpr int NG = SPW / 2;   // 32-column groups per wavefront
+  constexpr int DIM = 32 * GPT;
+  static_assert(NG % GPT == 0 || GPT > NG, "a wavefront's groups start at a table boundary, or lie in one table");
+  const AheadJob::Head hd = J.head;
+  const TableArgs& ta = J.g.ta;
+  const HashSrc& hs = J.g.hs;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int h = lane >> 5, r = lane & 31;
+
+  // The hash constants and row offsets of this wavefront's tables, read
+  // before anything waits: argument reads that miss the scalar cache take a
+  // memory latency each, and here they overlap the id loads instead of
+  // waiting in the chain behind them.
+  constexpr int NT = GPT > NG ? 1 : NG / GPT;   // tables per wavefront
+  TableHash th[NT];
+  int64_t row_off[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int j = (32 * NG * wave) / DIM + u;
+    th[u] = table_hash(hs.a, j);
+    row_off[u] = ta.row_offset[j];
+  }
+  // All of these and the head in flight together, then one wait: the asm
+  // takes them as operands, so their loads are all issued before it (left
+  // to itself the compiler issues a load where its value is first needed
+  // and waits for it there, one round trip each).
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::"s"(hd.tokens), "s"(hd.proj), "s"(hd.hist), "s"(hd.w_frag), "s"(hd.rows), "s"(hd.scale),
+               "s"(hd.kv_out), "s"(hd.st_ids), "s"(hd.st_pos));
+  asm volatile("" ::"s"(hd.T), "s"(hd.max_n), "s"(hd.vocab), "s"(hd.n_tok), "s"(hd.N), "s"(hd.tiles_f),
+               "s"(hd.has_state), "s"(hd.slot));
+  const uint32_t slot = hd.slot;
+  const WindowSrc win{hd.tokens, hd.proj, hd.hist, hd.err, hd.T, hd.max_n, hd.vocab};
+#pragma unroll
+  for (int u = 0; u < NT; ++u)
+    asm volatile("" ::"s"(th[u].m[0]), "s"(th[u].m[1]), "s"(th[u].m[2]), "s"(th[u].m[3]), "s"(th[u].inv),
+                 "s"(th[u].prime), "s"(row_off[u]));
+
+  // Steps 1-2: the suffix window of this lane's own token 64tt + 32h + r, so
+  // that the lane pair (r, 32 + r) holds the tile's tokens r and 32 + r
+  // between them (tokens past the end take the last one's; their columns are
+  // not stored)
+  const uint32_t n_tok = static_cast<uint32_t>(hd.n_tok);
+  const uint32_t T = static_cast<uint32_t>(hd.T);
+  uint32_t b[1], t[1];
+  {
+    const uint32_t tok = static_cast<uint32_t>(tt) * kFragTile + 32 * h + r;
+    const uint32_t tc = tok < n_tok ? tok : n_tok - 1;
+    b[0] = tc / T;
+    t[0] = tc - b[0] * T;
+  }
+  uint32_t xp[1][ENGRAM_MAX_ORDER], hv[1][ENGRAM_MAX_ORDER];
+  window_loads<1, HIST_ALL>(win, b, t, xp, hv);
+  // With decode states: this workgroup's history reads are done once every
+  // wavefront holds hv (the asm makes each wait for it, which costs nothing
+  // here: the history returned before the token ids the P lookups needed),
+  // so the arrival is counted now and its round trip overlaps the rest; the
+  // count is relaxed, as the reads have all returned and it orders nothing
+  // but the arrivals themselves.
+  uint32_t arrived_before;   // thread 0's count (the other lanes never read it)
+  if (hd.has_state) {
+    asm volatile("" ::"v"(hv[0][1]), "v"(hv[0][2]), "v"(hv[0][3]) : "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+      arrived_before = __hip_atomic_fetch_add(&ahead_arrivals[slot + tt], 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // W after the P lookups: its loads then stream in behind the P and row
+  // latencies, and (memory reads retiring in order) waiting for the P values
+  // does not wait for W
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4_t wa[2][SPW];
+  load_w<SPW>(hd.w_frag, tf, wa);
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t x[1][ENGRAM_MAX_ORDER];
+  window_select<1>(t, xp, hv, x);
+
+  // Steps 3-4: this wavefront's groups are columns 32(NG wave + q) .. +31,
+  // in table j at column c0 (uniform over the wavefront); lane half h reads
+  // the group's values 16h .. 16h+15 of both tokens' rows.  Each lane hashes
+  // its own token once per table and trades the index with its pair lane
+  // (v_permlane32_swap), and so (below) the int8 row's scale.
+  RowRun<IN> run[2][NG];
+  float s_own[NG];
+  int32_t z_tb[2] = {0, 0};
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int k0 = 32 * (NG * wave + q);
+    const int j = k0 / DIM;
+    const int col = k0 - j * DIM + 16 * h;
+    const int u = GPT > NG ? 0 : q / GPT;
+    const int64_t row_offset = row_off[u];
+    if (q == 0 || q % GPT == 0) {   // the first group of a table (or of this wavefront)
+      const int32_t z = hash_of_ids(x[0], th[u]);
+      if constexpr (kDebugChecks) debug_record(hs.a.err, range_bit(z, th[u].prime, kErrRow));   // z < p by construction
+      const auto sw = __builtin_amdgcn_permlane32_swap(z, z, false, false);
+      const int32_t zp = h ? static_cast<int32_t>(sw[0]) : static_cast<int32_t>(sw[1]);   // the pair lane's
+      z_tb[0] = h ? zp : z;
+      z_tb[1] = h ? z : zp;
+      if constexpr (IN == ENGRAM_I8) s_own[q] = hd.scale[row_offset + z];
+    } else if constexpr (IN == ENGRAM_I8) {
+      s_own[q] = s_own[q - 1];
+    }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int64_t row = row_offset + z_tb[tb];
+      if constexpr (IN == ENGRAM_I8) {
+        run[tb][q].q = *reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(hd.rows) + row * DIM + col);
+      } else {
+        const u32x4_t* p = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(hd.rows) + row * DIM + col);
+        run[tb][q].lo = p[0];
+        run[tb][q].hi = p[1];
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (IN == ENGRAM_I8) {
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s_own[q]), __float_as_uint(s_own[q]), false,
+                                                        false);
+      const float sp = __uint_as_float(h ? sw[0] : sw[1]);
+      run[0][q].s = h ? sp : s_own[q];
+      run[1][q].s = h ? s_own[q] : sp;
+    }
+  }
+
+  // Step 5
+  f32x16_t acc[2][2];
+  zero_acc(acc);
+#pragma unroll
+  for (int st = 0; st < SPW; ++st) {
+    u32x4_t eb[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) eb[tb] = run_operand<IN>(run[tb][st >> 1], st & 1);
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wa[fb][st]),
+                                                              __builtin_bit_cast(bf16x8_t, eb[tb]), acc[fb][tb],
+                                                              0, 0, 0);
+  }
+  frag_epilogue(hd.kv_out, hd.N, hd.n_tok, tf, tt, acc);
+
+  // The decode state (T = 1: token tok is sequence tok) may only advance
+  // once every workgroup of this token tile has read its history: the last
+  // of the tile's feature workgroups to arrive writes the new ids, which the
+  // lanes of its first wavefront already hold (x, newest first), and clears
+  // the count.
+  if (hd.has_state) {
+    __shared__ uint32_t last;
+    if (threadIdx.x == 0) {
+      last = arrived_before == static_cast<uint32_t>(hd.tiles_f) - 1;
+      if (last) __hip_atomic_store(&ahead_arrivals[slot + tt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (last && threadIdx.x < 64) {
+      const int hl = hd.max_n - 1;
+      const int64_t tok = static_cast<int64_t>(tt) * kFragTile + 32 * h + r;   // this lane's own
+      if (tok < hd.n_tok) {
+#pragma unroll
+        for (int i = 0; i < ENGRAM_MAX_ORDER - 1; ++i)
+          if (i < hl) hd.st_ids[tok * hl + i] = static_cast<int32_t>(x[0][hl - 1 - i]);
+        hd.st_pos[tok] += 1;
+      }
+    }
+  }
+}
+
+// HIST_ALL: every token of both layers reads decode history (T <= N-1).
+// The grid is (feature tile, token tile, layer), so that a workgroup knows
+// its tile and layer before it reads any argument.
+template <int IN, int SPW, bool HIST_ALL, int GPT>
+__global__ void __launch_bounds__(64 * kFragWaves)
+ahead_fused_kernel(AheadJob a, AheadJob b) {
+  if (blockIdx.z == 0)
+    ahead_fused_body<IN, SPW, HIST_ALL, GPT>(a, blockIdx.x, blockIdx.y);
+  else
+    ahead_fused_body<IN, SPW, HIST_ALL, GPT>(b, blockIdx.x, blockIdx.y);
+}
+
+// Kernels with more than 64 KiB of dynamic LDS, raised once per device.
+hipError_t raise_lds(const void* kernel, std::atomic<uint64_t>& attr_set) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if ((attr_set.load() & bit) == 0) {
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kFragLds);
+    if (e != hipSuccess) return e;
+    attr_set.fetch_or(bit);
+  }
+  return hipSuccess;
+}
+
+template <int SPW>
+hipError_t launch_frag2(const ProjGateArgs& a, const ProjGateArgs& b, hipStream_t s) {
+  static std::atomic<uint64_t> attr_set{0};
+  const hipError_t e = raise_lds(reinterpret_cast<const void*>(proj_frag2_kernel<SPW>), attr_set);
+  if (e != hipSuccess) return e;
+  const uint32_t na = static_cast<uint32_t>(a.tiles_f * a.tiles_t), nb = static_cast<uint32_t>(b.tiles_f * b.tiles_t);
+  launch_k((proj_frag2_kernel<SPW>), dim3(na + nb), dim3(64 * kFragWaves), kFragLds, s, a, b, na);
+  return hipGetLastError();
+}
+
+std::atomic<uint32_t> g_next_slot{0};
+
+template <int IN, int SPW, bool HIST_ALL, int GPT>
+hipError_t launch_fused_t(AheadJob a, AheadJob b, hipStream_t s) {
+  static std::atomic<uint64_t> attr_set{0};
+  const hipError_t e = raise_lds(reinterpret_cast<const void*>(ahead_fused_kernel<IN, SPW, HIST_ALL, GPT>), attr_set);
+  if (e != hipSuccess) return e;
+  const uint32_t na = static_cast<uint32_t>(a.p.tiles_f * a.p.tiles_t);
+  const uint32_t nb = static_cast<uint32_t>(b.p.tiles_f * b.p.tiles_t);
+  // a block of 2 kAheadTiles counts per launch: a's token tiles, then b's
+  const uint32_t slot = (g_next_slot.fetch_add(1) % (kAheadSlots / (2 * kAheadTiles))) * (2 * kAheadTiles);
+  a.head.slot = slot;
+  b.head.slot = slot + kAheadTiles;
+  // a's workgroups, then b's (as many: the two layers have the same tiles);
+  // workgroup i runs on XCD i % 8, so with 8 | tiles_f the token tiles of a
+  // feature tile share an XCD
+  launch_k((ahead_fused_kernel<IN, SPW, HIST_ALL, GPT>),
+           dim3(static_cast<unsigned>(a.p.tiles_f), static_cast<unsigned>(a.p.tiles_t), nb > 0 ? 2 : 1),
+           dim3(64 * kFragWaves), kFragLds, s, a, b);
+  return hipGetLastError();
+}
+
+template <int IN, int SPW, bool HIST_ALL>
+hipError_t launch_fused_g(const AheadJob& a, const AheadJob& b, hipStream_t s) {
+  switch (a.g.ta.dim) {
+    case 32: return launch_fused_t<IN, SPW, HIST_ALL, 1>(a, b, s);
+    case 64: return launch_fused_t<IN, SPW, HIST_ALL, 2>(a, b, s);
+    default: return launch_fused_t<IN, SPW, HIST_ALL, 4>(a, b, s);
+  }
+}
+
+template <int IN, bool HIST_ALL>
+hipError_t launch_fused_h(const AheadJob& a, const AheadJob& b, hipStream_t s) {
+  return a.p.K == 512 ? launch_fused_g<IN, 4, HIST_ALL>(a, b, s) : launch_fused_g<IN, 8, HIST_ALL>(a, b, s);
+}
+
+bool hist_all(const AheadJob& x) { return x.g.hs.hist != nullptr && x.g.hs.T <= x.g.hs.a.max_n - 1; }
+
+template <int IN>
+hipError_t launch_fused_in(const AheadJob& a, const AheadJob& b, bool has_b, hipStream_t s) {
+  return hist_all(a) && (!has_b || hist_all(b)) ? launch_fused_h<IN, true>(a, b, s) : launch_fused_h<IN, false>(a, b, s);
+}
+
+ProjGateArgs frag_shaped(const ProjGateArgs& x) {
+  ProjGateArgs y = x;
+  y.tiles_f = y.N / kFragTile;
+  y.tiles_t = static_cast<int>((y.n_tok + kFragTile - 1) / kFragTile);
+  return y;
+}
+
+}  // namespace
+
+bool proj_frag_for(int64_t n_tok, int N, int d, int K) {
+  return K % 128 == 0 && K <= 1024 && N % kFragTile == 0 && proj_gate_small_for(n_tok, N, d, K, false);
+}
+
+bool ahead_fused_for(const TableArgs& ta, int64_t n_tok, int N, int d, int K) {
+  return proj_frag_for(n_tok, N, d, K) && (K == 512 || K == 1024) && (ta.dim == 32 || ta.dim == 64 || ta.dim == 128) &&
+         (ta.dtype == ENGRAM_I8 || ta.dtype == ENGRAM_BF16) && reinterpret_cast<uintptr_t>(ta.rows) % 16 == 0 &&
+         ta.cache_slot == nullptr && ta.counts == nullptr;
+}
+
+hipError_t launch_project_frag(const ProjGateArgs& in_a, const ProjGateArgs* in_b, hipStream_t s) {
+  auto fits = [&](const ProjGateArgs& x) {
+    return x.kv_out != nullptr && x.w_frag != nullptr && x.e_scale == nullptr && x.K == in_a.K &&
+           proj_frag_for(x.n_tok, x.N, x.d, x.K);
+  };
+  if (!fits(in_a) || (in_b != nullptr && !fits(*in_b))) return hipErrorNotSupported;
+  const ProjGateArgs a = frag_shaped(in_a);
+  ProjGateArgs b = in_b != nullptr ? frag_shaped(*in_b) : ProjGateArgs{};
+  if (in_b == nullptr) b.tiles_f = b.tiles_t = 0;
+  if (a.tiles_t + b.tiles_t == 0) return hipSuccess;
+  switch (a.K / 128) {
+    case 1: return launch_frag2<1>(a, b, s);
+    case 2: return launch_frag2<2>(a, b, s);
+    case 3: return launch_frag2<3>(a, b, s);
+    case 4: return launch_frag2<4>(a, b, s);
+    case 5: return launch_frag2<5>(a, b, s);
+    case 6: return launch_frag2<6>(a, b, s);
+    case 7: return launch_frag2<7>(a, b, s);
+    default: return launch_frag2<8>(a, b, s);
+  }
+}
+
+hipError_t launch_ahead_fused(const AheadJob& in_a, const AheadJob* in_b, hipStream_t s) {
+  auto fits = [&](const AheadJob& x) {
+    return x.p.kv_out != nullptr && x.p.w_frag != nullptr && x.p.e_scale == nullptr && !x.g.hot &&
+           x.p.K == in_a.p.K && x.g.ta.dtype == in_a.g.ta.dtype && x.g.ta.dim == in_a.g.ta.dim &&
+           x.p.n_tok == x.g.n_tok &&
+           x.p.K == x.g.ta.n_tables * x.g.ta.dim && ahead_fused_for(x.g.ta, x.p.n_tok, x.p.N, x.p.d, x.p.K);
+  };
+  // with decode states (T = 1), at most kAheadTiles token tiles
+  auto state_fits = [](const AheadJob& x) {
+    return x.p.adv_B <= 0 || (x.p.adv_T == 1 && x.p.adv_B == x.p.n_tok && x.p.n_tok <= int64_t{kAheadTiles} * kFragTile);
+  };
+  if (!fits(in_a) || (in_b != nullptr && !fits(*in_b))) return hipErrorNotSupported;
+  if (!state_fits(in_a) || (in_b != nullptr && !state_fits(*in_b))) return hipErrorNotSupported;
+  AheadJob a = in_a, b = in_b != nullptr ? *in_b : AheadJob{};
+  auto shape = [](AheadJob& x) {
+    x.p = frag_shaped(x.p);
+    const HashSrc& hs = x.g.hs;
+    AheadJob::Head& hd = x.head;
+    hd = AheadJob::Head{};
+    hd.tokens = hs.tokens;
+    hd.proj = hs.proj;
+    hd.hist = hs.hist;
+    hd.w_frag = x.p.w_frag;
+    hd.rows = x.g.ta.rows;
+    hd.scale = x.g.ta.scale;
+    hd.kv_out = x.p.kv_out;
+    hd.st_ids = x.p.st_ids;
+    hd.st_pos = x.p.st_pos;
+    hd.err = hs.a.err;
+    hd.T = static_cast<int32_t>(hs.T);
+    hd.max_n = hs.a.max_n;
+    hd.vocab = hs.a.vocab;
+    hd.n_tok = static_cast<int32_t>(x.p.n_tok);
+    hd.N = x.p.N;
+    hd.tiles_f = x.p.tiles_f;
+    hd.has_state = x.p.adv_B > 0;
+  };
+  shape(a);
+  if (in_b != nullptr) {
+    shape(b);
+    if (b.p.tiles_f != a.p.tiles_f || b.p.tiles_t != a.p.tiles_t) return hipErrorNotSupported;
+  } else {
+    b.p.tiles_f = b.p.tiles_t = 0;
+  }
+  if (a.p.tiles_t == 0) return hipSuccess;
+  const bool has_b = in_b != nullptr;
+  return a.g.ta.dtype == ENGRAM_I8 ? launch_fused_in<ENGRAM_I8>(a, b, has_b, s)
+                                   : launch_fused_in<ENGRAM_BF16>(a, b, has_b, s);
+}
+
+}  // namespace engram

@@ -452,6 +452,10 @@ engram_status check_layer(const engram_layer* L, engram::HashArgs* ha, engram::T
     if (L->w_mx == nullptr) return fail(ENGRAM_EINVAL, "layer: w_mx_packed needs w_mx");
     if (!aligned(L->w_mx_packed, 16)) return fail(ENGRAM_EINVAL, "layer: w_mx_packed must be 16-byte aligned");
   }
+  if (L->w_packed != nullptr) {
+    if (L->gc.hdtype != ENGRAM_BF16) return fail(ENGRAM_EINVAL, "layer: w_packed needs a bf16 layer");
+    if (!aligned(L->w_packed, 16)) return fail(ENGRAM_EINVAL, "layer: w_packed must be 16-byte aligned");
+  }
   bool any_hot;
   return check_hot(L->hot, &L->hash, &L->tables, nullptr, &any_hot);
 }
@@ -559,12 +563,12 @@ engram_status check_call(const char* who, const engram_layer* L, const engram_de
 // Steps 1-4: indices hashed inside the gather.
 engram_status run_retrieve(const int32_t* tokens, int64_t B, int64_t T, const engram_layer* L,
                            const engram::HashArgs& ha, const engram::TableArgs& ta, int hdtype,
-                           const engram_decode_state* st, void* e, hipStream_t stream) {
+                           const engram_decode_state* st, void* e, hipStream_t stream, int out_order = -1) {
   // the hashed gather indexes tokens and (token, table) groups in 32 bits
   if (B * T >= (int64_t{1} << 31))
     return fail(ENGRAM_EUNSUPPORTED, "retrieve: B*T = %lld tokens, above 2^31-1 per call", static_cast<long long>(B * T));
   const int32_t* hist = st != nullptr ? st->ids : nullptr;
-  const int out = L->w_mx != nullptr ? engram::kGatherOutMXFP8 : hdtype;
+  const int out = out_order >= 0 ? out_order : (L->w_mx != nullptr ? engram::kGatherOutMXFP8 : hdtype);
   engram::HotArgs hot;
   bool any_hot;
   const engram_status r = check_hot(L->hot, &L->hash, &L->tables, &hot, &any_hot);
@@ -854,9 +858,12 @@ ENGRAM_API engram_status engram_forward_retrieved_prefetch(const int32_t* tokens
 
 namespace {
 
+// The gathered rows of each layer, for whole 64-token tiles (the
+// fragment-operand product reads whole tiles; the rows past the last token
+// only reach output columns that are not stored).
 size_t ahead_ws_bytes(int64_t n_tok, int32_t n_layers, const engram_layer* const* layers) {
   Carve c{nullptr};
-  for (int l = 0; l < n_layers; ++l) c.take<char>(rows_bytes(n_tok, layers[l]));
+  for (int l = 0; l < n_layers; ++l) c.take<char>(rows_bytes((n_tok + 63) / 64 * 64, layers[l]));
   return c.used;
 }
 
@@ -872,6 +879,12 @@ engram::GatherJob gather_job(const int32_t* tokens, int64_t T, int64_t n_tok, co
   j.out_dtype = L->w_mx != nullptr ? engram::kGatherOutMXFP8 : hdtype;
   j.hot = false;
   return j;
+}
+
+// Whether layer L's product in engram_project_ahead takes the fragment-operand
+// kernel (its gathered rows are then written in that kernel's operand order).
+bool ahead_frag(const engram_layer* L, int64_t n_tok, int N, int d, int K) {
+  return L->w_packed != nullptr && L->w_mx == nullptr && engram::proj_frag_for(n_tok, N, d, K);
 }
 
 }  // namespace
@@ -919,13 +932,13 @@ ENGRAM_API engram_status engram_project_ahead(const int32_t* tokens, int64_t B, 
     return fail(ENGRAM_EINVAL, "project_ahead: workspace needs %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
   // the product of each layer, and whether it takes the small-batch kernel
   engram::ProjGateArgs pa[ENGRAM_MAX_AHEAD_LAYERS];
-  bool small[ENGRAM_MAX_AHEAD_LAYERS];
+  bool small[ENGRAM_MAX_AHEAD_LAYERS], frag[ENGRAM_MAX_AHEAD_LAYERS], fused[ENGRAM_MAX_AHEAD_LAYERS];
   void* e[ENGRAM_MAX_AHEAD_LAYERS];
   Carve c{static_cast<char*>(ws)};
   for (int l = 0; l < n_layers; ++l) {
     const engram_layer* L = layers[l];
     engram_decode_state* st = states != nullptr ? states[l] : nullptr;
-    e[l] = c.take<char>(rows_bytes(n_tok, L));
+    e[l] = c.take<char>(rows_bytes((n_tok + 63) / 64 * 64, L));
     const int64_t d_mem = static_cast<int64_t>(L->tables.n_tables) * L->tables.dim;
     const int M = g[l].branches, d = g[l].d;
     const bool mx = L->w_mx != nullptr;
@@ -955,6 +968,9 @@ ENGRAM_API engram_status engram_project_ahead(const int32_t* tokens, int64_t B, 
       p.adv_B = static_cast<int32_t>(B);
     }
     small[l] = engram::proj_gate_small_for(n_tok, p.N, d, p.K, mx) && p.K % (mx ? 512 : 64) == 0;
+    frag[l] = ahead_frag(L, n_tok, p.N, d, p.K);
+    if (frag[l]) p.w_frag = static_cast<const uint16_t*>(L->w_packed);
+    fused[l] = frag[l] && engram::ahead_fused_for(ta[l], n_tok, p.N, d, p.K);
     if (!small[l] && (mx || st != nullptr))
       return fail(ENGRAM_EUNSUPPORTED,
                   "project_ahead: layer %d's product (%lld tokens x %d columns) is above the small-batch range, which "
@@ -964,13 +980,35 @@ ENGRAM_API engram_status engram_project_ahead(const int32_t* tokens, int64_t B, 
   prof_begin();
   for (int l = 0; l < n_layers; l += 2) {
     const bool pair = l + 1 < n_layers;
+    // Steps 1-5 of the pair in one launch where both layers allow it
+    if (fused[l] && (!pair || fused[l + 1])) {
+      engram::AheadJob ja{}, jb{};
+      ja.g = gather_job(tokens, T, n_tok, layers[l], ha[l], ta[l], g[l].hdtype,
+                        states != nullptr ? states[l] : nullptr, e[l]);
+      ja.p = pa[l];
+      if (pair) {
+        jb.g = gather_job(tokens, T, n_tok, layers[l + 1], ha[l + 1], ta[l + 1], g[l + 1].hdtype,
+                          states != nullptr ? states[l + 1] : nullptr, e[l + 1]);
+        jb.p = pa[l + 1];
+      }
+      prof_mark(stream, "gather_proj_kernel");
+      const hipError_t he = engram::launch_ahead_fused(ja, pair ? &jb : nullptr, stream);
+      if (he != hipErrorNotSupported) {
+        if ((r = hip_status(he, "gather+projection launch")) != ENGRAM_OK) return r;
+        continue;
+      }
+    }
     // Steps 1-4 of the pair in one launch where the formats match
-    const engram::GatherJob ja = gather_job(tokens, T, n_tok, layers[l], ha[l], ta[l], g[l].hdtype,
-                                            states != nullptr ? states[l] : nullptr, e[l]);
+    const int out_a = frag[l] ? engram::kGatherOutFrag16 : -1;
+    const int out_b = pair && frag[l + 1] ? engram::kGatherOutFrag16 : -1;
+    engram::GatherJob ja = gather_job(tokens, T, n_tok, layers[l], ha[l], ta[l], g[l].hdtype,
+                                      states != nullptr ? states[l] : nullptr, e[l]);
+    if (out_a >= 0) ja.out_dtype = out_a;
     bool gathered = false;
     if (pair) {
-      const engram::GatherJob jb = gather_job(tokens, T, n_tok, layers[l + 1], ha[l + 1], ta[l + 1], g[l + 1].hdtype,
-                                              states != nullptr ? states[l + 1] : nullptr, e[l + 1]);
+      engram::GatherJob jb = gather_job(tokens, T, n_tok, layers[l + 1], ha[l + 1], ta[l + 1], g[l + 1].hdtype,
+                                        states != nullptr ? states[l + 1] : nullptr, e[l + 1]);
+      if (out_b >= 0) jb.out_dtype = out_b;
       prof_mark(stream, "gather2_kernel");
       const hipError_t he = engram::launch_hash_gather2(ja, jb, stream);
       if (he != hipErrorNotSupported) {
@@ -981,7 +1019,8 @@ ENGRAM_API engram_status engram_project_ahead(const int32_t* tokens, int64_t B, 
     if (!gathered) {
       for (int k = l; k < l + (pair ? 2 : 1); ++k) {
         engram_decode_state* st = states != nullptr ? states[k] : nullptr;
-        if ((r = run_retrieve(tokens, B, T, layers[k], ha[k], ta[k], g[k].hdtype, st, e[k], stream)) != ENGRAM_OK)
+        if ((r = run_retrieve(tokens, B, T, layers[k], ha[k], ta[k], g[k].hdtype, st, e[k], stream,
+                              frag[k] ? engram::kGatherOutFrag16 : -1)) != ENGRAM_OK)
           return r;
       }
     }
@@ -1167,6 +1206,19 @@ ENGRAM_API engram_status engram_quantize_mxfp8(const void* x, engram_dtype dtype
   if (!aligned(x, dtype == ENGRAM_F32 ? 32 : 16) || !aligned(q, 8))
     return fail(ENGRAM_EINVAL, "quantize_mxfp8: x must be 16-byte (BF16) or 32-byte (F32) aligned, q 8-byte");
   return hip_status(engram::launch_mx_quantize(x, dtype, rows, cols, q, scale, stream), "quantize launch");
+}
+
+ENGRAM_API engram_status engram_pack_bf16(const void* w, int64_t rows, int64_t cols, void* packed,
+                                          hipStream_t stream) {
+  if (rows < 0 || cols < 0 || rows % 32 != 0 || cols % 16 != 0)
+    return fail(ENGRAM_EINVAL, "pack_bf16: rows a non-negative multiple of 32 and cols of 16");
+  if (rows * cols == 0) return ENGRAM_OK;
+  if (w == nullptr || packed == nullptr) return fail(ENGRAM_EINVAL, "pack_bf16: w and packed must be non-NULL");
+  if (!aligned(w, 16) || !aligned(packed, 16))
+    return fail(ENGRAM_EINVAL, "pack_bf16: w and packed must be 16-byte aligned");
+  return hip_status(engram::launch_bf16_pack(static_cast<const uint16_t*>(w), rows, cols,
+                                             static_cast<uint16_t*>(packed), stream),
+                    "pack launch");
 }
 
 ENGRAM_API engram_status engram_pack_mxfp8(const uint8_t* q, const uint8_t* scale, int64_t rows, int64_t cols,

@@ -59,6 +59,18 @@ struct HotArgs {
 };
 
 // Where the fused hash+gather reads its ids.
+// What Steps 1-2 read: the token ids, P, the decode history (null = pad 0)
+// and the window's shape, in one 48-byte block.
+struct WindowSrc {
+  const int32_t* tokens;
+  const int32_t* proj;
+  const int32_t* hist;
+  uint32_t* err;   // debug build: the caller's error word, or null
+  int32_t T;       // tokens per sequence (the batch below 2^31 tokens)
+  int32_t max_n;
+  int32_t vocab;
+};
+
 struct HashSrc {
   const int32_t* tokens;
   const int32_t* proj;
@@ -94,10 +106,24 @@ hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t co
 // of the FP8 matrix cores; rows a multiple of 32, cols of 256.
 hipError_t launch_mx_pack(const uint8_t* q, const uint8_t* scale, int64_t rows, int64_t cols, uint8_t* packed,
                           hipStream_t s);
+// bf16 W [rows][cols] as A operands of v_mfma_f32_32x32x16_bf16, in the
+// kGatherOutFrag16 order with row blocks for token blocks; rows a multiple of
+// 32, cols of 32.
+hipError_t launch_bf16_pack(const uint16_t* w, int64_t rows, int64_t cols, uint16_t* packed, hipStream_t s);
 
 // Gather output in MXFP8: [n_tok][n_tables*dim] E4M3 codes followed by
 // [n_tok][n_tables*dim/32] scale bytes (dim a multiple of 32).
 constexpr int kGatherOutMXFP8 = 3;
+// Gather output in bf16 as operands of v_mfma_f32_32x32x16_bf16 (the B
+// side): for token block tb (32 tokens), K16 step ks and lane l = 32h + r,
+// 16 bytes at lane slot (tb * K/16 + ks) * 64 + l hold the 8 values of token
+// 32tb + r at columns 32(ks/2) + 16h + 8(ks%2) .. +7.  Within every 32-column
+// group the two steps take the group's halves crosswise, so that one lane's
+// two steps read 16 consecutive values of a row; W packs the same way
+// (launch_bf16_pack), and the product is the same sum in another order.  K a
+// multiple of 32; the last block is whole, its rows past the last token left
+// unwritten.
+constexpr int kGatherOutFrag16 = 4;
 
 hipError_t launch_gather(const int32_t* z, int64_t n_tok, const TableArgs& ta, int out_dtype,
                          void* e, hipStream_t s);
@@ -149,6 +175,9 @@ struct ProjGateArgs {
   // ([n_tok][N] float32: v, then the keys) instead of v and the gate sums; H
   // is then not read
   float* kv_out;
+  // with kv_out: W and e both in fragment order (launch_bf16_pack,
+  // kGatherOutFrag16), for the register-operand decode product
+  const uint16_t* w_frag;
   // Decode-state advance folded into this launch (adv_B > 0): workgroup 0
   // shifts the last N-1 compressed ids of every sequence's T = adv_T new
   // tokens into st_ids and adds adv_T to st_pos.  Nothing in the launch reads
@@ -184,8 +213,16 @@ hipError_t launch_proj_gate(const ProjGateArgs& a, hipStream_t s);
 // Step 5 of up to two layers into float32 rows (ProjGateArgs.kv_out set on
 // both) with the small-batch kernel, in one launch; hipErrorNotSupported
 // (nothing launched) when a layer's size or format does not take that kernel
-// or the two differ in format.  b may be null.
+// or the two differ in format.  b may be null.  Layers with w_frag set take
+// the fragment-operand kernel (both or neither of the two).
 hipError_t launch_project_layers(const ProjGateArgs& a, const ProjGateArgs* b, hipStream_t s);
+// Whether a float32 product of this size takes the fragment-operand kernel
+// (bf16, K a multiple of 128 up to 1024, in the small-batch range).
+bool proj_frag_for(int64_t n_tok, int N, int d, int K);
+// The fragment-operand product of one or two layers of the same K
+// (hipErrorNotSupported when a layer does not fit proj_frag_for).
+hipError_t launch_project_frag(const ProjGateArgs& a, const ProjGateArgs* b, hipStream_t s);
+
 
 // Whole-row gate statistics from given projections: stats [n_tok][1+M].
 hipError_t launch_gate_stats(const void* H, const void* kv, int64_t n_tok, const GateConvArgs& g, float4* stats,
@@ -235,6 +272,49 @@ hipError_t launch_conv_gather(const ConvArgs& a, int vdtype, const GatherJob& gj
 // hipErrorNotSupported (nothing launched) otherwise.  The two jobs travel in
 // the kernel-argument segment (about 4.4 KiB).
 hipError_t launch_hash_gather2(const GatherJob& a, const GatherJob& b, hipStream_t s);
+
+// Steps 1-5 of one layer in one launch: the fragment-operand product whose
+// wavefronts hash and read their own table rows (g.out_dtype unused; no hot
+// tier, cache or access counts).  p.e is unused.
+struct AheadJob {
+  // everything a workgroup reads, in the first 128 bytes (two scalar
+  // loads, in flight together): copies of fields of g and p
+  struct Head {
+    const int32_t* tokens;
+    const int32_t* proj;
+    const int32_t* hist;
+    const uint16_t* w_frag;
+    const void* rows;
+    const float* scale;
+    float* kv_out;
+    int32_t* st_ids;
+    int32_t* st_pos;
+    uint32_t* err;
+    int32_t T;
+    int32_t max_n;
+    int32_t vocab;
+    int32_t n_tok;
+    int32_t N;
+    int32_t tiles_f;
+    int32_t has_state;   // advance the decode state (T = 1)
+    uint32_t slot;       // the layer's first arrival count
+    int64_t pad[2];
+  } head;
+  GatherJob g;
+  ProjGateArgs p;
+};
+// Whether layer products with these tables take launch_ahead_fused: a
+// fragment-operand product with K = 512 or 1024, table dim 32, 64 or 128,
+// int8 or bf16 rows.
+bool ahead_fused_for(const TableArgs& ta, int64_t n_tok, int N, int d, int K);
+// One or two layers (same K and table dtype; b may be null).  A launch that
+// advances decode states (T = 1, up to 2048 sequences) has the last
+// workgroup of each token tile to finish its reads do that tile's advance,
+// counted in device-global arrival slots; calls that run concurrently on one
+// device take different slots (blocks of a ring of kAheadSlots, taken in
+// turn: 64 launches may be in flight at once).
+constexpr int kAheadSlots = 4096;
+hipError_t launch_ahead_fused(const AheadJob& a, const AheadJob* b, hipStream_t s);
 
 // Writes the chunk's last conv inputs into the circular state, shifts ids
 // (when tokens/proj are given) and advances pos.

@@ -149,6 +149,7 @@ template <int IN, bool HOT>
 hipError_t launch_hashed(int64_t n_tok, const TableArgs& ta, int out, void* e, const HashSrc& hs, hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
   if (out == kOutMXFP8) return launch_hashed_items<IN, kOutMXFP8, HOT>(n_tok, ta, e, hs, s);
+  if (out == kOutFrag16) return launch_hashed_items<IN, kOutFrag16, HOT>(n_tok, ta, e, hs, s);
   if (out == ENGRAM_BF16) return launch_hashed_items<IN, ENGRAM_BF16, HOT>(n_tok, ta, e, hs, s);
   return launch_hashed_items<IN, ENGRAM_F32, HOT>(n_tok, ta, e, hs, s);
 }
@@ -156,6 +157,7 @@ hipError_t launch_hashed(int64_t n_tok, const TableArgs& ta, int out, void* e, c
 template <int IN>
 hipError_t launch_gather2_in(const GatherJob& a, const GatherJob& b, hipStream_t s) {
   if (a.out_dtype == kOutMXFP8) return launch_gather2_t<IN, kOutMXFP8>(a, b, s);
+  if (a.out_dtype == kOutFrag16) return launch_gather2_t<IN, kOutFrag16>(a, b, s);
   if (a.out_dtype == ENGRAM_BF16) return launch_gather2_t<IN, ENGRAM_BF16>(a, b, s);
   return launch_gather2_t<IN, ENGRAM_F32>(a, b, s);
 }

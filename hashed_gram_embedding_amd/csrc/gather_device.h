@@ -13,6 +13,7 @@
 namespace engram {
 
 constexpr int kOutMXFP8 = kGatherOutMXFP8;
+constexpr int kOutFrag16 = kGatherOutFrag16;
 
 template <int IN>
 __device__ __forceinline__ void load8(const void* base, const float* scale, int64_t row, int dim,
@@ -107,7 +108,6 @@ __device__ __forceinline__ void hashed_gather_body(uint32_t gid, uint32_t n_tok,
   const int64_t row_offset = ta.row_offset[j];
   const TableHash th = table_hash(hs.a, j);
   const uint32_t T = static_cast<uint32_t>(hs.T);
-  const int hist_len = hs.a.max_n - 1;
 
   uint32_t b[ITEMS], t[ITEMS];
   bool live[ITEMS];
@@ -119,32 +119,9 @@ __device__ __forceinline__ void hashed_gather_body(uint32_t gid, uint32_t n_tok,
     b[q] = tc / T;
     t[q] = tc - b[q] * T;
   }
-  // Steps 1-2: ids of the suffix window, newest first (clamped positions,
-  // patched from the history below)
-  int32_t tk[ITEMS][ENGRAM_MAX_ORDER];
-#pragma unroll
-  for (int q = 0; q < ITEMS; ++q)
-#pragma unroll
-    for (int i = 0; i < ENGRAM_MAX_ORDER; ++i)
-      tk[q][i] = hs.tokens[b[q] * T + (t[q] >= static_cast<uint32_t>(i) ? t[q] - i : 0u)];
+  // Steps 1-2: ids of the suffix window, newest first
   uint32_t x[ITEMS][ENGRAM_MAX_ORDER];
-#pragma unroll
-  for (int q = 0; q < ITEMS; ++q)
-#pragma unroll
-    for (int i = 0; i < ENGRAM_MAX_ORDER; ++i)
-      x[q][i] = static_cast<uint32_t>(hs.proj[token_in_vocab(tk[q][i], hs.a.vocab, hs.a.err)]);
-#pragma unroll
-  for (int q = 0; q < ITEMS; ++q) {
-    if (t[q] < static_cast<uint32_t>(hist_len)) {
-#pragma unroll
-      for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) {
-        const int p = static_cast<int>(t[q]) - i;
-        if (p < 0)
-          x[q][i] = hs.hist != nullptr && hist_len + p >= 0
-                        ? static_cast<uint32_t>(hs.hist[b[q] * hist_len + hist_len + p]) : 0u;
-      }
-    }
-  }
+  window_ids_n<ITEMS>(hs, b, t, x);
   // Step 3: cold row of every item
   int64_t crow[ITEMS];
 #pragma unroll
@@ -236,9 +213,19 @@ __device__ __forceinline__ void hashed_gather_body(uint32_t gid, uint32_t n_tok,
   }
   const int64_t dm = static_cast<int64_t>(nt) * ta.dim;
 #pragma unroll
-  for (int q = 0; q < ITEMS; ++q)
-    store8<IN, OUT>(e, (static_cast<int64_t>(g) * ITEMS + q) * dm + j * ta.dim + c * 8,
-                    static_cast<int64_t>(n_tok) * dm, c, f[q], raw[q], live[q]);
+  for (int q = 0; q < ITEMS; ++q) {
+    const int64_t tok = static_cast<int64_t>(g) * ITEMS + q;
+    const int64_t k = static_cast<int64_t>(j) * ta.dim + c * 8;
+    if constexpr (OUT == kOutFrag16) {
+      // columns 32q + 16h + 8s .. +7 land in lane slot 32h + tok % 32 of
+      // fragment (tok / 32, step 2q + s)
+      const int64_t ks = (k >> 5) * 2 + ((k >> 3) & 1);
+      const int64_t slot = ((tok >> 5) * (dm >> 4) + ks) * 64 + ((k >> 4) & 1) * 32 + (tok & 31);
+      store8<IN, ENGRAM_BF16>(e, slot * 8, 0, c, f[q], raw[q], live[q]);
+    } else {
+      store8<IN, OUT>(e, tok * dm + k, static_cast<int64_t>(n_tok) * dm, c, f[q], raw[q], live[q]);
+    }
+  }
 }
 
 // Items per thread of the hashed gather for n_tok tokens and per_group

@@ -58,6 +58,90 @@ __device__ __forceinline__ void window_ids(const int32_t* __restrict__ tokens, c
   }
 }
 
+__device__ __forceinline__ WindowSrc window_src(const HashSrc& hs) {
+  return WindowSrc{hs.tokens, hs.proj, hs.hist, hs.a.err, static_cast<int32_t>(hs.T), hs.a.max_n, hs.a.vocab};
+}
+
+// Steps 1-2 for ITEMS tokens at positions t[q] of sequences b[q], in two
+// halves so that a kernel can issue other loads in between.  window_loads
+// loads the P values of the window's tokens (xp) and the history ids that
+// positions before the sequence start need (hv, 0 where there are none):
+// the history index does not depend on the token ids, so those loads go out
+// just before the token loads, into registers of their own, and the P
+// lookups take the second and last memory latency.  (Memory reads return in
+// order, so once the P lookups are issued the history has arrived.)
+// window_select then forms x[q][i] = x'_{t-i}, newest first.
+// HIST_ALL: the caller guarantees hs.hist != null and T <= max_n - 1 (every
+// token reads history, as in decode), so that the choice below is not a
+// branch in the kernel.
+template <int ITEMS, bool HIST_ALL = false>
+__device__ __forceinline__ void window_loads(const WindowSrc& hs, const uint32_t (&b)[ITEMS],
+                                             const uint32_t (&t)[ITEMS], uint32_t (&xp)[ITEMS][ENGRAM_MAX_ORDER],
+                                             uint32_t (&hv)[ITEMS][ENGRAM_MAX_ORDER]) {
+  const uint32_t T = static_cast<uint32_t>(hs.T);
+  const int hl = hs.max_n - 1;
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q)
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) hv[q][i] = 0u;
+  if (HIST_ALL || (hs.hist != nullptr && T <= static_cast<uint32_t>(hl))) {
+    // every token reads history (decode): loads without branches or
+    // selects, so that none waits for another.  For i <= hl and t < i the
+    // index hl + t - i is in range; positions i > hl (>= the largest order)
+    // enter no hash (their multipliers are 0) and no hot key, so the clamped
+    // index serves them as well as the pad would.
+#pragma unroll
+    for (int q = 0; q < ITEMS; ++q)
+#pragma unroll
+      for (int i = 1; i < ENGRAM_MAX_ORDER; ++i) {
+        const int idx = hl + static_cast<int>(t[q]) - i;   // index in the history of position t - i
+        hv[q][i] = static_cast<uint32_t>(hs.hist[b[q] * hl + min(max(idx, 0), hl - 1)]);
+      }
+  } else if (!HIST_ALL && hs.hist != nullptr) {
+    // only tokens near a sequence start do
+#pragma unroll
+    for (int q = 0; q < ITEMS; ++q) {
+      if (t[q] < static_cast<uint32_t>(hl)) {
+#pragma unroll
+        for (int i = 1; i < ENGRAM_MAX_ORDER; ++i) {
+          const int idx = hl + static_cast<int>(t[q]) - i;
+          if (idx >= 0 && idx < hl) hv[q][i] = static_cast<uint32_t>(hs.hist[b[q] * hl + idx]);
+        }
+      }
+    }
+  }
+  int32_t tk[ITEMS][ENGRAM_MAX_ORDER];
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q)
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDER; ++i)
+      tk[q][i] = hs.tokens[b[q] * T + (t[q] >= static_cast<uint32_t>(i) ? t[q] - i : 0u)];
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q)
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDER; ++i)
+      xp[q][i] = static_cast<uint32_t>(hs.proj[token_in_vocab(tk[q][i], hs.vocab, hs.err)]);
+}
+
+template <int ITEMS>
+__device__ __forceinline__ void window_select(const uint32_t (&t)[ITEMS], const uint32_t (&xp)[ITEMS][ENGRAM_MAX_ORDER],
+                                              const uint32_t (&hv)[ITEMS][ENGRAM_MAX_ORDER],
+                                              uint32_t (&x)[ITEMS][ENGRAM_MAX_ORDER]) {
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q)
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDER; ++i)
+      x[q][i] = t[q] >= static_cast<uint32_t>(i) ? xp[q][i] : hv[q][i];   // before the start: history or pad 0
+}
+
+template <int ITEMS>
+__device__ __forceinline__ void window_ids_n(const HashSrc& hs, const uint32_t (&b)[ITEMS],
+                                             const uint32_t (&t)[ITEMS], uint32_t (&x)[ITEMS][ENGRAM_MAX_ORDER]) {
+  uint32_t xp[ITEMS][ENGRAM_MAX_ORDER], hv[ITEMS][ENGRAM_MAX_ORDER];
+  window_loads<ITEMS>(window_src(hs), b, t, xp, hv);
+  window_select<ITEMS>(t, xp, hv, x);
+}
+
 // Hash constants of table j.  Kernels read them before the token ids, so
 // that these argument loads and the id loads are in flight together.  The
 // multipliers of positions i >= n are 0, so every position can be taken
@@ -97,6 +181,29 @@ __device__ __forceinline__ int32_t hash_index(const int32_t* __restrict__ tokens
   uint32_t x[ENGRAM_MAX_ORDER];
   window_ids(tokens, proj, hist, a.max_n, a.vocab, a.err, b, t, T, x);
   return hash_of_ids(x, th);
+}
+
+// Decode-state advance (ProjGateArgs.adv_B > 0), by the threads of
+// workgroup 0: ids <- last N-1 of (ids ++ P(tokens)), pos += T.
+__device__ __forceinline__ void advance_state(const ProjGateArgs& a, uint32_t bid) {
+  if (a.adv_B <= 0 || bid != 0) return;
+  const int hl = a.max_n - 1;
+  for (int b = threadIdx.x; b < a.adv_B; b += blockDim.x) {
+    int32_t next[ENGRAM_MAX_ORDER];
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDER - 1; ++i) {
+      if (i < hl) {
+        const int64_t idx = static_cast<int64_t>(a.adv_T) + i;   // index in (old ids ++ chunk ids)
+        next[i] = idx < hl ? a.st_ids[static_cast<int64_t>(b) * hl + idx]
+                           : a.proj[token_in_vocab(a.tokens[static_cast<int64_t>(b) * a.adv_T + idx - hl], a.vocab,
+                                                   a.err)];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDER - 1; ++i)
+      if (i < hl) a.st_ids[static_cast<int64_t>(b) * hl + i] = next[i];
+    a.st_pos[b] += a.adv_T;
+  }
 }
 
 }  // namespace engram

@@ -69,7 +69,33 @@ mx_pack_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ scale,
   }
 }
 
+// bf16 W as A operands of v_mfma_f32_32x32x16_bf16: for 32-row block b and
+// K16 step ks, lane l = 32h + r holds the 8 values of row 32b + r at columns
+// 32(ks/2) + 16h + 8(ks%2) .. +7 (the halves of each 32-column group taken
+// crosswise, as the gathered rows are).  One thread per (block, step, lane).
+__global__ void __launch_bounds__(256)
+bf16_pack_kernel(const uint16_t* __restrict__ w, int64_t rows, int cols, uint16_t* __restrict__ packed) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int ks_n = cols / 16;
+  if (gid >= rows / 32 * ks_n * 64) return;
+  const int lane = static_cast<int>(gid & 63);
+  const int64_t rest = gid >> 6;
+  const int ks = static_cast<int>(rest % ks_n);
+  const int64_t row = rest / ks_n * 32 + (lane & 31);
+  const int col = (ks >> 1) * 32 + (lane >> 5) * 16 + (ks & 1) * 8;
+  reinterpret_cast<uint4*>(packed)[gid] = *reinterpret_cast<const uint4*>(w + row * cols + col);
+}
+
 }  // namespace
+
+hipError_t launch_bf16_pack(const uint16_t* w, int64_t rows, int64_t cols, uint16_t* packed, hipStream_t s) {
+  if (rows % 32 != 0 || cols % 32 != 0) return hipErrorInvalidValue;
+  const int64_t n = rows / 32 * (cols / 16) * 64;
+  if (n == 0) return hipSuccess;
+  launch_k(bf16_pack_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, w, rows,
+           static_cast<int>(cols), packed);
+  return hipGetLastError();
+}
 
 hipError_t launch_mx_pack(const uint8_t* q, const uint8_t* scale, int64_t rows, int64_t cols, uint8_t* packed,
                           hipStream_t s) {

@@ -60,29 +60,6 @@ constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
-// Decode-state advance (ProjGateArgs.adv_B > 0), by the threads of
-// workgroup 0: ids <- last N-1 of (ids ++ P(tokens)), pos += T.
-__device__ __forceinline__ void advance_state(const ProjGateArgs& a, uint32_t bid) {
-  if (a.adv_B <= 0 || bid != 0) return;
-  const int hl = a.max_n - 1;
-  for (int b = threadIdx.x; b < a.adv_B; b += blockDim.x) {
-    int32_t next[ENGRAM_MAX_ORDER];
-#pragma unroll
-    for (int i = 0; i < ENGRAM_MAX_ORDER - 1; ++i) {
-      if (i < hl) {
-        const int64_t idx = static_cast<int64_t>(a.adv_T) + i;   // index in (old ids ++ chunk ids)
-        next[i] = idx < hl ? a.st_ids[static_cast<int64_t>(b) * hl + idx]
-                           : a.proj[token_in_vocab(a.tokens[static_cast<int64_t>(b) * a.adv_T + idx - hl], a.vocab,
-                                                   a.err)];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < ENGRAM_MAX_ORDER - 1; ++i)
-      if (i < hl) a.st_ids[static_cast<int64_t>(b) * hl + i] = next[i];
-    a.st_pos[b] += a.adv_T;
-  }
-}
-
 // Main loop: slices go straight into LDS (global_load_lds_dwordx4), NBUF - 1
 // of them in flight while the oldest landed one is multiplied.  With one
 // slice in flight (NBUF = 2) the loop waits about as long for each slice as
@@ -1206,6 +1183,8 @@ hipError_t launch_small2(const ProjGateArgs& a, const ProjGateArgs& b, hipStream
 }
 
 hipError_t launch_project_layers(const ProjGateArgs& in_a, const ProjGateArgs* in_b, hipStream_t s) {
+  if (in_a.w_frag != nullptr) return launch_project_frag(in_a, in_b, s);
+  if (in_b != nullptr && in_b->w_frag != nullptr) return hipErrorNotSupported;
   const bool mx = in_a.e_scale != nullptr;
   auto fits = [&](const ProjGateArgs& x) {
     return x.kv_out != nullptr && (x.e_scale != nullptr) == mx && x.N % kSmallTF == 0 &&

@@ -60,7 +60,7 @@ class HotTierStruct(ctypes.Structure):
 class LayerStruct(ctypes.Structure):
     _fields_ = [("hash", HashParams), ("tables", Tables), ("w", ctypes.c_void_p), ("gc", GateConvParams),
                 ("w_mx", ctypes.c_void_p), ("w_mx_scale", ctypes.c_void_p), ("w_mx_packed", ctypes.c_void_p),
-                ("hot", ctypes.POINTER(HotTierStruct))]
+                ("w_packed", ctypes.c_void_p), ("hot", ctypes.POINTER(HotTierStruct))]
 
 
 class DecodeStateStruct(ctypes.Structure):
@@ -112,6 +112,7 @@ def load_library(path: str) -> ctypes.CDLL:
                                            ctypes.POINTER(DecodeStateStruct), vp, vp, vp, sz, vp]),
         "engram_quantize_mxfp8": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "engram_pack_mxfp8": (i32, [vp, vp, i64, i64, vp, vp]),
+        "engram_pack_bf16": (i32, [vp, i64, i64, vp, vp]),
         "engram_project_ahead_workspace": (sz, [i64, i64, i32, ctypes.POINTER(ctypes.POINTER(LayerStruct))]),
         "engram_project_ahead": (i32, [vp, i64, i64, i32, ctypes.POINTER(ctypes.POINTER(LayerStruct)),
                                        ctypes.POINTER(ctypes.POINTER(DecodeStateStruct)), ctypes.POINTER(vp), vp, sz,
@@ -154,6 +155,7 @@ def exported_names():
             "engram_forward_workspace", "engram_forward", "engram_forward_noalloc", "engram_retrieve", "engram_forward_retrieved_workspace",
             "engram_forward_retrieved", "engram_cache_build_workspace", "engram_cache_build",
             "engram_cache_update_workspace", "engram_cache_update", "engram_quantize_mxfp8", "engram_pack_mxfp8",
+            "engram_pack_bf16",
             "engram_project_ahead_workspace", "engram_project_ahead", "engram_forward_projected_workspace",
             "engram_forward_projected",
             "engram_hot_buckets", "engram_hot_build", "engram_hot_lookup", "engram_forward_retrieved_prefetch",
@@ -218,7 +220,7 @@ class Layer:
 
     def __init__(self, li, hdtype: str, device="cuda", rows_device: Optional[torch.Tensor] = None,
                  rows_ptr: Optional[int] = None, scale_ptr: Optional[int] = None, mxfp8: bool = False,
-                 mx_packed: bool = True):
+                 mx_packed: bool = True, bf16_packed: bool = True):
         hp, tab = li.hash, li.tables
         self.li = li
         self.hdtype = _DT[hdtype]
@@ -247,6 +249,12 @@ class Layer:
         self.s.w = self.w.data_ptr()
         self.s.gc = GateConvParams(li.d, li.branches, li.kernel_w, li.dilation, li.eps, self.hdtype,
                                    self.conv_w.data_ptr())
+        self.w_packed = None
+        if bf16_packed and hdtype == "bf16" and self.w.shape[0] % 32 == 0 and self.w.shape[1] % 16 == 0:
+            # the fragment-ordered copy that the decode-size product loads into registers
+            self.w_packed = torch.empty_like(self.w)
+            pack_bf16(self.w, self.w_packed)
+            self.s.w_packed = self.w_packed.data_ptr()
         self.mxfp8 = mxfp8
         if mxfp8:
             n, k = self.w.shape
@@ -594,6 +602,12 @@ def pack_mxfp8(q: torch.Tensor, scale: torch.Tensor, packed: torch.Tensor, strea
     matrix cores' operand order (uint8 [rows*cols + rows*cols/32])."""
     rows, cols = q.shape
     _check(lib().engram_pack_mxfp8(_ptr(q), _ptr(scale), rows, cols, _ptr(packed), _stream(stream)))
+
+
+def pack_bf16(w: torch.Tensor, packed: torch.Tensor, stream=None):
+    """The bf16 W [rows, cols] in the matrix cores' operand order (same size)."""
+    rows, cols = w.shape
+    _check(lib().engram_pack_bf16(_ptr(w), rows, cols, _ptr(packed), _stream(stream)))
 
 
 def hot_lookup(tokens: torch.Tensor, spec, hot: HotTier, hist: Optional[torch.Tensor] = None,

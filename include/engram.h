@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 5
+#define ENGRAM_ABI_VERSION 6
 #define ENGRAM_MAX_TABLES 32 /* (N-1)*K */
 #define ENGRAM_MAX_ORDER 4   /* N */
 #define ENGRAM_MAX_KERNEL_W 8
@@ -188,6 +188,12 @@ typedef struct engram_layer {
      workgroup's token rows held on chip while W streams past them; results
      are identical to those without it.                                       */
   const uint8_t* w_mx_packed;
+  /* optional (NULL = none; bf16 layers): w in matrix-core fragment order from
+     engram_pack_bf16, 16-byte aligned.  Read only by engram_project_ahead,
+     whose bf16 products with n_tables*dim a multiple of 128 up to 1024 then
+     load both operands straight into registers; the float32 results agree
+     with those without it to rounding (the sums run in another order).        */
+  const void* w_packed;
   /* optional Engram-Nine hot tier (read on the host during each call; NULL =
      none): used by engram_forward and engram_retrieve.  Needs F32 or BF16
      tables; a hot hit reads no cold row and counts no access.                  */
@@ -352,7 +358,8 @@ engram_status engram_forward_retrieved_prefetch(const int32_t* tokens, const voi
  * engram_forward_projected reads them as advanced.  Layers go in pairs: one
  * launch gathers both layers' rows, one launch multiplies both (the
  * small-batch product; n_tok*(1+M)*d within its range, which a decode batch
- * of a few hundred sequences is).  Larger bf16 products without states run
+ * of a few hundred sequences is; layers with w_packed take its
+ * fragment-operand form).  Larger bf16 products without states run
  * the general product per layer; larger ones with states, or MXFP8 ones, are
  * ENGRAM_EUNSUPPORTED.  ws: at least engram_project_ahead_workspace() bytes,
  * 256-byte aligned (the gathered rows).
@@ -439,6 +446,14 @@ engram_status engram_quantize_mxfp8(const void* x, engram_dtype dtype, int64_t r
  * no-op. */
 engram_status engram_pack_mxfp8(const uint8_t* q, const uint8_t* scale, int64_t rows, int64_t cols,
                                 uint8_t* packed, hipStream_t stream);
+
+/* The bf16 W of a layer (w [rows][cols], device, 16-byte aligned) in the
+ * operand order of the bf16 matrix cores, for engram_layer.w_packed: packed
+ * (device, 16-byte aligned, rows*cols*2 bytes, owned by the caller) holds,
+ * for each 32-row block b and 16-column step s, 64 lane slots of 16 bytes
+ * (lane l = 32h + r: columns 16s + 8h .. +7 of row 32b + r).  rows a multiple
+ * of 32, cols of 16 (EINVAL otherwise); rows*cols = 0 is a no-op. */
+engram_status engram_pack_bf16(const void* w, int64_t rows, int64_t cols, void* packed, hipStream_t stream);
 
 /* Engram-Nine hot tier set-up and lookup (see engram_hot_tier).
  *

@@ -39,7 +39,7 @@ def test_exports_match_header():
 
 
 def test_abi_version():
-    assert eg.lib().engram_abi_version() == 5
+    assert eg.lib().engram_abi_version() == 6
 
 
 def _hash_params(**over):
@@ -354,6 +354,29 @@ def test_packed_mxfp8_weights_are_checked():
         need = L.engram_forward_workspace(1, 64, ctypes.byref(lay))
         st, msg = _status(L.engram_forward, p, p, 1, 64, ctypes.byref(lay), None, None, None, p, need, None)
         assert st == eg.EINVAL and text in msg, msg
+
+
+def test_packed_bf16_weights_are_checked():
+    """engram_pack_bf16 takes whole 32-row blocks and 16-column steps, and a
+    layer's packed bf16 W needs a bf16 layer and 16-byte alignment; all
+    refused before anything launches."""
+    L = eg.lib()
+    p = ctypes.c_void_p(0x10000)
+    for rows, cols in ((33, 64), (32, 24), (-32, 64), (64, -16)):
+        st, msg = _status(L.engram_pack_bf16, p, rows, cols, p, None)
+        assert st == eg.EINVAL and "pack_bf16" in msg, (rows, cols)
+    assert L.engram_pack_bf16(None, 0, 64, None, None) == eg.OK          # empty: a no-op
+    st, msg = _status(L.engram_pack_bf16, None, 32, 64, p, None)
+    assert st == eg.EINVAL and "non-NULL" in msg
+    st, msg = _status(L.engram_pack_bf16, p, 32, 64, ctypes.c_void_p(0x10008), None)
+    assert st == eg.EINVAL and "aligned" in msg
+    hp, keep_h = _hash_params()
+    t, keep_t = _tables(dtype=eg.BF16, dim=32)
+    for hdtype, packed, text in ((eg.F32, 0x40000, "bf16 layer"), (eg.BF16, 0x40008, "aligned")):
+        lay = eg.LayerStruct(hp, t, 0x10000, _gc(d=256, hdtype=hdtype), None, None, None, packed)
+        need = L.engram_forward_workspace(1, 64, ctypes.byref(lay))
+        st, msg = _status(L.engram_forward, p, p, 1, 64, ctypes.byref(lay), None, None, None, p, need, None)
+        assert st == eg.EINVAL and text in msg and "w_packed" in msg, msg
 
 
 def test_forward_noalloc_rejects_calls_beyond_its_scratch():
