@@ -350,14 +350,11 @@ __device__ __forceinline__ void ahead_fused_body(const AheadJob& J, int tf, int 
   // of the tile's feature workgroups to arrive writes the new ids, which the
   // lanes of its first wavefront already hold (x, newest first), and clears
   // the count.
-  if (hd.has_state) {
-    __shared__ uint32_t last;
-    if (threadIdx.x == 0) {
-      last = arrived_before == static_cast<uint32_t>(hd.tiles_f) - 1;
-      if (last) __hip_atomic_store(&ahead_arrivals[slot + tt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (last && threadIdx.x < 64) {
+  if (hd.has_state && wave == 0) {
+    // thread 0 holds the count; its wavefront writes (no barrier needed)
+    const bool last = __builtin_amdgcn_readfirstlane(arrived_before) == static_cast<uint32_t>(hd.tiles_f) - 1;
+    if (last) {
+      if (lane == 0) __hip_atomic_store(&ahead_arrivals[slot + tt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int hl = hd.max_n - 1;
       const int64_t tok = static_cast<int64_t>(tt) * kFragTile + 32 * h + r;   // this lane's own
       if (tok < hd.n_tok) {

@@ -585,6 +585,144 @@ __device__ __forceinline__ void conv_strip_body(const ConvArgs& a, int spx, int 
   }
 }
 
+// Steps 6-8 of one decode token (T = 1) on its float32 [v | k^(0..M-1)] row
+// (ConvArgs.sums_from_kv), for the pages' conv (w = 4, dilation 3) and d <=
+// 1024: workgroup (b, m) holds the token's whole row, 4 channels a thread.
+// The same arithmetic as the single-token strip conv, laid out for latency:
+// every argument is read up front in one batch, and pos (which the state's
+// halo slots depend on) is loaded with the row, H and the conv weights, so
+// that the chain is arguments -> (pos, row) -> state rows, with the gate's
+// block reduction inside the last latency.
+template <int HT>
+__global__ void __launch_bounds__(256)
+conv_decode_kernel(ConvArgs a) {
+  constexpr int KW = 4, DIL = 3, SPAN = (KW - 1) * DIL, CPT = 4;
+  const int b = blockIdx.x, m = blockIdx.y, tid = threadIdx.x;
+  void* const Hp = a.H;
+  const float* const vp = static_cast<const float*>(a.v);
+  const int64_t v_stride = a.v_stride;
+  const float* const conv_w = a.g.conv_w;
+  const int d = a.g.d, M = a.g.branches;
+  const float eps = a.g.eps;
+  float* const st_conv = a.st.conv;
+  const int32_t* const st_pos = a.st.pos;
+  const int has_state = a.has_state, pos_adv = a.pos_advanced, commit_u = a.commit_u;
+  float* const alpha_out = a.alpha_out;
+  float* const gamma_out = a.gamma_out;
+  float* const y_out = a.y_out;
+  // one batch of argument loads, then one wait (the compiler would otherwise
+  // issue each where it is first needed and wait for it there)
+  asm volatile("" ::"s"(Hp), "s"(vp), "s"(v_stride), "s"(conv_w), "s"(d), "s"(M), "s"(eps), "s"(st_conv),
+               "s"(st_pos), "s"(has_state), "s"(pos_adv), "s"(commit_u));
+  asm volatile("" ::"s"(alpha_out), "s"(gamma_out), "s"(y_out));
+  __builtin_amdgcn_sched_barrier(0);
+
+  const uint32_t c = tid * CPT;
+  const bool active = c < static_cast<uint32_t>(d);
+  const uint32_t cc = active ? c : 0;
+  const int64_t row = b;   // T = 1: token b of the batch
+  const float* vrow = vp + row * v_stride;
+  char* hrow = static_cast<char*>(Hp) + (row * M + m) * d * (HT == ENGRAM_BF16 ? 2 : 4);
+  const int32_t pos_raw = has_state ? st_pos[b] : 0;
+  float v[CPT], kk[CPT], h[CPT];
+  loadc<ENGRAM_F32, CPT>(vrow, cc, v);
+  loadc<ENGRAM_F32, CPT>(vrow, static_cast<uint32_t>((1 + m) * d) + cc, kk);
+  loadc<HT, CPT>(hrow, cc, h);
+  float wt[CPT][KW];
+  {
+    const float* wm = conv_w + static_cast<int64_t>(m) * d * KW;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const float4 q = *reinterpret_cast<const float4*>(wm + (cc + i) * KW);
+      wt[i][0] = q.x; wt[i][1] = q.y; wt[i][2] = q.z; wt[i][3] = q.w;
+    }
+  }
+  // the taps' halo rows r = 0, 3, 6 (positions pos - 9, - 6, - 3): the
+  // state's ring slots, which already hold u (gamma 1); without a state the
+  // chunk starts here, and they are padding (gamma 0 times the clamped row)
+  const int64_t pos = static_cast<int64_t>(pos_raw) - (pos_adv ? 1 : 0);
+  float hv[KW - 1][CPT];
+  float hg = 0.f;
+  if (has_state) {
+    hg = 1.0f;
+#pragma unroll
+    for (int j = 0; j < KW - 1; ++j) {
+      int slot = static_cast<int>((pos + (j * DIL - SPAN)) % SPAN);
+      if (slot < 0) slot += SPAN;
+      loadc<ENGRAM_F32, CPT>(st_conv + ((static_cast<int64_t>(b) * M + m) * SPAN + slot) * d, cc, hv[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KW - 1; ++j)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) hv[j][i] = v[i];
+  }
+
+  // the gate's four sums over the row (the strip conv's order)
+  __shared__ float4 wsum[4];
+  __shared__ float ag[2];
+  float s_hh = 0.f, s_kk = 0.f, s_hk = 0.f, s_vv = 0.f;
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      s_hh += h[i] * h[i];
+      s_kk += kk[i] * kk[i];
+      s_hk += h[i] * kk[i];
+      s_vv += v[i] * v[i];
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    s_hh += __shfl_xor(s_hh, off, 64);
+    s_kk += __shfl_xor(s_kk, off, 64);
+    s_hk += __shfl_xor(s_hk, off, 64);
+    s_vv += __shfl_xor(s_vv, off, 64);
+  }
+  if ((tid & 63) == 0) wsum[tid >> 6] = make_float4(s_hh, s_kk, s_hk, s_vv);
+  __syncthreads();
+  if (tid == 0) {
+    float4 q = wsum[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) q = make_float4(q.x + wsum[w].x, q.y + wsum[w].y, q.z + wsum[w].z, q.w + wsum[w].w);
+    const float inv_d = 1.0f / static_cast<float>(d);
+    const float rh = 1.0f / sqrtf(q.x * inv_d + eps);
+    const float rk = 1.0f / sqrtf(q.y * inv_d + eps);
+    const float logit = q.z * rh * rk / sqrtf(static_cast<float>(d));
+    const float al = 1.0f / (1.0f + expf(-logit));
+    const float gm = al / sqrtf(al * al * (q.w * inv_d) + eps);
+    const int64_t o = row * M + m;
+    if (alpha_out != nullptr) alpha_out[o] = al;
+    if (gamma_out != nullptr) gamma_out[o] = gm;
+    ag[0] = al;
+    ag[1] = gm;
+  }
+  __syncthreads();
+  const float al = ag[0], gm = ag[1];
+
+  // u = gamma v, the dilated causal taps, SiLU, residual
+  float u[CPT], y[CPT], hn[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    u[i] = gm * v[i];
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < KW - 1; ++j) acc += wt[i][j] * (hg * hv[j][i]);
+    acc += wt[i][KW - 1] * u[i];
+    y[i] = silu(acc) + al * v[i];
+    hn[i] = h[i] + y[i];
+  }
+  if (active) {
+    storec<HT, CPT>(hrow, c, hn);
+    if (y_out != nullptr) storec<ENGRAM_F32, CPT>(y_out + (row * M + m) * d, c, y);
+    // the new position's conv input goes to its ring slot (pos % SPAN, which
+    // held position pos - SPAN: read above as the oldest tap, by this thread)
+    if (commit_u && has_state) {
+      const int slot = static_cast<int>(pos % SPAN);
+      storec<ENGRAM_F32, CPT>(st_conv + ((static_cast<int64_t>(b) * M + m) * SPAN + slot) * d, c, u);
+    }
+  }
+}
+
 template <int HT, int VT, int KW, int DIL, int TS, int CPT>
 __global__ void __launch_bounds__(256)
 conv_strip_kernel(ConvArgs a, int spx) {
@@ -798,9 +936,16 @@ hipError_t launch_conv_gather(const ConvArgs& a, int vdtype, const GatherJob& gj
 hipError_t launch_conv(const ConvArgs& a, int vdtype, hipStream_t s) {
   if (a.B * a.T == 0) return hipSuccess;
   if (a.sums_from_kv) {
-    // the single-token strip conv with the whole row in one workgroup
-    if (conv_strip_ts(a) != 1 || a.g.d > 256 * 4 || vdtype != ENGRAM_F32) return hipErrorInvalidValue;
-    return launch_conv_strip<4, 3, 1, 4>(a, vdtype, s);
+    // a single token per sequence with the whole row in one workgroup
+    if (conv_strip_ts(a) != 1 || a.g.d > 256 * 4 || vdtype != ENGRAM_F32 || a.B > 0x7fffffff ||
+        a.g.branches > 65535)
+      return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(a.B), static_cast<unsigned>(a.g.branches));
+    if (a.g.hdtype == ENGRAM_BF16)
+      launch_k(conv_decode_kernel<ENGRAM_BF16>, grid, dim3(256), 0, s, a);
+    else
+      launch_k(conv_decode_kernel<ENGRAM_F32>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
   }
   // both conv kernels stage at most kConvMaxStats statistics per row (the
   // projection launchers never produce more)

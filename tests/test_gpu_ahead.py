@@ -149,6 +149,7 @@ CASES = [
     ("3 layers M=4", dict(B=2, T=40, layers=3, branches=4), False, ["gather_proj_kernel", "gather_proj_kernel"]),
     ("3 layers M=4 lds", dict(B=2, T=40, layers=3, branches=4), None, ["gather2_kernel", "proj_kv_kernel",
                                                                        "gather_kernel<hashed>", "proj_kv_kernel"]),
+    ("one token M=2", dict(B=64, T=1, layers=2, branches=2), False, ["gather_proj_kernel"]),
     ("mxfp8 2 layers", dict(B=2, T=40, layers=2, branches=2), True, ["gather2_kernel", "proj_kv_kernel"]),
     ("general product", dict(B=1, T=1500, layers=2, branches=1), False, ["gather2_kernel", "gemm_kernel",
                                                                          "gemm_kernel"]),
@@ -171,7 +172,11 @@ def test_layers_ahead_without_state(name, kw, mx, want):
     H = eg.to_device(w.H, "bf16", DEV)
     for li, (L, lay) in enumerate(zip(Ls, lays)):
         h_in = H.view(torch.int16).cpu().numpy().view(np.uint16).copy()
-        alpha, y = eg.forward_projected(out["kv"][li], H, L, B, T, want_alpha=True, want_y=True)
+        res = {}
+        names = stages(lambda: res.setdefault("ay", eg.forward_projected(out["kv"][li], H, L, B, T, want_alpha=True,
+                                                                          want_y=True)))
+        assert names == (["conv_kernel"] if T == 1 else ["gate_stats_kernel", "conv_kernel"]), names
+        alpha, y = res["ay"]
         torch.cuda.synchronize()
         ref = orc.forward(w.tokens, h_in, lay, "bf16", gemm="mxfp8" if mx else "exact")
         check_bf16_layer(to_f64(alpha), ref["alpha"], to_f64(y), ref["Y"], to_f64(H), orc.bf16_to_f64(h_in),
