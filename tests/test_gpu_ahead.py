@@ -57,6 +57,8 @@ FUSED = ["gather_proj_kernel"]
 # (table dims not a multiple of 32); and the LDS-staged product.
 KV_CASES = [
     ("K1024 fused", 3, dict(B=3, T=37), True, FUSED),
+    ("K1024 fused 64-token tiles", 3, dict(B=3, T=100), True, FUSED),
+    ("K512 fused 64-token tiles", 3, dict(B=2, T=200, table_dim=32), True, FUSED),
     ("K1024 lds", 3, dict(B=3, T=37), False, GATHER_THEN_PRODUCT),
     ("K768 frag", 3, dict(B=2, T=50, table_dim=48), True, GATHER_THEN_PRODUCT),
     ("K512 fused", 3, dict(B=2, T=45, table_dim=32), True, FUSED),
@@ -94,16 +96,19 @@ def test_projections_ahead_against_exact_product(name, cfg, kw, packed, want):
         assert np.all(err <= bound), (name, li, float(np.max(err - bound)))
 
 
-@pytest.mark.parametrize("mx,packed", [(False, True), (False, False), (True, False)],
-                         ids=["bf16-fused", "bf16-lds", "mxfp8"])
-def test_decode_two_layers_ahead(mx, packed):
-    """256 sequences with int8 tables: a 16-token prefill per layer through
+@pytest.mark.parametrize("mx,packed,S", [(False, True, 256), (False, True, 64), (False, False, 256),
+                                          (True, False, 256)],
+                         ids=["bf16-fused", "bf16-fused-32-token-tiles", "bf16-lds", "mxfp8"])
+def test_decode_two_layers_ahead(mx, packed, S):
+    """S sequences with int8 tables: a 16-token prefill per layer through
     engram_forward, then 3 decode steps in which both layers' Steps 1-5 run
-    in two launches and each layer's gate, conv and residual in one; H flows
-    from layer 0 into layer 1 and the states advance as in engram_forward."""
-    log(f"decode ahead mx={mx} packed={packed}")
-    w = inputs.make_config(3, T=3, rows_per_table=997)
-    S, M, d = w.B, 1, 1024
+    in one launch (two with the LDS-staged or FP8 product) and each layer's
+    gate, conv and residual in one; H flows from layer 0 into layer 1 and
+    the states advance as in engram_forward.  (At 64 sequences the fused
+    launch takes 32-token tiles.)"""
+    log(f"decode ahead mx={mx} packed={packed} S={S}")
+    w = inputs.make_config(3, B=S, T=3, rows_per_table=997)
+    M, d = 1, 1024
     lays = w.layers
     Ls = [eg.Layer(l, "bf16", DEV, mxfp8=mx, bf16_packed=packed) for l in lays]
     sts = [eg.DecodeState(S, 3, M, 9, d, DEV) for _ in Ls]
