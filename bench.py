@@ -355,7 +355,7 @@ KERNEL_SOURCES = {
     "gather2_kernel": (r"hashed_gather2_kernel<", ["gather.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
     "proj_kv_kernel": (r"proj_(gate_small2|frag2)_kernel<", ["proj_gate.hip", "ahead.hip"]),
     "gather_proj_kernel": (r"ahead_fused_kernel<", ["ahead.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
-    "conv_kernel": (r"conv_(strip_)?kernel<", ["gate_conv.hip"]),
+    "conv_kernel": (r"conv_(strip_|decode_)?kernel<", ["gate_conv.hip"]),
     "conv_gather_kernel": (r"conv_gather_kernel<",
                            ["gate_conv.hip", "gather_device.h", "hash_device.h", "hot_device.h"]),
 }
