@@ -315,12 +315,12 @@ def make_config(config: int, *, B: Optional[int] = None, T: Optional[int] = None
                 table_dim: Optional[int] = None, layers: Optional[int] = None,
                 context_len: int = 16, uniform_tokens: bool = False,
                 rows_per_table: Optional[int] = None, d: Optional[int] = None,
-                branches: Optional[int] = None) -> Workload:
+                branches: Optional[int] = None, heads: Optional[int] = None) -> Workload:
     """Build workload `config` (0..4).
 
-    B, T, layers, and (for small tests) the rows per table, the hidden width d
-    and the branch count may be overridden; the tables then hold the first
-    primes >= rows_per_table.
+    B, T, layers, and (for small tests) the rows per table, the hidden width d,
+    the branch count and (configs 1-4) the heads per order may be overridden;
+    the tables then hold the first primes >= rows_per_table.
     """
     if config == 0:
         B = B or 1
@@ -337,7 +337,7 @@ def make_config(config: int, *, B: Optional[int] = None, T: Optional[int] = None
         return Workload(CONFIG_NAMES[0], 0, F32, B, T, tokens, H, [lay])
 
     dd = d or 1024
-    common = dict(vocab=128_000, vocab_c=98_560, max_n=3, heads=8, dim=table_dim or 64, d=dd,
+    common = dict(vocab=128_000, vocab_c=98_560, max_n=3, heads=heads or 8, dim=table_dim or 64, d=dd,
                   store_dtype=BF16, w_std=1.0 / 32)
     c1_start = rows_per_table or C1_PRIME_START
     c4_start = rows_per_table or C4_PRIME_START

@@ -59,6 +59,10 @@ KV_CASES = [
     ("K1024 fused", 3, dict(B=3, T=37), True, FUSED),
     ("K1024 fused 64-token tiles", 3, dict(B=3, T=100), True, FUSED),
     ("K512 fused 64-token tiles", 3, dict(B=2, T=200, table_dim=32), True, FUSED),
+    ("K1024 dim 32 fused", 3, dict(B=2, T=45, table_dim=32, heads=16), True, FUSED),
+    ("K1024 dim 32 fused 64-token tiles", 3, dict(B=2, T=200, table_dim=32, heads=16), True, FUSED),
+    ("K1024 dim 128 fused", 3, dict(B=2, T=45, table_dim=128, heads=4), True, FUSED),
+    ("K512 dim 128 fused 64-token tiles", 3, dict(B=2, T=200, table_dim=128, heads=2), True, FUSED),
     ("K1024 lds", 3, dict(B=3, T=37), False, GATHER_THEN_PRODUCT),
     ("K768 frag", 3, dict(B=2, T=50, table_dim=48), True, GATHER_THEN_PRODUCT),
     ("K512 fused", 3, dict(B=2, T=45, table_dim=32), True, FUSED),
