@@ -85,7 +85,7 @@ def parse(argv=None):
     ap.add_argument("--no-layer-prefetch", action="store_true",
                     help="config 3: the same as --decode-schedule plain")
     ap.add_argument("--decode-schedule", choices=["ahead", "prefetch", "plain"], default="ahead",
-                    help="config 3: 'ahead' runs both layers' Steps 1-5 in two launches (engram_project_ahead) and "
+                    help="config 3: 'ahead' runs both layers' Steps 1-5 in one launch (engram_project_ahead) and "
                          "each layer's Steps 6-8 in one (engram_forward_projected); 'prefetch' carries the next "
                          "layer's retrieval in the conv launch (engram_forward_retrieved_prefetch); 'plain' is "
                          "engram_forward per layer")
@@ -303,7 +303,7 @@ def build_case(args, cfg, torch, eg, inputs, w=None, per_graph=10, hot_host=None
         case.extra["decode"] = "256 sequences x 1 token, 2 layers, after a 16-token prefill" + {
             "plain": "; engram_forward per layer",
             "prefetch": "; layer 1's retrieval runs inside layer 0's conv launch",
-            "ahead": "; both layers' Steps 1-5 in two launches ahead of the hidden states, then one gate+conv "
+            "ahead": "; both layers' Steps 1-5 in one launch ahead of the hidden states, then one gate+conv "
                      "launch per layer"}[schedule]
         case.extra["rotation"] = {"token_batches": ring, "hidden_batches": ring,
                                   "table_row_bytes_per_batch": rows_per_batch(w.layers, S)}

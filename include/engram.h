@@ -355,14 +355,19 @@ engram_status engram_forward_retrieved_prefetch(const int32_t* tokens, const voi
  * with the fused projection (d a multiple of 128 up to 4096); with states
  * (states[l] non-NULL for every layer, with ids), T must be 1 and each
  * state's ids and pos advance by that token here, so that the matching
- * engram_forward_projected reads them as advanced.  Layers go in pairs: one
- * launch gathers both layers' rows, one launch multiplies both (the
- * small-batch product; n_tok*(1+M)*d within its range, which a decode batch
- * of a few hundred sequences is; layers with w_packed take its
- * fragment-operand form).  Larger bf16 products without states run
- * the general product per layer; larger ones with states, or MXFP8 ones, are
- * ENGRAM_EUNSUPPORTED.  ws: at least engram_project_ahead_workspace() bytes,
- * 256-byte aligned (the gathered rows).
+ * engram_forward_projected reads them as advanced.  Layers go in pairs, in
+ * the small-batch range (n_tok*(1+M)*d within it, which a decode batch of a
+ * few hundred sequences is): with w_packed, int8 or bf16 tables of dim 32, 64
+ * or 128 (n_tables*dim = 512 or 1024), no HBM cache and no access counts,
+ * and at most 2048 sequences when states advance, one launch does both
+ * layers' Steps 1-5; otherwise one launch gathers both layers' rows and one
+ * multiplies both.  Larger bf16 products without states run the general
+ * product per layer; larger ones with states, or MXFP8 ones, are
+ * ENGRAM_EUNSUPPORTED.  The one-launch form advances states through
+ * arrival counts in a device-global ring: calls with states may overlap on
+ * one device (other streams, several graphs) up to 32 at a time.  ws: at
+ * least engram_project_ahead_workspace() bytes, 256-byte aligned (the
+ * gathered rows).
  *
  * engram_forward_projected: Steps 6-8 of layer L on kv from
  * engram_project_ahead with the same B, T and state; H as for engram_forward
