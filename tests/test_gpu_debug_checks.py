@@ -141,3 +141,27 @@ def test_out_of_range_hot_rows_read_as_cold_and_are_reported(debug_lib):
     expect = before.clone()
     expect[..., 0][before[..., 0] == r] = -1
     assert torch.equal(after, expect)
+
+
+def test_steps_ahead_out_of_range_tokens_are_clamped_and_reported(debug_lib):
+    """The one-launch Steps 1-5 of two decode layers (engram_project_ahead
+    with a packed W) checks the raw ids as the gather does, and the decode
+    state advances with the clamped ids."""
+    log("debug build: out-of-range token ids in the fused Steps 1-5")
+    w = inputs.make_config(3, B=64, T=1, rows_per_table=997)
+    V = w.layers[0].hash.vocab
+    bad = w.tokens.copy()
+    bad[0, 0], bad[5, 0], bad[40, 0] = -3, V + 7, V
+    clamped = np.clip(bad, 0, V - 1)
+    Ls = [eg.Layer(lay, "bf16", DEV) for lay in w.layers]
+    assert all(L.w_packed is not None for L in Ls)
+    st_bad = [eg.DecodeState(64, 3, 1, 9, 1024, DEV) for _ in Ls]
+    st_ref = [eg.DecodeState(64, 3, 1, 9, 1024, DEV) for _ in Ls]
+    kv_bad = eg.project_ahead(torch.from_numpy(bad).to(DEV), Ls, states=st_bad)
+    assert eg.debug_read_errors() == eg.ERR_TOKEN
+    kv_ref = eg.project_ahead(torch.from_numpy(clamped).to(DEV), Ls, states=st_ref)
+    assert eg.debug_read_errors() == 0
+    torch.cuda.synchronize()
+    for a, b, sa, sb in zip(kv_bad, kv_ref, st_bad, st_ref):
+        assert torch.equal(a, b)
+        assert torch.equal(sa.ids, sb.ids) and torch.equal(sa.pos, sb.pos)
