@@ -21,17 +21,17 @@
 //                       design of the DRAM offload study, "Engram embedding
 //                       extension: co-design for efficient DRAM/SSD offload",
 //                       decode section).
-// A workgroup's 64 x 64 output tile is split over its 8 wavefronts along K
-// (K/8 each); the 8 partial tiles meet in LDS (128 KiB) at the end.  Tiles run
-// feature tile fastest, so the token tiles that share a W tile share the
-// workgroup index modulo 8, and so an XCD and its L2.
+// A workgroup's 64 x 64 output tile (64 x 32 in small fused launches) is
+// split over its 8 wavefronts along K (K/8 each); the 8 partial tiles meet in
+// LDS (128 or 64 KiB) at the end.  Tiles run feature tile fastest, so the
+// token tiles that share a W tile share the workgroup index modulo 8, and so
+// an XCD and its L2.
 //
 // The K order inside the matrix operations: lane l = 32h + r of K16 step ks
 // takes columns 32(ks/2) + 16h + 8(ks%2) .. +7, so that a lane's two steps of
 // a 32-column group read 16 consecutive values of one table row (16 bytes of
 // an int8 row); W is packed the same way, so the sum is that of W e in
 // another order.
-#include <algorithm>
 #include <atomic>
 
 #include "device_util.h"
@@ -121,12 +121,13 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[2][TB]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 
-// This wavefront's W operands: K16 steps wave*SPW .. +SPW-1 of the 32-row
-// blocks 2tf and 2tf+1, step by step, so that step s waits only for its own.
 // The wavefront index, known to the compiler as uniform (so that what it
 // selects, table arguments and base addresses, stays in scalar registers).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// This wavefront's W operands: K16 steps wave*SPW .. +SPW-1 of the 32-row
+// blocks 2tf and 2tf+1 (K = 128 SPW), step by step, so that step s waits
+// only for its own.
 template <int SPW>
 __device__ __forceinline__ void load_w(const uint16_t* w_frag, int tf, u32x4_t (&wa)[2][SPW]) {
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -229,10 +230,7 @@ __device__ __forceinline__ void ahead_fused_body(const AheadJob& J, int tf, int 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int h = lane >> 5, r = lane & 31;
 
-  // The hash constants and row offsets of this wavefront's tables, read
-  // before anything waits: argument reads that miss the scalar cache take a
-  // memory latency each, and here they overlap the id loads instead of
-  // waiting in the chain behind them.
+  // The hash constants and row offsets of this wavefront's tables.
   constexpr int NT = GPT > NG ? 1 : NG / GPT;   // tables per wavefront
   TableHash th[NT];
   int64_t row_off[NT];
@@ -242,10 +240,11 @@ __device__ __forceinline__ void ahead_fused_body(const AheadJob& J, int tf, int 
     th[u] = table_hash(hs.a, j);
     row_off[u] = ta.row_offset[j];
   }
-  // All of these and the head in flight together, then one wait: the asm
-  // takes them as operands, so their loads are all issued before it (left
-  // to itself the compiler issues a load where its value is first needed
-  // and waits for it there, one round trip each).
+  // These and the head are read in one batch of scalar loads and one wait:
+  // the asm statements take them all as operands, so every load is issued
+  // before them.  Left to itself the compiler issues each argument read
+  // where its value is first needed and waits for it there, one memory
+  // round trip each (several, in a chain, before the first id load).
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::"s"(hd.tokens), "s"(hd.proj), "s"(hd.hist), "s"(hd.w_frag), "s"(hd.rows), "s"(hd.scale),
                "s"(hd.kv_out), "s"(hd.st_ids), "s"(hd.st_pos));
