@@ -589,9 +589,9 @@ __device__ __forceinline__ void conv_strip_body(const ConvArgs& a, int spx, int 
 // (ConvArgs.sums_from_kv), for the pages' conv (w = 4, dilation 3) and d <=
 // 1024: workgroup (b, m) holds the token's whole row, 4 channels a thread.
 // The same arithmetic as the single-token strip conv, laid out for latency:
-// every argument is read up front in one batch, and pos (which the state's
-// halo slots depend on) is loaded with the row, H and the conv weights, so
-// that the chain is arguments -> (pos, row) -> state rows, with the gate's
+// every argument is read up front in one batch, then pos (which the state's
+// halo slots depend on), the row, H and the conv weights are read together,
+// so that the chain is arguments -> (pos, row) -> state rows, with the gate's
 // block reduction inside the last latency.
 template <int HT>
 __global__ void __launch_bounds__(256)
@@ -623,7 +623,16 @@ conv_decode_kernel(ConvArgs a) {
   const int64_t row = b;   // T = 1: token b of the batch
   const float* vrow = vp + row * v_stride;
   char* hrow = static_cast<char*>(Hp) + (row * M + m) * d * (HT == ENGRAM_BF16 ? 2 : 4);
-  const int32_t pos_raw = has_state ? st_pos[b] : 0;
+  // pos first in the memory queue, from a valid address either way, so that
+  // waiting for it (reads retire in order) waits for nothing else.  The
+  // offset is a zero the compiler cannot see through: as a per-lane value,
+  // pos is not moved to a scalar register at the load, which would wait for
+  // it there, before the row's reads are issued.
+  int32_t lane0;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(lane0));
+  const int32_t* const pos_p = has_state ? st_pos + b : reinterpret_cast<const int32_t*>(vp);
+  const int32_t pos_ld = pos_p[lane0];
+  __builtin_amdgcn_sched_barrier(0);
   float v[CPT], kk[CPT], h[CPT];
   loadc<ENGRAM_F32, CPT>(vrow, cc, v);
   loadc<ENGRAM_F32, CPT>(vrow, static_cast<uint32_t>((1 + m) * d) + cc, kk);
@@ -638,24 +647,29 @@ conv_decode_kernel(ConvArgs a) {
     }
   }
   // the taps' halo rows r = 0, 3, 6 (positions pos - 9, - 6, - 3): the
-  // state's ring slots, which already hold u (gamma 1); without a state the
-  // chunk starts here, and they are padding (gamma 0 times the clamped row)
-  const int64_t pos = static_cast<int64_t>(pos_raw) - (pos_adv ? 1 : 0);
+  // state's ring slots (pos + 3 r) % 9, which already hold u (gamma 1).
+  // Without a state the chunk starts here and they are padding; as zeros
+  // they add +0 to a sum that starts at +0, as gamma 0 times the clamped row
+  // does in the strip conv, so both give the same bits.  (Padding taken from
+  // v would make the state's reads wait for v's.)
+  __builtin_amdgcn_sched_barrier(0);
+  int p9 = 0;
   float hv[KW - 1][CPT];
-  float hg = 0.f;
   if (has_state) {
-    hg = 1.0f;
+    p9 = (pos_ld - (pos_adv ? 1 : 0)) % SPAN;
+    if (p9 < 0) p9 += SPAN;
+    const float* ring = st_conv + (static_cast<int64_t>(b) * M + m) * SPAN * d;
 #pragma unroll
     for (int j = 0; j < KW - 1; ++j) {
-      int slot = static_cast<int>((pos + (j * DIL - SPAN)) % SPAN);
-      if (slot < 0) slot += SPAN;
-      loadc<ENGRAM_F32, CPT>(st_conv + ((static_cast<int64_t>(b) * M + m) * SPAN + slot) * d, cc, hv[j]);
+      int slot = p9 + j * DIL;
+      if (slot >= SPAN) slot -= SPAN;
+      loadc<ENGRAM_F32, CPT>(ring + static_cast<int64_t>(slot) * d, cc, hv[j]);
     }
   } else {
 #pragma unroll
     for (int j = 0; j < KW - 1; ++j)
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) hv[j][i] = v[i];
+      for (int i = 0; i < CPT; ++i) hv[j][i] = 0.f;
   }
 
   // the gate's four sums over the row (the strip conv's order)
@@ -706,7 +720,7 @@ conv_decode_kernel(ConvArgs a) {
     u[i] = gm * v[i];
     float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < KW - 1; ++j) acc += wt[i][j] * (hg * hv[j][i]);
+    for (int j = 0; j < KW - 1; ++j) acc += wt[i][j] * hv[j][i];
     acc += wt[i][KW - 1] * u[i];
     y[i] = silu(acc) + al * v[i];
     hn[i] = h[i] + y[i];
@@ -716,10 +730,8 @@ conv_decode_kernel(ConvArgs a) {
     if (y_out != nullptr) storec<ENGRAM_F32, CPT>(y_out + (row * M + m) * d, c, y);
     // the new position's conv input goes to its ring slot (pos % SPAN, which
     // held position pos - SPAN: read above as the oldest tap, by this thread)
-    if (commit_u && has_state) {
-      const int slot = static_cast<int>(pos % SPAN);
-      storec<ENGRAM_F32, CPT>(st_conv + ((static_cast<int64_t>(b) * M + m) * SPAN + slot) * d, c, u);
-    }
+    if (commit_u && has_state)
+      storec<ENGRAM_F32, CPT>(st_conv + ((static_cast<int64_t>(b) * M + m) * SPAN + p9) * d, c, u);
   }
 }
 
