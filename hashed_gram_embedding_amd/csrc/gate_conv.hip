@@ -386,17 +386,25 @@ __device__ __forceinline__ void conv_strip_body(const ConvArgs& a, int spx, int 
   const int nqb = a.qv + a.qk;
 
   // ---- issue every load ----
+  // A strip that starts the chunk with a decode state reads its halo from
+  // the state's ring slots, which depend on pos: pos is read first (reads
+  // retire in order, so waiting for it waits for nothing else), as a
+  // per-lane value (the compiler moves a uniform load's value to a scalar
+  // register at the load and waits for it there), and the halo reads are
+  // issued after the strip's own rows, H and the weights.
+  const bool ring_halo = a.has_state && t0 < SPAN;
+  int32_t pos_ld = 0;
+  if (ring_halo) {
+    int32_t lane0;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(lane0));
+    pos_ld = a.st.pos[b + lane0];
+  }
+  __builtin_amdgcn_sched_barrier(0);
   float v[R][CPT];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int t = t0 - SPAN + r;
-    if (r < SPAN && t < 0 && a.has_state) {
-      // halo before the chunk: the state's circular slot of position pos + t
-      const int64_t pos = static_cast<int64_t>(a.st.pos[b]) - (a.pos_advanced ? T : 0);
-      int slot = static_cast<int>((pos + t) % SPAN);
-      if (slot < 0) slot += SPAN;
-      loadc<ENGRAM_F32, CPT>(a.st.conv + ((static_cast<int64_t>(b) * M + m) * SPAN + slot) * d, cc, v[r]);
-    } else {
+    if (!(r < SPAN && t < 0 && ring_halo)) {
       const int tc = t < 0 ? 0 : (t >= Ti ? Ti - 1 : t);
       loadc<VT, CPT>(vseq + static_cast<int64_t>(tc) * vrow, cc, v[r]);
     }
@@ -418,6 +426,22 @@ __device__ __forceinline__ void conv_strip_body(const ConvArgs& a, int spx, int 
       } else {
 #pragma unroll
         for (int j = 0; j < KW; ++j) wt[i][j] = wm[(cc + i) * KW + j];
+      }
+    }
+  }
+  // the halo before the chunk: the state's ring slot of position pos + t
+  int p0 = 0;   // pos at the chunk's start, mod SPAN
+  if (ring_halo) {
+    p0 = (pos_ld - (a.pos_advanced ? Ti : 0)) % SPAN;
+    if (p0 < 0) p0 += SPAN;
+    const float* ring = a.st.conv + (static_cast<int64_t>(b) * M + m) * SPAN * d;
+#pragma unroll
+    for (int r = 0; r < SPAN; ++r) {
+      const int t = t0 - SPAN + r;
+      if (t < 0) {
+        int slot = (p0 + t) % SPAN;
+        if (slot < 0) slot += SPAN;
+        loadc<ENGRAM_F32, CPT>(ring + static_cast<int64_t>(slot) * d, cc, v[r]);
       }
     }
   }
@@ -575,8 +599,7 @@ __device__ __forceinline__ void conv_strip_body(const ConvArgs& a, int spx, int 
   // workgroup reads the slot).
   if constexpr (TS == 1) {
     if (a.commit_u && active) {
-      const int64_t pos = static_cast<int64_t>(a.st.pos[b]) - (a.pos_advanced ? T : 0);
-      const int slot = static_cast<int>(pos % SPAN);
+      const int slot = p0;   // T = 1: the chunk's one position
       float uc[CPT];
 #pragma unroll
       for (int i = 0; i < CPT; ++i) uc[i] = u[SPAN][i];
