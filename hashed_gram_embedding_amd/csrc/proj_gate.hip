@@ -305,15 +305,26 @@ proj_gate_kernel(ProjGateArgs a) {
       s3 += __shfl_xor(s3, 32, 64);
       if ((lane >> 5) == 0) red[tl * WF + wf] = make_float4(0.f, 0.f, 0.f, s3);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wavefront's block is in LDS
+      // every LDS read first, then the (ragged-guarded) stores: a read inside
+      // each guarded store would go out and be waited for one at a time
+      // (native vectors: an array of HIP's float4 structs stays in scratch)
+      constexpr int NIT = 32 * VC / 64;
+      typedef float f32x4_t __attribute__((ext_vector_type(4)));
+      f32x4_t xs[NIT];
 #pragma unroll
-      for (int it = 0; it < 32 * VC / 64; ++it) {
+      for (int it = 0; it < NIT; ++it) {
+        const int u = it * 64 + lane;
+        const int rr = u / VC, c = u % VC;
+        xs[it] = reinterpret_cast<const f32x4_t*>(Vs)[rr * VC + (c ^ (rr & 15))];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next block's writes
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
         const int u = it * 64 + lane;
         const int rr = u / VC, c = u % VC;
         const int64_t trow = wt * (TK / WT) + j * 32 + rr;
-        const float4 x = Vs[rr * VC + (c ^ (rr & 15))];
-        if (t0 + trow < a.n_tok) *reinterpret_cast<float4*>(vrow0 + trow * d + c * 4) = x;
+        if (t0 + trow < a.n_tok) *reinterpret_cast<f32x4_t*>(vrow0 + trow * d + c * 4) = xs[it];
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next block's writes
     }
   } else {
     // The h values of this block go into LDS with 16-byte direct loads, a
@@ -387,7 +398,9 @@ proj_gate_kernel(ProjGateArgs a) {
       if ((lane >> 5) == 0) red[tl * WF + wf] = make_float4(s0, s1j, s2, 0.f);
     }
   }
-  __syncthreads();
+  // the partials are in LDS; the v stores need not have landed (a full
+  // __syncthreads would also wait for them)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   for (int tl = tid; tl < TK; tl += kThreads) {
     const int64_t tok = t0 + tl;
     if (tok < a.n_tok) {
