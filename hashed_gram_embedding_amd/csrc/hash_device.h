@@ -65,11 +65,12 @@ __device__ __forceinline__ WindowSrc window_src(const HashSrc& hs) {
 // Steps 1-2 for ITEMS tokens at positions t[q] of sequences b[q], in two
 // halves so that a kernel can issue other loads in between.  window_loads
 // loads the P values of the window's tokens (xp) and the history ids that
-// positions before the sequence start need (hv, 0 where there are none):
-// the history index does not depend on the token ids, so those loads go out
-// just before the token loads, into registers of their own, and the P
-// lookups take the second and last memory latency.  (Memory reads return in
-// order, so once the P lookups are issued the history has arrived.)
+// positions before the sequence start need (hv, 0 where there are none).
+// With HIST_ALL the history index does not depend on the token ids, so
+// those loads go out just before the token loads, into registers of their
+// own, and the P lookups take the second and last memory latency.  (Memory
+// reads return in order, so once the P lookups are issued the history has
+// arrived.)
 // window_select then forms x[q][i] = x'_{t-i}, newest first.
 // HIST_ALL: the caller guarantees hs.hist != null and T <= max_n - 1 (every
 // token reads history, as in decode), so that the choice below is not a
@@ -80,16 +81,12 @@ __device__ __forceinline__ void window_loads(const WindowSrc& hs, const uint32_t
                                              uint32_t (&hv)[ITEMS][ENGRAM_MAX_ORDER]) {
   const uint32_t T = static_cast<uint32_t>(hs.T);
   const int hl = hs.max_n - 1;
-#pragma unroll
-  for (int q = 0; q < ITEMS; ++q)
-#pragma unroll
-    for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) hv[q][i] = 0u;
-  if (HIST_ALL || (hs.hist != nullptr && T <= static_cast<uint32_t>(hl))) {
-    // every token reads history (decode): loads without branches or
-    // selects, so that none waits for another.  For i <= hl and t < i the
-    // index hl + t - i is in range; positions i > hl (>= the largest order)
-    // enter no hash (their multipliers are 0) and no hot key, so the clamped
-    // index serves them as well as the pad would.
+  // every token reads history (decode): loads without branches or selects,
+  // so that none waits for another.  For i <= hl and t < i the index
+  // hl + t - i is in range; positions i > hl (>= the largest order) enter no
+  // hash (their multipliers are 0) and no hot key, so the clamped index
+  // serves them as well as the pad would.
+  auto hist_all = [&]() {
 #pragma unroll
     for (int q = 0; q < ITEMS; ++q)
 #pragma unroll
@@ -97,19 +94,12 @@ __device__ __forceinline__ void window_loads(const WindowSrc& hs, const uint32_t
         const int idx = hl + static_cast<int>(t[q]) - i;   // index in the history of position t - i
         hv[q][i] = static_cast<uint32_t>(hs.hist[b[q] * hl + min(max(idx, 0), hl - 1)]);
       }
-  } else if (!HIST_ALL && hs.hist != nullptr) {
-    // only tokens near a sequence start do
+  };
 #pragma unroll
-    for (int q = 0; q < ITEMS; ++q) {
-      if (t[q] < static_cast<uint32_t>(hl)) {
+  for (int q = 0; q < ITEMS; ++q)
 #pragma unroll
-        for (int i = 1; i < ENGRAM_MAX_ORDER; ++i) {
-          const int idx = hl + static_cast<int>(t[q]) - i;
-          if (idx >= 0 && idx < hl) hv[q][i] = static_cast<uint32_t>(hs.hist[b[q] * hl + idx]);
-        }
-      }
-    }
-  }
+    for (int i = 0; i < ENGRAM_MAX_ORDER; ++i) hv[q][i] = 0u;
+  if constexpr (HIST_ALL) hist_all();
   int32_t tk[ITEMS][ENGRAM_MAX_ORDER];
 #pragma unroll
   for (int q = 0; q < ITEMS; ++q)
@@ -121,6 +111,27 @@ __device__ __forceinline__ void window_loads(const WindowSrc& hs, const uint32_t
 #pragma unroll
     for (int i = 0; i < ENGRAM_MAX_ORDER; ++i)
       xp[q][i] = static_cast<uint32_t>(hs.proj[token_in_vocab(tk[q][i], hs.vocab, hs.err)]);
+  // Otherwise the history (if any) is read after the P lookups are issued:
+  // its branches ahead of the token loads made the compiler wait, on every
+  // path, for the loads issued before them (the callers' table constants)
+  // before reading the token ids.
+  if constexpr (!HIST_ALL) {
+    if (hs.hist != nullptr && T <= static_cast<uint32_t>(hl)) {
+      hist_all();
+    } else if (hs.hist != nullptr) {
+      // only tokens near a sequence start do
+#pragma unroll
+      for (int q = 0; q < ITEMS; ++q) {
+        if (t[q] < static_cast<uint32_t>(hl)) {
+#pragma unroll
+          for (int i = 1; i < ENGRAM_MAX_ORDER; ++i) {
+            const int idx = hl + static_cast<int>(t[q]) - i;
+            if (idx >= 0 && idx < hl) hv[q][i] = static_cast<uint32_t>(hs.hist[b[q] * hl + idx]);
+          }
+        }
+      }
+    }
+  }
 }
 
 template <int ITEMS>
