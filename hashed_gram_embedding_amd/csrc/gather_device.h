@@ -94,6 +94,27 @@ __device__ __forceinline__ void store8(void* e, int64_t out, int64_t mx_scale_ba
 template <int IN, int OUT, bool HOT, int ITEMS>
 __device__ __forceinline__ void hashed_gather_body(uint32_t gid, uint32_t n_tok, const TableArgs& ta,
                                                    void* __restrict__ e, const HashSrc& hs) {
+  // Every scalar argument the path needs is read in one batch with one wait:
+  // the asm statements take them as operands, so all their loads are issued
+  // before them.  Left to itself the compiler reads the grid bound's
+  // arguments, waits, then reads the rest and waits again, two round trips
+  // before the first id load.
+  {
+    const void* const p0 = hs.tokens;
+    const void* const p1 = hs.proj;
+    const void* const p2 = hs.hist;
+    const void* const p3 = ta.rows;
+    const void* const p4 = ta.scale;
+    const void* const p5 = ta.cache_slot;
+    const void* const p6 = ta.counts;
+    const void* const p7 = e;
+    const int32_t i0 = ta.n_tables, i1 = ta.dim, i2 = hs.a.max_n, i3 = hs.a.vocab;
+    const int64_t i4 = hs.T;
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"s"(p0), "s"(p1), "s"(p2), "s"(p3), "s"(p4), "s"(p5), "s"(p6), "s"(p7));
+    asm volatile("" ::"s"(i0), "s"(i1), "s"(i2), "s"(i3), "s"(i4), "s"(n_tok));
+    __builtin_amdgcn_sched_barrier(0);
+  }
   const uint32_t nt = static_cast<uint32_t>(ta.n_tables);
   const uint32_t chunks = static_cast<uint32_t>(ta.dim) >> 3;
   const uint32_t per_group = nt * chunks;
