@@ -350,6 +350,30 @@ __device__ __forceinline__ void conv_strip_body(const ConvArgs& a, int spx, int 
   __shared__ float alpha_s[R];
   __shared__ float gamma_s[R];
   const GateConvArgs& g = a.g;
+  // Every scalar argument read in one batch with one wait (the asm
+  // statements take them as operands, so all their loads are issued before
+  // them); left to itself the compiler issues each where it is first needed
+  // and waits there, three or four round trips before the first row read.
+  {
+    const void* const p0 = a.H;
+    const void* const p1 = a.v;
+    const void* const p2 = a.stats;
+    const void* const p3 = g.conv_w;
+    const void* const p4 = a.st.conv;
+    const void* const p5 = a.st.pos;
+    const void* const p6 = a.alpha_out;
+    const void* const p7 = a.gamma_out;
+    const void* const p8 = a.y_out;
+    const int64_t l0 = a.v_stride, l1 = a.T;
+    const int32_t i0 = a.qv, i1 = a.qk, i2 = a.nq, i3 = a.kq0, i4 = g.d, i5 = g.branches, i6 = a.has_state,
+                  i7 = a.pos_advanced, i8 = a.commit_u, i9 = a.sums_from_kv;
+    const float f0 = g.eps;
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"s"(p0), "s"(p1), "s"(p2), "s"(p3), "s"(p4), "s"(p5), "s"(p6), "s"(p7), "s"(p8));
+    asm volatile("" ::"s"(l0), "s"(l1), "s"(i0), "s"(i1), "s"(i2), "s"(i3), "s"(i4), "s"(i5), "s"(i6), "s"(i7),
+                 "s"(i8), "s"(i9), "s"(f0));
+    __builtin_amdgcn_sched_barrier(0);
+  }
   const int M = g.branches;
   const int d = g.d;
   const int64_t T = a.T;
